@@ -1,0 +1,529 @@
+"""Pins for the CPU oracle (CPU only).
+
+Every check compares the oracle with something other than itself: torch's
+nn.MultiheadAttention (a library routine), closed forms, invariants the kpnn2
+page states, the page's worked example, and brute force on tiny inputs. The
+mutation tests at the end plant plausible mistakes in copies of the oracle's
+C source and require that some pin fails for each.
+"""
+import json
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from graph_sparse_head_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _params64(rng, E, bias=True):
+    p = {}
+    for n in "qkvo":
+        p["w" + n] = rng.uniform(-0.5, 0.5, size=(E, E))
+        p["b" + n] = rng.normal(0, 0.1, size=E) if bias else None
+    return p
+
+
+def _torch_mha(E, H, params, xq, xk, xv, mask=None):
+    """torch.nn.MultiheadAttention in float64 loaded with the same weights.
+
+    mask: bool (L, S), True where the pair is not an edge. Returns output
+    (B, L, E) and per-head weights (B, H, L, S)."""
+    bias = params["bq"] is not None
+    mha = torch.nn.MultiheadAttention(E, H, bias=bias, batch_first=True).double()
+    with torch.no_grad():
+        mha.in_proj_weight.copy_(torch.from_numpy(np.concatenate(
+            [params["wq"], params["wk"], params["wv"]], 0)))
+        mha.out_proj.weight.copy_(torch.from_numpy(params["wo"]))
+        if bias:
+            mha.in_proj_bias.copy_(torch.from_numpy(np.concatenate(
+                [params["bq"], params["bk"], params["bv"]], 0)))
+            mha.out_proj.bias.copy_(torch.from_numpy(params["bo"]))
+    mha.train(False)
+    m = None if mask is None else torch.from_numpy(mask)
+    with torch.no_grad():
+        out, w = mha(torch.from_numpy(xq), torch.from_numpy(xk), torch.from_numpy(xv),
+                     attn_mask=m, need_weights=True, average_attn_weights=False)
+    return out.numpy(), w.numpy()
+
+
+def _dense_masked_numpy(E, H, params, xq, xk, xv, src, tgt):
+    """Dense scores for every (target, source) pair, non-edges set to -inf."""
+    B, L, _ = xq.shape
+    S = xk.shape[1]
+    d = E // H
+
+    def lin(x, w, b):
+        return x @ w.T + (0.0 if b is None else b)
+
+    Q, K, V = lin(xq, params["wq"], params["bq"]), lin(xk, params["wk"], params["bk"]), \
+        lin(xv, params["wv"], params["bv"])
+    allowed = np.zeros((L, S), bool)
+    allowed[tgt, src] = True
+    out = np.empty((B, L, E))
+    for b in range(B):
+        heads = []
+        for h in range(H):
+            sl = slice(h * d, (h + 1) * d)
+            z = Q[b][:, sl] @ K[b][:, sl].T / math.sqrt(d)
+            z = np.where(allowed, z, -np.inf)
+            with np.errstate(invalid="ignore"):
+                p = np.exp(z - z.max(axis=1, keepdims=True))
+                p = p / p.sum(axis=1, keepdims=True)
+            heads.append(p @ V[b][:, sl])
+        out[b] = lin(np.concatenate(heads, axis=1), params["wo"], params["bo"])
+    return out
+
+
+def _run(E, H, params, xq, xk, xv, src, tgt, **kw):
+    B, L, _ = xq.shape
+    S = xk.shape[1]
+    return oracle.forward(B, L, S, E, H, xq, xk, xv, params, src, tgt, **kw)
+
+
+# ---------------------------------------------------------------------------
+# (a) brute-force masked dense MHA on tiny random graphs
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_masked_dense_mha(seed):
+    rng = np.random.default_rng(1000 + seed)
+    H = int(rng.choice([1, 2, 4]))
+    E = H * int(rng.choice([1, 2, 3, 4]))
+    while E > 16:
+        E -= H
+    L = int(rng.integers(1, 13))
+    S = L if rng.random() < 0.6 else int(rng.integers(1, 13))
+    B = int(rng.integers(1, 4))
+    src, tgt = synth.random_graph(rng, L, S, float(rng.uniform(0.1, 0.7)))
+    if src.size == 0:
+        src, tgt = np.array([0], np.int64), np.array([0], np.int64)
+    params = _params64(rng, E, bias=bool(rng.random() < 0.8))
+    xq = rng.standard_normal((B, L, E))
+    same = S == L and rng.random() < 0.5
+    xk = xq if same else rng.standard_normal((B, S, E))
+    xv = xk if (same or rng.random() < 0.5) else rng.standard_normal((B, S, E))
+    res = _run(E, H, params, xq, xk, xv, src, tgt, want_weights=True)
+    has_src = np.bincount(tgt, minlength=L) > 0
+
+    dense = _dense_masked_numpy(E, H, params, xq, xk, xv, src, tgt)
+    np.testing.assert_allclose(res["out"][:, has_src], dense[:, has_src], rtol=0, atol=1e-12)
+
+    mask = np.ones((L, S), bool)
+    mask[tgt, src] = False
+    t_out, t_w = _torch_mha(E, H, params, xq, xk, xv, mask)
+    np.testing.assert_allclose(res["out"][:, has_src], t_out[:, has_src], rtol=0, atol=1e-12)
+    # per-head weights gathered at the live pairs
+    np.testing.assert_allclose(res["weights"], np.transpose(t_w[:, :, tgt, src], (0, 2, 1)),
+                               rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# (b) the complete graph is ordinary dense MHA
+
+
+@pytest.mark.parametrize("bias", ["normal", "zero", "none"])
+def test_complete_graph_equals_dense_mha(bias):
+    c = synth.complete(bias=bias)
+    res = oracle.case_forward(c, want_weights=True)
+    params = {k: oracle.widen(v, "f32") for k, v in c.params.items()}
+    x = oracle.widen(c.xq, "f32")
+    t_out, t_w = _torch_mha(c.E, c.H, params, x, x, x)
+    np.testing.assert_allclose(res["out"], t_out, rtol=0, atol=1e-12)
+    avg = oracle.average_heads(res["weights"])                 # (B, nnz)
+    t_avg = t_w.mean(axis=1)                                   # (B, L, S)
+    np.testing.assert_allclose(avg, t_avg[:, c.tgt, c.src], rtol=0, atol=1e-12)
+
+
+def test_dense_lesson_shapes_and_equality():
+    g = json.load(open(os.path.join(GOLD, "dense_lesson.json")))
+    E, H, n, B = g["embed_dim"], g["num_heads"], g["tokens"], g["batch"]
+    rng = np.random.default_rng(7)
+    params = _params64(rng, E)
+    x = rng.standard_normal((B, n, E))
+    s, t = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    src, tgt = s.ravel(), t.ravel()
+    res = _run(E, H, params, x, x, x, src, tgt, want_weights=True)
+    t_out, t_w = _torch_mha(E, H, params, x, x, x)
+    assert list(res["out"].shape) == g["output_shape"]
+    dense_avg = np.zeros((B, n, n))
+    dense_avg[:, tgt, src] = oracle.average_heads(res["weights"])
+    assert list(dense_avg.shape) == g["averaged_weights_shape"]
+    assert np.abs(res["out"] - t_out).max() <= 1e-12
+    assert np.allclose(res["out"], t_out, atol=g["allclose_atol"])
+    np.testing.assert_allclose(dense_avg, t_w.mean(axis=1), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# (c) softmax invariants
+
+
+@pytest.mark.parametrize("maker", ["tiny", "small_gene", "small_bipartite"])
+def test_softmax_invariants(maker):
+    c = {"tiny": synth.tiny,
+         "small_gene": lambda: synth.gene(n=300, B=3, max_deg=60, dtype="f32"),
+         "small_bipartite": lambda: synth.bipartite(L=40, S=300, B=2, E=32, H=4, lo=2, hi=60)}[maker]()
+    res = oracle.case_forward(c, want_weights=True)
+    w = res["weights"]
+    assert np.isfinite(w).all() and (w >= 0).all()
+    sums = np.zeros((c.B, c.L, c.H))
+    np.add.at(sums, (slice(None), res["tgt"]), w)
+    deg = np.bincount(res["tgt"], minlength=c.L)
+    np.testing.assert_allclose(sums[:, deg > 0], 1.0, rtol=0, atol=1e-12)
+    assert (sums[:, deg == 0] == 0).all()
+    # a target without an edge outputs exactly the out_proj bias
+    bo = oracle.widen(c.params["bo"], c.dtype)
+    assert (res["out"][:, deg == 0] == bo).all()
+
+
+# ---------------------------------------------------------------------------
+# (d) locality by perturbation
+
+
+def test_locality_same_tokens():
+    c = synth.gene(n=200, B=2, E=16, H=2, dtype="f32", max_deg=40)
+    base = oracle.case_forward(c)
+    src, tgt = base["src"], base["tgt"]
+    rng = np.random.default_rng(3)
+    for j in rng.choice(c.L, 8, replace=False):
+        x = c.xq.copy()
+        x[1, j] += 0.5
+        c2 = synth.Case(**{**c.__dict__, "xq": x, "xk": x, "xv": x})
+        out = oracle.case_forward(c2)["out"]
+        allowed = {int(j)} | set(tgt[src == j].tolist())
+        changed = set(np.nonzero((out[1] != base["out"][1]).any(axis=1))[0].tolist())
+        assert changed <= allowed
+        if (tgt == j).sum() >= 2:
+            assert int(j) in changed                 # its query reweighs its sources
+        else:
+            # zero sources: the bias; one source: weight 1 whatever the query
+            assert int(j) not in changed
+        assert (out[0] == base["out"][0]).all()      # other sample untouched
+        for t in allowed - {int(j)}:
+            assert t in changed
+
+
+def test_locality_bipartite():
+    c = synth.bipartite(L=30, S=200, B=1, E=16, H=2, lo=2, hi=40)
+    base = oracle.case_forward(c)
+    src, tgt = base["src"], base["tgt"]
+    xq = c.xq.copy()
+    xq[0, 5] += 1.0
+    out = oracle.case_forward(synth.Case(**{**c.__dict__, "xq": xq}))["out"]
+    assert set(np.nonzero((out[0] != base["out"][0]).any(axis=1))[0].tolist()) == {5}
+    g = int(src[0])
+    xkv = c.xk.copy()
+    xkv[0, g] += 1.0
+    out = oracle.case_forward(synth.Case(**{**c.__dict__, "xk": xkv, "xv": xkv}))["out"]
+    changed = set(np.nonzero((out[0] != base["out"][0]).any(axis=1))[0].tolist())
+    assert changed == set(tgt[src == g].tolist())
+
+
+# ---------------------------------------------------------------------------
+# (e) the parameters do not depend on the graph
+
+
+def test_parameter_count_independent_of_graph():
+    E, H = 16, 4
+    rng = np.random.default_rng(5)
+    params = _params64(rng, E)
+    assert sum(v.size for k, v in params.items() if k[0] == "w") == 4 * E * E
+    assert sum(v.size for k, v in params.items() if k[0] == "b") == 4 * E
+    for L, S, p in ((5, 5, 0.5), (9, 3, 0.4), (2, 11, 0.9)):
+        src, tgt = synth.random_graph(rng, L, S, p)
+        if src.size == 0:
+            continue
+        x = rng.standard_normal((1, L, E))
+        k = rng.standard_normal((1, S, E))
+        assert _run(E, H, params, x, k, k, src, tgt)["out"].shape == (1, L, E)
+
+
+# ---------------------------------------------------------------------------
+# worked example of the kpnn2 page
+
+
+def test_worked_example():
+    g = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    src0 = np.array([p[0] for p in g["given_pairs_src_tgt"]])
+    tgt0 = np.array([p[1] for p in g["given_pairs_src_tgt"]])
+    E, H, B = g["embed_dim"], g["num_heads"], g["batch"]
+    n = len(g["nodes"])
+    src, tgt = oracle.prepare_edges(src0, tgt0, n, n, E, H, add_self_loops=True)
+    gw = g["with_self_loops"]
+    assert src.shape[0] == gw["nnz"] and E // H == gw["head_dim"]
+    printed = [f"{g['nodes'][s]} -> {g['nodes'][t]}" for s, t in zip(src, tgt)]
+    assert printed == gw["printed_edges"]
+    c = synth.worked_example(B=B, add_self_loops=True)
+    res = oracle.case_forward(c, want_weights=True, want_mixed=True)
+    assert list(res["out"].shape) == gw["output_shape"]
+    assert list(oracle.average_heads(res["weights"]).shape) == gw["weights_shape"]
+    # x (node 2) has only its own loop: weight 1 and it passes on its own value
+    e_x = int(np.nonzero((src == 2) & (tgt == 2))[0][0])
+    assert (res["weights"][:, e_x, :] == 1.0).all()
+    p = {k: oracle.widen(v, "f32") for k, v in c.params.items()}
+    x = oracle.widen(c.xq, "f32")
+    v_x = np.array([[sum(x[b, 2, i] * p["wv"][o, i] for i in range(E)) + p["bv"][o]
+                     for o in range(E)] for b in range(B)])
+    np.testing.assert_allclose(res["mixed"][:, 2], v_x, rtol=0, atol=1e-14)
+
+    gn = g["without_self_loops"]
+    src, tgt = oracle.prepare_edges(src0, tgt0, n, n, E, H, add_self_loops=False)
+    assert src.shape[0] == gn["nnz"]
+    c = synth.worked_example(B=B, add_self_loops=False)
+    res = oracle.case_forward(c, want_weights=True)
+    assert (res["out"][:, 2] == p["bo"]).all()          # x has no source
+    assert np.isfinite(res["out"]).all()
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+
+
+def test_degree_one_is_exact():
+    rng = np.random.default_rng(11)
+    E, H, B, n = 12, 3, 2, 6
+    params = _params64(rng, E)
+    x = rng.standard_normal((B, n, E))
+    src = np.array([3, 0, 5])
+    tgt = np.array([1, 4, 2])
+    res = _run(E, H, params, x, x, x, src, tgt, want_weights=True, want_mixed=True)
+    assert (res["weights"] == 1.0).all()
+    V = x @ params["wv"].T + params["bv"]
+    for s, t in zip(src, tgt):
+        np.testing.assert_allclose(res["mixed"][:, t], V[:, s], rtol=0, atol=1e-14)
+
+
+def test_identical_keys_share_weight_equally():
+    rng = np.random.default_rng(12)
+    E, H, B, L, S = 8, 2, 2, 4, 9
+    params = _params64(rng, E)
+    xq = rng.standard_normal((B, L, E))
+    xk = np.repeat(rng.standard_normal((B, 1, E)), S, axis=1)     # every key token equal
+    xv = rng.standard_normal((B, S, E))
+    src, tgt = synth.random_graph(rng, L, S, 0.6)
+    res = _run(E, H, params, xq, xk, xv, src, tgt, want_weights=True, want_mixed=True)
+    deg = np.bincount(tgt, minlength=L)
+    np.testing.assert_allclose(res["weights"], (1.0 / deg[tgt])[None, :, None] *
+                               np.ones((B, 1, H)), rtol=0, atol=1e-15)
+    V = xv @ params["wv"].T + params["bv"]
+    for t in range(L):
+        if deg[t]:
+            np.testing.assert_allclose(res["mixed"][:, t], V[:, src[tgt == t]].mean(axis=1),
+                                       rtol=0, atol=1e-13)
+
+
+def test_identical_values_pass_through():
+    rng = np.random.default_rng(13)
+    E, H, B, L, S = 8, 4, 3, 5, 7
+    params = _params64(rng, E)
+    xq = rng.standard_normal((B, L, E))
+    xk = rng.standard_normal((B, S, E))
+    xv = np.repeat(rng.standard_normal((B, 1, E)), S, axis=1)
+    src, tgt = synth.random_graph(rng, L, S, 0.7)
+    res = _run(E, H, params, xq, xk, xv, src, tgt, want_mixed=True)
+    V = xv[:, 0] @ params["wv"].T + params["bv"]
+    deg = np.bincount(tgt, minlength=L)
+    for t in range(L):
+        if deg[t]:
+            np.testing.assert_allclose(res["mixed"][:, t], V, rtol=0, atol=1e-13)
+
+
+def test_head_decomposition():
+    """Head h of a 4-head layer equals a 1-head layer whose projections keep
+    only head h's channels (queries scaled by 2 so that 1/sqrt(E) matches
+    1/sqrt(d) with E = 4 d); out_proj is linear, so the heads' shares add up."""
+    rng = np.random.default_rng(14)
+    E, H, B, L, S = 16, 4, 2, 6, 8
+    d = E // H
+    params = _params64(rng, E)
+    xq = rng.standard_normal((B, L, E))
+    xk = rng.standard_normal((B, S, E))
+    xv = rng.standard_normal((B, S, E))
+    src, tgt = synth.random_graph(rng, L, S, 0.5)
+    full = _run(E, H, params, xq, xk, xv, src, tgt)["out"]
+    total = np.zeros_like(full)
+    for h in range(H):
+        keep = np.zeros((E, 1))
+        keep[h * d:(h + 1) * d] = 1.0
+        ph = {"wq": 2.0 * params["wq"] * keep, "bq": 2.0 * params["bq"] * keep[:, 0],
+              "wk": params["wk"] * keep, "bk": params["bk"] * keep[:, 0],
+              "wv": params["wv"] * keep, "bv": params["bv"] * keep[:, 0],
+              "wo": params["wo"], "bo": np.zeros(E)}
+        total += _run(E, 1, ph, xq, xk, xv, src, tgt)["out"]
+    np.testing.assert_allclose(total + params["bo"], full, rtol=0, atol=1e-12)
+
+
+def test_edge_order_equivariance():
+    c = synth.gene(n=150, B=2, E=16, H=4, dtype="f32", max_deg=30)
+    base = oracle.case_forward(c, want_weights=True)
+    perm = np.random.default_rng(4).permutation(c.nnz0)
+    c2 = synth.Case(**{**c.__dict__, "src": c.src[perm], "tgt": c.tgt[perm]})
+    res = oracle.case_forward(c2, want_weights=True)
+    np.testing.assert_allclose(res["out"], base["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["weights"], base["weights"][:, perm], rtol=0, atol=1e-12)
+
+
+def test_rows_subset_matches_full():
+    c = synth.bipartite(L=50, S=400, B=3, E=32, H=4, lo=2, hi=80)
+    full = oracle.case_forward(c, want_weights=True)
+    rng = np.random.default_rng(8)
+    rows = np.stack([rng.integers(0, c.B, 40), rng.integers(0, c.L, 40)], axis=1)
+    sub = oracle.case_forward(c, rows=rows, want_weights=True)
+    assert (sub["out"] == full["out"][rows[:, 0], rows[:, 1]]).all()
+    tgt = full["tgt"]
+    for b, t in rows:
+        sel = tgt == t
+        assert (sub["weights"][b][sel] == full["weights"][b][sel]).all()
+
+
+# ---------------------------------------------------------------------------
+# constructor rules
+
+
+def test_prepare_edges_rules():
+    pe = oracle.prepare_edges
+    ok = ([0, 1], [1, 0])
+    with pytest.raises(oracle.OracleError) as e:
+        pe([], [], 2, 2, 4, 2)
+    assert e.value.code == "index_empty"
+    with pytest.raises(oracle.OracleError) as e:
+        pe([0, 1], [1], 2, 2, 4, 2)
+    assert e.value.code == "arg"
+    with pytest.raises(oracle.OracleError) as e:
+        pe([0, 2], [1, 0], 2, 2, 4, 2)
+    assert e.value.code == "index_range"
+    with pytest.raises(oracle.OracleError) as e:
+        pe([0, 1], [1, -1], 2, 2, 4, 2)
+    assert e.value.code == "index_range"
+    with pytest.raises(oracle.OracleError) as e:
+        pe([0, 1, 0], [1, 0, 1], 2, 2, 4, 2)
+    assert e.value.code == "index_duplicate"
+    for sizes in ((0, 2, 4, 2), (2, 0, 4, 2), (2, 2, 0, 2), (2, 2, 4, 0), (2, 2, 6, 4)):
+        with pytest.raises(oracle.OracleError) as e:
+            pe(*ok, *sizes)
+        assert e.value.code == "size"
+    with pytest.raises(oracle.OracleError) as e:
+        pe([0], [0], 2, 3, 4, 2, add_self_loops=True)
+    assert e.value.code == "self_loops"
+    with pytest.raises(oracle.OracleError):
+        pe({0, 1}, [1, 0], 2, 2, 4, 2)
+    with pytest.raises(oracle.OracleError):
+        pe([0.0, 1.0], [1, 0], 2, 2, 4, 2)
+    with pytest.raises(oracle.OracleError):
+        pe([[0, 1]], [[1, 0]], 2, 2, 4, 2)
+
+
+def test_self_loops_appended_after_pairs_without_duplicates():
+    s0 = np.array([2, 0, 3, 1])
+    t0 = np.array([2, 1, 0, 3])
+    s_keep, t_keep = s0.copy(), t0.copy()
+    src, tgt = oracle.prepare_edges(s0, t0, 5, 5, 4, 1, add_self_loops=True)
+    assert (s0 == s_keep).all() and (t0 == t_keep).all()          # not mutated
+    assert src.tolist() == [2, 0, 3, 1, 0, 1, 3, 4]
+    assert tgt.tolist() == [2, 1, 0, 3, 0, 1, 3, 4]
+    c = synth.complete()
+    src, _ = oracle.prepare_edges(c.src, c.tgt, 64, 64, 64, 4, add_self_loops=True)
+    assert src.shape[0] == 4096                                     # loops already there
+
+
+# ---------------------------------------------------------------------------
+# integer layout references
+
+
+def _csr_brute(src, tgt, L):
+    row_ptr = [0]
+    s_out, e_out = [], []
+    for t in range(L):
+        ent = sorted((int(s), e) for e, (s, tt) in enumerate(zip(src, tgt)) if tt == t)
+        s_out += [s for s, _ in ent]
+        e_out += [e for _, e in ent]
+        row_ptr.append(len(s_out))
+    return row_ptr, s_out, e_out
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_csr_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    L, S = int(rng.integers(1, 20)), int(rng.integers(1, 20))
+    src, tgt = synth.random_graph(rng, L, S, float(rng.uniform(0.05, 0.9)))
+    rp, cs, ce = oracle.csr(src, tgt, L)
+    brp, bcs, bce = _csr_brute(src, tgt, L)
+    assert rp.tolist() == brp and cs.tolist() == bcs and ce.tolist() == bce
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 7, 64])
+def test_work_split_brute_force(chunk):
+    rng = np.random.default_rng(chunk)
+    deg = rng.integers(0, 30, size=40)
+    deg[3] = 200
+    row_ptr = np.concatenate([[0], np.cumsum(deg)])
+    ws = oracle.work_split(row_ptr, chunk)
+    lens = ws["task_end"] - ws["task_begin"]
+    assert (lens <= chunk).all() and (np.diff(lens) <= 0).all()
+    covered = np.zeros(row_ptr[-1], int)
+    for t, b, e, s in zip(ws["task_target"], ws["task_begin"], ws["task_end"], ws["task_slot"]):
+        assert row_ptr[t] <= b <= e <= row_ptr[t + 1]
+        covered[b:e] += 1
+    assert (covered == 1).all()
+    n_pieces = np.bincount(ws["task_target"], minlength=40)
+    assert (n_pieces == np.maximum(1, -(-deg // chunk))).all()
+    # split targets own consecutive slots, numbered in ascending target order
+    slot = 0
+    for t, s0, n in zip(ws["split_target"], ws["split_slot0"], ws["split_count"]):
+        assert s0 == slot and n == n_pieces[t] and n > 1
+        slots = sorted(ws["task_slot"][ws["task_target"] == t].tolist())
+        assert slots == list(range(s0, s0 + n))
+        slot += n
+    assert ws["n_slots"] == slot
+    assert (ws["task_slot"][np.isin(ws["task_target"], ws["split_target"], invert=True)] == -1).all()
+    # ties in length keep ascending (target, piece) order
+    key = list(zip(-lens, ws["task_target"], ws["task_begin"]))
+    assert key == sorted(key)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must make some pin above fail
+
+
+MUTATIONS = {
+    "transposed_weight": ("acc += x[i] * w[o * E + i];", "acc += x[i] * w[i * E + o];"),
+    "no_sqrt_d": ("score[j] = dot / sqrt_d;", "score[j] = dot;"),
+    "dropped_bias": ("y[o] = acc + (b ? b[o] : 0.0);", "y[o] = acc;"),
+    "key_from_target": ("const double *kh = K + (b * S + src[into_t[first[t] + j]]) * E + h * d;",
+                        "const double *kh = K + (b * S + t % S) * E + h * d;"),
+    "value_wrong_head": ("V[(b * S + src[into_t[first[t] + j]]) * E + h * d + c]",
+                         "V[(b * S + src[into_t[first[t] + j]]) * E + c]"),
+    "no_normalise": ("w[j] = exp(score[j] - m) / den;", "w[j] = exp(score[j] - m);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
+    old, new = MUTATIONS[name]
+    text = open(oracle._SRC).read()
+    assert old in text, name
+    src_path = tmp_path / "mut.c"
+    src_path.write_text(text.replace(old, new))
+    lib_path = tmp_path / "mut.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", str(src_path),
+                    "-o", str(lib_path), "-lm"], check=True)
+    monkeypatch.setattr(oracle, "_lib", None)
+    monkeypatch.setattr(oracle, "_LIB", str(lib_path))
+    failures = 0
+    for seed in range(12):
+        try:
+            test_masked_dense_mha(seed)
+        except AssertionError:
+            failures += 1
+    try:
+        test_complete_graph_equals_dense_mha("normal")
+    except AssertionError:
+        failures += 1
+    monkeypatch.setattr(oracle, "_lib", None)
+    assert failures > 0, f"no pin caught mutation {name}"
