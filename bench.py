@@ -1,0 +1,193 @@
+"""Forward throughput of packed multi-head attention over live edges on one GPU.
+
+One step = one pma_forward over one batch: the q/k/v projections, the fused
+edge kernel (scores, online softmax, mix), the merge of split targets and
+out_proj, on the gene-regulatory-prior workload (n = 20,000 nodes, Zipf 1.5
+source hubs, log-normal in-degree of mean 10, B = 32, E = 64, H = 4, bf16
+tokens, fp32 softmax and accumulation). Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
+
+Prints one JSON line. ``value`` is edge-heads per second (nnz * H * B per
+forward); ``roofline`` rates the edge kernel, timed with HIP events on the
+forward's own stream, against MI355X's 8 TB/s HBM; ``cpu_baseline`` times the
+plain CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "edge-heads/s fwd (nnz·H·B per sec) + % HBM roofline, 20k-node gene graph"
+HBM_PEAK_GBS = 8000.0
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "edge_gene_traffic.json")
+
+
+def _workload(name: str):
+    from graph_sparse_head_amd import synth
+    return synth.make_config(name)
+
+
+def edge_kernel_bytes(B, L, nnz, E, s, weights=False, H=1, average=True):
+    """Algorithmic bytes of one edge-kernel launch: per sample, read each
+    target's query row and write its mixed row, and gather one key row and one
+    value row per live edge; plus the target-grouped edge index (row pointers
+    and one source id per edge). need_weights adds one fp32 weight per edge
+    (per head unless averaged) and the edge-order map."""
+    b = B * (L * E * s + nnz * 2 * E * s + L * E * s) + 4 * (L + 1) + 4 * nnz
+    if weights:
+        b += 4 * nnz + 4 * B * nnz * (1 if average else H)
+    return b
+
+
+def _traffic(cfg_name: str):
+    """HBM bytes per edge-kernel launch from committed rocprofv3 counters, if
+    they were taken for this kernel build and workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != cfg_name or t.get("kernel_sha") != _kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _kernel_sha():
+    import hashlib
+    p = os.path.join(ROOT, "graph_sparse_head_amd", "csrc", "edge.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_baseline(case, budget_s: float = 20.0):
+    """The oracle on a bounded sample: whole forwards for the first samples
+    of the batch, as many as fit the time budget (at least one)."""
+    import oracle
+    from graph_sparse_head_amd import synth
+
+    src, tgt = oracle.prepare_edges(case.src, case.tgt, case.L, case.S, case.E, case.H,
+                                    case.add_self_loops)
+    params = {k: oracle.widen(v, case.dtype) for k, v in case.params.items()}
+    xq = oracle.widen(case.xq[:1], case.dtype)
+    cores = oracle.num_threads(0)
+    t0 = time.perf_counter()
+    oracle.forward(1, case.L, case.S, case.E, case.H, xq, xq, xq, params, src, tgt)
+    one = time.perf_counter() - t0
+    nb = int(max(1, min(case.B, budget_s // max(one, 1e-3))))
+    if nb > 1:
+        xq = oracle.widen(case.xq[:nb], case.dtype)
+        t0 = time.perf_counter()
+        oracle.forward(nb, case.L, case.S, case.E, case.H, xq, xq, xq, params, src, tgt)
+        dt = time.perf_counter() - t0
+    else:
+        dt = one
+    eh = src.shape[0] * case.H * nb
+    return {"value": eh / dt, "unit": "edge-heads/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nb} of {case.B} samples, every target (whole forward, fp64), "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gene",
+                    choices=["tiny", "complete", "gene", "bipartite", "large"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without per-stage events (no roofline)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this path runs on a single GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import graph_sparse_head_amd as pma
+    from graph_sparse_head_amd import synth
+
+    case = _workload(args.config)
+    dev = synth.to_torch(case)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    plan = pma.pma_create(case.src, case.tgt, case.L, case.S, case.E, case.H,
+                          add_self_loops=case.add_self_loops, dtype=case.dtype)
+    create_ms = (time.perf_counter() - t0) * 1e3
+    nnz = plan.nnz
+    info = pma.pma_plan_info(plan)
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    out = torch.empty(case.B, case.L, case.E, dtype=tdt, device="cuda")
+    weights = None
+    if case.need_weights:
+        shape = (case.B, nnz) if case.average else (case.B, nnz, case.H)
+        weights = torch.empty(shape, dtype=torch.float32, device="cuda")
+
+    def step():
+        pma.pma_forward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"],
+                        dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"], out=out,
+                        weights=weights, need_weights=case.need_weights,
+                        average_attn_weights=case.average)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        pma.pma_profile(plan, True)
+        pma.pma_profile_read(plan)          # discard anything earlier
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    stages = pma.pma_profile_read(plan) if not args.no_profile else None
+    ms_per_step = total_ms / args.steps
+    edge_heads = nnz * case.H * case.B
+    value = edge_heads / (ms_per_step * 1e-3)
+
+    es = 2 if case.dtype == "bf16" else 4
+    res = {
+        "metric": METRIC, "value": value, "unit": "edge-heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": f"{case.name}: L={case.L} S={case.S} nnz={nnz} B={case.B} "
+                               f"E={case.E} H={case.H} {case.dtype}"
+                               f"{' need_weights' if case.need_weights else ''}",
+                   "batch": case.B, "nodes": case.L, "nnz": nnz, "embed_dim": case.E,
+                   "num_heads": case.H, "parallelism": "single GPU"},
+    }
+    if stages is not None:
+        edge_ms, edge_calls = stages["edge"]
+        edge_avg_s = edge_ms / max(edge_calls, 1) * 1e-3
+        nbytes = edge_kernel_bytes(case.B, case.L, nnz, case.E, es, case.need_weights, case.H,
+                                   case.average)
+        achieved = nbytes / edge_avg_s / 1e9
+        traffic = _traffic(args.config)
+        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                           "kernel": "edge_fast", "bytes_per_launch": nbytes,
+                           "avg_launch_us": edge_avg_s * 1e6}
+        res["stages_us"] = {k: (v[0] / max(v[1], 1)) * 1e3 for k, v in stages.items() if v[1]}
+    res["create_ms"] = create_ms
+    res["plan"] = {k: info[k] for k in ("n_tasks", "n_split", "chunk", "max_degree")}
+    pma.pma_destroy(plan)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+"""Packed multi-head attention over live edges on AMD MI355X (gfx950).
+
+A thin binding over ``libpma.so`` (declared in ``include/pma.h``): every
+function here has the C entry point's name and only marshals arguments; all
+of the computation runs in the library's HIP kernels. Device tensors are
+passed as raw pointers; the stream defaults to torch's current stream.
+
+There is no CPU fallback: when ``libpma.so`` is missing, the first call
+raises ``ImportError`` (build it with ``python -m graph_sparse_head_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "PmaError", "Plan", "pma_create", "pma_forward", "pma_destroy", "pma_nnz", "pma_edges",
+    "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
+    "pma_profile_read", "STATUS", "STAGES", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpma.so")
+_lib = None
+
+STATUS = {
+    0: "PMA_OK", 1: "PMA_E_NULL", 2: "PMA_E_SIZE", 3: "PMA_E_INDEX_EMPTY",
+    4: "PMA_E_INDEX_RANGE", 5: "PMA_E_INDEX_DUPLICATE", 6: "PMA_E_SELF_LOOPS",
+    7: "PMA_E_DTYPE", 8: "PMA_E_ARG", 9: "PMA_E_OOM", 10: "PMA_E_DEVICE",
+    11: "PMA_E_UNSUPPORTED",
+}
+STAGES = ("proj_in", "edge", "merge", "weights", "out")
+_DTYPES = {"f32": 0, "bf16": 1}
+
+
+class PmaError(RuntimeError):
+    """A non-zero pma_status; ``name`` is its enum name."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {message}")
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("query_features", ctypes.c_int64), ("key_features", ctypes.c_int64),
+                ("embed_dim", ctypes.c_int64), ("num_heads", ctypes.c_int64),
+                ("nnz", ctypes.c_int64), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("n_tasks", ctypes.c_int64), ("n_split", ctypes.c_int64),
+                ("n_slots", ctypes.c_int64), ("max_degree", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing; build it with "
+                          "`python -m graph_sparse_head_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    st = ctypes.c_int
+    sig = {
+        "pma_create": (st, [ctypes.POINTER(P), P, P, I64, I64, I64, I64, I64, I32, I32, P]),
+        "pma_forward": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P]),
+        "pma_destroy": (st, [P]),
+        "pma_nnz": (I64, [P]),
+        "pma_edges": (st, [P, P, P]),
+        "pma_last_error": (ctypes.c_char_p, []),
+        "pma_plan_info": (st, [P, ctypes.POINTER(_Info)]),
+        "pma_csr": (st, [P, P, P, P]),
+        "pma_work_split": (st, [P] + [P] * 7),
+        "pma_profile": (st, [P, I32]),
+        "pma_profile_read": (st, [P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PmaError(status, pma_last_error())
+
+
+def _host_i64(x, name: str) -> np.ndarray:
+    """Host int64 copy of an index argument (tensor, ndarray or sequence)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(x)
+    if a.ndim != 1:
+        raise PmaError(8, f"{name} must be 1-D")
+    if a.size and (a.dtype == np.bool_ or not np.issubdtype(a.dtype, np.integer)):
+        raise PmaError(8, f"{name} must hold integers")
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return ctypes.c_void_p(None)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """Owner of a ``pma_plan *``; release it with ``pma_destroy``."""
+
+    def __init__(self, handle: ctypes.c_void_p, dtype: str, L: int, S: int, E: int, H: int):
+        self.handle = handle
+        self.dtype, self.L, self.S, self.E, self.H = dtype, L, S, E, H
+
+    @property
+    def nnz(self) -> int:
+        return pma_nnz(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        pma_destroy(self)
+
+
+def pma_last_error() -> str:
+    return _load().pma_last_error().decode()
+
+
+def pma_create(source_index, target_index, query_features: int, key_features: int,
+               embed_dim: int, num_heads: int, add_self_loops: bool = False,
+               dtype: str = "f32", stream=None) -> Plan:
+    """Build a plan for one graph (see ``pma_create`` in include/pma.h)."""
+    lib = _load()
+    src = _host_i64(source_index, "source_index")
+    tgt = _host_i64(target_index, "target_index")
+    if src.shape[0] != tgt.shape[0]:
+        raise PmaError(8, "source_index and target_index differ in length")
+    if dtype not in _DTYPES:
+        raise PmaError(7, f"dtype must be one of {sorted(_DTYPES)}")
+    if not isinstance(add_self_loops, (bool, np.bool_)):
+        raise PmaError(8, "add_self_loops must be a bool")
+    h = ctypes.c_void_p()
+    st = lib.pma_create(ctypes.byref(h), src.ctypes.data, tgt.ctypes.data, src.shape[0],
+                        int(query_features), int(key_features), int(embed_dim), int(num_heads),
+                        int(bool(add_self_loops)), _DTYPES[dtype], _stream_ptr(stream))
+    _check(st)
+    return Plan(h, dtype, int(query_features), int(key_features), int(embed_dim), int(num_heads))
+
+
+def _dptr(t, name: str, dtype, shape_tail: Optional[Sequence[int]] = None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise PmaError(8, f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise PmaError(7, f"{name} has dtype {t.dtype}, the plan uses {dtype}")
+    if not t.is_contiguous():
+        raise PmaError(8, f"{name} must be contiguous")
+    if shape_tail is not None and tuple(t.shape[-len(shape_tail):]) != tuple(shape_tail):
+        raise PmaError(2, f"{name} has shape {tuple(t.shape)}, expected (..., "
+                          f"{', '.join(map(str, shape_tail))})")
+    return t.data_ptr()
+
+
+def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                out=None, weights=None, need_weights: bool = False,
+                average_attn_weights: bool = True, stream=None):
+    """One forward pass (see ``pma_forward`` in include/pma.h).
+
+    query (..., L, E), key / value (..., S, E) contiguous GPU tensors of the
+    plan's dtype with equal leading axes. ``out`` and ``weights`` may be given
+    (preallocated) or are allocated here. Returns (out, weights or None).
+    """
+    import torch
+    lib = _load()
+    tdt = torch.float32 if plan.dtype == "f32" else torch.bfloat16
+    L, S, E, H = plan.L, plan.S, plan.E, plan.H
+    if query.dim() < 2 or key.dim() < 2 or value.dim() < 2:
+        raise PmaError(2, "query, key and value need at least 2 dimensions")
+    lead = tuple(query.shape[:-2])
+    if tuple(key.shape[:-2]) != lead or tuple(value.shape[:-2]) != lead:
+        raise PmaError(2, "the batch axes of query, key and value differ")
+    B = int(np.prod(lead)) if lead else 1
+    qp = _dptr(query, "query", tdt, (L, E))
+    kp = _dptr(key, "key", tdt, (S, E))
+    vp = _dptr(value, "value", tdt, (S, E))
+    wps = [_dptr(w, n, tdt, (E, E)) for w, n in ((q_w, "q_w"), (k_w, "k_w"), (v_w, "v_w"),
+                                                  (o_w, "o_w"))]
+    bps = [_dptr(b, n, tdt, (E,)) for b, n in ((q_b, "q_b"), (k_b, "k_b"), (v_b, "v_b"),
+                                                (o_b, "o_b"))]
+    if out is None:
+        out = torch.empty(lead + (L, E), dtype=tdt, device=query.device)
+    op = _dptr(out, "out", tdt, (L, E))
+    want_w = need_weights or weights is not None
+    if want_w and weights is None:
+        nnz = pma_nnz(plan)
+        shape = lead + ((nnz,) if average_attn_weights else (nnz, H))
+        weights = torch.empty(shape, dtype=torch.float32, device=query.device)
+    wp = _dptr(weights, "weights", torch.float32) if want_w else None
+    st = lib.pma_forward(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1], wps[2],
+                         bps[2], wps[3], bps[3], op, wp, int(bool(average_attn_weights)),
+                         _stream_ptr(stream))
+    _check(st)
+    return out, (weights if want_w else None)
+
+
+def pma_destroy(plan: Plan) -> None:
+    if plan is None or plan.handle is None or not plan.handle.value:
+        return
+    _check(_load().pma_destroy(plan.handle))
+    plan.handle = ctypes.c_void_p()
+
+
+def pma_nnz(plan: Plan) -> int:
+    return int(_load().pma_nnz(plan.handle))
+
+
+def pma_edges(plan: Plan):
+    n = pma_nnz(plan)
+    src = np.empty(n, np.int64)
+    tgt = np.empty(n, np.int64)
+    _check(_load().pma_edges(plan.handle, src.ctypes.data, tgt.ctypes.data))
+    return src, tgt
+
+
+def pma_plan_info(plan: Plan) -> dict:
+    info = _Info()
+    _check(_load().pma_plan_info(plan.handle, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in _Info._fields_}
+
+
+def pma_csr(plan: Plan):
+    info = pma_plan_info(plan)
+    L, n = info["query_features"], info["nnz"]
+    row_ptr = np.empty(L + 1, np.int64)
+    src = np.empty(n, np.int64)
+    eid = np.empty(n, np.int64)
+    _check(_load().pma_csr(plan.handle, row_ptr.ctypes.data, src.ctypes.data, eid.ctypes.data))
+    return row_ptr, src, eid
+
+
+def pma_work_split(plan: Plan) -> dict:
+    info = pma_plan_info(plan)
+    nt, ns = info["n_tasks"], info["n_split"]
+    out = {k: np.empty(nt, np.int64) for k in ("task_target", "task_begin", "task_end",
+                                               "task_slot")}
+    out.update({k: np.empty(max(ns, 1), np.int64) for k in ("split_target", "split_slot0",
+                                                             "split_count")})
+    _check(_load().pma_work_split(plan.handle, *(out[k].ctypes.data for k in (
+        "task_target", "task_begin", "task_end", "task_slot", "split_target", "split_slot0",
+        "split_count"))))
+    for k in ("split_target", "split_slot0", "split_count"):
+        out[k] = out[k][:ns]
+    out["n_slots"] = info["n_slots"]
+    return out
+
+
+def pma_profile(plan: Plan, enable: bool) -> None:
+    _check(_load().pma_profile(plan.handle, int(bool(enable))))
+
+
+def pma_profile_read(plan: Plan) -> dict:
+    """Per stage: (summed milliseconds, launches timed) since the last read."""
+    ms = np.zeros(len(STAGES), np.float64)
+    calls = np.zeros(len(STAGES), np.int64)
+    _check(_load().pma_profile_read(plan.handle, ms.ctypes.data, calls.ctypes.data))
+    return {name: (float(ms[i]), int(calls[i])) for i, name in enumerate(STAGES)}

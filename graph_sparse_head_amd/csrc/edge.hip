@@ -1,0 +1,441 @@
+// Score, softmax and mix over the live edges (kpnn2 PackedMultiheadAttention
+// page, "Notes" steps 2-4): for target t, head h and sample b,
+//   score[e] = dot(q_h[t], k_h[s_e]) / sqrt(d) for the edges e into t,
+//   weight[e] = softmax of those scores over the edges into t only,
+//   mixed_h[t] = sum_e weight[e] v_h[s_e],
+// and a target without edges mixes to zeros (same page, paragraph after the
+// steps). The page states the result; how it is evaluated here is this
+// library's design:
+//   * no per-edge score array: a running maximum and running sum (online
+//     softmax) rescale the partial mix as edges stream past, evaluated in base
+//     2 (scores pre-multiplied by log2(e) / sqrt(d), weights from exp2);
+//   * one wavefront handles one piece of a target's edge list for a group of
+//     samples; each lane owns a 16-byte chunk of one sample's row, so a head
+//     spans LPH = d / CH adjacent lanes and its dot product is reduced with
+//     DPP lane swaps;
+//   * targets longer than the plan's chunk are split into pieces whose
+//     (max, sum, partial mix) are merged afterwards in a fixed order;
+//   * with need_weights the log2-domain scores are stored per CSR position
+//     and normalised once the final (max, sum) of each target is known.
+//
+// Workspace layouts (elements):
+//   qt[L][B][E], kv[S][2][B][E] (keys, then values, of one source),
+//   mixed[L][B][E], part_acc[slot][B][E], part_ml[slot][B][H][2],
+//   stat_ml[L][B][H][2], scores[nnz][B][H].
+#include <math.h>
+
+#include "pma_internal.h"
+
+namespace pma {
+namespace {
+
+struct EdgeK {
+    const int32_t *csr_src, *csr_tgt, *csr_eid;
+    const int32_t *task_target, *task_begin, *task_end, *task_slot;
+    const int32_t *split_target, *split_slot0, *split_count;
+    int64_t n_tasks, n_split;
+    int B, E, H, d;
+    int64_t nnz;
+    int passes;          // wavefronts per piece (sample groups)
+    float scale;         // log2(e) / sqrt(d)
+    const void *qt, *kv;
+    void *mixed;
+    float *part_acc, *part_ml, *stat_ml, *scores, *weights;
+    int average;
+};
+
+__device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ inline uint16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL> __device__ inline float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of G lanes; every lane of the group gets the
+// same bits (each step adds a lane to its partner, and fp addition commutes).
+template <int G> __device__ inline float group_sum(float x)
+{
+    if constexpr (G >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (G >= 16) x += dpp<0x140>(x); // row_mirror
+    if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+// CH elements of type T as floats, from one aligned load.
+template <typename T, int CH> struct Chunk {
+    float v[CH];
+    __device__ inline void load(const T *p)
+    {
+        if constexpr (sizeof(T) == 4) {
+            static_assert(CH == 4, "fp32 chunks are 16 bytes");
+            float4 f = *reinterpret_cast<const float4 *>(p);
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
+            static_assert(CH == 8, "bf16 chunks are 16 bytes");
+            uint4 u = *reinterpret_cast<const uint4 *>(p);
+            uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(w[i] << 16);
+                v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        }
+    }
+    __device__ inline void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) v[i] = 0.f;
+    }
+};
+
+template <typename T, int CH> __device__ inline void store_chunk(T *p, const float *v)
+{
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        uint4 u;
+        u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+        u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+        *reinterpret_cast<uint4 *>(p) = u;
+    }
+}
+
+// Fast path: d = CH * LPH with 16-byte chunks. U edges per step.
+template <typename T, int CH, int LPH, int U>
+__global__ void __launch_bounds__(256) edge_fast(EdgeK a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= a.n_tasks * a.passes)
+        return;
+    const int64_t task = unit / a.passes;
+    const int pass = (int)(unit - task * a.passes);
+    const int t = a.task_target[task];
+    const int beg = a.task_begin[task], end = a.task_end[task];
+    const int slot = a.task_slot[task];
+
+    const int B = a.B, E = a.E;
+    const int cpr = E / CH;                       // chunks per sample row
+    const int c = pass * 64 + lane;
+    const bool active = c < B * cpr;
+    const int b = active ? c / cpr : 0;
+    const int cr = c - b * cpr;
+    const int col = active ? cr * CH : 0;
+    const int h = active ? cr / LPH : 0;
+    const bool head_lead = (lane % LPH) == 0;
+
+    const T *qt = reinterpret_cast<const T *>(a.qt);
+    const T *kv = reinterpret_cast<const T *>(a.kv);
+    Chunk<T, CH> q;
+    if (active)
+        q.load(qt + ((int64_t)t * B + b) * E + col);
+    else
+        q.zero();
+#pragma unroll
+    for (int i = 0; i < CH; ++i) q.v[i] *= a.scale;
+
+    const int64_t row2 = (int64_t)2 * B * E;     // one source's keys + values
+    const int64_t voff = (int64_t)B * E;
+    const T *kvl = kv + (int64_t)b * E + col;
+
+    float m = -INFINITY, l = 0.f;
+    float acc[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc[i] = 0.f;
+
+    for (int p = beg; p < end; p += U) {
+        const int n = end - p < U ? end - p : U;
+        int s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) s[u] = a.csr_src[u < n ? p + u : p];
+        Chunk<T, CH> kk[U], vv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const T *base = kvl + (int64_t)s[u] * row2;
+            if (active) {
+                kk[u].load(base);
+                vv[u].load(base + voff);
+            } else {
+                kk[u].zero();
+                vv[u].zero();
+            }
+        }
+        float sc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) dot = fmaf(q.v[i], kk[u].v[i], dot);
+            dot = group_sum<LPH>(dot);
+            sc[u] = u < n ? dot : -INFINITY;
+        }
+        if (a.scores && active && head_lead) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (u < n)
+                    a.scores[(((int64_t)(p + u)) * B + b) * a.H + h] = sc[u];
+        }
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u]);
+        const float alpha = fast_exp2(m - mx);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float pe = fast_exp2(sc[u] - mx);
+            l += pe;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u].v[i], acc[i]);
+        }
+        m = mx;
+    }
+
+    if (!active)
+        return;
+    if (slot < 0) {
+        float out[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
+        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col, out);
+        if (a.stat_ml && head_lead) {
+            float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
+            st[0] = m;
+            st[1] = l;
+        }
+    } else {
+        float *pa = a.part_acc + ((int64_t)slot * B + b) * E + col;
+        *reinterpret_cast<float4 *>(pa) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if constexpr (CH == 8)
+            *reinterpret_cast<float4 *>(pa + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if (head_lead) {
+            float *pm = a.part_ml + (((int64_t)slot * B + b) * a.H + h) * 2;
+            pm[0] = m;
+            pm[1] = l;
+        }
+    }
+}
+
+// Any head size: one thread per (piece, sample, channel). Each thread forms
+// the full dot product of its head on every edge.
+template <typename T>
+__global__ void __launch_bounds__(256) edge_generic(EdgeK a)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int B = a.B, E = a.E, d = a.d;
+    const int64_t per_task = (int64_t)B * E;
+    const int64_t task = idx / per_task;
+    if (task >= a.n_tasks)
+        return;
+    const int rem = (int)(idx - task * per_task);
+    const int b = rem / E, col = rem - b * E;
+    const int h = col / d, c0 = h * d;
+    const int t = a.task_target[task];
+    const int beg = a.task_begin[task], end = a.task_end[task];
+    const int slot = a.task_slot[task];
+    const T *qt = reinterpret_cast<const T *>(a.qt) + ((int64_t)t * B + b) * E + c0;
+    const T *kv = reinterpret_cast<const T *>(a.kv);
+    const int64_t row2 = (int64_t)2 * B * E, voff = (int64_t)B * E;
+    auto ld = [](const T *p) -> float {
+        if constexpr (sizeof(T) == 2) return bf2f(*p); else return *p;
+    };
+    float m = -INFINITY, l = 0.f, acc = 0.f;
+    for (int p = beg; p < end; ++p) {
+        const T *kr = kv + (int64_t)a.csr_src[p] * row2 + (int64_t)b * E + c0;
+        float dot = 0.f;
+        for (int i = 0; i < d; ++i) dot = fmaf(ld(qt + i) * a.scale, ld(kr + i), dot);
+        if (a.scores && col == c0)
+            a.scores[((int64_t)p * B + b) * a.H + h] = dot;
+        const float mx = fmaxf(m, dot);
+        const float alpha = fast_exp2(m - mx), pe = fast_exp2(dot - mx);
+        l = l * alpha + pe;
+        acc = fmaf(pe, ld(kr + voff + (col - c0)), acc * alpha);
+        m = mx;
+    }
+    if (slot < 0) {
+        const float o = l > 0.f ? acc / l : 0.f;
+        T *dst = reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col;
+        if constexpr (sizeof(T) == 2) *dst = f2bf(o); else *dst = o;
+        if (a.stat_ml && col == c0) {
+            float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
+            st[0] = m;
+            st[1] = l;
+        }
+    } else {
+        a.part_acc[((int64_t)slot * B + b) * E + col] = acc;
+        if (col == c0) {
+            float *pm = a.part_ml + (((int64_t)slot * B + b) * a.H + h) * 2;
+            pm[0] = m;
+            pm[1] = l;
+        }
+    }
+}
+
+// Merge the pieces of each split target, in piece order.
+template <typename T>
+__global__ void __launch_bounds__(256) merge_kernel(EdgeK a)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int B = a.B, E = a.E;
+    const int64_t per = (int64_t)B * E;
+    const int64_t k = idx / per;
+    if (k >= a.n_split)
+        return;
+    const int rem = (int)(idx - k * per);
+    const int b = rem / E, col = rem - b * E, h = col / a.d;
+    const int t = a.split_target[k], s0 = a.split_slot0[k], n = a.split_count[k];
+    float M = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        M = fmaxf(M, a.part_ml[(((int64_t)(s0 + j) * B + b) * a.H + h) * 2]);
+    float l = 0.f, acc = 0.f;
+    for (int j = 0; j < n; ++j) {
+        const float *pm = a.part_ml + (((int64_t)(s0 + j) * B + b) * a.H + h) * 2;
+        const float w = fast_exp2(pm[0] - M);
+        l = fmaf(pm[1], w, l);
+        acc = fmaf(a.part_acc[((int64_t)(s0 + j) * B + b) * E + col], w, acc);
+    }
+    const float o = l > 0.f ? acc / l : 0.f;
+    T *dst = reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col;
+    if constexpr (sizeof(T) == 2) *dst = f2bf(o); else *dst = o;
+    if (a.stat_ml && col == h * a.d) {
+        float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
+        st[0] = M;
+        st[1] = l;
+    }
+}
+
+// need_weights: weight = exp2(score - max) / sum, written in edge order.
+__global__ void __launch_bounds__(256) weights_kernel(EdgeK a)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int B = a.B, H = a.H;
+    if (idx >= a.nnz * B)
+        return;
+    const int64_t p = idx / B;
+    const int b = (int)(idx - p * B);
+    const int t = a.csr_tgt[p];
+    const int64_t e = a.csr_eid[p];
+    const float *sc = a.scores + (p * B + b) * H;
+    const float *st = a.stat_ml + ((int64_t)t * B + b) * H * 2;
+    if (a.average) {
+        float sum = 0.f;
+        for (int h = 0; h < H; ++h) sum += fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1];
+        a.weights[(int64_t)b * a.nnz + e] = sum / (float)H;
+    } else {
+        float *w = a.weights + ((int64_t)b * a.nnz + e) * H;
+        for (int h = 0; h < H; ++h) w[h] = fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1];
+    }
+}
+
+EdgeK make_k(const EdgeArgs &x)
+{
+    EdgeK k;
+    const GraphDev *g = x.g;
+    k.csr_src = g->csr_src;
+    k.csr_tgt = g->csr_tgt;
+    k.csr_eid = g->csr_eid;
+    k.task_target = g->task_target;
+    k.task_begin = g->task_begin;
+    k.task_end = g->task_end;
+    k.task_slot = g->task_slot;
+    k.split_target = g->split_target;
+    k.split_slot0 = g->split_slot0;
+    k.split_count = g->split_count;
+    k.n_tasks = g->n_tasks;
+    k.n_split = g->n_split;
+    k.B = (int)x.B;
+    k.E = (int)x.E;
+    k.H = (int)x.H;
+    k.d = (int)(x.E / x.H);
+    k.nnz = x.nnz;
+    k.passes = 1;
+    k.scale = (float)(1.4426950408889634 / sqrt((double)k.d));
+    k.qt = x.qt;
+    k.kv = x.kv;
+    k.mixed = x.mixed;
+    k.part_acc = x.part_acc;
+    k.part_ml = x.part_ml;
+    k.stat_ml = x.stat_ml;
+    k.scores = x.scores;
+    k.weights = x.weights;
+    k.average = x.average;
+    return k;
+}
+
+template <typename T, int CH, int LPH>
+hipError_t run_fast(EdgeK k, hipStream_t s)
+{
+    const int64_t chunks = (int64_t)k.B * (k.E / CH);
+    k.passes = (int)((chunks + 63) / 64);
+    const int64_t units = k.n_tasks * k.passes;
+    edge_fast<T, CH, LPH, 4><<<(unsigned)((units + 3) / 4), 256, 0, s>>>(k);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_edge(EdgeK k, hipStream_t s)
+{
+    constexpr int CH = 16 / sizeof(T);
+    if (k.d % CH == 0) {
+        switch (k.d / CH) {
+        case 1: return run_fast<T, CH, 1>(k, s);
+        case 2: return run_fast<T, CH, 2>(k, s);
+        case 4: return run_fast<T, CH, 4>(k, s);
+        case 8: return run_fast<T, CH, 8>(k, s);
+        case 16: return run_fast<T, CH, 16>(k, s);
+        default: break;
+        }
+    }
+    const int64_t n = k.n_tasks * k.B * k.E;
+    edge_generic<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
+{
+    EdgeK k = make_k(x);
+    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, s) : dispatch_edge<float>(k, s);
+    return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+}
+
+pma_status launch_merge(const EdgeArgs &x, hipStream_t s)
+{
+    EdgeK k = make_k(x);
+    if (k.n_split == 0)
+        return PMA_OK;
+    const int64_t n = k.n_split * k.B * k.E;
+    if (x.dt == PMA_BF16)
+        merge_kernel<uint16_t><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
+    else
+        merge_kernel<float><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
+    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+}
+
+pma_status launch_weights(const EdgeArgs &x, hipStream_t s)
+{
+    EdgeK k = make_k(x);
+    const int64_t n = k.nnz * k.B;
+    weights_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
+    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+}
+
+}  // namespace pma

@@ -1,0 +1,460 @@
+// Device-side index build: edges grouped by target with sources ascending
+// (CSR by target), duplicate-pair detection, and the split of every target
+// into pieces of at most `chunk` edges.
+//
+// The softmax of the kpnn2 PackedMultiheadAttention page runs over "the edges
+// into each target" ("Notes", step 3); grouping the edges by target makes
+// each softmax one contiguous segment. Sorting each segment by source makes
+// the layout unique (pairs do not repeat), so the build is deterministic, and
+// puts a repeated pair next to its twin, which is how the constructor's
+// "must not repeat a (source, target) pair" rule is checked.
+//
+// Sorting is a stable least-significant-digit radix sort on 8-bit digits:
+// source digits first, then target digits. Each pass counts digits per tile,
+// scans the (digit, tile) counts, and scatters every tile in order, so equal
+// digits keep their relative order without atomics.
+#include <stdio.h>
+#include <string.h>
+
+#include "pma_internal.h"
+
+namespace pma {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kItems = 8;
+constexpr int kTile = kThreads * kItems;  // 2048 elements per tile
+
+#define PMA_TRY(call)                                                                  \
+    do {                                                                               \
+        hipError_t e_ = (call);                                                        \
+        if (e_ != hipSuccess) {                                                        \
+            snprintf(err, errlen, "%s failed: %s", #call, hipGetErrorString(e_));      \
+            st = (e_ == hipErrorOutOfMemory) ? PMA_E_OOM : PMA_E_DEVICE;               \
+            goto fail;                                                                 \
+        }                                                                              \
+    } while (0)
+
+// Exclusive prefix sum of one value per thread over a 256-thread block.
+__device__ int block_exclusive_scan(int v, int *lds, int *total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        lds[wid] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        int s = lds[w];
+        before += (w < wid) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
+// ---- device-wide exclusive scan ------------------------------------------
+
+__global__ void __launch_bounds__(kThreads) scan_tile_sums(const int32_t *in, int64_t n,
+                                                           int32_t *tile_sums)
+{
+    __shared__ int lds[kThreads / 64];
+    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j)
+        s += (base + j < n) ? in[base + j] : 0;
+    int tot;
+    block_exclusive_scan(s, lds, &tot);
+    if (threadIdx.x == 0)
+        tile_sums[blockIdx.x] = tot;
+}
+
+// One block scans all tile sums in place (exclusive), carrying across rounds.
+__global__ void __launch_bounds__(kThreads) scan_tile_offsets(int32_t *tile_sums, int64_t nt,
+                                                              int32_t *total)
+{
+    __shared__ int lds[kThreads / 64];
+    int carry = 0;
+    for (int64_t base = 0; base < nt; base += kThreads) {
+        int64_t i = base + threadIdx.x;
+        int v = (i < nt) ? tile_sums[i] : 0;
+        int tot;
+        int ex = block_exclusive_scan(v, lds, &tot);
+        if (i < nt)
+            tile_sums[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0 && total)
+        *total = carry;
+}
+
+__global__ void __launch_bounds__(kThreads) scan_apply(const int32_t *in, int32_t *out,
+                                                       int64_t n, const int32_t *tile_offs)
+{
+    __shared__ int lds[kThreads / 64];
+    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+    int v[kItems];
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        v[j] = (base + j < n) ? in[base + j] : 0;
+        s += v[j];
+    }
+    int tot;
+    int run = tile_offs[blockIdx.x] + block_exclusive_scan(s, lds, &tot);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        if (base + j < n)
+            out[base + j] = run;
+        run += v[j];
+    }
+}
+
+// ---- radix sort pass -------------------------------------------------------
+
+__global__ void __launch_bounds__(kThreads) radix_count(const int32_t *keys, const int32_t *perm,
+                                                        int64_t n, int shift, int32_t *counts,
+                                                        int64_t ntiles)
+{
+    __shared__ int hist[256];
+    hist[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        int64_t i = base + j * kThreads + threadIdx.x;
+        if (i < n)
+            atomicAdd(&hist[(keys[perm[i]] >> shift) & 255], 1);
+    }
+    __syncthreads();
+    counts[(int64_t)threadIdx.x * ntiles + blockIdx.x] = hist[threadIdx.x];
+}
+
+// Thread `d` walks the tile in order and moves the elements of digit d to
+// their scanned offsets: a stable scatter without atomics.
+__global__ void __launch_bounds__(kThreads) radix_scatter(const int32_t *keys,
+                                                          const int32_t *perm_in, int64_t n,
+                                                          int shift, const int32_t *offs,
+                                                          int64_t ntiles, int32_t *perm_out)
+{
+    __shared__ int32_t val[kTile];
+    __shared__ uint32_t dig4[kTile / 4];
+    uint8_t *dig = reinterpret_cast<uint8_t *>(dig4);
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+    const int cnt = (int)((n - base) < kTile ? (n - base) : kTile);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+        int i = j * kThreads + threadIdx.x;
+        if (i < cnt) {
+            int32_t v = perm_in[base + i];
+            val[i] = v;
+            dig[i] = (uint8_t)((keys[v] >> shift) & 255);
+        } else {
+            dig[i] = 0;
+        }
+    }
+    __syncthreads();
+    const uint32_t me = threadIdx.x;
+    int64_t pos = offs[(int64_t)me * ntiles + blockIdx.x];
+    const int words = (cnt + 3) >> 2;
+    for (int w = 0; w < words; ++w) {
+        uint32_t d4 = dig4[w];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int i = w * 4 + k;
+            if (((d4 >> (8 * k)) & 255) == me && i < cnt)
+                perm_out[pos++] = val[i];
+        }
+    }
+}
+
+__global__ void iota_kernel(int32_t *a, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        a[i] = (int32_t)i;
+}
+
+__global__ void degree_kernel(const int32_t *tgt, int64_t nnz, int32_t *deg)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nnz)
+        atomicAdd(&deg[tgt[i]], 1);
+}
+
+// CSR arrays from the sorted permutation, and the duplicate check: after the
+// sort a repeated (source, target) pair sits next to its twin.
+__global__ void csr_fill(const int32_t *perm, const int32_t *src, const int32_t *tgt, int64_t nnz,
+                         int32_t *csr_src, int32_t *csr_tgt, int32_t *csr_eid, int32_t *dup)
+{
+    int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= nnz)
+        return;
+    int32_t e = perm[p];
+    int32_t s = src[e], t = tgt[e];
+    csr_src[p] = s;
+    csr_tgt[p] = t;
+    csr_eid[p] = e;
+    if (p > 0) {
+        int32_t e0 = perm[p - 1];
+        if (src[e0] == s && tgt[e0] == t)
+            *dup = 1;
+    }
+}
+
+// Per target: number of pieces, partial slots and split flag.
+__global__ void split_count_kernel(const int32_t *deg, int64_t L, int chunk, int32_t *n_piece,
+                                   int32_t *n_slot, int32_t *is_split, int32_t *max_deg)
+{
+    int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= L)
+        return;
+    int32_t g = deg[t];
+    int32_t n = g > chunk ? (int32_t)((g + (int64_t)chunk - 1) / chunk) : 1;
+    n_piece[t] = n;
+    n_slot[t] = n > 1 ? n : 0;
+    is_split[t] = n > 1 ? 1 : 0;
+    atomicMax(max_deg, g);
+}
+
+__global__ void split_fill_kernel(const int32_t *row_ptr, int64_t L, int chunk,
+                                  const int32_t *piece_base, const int32_t *slot_base,
+                                  const int32_t *split_base, int32_t *t_target, int32_t *t_begin,
+                                  int32_t *t_end, int32_t *t_slot, int32_t *t_key,
+                                  int32_t *s_target, int32_t *s_slot0, int32_t *s_count)
+{
+    int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= L)
+        return;
+    const int64_t r0 = row_ptr[t], g = row_ptr[t + 1] - r0;
+    const int64_t n = g > chunk ? (g + chunk - 1) / chunk : 1;
+    const int64_t pb = piece_base[t];
+    for (int64_t j = 0; j < n; ++j) {
+        int64_t b = r0 + (j * g) / n, e = r0 + ((j + 1) * g) / n;
+        t_target[pb + j] = (int32_t)t;
+        t_begin[pb + j] = (int32_t)b;
+        t_end[pb + j] = (int32_t)e;
+        t_slot[pb + j] = n > 1 ? (int32_t)(slot_base[t] + j) : -1;
+        t_key[pb + j] = chunk - (int32_t)(e - b);  // ascending key = descending length
+    }
+    if (n > 1) {
+        const int32_t k = split_base[t];
+        s_target[k] = (int32_t)t;
+        s_slot0[k] = slot_base[t];
+        s_count[k] = (int32_t)n;
+    }
+}
+
+__global__ void gather4_kernel(const int32_t *perm, int64_t n, const int32_t *a0,
+                               const int32_t *a1, const int32_t *a2, const int32_t *a3,
+                               int32_t *o0, int32_t *o1, int32_t *o2, int32_t *o3)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n)
+        return;
+    int32_t p = perm[i];
+    o0[i] = a0[p];
+    o1[i] = a1[p];
+    o2[i] = a2[p];
+    o3[i] = a3[p];
+}
+
+inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+// Exclusive scan of n values (in -> out, may alias); writes the total to
+// *total_dev if not null. tmp holds ceil(n / kTile) ints.
+hipError_t scan_exclusive(const int32_t *in, int32_t *out, int64_t n, int32_t *total_dev,
+                          int32_t *tmp, hipStream_t s)
+{
+    if (n <= 0) {
+        if (total_dev)
+            return hipMemsetAsync(total_dev, 0, sizeof(int32_t), s);
+        return hipSuccess;
+    }
+    const int64_t nt = (n + kTile - 1) / kTile;
+    scan_tile_sums<<<(unsigned)nt, kThreads, 0, s>>>(in, n, tmp);
+    scan_tile_offsets<<<1, kThreads, 0, s>>>(tmp, nt, total_dev);
+    scan_apply<<<(unsigned)nt, kThreads, 0, s>>>(in, out, n, tmp);
+    return hipGetLastError();
+}
+
+int bits_for(int64_t maxval)
+{
+    int b = 0;
+    while (b < 63 && (int64_t(1) << b) <= maxval)
+        ++b;
+    return b;
+}
+
+// Stable sort of `perm` (n entries) by keys[perm[i]] over `bits` low bits.
+// Uses perm_tmp (n), counts (256 * tiles) and scan_tmp (>= 256 * tiles / kTile + 1).
+hipError_t radix_sort_perm(const int32_t *keys, int bits, int32_t *&perm, int32_t *&perm_tmp,
+                           int64_t n, int32_t *counts, int32_t *scan_tmp, hipStream_t s)
+{
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    for (int shift = 0; shift < bits; shift += 8) {
+        radix_count<<<(unsigned)ntiles, kThreads, 0, s>>>(keys, perm, n, shift, counts, ntiles);
+        hipError_t e = scan_exclusive(counts, counts, 256 * ntiles, nullptr, scan_tmp, s);
+        if (e != hipSuccess)
+            return e;
+        radix_scatter<<<(unsigned)ntiles, kThreads, 0, s>>>(keys, perm, n, shift, counts, ntiles,
+                                                            perm_tmp);
+        int32_t *t = perm;
+        perm = perm_tmp;
+        perm_tmp = t;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+void free_graph(GraphDev *g)
+{
+    int32_t **ptrs[] = {&g->row_ptr,    &g->csr_src,    &g->csr_tgt,     &g->csr_eid,
+                        &g->task_target, &g->task_begin, &g->task_end,    &g->task_slot,
+                        &g->split_target, &g->split_slot0, &g->split_count};
+    for (int32_t **p : ptrs) {
+        if (*p)
+            (void)hipFree(*p);
+        *p = nullptr;
+    }
+}
+
+pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, int64_t L,
+                       int64_t S, int chunk, hipStream_t stream, GraphDev *g, char *err,
+                       size_t errlen)
+{
+    pma_status st = PMA_OK;
+    int32_t *d_src = nullptr, *d_tgt = nullptr, *perm = nullptr, *perm_tmp = nullptr;
+    int32_t *counts = nullptr, *scan_tmp = nullptr, *deg = nullptr, *small = nullptr;
+    int32_t *n_piece = nullptr, *n_slot = nullptr, *is_split = nullptr;
+    int32_t *piece_base = nullptr, *slot_base = nullptr, *split_base = nullptr;
+    int32_t *t_target = nullptr, *t_begin = nullptr, *t_end = nullptr, *t_slot = nullptr,
+            *t_key = nullptr, *tperm = nullptr, *tperm_tmp = nullptr;
+    int32_t h_small[8] = {0};
+    const int64_t n_sort = nnz > L ? nnz : L;
+    const int64_t ntiles = (n_sort + kTile - 1) / kTile;
+    const int64_t count_len = 256 * ntiles;
+    const int64_t scan_len = (count_len > n_sort ? count_len : n_sort) / kTile + 2;
+    const size_t i4 = sizeof(int32_t);
+
+    // small[]: 0 dup flag, 1 n_tasks, 2 n_slots, 3 n_split, 4 max degree, 5 nnz total
+    PMA_TRY(hipMalloc(&d_src, nnz * i4));
+    PMA_TRY(hipMalloc(&d_tgt, nnz * i4));
+    PMA_TRY(hipMalloc(&perm, nnz * i4));
+    PMA_TRY(hipMalloc(&perm_tmp, nnz * i4));
+    PMA_TRY(hipMalloc(&counts, count_len * i4));
+    PMA_TRY(hipMalloc(&scan_tmp, scan_len * i4));
+    PMA_TRY(hipMalloc(&deg, L * i4));
+    PMA_TRY(hipMalloc(&small, 8 * i4));
+    PMA_TRY(hipMalloc(&g->row_ptr, (L + 1) * i4));
+    PMA_TRY(hipMalloc(&g->csr_src, nnz * i4));
+    PMA_TRY(hipMalloc(&g->csr_tgt, nnz * i4));
+    PMA_TRY(hipMalloc(&g->csr_eid, nnz * i4));
+    PMA_TRY(hipMalloc(&n_piece, L * i4));
+    PMA_TRY(hipMalloc(&n_slot, L * i4));
+    PMA_TRY(hipMalloc(&is_split, L * i4));
+    PMA_TRY(hipMalloc(&piece_base, L * i4));
+    PMA_TRY(hipMalloc(&slot_base, L * i4));
+    PMA_TRY(hipMalloc(&split_base, L * i4));
+
+    PMA_TRY(hipMemcpyAsync(d_src, h_src, nnz * i4, hipMemcpyHostToDevice, stream));
+    PMA_TRY(hipMemcpyAsync(d_tgt, h_tgt, nnz * i4, hipMemcpyHostToDevice, stream));
+    PMA_TRY(hipMemsetAsync(deg, 0, L * i4, stream));
+    PMA_TRY(hipMemsetAsync(small, 0, 8 * i4, stream));
+
+    // 1. sort edge ids by (target, source)
+    iota_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, nnz);
+    PMA_TRY(radix_sort_perm(d_src, bits_for(S - 1), perm, perm_tmp, nnz, counts, scan_tmp, stream));
+    PMA_TRY(radix_sort_perm(d_tgt, bits_for(L - 1), perm, perm_tmp, nnz, counts, scan_tmp, stream));
+    csr_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, d_src, d_tgt, nnz, g->csr_src,
+                                                     g->csr_tgt, g->csr_eid, small + 0);
+    // 2. row pointers
+    degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(d_tgt, nnz, deg);
+    PMA_TRY(scan_exclusive(deg, g->row_ptr, L, g->row_ptr + L, scan_tmp, stream));
+    // 3. pieces per target
+    split_count_kernel<<<grid_for(L, 256), 256, 0, stream>>>(deg, L, chunk, n_piece, n_slot,
+                                                             is_split, small + 4);
+    PMA_TRY(scan_exclusive(n_piece, piece_base, L, small + 1, scan_tmp, stream));
+    PMA_TRY(scan_exclusive(n_slot, slot_base, L, small + 2, scan_tmp, stream));
+    PMA_TRY(scan_exclusive(is_split, split_base, L, small + 3, scan_tmp, stream));
+    PMA_TRY(hipGetLastError());
+    PMA_TRY(hipMemcpyAsync(h_small, small, 8 * i4, hipMemcpyDeviceToHost, stream));
+    PMA_TRY(hipStreamSynchronize(stream));
+    if (h_small[0]) {
+        snprintf(err, errlen, "target_index/source_index repeat a (source, target) pair");
+        st = PMA_E_INDEX_DUPLICATE;
+        goto fail;
+    }
+    g->n_tasks = h_small[1];
+    g->n_slots = h_small[2];
+    g->n_split = h_small[3];
+    g->max_degree = h_small[4];
+    {
+        const int64_t nt = g->n_tasks, ns = g->n_split > 0 ? g->n_split : 1;
+        PMA_TRY(hipMalloc(&t_target, nt * i4));
+        PMA_TRY(hipMalloc(&t_begin, nt * i4));
+        PMA_TRY(hipMalloc(&t_end, nt * i4));
+        PMA_TRY(hipMalloc(&t_slot, nt * i4));
+        PMA_TRY(hipMalloc(&t_key, nt * i4));
+        PMA_TRY(hipMalloc(&tperm, nt * i4));
+        PMA_TRY(hipMalloc(&tperm_tmp, nt * i4));
+        PMA_TRY(hipMalloc(&g->task_target, nt * i4));
+        PMA_TRY(hipMalloc(&g->task_begin, nt * i4));
+        PMA_TRY(hipMalloc(&g->task_end, nt * i4));
+        PMA_TRY(hipMalloc(&g->task_slot, nt * i4));
+        PMA_TRY(hipMalloc(&g->split_target, ns * i4));
+        PMA_TRY(hipMalloc(&g->split_slot0, ns * i4));
+        PMA_TRY(hipMalloc(&g->split_count, ns * i4));
+        int32_t *sc = nullptr;
+        const int64_t ntt = (nt + kTile - 1) / kTile;
+        PMA_TRY(hipMalloc(&sc, 256 * ntt * i4));
+        split_fill_kernel<<<grid_for(L, 256), 256, 0, stream>>>(
+            g->row_ptr, L, chunk, piece_base, slot_base, split_base, t_target, t_begin, t_end,
+            t_slot, t_key, g->split_target, g->split_slot0, g->split_count);
+        iota_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(tperm, nt);
+        hipError_t e = radix_sort_perm(t_key, bits_for(chunk), tperm, tperm_tmp, nt, sc, scan_tmp,
+                                       stream);
+        if (e == hipSuccess) {
+            gather4_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(
+                tperm, nt, t_target, t_begin, t_end, t_slot, g->task_target, g->task_begin,
+                g->task_end, g->task_slot);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+        (void)hipFree(sc);
+        if (e != hipSuccess) {
+            snprintf(err, errlen, "work split: %s", hipGetErrorString(e));
+            st = PMA_E_DEVICE;
+            goto fail;
+        }
+    }
+    goto done;
+
+fail:
+    (void)hipStreamSynchronize(stream);
+    free_graph(g);
+done:
+    {
+        int32_t *tmps[] = {d_src,     d_tgt,     perm,       perm_tmp,   counts,   scan_tmp,
+                           deg,       small,     n_piece,    n_slot,     is_split, piece_base,
+                           slot_base, split_base, t_target,  t_begin,    t_end,    t_slot,
+                           t_key,     tperm,     tperm_tmp};
+        for (int32_t *p : tmps)
+            if (p)
+                (void)hipFree(p);
+    }
+    return st;
+}
+
+}  // namespace pma

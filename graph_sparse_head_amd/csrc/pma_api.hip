@@ -1,0 +1,480 @@
+// The C ABI: plan construction, the forward pass and inspection.
+// Argument checks follow the kpnn2 PackedMultiheadAttention page (constructor
+// parameter table, "Raises", forward "Raises"); all of them run on the host
+// before any HIP call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "pma_internal.h"
+
+#define PMA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pma_status fail(pma_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+constexpr int kChunk = 64;            // most edges one piece of a target covers
+constexpr int64_t kI32 = 2147483647;  // device edge indices are int32
+
+struct EventPair {
+    hipEvent_t a, b;
+    int stage;
+};
+
+}  // namespace
+
+struct pma_plan {
+    int64_t L = 0, S = 0, E = 0, H = 0, nnz = 0;
+    pma_dtype dtype = PMA_F32;
+    int chunk = kChunk;
+    std::vector<int64_t> h_src, h_tgt;
+    pma::GraphDev g;
+    // workspace, grown on demand
+    int64_t ws_B = 0;
+    bool ws_weights = false;
+    void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
+    float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
+    // profiling
+    bool prof = false;
+    std::vector<EventPair> pending;
+    std::vector<hipEvent_t> pool;
+    double ms[PMA_NUM_STAGES] = {0};
+    int64_t calls[PMA_NUM_STAGES] = {0};
+};
+
+namespace {
+
+void free_workspace(pma_plan *p)
+{
+    void *ptrs[] = {p->qt, p->kv, p->mixed, p->part_acc, p->part_ml, p->stat_ml, p->scores};
+    for (void *q : ptrs)
+        if (q)
+            (void)hipFree(q);
+    p->qt = p->kv = p->mixed = nullptr;
+    p->part_acc = p->part_ml = p->stat_ml = p->scores = nullptr;
+    p->ws_B = 0;
+    p->ws_weights = false;
+}
+
+pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
+{
+    if (B <= p->ws_B && (!weights || p->ws_weights))
+        return PMA_OK;
+    const int64_t nB = B > p->ws_B ? B : p->ws_B;
+    const bool nw = weights || p->ws_weights;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return fail(PMA_E_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    free_workspace(p);
+    const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
+    const size_t slots = (size_t)(p->g.n_slots > 0 ? p->g.n_slots : 1);
+    struct {
+        void **ptr;
+        size_t bytes;
+    } want[] = {
+        {&p->qt, (size_t)p->L * nB * p->E * es},
+        {&p->kv, (size_t)p->S * 2 * nB * p->E * es},
+        {&p->mixed, (size_t)p->L * nB * p->E * es},
+        {(void **)&p->part_acc, slots * nB * p->E * 4},
+        {(void **)&p->part_ml, slots * nB * p->H * 2 * 4},
+        {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
+        {(void **)&p->scores, nw ? (size_t)p->nnz * nB * p->H * 4 : 0},
+    };
+    for (auto &w : want) {
+        if (w.bytes == 0)
+            continue;
+        e = hipMalloc(w.ptr, w.bytes);
+        if (e != hipSuccess) {
+            free_workspace(p);
+            return fail(e == hipErrorOutOfMemory ? PMA_E_OOM : PMA_E_DEVICE,
+                        "workspace allocation of %zu bytes: %s", w.bytes, hipGetErrorString(e));
+        }
+    }
+    p->ws_B = nB;
+    p->ws_weights = nw;
+    return PMA_OK;
+}
+
+hipEvent_t take_event(pma_plan *p)
+{
+    if (!p->pool.empty()) {
+        hipEvent_t ev = p->pool.back();
+        p->pool.pop_back();
+        return ev;
+    }
+    hipEvent_t ev = nullptr;
+    if (hipEventCreate(&ev) != hipSuccess)
+        return nullptr;
+    return ev;
+}
+
+struct StageTimer {
+    pma_plan *p;
+    hipStream_t s;
+    EventPair cur{nullptr, nullptr, -1};
+    void begin(int stage)
+    {
+        if (!p->prof)
+            return;
+        cur.a = take_event(p);
+        cur.b = take_event(p);
+        cur.stage = stage;
+        if (cur.a)
+            (void)hipEventRecord(cur.a, s);
+    }
+    void end()
+    {
+        if (!p->prof || cur.stage < 0)
+            return;
+        if (cur.a && cur.b) {
+            (void)hipEventRecord(cur.b, s);
+            p->pending.push_back(cur);
+        }
+        cur.stage = -1;
+    }
+};
+
+}  // namespace
+
+PMA_API const char *pma_last_error(void) { return g_err; }
+
+PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
+                              const int64_t *target_index, int64_t nnz, int64_t query_features,
+                              int64_t key_features, int64_t embed_dim, int64_t num_heads,
+                              int add_self_loops, pma_dtype dtype, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!plan)
+        return fail(PMA_E_NULL, "plan is NULL");
+    *plan = nullptr;
+    if (dtype != PMA_F32 && dtype != PMA_BF16)
+        return fail(PMA_E_DTYPE, "dtype %d is not PMA_F32 or PMA_BF16", (int)dtype);
+    if (add_self_loops != 0 && add_self_loops != 1)
+        return fail(PMA_E_ARG, "add_self_loops must be 0 or 1");
+    const int64_t L = query_features, S = key_features, E = embed_dim, H = num_heads;
+    if (L <= 0 || S <= 0 || E <= 0 || H <= 0)
+        return fail(PMA_E_SIZE, "sizes must be positive (L=%lld S=%lld E=%lld H=%lld)",
+                    (long long)L, (long long)S, (long long)E, (long long)H);
+    if (E % H != 0)
+        return fail(PMA_E_SIZE, "embed_dim %lld is not divisible by num_heads %lld",
+                    (long long)E, (long long)H);
+    if (nnz < 1)
+        return fail(PMA_E_INDEX_EMPTY, "the indices are empty (nnz = %lld)", (long long)nnz);
+    if (!source_index || !target_index)
+        return fail(PMA_E_NULL, "source_index or target_index is NULL");
+    if (add_self_loops && L != S)
+        return fail(PMA_E_SELF_LOOPS,
+                    "add_self_loops needs query_features == key_features (%lld != %lld)",
+                    (long long)L, (long long)S);
+    for (int64_t i = 0; i < nnz; ++i) {
+        if (source_index[i] < 0 || source_index[i] >= S)
+            return fail(PMA_E_INDEX_RANGE, "source_index[%lld] = %lld outside [0, %lld)",
+                        (long long)i, (long long)source_index[i], (long long)S);
+        if (target_index[i] < 0 || target_index[i] >= L)
+            return fail(PMA_E_INDEX_RANGE, "target_index[%lld] = %lld outside [0, %lld)",
+                        (long long)i, (long long)target_index[i], (long long)L);
+    }
+    if (L > kI32 || S > kI32 || nnz > kI32)
+        return fail(PMA_E_UNSUPPORTED, "more than 2^31 - 1 edges or tokens");
+
+    pma_plan *p = new (std::nothrow) pma_plan;
+    if (!p)
+        return fail(PMA_E_OOM, "host allocation failed");
+    try {
+        p->h_src.assign(source_index, source_index + nnz);
+        p->h_tgt.assign(target_index, target_index + nnz);
+        if (add_self_loops) {
+            std::vector<char> has(L, 0);
+            for (int64_t i = 0; i < nnz; ++i)
+                if (source_index[i] == target_index[i])
+                    has[source_index[i]] = 1;
+            for (int64_t i = 0; i < L; ++i)
+                if (!has[i]) {
+                    p->h_src.push_back(i);
+                    p->h_tgt.push_back(i);
+                }
+        }
+    } catch (...) {
+        delete p;
+        return fail(PMA_E_OOM, "host allocation failed");
+    }
+    p->L = L;
+    p->S = S;
+    p->E = E;
+    p->H = H;
+    p->nnz = (int64_t)p->h_src.size();
+    p->dtype = dtype;
+    if (p->nnz + L > kI32) {
+        delete p;
+        return fail(PMA_E_UNSUPPORTED, "nnz + query_features exceeds 2^31 - 1");
+    }
+    std::vector<int32_t> s32, t32;
+    try {
+        s32.resize(p->nnz);
+        t32.resize(p->nnz);
+    } catch (...) {
+        delete p;
+        return fail(PMA_E_OOM, "host allocation failed");
+    }
+    for (int64_t i = 0; i < p->nnz; ++i) {
+        s32[i] = (int32_t)p->h_src[i];
+        t32[i] = (int32_t)p->h_tgt[i];
+    }
+    char err[256] = "";
+    pma_status st = pma::build_graph(s32.data(), t32.data(), p->nnz, L, S, p->chunk, stream,
+                                     &p->g, err, sizeof err);
+    if (st != PMA_OK) {
+        delete p;
+        return fail(st, "%s", err);
+    }
+    *plan = p;
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_destroy(pma_plan *plan)
+{
+    if (!plan)
+        return PMA_OK;
+    (void)hipDeviceSynchronize();
+    pma::free_graph(&plan->g);
+    free_workspace(plan);
+    for (auto &ev : plan->pending) {
+        (void)hipEventDestroy(ev.a);
+        (void)hipEventDestroy(ev.b);
+    }
+    for (hipEvent_t ev : plan->pool)
+        (void)hipEventDestroy(ev);
+    delete plan;
+    return PMA_OK;
+}
+
+PMA_API int64_t pma_nnz(const pma_plan *plan) { return plan ? plan->nnz : -1; }
+
+PMA_API pma_status pma_edges(const pma_plan *plan, int64_t *src_out, int64_t *tgt_out)
+{
+    if (!plan || !src_out || !tgt_out)
+        return fail(PMA_E_NULL, "NULL argument");
+    memcpy(src_out, plan->h_src.data(), plan->nnz * sizeof(int64_t));
+    memcpy(tgt_out, plan->h_tgt.data(), plan->nnz * sizeof(int64_t));
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_plan_info(const pma_plan *plan, pma_info *info)
+{
+    if (!plan || !info)
+        return fail(PMA_E_NULL, "NULL argument");
+    info->query_features = plan->L;
+    info->key_features = plan->S;
+    info->embed_dim = plan->E;
+    info->num_heads = plan->H;
+    info->nnz = plan->nnz;
+    info->dtype = (int32_t)plan->dtype;
+    info->chunk = plan->chunk;
+    info->n_tasks = plan->g.n_tasks;
+    info->n_split = plan->g.n_split;
+    info->n_slots = plan->g.n_slots;
+    info->max_degree = plan->g.max_degree;
+    return PMA_OK;
+}
+
+namespace {
+
+pma_status copy_widen(const int32_t *dev, int64_t n, int64_t *host)
+{
+    if (n <= 0)
+        return PMA_OK;
+    std::vector<int32_t> tmp(n);
+    hipError_t e = hipMemcpy(tmp.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(PMA_E_DEVICE, "hipMemcpy: %s", hipGetErrorString(e));
+    for (int64_t i = 0; i < n; ++i)
+        host[i] = tmp[i];
+    return PMA_OK;
+}
+
+}  // namespace
+
+PMA_API pma_status pma_csr(const pma_plan *plan, int64_t *row_ptr, int64_t *src, int64_t *eid)
+{
+    if (!plan || !row_ptr || !src || !eid)
+        return fail(PMA_E_NULL, "NULL argument");
+    pma_status st = copy_widen(plan->g.row_ptr, plan->L + 1, row_ptr);
+    if (st == PMA_OK)
+        st = copy_widen(plan->g.csr_src, plan->nnz, src);
+    if (st == PMA_OK)
+        st = copy_widen(plan->g.csr_eid, plan->nnz, eid);
+    return st;
+}
+
+PMA_API pma_status pma_work_split(const pma_plan *plan, int64_t *task_target,
+                                  int64_t *task_begin, int64_t *task_end, int64_t *task_slot,
+                                  int64_t *split_target, int64_t *split_slot0,
+                                  int64_t *split_count)
+{
+    if (!plan || !task_target || !task_begin || !task_end || !task_slot ||
+        (plan->g.n_split > 0 && (!split_target || !split_slot0 || !split_count)))
+        return fail(PMA_E_NULL, "NULL argument");
+    const pma::GraphDev &g = plan->g;
+    pma_status st = copy_widen(g.task_target, g.n_tasks, task_target);
+    if (st == PMA_OK) st = copy_widen(g.task_begin, g.n_tasks, task_begin);
+    if (st == PMA_OK) st = copy_widen(g.task_end, g.n_tasks, task_end);
+    if (st == PMA_OK) st = copy_widen(g.task_slot, g.n_tasks, task_slot);
+    if (st == PMA_OK) st = copy_widen(g.split_target, g.n_split, split_target);
+    if (st == PMA_OK) st = copy_widen(g.split_slot0, g.n_split, split_slot0);
+    if (st == PMA_OK) st = copy_widen(g.split_count, g.n_split, split_count);
+    return st;
+}
+
+PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                               const void *value, const void *q_w, const void *q_b,
+                               const void *k_w, const void *k_b, const void *v_w,
+                               const void *v_b, const void *o_w, const void *o_b, void *out,
+                               float *weights, int average_attn_weights, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!plan)
+        return fail(PMA_E_NULL, "plan is NULL");
+    if (batch <= 0)
+        return fail(PMA_E_SIZE, "batch must be positive (got %lld)", (long long)batch);
+    if (!query || !key || !value || !q_w || !k_w || !v_w || !o_w || !out)
+        return fail(PMA_E_NULL, "a token, weight or output pointer is NULL");
+    const int nb = (q_b != nullptr) + (k_b != nullptr) + (v_b != nullptr) + (o_b != nullptr);
+    if (nb != 0 && nb != 4)
+        return fail(PMA_E_ARG, "biases must be all given or all NULL");
+    if (average_attn_weights != 0 && average_attn_weights != 1)
+        return fail(PMA_E_ARG, "average_attn_weights must be 0 or 1");
+    pma_plan *p = plan;
+    const int64_t B = batch, L = p->L, S = p->S, E = p->E;
+    if ((L > S ? L : S) * B * 2 * E > ((int64_t)1 << 40))
+        return fail(PMA_E_UNSUPPORTED, "batch too large for one forward");
+    pma_status st = ensure_workspace(p, B, weights != nullptr, stream);
+    if (st != PMA_OK)
+        return st;
+    StageTimer tm{p, stream};
+    const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
+    char *kvc = static_cast<char *>(p->kv);
+
+    // Step 1: projections. qt[l][b][E], kv[s][keys | values][b][E].
+    tm.begin(PMA_STAGE_PROJ_IN);
+    const pma::ProjOut oq{q_w, q_b, p->qt, E, B * E};
+    const pma::ProjOut ok{k_w, k_b, kvc, E, 2 * B * E};
+    const pma::ProjOut ov{v_w, v_b, kvc + (size_t)B * E * es, E, 2 * B * E};
+    if (query == key && key == value && L == S) {
+        pma::ProjArgs a{query, B * L, L, B, 0, 3, {oq, ok, ov}};
+        st = pma::launch_proj(a, E, p->dtype, stream);
+    } else {
+        pma::ProjArgs aq{query, B * L, L, B, 0, 1, {oq}};
+        st = pma::launch_proj(aq, E, p->dtype, stream);
+        if (st == PMA_OK && key == value) {
+            pma::ProjArgs akv{key, B * S, S, B, 0, 2, {ok, ov}};
+            st = pma::launch_proj(akv, E, p->dtype, stream);
+        } else if (st == PMA_OK) {
+            pma::ProjArgs ak{key, B * S, S, B, 0, 1, {ok}};
+            st = pma::launch_proj(ak, E, p->dtype, stream);
+            if (st == PMA_OK) {
+                pma::ProjArgs av{value, B * S, S, B, 0, 1, {ov}};
+                st = pma::launch_proj(av, E, p->dtype, stream);
+            }
+        }
+    }
+    tm.end();
+    if (st != PMA_OK)
+        return fail(st, "projection launch failed: %s", hipGetErrorString(hipGetLastError()));
+
+    // Steps 2-4: scores, softmax and mix over the live edges.
+    pma::EdgeArgs ea;
+    ea.g = &p->g;
+    ea.B = B;
+    ea.L = L;
+    ea.S = S;
+    ea.E = E;
+    ea.H = p->H;
+    ea.nnz = p->nnz;
+    ea.dt = p->dtype;
+    ea.qt = p->qt;
+    ea.kv = p->kv;
+    ea.mixed = p->mixed;
+    ea.part_acc = p->part_acc;
+    ea.part_ml = p->part_ml;
+    ea.stat_ml = weights ? p->stat_ml : nullptr;
+    ea.scores = weights ? p->scores : nullptr;
+    ea.weights = weights;
+    ea.average = average_attn_weights;
+    tm.begin(PMA_STAGE_EDGE);
+    st = pma::launch_edge(ea, stream);
+    tm.end();
+    if (st == PMA_OK && p->g.n_split > 0) {
+        tm.begin(PMA_STAGE_MERGE);
+        st = pma::launch_merge(ea, stream);
+        tm.end();
+    }
+    if (st == PMA_OK && weights) {
+        tm.begin(PMA_STAGE_WEIGHTS);
+        st = pma::launch_weights(ea, stream);
+        tm.end();
+    }
+    if (st != PMA_OK)
+        return fail(st, "edge launch failed: %s", hipGetErrorString(hipGetLastError()));
+
+    // Step 5: join heads (already contiguous) and out_proj, back to (B, L, E).
+    tm.begin(PMA_STAGE_OUT);
+    const pma::ProjOut oo{o_w, o_b, out, L * E, E};
+    pma::ProjArgs ao{p->mixed, L * B, L, B, 1, 1, {oo}};
+    st = pma::launch_proj(ao, E, p->dtype, stream);
+    tm.end();
+    if (st != PMA_OK)
+        return fail(st, "out_proj launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_profile(pma_plan *plan, int enable)
+{
+    if (!plan)
+        return fail(PMA_E_NULL, "plan is NULL");
+    if (enable != 0 && enable != 1)
+        return fail(PMA_E_ARG, "enable must be 0 or 1");
+    plan->prof = enable != 0;
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_profile_read(pma_plan *plan, double *ms, int64_t *calls)
+{
+    if (!plan || !ms || !calls)
+        return fail(PMA_E_NULL, "NULL argument");
+    pma_status st = PMA_OK;
+    for (auto &ev : plan->pending) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(ev.b);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&t, ev.a, ev.b);
+        if (e != hipSuccess)
+            st = fail(PMA_E_DEVICE, "event timing: %s", hipGetErrorString(e));
+        else {
+            plan->ms[ev.stage] += t;
+            plan->calls[ev.stage] += 1;
+        }
+        plan->pool.push_back(ev.a);
+        plan->pool.push_back(ev.b);
+    }
+    plan->pending.clear();
+    for (int i = 0; i < PMA_NUM_STAGES; ++i) {
+        ms[i] = plan->ms[i];
+        calls[i] = plan->calls[i];
+        plan->ms[i] = 0;
+        plan->calls[i] = 0;
+    }
+    return st;
+}

@@ -1,0 +1,79 @@
+// Internal declarations shared by the library's HIP sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pma.h"
+
+namespace pma {
+
+// ---- index build (index_build.hip) ---------------------------------------
+
+// Device arrays describing one graph; owned by the plan.
+struct GraphDev {
+    int32_t *row_ptr = nullptr;   // L + 1
+    int32_t *csr_src = nullptr;   // nnz, per target ascending source
+    int32_t *csr_tgt = nullptr;   // nnz
+    int32_t *csr_eid = nullptr;   // nnz, position in the edge order
+    int32_t *task_target = nullptr, *task_begin = nullptr, *task_end = nullptr,
+            *task_slot = nullptr; // n_tasks each
+    int32_t *split_target = nullptr, *split_slot0 = nullptr, *split_count = nullptr; // n_split
+    int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0;
+};
+
+// Builds every array of GraphDev from host edges (already validated, loops
+// appended). Returns PMA_OK, PMA_E_INDEX_DUPLICATE, PMA_E_OOM or
+// PMA_E_DEVICE. Blocks on `stream` once. On failure frees what it made.
+pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, int64_t L,
+                       int64_t S, int chunk, hipStream_t stream, GraphDev *g, char *err,
+                       size_t errlen);
+void free_graph(GraphDev *g);
+
+// ---- projections (proj.hip) ----------------------------------------------
+
+// Output block of a projection launch: y = x W^T + b written at
+// dst + b_idx * sb + i_idx * si (elements), row of E channels.
+struct ProjOut {
+    const void *w;   // (E, E) [out][in]
+    const void *b;   // (E) or nullptr
+    void *dst;
+    int64_t sb, si;  // element strides of the sample and token index
+};
+
+// Input rows are contiguous rows of E elements at x. Row r decomposes as
+//   token_major == 0:  r = b * n + i   (batch-first tokens)
+//   token_major == 1:  r = i * B + b   (the library's target-major layout)
+struct ProjArgs {
+    const void *x;
+    int64_t rows;     // B * n
+    int64_t n, B;
+    int token_major;
+    int nblk;         // 1..3 output blocks
+    ProjOut out[3];
+};
+
+pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s);
+
+// ---- edge attention (edge.hip) -------------------------------------------
+
+struct EdgeArgs {
+    const GraphDev *g;
+    int64_t B, L, S, E, H, nnz;
+    pma_dtype dt;
+    const void *qt;     // [L][B][E]
+    const void *kv;     // [S][2][B][E]: keys then values of one source
+    void *mixed;        // [L][B][E]
+    float *part_acc;    // [slot][B][E]
+    float *part_ml;     // [slot][B][H][2]
+    float *stat_ml;     // [L][B][H][2] final (max, sum) or nullptr
+    float *scores;      // [B][nnz][H] log2-domain scores by CSR position, or nullptr
+    float *weights;     // caller's weights or nullptr
+    int average;
+};
+
+pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
+pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
+pma_status launch_weights(const EdgeArgs &a, hipStream_t s);
+
+}  // namespace pma

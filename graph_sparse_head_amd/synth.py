@@ -335,3 +335,27 @@ def make_config(name: str) -> Case:
     """The five named workloads at their full sizes."""
     return {"tiny": tiny, "complete": complete, "gene": gene, "bipartite": bipartite,
             "large": large}[name]()
+
+
+def to_torch(case: Case, device: str = "cuda") -> Dict[str, object]:
+    """Move a case's tokens and parameters to ``device`` as torch tensors of
+    its dtype (bf16 bit patterns are reinterpreted, not converted). Tensors
+    that were one array stay one tensor."""
+    import torch
+
+    def conv(a):
+        if a is None:
+            return None
+        if case.dtype == "bf16":
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+        return t.to(device)
+
+    out: Dict[str, object] = {}
+    out["xq"] = conv(case.xq)
+    out["xk"] = out["xq"] if case.xk is case.xq else conv(case.xk)
+    out["xv"] = out["xk"] if case.xv is case.xk else conv(case.xv)
+    for k, v in case.params.items():
+        out[k] = conv(v)
+    return out

@@ -1,0 +1,206 @@
+/*
+ * pma.h -- packed multi-head attention over live edges, for AMD MI355X (gfx950).
+ *
+ * Each target token attends only to its listed sources. For every live edge
+ * e from source s to target t, each head scores dot(q[t], k[s]) / sqrt(d);
+ * a softmax over the edges into each target turns the scores into weights;
+ * the weights mix the sources' values; the heads are joined and passed
+ * through out_proj. q, k, v and out come from four embed_dim x embed_dim
+ * projections shared by every node and edge. (kpnn2 0.3.0 API reference,
+ * PackedMultiheadAttention: class docstring and "Notes", steps 1-5.)
+ * Dense nn.MultiheadAttention is the special case of a complete graph
+ * (continuiti MultiHeadAttention page: MultiHead = Concat(head_i) W^O + b^O).
+ *
+ * Conventions shared by every call:
+ *   - L = query_features (tokens that attend), S = key_features (tokens
+ *     attended to), E = embed_dim, H = num_heads, d = E / H. Head h uses
+ *     channels [h d, (h + 1) d) of each projection.
+ *   - A projection is y = x W^T + b with W stored row-major [out][in]
+ *     (E x E) and b of length E, as nn.Linear stores it.
+ *   - Tokens are batch-first and contiguous: query (B, L, E), key and value
+ *     (B, S, E), out (B, L, E), where B is the product of the leading axes
+ *     (1 for unbatched input). The graph is shared by all B samples.
+ *   - Floating-point tensors (tokens, weights, biases, out) all have the
+ *     plan's dtype. Products and sums accumulate in fp32; with PMA_BF16 the
+ *     library keeps its q, k, v and mixed intermediates in bf16 (round to
+ *     nearest even) and rounds out the same way.
+ *   - Every call returns a status and never throws. On failure,
+ *     pma_last_error() holds a message for the calling thread.
+ */
+#ifndef PMA_H
+#define PMA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pma_plan pma_plan; /* opaque */
+
+typedef enum {
+    PMA_F32 = 0,  /* fp32 tokens and parameters */
+    PMA_BF16 = 1  /* bf16 tokens and parameters, fp32 softmax and accumulation */
+} pma_dtype;
+
+typedef enum {
+    PMA_OK = 0,
+    PMA_E_NULL = 1,            /* a required pointer is NULL */
+    PMA_E_SIZE = 2,            /* a size is not positive, or E % H != 0 */
+    PMA_E_INDEX_EMPTY = 3,     /* nnz < 1 */
+    PMA_E_INDEX_RANGE = 4,     /* a source >= S or a target >= L, or negative */
+    PMA_E_INDEX_DUPLICATE = 5, /* a (source, target) pair occurs twice */
+    PMA_E_SELF_LOOPS = 6,      /* add_self_loops with L != S */
+    PMA_E_DTYPE = 7,           /* not a pma_dtype value */
+    PMA_E_ARG = 8,             /* another invalid argument (flag, bias pointers) */
+    PMA_E_OOM = 9,             /* a host or device allocation failed */
+    PMA_E_DEVICE = 10,         /* a HIP call or kernel launch failed */
+    PMA_E_UNSUPPORTED = 11     /* sizes beyond the library's 32-bit edge indexing */
+} pma_status;
+
+/* Stages that pma_profile_read reports, in launch order. */
+typedef enum {
+    PMA_STAGE_PROJ_IN = 0, /* q / k / v projections */
+    PMA_STAGE_EDGE = 1,    /* fused score, online softmax and mix over the edges */
+    PMA_STAGE_MERGE = 2,   /* merge of targets split into several pieces */
+    PMA_STAGE_WEIGHTS = 3, /* need_weights: one weight per live edge */
+    PMA_STAGE_OUT = 4,     /* out_proj */
+    PMA_NUM_STAGES = 5
+} pma_stage;
+
+/*
+ * pma_create -- build a plan for one graph.
+ *
+ * Follows the kpnn2 PackedMultiheadAttention constructor (parameter table and
+ * "Raises"): source_index[i] is the key/value position that edge i reads from
+ * (0 <= source < key_features), target_index[i] the query position that
+ * attends along it (0 <= target < query_features); the two arrays pair up by
+ * position, hold nnz >= 1 entries and must not repeat a (source, target) pair.
+ * embed_dim must be divisible by num_heads. With add_self_loops != 0 (which
+ * needs query_features == key_features) every missing pair (i, i) is appended
+ * after the given pairs, in ascending i; existing loops are kept, not
+ * duplicated. The edge order so formed is the order of the per-edge weights
+ * pma_forward returns.
+ *
+ *   plan            out: the new plan, or NULL on failure.
+ *   source_index,   HOST arrays of nnz int64; read during the call and
+ *   target_index    copied, never modified or retained.
+ *   nnz             number of given pairs.
+ *   query_features  L; key_features S; embed_dim E; num_heads H (all > 0).
+ *   add_self_loops  0 or 1.
+ *   dtype           dtype of every floating-point tensor used with the plan.
+ *   stream          stream for the device-side index build. The call blocks
+ *                   until that build finishes (it reads back a duplicate flag).
+ *
+ * Errors: PMA_E_NULL, PMA_E_SIZE, PMA_E_INDEX_EMPTY, PMA_E_INDEX_RANGE,
+ * PMA_E_INDEX_DUPLICATE, PMA_E_SELF_LOOPS, PMA_E_DTYPE, PMA_E_ARG (flag not
+ * 0/1), PMA_E_UNSUPPORTED (nnz, L or S beyond 2^31 - 1 entries), PMA_E_OOM,
+ * PMA_E_DEVICE. On any error nothing stays allocated and *plan is NULL.
+ * Argument errors are detected before any HIP call.
+ */
+pma_status pma_create(pma_plan **plan, const int64_t *source_index, const int64_t *target_index,
+                      int64_t nnz, int64_t query_features, int64_t key_features,
+                      int64_t embed_dim, int64_t num_heads, int add_self_loops, pma_dtype dtype,
+                      hipStream_t stream);
+
+/*
+ * pma_forward -- one forward pass over a batch (kpnn2 page, forward, and
+ * "Notes" steps 1-5).
+ *
+ *   batch           B > 0: samples in the leading axes (1 if unbatched).
+ *   query           DEVICE (B, L, E); key, value DEVICE (B, S, E). They may
+ *                   be the same pointer (attention within one graph); the
+ *                   library then projects each token row once.
+ *   q_w, k_w, v_w,  DEVICE (E, E) [out][in] projection weights.
+ *   o_w
+ *   q_b, k_b, v_b,  DEVICE (E) biases: all four given, or all four NULL
+ *   o_b             (bias = False).
+ *   out             DEVICE (B, L, E). A target with no live edge gets exactly
+ *                   o_b (zeros without bias): it mixes to zeros, not NaN.
+ *   weights         NULL (need_weights = False), or DEVICE fp32 receiving the
+ *                   softmax weight of every live edge in edge order: (B, nnz)
+ *                   averaged over heads when average_attn_weights != 0, else
+ *                   (B, nnz, H). Weights into one target sum to 1.
+ *   stream          all work is enqueued on this stream; the call does not
+ *                   synchronise (except the first time a larger batch needs
+ *                   a larger workspace, which waits for the stream before
+ *                   reallocating).
+ *
+ * Tokens, parameters, out and weights are borrowed: they belong to the
+ * caller and must stay valid until the enqueued work completes. A plan must
+ * not run two forwards at once (they share the plan's workspace). Inputs
+ * must not overlap out or weights.
+ *
+ * Errors: PMA_E_NULL (plan, a token, a weight or out is NULL), PMA_E_SIZE
+ * (batch <= 0), PMA_E_ARG (biases neither all given nor all NULL, flag not
+ * 0/1), PMA_E_OOM, PMA_E_DEVICE.
+ */
+pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                       const void *value, const void *q_w, const void *q_b, const void *k_w,
+                       const void *k_b, const void *v_w, const void *v_b, const void *o_w,
+                       const void *o_b, void *out, float *weights, int average_attn_weights,
+                       hipStream_t stream);
+
+/* pma_destroy -- free the plan and everything it owns. NULL is a no-op.
+   Waits for the device before freeing. */
+pma_status pma_destroy(pma_plan *plan);
+
+/* Number of live edges, counting appended self-loops (kpnn2 page, attribute
+   nnz); -1 for a NULL plan. */
+int64_t pma_nnz(const pma_plan *plan);
+
+/* The final edge order (given pairs, then appended loops): HOST outputs of
+   pma_nnz(plan) int64 each. It is the order of the weights pma_forward
+   returns (kpnn2 page, forward "Returns"). */
+pma_status pma_edges(const pma_plan *plan, int64_t *src_out, int64_t *tgt_out);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *pma_last_error(void);
+
+/* ---- inspection (tests and tools) ------------------------------------- */
+
+typedef struct {
+    int64_t query_features, key_features, embed_dim, num_heads, nnz;
+    int32_t dtype;
+    int32_t chunk;      /* most edges one piece of a target covers */
+    int64_t n_tasks;    /* pieces: one per target, more for targets above chunk */
+    int64_t n_split;    /* targets split into more than one piece */
+    int64_t n_slots;    /* partial-result slots of the split targets */
+    int64_t max_degree; /* largest in-degree */
+} pma_info;
+
+pma_status pma_plan_info(const pma_plan *plan, pma_info *info);
+
+/* The plan's target-grouped edges, copied to HOST memory (blocking):
+   row_ptr (L + 1), src (nnz) and eid (nnz), where row_ptr[t] counts the edges
+   whose target is below t, each target's edges are ordered by ascending
+   source, and eid is the entry's position in the edge order. */
+pma_status pma_csr(const pma_plan *plan, int64_t *row_ptr, int64_t *src, int64_t *eid);
+
+/* The plan's pieces, copied to HOST memory (blocking): per piece its target,
+   first and end CSR position and partial slot (-1 when the target is one
+   piece), ordered by descending length, then target, then position; per
+   split target its id, first slot and piece count, in ascending target
+   order. A target of in-degree g has max(1, ceil(g / chunk)) pieces, piece j
+   covering positions row_ptr[t] + floor(j g / n) .. row_ptr[t] + floor((j+1) g / n). */
+pma_status pma_work_split(const pma_plan *plan, int64_t *task_target, int64_t *task_begin,
+                          int64_t *task_end, int64_t *task_slot, int64_t *split_target,
+                          int64_t *split_slot0, int64_t *split_count);
+
+/* ---- profiling -------------------------------------------------------- */
+
+/* Turn per-stage HIP-event timing on (1) or off (0). While on, each forward
+   records events around its stages on its own stream. */
+pma_status pma_profile(pma_plan *plan, int enable);
+
+/* Wait for the recorded events, then return per stage the summed elapsed
+   milliseconds (ms[PMA_NUM_STAGES]) and launches timed (calls[PMA_NUM_STAGES])
+   since the last read, and reset the sums. */
+pma_status pma_profile_read(pma_plan *plan, double *ms, int64_t *calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMA_H */

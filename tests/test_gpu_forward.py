@@ -1,0 +1,205 @@
+"""GPU forward parity with the oracle (fp32 <= 1e-5, bf16 <= 2e-2 max-abs-rel,
+the tolerance measured over the whole output / weights tensor), plus the
+exact special cases: a target without edges outputs exactly the out_proj bias,
+a target with one edge gives it weight exactly 1."""
+import numpy as np
+import pytest
+import torch
+
+import graph_sparse_head_amd as pma
+import oracle
+from graph_sparse_head_amd import synth
+from gpu_helpers import TOL, max_abs_rel, run, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_check(case, need_weights=True, average=True, lead=None):
+    print(f"[forward] {case.name} B={case.B} L={case.L} S={case.S} E={case.E} H={case.H} "
+          f"{case.dtype} w={need_weights} avg={average}", flush=True)
+    out, w, plan = run(case, need_weights=need_weights, average=average, lead=lead)
+    try:
+        ref = oracle.case_forward(case, want_weights=need_weights)
+        err = max_abs_rel(out, ref["out"])
+        assert err <= TOL[case.dtype], err
+        deg = np.bincount(ref["tgt"], minlength=case.L)
+        bo = case.params["bo"]
+        bo64 = np.zeros(case.E) if bo is None else oracle.widen(bo, case.dtype)
+        assert (out[:, deg == 0] == bo64).all()               # exactly the bias
+        if need_weights:
+            rw = ref["weights"]
+            rw = oracle.average_heads(rw) if average else rw
+            werr = max_abs_rel(w, rw)
+            assert werr <= TOL[case.dtype], werr
+            one = deg[ref["tgt"]] == 1
+            assert (w[:, one] == 1.0).all()                     # lone edge: weight 1
+            assert (w >= 0).all()
+        return out, w
+    finally:
+        pma.pma_destroy(plan)
+
+
+def test_tiny_averaged():
+    _full_check(synth.tiny(), need_weights=True, average=True)
+
+
+def test_tiny_per_head():
+    _full_check(synth.tiny(), need_weights=True, average=False)
+
+
+@pytest.mark.parametrize("bias", ["normal", "zero", "none"])
+def test_complete(bias):
+    _full_check(synth.complete(bias=bias), need_weights=True, average=True)
+
+
+def test_complete_without_weights():
+    _full_check(synth.complete(), need_weights=False)
+
+
+@pytest.mark.parametrize("loops", [True, False])
+def test_worked_example(loops):
+    c = synth.worked_example(add_self_loops=loops)
+    out, w = _full_check(c, need_weights=True, average=False)
+    assert w.shape == (2, 8 if loops else 4, 2)
+
+
+# fast paths (16-byte chunks) and the generic kernels, several tiles + ragged tails
+SMALL = [
+    # (name, seed, B, L, S, E, H, p, dtype, same_kv, same_qkv, loops)
+    ("f32_d16", 1, 3, 300, 300, 64, 4, 0.03, "f32", True, True, False),
+    ("f32_d16_bip", 2, 5, 70, 410, 128, 8, 0.05, "f32", True, False, False),
+    ("f32_d32_sep", 3, 2, 130, 170, 128, 4, 0.04, "f32", False, False, False),
+    ("f32_d4", 4, 4, 90, 90, 64, 16, 0.05, "f32", True, True, True),
+    ("f32_d8", 5, 3, 100, 100, 64, 8, 0.05, "f32", True, True, False),
+    ("bf16_d16", 6, 7, 333, 333, 64, 4, 0.03, "bf16", True, True, False),
+    ("bf16_d16_E128", 7, 3, 250, 250, 128, 8, 0.04, "bf16", True, True, True),
+    ("bf16_d32_sep", 8, 2, 120, 260, 128, 4, 0.05, "bf16", False, False, False),
+    ("bf16_d8", 9, 5, 100, 100, 64, 8, 0.05, "bf16", True, True, False),
+    ("bf16_d64", 10, 2, 80, 80, 128, 2, 0.08, "bf16", True, True, False),
+    ("f32_generic_d12", 11, 3, 60, 70, 48, 4, 0.1, "f32", True, False, False),
+    ("bf16_generic_d4", 12, 2, 50, 50, 16, 4, 0.1, "bf16", True, True, False),
+    ("f32_odd_E", 13, 2, 40, 40, 20, 5, 0.2, "f32", True, True, True),
+    ("f32_B1", 14, 1, 200, 200, 64, 4, 0.05, "f32", True, True, False),
+    ("bf16_B1", 15, 1, 200, 200, 64, 4, 0.05, "bf16", True, True, False),
+    ("f32_bigB", 16, 40, 60, 60, 64, 4, 0.1, "f32", True, True, False),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("avg", [True, False])
+def test_small_random(spec, avg):
+    name, seed, B, L, S, E, H, p, dt, same_kv, same_qkv, loops = spec
+    c = synth.random_case(seed, B, L, S, E, H, p, dtype=dt, same_kv=same_kv, same_qkv=same_qkv,
+                          add_self_loops=loops, name=name)
+    _full_check(c, need_weights=True, average=avg)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_no_bias_no_weights(dt):
+    c = synth.random_case(21, 3, 150, 150, 64, 4, 0.05, dtype=dt, bias="none", name="nobias")
+    _full_check(c, need_weights=False)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_leading_axes(dt):
+    c = synth.random_case(22, 6, 100, 100, 64, 4, 0.05, dtype=dt, name="lead")
+    _full_check(c, need_weights=True, average=False, lead=(2, 3))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("deg", [65, 300, 1500])
+def test_split_targets(dt, deg):
+    """Targets above the plan's chunk are split into pieces and merged."""
+    rng = np.random.default_rng(deg)
+    L, S, B, E, H = 40, 2000, 3, 64, 4
+    src, tgt = [], []
+    for t in range(L):
+        d = deg if t % 3 == 0 else int(rng.integers(0, 70))
+        s = rng.choice(S, size=d, replace=False)
+        src += s.tolist()
+        tgt += [t] * d
+    c = synth.random_case(30, B, L, S, E, H, 0.0, dtype=dt, name=f"split{deg}")
+    c.src, c.tgt = np.array(src, np.int64), np.array(tgt, np.int64)
+    perm = rng.permutation(c.src.shape[0])
+    c.src, c.tgt = c.src[perm], c.tgt[perm]
+    _full_check(c, need_weights=True, average=False)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_deterministic(dt):
+    c = synth.random_case(40, 4, 300, 300, 64, 4, 0.05, dtype=dt, name="det")
+    out1, w1, plan = run(c, need_weights=True, average=False)
+    try:
+        out2, w2, _ = run(c, plan=plan, need_weights=True, average=False)
+        assert (out1 == out2).all() and (w1 == w2).all()
+    finally:
+        pma.pma_destroy(plan)
+
+
+def test_plan_reuse_growing_batch():
+    """One plan, a small batch then a larger one (the workspace grows)."""
+    base = synth.random_case(41, 2, 120, 120, 64, 4, 0.06, dtype="f32", name="grow")
+    big = synth.random_case(41, 9, 120, 120, 64, 4, 0.06, dtype="f32", name="grow")
+    big.src, big.tgt = base.src, base.tgt
+    out, _, plan = run(base, need_weights=False)
+    try:
+        assert max_abs_rel(out, oracle.case_forward(base)["out"]) <= TOL["f32"]
+        out, w, _ = run(big, plan=plan, need_weights=True, average=True)
+        ref = oracle.case_forward(big, want_weights=True)
+        assert max_abs_rel(out, ref["out"]) <= TOL["f32"]
+        assert max_abs_rel(w, oracle.average_heads(ref["weights"])) <= TOL["f32"]
+    finally:
+        pma.pma_destroy(plan)
+
+
+def test_forward_rejects():
+    c = synth.tiny()
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H)
+    dev = synth.to_torch(c)
+    try:
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_forward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"],
+                            dev["wk"], None, dev["wv"], dev["bv"], dev["wo"], dev["bo"])
+        assert e.value.name == "PMA_E_ARG"
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_forward(plan, dev["xq"].double(), dev["xk"], dev["xv"], dev["wq"], dev["bq"],
+                            dev["wk"], dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"])
+        assert e.value.name == "PMA_E_DTYPE"
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_forward(plan, dev["xq"][:, :5].contiguous(), dev["xk"], dev["xv"], dev["wq"], dev["bq"],
+                            dev["wk"], dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"])
+        assert e.value.name == "PMA_E_SIZE"
+    finally:
+        pma.pma_destroy(plan)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows checked against the oracle
+
+
+@pytest.mark.parametrize("name", ["gene", "bipartite", "large"])
+def test_full_size_sampled(name):
+    c = synth.make_config(name)
+    print(f"[forward] full {name} nnz0={c.nnz0}", flush=True)
+    out, w, plan = run(c)
+    try:
+        src, tgt = pma.pma_edges(plan)
+        rows = sample_rows(c, tgt)
+        ref = oracle.case_forward(c, rows=rows, want_weights=c.need_weights)
+        got = out[rows[:, 0], rows[:, 1]]
+        err = max_abs_rel(got, ref["out"])
+        assert err <= TOL[c.dtype], err
+        deg = np.bincount(tgt, minlength=c.L)
+        bo = oracle.widen(c.params["bo"], c.dtype)
+        assert (out[:, deg == 0] == bo).all()
+        if c.need_weights:
+            rw = oracle.average_heads(ref["weights"])
+            have = ~np.isnan(rw)
+            werr = max_abs_rel(w[have], rw[have])
+            assert werr <= TOL[c.dtype], werr
+            # every target's weights sum to 1 (or 0 without edges), at every sample
+            sums = np.zeros((c.B, c.L))
+            np.add.at(sums, (slice(None), tgt), w)
+            assert np.abs(sums[:, deg > 0] - 1).max() <= 1e-4
+    finally:
+        pma.pma_destroy(plan)
