@@ -75,30 +75,25 @@ template <int G> __device__ inline float group_sum(float x)
     return x;
 }
 
-// CH elements of type T as floats, from one aligned load.
+// CH elements of type T in one 16-byte word, widened to fp32 on use.
 template <typename T, int CH> struct Chunk {
-    float v[CH];
-    __device__ inline void load(const T *p)
+    uint4 u;
+    __device__ inline void load(const T *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ inline void zero() { u = make_uint4(0, 0, 0, 0); }
+    __device__ inline uint32_t word(int k) const
+    {
+        return k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
+    }
+    __device__ inline float operator[](int i) const
     {
         if constexpr (sizeof(T) == 4) {
             static_assert(CH == 4, "fp32 chunks are 16 bytes");
-            float4 f = *reinterpret_cast<const float4 *>(p);
-            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+            return __uint_as_float(word(i));
         } else {
             static_assert(CH == 8, "bf16 chunks are 16 bytes");
-            uint4 u = *reinterpret_cast<const uint4 *>(p);
-            uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = __uint_as_float(w[i] << 16);
-                v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-            }
+            const uint32_t w = word(i >> 1);
+            return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
         }
-    }
-    __device__ inline void zero()
-    {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) v[i] = 0.f;
     }
 };
 
@@ -142,13 +137,16 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
 
     const T *qt = reinterpret_cast<const T *>(a.qt);
     const T *kv = reinterpret_cast<const T *>(a.kv);
-    Chunk<T, CH> q;
-    if (active)
-        q.load(qt + ((int64_t)t * B + b) * E + col);
-    else
-        q.zero();
+    float q[CH];
+    {
+        Chunk<T, CH> qc;
+        if (active)
+            qc.load(qt + ((int64_t)t * B + b) * E + col);
+        else
+            qc.zero();
 #pragma unroll
-    for (int i = 0; i < CH; ++i) q.v[i] *= a.scale;
+        for (int i = 0; i < CH; ++i) q[i] = qc[i] * a.scale;
+    }
 
     const int64_t row2 = (int64_t)2 * B * E;     // one source's keys + values
     const int64_t voff = (int64_t)B * E;
@@ -181,7 +179,7 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
         for (int u = 0; u < U; ++u) {
             float dot = 0.f;
 #pragma unroll
-            for (int i = 0; i < CH; ++i) dot = fmaf(q.v[i], kk[u].v[i], dot);
+            for (int i = 0; i < CH; ++i) dot = fmaf(q[i], kk[u][i], dot);
             dot = group_sum<LPH>(dot);
             sc[u] = u < n ? dot : -INFINITY;
         }
@@ -203,7 +201,7 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
             const float pe = fast_exp2(sc[u] - mx);
             l += pe;
 #pragma unroll
-            for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u].v[i], acc[i]);
+            for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u][i], acc[i]);
         }
         m = mx;
     }
@@ -288,9 +286,60 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
     }
 }
 
-// Merge the pieces of each split target, in piece order.
+// Merge the pieces of each split target, in piece order. Same lane layout
+// as edge_fast: one wavefront per (split target, sample group).
+template <typename T, int CH, int LPH>
+__global__ void __launch_bounds__(256) merge_fast(EdgeK a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= a.n_split * a.passes)
+        return;
+    const int64_t k = unit / a.passes;
+    const int pass = (int)(unit - k * a.passes);
+    const int B = a.B, E = a.E, H = a.H;
+    const int cpr = E / CH;
+    const int c = pass * 64 + lane;
+    if (c >= B * cpr)
+        return;
+    const int b = c / cpr, cr = c - b * cpr, col = cr * CH, h = cr / LPH;
+    const int t = a.split_target[k], s0 = a.split_slot0[k], n = a.split_count[k];
+    float M = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        M = fmaxf(M, a.part_ml[(((int64_t)(s0 + j) * B + b) * H + h) * 2]);
+    float l = 0.f, acc[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc[i] = 0.f;
+    for (int j = 0; j < n; ++j) {
+        const float2 ml = *reinterpret_cast<const float2 *>(
+            a.part_ml + (((int64_t)(s0 + j) * B + b) * H + h) * 2);
+        const float w = fast_exp2(ml.x - M);
+        l = fmaf(ml.y, w, l);
+        const float4 *pa = reinterpret_cast<const float4 *>(
+            a.part_acc + ((int64_t)(s0 + j) * B + b) * E + col);
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) {
+            const float4 v = pa[q];
+            acc[4 * q + 0] = fmaf(v.x, w, acc[4 * q + 0]);
+            acc[4 * q + 1] = fmaf(v.y, w, acc[4 * q + 1]);
+            acc[4 * q + 2] = fmaf(v.z, w, acc[4 * q + 2]);
+            acc[4 * q + 3] = fmaf(v.w, w, acc[4 * q + 3]);
+        }
+    }
+    float out[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
+    store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col, out);
+    if (a.stat_ml && (lane % LPH) == 0) {
+        float *st = a.stat_ml + (((int64_t)t * B + b) * H + h) * 2;
+        st[0] = M;
+        st[1] = l;
+    }
+}
+
+// Any head size: one thread per (split target, sample, channel).
 template <typename T>
-__global__ void __launch_bounds__(256) merge_kernel(EdgeK a)
+__global__ void __launch_bounds__(256) merge_generic(EdgeK a)
 {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int B = a.B, E = a.E;
@@ -408,6 +457,35 @@ hipError_t dispatch_edge(EdgeK k, hipStream_t s)
     return hipGetLastError();
 }
 
+template <typename T, int CH, int LPH>
+hipError_t run_merge(EdgeK k, hipStream_t s)
+{
+    const int64_t chunks = (int64_t)k.B * (k.E / CH);
+    k.passes = (int)((chunks + 63) / 64);
+    const int64_t units = k.n_split * k.passes;
+    merge_fast<T, CH, LPH><<<(unsigned)((units + 3) / 4), 256, 0, s>>>(k);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_merge(EdgeK k, hipStream_t s)
+{
+    constexpr int CH = 16 / sizeof(T);
+    if (k.d % CH == 0) {
+        switch (k.d / CH) {
+        case 1: return run_merge<T, CH, 1>(k, s);
+        case 2: return run_merge<T, CH, 2>(k, s);
+        case 4: return run_merge<T, CH, 4>(k, s);
+        case 8: return run_merge<T, CH, 8>(k, s);
+        case 16: return run_merge<T, CH, 16>(k, s);
+        default: break;
+        }
+    }
+    const int64_t n = k.n_split * k.B * k.E;
+    merge_generic<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
@@ -422,12 +500,8 @@ pma_status launch_merge(const EdgeArgs &x, hipStream_t s)
     EdgeK k = make_k(x);
     if (k.n_split == 0)
         return PMA_OK;
-    const int64_t n = k.n_split * k.B * k.E;
-    if (x.dt == PMA_BF16)
-        merge_kernel<uint16_t><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
-    else
-        merge_kernel<float><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
-    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+    hipError_t e = x.dt == PMA_BF16 ? dispatch_merge<uint16_t>(k, s) : dispatch_merge<float>(k, s);
+    return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
 pma_status launch_weights(const EdgeArgs &x, hipStream_t s)

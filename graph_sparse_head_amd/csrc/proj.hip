@@ -52,18 +52,28 @@ __device__ inline int64_t out_offset(const ProjArgs &a, const ProjOut &o, uint32
     return (int64_t)b * o.sb + (int64_t)i * o.si;
 }
 
-// One wave computes RG x 16 token rows for every output channel of every block.
+// One wave computes RG x 16 token rows for every output channel of every
+// block. Each block's tile goes through LDS so that the stores are whole
+// 16-byte chunks of whole rows (the destination rows of consecutive tokens
+// are far apart in the q / k / v layouts).
 template <typename T, int K, int RG>
 __global__ void __launch_bounds__(256) proj_mfma(ProjArgs a)
 {
     constexpr int NKS = K / Elem<T>::kStep;
+    constexpr int E = K;
+    constexpr int ROWS = RG * 16;
+    constexpr int PITCH = E * (int)sizeof(T) + 16;       // bytes per staged row
+    constexpr int CPR = E * (int)sizeof(T) / 16;         // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;                        // rows stored per instruction
+    __shared__ __attribute__((aligned(16))) char stage_all[4][ROWS * PITCH];
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t row0 = wave * (RG * 16);
+    const int wid = threadIdx.x >> 6;
+    char *stage = stage_all[wid];
+    const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
+    const int64_t row0 = wave * ROWS;
     if (row0 >= a.rows)
         return;
     const int lr = lane & 15, lg = lane >> 4;
-    const int E = K;
 
     // Token-row fragments: row (row0 + rg*16 + lr), k = ks*kStep + lg*kVec ..
     uint4 xf[RG][NKS];
@@ -84,13 +94,6 @@ __global__ void __launch_bounds__(256) proj_mfma(ProjArgs a)
         const ProjOut &o = a.out[blk];
         const T *W = reinterpret_cast<const T *>(o.w);
         const T *bias = reinterpret_cast<const T *>(o.b);
-        T *dst = reinterpret_cast<T *>(o.dst);
-        int64_t roff[RG];
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            const int64_t r = row0 + rg * 16 + lr;
-            roff[rg] = r < a.rows ? out_offset(a, o, (uint32_t)r) : 0;
-        }
         for (int nt = 0; nt < E / 16; ++nt) {
             uint4 wf[NKS];
             const T *wr = W + (int64_t)(nt * 16 + lr) * E + lg * Elem<T>::kVec;
@@ -132,22 +135,37 @@ __global__ void __launch_bounds__(256) proj_mfma(ProjArgs a)
             }
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
-                const int64_t r = row0 + rg * 16 + lr;
-                if (r >= a.rows)
-                    continue;
-                T *d = dst + roff[rg] + n;
+                char *d = stage + (rg * 16 + lr) * PITCH + n * (int)sizeof(T);
                 if constexpr (sizeof(T) == 2) {
                     uint2 pk;
                     pk.x = (uint32_t)f2bf(acc[rg][0] + bv[0]) | ((uint32_t)f2bf(acc[rg][1] + bv[1]) << 16);
                     pk.y = (uint32_t)f2bf(acc[rg][2] + bv[2]) | ((uint32_t)f2bf(acc[rg][3] + bv[3]) << 16);
                     *reinterpret_cast<uint2 *>(d) = pk;
                 } else {
-                    float4 v = make_float4(acc[rg][0] + bv[0], acc[rg][1] + bv[1], acc[rg][2] + bv[2],
-                                           acc[rg][3] + bv[3]);
-                    *reinterpret_cast<float4 *>(d) = v;
+                    *reinterpret_cast<float4 *>(d) = make_float4(
+                        acc[rg][0] + bv[0], acc[rg][1] + bv[1], acc[rg][2] + bv[2], acc[rg][3] + bv[3]);
                 }
             }
         }
+        // the wave reads back its own staged rows: no cross-wave sharing
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        T *dst = reinterpret_cast<T *>(o.dst);
+        const int cr = lane % CPR, rr = lane / CPR;
+#pragma unroll
+        for (int it = 0; it < ROWS / RPI; ++it) {
+            const int lrow = it * RPI + rr;
+            const int64_t r = row0 + lrow;
+            if (r < a.rows) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(stage + lrow * PITCH + cr * 16);
+                T *dp = dst + out_offset(a, o, (uint32_t)r) + cr * (16 / (int)sizeof(T));
+                *reinterpret_cast<uint4 *>(dp) = v;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -220,14 +238,14 @@ pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s
         if (E == 64)
             e = run_mfma<uint16_t, 64, 4>(a, s);
         else if (E == 128)
-            e = run_mfma<uint16_t, 128, 4>(a, s);
+            e = run_mfma<uint16_t, 128, 2>(a, s);
         else
             e = run_generic<uint16_t>(a, E, s);
     } else {
         if (E == 64)
             e = run_mfma<float, 64, 2>(a, s);
         else if (E == 128)
-            e = run_mfma<float, 128, 2>(a, s);
+            e = run_mfma<float, 128, 1>(a, s);
         else
             e = run_generic<float>(a, E, s);
     }
