@@ -229,7 +229,7 @@ __global__ void split_count_kernel(const int32_t *deg, int64_t L, int chunk, int
 __global__ void split_fill_kernel(const int32_t *row_ptr, int64_t L, int chunk,
                                   const int32_t *piece_base, const int32_t *slot_base,
                                   const int32_t *split_base, int32_t *t_target, int32_t *t_begin,
-                                  int32_t *t_end, int32_t *t_slot, int32_t *t_key,
+                                  int32_t *t_end, int32_t *t_slot, int32_t *t_split, int32_t *t_key,
                                   int32_t *s_target, int32_t *s_slot0, int32_t *s_count)
 {
     int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -244,6 +244,7 @@ __global__ void split_fill_kernel(const int32_t *row_ptr, int64_t L, int chunk,
         t_begin[pb + j] = (int32_t)b;
         t_end[pb + j] = (int32_t)e;
         t_slot[pb + j] = n > 1 ? (int32_t)(slot_base[t] + j) : -1;
+        t_split[pb + j] = n > 1 ? split_base[t] : -1;
         t_key[pb + j] = chunk - (int32_t)(e - b);  // ascending key = descending length
     }
     if (n > 1) {
@@ -254,9 +255,10 @@ __global__ void split_fill_kernel(const int32_t *row_ptr, int64_t L, int chunk,
     }
 }
 
-__global__ void gather4_kernel(const int32_t *perm, int64_t n, const int32_t *a0,
+__global__ void gather5_kernel(const int32_t *perm, int64_t n, const int32_t *a0,
                                const int32_t *a1, const int32_t *a2, const int32_t *a3,
-                               int32_t *o0, int32_t *o1, int32_t *o2, int32_t *o3)
+                               const int32_t *a4, int32_t *o0, int32_t *o1, int32_t *o2,
+                               int32_t *o3, int32_t *o4)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n)
@@ -266,6 +268,7 @@ __global__ void gather4_kernel(const int32_t *perm, int64_t n, const int32_t *a0
     o1[i] = a1[p];
     o2[i] = a2[p];
     o3[i] = a3[p];
+    o4[i] = a4[p];
 }
 
 inline unsigned grid_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
@@ -319,9 +322,9 @@ hipError_t radix_sort_perm(const int32_t *keys, int bits, int32_t *&perm, int32_
 
 void free_graph(GraphDev *g)
 {
-    int32_t **ptrs[] = {&g->row_ptr,    &g->csr_src,    &g->csr_tgt,     &g->csr_eid,
-                        &g->task_target, &g->task_begin, &g->task_end,    &g->task_slot,
-                        &g->split_target, &g->split_slot0, &g->split_count};
+    int32_t **ptrs[] = {&g->row_ptr,     &g->csr_src,     &g->csr_tgt,    &g->csr_eid,
+                        &g->task_target, &g->task_begin,  &g->task_end,   &g->task_slot,
+                        &g->task_split,  &g->split_target, &g->split_slot0, &g->split_count};
     for (int32_t **p : ptrs) {
         if (*p)
             (void)hipFree(*p);
@@ -339,7 +342,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     int32_t *n_piece = nullptr, *n_slot = nullptr, *is_split = nullptr;
     int32_t *piece_base = nullptr, *slot_base = nullptr, *split_base = nullptr;
     int32_t *t_target = nullptr, *t_begin = nullptr, *t_end = nullptr, *t_slot = nullptr,
-            *t_key = nullptr, *tperm = nullptr, *tperm_tmp = nullptr;
+            *t_split = nullptr, *t_key = nullptr, *tperm = nullptr, *tperm_tmp = nullptr;
     int32_t h_small[8] = {0};
     const int64_t n_sort = nnz > L ? nnz : L;
     const int64_t ntiles = (n_sort + kTile - 1) / kTile;
@@ -405,6 +408,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
         PMA_TRY(hipMalloc(&t_begin, nt * i4));
         PMA_TRY(hipMalloc(&t_end, nt * i4));
         PMA_TRY(hipMalloc(&t_slot, nt * i4));
+        PMA_TRY(hipMalloc(&t_split, nt * i4));
         PMA_TRY(hipMalloc(&t_key, nt * i4));
         PMA_TRY(hipMalloc(&tperm, nt * i4));
         PMA_TRY(hipMalloc(&tperm_tmp, nt * i4));
@@ -412,6 +416,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
         PMA_TRY(hipMalloc(&g->task_begin, nt * i4));
         PMA_TRY(hipMalloc(&g->task_end, nt * i4));
         PMA_TRY(hipMalloc(&g->task_slot, nt * i4));
+        PMA_TRY(hipMalloc(&g->task_split, nt * i4));
         PMA_TRY(hipMalloc(&g->split_target, ns * i4));
         PMA_TRY(hipMalloc(&g->split_slot0, ns * i4));
         PMA_TRY(hipMalloc(&g->split_count, ns * i4));
@@ -420,14 +425,14 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
         PMA_TRY(hipMalloc(&sc, 256 * ntt * i4));
         split_fill_kernel<<<grid_for(L, 256), 256, 0, stream>>>(
             g->row_ptr, L, chunk, piece_base, slot_base, split_base, t_target, t_begin, t_end,
-            t_slot, t_key, g->split_target, g->split_slot0, g->split_count);
+            t_slot, t_split, t_key, g->split_target, g->split_slot0, g->split_count);
         iota_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(tperm, nt);
         hipError_t e = radix_sort_perm(t_key, bits_for(chunk), tperm, tperm_tmp, nt, sc, scan_tmp,
                                        stream);
         if (e == hipSuccess) {
-            gather4_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(
-                tperm, nt, t_target, t_begin, t_end, t_slot, g->task_target, g->task_begin,
-                g->task_end, g->task_slot);
+            gather5_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(
+                tperm, nt, t_target, t_begin, t_end, t_slot, t_split, g->task_target,
+                g->task_begin, g->task_end, g->task_slot, g->task_split);
             e = hipGetLastError();
         }
         if (e == hipSuccess)
@@ -449,7 +454,7 @@ done:
         int32_t *tmps[] = {d_src,     d_tgt,     perm,       perm_tmp,   counts,   scan_tmp,
                            deg,       small,     n_piece,    n_slot,     is_split, piece_base,
                            slot_base, split_base, t_target,  t_begin,    t_end,    t_slot,
-                           t_key,     tperm,     tperm_tmp};
+                           t_split,   t_key,     tperm,      tperm_tmp};
         for (int32_t *p : tmps)
             if (p)
                 (void)hipFree(p);

@@ -44,9 +44,10 @@ struct pma_plan {
     pma::GraphDev g;
     // workspace, grown on demand
     int64_t ws_B = 0;
-    bool ws_weights = false;
+    bool ws_weights = false, ws_unfused = false;
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
+    int *counters = nullptr;
     // profiling
     bool prof = false;
     std::vector<EventPair> pending;
@@ -59,22 +60,27 @@ namespace {
 
 void free_workspace(pma_plan *p)
 {
-    void *ptrs[] = {p->qt, p->kv, p->mixed, p->part_acc, p->part_ml, p->stat_ml, p->scores};
+    void *ptrs[] = {p->qt,      p->kv,      p->mixed,  p->part_acc,
+                    p->part_ml, p->stat_ml, p->scores, p->counters};
     for (void *q : ptrs)
         if (q)
             (void)hipFree(q);
     p->qt = p->kv = p->mixed = nullptr;
     p->part_acc = p->part_ml = p->stat_ml = p->scores = nullptr;
+    p->counters = nullptr;
     p->ws_B = 0;
-    p->ws_weights = false;
+    p->ws_weights = p->ws_unfused = false;
 }
 
-pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
+// Buffers for a batch of B: k/v always; q and mixed only for the unfused
+// kernels; scores and final (max, sum) only for need_weights.
+pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, bool unfused, hipStream_t s)
 {
-    if (B <= p->ws_B && (!weights || p->ws_weights))
+    if (B <= p->ws_B && (!weights || p->ws_weights) && (!unfused || p->ws_unfused))
         return PMA_OK;
     const int64_t nB = B > p->ws_B ? B : p->ws_B;
     const bool nw = weights || p->ws_weights;
+    const bool nu = unfused || p->ws_unfused;
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess)
         return fail(PMA_E_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
@@ -85,9 +91,10 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
         void **ptr;
         size_t bytes;
     } want[] = {
-        {&p->qt, (size_t)p->L * nB * p->E * es},
+        {&p->qt, nu ? (size_t)p->L * nB * p->E * es : 0},
         {&p->kv, (size_t)p->S * 2 * nB * p->E * es},
-        {&p->mixed, (size_t)p->L * nB * p->E * es},
+        {&p->mixed, nu ? (size_t)p->L * nB * p->E * es : 0},
+        {(void **)&p->counters, slots * (size_t)((nB + 15) / 16) * sizeof(int)},
         {(void **)&p->part_acc, slots * nB * p->E * 4},
         {(void **)&p->part_ml, slots * nB * p->H * 2 * 4},
         {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
@@ -103,8 +110,16 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
                         "workspace allocation of %zu bytes: %s", w.bytes, hipGetErrorString(e));
         }
     }
+    e = hipMemsetAsync(p->counters, 0, slots * (size_t)((nB + 15) / 16) * sizeof(int), s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        free_workspace(p);
+        return fail(PMA_E_DEVICE, "workspace clear: %s", hipGetErrorString(e));
+    }
     p->ws_B = nB;
     p->ws_weights = nw;
+    p->ws_unfused = nu;
     return PMA_OK;
 }
 
@@ -360,24 +375,32 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     const int64_t B = batch, L = p->L, S = p->S, E = p->E;
     if ((L > S ? L : S) * B * 2 * E > ((int64_t)1 << 40))
         return fail(PMA_E_UNSUPPORTED, "batch too large for one forward");
-    pma_status st = ensure_workspace(p, B, weights != nullptr, stream);
+    // The fused kernel needs E in {64, 128}, d in {8, 16, 32} and 16-byte
+    // aligned caller tensors; anything else runs the separate kernels.
+    const uintptr_t align_bits = (uintptr_t)query | (uintptr_t)key | (uintptr_t)value |
+                                 (uintptr_t)q_w | (uintptr_t)o_w | (uintptr_t)out;
+    const bool fused = pma::fused_supported(E, p->H, p->dtype) && (align_bits & 15) == 0;
+    pma_status st = ensure_workspace(p, B, weights != nullptr, !fused, stream);
     if (st != PMA_OK)
         return st;
     StageTimer tm{p, stream};
     const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
     char *kvc = static_cast<char *>(p->kv);
 
-    // Step 1: projections. qt[l][b][E], kv[s][keys | values][b][E].
+    // Step 1 (keys and values; queries too on the unfused path).
+    // qt[l][b][E], kv[s][keys | values][b][E].
     tm.begin(PMA_STAGE_PROJ_IN);
     const pma::ProjOut oq{q_w, q_b, p->qt, E, B * E};
     const pma::ProjOut ok{k_w, k_b, kvc, E, 2 * B * E};
     const pma::ProjOut ov{v_w, v_b, kvc + (size_t)B * E * es, E, 2 * B * E};
-    if (query == key && key == value && L == S) {
+    if (!fused && query == key && key == value && L == S) {
         pma::ProjArgs a{query, B * L, L, B, 0, 3, {oq, ok, ov}};
         st = pma::launch_proj(a, E, p->dtype, stream);
     } else {
-        pma::ProjArgs aq{query, B * L, L, B, 0, 1, {oq}};
-        st = pma::launch_proj(aq, E, p->dtype, stream);
+        if (!fused) {
+            pma::ProjArgs aq{query, B * L, L, B, 0, 1, {oq}};
+            st = pma::launch_proj(aq, E, p->dtype, stream);
+        }
         if (st == PMA_OK && key == value) {
             pma::ProjArgs akv{key, B * S, S, B, 0, 2, {ok, ov}};
             st = pma::launch_proj(akv, E, p->dtype, stream);
@@ -394,7 +417,6 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     if (st != PMA_OK)
         return fail(st, "projection launch failed: %s", hipGetErrorString(hipGetLastError()));
 
-    // Steps 2-4: scores, softmax and mix over the live edges.
     pma::EdgeArgs ea;
     ea.g = &p->g;
     ea.B = B;
@@ -413,6 +435,44 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
+
+    if (fused) {
+        // Steps 1 (queries) to 5 in one kernel.
+        pma::FusedArgs fa;
+        fa.g = &p->g;
+        fa.B = B;
+        fa.L = L;
+        fa.S = S;
+        fa.E = E;
+        fa.H = p->H;
+        fa.nnz = p->nnz;
+        fa.dt = p->dtype;
+        fa.xq = query;
+        fa.wq = q_w;
+        fa.bq = q_b;
+        fa.wo = o_w;
+        fa.bo = o_b;
+        fa.kv = p->kv;
+        fa.out = out;
+        fa.part_acc = p->part_acc;
+        fa.part_ml = p->part_ml;
+        fa.counters = p->counters;
+        fa.stat_ml = ea.stat_ml;
+        fa.scores = ea.scores;
+        tm.begin(PMA_STAGE_EDGE);
+        st = pma::launch_fused(fa, stream);
+        tm.end();
+        if (st == PMA_OK && weights) {
+            tm.begin(PMA_STAGE_WEIGHTS);
+            st = pma::launch_weights(ea, stream);
+            tm.end();
+        }
+        if (st != PMA_OK)
+            return fail(st, "edge launch failed: %s", hipGetErrorString(hipGetLastError()));
+        return PMA_OK;
+    }
+
+    // Steps 2-4: scores, softmax and mix over the live edges.
     tm.begin(PMA_STAGE_EDGE);
     st = pma::launch_edge(ea, stream);
     tm.end();

@@ -17,7 +17,7 @@ struct GraphDev {
     int32_t *csr_tgt = nullptr;   // nnz
     int32_t *csr_eid = nullptr;   // nnz, position in the edge order
     int32_t *task_target = nullptr, *task_begin = nullptr, *task_end = nullptr,
-            *task_slot = nullptr; // n_tasks each
+            *task_slot = nullptr, *task_split = nullptr; // n_tasks each; split index or -1
     int32_t *split_target = nullptr, *split_slot0 = nullptr, *split_count = nullptr; // n_split
     int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0;
 };
@@ -67,12 +67,30 @@ struct EdgeArgs {
     float *part_acc;    // [slot][B][E]
     float *part_ml;     // [slot][B][H][2]
     float *stat_ml;     // [L][B][H][2] final (max, sum) or nullptr
-    float *scores;      // [B][nnz][H] log2-domain scores by CSR position, or nullptr
+    float *scores;      // [nnz][B][H] log2-domain scores by CSR position, or nullptr
     float *weights;     // caller's weights or nullptr
     int average;
 };
 
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
+
+// ---- fused q projection + edges + out_proj (attend.hip) --------------------
+
+struct FusedArgs {
+    const GraphDev *g;
+    int64_t B, L, S, E, H, nnz;
+    pma_dtype dt;
+    const void *xq;                 // caller's (B, L, E) query tokens
+    const void *wq, *bq, *wo, *bo;  // caller's parameters (biases may be null)
+    const void *kv;                 // [S][2][B][E]
+    void *out;                      // caller's (B, L, E)
+    float *part_acc, *part_ml;      // as in EdgeArgs
+    int *counters;                  // [n_split][ceil(B / 16)], zero
+    float *stat_ml, *scores;        // need_weights only
+};
+
+bool fused_supported(int64_t E, int64_t H, pma_dtype dt);
+pma_status launch_fused(const FusedArgs &a, hipStream_t s);
 pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
 pma_status launch_weights(const EdgeArgs &a, hipStream_t s);
 
