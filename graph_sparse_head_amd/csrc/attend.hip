@@ -24,10 +24,10 @@
 // lane, so its dot product needs no cross-lane reduction.
 //
 // A target longer than the plan's chunk is split into pieces; each piece
-// stores its running (max, sum, partial mix) and the last piece to finish
-// (an agent-scope counter, release/acquire fences) merges them in piece
-// order and runs out_proj. The merged result does not depend on which piece
-// finished last.
+// stores its running (max, sum, partial mix), and merge_out, launched next,
+// combines them in piece order and runs out_proj. (A last-piece-merges
+// scheme needs agent-scope release/acquire fences, which write back and
+// invalidate the L2 of an XCD each time; measured, it was slower.)
 #include <math.h>
 
 #include "pma_internal.h"
@@ -42,8 +42,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 struct FusedK {
     const int32_t *csr_src;
     const int32_t *task_target, *task_begin, *task_end, *task_slot, *task_split;
-    const int32_t *split_slot0, *split_count;
-    int64_t n_tasks;
+    const int32_t *split_target, *split_slot0, *split_count;
+    int64_t n_tasks, n_split;
     int B, L, H, passes;
     int64_t nnz;
     float scale;         // log2(e) / sqrt(d)
@@ -53,7 +53,6 @@ struct FusedK {
     void *out;           // (B, L, E)
     float *part_acc;     // [slot][B][E]
     float *part_ml;      // [slot][B][H][2]
-    int *counters;       // [split][passes], zero between launches
     float *stat_ml;      // [L][B][H][2] or nullptr
     float *scores;       // [nnz][B][H] or nullptr
 };
@@ -147,6 +146,54 @@ template <typename T, int N> __device__ inline void pack(const float *v, uint4 *
                 x[j] = (uint32_t)f2bf(v[8 * k + 2 * j]) | ((uint32_t)f2bf(v[8 * k + 2 * j + 1]) << 16);
             w[k] = make_uint4(x[0], x[1], x[2], x[3]);
         }
+    }
+}
+
+// Steps 4 (end) and 5 for one (target, sample) row slice: mixed = acc / sum
+// (zeros without edges), optional final (max, sum), out = mixed Wo^T + bo.
+template <typename T, int E, int D>
+__device__ inline void finish(const FusedK &a, int t, int b, bool valid, int lane,
+                              const float *m, const float *l, const float *acc)
+{
+    constexpr int CPL = E / 4;
+    constexpr int HL = D <= CPL ? CPL / D : 1;
+    constexpr int GH = D <= CPL ? 1 : D / CPL;
+    constexpr int HC = D <= CPL ? D : CPL;
+    constexpr int VPL = CPL * (int)sizeof(T) / 16;
+    constexpr int EPW = 16 / (int)sizeof(T);
+    const int g = lane >> 4;
+    const int B = a.B;
+    const int c0 = g * CPL;
+    const int h0 = GH == 1 ? g * HL : g / GH;
+    const bool head_lead = GH == 1 || (g % GH) == 0;
+    // ---- step 4 end: mixed = acc / sum (zeros without edges)
+    float mix[CPL];
+#pragma unroll
+    for (int j = 0; j < HL; ++j)
+#pragma unroll
+        for (int i = 0; i < HC; ++i)
+            mix[j * HC + i] = l[j] > 0.f ? acc[j * HC + i] / l[j] : 0.f;
+    if (a.stat_ml && valid && head_lead) {
+#pragma unroll
+        for (int j = 0; j < HL; ++j) {
+            float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h0 + j) * 2;
+            st[0] = m[j];
+            st[1] = l[j];
+        }
+    }
+
+    // ---- step 5: out = mixed Wo^T + bo
+    uint4 ms[VPL];
+    pack<T, CPL>(mix, ms);
+    float o[CPL];
+    project<T, E>(ms, reinterpret_cast<const T *>(a.wo), reinterpret_cast<const T *>(a.bo), lane, o);
+    if (valid) {
+        uint4 ow[VPL];
+        pack<T, CPL>(o, ow);
+        T *dst = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.L + t) * E + c0;
+#pragma unroll
+        for (int w = 0; w < VPL; ++w)
+            *reinterpret_cast<uint4 *>(dst + w * EPW) = ow[w];
     }
 }
 
@@ -283,10 +330,10 @@ __global__ void __launch_bounds__(256) attend_fused(FusedK a)
         }
     }
 
-    // ---- pieces of a split target: the last one to finish merges them
+    // ---- a piece of a split target leaves (max, sum, partial mix) for merge_out
     if (slot >= 0) {
-        float *pa = a.part_acc + ((int64_t)slot * B + b) * E + c0;
         if (valid) {
+            float *pa = a.part_acc + ((int64_t)slot * B + b) * E + c0;
 #pragma unroll
             for (int k = 0; k < CPL / 4; ++k)
                 reinterpret_cast<float4 *>(pa)[k] =
@@ -300,82 +347,66 @@ __global__ void __launch_bounds__(256) attend_fused(FusedK a)
                 }
             }
         }
-        __threadfence();
-        const int k = a.task_split[task];
-        const int cnt_idx = k * a.passes + pass;
-        const int npieces = a.split_count[k];
-        int old = 0;
-        if (lane == 0)
-            old = __hip_atomic_fetch_add(&a.counters[cnt_idx], 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-        old = __shfl(old, 0, 64);
-        if (old != npieces - 1)
-            return;
-        __threadfence();
-        const int s0 = a.split_slot0[k];
+        return;
+    }
+
+    finish<T, E, D>(a, t, b, valid, lane, m, l, acc);
+}
+
+// Merge the pieces of each split target in piece order, then out_proj.
+// One wavefront per (split target, 16 samples), lanes as in attend_fused.
+template <typename T, int E, int D>
+__global__ void __launch_bounds__(256) merge_out(FusedK a)
+{
+    constexpr int CPL = E / 4;
+    constexpr int HL = D <= CPL ? CPL / D : 1;
+    constexpr int GH = D <= CPL ? 1 : D / CPL;
+    constexpr int HC = D <= CPL ? D : CPL;
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= a.n_split * a.passes)
+        return;
+    const int k = (int)(unit / a.passes);
+    const int pass = (int)(unit - (int64_t)k * a.passes);
+    const int g = lane >> 4, n = lane & 15;
+    const int B = a.B;
+    const int b = pass * 16 + n;
+    const bool valid = b < B;
+    const int c0 = g * CPL;
+    const int h0 = GH == 1 ? g * HL : g / GH;
+    const int t = a.split_target[k], s0 = a.split_slot0[k], np = a.split_count[k];
+    float m[HL], l[HL], acc[CPL];
+#pragma unroll
+    for (int j = 0; j < HL; ++j) {
+        float M = -INFINITY;
+        for (int q = 0; q < np && valid; ++q)
+            M = fmaxf(M, a.part_ml[(((int64_t)(s0 + q) * B + b) * a.H + h0 + j) * 2]);
+        m[j] = M;
+        l[j] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+    for (int q = 0; q < np && valid; ++q) {
+        const float4 *pq = reinterpret_cast<const float4 *>(
+            a.part_acc + ((int64_t)(s0 + q) * B + b) * E + c0);
 #pragma unroll
         for (int j = 0; j < HL; ++j) {
-            float M = -INFINITY;
-            for (int q = 0; q < npieces && valid; ++q)
-                M = fmaxf(M, a.part_ml[(((int64_t)(s0 + q) * B + b) * a.H + h0 + j) * 2]);
-            m[j] = M;
-            l[j] = 0.f;
-        }
+            const float2 ml = *reinterpret_cast<const float2 *>(
+                a.part_ml + (((int64_t)(s0 + q) * B + b) * a.H + h0 + j) * 2);
+            const float w = fast_exp2(ml.x - m[j]);
+            l[j] = fmaf(ml.y, w, l[j]);
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
-        for (int q = 0; q < npieces && valid; ++q) {
-            const float4 *pq = reinterpret_cast<const float4 *>(
-                a.part_acc + ((int64_t)(s0 + q) * B + b) * E + c0);
-#pragma unroll
-            for (int j = 0; j < HL; ++j) {
-                const float2 ml = *reinterpret_cast<const float2 *>(
-                    a.part_ml + (((int64_t)(s0 + q) * B + b) * a.H + h0 + j) * 2);
-                const float w = fast_exp2(ml.x - m[j]);
-                l[j] = fmaf(ml.y, w, l[j]);
-#pragma unroll
-                for (int i4 = 0; i4 < HC / 4; ++i4) {
-                    const float4 v = pq[(j * HC) / 4 + i4];
-                    const int i = j * HC + 4 * i4;
-                    acc[i] = fmaf(v.x, w, acc[i]);
-                    acc[i + 1] = fmaf(v.y, w, acc[i + 1]);
-                    acc[i + 2] = fmaf(v.z, w, acc[i + 2]);
-                    acc[i + 3] = fmaf(v.w, w, acc[i + 3]);
-                }
+            for (int i4 = 0; i4 < HC / 4; ++i4) {
+                const float4 v = pq[(j * HC) / 4 + i4];
+                const int i = j * HC + 4 * i4;
+                acc[i] = fmaf(v.x, w, acc[i]);
+                acc[i + 1] = fmaf(v.y, w, acc[i + 1]);
+                acc[i + 2] = fmaf(v.z, w, acc[i + 2]);
+                acc[i + 3] = fmaf(v.w, w, acc[i + 3]);
             }
         }
-        if (lane == 0)
-            a.counters[cnt_idx] = 0;   // ready for the next launch
     }
-
-    // ---- step 4 end: mixed = acc / sum (zeros without edges)
-    float mix[CPL];
-#pragma unroll
-    for (int j = 0; j < HL; ++j)
-#pragma unroll
-        for (int i = 0; i < HC; ++i)
-            mix[j * HC + i] = l[j] > 0.f ? acc[j * HC + i] / l[j] : 0.f;
-    if (a.stat_ml && valid && head_lead) {
-#pragma unroll
-        for (int j = 0; j < HL; ++j) {
-            float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h0 + j) * 2;
-            st[0] = m[j];
-            st[1] = l[j];
-        }
-    }
-
-    // ---- step 5: out = mixed Wo^T + bo
-    uint4 ms[VPL];
-    pack<T, CPL>(mix, ms);
-    float o[CPL];
-    project<T, E>(ms, reinterpret_cast<const T *>(a.wo), reinterpret_cast<const T *>(a.bo), lane, o);
-    if (valid) {
-        uint4 ow[VPL];
-        pack<T, CPL>(o, ow);
-        T *dst = reinterpret_cast<T *>(a.out) + ((int64_t)b * a.L + t) * E + c0;
-#pragma unroll
-        for (int w = 0; w < VPL; ++w)
-            *reinterpret_cast<uint4 *>(dst + w * EPW) = ow[w];
-    }
+    finish<T, E, D>(a, t, b, valid, lane, m, l, acc);
 }
 
 template <typename T, int E, int D, int U>
@@ -386,14 +417,22 @@ hipError_t run(const FusedK &k, hipStream_t s)
     return hipGetLastError();
 }
 
+template <typename T, int E, int D>
+hipError_t run_merge(const FusedK &k, hipStream_t s)
+{
+    const int64_t units = k.n_split * k.passes;
+    merge_out<T, E, D><<<(unsigned)((units + 3) / 4), 256, 0, s>>>(k);
+    return hipGetLastError();
+}
+
 template <typename T, int E>
-hipError_t dispatch_d(const FusedK &k, int d, hipStream_t s)
+hipError_t dispatch_d(const FusedK &k, int d, bool merge, hipStream_t s)
 {
     constexpr int U = (E * (int)sizeof(T) <= 128) ? 4 : (E * (int)sizeof(T) <= 256 ? 2 : 1);
     switch (d) {
-    case 8: return run<T, E, 8, U>(k, s);
-    case 16: return run<T, E, 16, U>(k, s);
-    case 32: return run<T, E, 32, U>(k, s);
+    case 8: return merge ? run_merge<T, E, 8>(k, s) : run<T, E, 8, U>(k, s);
+    case 16: return merge ? run_merge<T, E, 16>(k, s) : run<T, E, 16, U>(k, s);
+    case 32: return merge ? run_merge<T, E, 32>(k, s) : run<T, E, 32, U>(k, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -411,7 +450,7 @@ bool fused_supported(int64_t E, int64_t H, pma_dtype dt)
     return dt == PMA_BF16 || dt == PMA_F32;
 }
 
-pma_status launch_fused(const FusedArgs &x, hipStream_t s)
+pma_status launch_fused(const FusedArgs &x, bool merge, hipStream_t s)
 {
     FusedK k;
     const GraphDev *g = x.g;
@@ -440,14 +479,18 @@ pma_status launch_fused(const FusedArgs &x, hipStream_t s)
     k.out = x.out;
     k.part_acc = x.part_acc;
     k.part_ml = x.part_ml;
-    k.counters = x.counters;
     k.stat_ml = x.stat_ml;
     k.scores = x.scores;
     hipError_t e;
+    k.n_split = g->n_split;
+    k.split_target = g->split_target;
+    if (merge && k.n_split == 0)
+        return PMA_OK;
     if (x.dt == PMA_BF16)
-        e = x.E == 64 ? dispatch_d<uint16_t, 64>(k, d, s) : dispatch_d<uint16_t, 128>(k, d, s);
+        e = x.E == 64 ? dispatch_d<uint16_t, 64>(k, d, merge, s)
+                      : dispatch_d<uint16_t, 128>(k, d, merge, s);
     else
-        e = x.E == 64 ? dispatch_d<float, 64>(k, d, s) : dispatch_d<float, 128>(k, d, s);
+        e = x.E == 64 ? dispatch_d<float, 64>(k, d, merge, s) : dispatch_d<float, 128>(k, d, merge, s);
     return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 

@@ -112,9 +112,17 @@ template <typename T, int CH> __device__ inline void store_chunk(T *p, const flo
 }
 
 // Fast path: d = CH * LPH with 16-byte chunks. U edges per step.
+//
+// Per edge the source's row base is wave-uniform (scalar registers) and each
+// lane adds a fixed 32-bit byte offset, so the gather costs no vector
+// address arithmetic. Lanes past the last chunk read lane 0's address and
+// discard the data. bf16 scores use v_dot2 on the stored bf16 q and k words
+// (fp32 products and sums) and are scaled afterwards.
 template <typename T, int CH, int LPH, int U>
 __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
 {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    constexpr bool BF = sizeof(T) == 2;
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= a.n_tasks * a.passes)
@@ -136,21 +144,19 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
     const bool head_lead = (lane % LPH) == 0;
 
     const T *qt = reinterpret_cast<const T *>(a.qt);
-    const T *kv = reinterpret_cast<const T *>(a.kv);
-    float q[CH];
-    {
-        Chunk<T, CH> qc;
-        if (active)
-            qc.load(qt + ((int64_t)t * B + b) * E + col);
-        else
-            qc.zero();
+    Chunk<T, CH> q;
+    q.load(qt + ((int64_t)t * B + b) * E + col);
+    float qf[BF ? 1 : CH];
+    if constexpr (!BF) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) q[i] = qc[i] * a.scale;
+        for (int i = 0; i < CH; ++i) qf[i] = q[i] * a.scale;
     }
 
-    const int64_t row2 = (int64_t)2 * B * E;     // one source's keys + values
-    const int64_t voff = (int64_t)B * E;
-    const T *kvl = kv + (int64_t)b * E + col;
+    // byte offsets: one source's keys+values row, the values inside it, this lane
+    const uint64_t row2 = (uint64_t)2 * B * E * sizeof(T);
+    const uint32_t voff = (uint32_t)(B * E * sizeof(T));
+    const uint32_t loff = (uint32_t)((b * E + col) * sizeof(T));
+    const char *kvb = reinterpret_cast<const char *>(a.kv);
 
     float m = -INFINITY, l = 0.f;
     float acc[CH];
@@ -159,28 +165,30 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
 
     for (int p = beg; p < end; p += U) {
         const int n = end - p < U ? end - p : U;
-        int s[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) s[u] = a.csr_src[u < n ? p + u : p];
         Chunk<T, CH> kk[U], vv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const T *base = kvl + (int64_t)s[u] * row2;
-            if (active) {
-                kk[u].load(base);
-                vv[u].load(base + voff);
-            } else {
-                kk[u].zero();
-                vv[u].zero();
-            }
+            const int s = a.csr_src[p + u];                   // padded past nnz
+            const char *base = kvb + (uint64_t)s * row2;      // uniform
+            kk[u].u = *reinterpret_cast<const uint4 *>(base + loff);
+            vv[u].u = *reinterpret_cast<const uint4 *>(base + voff + loff);
         }
         float sc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float dot = 0.f;
+            if constexpr (BF) {
 #pragma unroll
-            for (int i = 0; i < CH; ++i) dot = fmaf(q[i], kk[u][i], dot);
+                for (int k = 0; k < 4; ++k)
+                    dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.word(k)),
+                                                          __builtin_bit_cast(bf16x2, kk[u].word(k)),
+                                                          dot, false);
+            } else {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) dot = fmaf(qf[i], kk[u][i], dot);
+            }
             dot = group_sum<LPH>(dot);
+            if constexpr (BF) dot *= a.scale;
             sc[u] = u < n ? dot : -INFINITY;
         }
         if (a.scores && active && head_lead) {
@@ -429,26 +437,30 @@ EdgeK make_k(const EdgeArgs &x)
 }
 
 template <typename T, int CH, int LPH>
-hipError_t run_fast(EdgeK k, hipStream_t s)
+hipError_t run_fast(EdgeK k, int unroll, hipStream_t s)
 {
     const int64_t chunks = (int64_t)k.B * (k.E / CH);
     k.passes = (int)((chunks + 63) / 64);
     const int64_t units = k.n_tasks * k.passes;
-    edge_fast<T, CH, LPH, 4><<<(unsigned)((units + 3) / 4), 256, 0, s>>>(k);
+    const unsigned blocks = (unsigned)((units + 3) / 4);
+    if (unroll == 8)
+        edge_fast<T, CH, LPH, 8><<<blocks, 256, 0, s>>>(k);
+    else
+        edge_fast<T, CH, LPH, 4><<<blocks, 256, 0, s>>>(k);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_edge(EdgeK k, hipStream_t s)
+hipError_t dispatch_edge(EdgeK k, int unroll, hipStream_t s)
 {
     constexpr int CH = 16 / sizeof(T);
     if (k.d % CH == 0) {
         switch (k.d / CH) {
-        case 1: return run_fast<T, CH, 1>(k, s);
-        case 2: return run_fast<T, CH, 2>(k, s);
-        case 4: return run_fast<T, CH, 4>(k, s);
-        case 8: return run_fast<T, CH, 8>(k, s);
-        case 16: return run_fast<T, CH, 16>(k, s);
+        case 1: return run_fast<T, CH, 1>(k, unroll, s);
+        case 2: return run_fast<T, CH, 2>(k, unroll, s);
+        case 4: return run_fast<T, CH, 4>(k, unroll, s);
+        case 8: return run_fast<T, CH, 8>(k, unroll, s);
+        case 16: return run_fast<T, CH, 16>(k, unroll, s);
         default: break;
         }
     }
@@ -491,7 +503,8 @@ hipError_t dispatch_merge(EdgeK k, hipStream_t s)
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
 {
     EdgeK k = make_k(x);
-    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, s) : dispatch_edge<float>(k, s);
+    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, x.unroll, s)
+                                    : dispatch_edge<float>(k, x.unroll, s);
     return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 

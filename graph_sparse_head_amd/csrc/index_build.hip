@@ -24,6 +24,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kItems = 8;
 constexpr int kTile = kThreads * kItems;  // 2048 elements per tile
+// Pieces run longest first in buckets of 16 edges, and by ascending target
+// inside a bucket, so that wavefronts resident together touch nearby token
+// rows (fewer address-translation misses than a strict length order).
+constexpr int kLenBucketShift = 4;
 
 #define PMA_TRY(call)                                                                  \
     do {                                                                               \
@@ -245,7 +249,7 @@ __global__ void split_fill_kernel(const int32_t *row_ptr, int64_t L, int chunk,
         t_end[pb + j] = (int32_t)e;
         t_slot[pb + j] = n > 1 ? (int32_t)(slot_base[t] + j) : -1;
         t_split[pb + j] = n > 1 ? split_base[t] : -1;
-        t_key[pb + j] = chunk - (int32_t)(e - b);  // ascending key = descending length
+        t_key[pb + j] = (chunk - (int32_t)(e - b)) >> kLenBucketShift;  // longest buckets first
     }
     if (n > 1) {
         const int32_t k = split_base[t];
@@ -360,7 +364,10 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     PMA_TRY(hipMalloc(&deg, L * i4));
     PMA_TRY(hipMalloc(&small, 8 * i4));
     PMA_TRY(hipMalloc(&g->row_ptr, (L + 1) * i4));
-    PMA_TRY(hipMalloc(&g->csr_src, nnz * i4));
+    // csr_src carries kSrcPad zero entries past nnz so that kernels may read a
+    // fixed number of indices at a time without clamping.
+    PMA_TRY(hipMalloc(&g->csr_src, (nnz + kSrcPad) * i4));
+    PMA_TRY(hipMemsetAsync(g->csr_src + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMalloc(&g->csr_tgt, nnz * i4));
     PMA_TRY(hipMalloc(&g->csr_eid, nnz * i4));
     PMA_TRY(hipMalloc(&n_piece, L * i4));
@@ -427,7 +434,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
             g->row_ptr, L, chunk, piece_base, slot_base, split_base, t_target, t_begin, t_end,
             t_slot, t_split, t_key, g->split_target, g->split_slot0, g->split_count);
         iota_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(tperm, nt);
-        hipError_t e = radix_sort_perm(t_key, bits_for(chunk), tperm, tperm_tmp, nt, sc, scan_tmp,
+        hipError_t e = radix_sort_perm(t_key, bits_for(chunk >> kLenBucketShift), tperm, tperm_tmp, nt, sc, scan_tmp,
                                        stream);
         if (e == hipSuccess) {
             gather5_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(

@@ -4,6 +4,7 @@
 // before any HIP call.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -26,7 +27,7 @@ pma_status fail(pma_status st, const char *fmt, ...)
     return st;
 }
 
-constexpr int kChunk = 64;            // most edges one piece of a target covers
+constexpr int kChunk = 256;           // most edges one piece of a target covers
 constexpr int64_t kI32 = 2147483647;  // device edge indices are int32
 
 struct EventPair {
@@ -40,6 +41,8 @@ struct pma_plan {
     int64_t L = 0, S = 0, E = 0, H = 0, nnz = 0;
     pma_dtype dtype = PMA_F32;
     int chunk = kChunk;
+    bool use_fused = false;     // PMA_FUSED=1: fused q/edge/out kernel where supported
+    int edge_unroll = 4;        // PMA_EDGE_UNROLL: edges per step of the edge kernel (4, 8)
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
     // workspace, grown on demand
@@ -47,7 +50,6 @@ struct pma_plan {
     bool ws_weights = false, ws_unfused = false;
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
-    int *counters = nullptr;
     // profiling
     bool prof = false;
     std::vector<EventPair> pending;
@@ -60,14 +62,12 @@ namespace {
 
 void free_workspace(pma_plan *p)
 {
-    void *ptrs[] = {p->qt,      p->kv,      p->mixed,  p->part_acc,
-                    p->part_ml, p->stat_ml, p->scores, p->counters};
+    void *ptrs[] = {p->qt, p->kv, p->mixed, p->part_acc, p->part_ml, p->stat_ml, p->scores};
     for (void *q : ptrs)
         if (q)
             (void)hipFree(q);
     p->qt = p->kv = p->mixed = nullptr;
     p->part_acc = p->part_ml = p->stat_ml = p->scores = nullptr;
-    p->counters = nullptr;
     p->ws_B = 0;
     p->ws_weights = p->ws_unfused = false;
 }
@@ -94,7 +94,6 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, bool unfused, 
         {&p->qt, nu ? (size_t)p->L * nB * p->E * es : 0},
         {&p->kv, (size_t)p->S * 2 * nB * p->E * es},
         {&p->mixed, nu ? (size_t)p->L * nB * p->E * es : 0},
-        {(void **)&p->counters, slots * (size_t)((nB + 15) / 16) * sizeof(int)},
         {(void **)&p->part_acc, slots * nB * p->E * 4},
         {(void **)&p->part_ml, slots * nB * p->H * 2 * 4},
         {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
@@ -109,13 +108,6 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, bool unfused, 
             return fail(e == hipErrorOutOfMemory ? PMA_E_OOM : PMA_E_DEVICE,
                         "workspace allocation of %zu bytes: %s", w.bytes, hipGetErrorString(e));
         }
-    }
-    e = hipMemsetAsync(p->counters, 0, slots * (size_t)((nB + 15) / 16) * sizeof(int), s);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(s);
-    if (e != hipSuccess) {
-        free_workspace(p);
-        return fail(PMA_E_DEVICE, "workspace clear: %s", hipGetErrorString(e));
     }
     p->ws_B = nB;
     p->ws_weights = nw;
@@ -232,6 +224,21 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     p->H = H;
     p->nnz = (int64_t)p->h_src.size();
     p->dtype = dtype;
+    // Tuning knobs read once per plan: PMA_CHUNK (most edges per piece,
+    // 1..65535), PMA_FUSED (1: the fused kernel where it applies) and
+    // PMA_EDGE_UNROLL (4 or 8).
+    if (const char *ev = getenv("PMA_CHUNK")) {
+        const long c = strtol(ev, nullptr, 10);
+        if (c >= 1 && c <= 65535)
+            p->chunk = (int)c;
+    }
+    if (const char *ev = getenv("PMA_FUSED"))
+        p->use_fused = ev[0] == '1';
+    if (const char *ev = getenv("PMA_EDGE_UNROLL")) {
+        const long u = strtol(ev, nullptr, 10);
+        if (u == 4 || u == 8)
+            p->edge_unroll = (int)u;
+    }
     if (p->nnz + L > kI32) {
         delete p;
         return fail(PMA_E_UNSUPPORTED, "nnz + query_features exceeds 2^31 - 1");
@@ -379,7 +386,8 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     // aligned caller tensors; anything else runs the separate kernels.
     const uintptr_t align_bits = (uintptr_t)query | (uintptr_t)key | (uintptr_t)value |
                                  (uintptr_t)q_w | (uintptr_t)o_w | (uintptr_t)out;
-    const bool fused = pma::fused_supported(E, p->H, p->dtype) && (align_bits & 15) == 0;
+    const bool fused = p->use_fused && pma::fused_supported(E, p->H, p->dtype) &&
+                       (align_bits & 15) == 0;
     pma_status st = ensure_workspace(p, B, weights != nullptr, !fused, stream);
     if (st != PMA_OK)
         return st;
@@ -435,6 +443,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
+    ea.unroll = p->edge_unroll;
 
     if (fused) {
         // Steps 1 (queries) to 5 in one kernel.
@@ -456,12 +465,16 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
         fa.out = out;
         fa.part_acc = p->part_acc;
         fa.part_ml = p->part_ml;
-        fa.counters = p->counters;
         fa.stat_ml = ea.stat_ml;
         fa.scores = ea.scores;
         tm.begin(PMA_STAGE_EDGE);
-        st = pma::launch_fused(fa, stream);
+        st = pma::launch_fused(fa, false, stream);
         tm.end();
+        if (st == PMA_OK && p->g.n_split > 0) {
+            tm.begin(PMA_STAGE_MERGE);
+            st = pma::launch_fused(fa, true, stream);
+            tm.end();
+        }
         if (st == PMA_OK && weights) {
             tm.begin(PMA_STAGE_WEIGHTS);
             st = pma::launch_weights(ea, stream);

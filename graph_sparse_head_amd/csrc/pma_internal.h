@@ -10,10 +10,13 @@ namespace pma {
 
 // ---- index build (index_build.hip) ---------------------------------------
 
+// Zero entries kept after the last source index (see GraphDev::csr_src).
+constexpr int kSrcPad = 16;
+
 // Device arrays describing one graph; owned by the plan.
 struct GraphDev {
     int32_t *row_ptr = nullptr;   // L + 1
-    int32_t *csr_src = nullptr;   // nnz, per target ascending source
+    int32_t *csr_src = nullptr;   // nnz (+ kSrcPad zeros), per target ascending source
     int32_t *csr_tgt = nullptr;   // nnz
     int32_t *csr_eid = nullptr;   // nnz, position in the edge order
     int32_t *task_target = nullptr, *task_begin = nullptr, *task_end = nullptr,
@@ -70,6 +73,7 @@ struct EdgeArgs {
     float *scores;      // [nnz][B][H] log2-domain scores by CSR position, or nullptr
     float *weights;     // caller's weights or nullptr
     int average;
+    int unroll = 4;     // edges per step of edge_fast (4 or 8)
 };
 
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
@@ -85,12 +89,12 @@ struct FusedArgs {
     const void *kv;                 // [S][2][B][E]
     void *out;                      // caller's (B, L, E)
     float *part_acc, *part_ml;      // as in EdgeArgs
-    int *counters;                  // [n_split][ceil(B / 16)], zero
     float *stat_ml, *scores;        // need_weights only
 };
 
 bool fused_supported(int64_t E, int64_t H, pma_dtype dt);
-pma_status launch_fused(const FusedArgs &a, hipStream_t s);
+// merge == false: every piece (attend_fused); true: split targets (merge_out).
+pma_status launch_fused(const FusedArgs &a, bool merge, hipStream_t s);
 pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
 pma_status launch_weights(const EdgeArgs &a, hipStream_t s);
 

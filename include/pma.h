@@ -61,11 +61,13 @@ typedef enum {
 
 /* Stages that pma_profile_read reports, in launch order. */
 typedef enum {
-    PMA_STAGE_PROJ_IN = 0, /* q / k / v projections */
-    PMA_STAGE_EDGE = 1,    /* fused score, online softmax and mix over the edges */
-    PMA_STAGE_MERGE = 2,   /* merge of targets split into several pieces */
+    PMA_STAGE_PROJ_IN = 0, /* k / v projections (and q on the separate-kernel path) */
+    PMA_STAGE_EDGE = 1,    /* score, online softmax and mix over the edges; on the
+                              fused path also q_proj and out_proj */
+    PMA_STAGE_MERGE = 2,   /* merge of targets split into several pieces; on the
+                              fused path also their out_proj */
     PMA_STAGE_WEIGHTS = 3, /* need_weights: one weight per live edge */
-    PMA_STAGE_OUT = 4,     /* out_proj */
+    PMA_STAGE_OUT = 4,     /* out_proj (separate-kernel path only) */
     PMA_NUM_STAGES = 5
 } pma_stage;
 
@@ -180,7 +182,8 @@ pma_status pma_csr(const pma_plan *plan, int64_t *row_ptr, int64_t *src, int64_t
 
 /* The plan's pieces, copied to HOST memory (blocking): per piece its target,
    first and end CSR position and partial slot (-1 when the target is one
-   piece), ordered by descending length, then target, then position; per
+   piece), ordered by (chunk - length) / 16 (longest bucket first), then
+   target, then position; per
    split target its id, first slot and piece count, in ascending target
    order. A target of in-degree g has max(1, ceil(g / chunk)) pieces, piece j
    covering positions row_ptr[t] + floor(j g / n) .. row_ptr[t] + floor((j+1) g / n). */

@@ -167,9 +167,10 @@ def work_split(row_ptr: np.ndarray, chunk: int):
 
     A target of degree g becomes n = max(1, ceil(g / chunk)) pieces; piece j
     covers CSR positions row_ptr[t] + floor(j g / n) .. row_ptr[t] +
-    floor((j+1) g / n). Pieces are ordered by descending length, ties by
-    ascending target then piece. Targets with n > 1 own n consecutive partial
-    slots, numbered in ascending target order; a lone piece has slot -1.
+    floor((j+1) g / n). Pieces are ordered by the bucket (chunk - length) // 16
+    (longest bucket first), ties by ascending target then piece. Targets with
+    n > 1 own n consecutive partial slots, numbered in ascending target order;
+    a lone piece has slot -1.
 
     Returns dict of int64 arrays: task_target, task_begin, task_end,
     task_slot; split_target, split_slot0, split_count; and n_slots.
@@ -193,7 +194,7 @@ def work_split(row_ptr: np.ndarray, chunk: int):
             b = int(row_ptr[t]) + (j * g) // n
             e = int(row_ptr[t]) + ((j + 1) * g) // n
             items.append((e - b, t, j, b, e))
-    items.sort(key=lambda it: (-it[0], it[1], it[2]))
+    items.sort(key=lambda it: ((chunk - it[0]) // 16, it[1], it[2]))
     tt = np.array([it[1] for it in items], np.int64)
     tb = np.array([it[3] for it in items], np.int64)
     te = np.array([it[4] for it in items], np.int64)
