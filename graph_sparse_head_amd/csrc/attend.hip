@@ -57,13 +57,12 @@ struct FusedK {
     float *scores;       // [nnz][B][H] or nullptr
 };
 
-__device__ inline uint16_t f2bf(float f)
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pack_bf16(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -143,7 +142,7 @@ template <typename T, int N> __device__ inline void pack(const float *v, uint4 *
             uint32_t x[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                x[j] = (uint32_t)f2bf(v[8 * k + 2 * j]) | ((uint32_t)f2bf(v[8 * k + 2 * j + 1]) << 16);
+                x[j] = pack_bf16(v[8 * k + 2 * j], v[8 * k + 2 * j + 1]);
             w[k] = make_uint4(x[0], x[1], x[2], x[3]);
         }
     }
@@ -241,7 +240,7 @@ __global__ void __launch_bounds__(256) attend_fused(FusedK a)
     if constexpr (BF) {
 #pragma unroll
         for (int i = 0; i < CPL / 2; ++i)
-            qb[i] = (uint32_t)f2bf(qf[2 * i]) | ((uint32_t)f2bf(qf[2 * i + 1]) << 16);
+            qb[i] = pack_bf16(qf[2 * i], qf[2 * i + 1]);
     } else {
 #pragma unroll
         for (int i = 0; i < CPL; ++i) qf[i] *= a.scale;

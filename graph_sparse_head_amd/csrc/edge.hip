@@ -18,10 +18,9 @@
 //   * with need_weights the log2-domain scores are stored per CSR position
 //     and normalised once the final (max, sum) of each target is known.
 //
-// Workspace layouts (elements):
-//   qt[L][B][E], kv[S][2][B][E] (keys, then values, of one source),
-//   mixed[L][B][E], part_acc[slot][B][E], part_ml[slot][B][H][2],
-//   stat_ml[L][B][H][2], scores[nnz][B][H].
+// Workspace layouts: q, keys/values and mixed rows are addressed through
+// element strides (Layout); part_acc[slot][B][E], part_ml[slot][B][H][2],
+// stat_ml[L][B][H][2], scores[nnz][B][H].
 #include <math.h>
 
 #include "pma_internal.h"
@@ -38,6 +37,7 @@ struct EdgeK {
     int64_t nnz;
     int passes;          // wavefronts per piece (sample groups)
     float scale;         // log2(e) / sqrt(d)
+    Layout lay;
     const void *qt, *kv;
     void *mixed;
     float *part_acc, *part_ml, *stat_ml, *scores, *weights;
@@ -46,14 +46,15 @@ struct EdgeK {
 
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-__device__ inline uint16_t f2bf(float f)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pack_bf16(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ inline uint16_t f2bf(float f) { return (uint16_t)(pack_bf16(f, 0.f) & 0xffffu); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -103,10 +104,10 @@ template <typename T, int CH> __device__ inline void store_chunk(T *p, const flo
         *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
     } else {
         uint4 u;
-        u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-        u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-        u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-        u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+        u.x = pack_bf16(v[0], v[1]);
+        u.y = pack_bf16(v[2], v[3]);
+        u.z = pack_bf16(v[4], v[5]);
+        u.w = pack_bf16(v[6], v[7]);
         *reinterpret_cast<uint4 *>(p) = u;
     }
 }
@@ -145,17 +146,17 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
 
     const T *qt = reinterpret_cast<const T *>(a.qt);
     Chunk<T, CH> q;
-    q.load(qt + ((int64_t)t * B + b) * E + col);
+    q.load(qt + t * a.lay.q_t + b * a.lay.q_b + col);
     float qf[BF ? 1 : CH];
     if constexpr (!BF) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) qf[i] = q[i] * a.scale;
     }
 
-    // byte offsets: one source's keys+values row, the values inside it, this lane
-    const uint64_t row2 = (uint64_t)2 * B * E * sizeof(T);
-    const uint32_t voff = (uint32_t)(B * E * sizeof(T));
-    const uint32_t loff = (uint32_t)((b * E + col) * sizeof(T));
+    // byte offsets: per source (uniform), values, this lane
+    const uint64_t row2 = (uint64_t)a.lay.kv_s * sizeof(T);
+    const uint64_t voff = (uint64_t)a.lay.kv_v * sizeof(T);
+    const uint64_t loff = (uint64_t)(b * a.lay.kv_b + col) * sizeof(T);
     const char *kvb = reinterpret_cast<const char *>(a.kv);
 
     float m = -INFINITY, l = 0.f;
@@ -220,7 +221,7 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
         float out[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
-        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col, out);
+        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
         if (a.stat_ml && head_lead) {
             float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
             st[0] = m;
@@ -256,15 +257,15 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
     const int t = a.task_target[task];
     const int beg = a.task_begin[task], end = a.task_end[task];
     const int slot = a.task_slot[task];
-    const T *qt = reinterpret_cast<const T *>(a.qt) + ((int64_t)t * B + b) * E + c0;
+    const T *qt = reinterpret_cast<const T *>(a.qt) + t * a.lay.q_t + b * a.lay.q_b + c0;
     const T *kv = reinterpret_cast<const T *>(a.kv);
-    const int64_t row2 = (int64_t)2 * B * E, voff = (int64_t)B * E;
+    const int64_t row2 = a.lay.kv_s, voff = a.lay.kv_v;
     auto ld = [](const T *p) -> float {
         if constexpr (sizeof(T) == 2) return bf2f(*p); else return *p;
     };
     float m = -INFINITY, l = 0.f, acc = 0.f;
     for (int p = beg; p < end; ++p) {
-        const T *kr = kv + (int64_t)a.csr_src[p] * row2 + (int64_t)b * E + c0;
+        const T *kr = kv + (int64_t)a.csr_src[p] * row2 + b * a.lay.kv_b + c0;
         float dot = 0.f;
         for (int i = 0; i < d; ++i) dot = fmaf(ld(qt + i) * a.scale, ld(kr + i), dot);
         if (a.scores && col == c0)
@@ -277,7 +278,7 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
     }
     if (slot < 0) {
         const float o = l > 0.f ? acc / l : 0.f;
-        T *dst = reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col;
+        T *dst = reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col;
         if constexpr (sizeof(T) == 2) *dst = f2bf(o); else *dst = o;
         if (a.stat_ml && col == c0) {
             float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
@@ -337,7 +338,7 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
     float out[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
-    store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col, out);
+    store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
     if (a.stat_ml && (lane % LPH) == 0) {
         float *st = a.stat_ml + (((int64_t)t * B + b) * H + h) * 2;
         st[0] = M;
@@ -369,7 +370,7 @@ __global__ void __launch_bounds__(256) merge_generic(EdgeK a)
         acc = fmaf(a.part_acc[((int64_t)(s0 + j) * B + b) * E + col], w, acc);
     }
     const float o = l > 0.f ? acc / l : 0.f;
-    T *dst = reinterpret_cast<T *>(a.mixed) + ((int64_t)t * B + b) * E + col;
+    T *dst = reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col;
     if constexpr (sizeof(T) == 2) *dst = f2bf(o); else *dst = o;
     if (a.stat_ml && col == h * a.d) {
         float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
@@ -424,6 +425,7 @@ EdgeK make_k(const EdgeArgs &x)
     k.nnz = x.nnz;
     k.passes = 1;
     k.scale = (float)(1.4426950408889634 / sqrt((double)k.d));
+    k.lay = x.lay;
     k.qt = x.qt;
     k.kv = x.kv;
     k.mixed = x.mixed;
@@ -499,6 +501,29 @@ hipError_t dispatch_merge(EdgeK k, hipStream_t s)
 }
 
 }  // namespace
+
+Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)
+{
+    Layout y;
+    if (batch_first) {
+        y.q_t = E;
+        y.q_b = L * E;
+        y.kv_s = E;
+        y.kv_b = S * E;
+        y.kv_v = B * S * E;
+        y.m_t = E;
+        y.m_b = L * E;
+    } else {
+        y.q_t = B * E;
+        y.q_b = E;
+        y.kv_s = 2 * B * E;
+        y.kv_b = E;
+        y.kv_v = B * E;
+        y.m_t = B * E;
+        y.m_b = E;
+    }
+    return y;
+}
 
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
 {

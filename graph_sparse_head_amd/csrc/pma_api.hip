@@ -43,6 +43,9 @@ struct pma_plan {
     int chunk = kChunk;
     bool use_fused = false;     // PMA_FUSED=1: fused q/edge/out kernel where supported
     int edge_unroll = 4;        // PMA_EDGE_UNROLL: edges per step of the edge kernel (4, 8)
+    int proj_order = 0;         // PMA_PROJ_ORDER: q/k/v rows visited batch- (0) or token-major (1)
+    int out_order = 1;          // PMA_OUT_ORDER: out_proj rows visited batch- (0) or token-major (1)
+    bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
     // workspace, grown on demand
@@ -234,6 +237,12 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     }
     if (const char *ev = getenv("PMA_FUSED"))
         p->use_fused = ev[0] == '1';
+    if (const char *ev = getenv("PMA_LAYOUT"))
+        p->batch_first_ws = strcmp(ev, "batch") == 0;
+    if (const char *ev = getenv("PMA_PROJ_ORDER"))
+        p->proj_order = ev[0] == '1';
+    if (const char *ev = getenv("PMA_OUT_ORDER"))
+        p->out_order = ev[0] == '1';
     if (const char *ev = getenv("PMA_EDGE_UNROLL")) {
         const long u = strtol(ev, nullptr, 10);
         if (u == 4 || u == 8)
@@ -394,31 +403,32 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     StageTimer tm{p, stream};
     const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
     char *kvc = static_cast<char *>(p->kv);
+    // the fused kernel reads the target-major layout
+    const pma::Layout lay = pma::make_layout(p->batch_first_ws && !fused, B, L, S, E);
 
     // Step 1 (keys and values; queries too on the unfused path).
-    // qt[l][b][E], kv[s][keys | values][b][E].
     tm.begin(PMA_STAGE_PROJ_IN);
-    const pma::ProjOut oq{q_w, q_b, p->qt, E, B * E};
-    const pma::ProjOut ok{k_w, k_b, kvc, E, 2 * B * E};
-    const pma::ProjOut ov{v_w, v_b, kvc + (size_t)B * E * es, E, 2 * B * E};
+    const pma::ProjOut oq{q_w, q_b, p->qt, lay.q_b, lay.q_t};
+    const pma::ProjOut ok{k_w, k_b, kvc, lay.kv_b, lay.kv_s};
+    const pma::ProjOut ov{v_w, v_b, kvc + (size_t)lay.kv_v * es, lay.kv_b, lay.kv_s};
+    const int po = p->proj_order;
+    auto in_args = [&](const void *x, int64_t n, int nblk, pma::ProjOut o0, pma::ProjOut o1,
+                       pma::ProjOut o2) {
+        pma::ProjArgs a{x, B * n, n, B, po, nblk, {o0, o1, o2}};
+        a.x_token_major = 0;   // caller tokens are batch-first
+        return a;
+    };
     if (!fused && query == key && key == value && L == S) {
-        pma::ProjArgs a{query, B * L, L, B, 0, 3, {oq, ok, ov}};
-        st = pma::launch_proj(a, E, p->dtype, stream);
+        st = pma::launch_proj(in_args(query, L, 3, oq, ok, ov), E, p->dtype, stream);
     } else {
-        if (!fused) {
-            pma::ProjArgs aq{query, B * L, L, B, 0, 1, {oq}};
-            st = pma::launch_proj(aq, E, p->dtype, stream);
-        }
+        if (!fused)
+            st = pma::launch_proj(in_args(query, L, 1, oq, oq, oq), E, p->dtype, stream);
         if (st == PMA_OK && key == value) {
-            pma::ProjArgs akv{key, B * S, S, B, 0, 2, {ok, ov}};
-            st = pma::launch_proj(akv, E, p->dtype, stream);
+            st = pma::launch_proj(in_args(key, S, 2, ok, ov, ov), E, p->dtype, stream);
         } else if (st == PMA_OK) {
-            pma::ProjArgs ak{key, B * S, S, B, 0, 1, {ok}};
-            st = pma::launch_proj(ak, E, p->dtype, stream);
-            if (st == PMA_OK) {
-                pma::ProjArgs av{value, B * S, S, B, 0, 1, {ov}};
-                st = pma::launch_proj(av, E, p->dtype, stream);
-            }
+            st = pma::launch_proj(in_args(key, S, 1, ok, ok, ok), E, p->dtype, stream);
+            if (st == PMA_OK)
+                st = pma::launch_proj(in_args(value, S, 1, ov, ov, ov), E, p->dtype, stream);
         }
     }
     tm.end();
@@ -434,6 +444,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.H = p->H;
     ea.nnz = p->nnz;
     ea.dt = p->dtype;
+    ea.lay = lay;
     ea.qt = p->qt;
     ea.kv = p->kv;
     ea.mixed = p->mixed;
@@ -505,7 +516,8 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     // Step 5: join heads (already contiguous) and out_proj, back to (B, L, E).
     tm.begin(PMA_STAGE_OUT);
     const pma::ProjOut oo{o_w, o_b, out, L * E, E};
-    pma::ProjArgs ao{p->mixed, L * B, L, B, 1, 1, {oo}};
+    pma::ProjArgs ao{p->mixed, L * B, L, B, p->out_order, 1, {oo}};
+    ao.x_token_major = lay.m_b == E ? 1 : 0;   // target-major or batch-first mixed
     st = pma::launch_proj(ao, E, p->dtype, stream);
     tm.end();
     if (st != PMA_OK)

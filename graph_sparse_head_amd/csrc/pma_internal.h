@@ -44,9 +44,12 @@ struct ProjOut {
     int64_t sb, si;  // element strides of the sample and token index
 };
 
-// Input rows are contiguous rows of E elements at x. Row r decomposes as
-//   token_major == 0:  r = b * n + i   (batch-first tokens)
-//   token_major == 1:  r = i * B + b   (the library's target-major layout)
+// Rows are visited in iteration order r = 0 .. rows-1, where r stands for
+// (sample b, token i) as
+//   token_major == 0:  r = b * n + i
+//   token_major == 1:  r = i * B + b
+// and the input row of (b, i) is x + (b * n + i) * E when x_token_major == 0
+// (batch-first tokens), x + (i * B + b) * E when 1 (target-major layout).
 struct ProjArgs {
     const void *x;
     int64_t rows;     // B * n
@@ -54,19 +57,32 @@ struct ProjArgs {
     int token_major;
     int nblk;         // 1..3 output blocks
     ProjOut out[3];
+    int x_token_major = -1;  // -1: same as token_major (rows read in storage order)
 };
 
 pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s);
 
 // ---- edge attention (edge.hip) -------------------------------------------
 
+// Element strides of the workspace tensors. Target-major: q and mixed
+// [L][B][E], keys and values [S][2][B][E] (one source's keys for all samples,
+// then its values). Batch-first: q and mixed [B][L][E], keys [B][S][E]
+// followed by values [B][S][E].
+struct Layout {
+    int64_t q_t, q_b;           // q row of (target t, sample b) at t*q_t + b*q_b
+    int64_t kv_s, kv_b, kv_v;   // key row of (source s, sample b) at s*kv_s + b*kv_b; values +kv_v
+    int64_t m_t, m_b;           // mixed row of (t, b) at t*m_t + b*m_b
+};
+Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E);
+
 struct EdgeArgs {
     const GraphDev *g;
     int64_t B, L, S, E, H, nnz;
     pma_dtype dt;
-    const void *qt;     // [L][B][E]
-    const void *kv;     // [S][2][B][E]: keys then values of one source
-    void *mixed;        // [L][B][E]
+    Layout lay;
+    const void *qt;     // q rows (layout lay)
+    const void *kv;     // key and value rows (layout lay)
+    void *mixed;        // mixed rows (layout lay)
     float *part_acc;    // [slot][B][E]
     float *part_ml;     // [slot][B][H][2]
     float *stat_ml;     // [L][B][H][2] final (max, sum) or nullptr

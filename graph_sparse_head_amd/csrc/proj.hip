@@ -19,15 +19,15 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
-__device__ inline uint16_t f2bf(float f)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pack_bf16(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ inline uint16_t f2bf(float f) { return (uint16_t)(pack_bf16(f, 0.f) & 0xffffu); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -38,6 +38,52 @@ template <> struct Elem<uint16_t> {
     static constexpr int kVec = 8;
     static constexpr int kStep = 32;
 };
+
+// Input row of iteration row r.
+__device__ inline int64_t in_row(const ProjArgs &a, int64_t r)
+{
+    if (a.x_token_major < 0 || a.x_token_major == a.token_major)
+        return r;
+    int64_t b, i;
+    if (a.token_major) {
+        i = r / a.B;
+        b = r - i * a.B;
+    } else {
+        b = r / a.n;
+        i = r - b * a.n;
+    }
+    return a.x_token_major ? i * a.B + b : b * a.n + i;
+}
+
+// (sample, token) of iteration row r
+__device__ inline void decompose(const ProjArgs &a, int64_t r, int64_t &b, int64_t &i)
+{
+    if (a.token_major) {
+        i = r / a.B;
+        b = r - i * a.B;
+    } else {
+        b = r / a.n;
+        i = r - b * a.n;
+    }
+}
+
+// (b, i) of iteration row r + step, from (b, i) of row r
+__device__ inline void advance(const ProjArgs &a, int64_t &b, int64_t &i, int step)
+{
+    if (a.token_major) {
+        b += step;
+        while (b >= a.B) {
+            b -= a.B;
+            ++i;
+        }
+    } else {
+        i += step;
+        while (i >= a.n) {
+            i -= a.n;
+            ++b;
+        }
+    }
+}
 
 __device__ inline int64_t out_offset(const ProjArgs &a, const ProjOut &o, uint32_t r)
 {
@@ -52,120 +98,147 @@ __device__ inline int64_t out_offset(const ProjArgs &a, const ProjOut &o, uint32
     return (int64_t)b * o.sb + (int64_t)i * o.si;
 }
 
-// One wave computes RG x 16 token rows for every output channel of every
-// block. Each block's tile goes through LDS so that the stores are whole
-// 16-byte chunks of whole rows (the destination rows of consecutive tokens
-// are far apart in the q / k / v layouts).
-template <typename T, int K, int RG>
-__global__ void __launch_bounds__(256) proj_mfma(ProjArgs a)
+// Persistent matrix-core projection. A workgroup of WAVES wavefronts first
+// copies the weight tiles of all its output blocks into LDS, laid out in
+// MFMA fragment order (one 1 KB fragment per (block, n-tile, k-step), lane l
+// at byte 16 l), so every later fragment read is one conflict-free 16-byte
+// LDS load. It then walks row tiles of WAVES x RG x 16 rows, stride gridDim.
+// Each wavefront keeps its rows' x fragments in registers and loads the next
+// tile's fragments before computing the current one. Every output block goes
+// through a per-wavefront LDS staging area so that stores are whole 16-byte
+// chunks of whole rows.
+template <typename T, int K, int RG, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
 {
     constexpr int NKS = K / Elem<T>::kStep;
     constexpr int E = K;
+    constexpr int NT = E / 16;
     constexpr int ROWS = RG * 16;
     constexpr int PITCH = E * (int)sizeof(T) + 16;       // bytes per staged row
     constexpr int CPR = E * (int)sizeof(T) / 16;         // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                        // rows stored per instruction
-    __shared__ __attribute__((aligned(16))) char stage_all[4][ROWS * PITCH];
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int nblk = a.nblk;
+    char *wl = lds;                                      // nblk * NT * NKS KB
+    char *stage = lds + nblk * NT * NKS * 1024 + (threadIdx.x >> 6) * (ROWS * PITCH);
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-    char *stage = stage_all[wid];
-    const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
-    const int64_t row0 = wave * ROWS;
-    if (row0 >= a.rows)
-        return;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // Token-row fragments: row (row0 + rg*16 + lr), k = ks*kStep + lg*kVec ..
-    uint4 xf[RG][NKS];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const int64_t r = row0 + rg * 16 + lr;
-        const T *xr = reinterpret_cast<const T *>(a.x) + r * E + lg * Elem<T>::kVec;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (r < a.rows)
-                xf[rg][ks] = *reinterpret_cast<const uint4 *>(xr + ks * Elem<T>::kStep);
-            else
-                xf[rg][ks] = make_uint4(0, 0, 0, 0);
-        }
+    // weights -> LDS in fragment order
+    const int nfrag_chunks = nblk * NT * NKS * 64;
+    for (int c = threadIdx.x; c < nfrag_chunks; c += WAVES * 64) {
+        const int f = c >> 6, l = c & 63;
+        const int ks = f % NKS, nt = (f / NKS) % NT, blk = f / (NKS * NT);
+        const T *W = reinterpret_cast<const T *>(a.out[blk].w);
+        const T *src = W + (int64_t)(nt * 16 + (l & 15)) * E + ks * Elem<T>::kStep +
+                       (l >> 4) * Elem<T>::kVec;
+        *reinterpret_cast<uint4 *>(wl + c * 16) = *reinterpret_cast<const uint4 *>(src);
     }
+    __syncthreads();
 
-    for (int blk = 0; blk < a.nblk; ++blk) {
-        const ProjOut &o = a.out[blk];
-        const T *W = reinterpret_cast<const T *>(o.w);
-        const T *bias = reinterpret_cast<const T *>(o.b);
-        for (int nt = 0; nt < E / 16; ++nt) {
-            uint4 wf[NKS];
-            const T *wr = W + (int64_t)(nt * 16 + lr) * E + lg * Elem<T>::kVec;
+    const int64_t tile_rows = (int64_t)WAVES * ROWS;
+    const int64_t ntiles = (a.rows + tile_rows - 1) / tile_rows;
+    uint4 xf[RG][NKS], xn[RG][NKS];
+    auto load_x = [&](int64_t tile, uint4 (&dst)[RG][NKS]) {
+        const int64_t row0 = tile * tile_rows + wid * ROWS;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            const int64_t r = row0 + rg * 16 + lr;
+            const T *xr = reinterpret_cast<const T *>(a.x) + in_row(a, r < a.rows ? r : 0) * E +
+                          lg * Elem<T>::kVec;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                wf[ks] = *reinterpret_cast<const uint4 *>(wr + ks * Elem<T>::kStep);
-            f32x4 acc[RG];
+                dst[rg][ks] = *reinterpret_cast<const uint4 *>(xr + ks * Elem<T>::kStep);
+        }
+    };
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles)
+        load_x(tile, xf);
+    for (; tile < ntiles; tile += gridDim.x) {
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles)
+            load_x(next, xn);
+        const int64_t row0 = tile * tile_rows + wid * ROWS;
+        // (sample, token) of this lane's first stored row, once per tile
+        const int cr = lane % CPR, rr = lane / CPR;
+        int64_t sb0, si0;
+        decompose(a, row0 + rr, sb0, si0);
+        for (int blk = 0; blk < nblk; ++blk) {
+            const ProjOut &o = a.out[blk];
+            const T *bias = reinterpret_cast<const T *>(o.b);
+#pragma unroll 2
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 acc[RG];
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
-                acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int rg = 0; rg < RG; ++rg)
+                    acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const uint4 wf = *reinterpret_cast<const uint4 *>(
+                        wl + (((blk * NT + nt) * NKS + ks) * 64 + lane) * 16);
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg) {
+                        if constexpr (sizeof(T) == 2) {
+                            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, wf), __builtin_bit_cast(bf16x8, xf[rg][ks]),
+                                acc[rg], 0, 0, 0);
+                        } else {
+                            const float *wv = reinterpret_cast<const float *>(&wf);
+                            const float *xv = reinterpret_cast<const float *>(&xf[rg][ks]);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                acc[rg] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[j], xv[j], acc[rg], 0, 0, 0);
+                        }
+                    }
+                }
+                // lane holds channels n = nt*16 + 4*lg + i of row (rg*16 + lr)
+                const int n = nt * 16 + 4 * lg;
+                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (bias) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (sizeof(T) == 2)
+                            bv[i] = bf2f(bias[n + i]);
+                        else
+                            bv[i] = bias[n + i];
+                    }
+                }
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
+                    char *d = stage + (rg * 16 + lr) * PITCH + n * (int)sizeof(T);
                     if constexpr (sizeof(T) == 2) {
-                        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, wf[ks]), __builtin_bit_cast(bf16x8, xf[rg][ks]),
-                            acc[rg], 0, 0, 0);
+                        uint2 pk;
+                        pk.x = pack_bf16(acc[rg][0] + bv[0], acc[rg][1] + bv[1]);
+                        pk.y = pack_bf16(acc[rg][2] + bv[2], acc[rg][3] + bv[3]);
+                        *reinterpret_cast<uint2 *>(d) = pk;
                     } else {
-                        const float *wv = reinterpret_cast<const float *>(&wf[ks]);
-                        const float *xv = reinterpret_cast<const float *>(&xf[rg][ks]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[rg] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[j], xv[j], acc[rg], 0, 0, 0);
+                        *reinterpret_cast<float4 *>(d) = make_float4(
+                            acc[rg][0] + bv[0], acc[rg][1] + bv[1], acc[rg][2] + bv[2], acc[rg][3] + bv[3]);
                     }
                 }
             }
-            // lane holds channels n = nt*16 + 4*lg + i of token row (rg*16 + lr)
-            const int n = nt * 16 + 4 * lg;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) {
+            // a wavefront reads back only its own staged rows (LDS operations
+            // of one wavefront complete in order)
+            T *dst = reinterpret_cast<T *>(o.dst) + cr * (16 / (int)sizeof(T));
+            int64_t sb = sb0, si = si0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if constexpr (sizeof(T) == 2)
-                        bv[i] = bf2f(bias[n + i]);
-                    else
-                        bv[i] = bias[n + i];
+            for (int it = 0; it < ROWS / RPI; ++it) {
+                const int lrow = it * RPI + rr;
+                const int64_t r = row0 + lrow;
+                if (r < a.rows) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(stage + lrow * PITCH + cr * 16);
+                    *reinterpret_cast<uint4 *>(dst + sb * o.sb + si * o.si) = v;
                 }
-            }
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
-                char *d = stage + (rg * 16 + lr) * PITCH + n * (int)sizeof(T);
-                if constexpr (sizeof(T) == 2) {
-                    uint2 pk;
-                    pk.x = (uint32_t)f2bf(acc[rg][0] + bv[0]) | ((uint32_t)f2bf(acc[rg][1] + bv[1]) << 16);
-                    pk.y = (uint32_t)f2bf(acc[rg][2] + bv[2]) | ((uint32_t)f2bf(acc[rg][3] + bv[3]) << 16);
-                    *reinterpret_cast<uint2 *>(d) = pk;
-                } else {
-                    *reinterpret_cast<float4 *>(d) = make_float4(
-                        acc[rg][0] + bv[0], acc[rg][1] + bv[1], acc[rg][2] + bv[2], acc[rg][3] + bv[3]);
-                }
+                advance(a, sb, si, RPI);
             }
         }
-        // the wave reads back its own staged rows: no cross-wave sharing
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        T *dst = reinterpret_cast<T *>(o.dst);
-        const int cr = lane % CPR, rr = lane / CPR;
+        if (next < ntiles) {
 #pragma unroll
-        for (int it = 0; it < ROWS / RPI; ++it) {
-            const int lrow = it * RPI + rr;
-            const int64_t r = row0 + lrow;
-            if (r < a.rows) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(stage + lrow * PITCH + cr * 16);
-                T *dp = dst + out_offset(a, o, (uint32_t)r) + cr * (16 / (int)sizeof(T));
-                *reinterpret_cast<uint4 *>(dp) = v;
-            }
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) xf[rg][ks] = xn[rg][ks];
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -178,7 +251,7 @@ __global__ void __launch_bounds__(256) proj_generic(ProjArgs a, int E)
     const int o = (int)(idx - r * E);
     if (r >= a.rows)
         return;
-    const T *x = reinterpret_cast<const T *>(a.x) + r * E;
+    const T *x = reinterpret_cast<const T *>(a.x) + in_row(a, r) * E;
     for (int blk = 0; blk < a.nblk; ++blk) {
         const ProjOut &po = a.out[blk];
         const T *w = reinterpret_cast<const T *>(po.w) + (int64_t)o * E;
@@ -203,12 +276,60 @@ __global__ void __launch_bounds__(256) proj_generic(ProjArgs a, int E)
     }
 }
 
-template <typename T, int K, int RG>
+int cu_count()
+{
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+constexpr int kLdsBytes = 160 * 1024;
+
+template <typename T, int K, int RG, int WAVES>
 hipError_t run_mfma(const ProjArgs &a, hipStream_t s)
 {
-    const int64_t waves = (a.rows + RG * 16 - 1) / (RG * 16);
-    const unsigned blocks = (unsigned)((waves + 3) / 4);
-    proj_mfma<T, K, RG><<<blocks, 256, 0, s>>>(a);
+    constexpr int NKS = K / Elem<T>::kStep;
+    constexpr int PITCH = K * (int)sizeof(T) + 16;
+    const size_t wbytes = (size_t)a.nblk * (K / 16) * NKS * 1024;
+    const size_t lds = wbytes + (size_t)WAVES * RG * 16 * PITCH;
+    if (lds > (size_t)kLdsBytes) {
+        // weights of all blocks do not fit: one launch per output block
+        for (int j = 0; j < a.nblk; ++j) {
+            ProjArgs one = a;
+            one.nblk = 1;
+            one.out[0] = a.out[j];
+            hipError_t e = run_mfma<T, K, RG, WAVES>(one, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    const int64_t tile_rows = (int64_t)WAVES * RG * 16;
+    const int64_t ntiles = (a.rows + tile_rows - 1) / tile_rows;
+    const int per_cu = (int)(kLdsBytes / lds) < 4 ? (int)(kLdsBytes / lds) : 4;
+    int64_t grid = (int64_t)cu_count() * (per_cu > 0 ? per_cu : 1);
+    if (grid > ntiles)
+        grid = ntiles;
+    if (lds > 64 * 1024) {
+        static bool raised = false;   // once per instantiation
+        if (!raised) {
+            hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&proj_mfma<T, K, RG, WAVES>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+            if (e != hipSuccess)
+                return e;
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL((proj_mfma<T, K, RG, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64),
+                       lds, s, a);
     return hipGetLastError();
 }
 
@@ -236,16 +357,16 @@ pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s
         e = dt == PMA_BF16 ? run_generic<uint16_t>(a, E, s) : run_generic<float>(a, E, s);
     } else if (dt == PMA_BF16) {
         if (E == 64)
-            e = run_mfma<uint16_t, 64, 4>(a, s);
+            e = run_mfma<uint16_t, 64, 1, 8>(a, s);
         else if (E == 128)
-            e = run_mfma<uint16_t, 128, 2>(a, s);
+            e = run_mfma<uint16_t, 128, 1, 8>(a, s);
         else
             e = run_generic<uint16_t>(a, E, s);
     } else {
         if (E == 64)
-            e = run_mfma<float, 64, 2>(a, s);
+            e = run_mfma<float, 64, 1, 8>(a, s);
         else if (E == 128)
-            e = run_mfma<float, 128, 1>(a, s);
+            e = run_mfma<float, 128, 1, 8>(a, s);
         else
             e = run_generic<float>(a, E, s);
     }
