@@ -36,6 +36,8 @@ struct EdgeK {
     int B, E, H, d;
     int64_t nnz;
     int passes;          // wavefronts per piece (sample groups)
+    int xcd_map;         // 1: sample group fixed per XCD (passes divides 8)
+    int nt;              // 1: non-temporal q loads and mixed stores
     float scale;         // log2(e) / sqrt(d)
     Layout lay;
     const void *qt, *kv;
@@ -48,6 +50,17 @@ __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h <<
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+__device__ inline uint4 load_nt(const void *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void store_nt(void *p, const uint4 &u)
+{
+    __builtin_nontemporal_store(u32x4_t{u.x, u.y, u.z, u.w}, reinterpret_cast<u32x4_t *>(p));
+}
 
 // two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ inline uint32_t pack_bf16(float lo, float hi)
@@ -98,18 +111,22 @@ template <typename T, int CH> struct Chunk {
     }
 };
 
-template <typename T, int CH> __device__ inline void store_chunk(T *p, const float *v)
+template <typename T, int CH> __device__ inline void store_chunk(T *p, const float *v, bool nt = false)
 {
+    uint4 u;
     if constexpr (sizeof(T) == 4) {
-        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        u = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                       __float_as_uint(v[3]));
     } else {
-        uint4 u;
         u.x = pack_bf16(v[0], v[1]);
         u.y = pack_bf16(v[2], v[3]);
         u.z = pack_bf16(v[4], v[5]);
         u.w = pack_bf16(v[6], v[7]);
-        *reinterpret_cast<uint4 *>(p) = u;
     }
+    if (nt)
+        store_nt(p, u);
+    else
+        *reinterpret_cast<uint4 *>(p) = u;
 }
 
 // Fast path: d = CH * LPH with 16-byte chunks. U edges per step.
@@ -125,11 +142,24 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     constexpr bool BF = sizeof(T) == 2;
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (unit >= a.n_tasks * a.passes)
-        return;
-    const int64_t task = unit / a.passes;
-    const int pass = (int)(unit - task * a.passes);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t task;
+    int pass;
+    if (a.xcd_map) {
+        // Workgroups are dealt to the 8 XCDs round-robin; XCD x serves sample
+        // group x % passes, so its L2 caches only that group's key/value rows.
+        const int x = blockIdx.x & 7, per = 8 / a.passes;
+        pass = x % a.passes;
+        task = ((int64_t)(blockIdx.x >> 3) * per + x / a.passes) * 4 + wave;
+        if (task >= a.n_tasks)
+            return;
+    } else {
+        const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
+        if (unit >= a.n_tasks * a.passes)
+            return;
+        task = unit / a.passes;
+        pass = (int)(unit - task * a.passes);
+    }
     const int t = a.task_target[task];
     const int beg = a.task_begin[task], end = a.task_end[task];
     const int slot = a.task_slot[task];
@@ -146,7 +176,10 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
 
     const T *qt = reinterpret_cast<const T *>(a.qt);
     Chunk<T, CH> q;
-    q.load(qt + t * a.lay.q_t + b * a.lay.q_b + col);
+    {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(qt + t * a.lay.q_t + b * a.lay.q_b + col);
+        q.u = a.nt ? load_nt(qp) : *qp;
+    }
     float qf[BF ? 1 : CH];
     if constexpr (!BF) {
 #pragma unroll
@@ -221,7 +254,8 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
         float out[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
-        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
+        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out,
+                           a.nt != 0);
         if (a.stat_ml && head_lead) {
             float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
             st[0] = m;
@@ -424,6 +458,8 @@ EdgeK make_k(const EdgeArgs &x)
     k.d = (int)(x.E / x.H);
     k.nnz = x.nnz;
     k.passes = 1;
+    k.xcd_map = x.xcd_map;
+    k.nt = x.nt;
     k.scale = (float)(1.4426950408889634 / sqrt((double)k.d));
     k.lay = x.lay;
     k.qt = x.qt;
@@ -443,8 +479,14 @@ hipError_t run_fast(EdgeK k, int unroll, hipStream_t s)
 {
     const int64_t chunks = (int64_t)k.B * (k.E / CH);
     k.passes = (int)((chunks + 63) / 64);
-    const int64_t units = k.n_tasks * k.passes;
-    const unsigned blocks = (unsigned)((units + 3) / 4);
+    unsigned blocks;
+    if (k.xcd_map && 8 % k.passes == 0) {
+        const int64_t per = 8 / k.passes;                       // workgroups per pass per round
+        blocks = (unsigned)(8 * ((k.n_tasks + 4 * per - 1) / (4 * per)));
+    } else {
+        k.xcd_map = 0;
+        blocks = (unsigned)((k.n_tasks * k.passes + 3) / 4);
+    }
     if (unroll == 8)
         edge_fast<T, CH, LPH, 8><<<blocks, 256, 0, s>>>(k);
     else

@@ -46,6 +46,8 @@ struct pma_plan {
     int proj_order = 0;         // PMA_PROJ_ORDER: q/k/v rows visited batch- (0) or token-major (1)
     int out_order = 1;          // PMA_OUT_ORDER: out_proj rows visited batch- (0) or token-major (1)
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
+    int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
+    int nt = 1;                 // PMA_NT=0: cached q loads / mixed stores
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
     // workspace, grown on demand
@@ -237,6 +239,10 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     }
     if (const char *ev = getenv("PMA_FUSED"))
         p->use_fused = ev[0] == '1';
+    if (const char *ev = getenv("PMA_XCD_MAP"))
+        p->xcd_map = ev[0] == '0' ? 0 : 1;
+    if (const char *ev = getenv("PMA_NT"))
+        p->nt = ev[0] != '0';
     if (const char *ev = getenv("PMA_LAYOUT"))
         p->batch_first_ws = strcmp(ev, "batch") == 0;
     if (const char *ev = getenv("PMA_PROJ_ORDER"))
@@ -455,6 +461,12 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.weights = weights;
     ea.average = average_attn_weights;
     ea.unroll = p->edge_unroll;
+    // Pinning sample groups to XCDs splits each source's key/value row across
+    // the L2s; it pays once the keys and values outgrow the 256 MB last-level
+    // cache (measured: large and bipartite workloads gain, the gene one loses).
+    ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map
+                                 : (2.0 * S * B * E * es > 256.0 * 1024 * 1024 ? 1 : 0);
+    ea.nt = p->nt;
 
     if (fused) {
         // Steps 1 (queries) to 5 in one kernel.

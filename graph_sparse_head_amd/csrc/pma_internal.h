@@ -90,6 +90,8 @@ struct EdgeArgs {
     float *weights;     // caller's weights or nullptr
     int average;
     int unroll = 4;     // edges per step of edge_fast (4 or 8)
+    int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
+    int nt = 1;         // non-temporal q loads / mixed stores
 };
 
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
