@@ -26,9 +26,15 @@ FLAGS = [
 ]
 
 
+# Per-file options. The edge kernels keep matrix-core accumulators in
+# ordinary VGPRs, so the fused out_proj epilogue does not raise the register
+# count (and lower the occupancy) of the latency-bound gather loop.
+EXTRA = {"edge.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln)

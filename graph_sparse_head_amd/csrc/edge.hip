@@ -41,9 +41,14 @@ struct EdgeK {
     float scale;         // log2(e) / sqrt(d)
     Layout lay;
     const void *qt, *kv;
+    uint64_t kv_bytes;   // size of the key/value workspace
     void *mixed;
     float *part_acc, *part_ml, *stat_ml, *scores, *weights;
     int average;
+    // out_proj in the epilogue (fuse_out): caller's Wo, bo, out (B, L, E)
+    int fuse_out, L;
+    const void *wo, *bo;
+    void *out;
 };
 
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -129,18 +134,225 @@ template <typename T, int CH> __device__ inline void store_chunk(T *p, const flo
         *reinterpret_cast<uint4 *>(p) = u;
 }
 
-// Fast path: d = CH * LPH with 16-byte chunks. U edges per step.
-//
-// Per edge the source's row base is wave-uniform (scalar registers) and each
-// lane adds a fixed 32-bit byte offset, so the gather costs no vector
-// address arithmetic. Lanes past the last chunk read lane 0's address and
-// discard the data. bf16 scores use v_dot2 on the stored bf16 q and k words
-// (fp32 products and sums) and are scaled afterwards.
-template <typename T, int CH, int LPH, int U>
-__global__ void __launch_bounds__(256) edge_fast(EdgeK a)
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// out = mixed Wo^T + bo (kpnn2 page, "Notes" step 5) for the samples of one
+// wavefront, straight from edge_fast's lane layout (lane = sample * CPR +
+// chunk, chunk = CH channels of mixed). MFMA 16x16 tiles: the A operand is
+// Wo, the B operand mixed^T with one column per sample. At k-step ks, lane
+// group g feeds chunk 4 ks + g of sample l % 16, fetched from its owner lane
+// with ds_bpermute; Wo is read in the same (natural) channel order. Row r of
+// n-tile nt is output channel (E/4)(r/4) + 4 nt + r%4, so each lane ends with
+// E/4 contiguous output channels of one sample and stores whole 16-byte words.
+// Wo as MFMA A fragments in LDS: fragment (n-tile nt, k-group kg) is 64
+// lanes x 16 bytes at byte ((nt * KG + kg) * 64 + lane) * 16, lane l holding
+// output channel (E/4)(l%16 / 4) + 4 nt + l%4 at channels (4 kg + l/16) * CH.
+template <typename T, int CH, int E>
+__device__ inline void stage_wo(const EdgeK &a, char *wlds)
 {
+    constexpr int KG = E / (4 * CH), NT = E / 16, CPL = E / 4;
+    const T *W = reinterpret_cast<const T *>(a.wo);
+    for (int f = threadIdx.x; f < NT * KG * 64; f += blockDim.x) {
+        const int lane = f & 63, fk = f >> 6, kg = fk % KG, nt = fk / KG;
+        const int n = lane & 15, g = lane >> 4;
+        const int orow = CPL * (n >> 2) + 4 * nt + (n & 3);
+        *reinterpret_cast<uint4 *>(wlds + f * 16) =
+            *reinterpret_cast<const uint4 *>(W + orow * E + (4 * kg + g) * CH);
+    }
+    // bias as fp32 after the fragments (zeros without bias)
+    float *bl = reinterpret_cast<float *>(wlds + NT * KG * 64 * 16);
+    const T *bias = reinterpret_cast<const T *>(a.bo);
+    for (int c = threadIdx.x; c < E; c += blockDim.x) {
+        float v = 0.f;
+        if (bias) {
+            if constexpr (sizeof(T) == 2)
+                v = bf2f(bias[c]);
+            else
+                v = bias[c];
+        }
+        bl[c] = v;
+    }
+}
+
+template <typename T, int CH, int E>
+__device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane, int t,
+                                     int b_first, const char *wlds)
+{
+    constexpr int CPR = E / CH;     // chunks per sample row
+    constexpr int SPW = 64 / CPR;   // samples per wavefront
+    constexpr int NT = E / 16;
+    constexpr int CPL = E / 4;      // output channels per lane
+    const int n = lane & 15, g = lane >> 4;
+    const bool has = n < SPW;
+    uint32_t w[4];                  // this lane's mixed chunk as 16 bytes of T
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16(mix[2 * j], mix[2 * j + 1]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(mix[j]);
+    }
+    // k-groups: 32 channels (bf16) or 16 channels (fp32) per group
+    constexpr int KG = E / (4 * CH);
+    uint32_t bw[KG][4];
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+        const int src = has ? n * CPR + 4 * kg + g : lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int v = __builtin_amdgcn_ds_bpermute(src << 2, (int)w[j]);
+            bw[kg][j] = has ? (uint32_t)v : 0u;
+        }
+    }
+    const int b = b_first + n;
+    const float *bl = reinterpret_cast<const float *>(wlds + NT * KG * 64 * 16);
+    // one n-tile at a time; results packed into T words as they are made
+    constexpr int OW = CPL * (int)sizeof(T) / 4;   // 32-bit words of this lane's output
+    uint32_t ow[OW];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const float4 b4 = *reinterpret_cast<const float4 *>(bl + CPL * g + 4 * nt);
+        f32x4_t acc = {b4.x, b4.y, b4.z, b4.w};   // bias first
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg) {
+            const uint4 wa = *reinterpret_cast<const uint4 *>(wlds + ((nt * KG + kg) * 64 + lane) * 16);
+            if constexpr (sizeof(T) == 2) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, wa),
+                    __builtin_bit_cast(bf16x8_t, make_uint4(bw[kg][0], bw[kg][1], bw[kg][2], bw[kg][3])),
+                    acc, 0, 0, 0);
+            } else {
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wa.x), __uint_as_float(bw[kg][0]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wa.y), __uint_as_float(bw[kg][1]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wa.z), __uint_as_float(bw[kg][2]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(wa.w), __uint_as_float(bw[kg][3]), acc, 0, 0, 0);
+            }
+        }
+        float o[4] = {acc[0], acc[1], acc[2], acc[3]};
+        if constexpr (sizeof(T) == 2) {
+            ow[2 * nt] = pack_bf16(o[0], o[1]);
+            ow[2 * nt + 1] = pack_bf16(o[2], o[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ow[4 * nt + i] = __float_as_uint(o[i]);
+        }
+    }
+    if (!has || b >= a.B)
+        return;
+    char *dst = reinterpret_cast<char *>(reinterpret_cast<T *>(a.out) + ((int64_t)b * a.L + t) * E + CPL * g);
+#pragma unroll
+    for (int k = 0; k < OW / 4; ++k) {
+        const uint4 v = make_uint4(ow[4 * k], ow[4 * k + 1], ow[4 * k + 2], ow[4 * k + 3]);
+        if (a.nt)
+            store_nt(dst + 16 * k, v);
+        else
+            *reinterpret_cast<uint4 *>(dst + 16 * k) = v;
+    }
+}
+
+// Fast path: d = CH * LPH with 16-byte chunks.
+//
+// Per edge the source's key/value row offset is wave-uniform: one scalar
+// multiply gives it, and each lane adds its fixed offset inside the row. When
+// the key/value workspace is under 4 GiB the gathers are buffer loads whose
+// scalar offset is that product (no vector address arithmetic; a read past
+// the buffer returns zeros instead of faulting); otherwise they are global
+// loads from a uniform 64-bit base. Lanes past the last chunk read lane 0's
+// address and discard the data. bf16 scores use v_dot2 on the stored bf16 q
+// and k words (fp32 products and sums) and are scaled afterwards. Edges run U
+// at a time, the remainder one at a time.
+template <typename T, int CH, int LPH, bool BUF> struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    constexpr bool BF = sizeof(T) == 2;
+    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+    static constexpr bool BF = sizeof(T) == 2;
+
+    const EdgeK &a;
+    int B, b, h;
+    bool active, head_lead;
+    Chunk<T, CH> q;
+    float qf[BF ? 1 : CH];
+    float m = -INFINITY, l = 0.f, acc[CH];
+    const char *kvb;
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint64_t row2, loff, vloff;
+
+    __device__ EdgeLane(const EdgeK &a_) : a(a_) {}
+
+    __device__ inline void gather(int s, Chunk<T, CH> &k, Chunk<T, CH> &v) const
+    {
+        if constexpr (BUF) {
+            const uint32_t so = (uint32_t)s * (uint32_t)row2;   // uniform
+            const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)loff, so, 0);
+            const u32x4 vw = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)vloff, so, 0);
+            k.u = make_uint4(kw.x, kw.y, kw.z, kw.w);
+            v.u = make_uint4(vw.x, vw.y, vw.z, vw.w);
+        } else {
+            const char *base = kvb + (uint64_t)s * row2;        // uniform
+            k.u = *reinterpret_cast<const uint4 *>(base + loff);
+            v.u = *reinterpret_cast<const uint4 *>(base + vloff);
+        }
+    }
+
+    // N edges starting at CSR position p, all of them live
+    template <int N> __device__ inline void step(int p)
+    {
+        Chunk<T, CH> kk[N], vv[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u) gather(a.csr_src[p + u], kk[u], vv[u]);
+        float sc[N];
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            float dot = 0.f;
+            if constexpr (BF) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.word(k)),
+                                                          __builtin_bit_cast(bf16x2, kk[u].word(k)),
+                                                          dot, false);
+            } else {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) dot = fmaf(qf[i], kk[u][i], dot);
+            }
+            dot = group_sum<LPH>(dot);
+            if constexpr (BF) dot *= a.scale;
+            sc[u] = dot;
+        }
+        if (a.scores && active && head_lead) {
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                a.scores[(((int64_t)(p + u)) * B + b) * a.H + h] = sc[u];
+        }
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < N; ++u) mx = fmaxf(mx, sc[u]);
+        const float alpha = fast_exp2(m - mx);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const float pe = fast_exp2(sc[u] - mx);
+            l += pe;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u][i], acc[i]);
+        }
+        m = mx;
+    }
+};
+
+template <typename T, int CH, int LPH, int U, int E_FUSE, bool BUF>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(E_FUSE != 128 ? 8 : 1)))   // 64 VGPRs, no spill
+edge_fast(EdgeK a)
+{
+    __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? E_FUSE * E_FUSE * sizeof(T) + 4 * E_FUSE : 16];
+    if constexpr (E_FUSE > 0) {
+        if (a.fuse_out) {   // uniform over the launch; before any wavefront exits
+            stage_wo<T, CH, E_FUSE>(a, wlds);
+            __syncthreads();
+        }
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t task;
@@ -164,110 +376,73 @@ __global__ void __launch_bounds__(256) edge_fast(EdgeK a)
     const int beg = a.task_begin[task], end = a.task_end[task];
     const int slot = a.task_slot[task];
 
+    EdgeLane<T, CH, LPH, BUF> st(a);
     const int B = a.B, E = a.E;
     const int cpr = E / CH;                       // chunks per sample row
     const int c = pass * 64 + lane;
-    const bool active = c < B * cpr;
-    const int b = active ? c / cpr : 0;
+    st.B = B;
+    st.active = c < B * cpr;
+    const int b = st.active ? c / cpr : 0;
     const int cr = c - b * cpr;
-    const int col = active ? cr * CH : 0;
-    const int h = active ? cr / LPH : 0;
-    const bool head_lead = (lane % LPH) == 0;
+    const int col = st.active ? cr * CH : 0;
+    st.b = b;
+    st.h = st.active ? cr / LPH : 0;
+    st.head_lead = (lane % LPH) == 0;
 
     const T *qt = reinterpret_cast<const T *>(a.qt);
-    Chunk<T, CH> q;
     {
         const uint4 *qp = reinterpret_cast<const uint4 *>(qt + t * a.lay.q_t + b * a.lay.q_b + col);
-        q.u = a.nt ? load_nt(qp) : *qp;
+        st.q.u = a.nt ? load_nt(qp) : *qp;
     }
-    float qf[BF ? 1 : CH];
-    if constexpr (!BF) {
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) qf[i] = q[i] * a.scale;
+        for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
     }
+    // byte offsets: per source (uniform), this lane's key and value chunks
+    st.row2 = (uint64_t)a.lay.kv_s * sizeof(T);
+    st.loff = (uint64_t)(b * a.lay.kv_b + col) * sizeof(T);
+    st.vloff = st.loff + (uint64_t)a.lay.kv_v * sizeof(T);
+    st.kvb = reinterpret_cast<const char *>(a.kv);
+    if constexpr (BUF)
+        st.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.kv), (short)0,
+                                                    (int)(uint32_t)a.kv_bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
 
-    // byte offsets: per source (uniform), values, this lane
-    const uint64_t row2 = (uint64_t)a.lay.kv_s * sizeof(T);
-    const uint64_t voff = (uint64_t)a.lay.kv_v * sizeof(T);
-    const uint64_t loff = (uint64_t)(b * a.lay.kv_b + col) * sizeof(T);
-    const char *kvb = reinterpret_cast<const char *>(a.kv);
+    int p = beg;
+    for (; p + U <= end; p += U)
+        st.template step<U>(p);
+    for (; p < end; ++p)
+        st.template step<1>(p);
 
-    float m = -INFINITY, l = 0.f;
-    float acc[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) acc[i] = 0.f;
-
-    for (int p = beg; p < end; p += U) {
-        const int n = end - p < U ? end - p : U;
-        Chunk<T, CH> kk[U], vv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int s = a.csr_src[p + u];                   // padded past nnz
-            const char *base = kvb + (uint64_t)s * row2;      // uniform
-            kk[u].u = *reinterpret_cast<const uint4 *>(base + loff);
-            vv[u].u = *reinterpret_cast<const uint4 *>(base + voff + loff);
-        }
-        float sc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float dot = 0.f;
-            if constexpr (BF) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.word(k)),
-                                                          __builtin_bit_cast(bf16x2, kk[u].word(k)),
-                                                          dot, false);
-            } else {
-#pragma unroll
-                for (int i = 0; i < CH; ++i) dot = fmaf(qf[i], kk[u][i], dot);
-            }
-            dot = group_sum<LPH>(dot);
-            if constexpr (BF) dot *= a.scale;
-            sc[u] = u < n ? dot : -INFINITY;
-        }
-        if (a.scores && active && head_lead) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (u < n)
-                    a.scores[(((int64_t)(p + u)) * B + b) * a.H + h] = sc[u];
-        }
-        float mx = m;
-#pragma unroll
-        for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u]);
-        const float alpha = fast_exp2(m - mx);
-        l *= alpha;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) acc[i] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float pe = fast_exp2(sc[u] - mx);
-            l += pe;
-#pragma unroll
-            for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u][i], acc[i]);
-        }
-        m = mx;
-    }
-
-    if (!active)
-        return;
+    const float m = st.m, l = st.l;
     if (slot < 0) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
         float out[CH];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
-        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out,
-                           a.nt != 0);
-        if (a.stat_ml && head_lead) {
-            float *st = a.stat_ml + (((int64_t)t * B + b) * a.H + h) * 2;
-            st[0] = m;
-            st[1] = l;
+        for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
+        if (st.active && a.stat_ml && st.head_lead) {
+            float *sp = a.stat_ml + (((int64_t)t * B + b) * a.H + st.h) * 2;
+            sp[0] = m;
+            sp[1] = l;
         }
-    } else {
+        if constexpr (E_FUSE > 0) {
+            if (a.fuse_out) {   // wave-uniform
+                out_proj_wave<T, CH, E_FUSE>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+                return;
+            }
+        }
+        if (st.active)
+            store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col,
+                               out, a.nt != 0);
+    } else if (st.active) {
         float *pa = a.part_acc + ((int64_t)slot * B + b) * E + col;
-        *reinterpret_cast<float4 *>(pa) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
         if constexpr (CH == 8)
-            *reinterpret_cast<float4 *>(pa + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        if (head_lead) {
-            float *pm = a.part_ml + (((int64_t)slot * B + b) * a.H + h) * 2;
+            *reinterpret_cast<float4 *>(pa + 4) =
+                make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
+        if (st.head_lead) {
+            float *pm = a.part_ml + (((int64_t)slot * B + b) * a.H + st.h) * 2;
             pm[0] = m;
             pm[1] = l;
         }
@@ -331,9 +506,16 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
 
 // Merge the pieces of each split target, in piece order. Same lane layout
 // as edge_fast: one wavefront per (split target, sample group).
-template <typename T, int CH, int LPH>
+template <typename T, int CH, int LPH, int E_FUSE>
 __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
 {
+    __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? E_FUSE * E_FUSE * sizeof(T) + 4 * E_FUSE : 16];
+    if constexpr (E_FUSE > 0) {
+        if (a.fuse_out) {
+            stage_wo<T, CH, E_FUSE>(a, wlds);
+            __syncthreads();
+        }
+    }
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (unit >= a.n_split * a.passes)
@@ -343,10 +525,10 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
     const int B = a.B, E = a.E, H = a.H;
     const int cpr = E / CH;
     const int c = pass * 64 + lane;
-    if (c >= B * cpr)
-        return;
-    const int b = c / cpr, cr = c - b * cpr, col = cr * CH, h = cr / LPH;
-    const int t = a.split_target[k], s0 = a.split_slot0[k], n = a.split_count[k];
+    const bool active = c < B * cpr;
+    const int b = active ? c / cpr : 0, cr = c - b * cpr, col = active ? cr * CH : 0;
+    const int h = active ? cr / LPH : 0;
+    const int t = a.split_target[k], s0 = a.split_slot0[k], n = active ? a.split_count[k] : 0;
     float M = -INFINITY;
     for (int j = 0; j < n; ++j)
         M = fmaxf(M, a.part_ml[(((int64_t)(s0 + j) * B + b) * H + h) * 2]);
@@ -372,12 +554,19 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
     float out[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
-    store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
-    if (a.stat_ml && (lane % LPH) == 0) {
+    if (active && a.stat_ml && (lane % LPH) == 0) {
         float *st = a.stat_ml + (((int64_t)t * B + b) * H + h) * 2;
         st[0] = M;
         st[1] = l;
     }
+    if constexpr (E_FUSE > 0) {
+        if (a.fuse_out) {
+            out_proj_wave<T, CH, E_FUSE>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+            return;
+        }
+    }
+    if (active)
+        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
 }
 
 // Any head size: one thread per (split target, sample, channel).
@@ -460,8 +649,14 @@ EdgeK make_k(const EdgeArgs &x)
     k.passes = 1;
     k.xcd_map = x.xcd_map;
     k.nt = x.nt;
+    k.fuse_out = x.fuse_out;
+    k.L = (int)x.L;
+    k.wo = x.wo;
+    k.bo = x.bo;
+    k.out = x.out;
     k.scale = (float)(1.4426950408889634 / sqrt((double)k.d));
     k.lay = x.lay;
+    k.kv_bytes = x.kv_bytes;
     k.qt = x.qt;
     k.kv = x.kv;
     k.mixed = x.mixed;
@@ -474,9 +669,10 @@ EdgeK make_k(const EdgeArgs &x)
     return k;
 }
 
-template <typename T, int CH, int LPH>
+template <typename T, int CH, int LPH, int E_FUSE>
 hipError_t run_fast(EdgeK k, int unroll, hipStream_t s)
 {
+    (void)unroll;
     const int64_t chunks = (int64_t)k.B * (k.E / CH);
     k.passes = (int)((chunks + 63) / 64);
     unsigned blocks;
@@ -487,11 +683,32 @@ hipError_t run_fast(EdgeK k, int unroll, hipStream_t s)
         k.xcd_map = 0;
         blocks = (unsigned)((k.n_tasks * k.passes + 3) / 4);
     }
-    if (unroll == 8)
-        edge_fast<T, CH, LPH, 8><<<blocks, 256, 0, s>>>(k);
+    if (k.kv_bytes < ((uint64_t)1 << 31))
+        edge_fast<T, CH, LPH, 4, E_FUSE, true><<<blocks, 256, 0, s>>>(k);
     else
-        edge_fast<T, CH, LPH, 4><<<blocks, 256, 0, s>>>(k);
+        edge_fast<T, CH, LPH, 4, E_FUSE, false><<<blocks, 256, 0, s>>>(k);
     return hipGetLastError();
+}
+
+// out_proj can run in the edge kernel's epilogue when a wavefront holds at
+// least 4 samples' rows (E / CH <= 16 chunks per row) and E is 64 or 128.
+template <typename T, int CH>
+constexpr bool fusable(int E)
+{
+    return (E == 64 || E == 128) && E / CH <= 16;
+}
+
+template <typename T, int CH, int LPH>
+hipError_t run_fast_any(EdgeK k, int unroll, hipStream_t s)
+{
+    if (k.fuse_out && k.E == 64 && fusable<T, CH>(64))
+        return run_fast<T, CH, LPH, 64>(k, unroll, s);
+    if constexpr (fusable<T, CH>(128)) {
+        if (k.fuse_out && k.E == 128)
+            return run_fast<T, CH, LPH, 128>(k, unroll, s);
+    }
+    k.fuse_out = 0;
+    return run_fast<T, CH, LPH, 0>(k, unroll, s);
 }
 
 template <typename T>
@@ -500,11 +717,11 @@ hipError_t dispatch_edge(EdgeK k, int unroll, hipStream_t s)
     constexpr int CH = 16 / sizeof(T);
     if (k.d % CH == 0) {
         switch (k.d / CH) {
-        case 1: return run_fast<T, CH, 1>(k, unroll, s);
-        case 2: return run_fast<T, CH, 2>(k, unroll, s);
-        case 4: return run_fast<T, CH, 4>(k, unroll, s);
-        case 8: return run_fast<T, CH, 8>(k, unroll, s);
-        case 16: return run_fast<T, CH, 16>(k, unroll, s);
+        case 1: return run_fast_any<T, CH, 1>(k, unroll, s);
+        case 2: return run_fast_any<T, CH, 2>(k, unroll, s);
+        case 4: return run_fast_any<T, CH, 4>(k, unroll, s);
+        case 8: return run_fast_any<T, CH, 8>(k, unroll, s);
+        case 16: return run_fast_any<T, CH, 16>(k, unroll, s);
         default: break;
         }
     }
@@ -519,7 +736,16 @@ hipError_t run_merge(EdgeK k, hipStream_t s)
     const int64_t chunks = (int64_t)k.B * (k.E / CH);
     k.passes = (int)((chunks + 63) / 64);
     const int64_t units = k.n_split * k.passes;
-    merge_fast<T, CH, LPH><<<(unsigned)((units + 3) / 4), 256, 0, s>>>(k);
+    const unsigned blocks = (unsigned)((units + 3) / 4);
+    if (k.fuse_out && k.E == 64 && fusable<T, CH>(64)) {
+        merge_fast<T, CH, LPH, 64><<<blocks, 256, 0, s>>>(k);
+    } else if (k.fuse_out && k.E == 128 && fusable<T, CH>(128)) {
+        if constexpr (fusable<T, CH>(128))
+            merge_fast<T, CH, LPH, 128><<<blocks, 256, 0, s>>>(k);
+    } else {
+        k.fuse_out = 0;
+        merge_fast<T, CH, LPH, 0><<<blocks, 256, 0, s>>>(k);
+    }
     return hipGetLastError();
 }
 
@@ -543,6 +769,15 @@ hipError_t dispatch_merge(EdgeK k, hipStream_t s)
 }
 
 }  // namespace
+
+bool out_fusable(int64_t E, int64_t H, pma_dtype dt)
+{
+    // E = 128 would stage a 32 KB Wo per 4-wavefront workgroup, which halves
+    // the gather's occupancy; measured, the separate out_proj is faster there.
+    const int64_t d = E / H;
+    const int64_t ch = dt == PMA_BF16 ? 8 : 4;
+    return E == 64 && d % ch == 0 && (d / ch) <= 16 && ((d / ch) & (d / ch - 1)) == 0;
+}
 
 Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)
 {

@@ -47,6 +47,7 @@ struct pma_plan {
     int out_order = 1;          // PMA_OUT_ORDER: out_proj rows visited batch- (0) or token-major (1)
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
+    bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
     int nt = 1;                 // PMA_NT=0: cached q loads / mixed stores
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
@@ -239,6 +240,8 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     }
     if (const char *ev = getenv("PMA_FUSED"))
         p->use_fused = ev[0] == '1';
+    if (const char *ev = getenv("PMA_FUSE_OUT"))
+        p->fuse_out = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
         p->xcd_map = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_NT"))
@@ -453,6 +456,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.lay = lay;
     ea.qt = p->qt;
     ea.kv = p->kv;
+    ea.kv_bytes = (uint64_t)p->S * 2 * B * E * es;
     ea.mixed = p->mixed;
     ea.part_acc = p->part_acc;
     ea.part_ml = p->part_ml;
@@ -464,6 +468,11 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     // Pinning sample groups to XCDs splits each source's key/value row across
     // the L2s; it pays once the keys and values outgrow the 256 MB last-level
     // cache (measured: large and bipartite workloads gain, the gene one loses).
+    ea.fuse_out = p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
+                  (((uintptr_t)o_w | (uintptr_t)out) & 15) == 0;
+    ea.wo = o_w;
+    ea.bo = o_b;
+    ea.out = out;
     ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map
                                  : (2.0 * S * B * E * es > 256.0 * 1024 * 1024 ? 1 : 0);
     ea.nt = p->nt;
@@ -524,6 +533,9 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     }
     if (st != PMA_OK)
         return fail(st, "edge launch failed: %s", hipGetErrorString(hipGetLastError()));
+
+    if (ea.fuse_out)
+        return PMA_OK;   // out_proj ran in the edge and merge kernels
 
     // Step 5: join heads (already contiguous) and out_proj, back to (B, L, E).
     tm.begin(PMA_STAGE_OUT);

@@ -82,6 +82,7 @@ struct EdgeArgs {
     Layout lay;
     const void *qt;     // q rows (layout lay)
     const void *kv;     // key and value rows (layout lay)
+    uint64_t kv_bytes = 0;  // size of kv
     void *mixed;        // mixed rows (layout lay)
     float *part_acc;    // [slot][B][E]
     float *part_ml;     // [slot][B][H][2]
@@ -92,7 +93,14 @@ struct EdgeArgs {
     int unroll = 4;     // edges per step of edge_fast (4 or 8)
     int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
     int nt = 1;         // non-temporal q loads / mixed stores
+    // out_proj fused into the edge and merge kernels (out_fusable)
+    int fuse_out = 0;
+    const void *wo = nullptr, *bo = nullptr;
+    void *out = nullptr;
 };
+
+// Whether edge_fast / merge_fast can apply out_proj themselves.
+bool out_fusable(int64_t E, int64_t H, pma_dtype dt);
 
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
 
