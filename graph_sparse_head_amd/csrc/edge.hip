@@ -670,9 +670,8 @@ EdgeK make_k(const EdgeArgs &x)
 }
 
 template <typename T, int CH, int LPH, int E_FUSE>
-hipError_t run_fast(EdgeK k, int unroll, hipStream_t s)
+hipError_t run_fast(EdgeK k, hipStream_t s)
 {
-    (void)unroll;
     const int64_t chunks = (int64_t)k.B * (k.E / CH);
     k.passes = (int)((chunks + 63) / 64);
     unsigned blocks;
@@ -699,29 +698,29 @@ constexpr bool fusable(int E)
 }
 
 template <typename T, int CH, int LPH>
-hipError_t run_fast_any(EdgeK k, int unroll, hipStream_t s)
+hipError_t run_fast_any(EdgeK k, hipStream_t s)
 {
     if (k.fuse_out && k.E == 64 && fusable<T, CH>(64))
-        return run_fast<T, CH, LPH, 64>(k, unroll, s);
+        return run_fast<T, CH, LPH, 64>(k, s);
     if constexpr (fusable<T, CH>(128)) {
         if (k.fuse_out && k.E == 128)
-            return run_fast<T, CH, LPH, 128>(k, unroll, s);
+            return run_fast<T, CH, LPH, 128>(k, s);
     }
     k.fuse_out = 0;
-    return run_fast<T, CH, LPH, 0>(k, unroll, s);
+    return run_fast<T, CH, LPH, 0>(k, s);
 }
 
 template <typename T>
-hipError_t dispatch_edge(EdgeK k, int unroll, hipStream_t s)
+hipError_t dispatch_edge(EdgeK k, hipStream_t s)
 {
     constexpr int CH = 16 / sizeof(T);
     if (k.d % CH == 0) {
         switch (k.d / CH) {
-        case 1: return run_fast_any<T, CH, 1>(k, unroll, s);
-        case 2: return run_fast_any<T, CH, 2>(k, unroll, s);
-        case 4: return run_fast_any<T, CH, 4>(k, unroll, s);
-        case 8: return run_fast_any<T, CH, 8>(k, unroll, s);
-        case 16: return run_fast_any<T, CH, 16>(k, unroll, s);
+        case 1: return run_fast_any<T, CH, 1>(k, s);
+        case 2: return run_fast_any<T, CH, 2>(k, s);
+        case 4: return run_fast_any<T, CH, 4>(k, s);
+        case 8: return run_fast_any<T, CH, 8>(k, s);
+        case 16: return run_fast_any<T, CH, 16>(k, s);
         default: break;
         }
     }
@@ -805,8 +804,7 @@ Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
 {
     EdgeK k = make_k(x);
-    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, x.unroll, s)
-                                    : dispatch_edge<float>(k, x.unroll, s);
+    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, s) : dispatch_edge<float>(k, s);
     return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 

@@ -41,10 +41,6 @@ struct pma_plan {
     int64_t L = 0, S = 0, E = 0, H = 0, nnz = 0;
     pma_dtype dtype = PMA_F32;
     int chunk = kChunk;
-    bool use_fused = false;     // PMA_FUSED=1: fused q/edge/out kernel where supported
-    int edge_unroll = 4;        // PMA_EDGE_UNROLL: edges per step of the edge kernel (4, 8)
-    int proj_order = 0;         // PMA_PROJ_ORDER: q/k/v rows visited batch- (0) or token-major (1)
-    int out_order = 1;          // PMA_OUT_ORDER: out_proj rows visited batch- (0) or token-major (1)
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
@@ -53,7 +49,7 @@ struct pma_plan {
     pma::GraphDev g;
     // workspace, grown on demand
     int64_t ws_B = 0;
-    bool ws_weights = false, ws_unfused = false;
+    bool ws_weights = false;
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
     // profiling
@@ -75,18 +71,17 @@ void free_workspace(pma_plan *p)
     p->qt = p->kv = p->mixed = nullptr;
     p->part_acc = p->part_ml = p->stat_ml = p->scores = nullptr;
     p->ws_B = 0;
-    p->ws_weights = p->ws_unfused = false;
+    p->ws_weights = false;
 }
 
-// Buffers for a batch of B: k/v always; q and mixed only for the unfused
-// kernels; scores and final (max, sum) only for need_weights.
-pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, bool unfused, hipStream_t s)
+// Buffers for a batch of B: q, keys/values, mixed and the split partials;
+// scores and final (max, sum) only for need_weights.
+pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
 {
-    if (B <= p->ws_B && (!weights || p->ws_weights) && (!unfused || p->ws_unfused))
+    if (B <= p->ws_B && (!weights || p->ws_weights))
         return PMA_OK;
     const int64_t nB = B > p->ws_B ? B : p->ws_B;
     const bool nw = weights || p->ws_weights;
-    const bool nu = unfused || p->ws_unfused;
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess)
         return fail(PMA_E_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
@@ -97,9 +92,9 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, bool unfused, 
         void **ptr;
         size_t bytes;
     } want[] = {
-        {&p->qt, nu ? (size_t)p->L * nB * p->E * es : 0},
+        {&p->qt, (size_t)p->L * nB * p->E * es},
         {&p->kv, (size_t)p->S * 2 * nB * p->E * es},
-        {&p->mixed, nu ? (size_t)p->L * nB * p->E * es : 0},
+        {&p->mixed, (size_t)p->L * nB * p->E * es},
         {(void **)&p->part_acc, slots * nB * p->E * 4},
         {(void **)&p->part_ml, slots * nB * p->H * 2 * 4},
         {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
@@ -117,7 +112,6 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, bool unfused, 
     }
     p->ws_B = nB;
     p->ws_weights = nw;
-    p->ws_unfused = nu;
     return PMA_OK;
 }
 
@@ -230,16 +224,17 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     p->H = H;
     p->nnz = (int64_t)p->h_src.size();
     p->dtype = dtype;
-    // Tuning knobs read once per plan: PMA_CHUNK (most edges per piece,
-    // 1..65535), PMA_FUSED (1: the fused kernel where it applies) and
-    // PMA_EDGE_UNROLL (4 or 8).
+    // Tuning knobs, read once per plan (defaults are the measured best):
+    //   PMA_CHUNK      most edges per piece of a target (1..65535)
+    //   PMA_FUSE_OUT   0: out_proj as a separate kernel
+    //   PMA_XCD_MAP    1 / 0: force or forbid one sample group per XCD
+    //   PMA_NT         0: cached instead of non-temporal q / mixed streams
+    //   PMA_LAYOUT     "batch": batch-first q / k / v / mixed workspace
     if (const char *ev = getenv("PMA_CHUNK")) {
         const long c = strtol(ev, nullptr, 10);
         if (c >= 1 && c <= 65535)
             p->chunk = (int)c;
     }
-    if (const char *ev = getenv("PMA_FUSED"))
-        p->use_fused = ev[0] == '1';
     if (const char *ev = getenv("PMA_FUSE_OUT"))
         p->fuse_out = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
@@ -248,15 +243,6 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
         p->nt = ev[0] != '0';
     if (const char *ev = getenv("PMA_LAYOUT"))
         p->batch_first_ws = strcmp(ev, "batch") == 0;
-    if (const char *ev = getenv("PMA_PROJ_ORDER"))
-        p->proj_order = ev[0] == '1';
-    if (const char *ev = getenv("PMA_OUT_ORDER"))
-        p->out_order = ev[0] == '1';
-    if (const char *ev = getenv("PMA_EDGE_UNROLL")) {
-        const long u = strtol(ev, nullptr, 10);
-        if (u == 4 || u == 8)
-            p->edge_unroll = (int)u;
-    }
     if (p->nnz + L > kI32) {
         delete p;
         return fail(PMA_E_UNSUPPORTED, "nnz + query_features exceeds 2^31 - 1");
@@ -400,38 +386,30 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     const int64_t B = batch, L = p->L, S = p->S, E = p->E;
     if ((L > S ? L : S) * B * 2 * E > ((int64_t)1 << 40))
         return fail(PMA_E_UNSUPPORTED, "batch too large for one forward");
-    // The fused kernel needs E in {64, 128}, d in {8, 16, 32} and 16-byte
-    // aligned caller tensors; anything else runs the separate kernels.
-    const uintptr_t align_bits = (uintptr_t)query | (uintptr_t)key | (uintptr_t)value |
-                                 (uintptr_t)q_w | (uintptr_t)o_w | (uintptr_t)out;
-    const bool fused = p->use_fused && pma::fused_supported(E, p->H, p->dtype) &&
-                       (align_bits & 15) == 0;
-    pma_status st = ensure_workspace(p, B, weights != nullptr, !fused, stream);
+    pma_status st = ensure_workspace(p, B, weights != nullptr, stream);
     if (st != PMA_OK)
         return st;
     StageTimer tm{p, stream};
     const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
     char *kvc = static_cast<char *>(p->kv);
-    // the fused kernel reads the target-major layout
-    const pma::Layout lay = pma::make_layout(p->batch_first_ws && !fused, B, L, S, E);
+    const pma::Layout lay = pma::make_layout(p->batch_first_ws, B, L, S, E);
 
-    // Step 1 (keys and values; queries too on the unfused path).
+    // Step 1: q, k, v projections into the workspace layout. Caller tokens are
+    // batch-first and read in storage order.
     tm.begin(PMA_STAGE_PROJ_IN);
     const pma::ProjOut oq{q_w, q_b, p->qt, lay.q_b, lay.q_t};
     const pma::ProjOut ok{k_w, k_b, kvc, lay.kv_b, lay.kv_s};
     const pma::ProjOut ov{v_w, v_b, kvc + (size_t)lay.kv_v * es, lay.kv_b, lay.kv_s};
-    const int po = p->proj_order;
     auto in_args = [&](const void *x, int64_t n, int nblk, pma::ProjOut o0, pma::ProjOut o1,
                        pma::ProjOut o2) {
-        pma::ProjArgs a{x, B * n, n, B, po, nblk, {o0, o1, o2}};
-        a.x_token_major = 0;   // caller tokens are batch-first
+        pma::ProjArgs a{x, B * n, n, B, 0, nblk, {o0, o1, o2}};
+        a.x_token_major = 0;
         return a;
     };
-    if (!fused && query == key && key == value && L == S) {
+    if (query == key && key == value && L == S) {
         st = pma::launch_proj(in_args(query, L, 3, oq, ok, ov), E, p->dtype, stream);
     } else {
-        if (!fused)
-            st = pma::launch_proj(in_args(query, L, 1, oq, oq, oq), E, p->dtype, stream);
+        st = pma::launch_proj(in_args(query, L, 1, oq, oq, oq), E, p->dtype, stream);
         if (st == PMA_OK && key == value) {
             st = pma::launch_proj(in_args(key, S, 2, ok, ov, ov), E, p->dtype, stream);
         } else if (st == PMA_OK) {
@@ -464,60 +442,21 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
-    ea.unroll = p->edge_unroll;
-    // Pinning sample groups to XCDs splits each source's key/value row across
-    // the L2s; it pays once the keys and values outgrow the 256 MB last-level
-    // cache (measured: large and bipartite workloads gain, the gene one loses).
+    ea.nt = p->nt;
+    // out_proj in the edge / merge epilogue where it applies (16-byte aligned
+    // Wo and out).
     ea.fuse_out = p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
                   (((uintptr_t)o_w | (uintptr_t)out) & 15) == 0;
     ea.wo = o_w;
     ea.bo = o_b;
     ea.out = out;
+    // Pinning sample groups to XCDs splits each source's key/value row across
+    // the L2s; it pays once the keys and values outgrow the 256 MB last-level
+    // cache (measured: large and bipartite workloads gain, the gene one loses).
     ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map
                                  : (2.0 * S * B * E * es > 256.0 * 1024 * 1024 ? 1 : 0);
-    ea.nt = p->nt;
 
-    if (fused) {
-        // Steps 1 (queries) to 5 in one kernel.
-        pma::FusedArgs fa;
-        fa.g = &p->g;
-        fa.B = B;
-        fa.L = L;
-        fa.S = S;
-        fa.E = E;
-        fa.H = p->H;
-        fa.nnz = p->nnz;
-        fa.dt = p->dtype;
-        fa.xq = query;
-        fa.wq = q_w;
-        fa.bq = q_b;
-        fa.wo = o_w;
-        fa.bo = o_b;
-        fa.kv = p->kv;
-        fa.out = out;
-        fa.part_acc = p->part_acc;
-        fa.part_ml = p->part_ml;
-        fa.stat_ml = ea.stat_ml;
-        fa.scores = ea.scores;
-        tm.begin(PMA_STAGE_EDGE);
-        st = pma::launch_fused(fa, false, stream);
-        tm.end();
-        if (st == PMA_OK && p->g.n_split > 0) {
-            tm.begin(PMA_STAGE_MERGE);
-            st = pma::launch_fused(fa, true, stream);
-            tm.end();
-        }
-        if (st == PMA_OK && weights) {
-            tm.begin(PMA_STAGE_WEIGHTS);
-            st = pma::launch_weights(ea, stream);
-            tm.end();
-        }
-        if (st != PMA_OK)
-            return fail(st, "edge launch failed: %s", hipGetErrorString(hipGetLastError()));
-        return PMA_OK;
-    }
-
-    // Steps 2-4: scores, softmax and mix over the live edges.
+    // Steps 2-4 (and 5 when fused): scores, softmax and mix over the live edges.
     tm.begin(PMA_STAGE_EDGE);
     st = pma::launch_edge(ea, stream);
     tm.end();
@@ -533,15 +472,16 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     }
     if (st != PMA_OK)
         return fail(st, "edge launch failed: %s", hipGetErrorString(hipGetLastError()));
-
     if (ea.fuse_out)
         return PMA_OK;   // out_proj ran in the edge and merge kernels
 
-    // Step 5: join heads (already contiguous) and out_proj, back to (B, L, E).
+    // Step 5: join heads (already contiguous) and out_proj, back to (B, L, E),
+    // visiting rows in mixed's storage order.
     tm.begin(PMA_STAGE_OUT);
     const pma::ProjOut oo{o_w, o_b, out, L * E, E};
-    pma::ProjArgs ao{p->mixed, L * B, L, B, p->out_order, 1, {oo}};
-    ao.x_token_major = lay.m_b == E ? 1 : 0;   // target-major or batch-first mixed
+    const int mixed_token_major = lay.m_b == E ? 1 : 0;
+    pma::ProjArgs ao{p->mixed, L * B, L, B, mixed_token_major, 1, {oo}};
+    ao.x_token_major = mixed_token_major;
     st = pma::launch_proj(ao, E, p->dtype, stream);
     tm.end();
     if (st != PMA_OK)

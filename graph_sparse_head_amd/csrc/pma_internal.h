@@ -90,7 +90,6 @@ struct EdgeArgs {
     float *scores;      // [nnz][B][H] log2-domain scores by CSR position, or nullptr
     float *weights;     // caller's weights or nullptr
     int average;
-    int unroll = 4;     // edges per step of edge_fast (4 or 8)
     int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
     int nt = 1;         // non-temporal q loads / mixed stores
     // out_proj fused into the edge and merge kernels (out_fusable)
@@ -104,23 +103,6 @@ bool out_fusable(int64_t E, int64_t H, pma_dtype dt);
 
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
 
-// ---- fused q projection + edges + out_proj (attend.hip) --------------------
-
-struct FusedArgs {
-    const GraphDev *g;
-    int64_t B, L, S, E, H, nnz;
-    pma_dtype dt;
-    const void *xq;                 // caller's (B, L, E) query tokens
-    const void *wq, *bq, *wo, *bo;  // caller's parameters (biases may be null)
-    const void *kv;                 // [S][2][B][E]
-    void *out;                      // caller's (B, L, E)
-    float *part_acc, *part_ml;      // as in EdgeArgs
-    float *stat_ml, *scores;        // need_weights only
-};
-
-bool fused_supported(int64_t E, int64_t H, pma_dtype dt);
-// merge == false: every piece (attend_fused); true: split targets (merge_out).
-pma_status launch_fused(const FusedArgs &a, bool merge, hipStream_t s);
 pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
 pma_status launch_weights(const EdgeArgs &a, hipStream_t s);
 

@@ -203,3 +203,33 @@ def test_full_size_sampled(name):
             assert np.abs(sums[:, deg > 0] - 1).max() <= 1e-4
     finally:
         pma.pma_destroy(plan)
+
+
+# ---------------------------------------------------------------------------
+# every tuning knob gives the same results (read at plan creation)
+
+KNOBS = [
+    {"PMA_FUSE_OUT": "0"},
+    {"PMA_LAYOUT": "batch"},
+    {"PMA_LAYOUT": "batch", "PMA_FUSE_OUT": "0"},
+    {"PMA_CHUNK": "3"},
+    {"PMA_CHUNK": "3", "PMA_FUSE_OUT": "0"},
+    {"PMA_XCD_MAP": "1"},
+    {"PMA_XCD_MAP": "0", "PMA_NT": "0"},
+]
+
+
+@pytest.mark.parametrize("knobs", KNOBS, ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+@pytest.mark.parametrize("shape", [("f32", 64, 4), ("bf16", 64, 4), ("bf16", 128, 8)])
+def test_tuning_knobs(knobs, shape, monkeypatch):
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, v)
+    dt, E, H = shape
+    c = synth.random_case(50, 5, 220, 220, E, H, 0.04, dtype=dt, name="knobs")
+    # two hub targets so that small chunks split them
+    rng = np.random.default_rng(51)
+    hub_src = rng.choice(220, size=150, replace=False)
+    keep = ~np.isin(c.tgt, [3, 17])
+    c.src = np.concatenate([c.src[keep], hub_src, hub_src[:90]])
+    c.tgt = np.concatenate([c.tgt[keep], np.full(150, 3), np.full(90, 17)])
+    _full_check(c, need_weights=True, average=False)

@@ -89,3 +89,10 @@ def test_duplicate_rejected_on_device(where):
     with pytest.raises(pma.PmaError) as e:
         pma.pma_create(src, tgt, c.L, c.S, c.E, c.H)
     assert e.value.name == "PMA_E_INDEX_DUPLICATE"
+
+
+@pytest.mark.parametrize("chunk", ["1", "7", "65535"])
+def test_work_split_chunk_knob(chunk, monkeypatch):
+    monkeypatch.setenv("PMA_CHUNK", chunk)
+    c = synth.gene(n=3000, B=1, max_deg=400, dtype="f32")
+    _check_plan(c.src, c.tgt, c.L, c.S, c.E, c.H)
