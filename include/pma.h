@@ -61,13 +61,13 @@ typedef enum {
 
 /* Stages that pma_profile_read reports, in launch order. */
 typedef enum {
-    PMA_STAGE_PROJ_IN = 0, /* k / v projections (and q on the separate-kernel path) */
-    PMA_STAGE_EDGE = 1,    /* score, online softmax and mix over the edges; on the
-                              fused path also q_proj and out_proj */
-    PMA_STAGE_MERGE = 2,   /* merge of targets split into several pieces; on the
-                              fused path also their out_proj */
+    PMA_STAGE_PROJ_IN = 0, /* q, k and v projections */
+    PMA_STAGE_EDGE = 1,    /* score, online softmax and mix over the edges; when
+                              out_proj is fused (embed_dim 64) also out_proj */
+    PMA_STAGE_MERGE = 2,   /* merge of targets split into several pieces; when
+                              out_proj is fused also their out_proj */
     PMA_STAGE_WEIGHTS = 3, /* need_weights: one weight per live edge */
-    PMA_STAGE_OUT = 4,     /* out_proj (separate-kernel path only) */
+    PMA_STAGE_OUT = 4,     /* out_proj when it is not fused */
     PMA_NUM_STAGES = 5
 } pma_stage;
 
