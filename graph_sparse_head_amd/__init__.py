@@ -50,7 +50,8 @@ class _Info(ctypes.Structure):
                 ("embed_dim", ctypes.c_int64), ("num_heads", ctypes.c_int64),
                 ("nnz", ctypes.c_int64), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("n_tasks", ctypes.c_int64), ("n_split", ctypes.c_int64),
-                ("n_slots", ctypes.c_int64), ("max_degree", ctypes.c_int64)]
+                ("n_slots", ctypes.c_int64), ("max_degree", ctypes.c_int64),
+                ("kv_rows", ctypes.c_int64)]
 
 
 def library_path() -> str:

@@ -23,6 +23,9 @@
 // stat_ml[L][B][H][2], scores[nnz][B][H].
 #include <math.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "pma_internal.h"
 
 namespace pma {
@@ -32,11 +35,16 @@ struct EdgeK {
     const int32_t *csr_src, *csr_tgt, *csr_eid;
     const int32_t *task_target, *task_begin, *task_end, *task_slot;
     const int32_t *split_target, *split_slot0, *split_count;
-    int64_t n_tasks, n_split;
+    int64_t n_tasks, n_split, n_slots;
     int B, E, H, d;
     int64_t nnz;
     int passes;          // wavefronts per piece (sample groups)
+    // n / passes and n / (E / CH) as (n * m) >> sh for n < 2^31 (see magic31)
+    uint32_t pass_m, cpr_m;
+    int pass_sh, cpr_sh;
     int xcd_map;         // 1: sample group fixed per XCD (passes divides 8)
+    uint32_t xcd_per;    // 8 / passes
+    uint32_t tstride;    // pieces between a wavefront's consecutive pieces
     int nt;              // 1: non-temporal q loads and mixed stores
     float scale;         // log2(e) / sqrt(d)
     Layout lay;
@@ -75,6 +83,12 @@ __device__ inline uint32_t pack_bf16(float lo, float hi)
 __device__ inline uint16_t f2bf(float f) { return (uint16_t)(pack_bf16(f, 0.f) & 0xffffu); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// floor(n / d) for n < 2^31 from a host-made multiplier (magic31)
+__device__ inline uint32_t div31(uint32_t n, uint32_t m, int sh)
+{
+    return (uint32_t)(((uint64_t)n * m) >> sh);
+}
 
 template <int CTRL> __device__ inline float dpp(float x)
 {
@@ -175,7 +189,7 @@ __device__ inline void stage_wo(const EdgeK &a, char *wlds)
     }
 }
 
-template <typename T, int CH, int E>
+template <typename T, int CH, int E, bool W32>
 __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane, int t,
                                      int b_first, const char *wlds)
 {
@@ -240,7 +254,12 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
     }
     if (!has || b >= a.B)
         return;
-    char *dst = reinterpret_cast<char *>(reinterpret_cast<T *>(a.out) + ((int64_t)b * a.L + t) * E + CPL * g);
+    T *o = reinterpret_cast<T *>(a.out);
+    if (W32)   // out under 2 GiB: 32-bit element offset
+        o += ((uint32_t)b * (uint32_t)a.L + (uint32_t)t) * (uint32_t)E + CPL * g;
+    else
+        o += ((int64_t)b * a.L + t) * E + CPL * g;
+    char *dst = reinterpret_cast<char *>(o);
 #pragma unroll
     for (int k = 0; k < OW / 4; ++k) {
         const uint4 v = make_uint4(ow[4 * k], ow[4 * k + 1], ow[4 * k + 2], ow[4 * k + 3]);
@@ -262,26 +281,30 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
 // address and discard the data. bf16 scores use v_dot2 on the stored bf16 q
 // and k words (fp32 products and sums) and are scaled afterwards. Edges run U
 // at a time, the remainder one at a time.
-template <typename T, int CH, int LPH, bool BUF> struct EdgeLane {
+template <typename T, int CH, int LPH, bool W32, bool SC> struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
     static constexpr bool BF = sizeof(T) == 2;
 
     const EdgeK &a;
+    const int32_t *src;   // csr_src, from a noalias kernel argument
     int B, b, h;
     bool active, head_lead;
     Chunk<T, CH> q;
     float qf[BF ? 1 : CH];
-    float m = -INFINITY, l = 0.f, acc[CH];
+    float l = 0.f, acc[CH];
     const char *kvb;
     __amdgpu_buffer_rsrc_t rsrc;
-    uint64_t row2, loff, vloff;
+    typedef typename std::conditional<W32, uint32_t, uint64_t>::type Off;
+    uint64_t row2;
+    Off loff, vloff;   // this lane's key and value chunk inside a source's rows
+    uint32_t sc_lane, sc_edge;            // scores element offsets: this lane's, per edge
 
     __device__ EdgeLane(const EdgeK &a_) : a(a_) {}
 
     __device__ inline void gather(int s, Chunk<T, CH> &k, Chunk<T, CH> &v) const
     {
-        if constexpr (BUF) {
+        if constexpr (W32) {
             const uint32_t so = (uint32_t)s * (uint32_t)row2;   // uniform
             const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)loff, so, 0);
             const u32x4 vw = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)vloff, so, 0);
@@ -295,57 +318,115 @@ template <typename T, int CH, int LPH, bool BUF> struct EdgeLane {
     }
 
     // N edges starting at CSR position p, all of them live
+    // First bf16 product of a score with a zero accumulator (the VOP3 form
+    // takes the 0 as an inline constant; v_dot2c would need it in a register).
+    __device__ static inline float dot2_first(uint32_t x, uint32_t y)
+    {
+        float r;
+        asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(x), "v"(y));
+        return r;
+    }
+
+    // N live edges starting at CSR position p.
+    //
+    // Softmax reference: the weight of an edge is exp2(score - ms), scores in
+    // log2 units. The reference ms moves up to the running maximum only when
+    // some lane's maximum exceeds it by more than kLazy, so most steps skip
+    // the rescale of the partial sums; weights stay below 2^kLazy. Any
+    // reference gives the same normalised result (the sum and the mix are
+    // both relative to it), and a lone edge still gets weight exp2(0) = 1.
+    static constexpr float kLazy = 8.f;
+    float smul, ms = -INFINITY;
+    bool fresh = true;
+
     template <int N> __device__ inline void step(int p)
     {
         Chunk<T, CH> kk[N], vv[N];
 #pragma unroll
-        for (int u = 0; u < N; ++u) gather(a.csr_src[p + u], kk[u], vv[u]);
+        for (int u = 0; u < N; ++u) gather(src[p + u], kk[u], vv[u]);
         float sc[N];
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            float dot = 0.f;
+            float dot;
             if constexpr (BF) {
+                dot = dot2_first(q.word(0), kk[u].word(0));
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                for (int k = 1; k < 4; ++k)
                     dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.word(k)),
                                                           __builtin_bit_cast(bf16x2, kk[u].word(k)),
                                                           dot, false);
             } else {
+                dot = 0.f;
 #pragma unroll
                 for (int i = 0; i < CH; ++i) dot = fmaf(qf[i], kk[u][i], dot);
             }
             dot = group_sum<LPH>(dot);
-            if constexpr (BF) dot *= a.scale;
+            if constexpr (BF) dot *= smul;   // fp32 q carries the scale already
             sc[u] = dot;
         }
-        if (a.scores && active && head_lead) {
+        if (SC && active && head_lead) {
 #pragma unroll
-            for (int u = 0; u < N; ++u)
-                a.scores[(((int64_t)(p + u)) * B + b) * a.H + h] = sc[u];
+            for (int u = 0; u < N; ++u) {
+                // (a store through a buffer resource would hide from alias
+                // analysis that csr_src is never written, and turn its
+                // uniform scalar loads into vector loads)
+                if constexpr (W32)
+                    a.scores[(uint32_t)(p + u) * sc_edge + sc_lane] = sc[u];
+                else
+                    a.scores[(((int64_t)(p + u)) * B + b) * a.H + h] = sc[u];
+            }
         }
-        float mx = m;
+        float mx = sc[0];
 #pragma unroll
-        for (int u = 0; u < N; ++u) mx = fmaxf(mx, sc[u]);
-        const float alpha = fast_exp2(m - mx);
-        l *= alpha;
+        for (int u = 1; u < N; ++u) mx = fmaxf(mx, sc[u]);
+        if (fresh) {   // wave-uniform: the partial sums are still zero
+            ms = mx;
+            fresh = false;
+        } else {
+            const bool need = mx > ms + kLazy;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = need ? mx : ms;
+                const float alpha = fast_exp2(ms - mn);
+                l *= alpha;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) acc[i] *= alpha;
+                for (int i = 0; i < CH; ++i) acc[i] *= alpha;
+                ms = mn;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            const float pe = fast_exp2(sc[u] - mx);
+            const float pe = fast_exp2(sc[u] - ms);
             l += pe;
+            if constexpr (BF) {
+                // The weight meets the bf16 values as a bf16 operand of
+                // v_dot2 (products and sums stay fp32): (p, 0) against a
+                // value word picks its low channel, (0, p) its high one.
+                const uint32_t plo = pack_bf16(pe, 0.f), phi = plo << 16;
 #pragma unroll
-            for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u][i], acc[i]);
+                for (int k = 0; k < 4; ++k) {
+                    const bf16x2 vw = __builtin_bit_cast(bf16x2, vv[u].word(k));
+                    acc[2 * k] = __builtin_amdgcn_fdot2_f32_bf16(
+                        vw, __builtin_bit_cast(bf16x2, plo), acc[2 * k], false);
+                    acc[2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                        vw, __builtin_bit_cast(bf16x2, phi), acc[2 * k + 1], false);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < CH; ++i) acc[i] = fmaf(pe, vv[u][i], acc[i]);
+            }
         }
-        m = mx;
     }
 };
 
-template <typename T, int CH, int LPH, int U, int E_FUSE, bool BUF>
+template <typename T, int CH, int LPH, int U, int E_FUSE, bool W32, bool SC>
 __global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(E_FUSE != 128 ? 8 : 1)))   // 64 VGPRs, no spill
-edge_fast(EdgeK a)
+__attribute__((amdgpu_waves_per_eu(8)))   // 64 VGPRs
+edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
+          const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end,
+          const int32_t *__restrict__ task_slot)
 {
+    // The index arrays come in as noalias arguments: no store of this kernel
+    // can reach them, so their wave-uniform reads stay scalar loads.
     __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? E_FUSE * E_FUSE * sizeof(T) + 4 * E_FUSE : 16];
     if constexpr (E_FUSE > 0) {
         if (a.fuse_out) {   // uniform over the launch; before any wavefront exits
@@ -354,98 +435,158 @@ edge_fast(EdgeK a)
         }
     }
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int64_t task;
-    int pass;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Each wavefront serves one sample group (pass) and walks the pieces
+    // task0, task0 + tstride, ... (the host keeps n_tasks * passes below 2^31
+    // and makes the wavefront count a multiple of passes).
+    uint32_t task, pass;
     if (a.xcd_map) {
         // Workgroups are dealt to the 8 XCDs round-robin; XCD x serves sample
-        // group x % passes, so its L2 caches only that group's key/value rows.
-        const int x = blockIdx.x & 7, per = 8 / a.passes;
-        pass = x % a.passes;
-        task = ((int64_t)(blockIdx.x >> 3) * per + x / a.passes) * 4 + wave;
-        if (task >= a.n_tasks)
-            return;
+        // group x % passes (passes divides 8), so its L2 caches only that
+        // group's key/value rows.
+        const uint32_t x = blockIdx.x & 7, xq = div31(x, a.pass_m, a.pass_sh);
+        pass = x - xq * a.passes;
+        task = ((blockIdx.x >> 3) * a.xcd_per + xq) * 4 + wave;
     } else {
-        const int64_t unit = (int64_t)blockIdx.x * 4 + wave;
-        if (unit >= a.n_tasks * a.passes)
-            return;
-        task = unit / a.passes;
-        pass = (int)(unit - task * a.passes);
+        const uint32_t w = blockIdx.x * 4 + wave;
+        task = div31(w, a.pass_m, a.pass_sh);
+        pass = w - task * a.passes;
     }
-    const int t = a.task_target[task];
-    const int beg = a.task_begin[task], end = a.task_end[task];
-    const int slot = a.task_slot[task];
+    if (task >= (uint32_t)a.n_tasks)
+        return;
 
-    EdgeLane<T, CH, LPH, BUF> st(a);
+    EdgeLane<T, CH, LPH, W32, SC> st(a);
+    st.src = csr_src;
     const int B = a.B, E = a.E;
     const int cpr = E / CH;                       // chunks per sample row
-    const int c = pass * 64 + lane;
+    const uint32_t c = pass * 64 + lane;
     st.B = B;
-    st.active = c < B * cpr;
-    const int b = st.active ? c / cpr : 0;
-    const int cr = c - b * cpr;
+    st.active = c < (uint32_t)(B * cpr);
+    const int b = st.active ? (int)div31(c, a.cpr_m, a.cpr_sh) : 0;
+    const int cr = (int)c - b * cpr;
     const int col = st.active ? cr * CH : 0;
     st.b = b;
     st.h = st.active ? cr / LPH : 0;
     st.head_lead = (lane % LPH) == 0;
-
-    const T *qt = reinterpret_cast<const T *>(a.qt);
-    {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(qt + t * a.lay.q_t + b * a.lay.q_b + col);
-        st.q.u = a.nt ? load_nt(qp) : *qp;
-    }
-    if constexpr (sizeof(T) == 4) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
-    }
+    st.smul = a.scale;
     // byte offsets: per source (uniform), this lane's key and value chunks
     st.row2 = (uint64_t)a.lay.kv_s * sizeof(T);
-    st.loff = (uint64_t)(b * a.lay.kv_b + col) * sizeof(T);
-    st.vloff = st.loff + (uint64_t)a.lay.kv_v * sizeof(T);
-    st.kvb = reinterpret_cast<const char *>(a.kv);
-    if constexpr (BUF)
+    if constexpr (W32) {
+        st.loff = ((uint32_t)b * (uint32_t)a.lay.kv_b + col) * (uint32_t)sizeof(T);
+        st.vloff = st.loff + (uint32_t)a.lay.kv_v * (uint32_t)sizeof(T);
         st.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.kv), (short)0,
                                                     (int)(uint32_t)a.kv_bytes, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
+        st.sc_edge = (uint32_t)(B * a.H);
+        st.sc_lane = (uint32_t)b * a.H + st.h;
+    } else {
+        st.loff = (uint64_t)(b * a.lay.kv_b + col) * sizeof(T);
+        st.vloff = st.loff + (uint64_t)a.lay.kv_v * sizeof(T);
+    }
+    st.kvb = reinterpret_cast<const char *>(a.kv);
 
-    int p = beg;
-    for (; p + U <= end; p += U)
-        st.template step<U>(p);
-    for (; p < end; ++p)
-        st.template step<1>(p);
+    const T *qt = reinterpret_cast<const T *>(a.qt);
+    auto load_q = [&](int tq) -> uint4 {
+        const T *qa;
+        if constexpr (W32)
+            qa = qt + ((uint32_t)tq * (uint32_t)a.lay.q_t + (uint32_t)b * (uint32_t)a.lay.q_b + col);
+        else
+            qa = qt + tq * a.lay.q_t + b * a.lay.q_b + col;
+        const uint4 *qp = reinterpret_cast<const uint4 *>(qa);
+        return a.nt ? load_nt(qp) : *qp;
+    };
 
-    const float m = st.m, l = st.l;
-    if (slot < 0) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        float out[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
-        if (st.active && a.stat_ml && st.head_lead) {
-            float *sp = a.stat_ml + (((int64_t)t * B + b) * a.H + st.h) * 2;
-            sp[0] = m;
-            sp[1] = l;
+    int t = task_target[task];
+    int beg = task_begin[task], end = task_end[task];
+    int slot = task_slot[task];
+    uint4 qn = load_q(t);
+    for (;;) {
+        // The next piece's bounds and query chunk are requested while this
+        // one runs (wave-uniform branch).
+        const uint32_t nxt = task + a.tstride;
+        const bool more = nxt < (uint32_t)a.n_tasks;
+        int t2 = 0, beg2 = 0, end2 = 0, slot2 = 0;
+        if (more) {
+            t2 = task_target[nxt];
+            beg2 = task_begin[nxt];
+            end2 = task_end[nxt];
+            slot2 = task_slot[nxt];
         }
-        if constexpr (E_FUSE > 0) {
-            if (a.fuse_out) {   // wave-uniform
-                out_proj_wave<T, CH, E_FUSE>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
-                return;
+        st.q.u = qn;
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
+        st.l = 0.f;
+        st.ms = -INFINITY;
+        st.fresh = true;
+
+        static_assert(U == 4, "the tail below covers up to 3 edges");
+        int p = beg;
+        for (; p + U <= end; p += U)
+            st.template step<U>(p);
+        if (p + 2 <= end) {
+            st.template step<2>(p);
+            p += 2;
+        }
+        if (p < end)
+            st.template step<1>(p);
+        if (more)
+            qn = load_q(t2);
+
+        const float m = st.ms, l = st.l;
+        if (slot < 0) {
+            const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+            float out[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
+            if (SC && st.active && st.head_lead) {
+                float *sp = a.stat_ml;
+                if constexpr (W32)
+                    sp += ((uint32_t)t * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
+                else
+                    sp += (((int64_t)t * B + b) * a.H + st.h) * 2;
+                *reinterpret_cast<float2 *>(sp) = make_float2(m, l);
             }
+            bool done = false;
+            if constexpr (E_FUSE > 0) {
+                if (a.fuse_out) {   // wave-uniform
+                    out_proj_wave<T, CH, E_FUSE, W32>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+                    done = true;
+                }
+            }
+            if (!done && st.active) {
+                T *dst = reinterpret_cast<T *>(a.mixed);
+                if constexpr (W32)
+                    dst += (uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col;
+                else
+                    dst += t * a.lay.m_t + b * a.lay.m_b + col;
+                store_chunk<T, CH>(dst, out, a.nt != 0);
+            }
+        } else if (st.active) {
+            float *pa = a.part_acc, *pm = a.part_ml;
+            if constexpr (W32) {
+                pa += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)E + col;
+                pm += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
+            } else {
+                pa += ((int64_t)slot * B + b) * E + col;
+                pm += (((int64_t)slot * B + b) * a.H + st.h) * 2;
+            }
+            *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
+            if constexpr (CH == 8)
+                *reinterpret_cast<float4 *>(pa + 4) =
+                    make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
+            if (st.head_lead)
+                *reinterpret_cast<float2 *>(pm) = make_float2(m, l);
         }
-        if (st.active)
-            store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col,
-                               out, a.nt != 0);
-    } else if (st.active) {
-        float *pa = a.part_acc + ((int64_t)slot * B + b) * E + col;
-        *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
-        if constexpr (CH == 8)
-            *reinterpret_cast<float4 *>(pa + 4) =
-                make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
-        if (st.head_lead) {
-            float *pm = a.part_ml + (((int64_t)slot * B + b) * a.H + st.h) * 2;
-            pm[0] = m;
-            pm[1] = l;
-        }
+        if (!more)
+            break;
+        task = nxt;
+        t = t2;
+        beg = beg2;
+        end = end2;
+        slot = slot2;
     }
 }
 
@@ -517,16 +658,17 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
         }
     }
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (unit >= a.n_split * a.passes)
+    const uint32_t unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (unit >= (uint32_t)(a.n_split * a.passes))
         return;
-    const int64_t k = unit / a.passes;
+    const uint32_t k = div31(unit, a.pass_m, a.pass_sh);
     const int pass = (int)(unit - k * a.passes);
     const int B = a.B, E = a.E, H = a.H;
     const int cpr = E / CH;
     const int c = pass * 64 + lane;
     const bool active = c < B * cpr;
-    const int b = active ? c / cpr : 0, cr = c - b * cpr, col = active ? cr * CH : 0;
+    const int b = active ? (int)div31(c, a.cpr_m, a.cpr_sh) : 0, cr = c - b * cpr,
+              col = active ? cr * CH : 0;
     const int h = active ? cr / LPH : 0;
     const int t = a.split_target[k], s0 = a.split_slot0[k], n = active ? a.split_count[k] : 0;
     float M = -INFINITY;
@@ -551,9 +693,10 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
             acc[4 * q + 3] = fmaf(v.w, w, acc[4 * q + 3]);
         }
     }
+    const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
     float out[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) out[i] = l > 0.f ? acc[i] / l : 0.f;
+    for (int i = 0; i < CH; ++i) out[i] = acc[i] * inv;
     if (active && a.stat_ml && (lane % LPH) == 0) {
         float *st = a.stat_ml + (((int64_t)t * B + b) * H + h) * 2;
         st[0] = M;
@@ -561,7 +704,7 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
     }
     if constexpr (E_FUSE > 0) {
         if (a.fuse_out) {
-            out_proj_wave<T, CH, E_FUSE>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+            out_proj_wave<T, CH, E_FUSE, false>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
             return;
         }
     }
@@ -625,11 +768,31 @@ __global__ void __launch_bounds__(256) weights_kernel(EdgeK a)
     }
 }
 
+// Multiplier and shift with floor(n / d) = (n * m) >> sh for 0 <= n < 2^31
+// and 1 <= d < 2^31: l = ceil(log2 d), m = floor(2^(31 + l) / d) + 1 < 2^32,
+// sh = 31 + l (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994, with N = 31).
+void magic31(uint32_t d, uint32_t &m, int &sh)
+{
+    int l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    m = (uint32_t)((((uint64_t)1 << (31 + l)) / d) + 1);
+    sh = 31 + l;
+}
+
+void set_passes(EdgeK &k, int ch)
+{
+    const int64_t chunks = (int64_t)k.B * (k.E / ch);
+    k.passes = (int)((chunks + 63) / 64);
+    magic31((uint32_t)k.passes, k.pass_m, k.pass_sh);
+    magic31((uint32_t)(k.E / ch), k.cpr_m, k.cpr_sh);
+}
+
 EdgeK make_k(const EdgeArgs &x)
 {
     EdgeK k;
     const GraphDev *g = x.g;
-    k.csr_src = g->csr_src;
+    k.csr_src = x.gather_src;   // key/value workspace rows
     k.csr_tgt = g->csr_tgt;
     k.csr_eid = g->csr_eid;
     k.task_target = g->task_target;
@@ -641,6 +804,7 @@ EdgeK make_k(const EdgeArgs &x)
     k.split_count = g->split_count;
     k.n_tasks = g->n_tasks;
     k.n_split = g->n_split;
+    k.n_slots = g->n_slots;
     k.B = (int)x.B;
     k.E = (int)x.E;
     k.H = (int)x.H;
@@ -648,6 +812,7 @@ EdgeK make_k(const EdgeArgs &x)
     k.nnz = x.nnz;
     k.passes = 1;
     k.xcd_map = x.xcd_map;
+    k.tstride = 0;
     k.nt = x.nt;
     k.fuse_out = x.fuse_out;
     k.L = (int)x.L;
@@ -669,58 +834,98 @@ EdgeK make_k(const EdgeArgs &x)
     return k;
 }
 
-template <typename T, int CH, int LPH, int E_FUSE>
-hipError_t run_fast(EdgeK k, hipStream_t s)
+int cu_count()
 {
-    const int64_t chunks = (int64_t)k.B * (k.E / CH);
-    k.passes = (int)((chunks + 63) / 64);
-    unsigned blocks;
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    if (dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <typename T, int CH, int LPH, int E_FUSE>
+hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
+{
+    set_passes(k, CH);
+    if (k.n_tasks * k.passes >= ((int64_t)1 << 31))
+        return hipErrorInvalidConfiguration;
+    // Workgroups of 4 wavefronts. With persist > 0 at most persist
+    // workgroups per CU are launched and each wavefront walks several
+    // pieces; otherwise one wavefront per (piece, sample group).
+    const int64_t cap = persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
+    int64_t blocks;
     if (k.xcd_map && 8 % k.passes == 0) {
-        const int64_t per = 8 / k.passes;                       // workgroups per pass per round
-        blocks = (unsigned)(8 * ((k.n_tasks + 4 * per - 1) / (4 * per)));
+        const int64_t per = 8 / k.passes;   // workgroups per pass per round of 8
+        int64_t rounds = (k.n_tasks + 4 * per - 1) / (4 * per);
+        rounds = std::min(rounds, std::max<int64_t>(1, cap / 8));
+        blocks = 8 * rounds;
+        k.xcd_per = (uint32_t)per;
+        k.tstride = (uint32_t)(rounds * per * 4);
     } else {
         k.xcd_map = 0;
-        blocks = (unsigned)((k.n_tasks * k.passes + 3) / 4);
+        // whole multiples of `passes` wavefronts, so each keeps its pass
+        const int64_t g = k.passes / std::__gcd<int64_t>(4, k.passes);
+        blocks = (k.n_tasks * k.passes + 3) / 4;
+        blocks = std::min(blocks, std::max<int64_t>(g, cap));
+        blocks = (blocks + g - 1) / g * g;
+        k.tstride = (uint32_t)(blocks * 4 / k.passes);
     }
-    if (k.kv_bytes < ((uint64_t)1 << 31))
-        edge_fast<T, CH, LPH, 4, E_FUSE, true><<<blocks, 256, 0, s>>>(k);
+    // 32-bit offsets when every tensor the kernel addresses is under 2 GiB
+    const uint64_t rows = (uint64_t)k.L * k.B * k.E * sizeof(T);
+    const uint64_t scores = k.scores ? (uint64_t)k.nnz * k.B * k.H * 4 : 0;
+    const uint64_t parts = (uint64_t)k.n_slots * k.B * k.E * 4;
+    const uint64_t stats = (uint64_t)k.L * k.B * k.H * 8;
+    const uint64_t lim = (uint64_t)1 << 31;
+    const bool w32 = k.kv_bytes < lim && rows < lim && scores < lim && parts < lim && stats < lim;
+    const unsigned nb = (unsigned)blocks;
+    if (w32 && k.scores)
+        edge_fast<T, CH, LPH, 4, E_FUSE, true, true><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
+    else if (w32)
+        edge_fast<T, CH, LPH, 4, E_FUSE, true, false><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
+    else if (k.scores)
+        edge_fast<T, CH, LPH, 4, E_FUSE, false, true><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
     else
-        edge_fast<T, CH, LPH, 4, E_FUSE, false><<<blocks, 256, 0, s>>>(k);
+        edge_fast<T, CH, LPH, 4, E_FUSE, false, false><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
     return hipGetLastError();
 }
 
 // out_proj can run in the edge kernel's epilogue when a wavefront holds at
-// least 4 samples' rows (E / CH <= 16 chunks per row) and E is 64 or 128.
+// least 4 samples' rows (E / CH <= 16 chunks per row); it is used for E = 64
+// (out_fusable).
 template <typename T, int CH>
 constexpr bool fusable(int E)
 {
-    return (E == 64 || E == 128) && E / CH <= 16;
+    return E == 64 && E / CH <= 16;
 }
 
 template <typename T, int CH, int LPH>
-hipError_t run_fast_any(EdgeK k, hipStream_t s)
+hipError_t run_fast_any(EdgeK k, int persist, hipStream_t s)
 {
     if (k.fuse_out && k.E == 64 && fusable<T, CH>(64))
-        return run_fast<T, CH, LPH, 64>(k, s);
-    if constexpr (fusable<T, CH>(128)) {
-        if (k.fuse_out && k.E == 128)
-            return run_fast<T, CH, LPH, 128>(k, s);
-    }
+        return run_fast<T, CH, LPH, 64>(k, persist, s);
     k.fuse_out = 0;
-    return run_fast<T, CH, LPH, 0>(k, s);
+    return run_fast<T, CH, LPH, 0>(k, persist, s);
 }
 
 template <typename T>
-hipError_t dispatch_edge(EdgeK k, hipStream_t s)
+hipError_t dispatch_edge(EdgeK k, int persist, hipStream_t s)
 {
     constexpr int CH = 16 / sizeof(T);
     if (k.d % CH == 0) {
         switch (k.d / CH) {
-        case 1: return run_fast_any<T, CH, 1>(k, s);
-        case 2: return run_fast_any<T, CH, 2>(k, s);
-        case 4: return run_fast_any<T, CH, 4>(k, s);
-        case 8: return run_fast_any<T, CH, 8>(k, s);
-        case 16: return run_fast_any<T, CH, 16>(k, s);
+        case 1: return run_fast_any<T, CH, 1>(k, persist, s);
+        case 2: return run_fast_any<T, CH, 2>(k, persist, s);
+        case 4: return run_fast_any<T, CH, 4>(k, persist, s);
+        case 8: return run_fast_any<T, CH, 8>(k, persist, s);
+        case 16: return run_fast_any<T, CH, 16>(k, persist, s);
         default: break;
         }
     }
@@ -732,15 +937,13 @@ hipError_t dispatch_edge(EdgeK k, hipStream_t s)
 template <typename T, int CH, int LPH>
 hipError_t run_merge(EdgeK k, hipStream_t s)
 {
-    const int64_t chunks = (int64_t)k.B * (k.E / CH);
-    k.passes = (int)((chunks + 63) / 64);
+    set_passes(k, CH);
     const int64_t units = k.n_split * k.passes;
+    if (units >= ((int64_t)1 << 31))
+        return hipErrorInvalidConfiguration;
     const unsigned blocks = (unsigned)((units + 3) / 4);
     if (k.fuse_out && k.E == 64 && fusable<T, CH>(64)) {
         merge_fast<T, CH, LPH, 64><<<blocks, 256, 0, s>>>(k);
-    } else if (k.fuse_out && k.E == 128 && fusable<T, CH>(128)) {
-        if constexpr (fusable<T, CH>(128))
-            merge_fast<T, CH, LPH, 128><<<blocks, 256, 0, s>>>(k);
     } else {
         k.fuse_out = 0;
         merge_fast<T, CH, LPH, 0><<<blocks, 256, 0, s>>>(k);
@@ -804,7 +1007,8 @@ Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
 {
     EdgeK k = make_k(x);
-    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, s) : dispatch_edge<float>(k, s);
+    hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, x.persist, s)
+                                    : dispatch_edge<float>(k, x.persist, s);
     return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 

@@ -16,6 +16,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "pma_internal.h"
 
 namespace pma {
@@ -215,6 +217,30 @@ __global__ void csr_fill(const int32_t *perm, const int32_t *src, const int32_t 
     }
 }
 
+// Sources that some edge reads (used[s] = 1), their compact numbering and
+// the edges' sources in that numbering (the key/value workspace then holds
+// only rows that are read).
+__global__ void mark_used(const int32_t *csr_src, int64_t nnz, int32_t *used)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < nnz)
+        used[csr_src[p]] = 1;   // every writer stores the same value
+}
+
+__global__ void kv_rows_fill(const int32_t *used, const int32_t *kv_map, int64_t S, int32_t *kv_rows)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < S && used[s])
+        kv_rows[kv_map[s]] = (int32_t)s;
+}
+
+__global__ void kv_remap(const int32_t *csr_src, const int32_t *kv_map, int64_t nnz, int32_t *csr_kv)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < nnz)
+        csr_kv[p] = kv_map[csr_src[p]];
+}
+
 // Per target: number of pieces, partial slots and split flag.
 __global__ void split_count_kernel(const int32_t *deg, int64_t L, int chunk, int32_t *n_piece,
                                    int32_t *n_slot, int32_t *is_split, int32_t *max_deg)
@@ -328,7 +354,8 @@ void free_graph(GraphDev *g)
 {
     int32_t **ptrs[] = {&g->row_ptr,     &g->csr_src,     &g->csr_tgt,    &g->csr_eid,
                         &g->task_target, &g->task_begin,  &g->task_end,   &g->task_slot,
-                        &g->task_split,  &g->split_target, &g->split_slot0, &g->split_count};
+                        &g->task_split,  &g->split_target, &g->split_slot0, &g->split_count,
+                        &g->csr_kv,      &g->kv_rows};
     for (int32_t **p : ptrs) {
         if (*p)
             (void)hipFree(*p);
@@ -347,14 +374,17 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     int32_t *piece_base = nullptr, *slot_base = nullptr, *split_base = nullptr;
     int32_t *t_target = nullptr, *t_begin = nullptr, *t_end = nullptr, *t_slot = nullptr,
             *t_split = nullptr, *t_key = nullptr, *tperm = nullptr, *tperm_tmp = nullptr;
+    int32_t *used = nullptr, *kv_map = nullptr;
     int32_t h_small[8] = {0};
-    const int64_t n_sort = nnz > L ? nnz : L;
+    // longest array any scan below sees
+    const int64_t n_sort = std::max(std::max(nnz, L), S);
     const int64_t ntiles = (n_sort + kTile - 1) / kTile;
     const int64_t count_len = 256 * ntiles;
     const int64_t scan_len = (count_len > n_sort ? count_len : n_sort) / kTile + 2;
     const size_t i4 = sizeof(int32_t);
 
-    // small[]: 0 dup flag, 1 n_tasks, 2 n_slots, 3 n_split, 4 max degree, 5 nnz total
+    // small[]: 0 dup flag, 1 n_tasks, 2 n_slots, 3 n_split, 4 max degree,
+    // 5 distinct sources read
     PMA_TRY(hipMalloc(&d_src, nnz * i4));
     PMA_TRY(hipMalloc(&d_tgt, nnz * i4));
     PMA_TRY(hipMalloc(&perm, nnz * i4));
@@ -376,6 +406,12 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     PMA_TRY(hipMalloc(&piece_base, L * i4));
     PMA_TRY(hipMalloc(&slot_base, L * i4));
     PMA_TRY(hipMalloc(&split_base, L * i4));
+    PMA_TRY(hipMalloc(&used, S * i4));
+    PMA_TRY(hipMalloc(&kv_map, S * i4));
+    PMA_TRY(hipMalloc(&g->kv_rows, S * i4));
+    PMA_TRY(hipMalloc(&g->csr_kv, (nnz + kSrcPad) * i4));
+    PMA_TRY(hipMemsetAsync(g->csr_kv + nnz, 0, kSrcPad * i4, stream));
+    PMA_TRY(hipMemsetAsync(used, 0, S * i4, stream));
 
     PMA_TRY(hipMemcpyAsync(d_src, h_src, nnz * i4, hipMemcpyHostToDevice, stream));
     PMA_TRY(hipMemcpyAsync(d_tgt, h_tgt, nnz * i4, hipMemcpyHostToDevice, stream));
@@ -388,6 +424,11 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     PMA_TRY(radix_sort_perm(d_tgt, bits_for(L - 1), perm, perm_tmp, nnz, counts, scan_tmp, stream));
     csr_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, d_src, d_tgt, nnz, g->csr_src,
                                                      g->csr_tgt, g->csr_eid, small + 0);
+    // 1b. compact numbering of the sources that are read
+    mark_used<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, nnz, used);
+    PMA_TRY(scan_exclusive(used, kv_map, S, small + 5, scan_tmp, stream));
+    kv_rows_fill<<<grid_for(S, 256), 256, 0, stream>>>(used, kv_map, S, g->kv_rows);
+    kv_remap<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, kv_map, nnz, g->csr_kv);
     // 2. row pointers
     degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(d_tgt, nnz, deg);
     PMA_TRY(scan_exclusive(deg, g->row_ptr, L, g->row_ptr + L, scan_tmp, stream));
@@ -409,6 +450,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     g->n_slots = h_small[2];
     g->n_split = h_small[3];
     g->max_degree = h_small[4];
+    g->n_kv = h_small[5];
     {
         const int64_t nt = g->n_tasks, ns = g->n_split > 0 ? g->n_split : 1;
         PMA_TRY(hipMalloc(&t_target, nt * i4));
@@ -461,7 +503,7 @@ done:
         int32_t *tmps[] = {d_src,     d_tgt,     perm,       perm_tmp,   counts,   scan_tmp,
                            deg,       small,     n_piece,    n_slot,     is_split, piece_base,
                            slot_base, split_base, t_target,  t_begin,    t_end,    t_slot,
-                           t_split,   t_key,     tperm,      tperm_tmp};
+                           t_split,   t_key,     tperm,      tperm_tmp, used,     kv_map};
         for (int32_t *p : tmps)
             if (p)
                 (void)hipFree(p);

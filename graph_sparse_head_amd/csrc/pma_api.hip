@@ -45,6 +45,8 @@ struct pma_plan {
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
     int nt = 1;                 // PMA_NT=0: cached q loads / mixed stores
+    int persist = 0;            // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece)
+    int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
     // workspace, grown on demand
@@ -230,6 +232,10 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     //   PMA_XCD_MAP    1 / 0: force or forbid one sample group per XCD
     //   PMA_NT         0: cached instead of non-temporal q / mixed streams
     //   PMA_LAYOUT     "batch": batch-first q / k / v / mixed workspace
+    //   PMA_PERSIST    n: at most n edge-kernel workgroups per CU, each
+    //                  wavefront walking several pieces (0: one per piece)
+    //   PMA_COMPACT    1 / 0: force or forbid projecting keys and values only
+    //                  for the sources some edge reads
     if (const char *ev = getenv("PMA_CHUNK")) {
         const long c = strtol(ev, nullptr, 10);
         if (c >= 1 && c <= 65535)
@@ -243,6 +249,13 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
         p->nt = ev[0] != '0';
     if (const char *ev = getenv("PMA_LAYOUT"))
         p->batch_first_ws = strcmp(ev, "batch") == 0;
+    if (const char *ev = getenv("PMA_COMPACT"))
+        p->compact = ev[0] == '0' ? 0 : 1;
+    if (const char *ev = getenv("PMA_PERSIST")) {
+        const long c = strtol(ev, nullptr, 10);
+        if (c >= 0 && c <= 64)
+            p->persist = (int)c;
+    }
     if (p->nnz + L > kI32) {
         delete p;
         return fail(PMA_E_UNSUPPORTED, "nnz + query_features exceeds 2^31 - 1");
@@ -313,6 +326,7 @@ PMA_API pma_status pma_plan_info(const pma_plan *plan, pma_info *info)
     info->n_split = plan->g.n_split;
     info->n_slots = plan->g.n_slots;
     info->max_degree = plan->g.max_degree;
+    info->kv_rows = plan->g.n_kv;
     return PMA_OK;
 }
 
@@ -392,10 +406,20 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     StageTimer tm{p, stream};
     const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
     char *kvc = static_cast<char *>(p->kv);
-    const pma::Layout lay = pma::make_layout(p->batch_first_ws, B, L, S, E);
+    // Keys and values are needed only for the sources some edge reads
+    // (n_kv of S). Projecting just those rows saves work unless query, key
+    // and value are one tensor and most sources are read: then one pass over
+    // the tokens that writes q, k and v at once moves fewer bytes (a separate
+    // key/value pass re-reads n_kv / S of the tokens; it pays below 3/5).
+    const bool shared = query == key && key == value && L == S;
+    const int64_t n_kv = p->g.n_kv;
+    const bool compact = n_kv < S && (p->compact >= 0 ? p->compact == 1 : (!shared || 5 * n_kv < 3 * S));
+    const int64_t S_ws = compact ? n_kv : S;   // key/value rows in the workspace
+    const pma::Layout lay = pma::make_layout(p->batch_first_ws, B, L, S_ws, E);
 
     // Step 1: q, k, v projections into the workspace layout. Caller tokens are
-    // batch-first and read in storage order.
+    // batch-first and read in storage order (key/value rows through the list
+    // of read sources when compact).
     tm.begin(PMA_STAGE_PROJ_IN);
     const pma::ProjOut oq{q_w, q_b, p->qt, lay.q_b, lay.q_t};
     const pma::ProjOut ok{k_w, k_b, kvc, lay.kv_b, lay.kv_s};
@@ -406,16 +430,24 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
         a.x_token_major = 0;
         return a;
     };
-    if (query == key && key == value && L == S) {
+    auto kv_args = [&](const void *x, int nblk, pma::ProjOut o0, pma::ProjOut o1) {
+        pma::ProjArgs a = in_args(x, S_ws, nblk, o0, o1, o1);
+        if (compact) {
+            a.row_list = p->g.kv_rows;
+            a.n_in = S;
+        }
+        return a;
+    };
+    if (shared && !compact) {
         st = pma::launch_proj(in_args(query, L, 3, oq, ok, ov), E, p->dtype, stream);
     } else {
         st = pma::launch_proj(in_args(query, L, 1, oq, oq, oq), E, p->dtype, stream);
         if (st == PMA_OK && key == value) {
-            st = pma::launch_proj(in_args(key, S, 2, ok, ov, ov), E, p->dtype, stream);
+            st = pma::launch_proj(kv_args(key, 2, ok, ov), E, p->dtype, stream);
         } else if (st == PMA_OK) {
-            st = pma::launch_proj(in_args(key, S, 1, ok, ok, ok), E, p->dtype, stream);
+            st = pma::launch_proj(kv_args(key, 1, ok, ok), E, p->dtype, stream);
             if (st == PMA_OK)
-                st = pma::launch_proj(in_args(value, S, 1, ov, ov, ov), E, p->dtype, stream);
+                st = pma::launch_proj(kv_args(value, 1, ov, ov), E, p->dtype, stream);
         }
     }
     tm.end();
@@ -424,6 +456,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
 
     pma::EdgeArgs ea;
     ea.g = &p->g;
+    ea.gather_src = compact ? p->g.csr_kv : p->g.csr_src;
     ea.B = B;
     ea.L = L;
     ea.S = S;
@@ -434,7 +467,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.lay = lay;
     ea.qt = p->qt;
     ea.kv = p->kv;
-    ea.kv_bytes = (uint64_t)p->S * 2 * B * E * es;
+    ea.kv_bytes = (uint64_t)S_ws * 2 * B * E * es;
     ea.mixed = p->mixed;
     ea.part_acc = p->part_acc;
     ea.part_ml = p->part_ml;
@@ -443,6 +476,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.weights = weights;
     ea.average = average_attn_weights;
     ea.nt = p->nt;
+    ea.persist = p->persist;
     // out_proj in the edge / merge epilogue where it applies (16-byte aligned
     // Wo and out).
     ea.fuse_out = p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
@@ -454,7 +488,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     // the L2s; it pays once the keys and values outgrow the 256 MB last-level
     // cache (measured: large and bipartite workloads gain, the gene one loses).
     ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map
-                                 : (2.0 * S * B * E * es > 256.0 * 1024 * 1024 ? 1 : 0);
+                                 : (2.0 * S_ws * B * E * es > 256.0 * 1024 * 1024 ? 1 : 0);
 
     // Steps 2-4 (and 5 when fused): scores, softmax and mix over the live edges.
     tm.begin(PMA_STAGE_EDGE);

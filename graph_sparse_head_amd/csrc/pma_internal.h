@@ -22,7 +22,10 @@ struct GraphDev {
     int32_t *task_target = nullptr, *task_begin = nullptr, *task_end = nullptr,
             *task_slot = nullptr, *task_split = nullptr; // n_tasks each; split index or -1
     int32_t *split_target = nullptr, *split_slot0 = nullptr, *split_count = nullptr; // n_split
-    int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0;
+    // Sources some edge reads, in ascending order (kv_rows[0, n_kv)), and each
+    // CSR entry's source as a position in that list (csr_kv, + kSrcPad zeros).
+    int32_t *kv_rows = nullptr, *csr_kv = nullptr;
+    int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0, n_kv = 0;
 };
 
 // Builds every array of GraphDev from host edges (already validated, loops
@@ -58,6 +61,10 @@ struct ProjArgs {
     int nblk;         // 1..3 output blocks
     ProjOut out[3];
     int x_token_major = -1;  // -1: same as token_major (rows read in storage order)
+    // With a row list, iteration token i of sample b reads input row
+    // b * n_in + row_list[i] (batch-first input of n_in tokens per sample).
+    const int32_t *row_list = nullptr;
+    int64_t n_in = 0;
 };
 
 pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s);
@@ -77,6 +84,7 @@ Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)
 
 struct EdgeArgs {
     const GraphDev *g;
+    const int32_t *gather_src;  // per CSR entry, the key/value workspace row it reads
     int64_t B, L, S, E, H, nnz;
     pma_dtype dt;
     Layout lay;
@@ -92,6 +100,8 @@ struct EdgeArgs {
     int average;
     int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
     int nt = 1;         // non-temporal q loads / mixed stores
+    int persist = 0;    // edge kernel: workgroups per CU, each wavefront walking
+                        // several pieces (0: one wavefront per piece and pass)
     // out_proj fused into the edge and merge kernels (out_fusable)
     int fuse_out = 0;
     const void *wo = nullptr, *bo = nullptr;

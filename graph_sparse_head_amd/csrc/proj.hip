@@ -42,6 +42,10 @@ template <> struct Elem<uint16_t> {
 // Input row of iteration row r.
 __device__ inline int64_t in_row(const ProjArgs &a, int64_t r)
 {
+    if (a.row_list) {   // batch-first input, iteration rows (sample, listed token)
+        const int64_t b = r / a.n, i = r - b * a.n;
+        return b * a.n_in + a.row_list[i];
+    }
     if (a.x_token_major < 0 || a.x_token_major == a.token_major)
         return r;
     int64_t b, i;

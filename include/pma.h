@@ -170,6 +170,8 @@ typedef struct {
     int64_t n_split;    /* targets split into more than one piece */
     int64_t n_slots;    /* partial-result slots of the split targets */
     int64_t max_degree; /* largest in-degree */
+    int64_t kv_rows;    /* distinct sources the edges read: the key/value rows a
+                           forward projects when it skips unread sources */
 } pma_info;
 
 pma_status pma_plan_info(const pma_plan *plan, pma_info *info);

@@ -209,6 +209,10 @@ def test_full_size_sampled(name):
 # every tuning knob gives the same results (read at plan creation)
 
 KNOBS = [
+    {},
+    {"PMA_COMPACT": "0"},
+    {"PMA_COMPACT": "1", "PMA_LAYOUT": "batch"},
+    {"PMA_PERSIST": "1"},
     {"PMA_FUSE_OUT": "0"},
     {"PMA_LAYOUT": "batch"},
     {"PMA_LAYOUT": "batch", "PMA_FUSE_OUT": "0"},
@@ -226,10 +230,24 @@ def test_tuning_knobs(knobs, shape, monkeypatch):
         monkeypatch.setenv(k, v)
     dt, E, H = shape
     c = synth.random_case(50, 5, 220, 220, E, H, 0.04, dtype=dt, name="knobs")
-    # two hub targets so that small chunks split them
+    # two hub targets so that small chunks split them; sources 120.. are never
+    # read, so that keys and values are projected for the read ones only
     rng = np.random.default_rng(51)
-    hub_src = rng.choice(220, size=150, replace=False)
-    keep = ~np.isin(c.tgt, [3, 17])
-    c.src = np.concatenate([c.src[keep], hub_src, hub_src[:90]])
-    c.tgt = np.concatenate([c.tgt[keep], np.full(150, 3), np.full(90, 17)])
+    hub_src = rng.choice(120, size=100, replace=False)
+    keep = ~np.isin(c.tgt, [3, 17]) & (c.src < 120)
+    c.src = np.concatenate([c.src[keep], hub_src, hub_src[:60]])
+    c.tgt = np.concatenate([c.tgt[keep], np.full(100, 3), np.full(60, 17)])
     _full_check(c, need_weights=True, average=False)
+
+
+@pytest.mark.parametrize("knobs", [{"PMA_PERSIST": "1"}, {"PMA_PERSIST": "1", "PMA_XCD_MAP": "1"},
+                                   {"PMA_PERSIST": "2", "PMA_CHUNK": "5"}],
+                         ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_wavefront_walks_pieces(knobs, dt, monkeypatch):
+    # More pieces than wavefronts: each wavefront of the edge kernel walks
+    # several pieces (its next piece's bounds and query fetched ahead).
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, v)
+    c = synth.random_case(52, 4, 6000, 6000, 64, 4, 0.0015, dtype=dt, name="walk")
+    _full_check(c, need_weights=True, average=True)

@@ -31,6 +31,7 @@ def _check_plan(src0, tgt0, L, S, E=8, H=2, loops=False):
             assert (ws[k] == ows[k]).all(), k
         assert ws["n_slots"] == ows["n_slots"]
         assert info["max_degree"] == int(np.diff(orp).max())
+        assert info["kv_rows"] == np.unique(src).shape[0]
     finally:
         pma.pma_destroy(plan)
 
