@@ -19,6 +19,7 @@ import numpy as np
 __all__ = [
     "PmaError", "Plan", "pma_create", "pma_forward", "pma_destroy", "pma_nnz", "pma_edges",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
+    "pma_profile_stages",
     "pma_profile_read", "STATUS", "STAGES", "library_path",
 ]
 
@@ -79,6 +80,7 @@ def _load():
         "pma_csr": (st, [P, P, P, P]),
         "pma_work_split": (st, [P] + [P] * 7),
         "pma_profile": (st, [P, I32]),
+        "pma_profile_stages": (st, [P, ctypes.c_uint32]),
         "pma_profile_read": (st, [P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -275,6 +277,14 @@ def pma_work_split(plan: Plan) -> dict:
 
 def pma_profile(plan: Plan, enable: bool) -> None:
     _check(_load().pma_profile(plan.handle, int(bool(enable))))
+
+
+def pma_profile_stages(plan: Plan, stages) -> None:
+    """Time only the named stages (an iterable of names from STAGES)."""
+    mask = 0
+    for name in stages:
+        mask |= 1 << STAGES.index(name)
+    _check(_load().pma_profile_stages(plan.handle, mask))
 
 
 def pma_profile_read(plan: Plan) -> dict:

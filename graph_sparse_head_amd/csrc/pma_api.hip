@@ -44,8 +44,8 @@ struct pma_plan {
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
-    int nt = 1;                 // PMA_NT=0: cached q loads / mixed stores
-    int persist = 0;            // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece)
+    int nt = -1;                // PMA_NT: non-temporal (1) or cached (0) q / mixed streams, auto (-1)
+    int persist = -1;           // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece, -1 auto)
     int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
@@ -55,7 +55,7 @@ struct pma_plan {
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
     // profiling
-    bool prof = false;
+    unsigned prof = 0;   // stages timed: bit s for stage s
     std::vector<EventPair> pending;
     std::vector<hipEvent_t> pool;
     double ms[PMA_NUM_STAGES] = {0};
@@ -136,7 +136,7 @@ struct StageTimer {
     EventPair cur{nullptr, nullptr, -1};
     void begin(int stage)
     {
-        if (!p->prof)
+        if (!((p->prof >> stage) & 1u))
             return;
         cur.a = take_event(p);
         cur.b = take_event(p);
@@ -230,7 +230,7 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     //   PMA_CHUNK      most edges per piece of a target (1..65535)
     //   PMA_FUSE_OUT   0: out_proj as a separate kernel
     //   PMA_XCD_MAP    1 / 0: force or forbid one sample group per XCD
-    //   PMA_NT         0: cached instead of non-temporal q / mixed streams
+    //   PMA_NT         1 / 0: non-temporal or cached q / mixed streams
     //   PMA_LAYOUT     "batch": batch-first q / k / v / mixed workspace
     //   PMA_PERSIST    n: at most n edge-kernel workgroups per CU, each
     //                  wavefront walking several pieces (0: one per piece)
@@ -246,7 +246,7 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     if (const char *ev = getenv("PMA_XCD_MAP"))
         p->xcd_map = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_NT"))
-        p->nt = ev[0] != '0';
+        p->nt = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_LAYOUT"))
         p->batch_first_ws = strcmp(ev, "batch") == 0;
     if (const char *ev = getenv("PMA_COMPACT"))
@@ -475,8 +475,13 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
-    ea.nt = p->nt;
-    ea.persist = p->persist;
+    // Automatic choices (measured on MI355X): stream q and mixed past the
+    // caches only when the workspace outgrows the 256 MB last-level cache;
+    // keep the edge kernel's wavefronts resident and walking pieces when
+    // pieces are short (then per-piece start-up latency dominates).
+    const double ws_bytes = ((double)L + 2.0 * S_ws) * B * E * es;
+    ea.nt = p->nt >= 0 ? p->nt : (ws_bytes > 256.0 * 1024 * 1024 ? 1 : 0);
+    ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 12 : 0);
     // out_proj in the edge / merge epilogue where it applies (16-byte aligned
     // Wo and out).
     ea.fuse_out = p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
@@ -484,11 +489,10 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.wo = o_w;
     ea.bo = o_b;
     ea.out = out;
-    // Pinning sample groups to XCDs splits each source's key/value row across
-    // the L2s; it pays once the keys and values outgrow the 256 MB last-level
-    // cache (measured: large and bipartite workloads gain, the gene one loses).
-    ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map
-                                 : (2.0 * S_ws * B * E * es > 256.0 * 1024 * 1024 ? 1 : 0);
+    // Pinning sample groups to XCDs (where the group count divides 8) gives
+    // each L2 the rows of one sample group only; measured faster on all three
+    // full-size workloads.
+    ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map : 1;
 
     // Steps 2-4 (and 5 when fused): scores, softmax and mix over the live edges.
     tm.begin(PMA_STAGE_EDGE);
@@ -529,7 +533,17 @@ PMA_API pma_status pma_profile(pma_plan *plan, int enable)
         return fail(PMA_E_NULL, "plan is NULL");
     if (enable != 0 && enable != 1)
         return fail(PMA_E_ARG, "enable must be 0 or 1");
-    plan->prof = enable != 0;
+    plan->prof = enable ? (1u << PMA_NUM_STAGES) - 1u : 0u;
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_profile_stages(pma_plan *plan, unsigned mask)
+{
+    if (!plan)
+        return fail(PMA_E_NULL, "plan is NULL");
+    if (mask >> PMA_NUM_STAGES)
+        return fail(PMA_E_ARG, "mask has bits beyond the %d stages", (int)PMA_NUM_STAGES);
+    plan->prof = mask;
     return PMA_OK;
 }
 

@@ -199,6 +199,12 @@ pma_status pma_work_split(const pma_plan *plan, int64_t *task_target, int64_t *t
    records events around its stages on its own stream. */
 pma_status pma_profile(pma_plan *plan, int enable);
 
+/* Time only the stages in `mask` (bit s for stage s; 0 turns timing off).
+   Each timed stage adds two event records per forward on its stream, which
+   themselves take some microseconds. Errors: PMA_E_NULL, PMA_E_ARG (bits
+   beyond PMA_NUM_STAGES). */
+pma_status pma_profile_stages(pma_plan *plan, unsigned mask);
+
 /* Wait for the recorded events, then return per stage the summed elapsed
    milliseconds (ms[PMA_NUM_STAGES]) and launches timed (calls[PMA_NUM_STAGES])
    since the last read, and reset the sums. */

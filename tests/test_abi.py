@@ -109,3 +109,4 @@ def test_null_plan_calls():
     calls = np.zeros(5, np.int64)
     assert pma.STATUS[lib.pma_profile_read(None, ms.ctypes.data, calls.ctypes.data)] == "PMA_E_NULL"
     assert pma.STATUS[lib.pma_edges(None, None, None)] == "PMA_E_NULL"
+    assert pma.STATUS[lib.pma_profile_stages(None, 1)] == "PMA_E_NULL"

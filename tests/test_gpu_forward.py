@@ -213,6 +213,7 @@ KNOBS = [
     {"PMA_COMPACT": "0"},
     {"PMA_COMPACT": "1", "PMA_LAYOUT": "batch"},
     {"PMA_PERSIST": "1"},
+    {"PMA_NT": "1", "PMA_PERSIST": "0"},
     {"PMA_FUSE_OUT": "0"},
     {"PMA_LAYOUT": "batch"},
     {"PMA_LAYOUT": "batch", "PMA_FUSE_OUT": "0"},
