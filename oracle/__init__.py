@@ -66,7 +66,7 @@ def _load():
     i64 = ctypes.c_int64
     lib.oracle_forward.restype = ctypes.c_int
     lib.oracle_forward.argtypes = [i64] * 5 + [p] * 3 + [p] * 8 + [i64, p, p] + [i64, p, p] + \
-        [p, p, p, ctypes.c_int]
+        [p, p, p, p, i64, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -232,13 +232,16 @@ def _ptr(a):
 
 def forward(B: int, L: int, S: int, E: int, H: int, xq, xk, xv, params: Dict[str, Optional[np.ndarray]],
             src, tgt, rows: Optional[np.ndarray] = None, want_weights: bool = False,
-            want_mixed: bool = False, nthreads: int = 0):
+            want_mixed: bool = False, nthreads: int = 0, key_padding_mask=None):
     """Packed multi-head attention forward in double precision.
 
     xq (B, L, E), xk / xv (B, S, E) float64; params wq bq wk bk wv bv wo bo
     (biases all present or all None); src / tgt the final edge list (see
     ``prepare_edges``). ``rows`` is an (n, 2) array of (sample, target) pairs
     to compute, or None for every row.
+
+    ``key_padding_mask``: None, or a boolean (S,) mask shared by every sample
+    or (B, S) per sample; True leaves that key out of the sample's softmax.
 
     Returns dict: "out" (n, E) or (B, L, E) when rows is None; "mixed" the
     joined heads before out_proj (same shape) if asked; "weights" (B, nnz, H)
@@ -267,6 +270,18 @@ def forward(B: int, L: int, S: int, E: int, H: int, xq, xk, xv, params: Dict[str
         rb = np.ascontiguousarray(rows[:, 0])
         rt = np.ascontiguousarray(rows[:, 1])
         assert (rb >= 0).all() and (rb < B).all() and (rt >= 0).all() and (rt < L).all()
+    kpm, kstride = None, 0
+    if key_padding_mask is not None:
+        km = np.asarray(key_padding_mask)
+        if km.dtype != np.bool_:
+            raise OracleError("arg", "key_padding_mask must be boolean")
+        if km.shape == (S,):
+            kstride = 0
+        elif km.shape == (B, S):
+            kstride = S
+        else:
+            raise OracleError("arg", f"key_padding_mask shape {km.shape} is not ({S},) or ({B}, {S})")
+        kpm = np.ascontiguousarray(km, np.uint8)
     out = np.empty((nrows, E), np.float64)
     mixed = np.empty((nrows, E), np.float64) if want_mixed else None
     weights = np.full((B, nnz, H), np.nan, np.float64) if want_weights else None
@@ -274,7 +289,8 @@ def forward(B: int, L: int, S: int, E: int, H: int, xq, xk, xv, params: Dict[str
                             _ptr(w["wq"]), _ptr(w["bq"]), _ptr(w["wk"]), _ptr(w["bk"]),
                             _ptr(w["wv"]), _ptr(w["bv"]), _ptr(w["wo"]), _ptr(w["bo"]),
                             nnz, _ptr(src), _ptr(tgt), nrows, _ptr(rb), _ptr(rt),
-                            _ptr(out), _ptr(mixed), _ptr(weights), int(nthreads))
+                            _ptr(out), _ptr(mixed), _ptr(weights), _ptr(kpm), int(kstride),
+                            int(nthreads))
     if rc != 0:
         raise MemoryError("oracle_forward ran out of memory")
     res = {"out": out if rows is not None else out.reshape(B, L, E)}
@@ -290,7 +306,8 @@ def average_heads(weights: np.ndarray) -> np.ndarray:
     return weights.mean(axis=-1)
 
 
-def case_forward(case, rows=None, want_weights=False, want_mixed=False, nthreads=0):
+def case_forward(case, rows=None, want_weights=False, want_mixed=False, nthreads=0,
+                 key_padding_mask=None):
     """``forward`` on a synthetic case (validates and appends loops first)."""
     src, tgt = prepare_edges(case.src, case.tgt, case.L, case.S, case.E, case.H,
                              case.add_self_loops)
@@ -300,6 +317,6 @@ def case_forward(case, rows=None, want_weights=False, want_mixed=False, nthreads
     xv = xk if case.xv is case.xk else widen(case.xv, case.dtype)
     res = forward(case.B, case.L, case.S, case.E, case.H, xq, xk, xv, params, src, tgt,
                   rows=rows, want_weights=want_weights, want_mixed=want_mixed,
-                  nthreads=nthreads)
+                  nthreads=nthreads, key_padding_mask=key_padding_mask)
     res["src"], res["tgt"] = src, tgt
     return res

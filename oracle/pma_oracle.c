@@ -19,6 +19,11 @@
  * A target with no live edge mixes to zeros, so its output is the out_proj
  * bias (same page, Notes, on queries with no live keys).
  *
+ * key_padding_mask (same page, forward parameter table and Notes step 3):
+ * for sample b, a key s with mask[b][s] set takes no part; the edges from it
+ * drop out of that sample's softmax (weight 0), and a target left with no
+ * edge mixes to zeros as above.
+ *
  * Every computed row is independent, so rows may be computed in parallel
  * (OpenMP); each row's arithmetic is sequential in edge order.
  */
@@ -66,6 +71,9 @@ int oracle_num_threads(int nthreads)
  *   mixed (nrows, E) or NULL: the joined heads before out_proj.
  *   weights (B, nnz, H) or NULL: per-head softmax weight of every edge into a
  *     requested row; entries of other edges are left untouched.
+ *   kpm: NULL, or key_padding_mask bytes, sample b's at kpm + b * kpm_bstride
+ *     (kpm_bstride = 0: one mask for every sample), S per sample; nonzero
+ *     means the key is left out.
  *
  * Returns 0, or -1 when memory runs out.
  */
@@ -75,7 +83,8 @@ int oracle_forward(int64_t B, int64_t L, int64_t S, int64_t E, int64_t H,
                    const double *wv, const double *bv, const double *wo, const double *bo,
                    int64_t nnz, const int64_t *src, const int64_t *tgt,
                    int64_t nrows, const int64_t *row_b, const int64_t *row_t,
-                   double *out, double *mixed, double *weights, int nthreads)
+                   double *out, double *mixed, double *weights,
+                   const unsigned char *kpm, int64_t kpm_bstride, int nthreads)
 {
     const int64_t d = E / H;
     const double sqrt_d = sqrt((double)d);
@@ -150,9 +159,17 @@ int oracle_forward(int64_t B, int64_t L, int64_t S, int64_t E, int64_t H,
             linear_row(E, xq + (b * L + t) * E, wq, bq, q);
             for (int64_t h = 0; h < H; ++h) {
                 const double *qh = q + h * d;
-                /* Step 2: one score per live edge into t. */
+                /* Step 2: one score per live edge into t (left out: keys that
+                   the mask drops for this sample). */
+                int64_t live = 0;
                 for (int64_t j = 0; j < deg; ++j) {
-                    const double *kh = K + (b * S + src[into_t[first[t] + j]]) * E + h * d;
+                    const int64_t s = src[into_t[first[t] + j]];
+                    if (kpm && kpm[b * kpm_bstride + s]) {
+                        score[j] = -INFINITY;
+                        continue;
+                    }
+                    ++live;
+                    const double *kh = K + (b * S + s) * E + h * d;
                     double dot = 0.0;
                     for (int64_t c = 0; c < d; ++c)
                         dot += qh[c] * kh[c];
@@ -165,14 +182,16 @@ int oracle_forward(int64_t B, int64_t L, int64_t S, int64_t E, int64_t H,
                         m = score[j];
                 double den = 0.0;
                 for (int64_t j = 0; j < deg; ++j)
-                    den += exp(score[j] - m);
+                    if (score[j] != -INFINITY)
+                        den += exp(score[j] - m);
                 for (int64_t j = 0; j < deg; ++j)
-                    w[j] = exp(score[j] - m) / den;
+                    w[j] = (live > 0 && score[j] != -INFINITY) ? exp(score[j] - m) / den : 0.0;
                 /* Step 4: mix the sources' values (zeros with no edge). */
                 for (int64_t c = 0; c < d; ++c) {
                     double acc = 0.0;
                     for (int64_t j = 0; j < deg; ++j)
-                        acc += w[j] * V[(b * S + src[into_t[first[t] + j]]) * E + h * d + c];
+                        if (w[j] != 0.0)
+                            acc += w[j] * V[(b * S + src[into_t[first[t] + j]]) * E + h * d + c];
                     mix[h * d + c] = acc;
                 }
                 if (weights)

@@ -30,11 +30,12 @@ def _params64(rng, E, bias=True):
     return p
 
 
-def _torch_mha(E, H, params, xq, xk, xv, mask=None):
+def _torch_mha(E, H, params, xq, xk, xv, mask=None, key_padding_mask=None):
     """torch.nn.MultiheadAttention in float64 loaded with the same weights.
 
-    mask: bool (L, S), True where the pair is not an edge. Returns output
-    (B, L, E) and per-head weights (B, H, L, S)."""
+    mask: bool (L, S), True where the pair is not an edge; key_padding_mask:
+    bool (B, S), True where the key is left out. Returns output (B, L, E) and
+    per-head weights (B, H, L, S)."""
     bias = params["bq"] is not None
     mha = torch.nn.MultiheadAttention(E, H, bias=bias, batch_first=True).double()
     with torch.no_grad():
@@ -47,9 +48,11 @@ def _torch_mha(E, H, params, xq, xk, xv, mask=None):
             mha.out_proj.bias.copy_(torch.from_numpy(params["bo"]))
     mha.train(False)
     m = None if mask is None else torch.from_numpy(mask)
+    kpm = None if key_padding_mask is None else torch.from_numpy(key_padding_mask)
     with torch.no_grad():
         out, w = mha(torch.from_numpy(xq), torch.from_numpy(xk), torch.from_numpy(xv),
-                     attn_mask=m, need_weights=True, average_attn_weights=False)
+                     attn_mask=m, key_padding_mask=kpm, need_weights=True,
+                     average_attn_weights=False)
     return out.numpy(), w.numpy()
 
 
@@ -122,6 +125,85 @@ def test_masked_dense_mha(seed):
     # per-head weights gathered at the live pairs
     np.testing.assert_allclose(res["weights"], np.transpose(t_w[:, :, tgt, src], (0, 2, 1)),
                                rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# key_padding_mask (kpnn2 page, forward parameter table; Notes step 3 and the
+# paragraph on queries with no live keys)
+
+
+def _mask_case(seed):
+    rng = np.random.default_rng(5000 + seed)
+    H = int(rng.choice([1, 2, 4]))
+    E = H * int(rng.choice([1, 2, 3]))
+    L = int(rng.integers(2, 12))
+    S = L if rng.random() < 0.5 else int(rng.integers(2, 12))
+    B = int(rng.integers(1, 4))
+    src, tgt = synth.random_graph(rng, L, S, float(rng.uniform(0.2, 0.8)))
+    if src.size == 0:
+        src, tgt = np.array([0], np.int64), np.array([0], np.int64)
+    params = _params64(rng, E, bias=bool(rng.random() < 0.8))
+    xq = rng.standard_normal((B, L, E))
+    xk = xq if (S == L and rng.random() < 0.5) else rng.standard_normal((B, S, E))
+    xv = xk if rng.random() < 0.5 else rng.standard_normal((B, S, E))
+    kpm = rng.random((B, S)) < float(rng.uniform(0.1, 0.6))
+    return B, L, S, E, H, params, xq, xk, xv, src, tgt, kpm
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_key_padding_mask_vs_torch(seed):
+    B, L, S, E, H, params, xq, xk, xv, src, tgt, kpm = _mask_case(seed)
+    res = _run(E, H, params, xq, xk, xv, src, tgt, want_weights=True, key_padding_mask=kpm)
+    pair = np.ones((L, S), bool)
+    pair[tgt, src] = False
+    t_out, t_w = _torch_mha(E, H, params, xq, xk, xv, pair, kpm)
+    live = np.zeros((B, L), bool)          # (b, t) with some unmasked source
+    for b in range(B):
+        keep = ~kpm[b, src]
+        live[b, np.unique(tgt[keep])] = True
+    np.testing.assert_allclose(res["out"][live], t_out[live], rtol=0, atol=1e-12)
+    # every masked edge weighs exactly 0; live rows' weights match torch
+    w = res["weights"]
+    for b in range(B):
+        assert (w[b][kpm[b, src]] == 0).all()
+        rows_live = live[b, tgt]
+        tw = np.transpose(t_w[b][:, tgt, src], (1, 0))
+        np.testing.assert_allclose(w[b][rows_live], tw[rows_live], rtol=0, atol=1e-12)
+    # a target whose sources are all masked outputs exactly the out_proj bias
+    bo = np.zeros(E) if params["bo"] is None else params["bo"]
+    assert (res["out"][~live] == bo).all()
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_key_padding_mask_is_edge_removal(seed):
+    # Masking a key for one sample equals deleting its edges for that sample.
+    B, L, S, E, H, params, xq, xk, xv, src, tgt, kpm = _mask_case(seed)
+    res = _run(E, H, params, xq, xk, xv, src, tgt, want_weights=True, key_padding_mask=kpm)
+    for b in range(B):
+        keep = ~kpm[b, src]
+        if not keep.any():
+            continue
+        r = oracle.forward(1, L, S, E, H, xq[b:b + 1], xk[b:b + 1], xv[b:b + 1], params,
+                           src[keep], tgt[keep], want_weights=True)
+        np.testing.assert_allclose(res["out"][b], r["out"][0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(res["weights"][b][keep], r["weights"][0], rtol=0, atol=1e-13)
+
+
+def test_key_padding_mask_shapes():
+    B, L, S, E, H, params, xq, xk, xv, src, tgt, kpm = _mask_case(3)
+    # all False is the unmasked forward, bit for bit
+    a = _run(E, H, params, xq, xk, xv, src, tgt, key_padding_mask=np.zeros((B, S), bool))
+    b = _run(E, H, params, xq, xk, xv, src, tgt)
+    assert (a["out"] == b["out"]).all()
+    # one (S,) mask applies to every sample
+    shared = kpm[0]
+    c = _run(E, H, params, xq, xk, xv, src, tgt, key_padding_mask=shared)
+    d = _run(E, H, params, xq, xk, xv, src, tgt, key_padding_mask=np.tile(shared, (B, 1)))
+    assert (c["out"] == d["out"]).all()
+    with pytest.raises(oracle.OracleError):
+        _run(E, H, params, xq, xk, xv, src, tgt, key_padding_mask=kpm.astype(np.float32))
+    with pytest.raises(oracle.OracleError):
+        _run(E, H, params, xq, xk, xv, src, tgt, key_padding_mask=np.zeros(S + 1, bool))
 
 
 # ---------------------------------------------------------------------------
@@ -496,11 +578,13 @@ MUTATIONS = {
     "transposed_weight": ("acc += x[i] * w[o * E + i];", "acc += x[i] * w[i * E + o];"),
     "no_sqrt_d": ("score[j] = dot / sqrt_d;", "score[j] = dot;"),
     "dropped_bias": ("y[o] = acc + (b ? b[o] : 0.0);", "y[o] = acc;"),
-    "key_from_target": ("const double *kh = K + (b * S + src[into_t[first[t] + j]]) * E + h * d;",
+    "key_from_target": ("const double *kh = K + (b * S + s) * E + h * d;",
                         "const double *kh = K + (b * S + t % S) * E + h * d;"),
     "value_wrong_head": ("V[(b * S + src[into_t[first[t] + j]]) * E + h * d + c]",
                          "V[(b * S + src[into_t[first[t] + j]]) * E + c]"),
-    "no_normalise": ("w[j] = exp(score[j] - m) / den;", "w[j] = exp(score[j] - m);"),
+    "no_normalise": ("exp(score[j] - m) / den : 0.0;", "exp(score[j] - m) : 0.0;"),
+    "mask_by_target": ("kpm[b * kpm_bstride + s]", "kpm[b * kpm_bstride + t % S]"),
+    "mask_ignored": ("if (kpm && kpm[b * kpm_bstride + s]) {", "if (0) {"),
 }
 
 
@@ -520,6 +604,10 @@ def test_pins_catch_planted_mistake(name, tmp_path, monkeypatch):
     for seed in range(12):
         try:
             test_masked_dense_mha(seed)
+        except AssertionError:
+            failures += 1
+        try:
+            test_key_padding_mask_vs_torch(seed)
         except AssertionError:
             failures += 1
     try:
