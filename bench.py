@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--config", default="gene",
                     choices=["tiny", "complete", "gene", "bipartite", "large"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--key-padding-mask", type=float, default=0.0, metavar="FRAC",
+                    help="mask this fraction of keys per sample (seeded); 0: no mask")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-stage events (no roofline)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -163,11 +165,16 @@ def main():
         shape = (case.B, nnz) if case.average else (case.B, nnz, case.H)
         weights = torch.empty(shape, dtype=torch.float32, device="cuda")
 
+    kpm = None
+    if args.key_padding_mask > 0:
+        kpm = torch.from_numpy(np.random.default_rng(3).random((case.B, case.S))
+                               < args.key_padding_mask).cuda()
+
     def step():
         pma.pma_forward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"],
                         dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"], out=out,
                         weights=weights, need_weights=case.need_weights,
-                        average_attn_weights=case.average)
+                        average_attn_weights=case.average, key_padding_mask=kpm)
 
     for _ in range(args.warmup):
         step()
@@ -224,7 +231,8 @@ def main():
         "dtype": case.dtype, "data": "synthetic",
         "config": {"workload": f"{case.name}: L={case.L} S={case.S} nnz={nnz} B={case.B} "
                                f"E={case.E} H={case.H} {case.dtype}"
-                               f"{' need_weights' if case.need_weights else ''}",
+                               f"{' need_weights' if case.need_weights else ''}"
+                               f"{f' key_padding_mask {args.key_padding_mask:g}' if kpm is not None else ''}",
                    "batch": case.B, "nodes": case.L, "nnz": nnz, "embed_dim": case.E,
                    "num_heads": case.H, "parallelism": "single GPU"},
     }

@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "PmaError", "Plan", "pma_create", "pma_forward", "pma_destroy", "pma_nnz", "pma_edges",
+    "PmaError", "Plan", "pma_create", "pma_forward", "pma_forward_masked", "pma_destroy",
+    "pma_nnz", "pma_edges",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
     "pma_profile_stages",
     "pma_profile_read", "STATUS", "STAGES", "library_path",
@@ -72,6 +73,8 @@ def _load():
     sig = {
         "pma_create": (st, [ctypes.POINTER(P), P, P, I64, I64, I64, I64, I64, I32, I32, P]),
         "pma_forward": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P]),
+        "pma_forward_masked": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, I32,
+                                    P]),
         "pma_destroy": (st, [P]),
         "pma_nnz": (I64, [P]),
         "pma_edges": (st, [P, P, P]),
@@ -184,12 +187,16 @@ def _dptr(t, name: str, dtype, shape_tail: Optional[Sequence[int]] = None):
 
 def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                 out=None, weights=None, need_weights: bool = False,
-                average_attn_weights: bool = True, stream=None):
-    """One forward pass (see ``pma_forward`` in include/pma.h).
+                average_attn_weights: bool = True, stream=None, key_padding_mask=None):
+    """One forward pass (see ``pma_forward`` / ``pma_forward_masked`` in
+    include/pma.h).
 
     query (..., L, E), key / value (..., S, E) contiguous GPU tensors of the
     plan's dtype with equal leading axes. ``out`` and ``weights`` may be given
-    (preallocated) or are allocated here. Returns (out, weights or None).
+    (preallocated) or are allocated here. ``key_padding_mask``: None, or a
+    boolean GPU tensor of shape (S,) (every sample) or (..., S) with the
+    query's leading axes; True leaves that key out. Returns (out, weights or
+    None).
     """
     import torch
     lib = _load()
@@ -217,11 +224,39 @@ def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w
         shape = lead + ((nnz,) if average_attn_weights else (nnz, H))
         weights = torch.empty(shape, dtype=torch.float32, device=query.device)
     wp = _dptr(weights, "weights", torch.float32) if want_w else None
-    st = lib.pma_forward(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1], wps[2],
-                         bps[2], wps[3], bps[3], op, wp, int(bool(average_attn_weights)),
-                         _stream_ptr(stream))
+    if key_padding_mask is None:
+        st = lib.pma_forward(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1], wps[2],
+                             bps[2], wps[3], bps[3], op, wp, int(bool(average_attn_weights)),
+                             _stream_ptr(stream))
+    else:
+        m = key_padding_mask
+        if tuple(m.shape) == (S,):
+            per_sample = 0
+        elif tuple(m.shape) == lead + (S,):
+            per_sample = 1
+        else:
+            raise PmaError(2, f"key_padding_mask has shape {tuple(m.shape)}, expected ({S},) "
+                              f"or {lead + (S,)}")
+        mp = _dptr(m, "key_padding_mask", torch.bool)
+        st = lib.pma_forward_masked(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1],
+                                    wps[2], bps[2], wps[3], bps[3], op, wp,
+                                    int(bool(average_attn_weights)), mp, per_sample,
+                                    _stream_ptr(stream))
     _check(st)
     return out, (weights if want_w else None)
+
+
+def pma_forward_masked(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                       key_padding_mask, out=None, weights=None, need_weights: bool = False,
+                       average_attn_weights: bool = True, stream=None):
+    """``pma_forward`` with a required key_padding_mask (boolean GPU tensor,
+    (S,) or the query's leading axes + (S,); True leaves that key out)."""
+    if key_padding_mask is None:
+        raise PmaError(1, "key_padding_mask is None")
+    return pma_forward(plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b, out=out,
+                       weights=weights, need_weights=need_weights,
+                       average_attn_weights=average_attn_weights, stream=stream,
+                       key_padding_mask=key_padding_mask)
 
 
 def pma_destroy(plan: Plan) -> None:

@@ -45,6 +45,11 @@ struct EdgeK {
     int xcd_map;         // 1: sample group fixed per XCD (passes divides 8)
     uint32_t xcd_per;    // 8 / passes
     uint32_t tstride;    // pieces between a wavefront's consecutive pieces
+    // key_padding_mask: sample b's bytes at kpm + b * kpm_bstride, indexed by
+    // source id (orig_src); nonzero leaves the key out. nullptr: no mask.
+    const uint8_t *kpm;
+    int64_t kpm_bstride;
+    const int32_t *orig_src;
     int nt;              // 1: non-temporal q loads and mixed stores
     float scale;         // log2(e) / sqrt(d)
     Layout lay;
@@ -281,13 +286,15 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
 // address and discard the data. bf16 scores use v_dot2 on the stored bf16 q
 // and k words (fp32 products and sums) and are scaled afterwards. Edges run U
 // at a time, the remainder one at a time.
-template <typename T, int CH, int LPH, bool W32, bool SC> struct EdgeLane {
+template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
     static constexpr bool BF = sizeof(T) == 2;
 
     const EdgeK &a;
-    const int32_t *src;   // csr_src, from a noalias kernel argument
+    const int32_t *src;   // gather rows, from a noalias kernel argument
+    const int32_t *osrc;  // source ids (for the key_padding_mask), noalias
+    uint32_t kpm_off;     // this lane's sample's first mask byte (with a.kpm)
     int B, b, h;
     bool active, head_lead;
     Chunk<T, CH> q;
@@ -364,6 +371,12 @@ template <typename T, int CH, int LPH, bool W32, bool SC> struct EdgeLane {
             if constexpr (BF) dot *= smul;   // fp32 q carries the scale already
             sc[u] = dot;
         }
+        if constexpr (KPM) {   // masked keys leave the softmax
+#pragma unroll
+            for (int u = 0; u < N; ++u)
+                if (a.kpm[kpm_off + (uint32_t)osrc[p + u]])
+                    sc[u] = -INFINITY;
+        }
         if (SC && active && head_lead) {
 #pragma unroll
             for (int u = 0; u < N; ++u) {
@@ -385,17 +398,21 @@ template <typename T, int CH, int LPH, bool W32, bool SC> struct EdgeLane {
         } else {
             const bool need = mx > ms + kLazy;
             if (__builtin_amdgcn_ballot_w64(need)) {
-                const float mn = need ? mx : ms;
-                const float alpha = fast_exp2(ms - mn);
+                // lanes that keep their reference scale by 1 (with a mask
+                // their reference may still be -inf, and -inf - -inf is NaN)
+                const float alpha = need ? fast_exp2(ms - mx) : 1.f;
                 l *= alpha;
 #pragma unroll
                 for (int i = 0; i < CH; ++i) acc[i] *= alpha;
-                ms = mn;
+                ms = need ? mx : ms;
             }
         }
+        // With a mask a lane may have seen no live key yet (ms = -inf); its
+        // masked scores must then give weight 0, not exp2(-inf + inf).
+        const float base = (KPM && ms == -INFINITY) ? 0.f : ms;
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            const float pe = fast_exp2(sc[u] - ms);
+            const float pe = fast_exp2(sc[u] - base);
             l += pe;
             if constexpr (BF) {
                 // The weight meets the bf16 values as a bf16 operand of
@@ -418,12 +435,12 @@ template <typename T, int CH, int LPH, bool W32, bool SC> struct EdgeLane {
     }
 };
 
-template <typename T, int CH, int LPH, int U, int E_FUSE, bool W32, bool SC>
+template <typename T, int CH, int LPH, int U, int E_FUSE, bool W32, bool SC, bool KPM>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(8)))   // 64 VGPRs
 edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
           const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end,
-          const int32_t *__restrict__ task_slot)
+          const int32_t *__restrict__ task_slot, const int32_t *__restrict__ orig_src)
 {
     // The index arrays come in as noalias arguments: no store of this kernel
     // can reach them, so their wave-uniform reads stay scalar loads.
@@ -455,8 +472,9 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     if (task >= (uint32_t)a.n_tasks)
         return;
 
-    EdgeLane<T, CH, LPH, W32, SC> st(a);
+    EdgeLane<T, CH, LPH, W32, SC, KPM> st(a);
     st.src = csr_src;
+    st.osrc = orig_src;
     const int B = a.B, E = a.E;
     const int cpr = E / CH;                       // chunks per sample row
     const uint32_t c = pass * 64 + lane;
@@ -469,6 +487,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     st.h = st.active ? cr / LPH : 0;
     st.head_lead = (lane % LPH) == 0;
     st.smul = a.scale;
+    st.kpm_off = (uint32_t)(b * a.kpm_bstride);
     // byte offsets: per source (uniform), this lane's key and value chunks
     st.row2 = (uint64_t)a.lay.kv_s * sizeof(T);
     if constexpr (W32) {
@@ -614,7 +633,13 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
         if constexpr (sizeof(T) == 2) return bf2f(*p); else return *p;
     };
     float m = -INFINITY, l = 0.f, acc = 0.f;
+    const uint8_t *kpm = a.kpm ? a.kpm + (int64_t)b * a.kpm_bstride : nullptr;
     for (int p = beg; p < end; ++p) {
+        if (kpm && kpm[a.orig_src[p]]) {   // key left out for this sample
+            if (a.scores && col == c0)
+                a.scores[((int64_t)p * B + b) * a.H + h] = -INFINITY;
+            continue;
+        }
         const T *kr = kv + (int64_t)a.csr_src[p] * row2 + b * a.lay.kv_b + c0;
         float dot = 0.f;
         for (int i = 0; i < d; ++i) dot = fmaf(ld(qt + i) * a.scale, ld(kr + i), dot);
@@ -680,7 +705,8 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
     for (int j = 0; j < n; ++j) {
         const float2 ml = *reinterpret_cast<const float2 *>(
             a.part_ml + (((int64_t)(s0 + j) * B + b) * H + h) * 2);
-        const float w = fast_exp2(ml.x - M);
+        // (a piece whose keys are all masked has l = 0 and m = -inf)
+        const float w = ml.y > 0.f ? fast_exp2(ml.x - M) : 0.f;
         l = fmaf(ml.y, w, l);
         const float4 *pa = reinterpret_cast<const float4 *>(
             a.part_acc + ((int64_t)(s0 + j) * B + b) * E + col);
@@ -731,7 +757,7 @@ __global__ void __launch_bounds__(256) merge_generic(EdgeK a)
     float l = 0.f, acc = 0.f;
     for (int j = 0; j < n; ++j) {
         const float *pm = a.part_ml + (((int64_t)(s0 + j) * B + b) * a.H + h) * 2;
-        const float w = fast_exp2(pm[0] - M);
+        const float w = pm[1] > 0.f ? fast_exp2(pm[0] - M) : 0.f;
         l = fmaf(pm[1], w, l);
         acc = fmaf(a.part_acc[((int64_t)(s0 + j) * B + b) * E + col], w, acc);
     }
@@ -760,11 +786,14 @@ __global__ void __launch_bounds__(256) weights_kernel(EdgeK a)
     const float *st = a.stat_ml + ((int64_t)t * B + b) * H * 2;
     if (a.average) {
         float sum = 0.f;
-        for (int h = 0; h < H; ++h) sum += fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1];
+        for (int h = 0; h < H; ++h)
+            if (st[2 * h + 1] > 0.f)   // l = 0: every key of the target masked
+                sum += fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1];
         a.weights[(int64_t)b * a.nnz + e] = sum / (float)H;
     } else {
         float *w = a.weights + ((int64_t)b * a.nnz + e) * H;
-        for (int h = 0; h < H; ++h) w[h] = fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1];
+        for (int h = 0; h < H; ++h)
+            w[h] = st[2 * h + 1] > 0.f ? fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1] : 0.f;
     }
 }
 
@@ -786,6 +815,18 @@ void set_passes(EdgeK &k, int ch)
     k.passes = (int)((chunks + 63) / 64);
     magic31((uint32_t)k.passes, k.pass_m, k.pass_sh);
     magic31((uint32_t)(k.E / ch), k.cpr_m, k.cpr_sh);
+}
+
+// Whether every tensor the edge kernel addresses is under 2 GiB (then it
+// uses 32-bit offsets).
+bool offsets32(const EdgeK &k, size_t es)
+{
+    const uint64_t rows = (uint64_t)k.L * k.B * k.E * es;
+    const uint64_t scores = k.scores ? (uint64_t)k.nnz * k.B * k.H * 4 : 0;
+    const uint64_t parts = (uint64_t)k.n_slots * k.B * k.E * 4;
+    const uint64_t stats = (uint64_t)k.L * k.B * k.H * 8;
+    const uint64_t lim = (uint64_t)1 << 31;
+    return k.kv_bytes < lim && rows < lim && scores < lim && parts < lim && stats < lim;
 }
 
 EdgeK make_k(const EdgeArgs &x)
@@ -813,6 +854,9 @@ EdgeK make_k(const EdgeArgs &x)
     k.passes = 1;
     k.xcd_map = x.xcd_map;
     k.tstride = 0;
+    k.kpm = x.kpm;
+    k.kpm_bstride = x.kpm_bstride;
+    k.orig_src = g->csr_src;
     k.nt = x.nt;
     k.fuse_out = x.fuse_out;
     k.L = (int)x.L;
@@ -878,22 +922,27 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
         blocks = (blocks + g - 1) / g * g;
         k.tstride = (uint32_t)(blocks * 4 / k.passes);
     }
-    // 32-bit offsets when every tensor the kernel addresses is under 2 GiB
-    const uint64_t rows = (uint64_t)k.L * k.B * k.E * sizeof(T);
-    const uint64_t scores = k.scores ? (uint64_t)k.nnz * k.B * k.H * 4 : 0;
-    const uint64_t parts = (uint64_t)k.n_slots * k.B * k.E * 4;
-    const uint64_t stats = (uint64_t)k.L * k.B * k.H * 8;
-    const uint64_t lim = (uint64_t)1 << 31;
-    const bool w32 = k.kv_bytes < lim && rows < lim && scores < lim && parts < lim && stats < lim;
+    const bool w32 = offsets32(k, sizeof(T));
     const unsigned nb = (unsigned)blocks;
-    if (w32 && k.scores)
-        edge_fast<T, CH, LPH, 4, E_FUSE, true, true><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
+#define PMA_EDGE_LAUNCH(W, S, M)                                                          \
+    edge_fast<T, CH, LPH, 4, E_FUSE, W, S, M><<<nb, 256, 0, s>>>(                        \
+        k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.orig_src)
+    if (k.kpm) {
+        if (!w32)   // refused by mask_supported()
+            return hipErrorInvalidValue;
+        if (k.scores)
+            PMA_EDGE_LAUNCH(true, true, true);
+        else
+            PMA_EDGE_LAUNCH(true, false, true);
+    } else if (w32 && k.scores)
+        PMA_EDGE_LAUNCH(true, true, false);
     else if (w32)
-        edge_fast<T, CH, LPH, 4, E_FUSE, true, false><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
+        PMA_EDGE_LAUNCH(true, false, false);
     else if (k.scores)
-        edge_fast<T, CH, LPH, 4, E_FUSE, false, true><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
+        PMA_EDGE_LAUNCH(false, true, false);
     else
-        edge_fast<T, CH, LPH, 4, E_FUSE, false, false><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot);
+        PMA_EDGE_LAUNCH(false, false, false);
+#undef PMA_EDGE_LAUNCH
     return hipGetLastError();
 }
 
@@ -971,6 +1020,14 @@ hipError_t dispatch_merge(EdgeK k, hipStream_t s)
 }
 
 }  // namespace
+
+bool mask_supported(const EdgeArgs &x)
+{
+    const EdgeK k = make_k(x);
+    const int64_t ch = x.dt == PMA_BF16 ? 8 : 4, d = x.E / x.H;
+    const bool fast = d % ch == 0 && (d / ch) <= 16 && ((d / ch) & (d / ch - 1)) == 0;
+    return !fast || offsets32(k, x.dt == PMA_BF16 ? 2 : 4);
+}
 
 bool out_fusable(int64_t E, int64_t H, pma_dtype dt)
 {

@@ -378,11 +378,13 @@ PMA_API pma_status pma_work_split(const pma_plan *plan, int64_t *task_target,
     return st;
 }
 
-PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const void *key,
-                               const void *value, const void *q_w, const void *q_b,
-                               const void *k_w, const void *k_b, const void *v_w,
-                               const void *v_b, const void *o_w, const void *o_b, void *out,
-                               float *weights, int average_attn_weights, hipStream_t stream)
+namespace {
+
+pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                        const void *value, const void *q_w, const void *q_b, const void *k_w,
+                        const void *k_b, const void *v_w, const void *v_b, const void *o_w,
+                        const void *o_b, void *out, float *weights, int average_attn_weights,
+                        const uint8_t *kpm, int kpm_per_sample, hipStream_t stream)
 {
     g_err[0] = 0;
     if (!plan)
@@ -475,6 +477,8 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
+    ea.kpm = kpm;
+    ea.kpm_bstride = kpm_per_sample ? S : 0;
     // Automatic choices (measured on MI355X): stream q and mixed past the
     // caches only when the workspace outgrows the 256 MB last-level cache;
     // keep the edge kernel's wavefronts resident and walking pieces when
@@ -493,6 +497,9 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     // each L2 the rows of one sample group only; measured faster on all three
     // full-size workloads.
     ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map : 1;
+
+    if (kpm && !pma::mask_supported(ea))
+        return fail(PMA_E_UNSUPPORTED, "key_padding_mask with a workspace tensor of 2 GiB or more");
 
     // Steps 2-4 (and 5 when fused): scores, softmax and mix over the live edges.
     tm.begin(PMA_STAGE_EDGE);
@@ -525,6 +532,36 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
     if (st != PMA_OK)
         return fail(st, "out_proj launch failed: %s", hipGetErrorString(hipGetLastError()));
     return PMA_OK;
+}
+
+}  // namespace
+
+PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                               const void *value, const void *q_w, const void *q_b,
+                               const void *k_w, const void *k_b, const void *v_w,
+                               const void *v_b, const void *o_w, const void *o_b, void *out,
+                               float *weights, int average_attn_weights, hipStream_t stream)
+{
+    return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                        out, weights, average_attn_weights, nullptr, 0, stream);
+}
+
+PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void *query,
+                                      const void *key, const void *value, const void *q_w,
+                                      const void *q_b, const void *k_w, const void *k_b,
+                                      const void *v_w, const void *v_b, const void *o_w,
+                                      const void *o_b, void *out, float *weights,
+                                      int average_attn_weights, const uint8_t *key_padding_mask,
+                                      int mask_per_sample, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!key_padding_mask)
+        return fail(PMA_E_NULL, "key_padding_mask is NULL");
+    if (mask_per_sample != 0 && mask_per_sample != 1)
+        return fail(PMA_E_ARG, "mask_per_sample must be 0 or 1");
+    return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                        out, weights, average_attn_weights, key_padding_mask, mask_per_sample,
+                        stream);
 }
 
 PMA_API pma_status pma_profile(pma_plan *plan, int enable)

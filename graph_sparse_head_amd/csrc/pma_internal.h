@@ -100,6 +100,8 @@ struct EdgeArgs {
     int average;
     int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
     int nt = 1;         // non-temporal q loads / mixed stores
+    const uint8_t *kpm = nullptr;  // key_padding_mask bytes (sample b at b * kpm_bstride)
+    int64_t kpm_bstride = 0;
     int persist = 0;    // edge kernel: workgroups per CU, each wavefront walking
                         // several pieces (0: one wavefront per piece and pass)
     // out_proj fused into the edge and merge kernels (out_fusable)
@@ -111,6 +113,9 @@ struct EdgeArgs {
 // Whether edge_fast / merge_fast can apply out_proj themselves.
 bool out_fusable(int64_t E, int64_t H, pma_dtype dt);
 
+// Whether the edge kernels take a key_padding_mask for these arguments (the
+// fast kernel needs every tensor under 2 GiB when masked).
+bool mask_supported(const EdgeArgs &x);
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
 
 pma_status launch_merge(const EdgeArgs &a, hipStream_t s);

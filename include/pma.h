@@ -144,6 +144,32 @@ pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const v
                        const void *o_b, void *out, float *weights, int average_attn_weights,
                        hipStream_t stream);
 
+/*
+ * pma_forward_masked -- pma_forward with a key_padding_mask (kpnn2 page,
+ * forward parameter table, key_padding_mask; "Notes" step 3 and the
+ * paragraph on queries with no live keys).
+ *
+ *   key_padding_mask  DEVICE bytes, one per key (source token): (B, S) when
+ *                     mask_per_sample = 1, else (S,) shared by every sample.
+ *                     Nonzero leaves that key out of the sample: the edges
+ *                     from it drop out of the softmax (weight 0) and the
+ *                     other edges into the same target share the whole
+ *                     weight. A target whose keys are all masked mixes to
+ *                     zeros, so its output is o_b. Borrowed like the tokens.
+ *   mask_per_sample   0 or 1.
+ *   other arguments   as pma_forward.
+ *
+ * Errors: those of pma_forward, and PMA_E_NULL (key_padding_mask NULL),
+ * PMA_E_ARG (mask_per_sample not 0/1), PMA_E_UNSUPPORTED (a workspace tensor
+ * of 2 GiB or more with a head size the 16-byte kernel serves).
+ */
+pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                              const void *value, const void *q_w, const void *q_b,
+                              const void *k_w, const void *k_b, const void *v_w, const void *v_b,
+                              const void *o_w, const void *o_b, void *out, float *weights,
+                              int average_attn_weights, const uint8_t *key_padding_mask,
+                              int mask_per_sample, hipStream_t stream);
+
 /* pma_destroy -- free the plan and everything it owns. NULL is a no-op.
    Waits for the device before freeing. */
 pma_status pma_destroy(pma_plan *plan);

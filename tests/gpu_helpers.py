@@ -30,9 +30,10 @@ def make_plan(case, stream=None):
                           add_self_loops=case.add_self_loops, dtype=case.dtype, stream=stream)
 
 
-def run(case, plan=None, need_weights=None, average=None, dev=None, lead=None):
+def run(case, plan=None, need_weights=None, average=None, dev=None, lead=None, kpm=None):
     """One forward on the GPU. Returns (out float64 (B, L, E), weights float64
-    or None, plan). ``lead`` reshapes the batch into several leading axes."""
+    or None, plan). ``lead`` reshapes the batch into several leading axes;
+    ``kpm`` is a numpy boolean key_padding_mask, (S,) or (B, S)."""
     import torch
     own = plan is None
     if own:
@@ -46,9 +47,14 @@ def run(case, plan=None, need_weights=None, average=None, dev=None, lead=None):
         q = q.reshape(*lead, case.L, case.E)
         k = q if dev["xk"] is dev["xq"] else k.reshape(*lead, case.S, case.E)
         v = k if dev["xv"] is dev["xk"] else v.reshape(*lead, case.S, case.E)
+    mask = None
+    if kpm is not None:
+        mask = torch.from_numpy(np.ascontiguousarray(kpm, np.bool_)).cuda()
+        if mask.dim() == 2 and lead is not None:
+            mask = mask.reshape(*lead, case.S)
     out, w = pma.pma_forward(plan, q, k, v, dev["wq"], dev["bq"], dev["wk"], dev["bk"],
                              dev["wv"], dev["bv"], dev["wo"], dev["bo"],
-                             need_weights=nw, average_attn_weights=avg)
+                             need_weights=nw, average_attn_weights=avg, key_padding_mask=mask)
     torch.cuda.synchronize()
     o = to_f64(out, case.dtype).reshape(case.B, case.L, case.E)
     wn = None
