@@ -45,10 +45,11 @@ struct EdgeK {
     int xcd_map;         // 1: sample group fixed per XCD (passes divides 8)
     uint32_t xcd_per;    // 8 / passes
     uint32_t tstride;    // pieces between a wavefront's consecutive pieces
-    // key_padding_mask: sample b's bytes at kpm + b * kpm_bstride, indexed by
-    // source id (orig_src); nonzero leaves the key out. nullptr: no mask.
-    const uint8_t *kpm;
-    int64_t kpm_bstride;
+    // key_padding_mask as bits: source s, sample b at bit b % 64 of
+    // kpm_bits[s * kpm_words + b / 64] (source id from orig_src); a set bit
+    // leaves the key out. nullptr: no mask.
+    const uint64_t *kpm_bits;
+    int kpm_words;
     const int32_t *orig_src;
     int nt;              // 1: non-temporal q loads and mixed stores
     float scale;         // log2(e) / sqrt(d)
@@ -294,7 +295,8 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
     const EdgeK &a;
     const int32_t *src;   // gather rows, from a noalias kernel argument
     const int32_t *osrc;  // source ids (for the key_padding_mask), noalias
-    uint32_t kpm_off;     // this lane's sample's first mask byte (with a.kpm)
+    const uint64_t *kbits;  // mask bits, from a noalias kernel argument
+    uint32_t kword;         // word of this wavefront's samples within a source's bits
     int B, b, h;
     bool active, head_lead;
     Chunk<T, CH> q;
@@ -372,10 +374,14 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
             sc[u] = dot;
         }
         if constexpr (KPM) {   // masked keys leave the softmax
+            // one uniform 64-bit word per edge holds the bits of all the
+            // wavefront's samples
 #pragma unroll
-            for (int u = 0; u < N; ++u)
-                if (a.kpm[kpm_off + (uint32_t)osrc[p + u]])
+            for (int u = 0; u < N; ++u) {
+                const uint64_t w = kbits[(uint32_t)osrc[p + u] * (uint32_t)a.kpm_words + kword];
+                if ((w >> (b & 63)) & 1u)
                     sc[u] = -INFINITY;
+            }
         }
         if (SC && active && head_lead) {
 #pragma unroll
@@ -440,7 +446,8 @@ __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(8)))   // 64 VGPRs
 edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
           const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end,
-          const int32_t *__restrict__ task_slot, const int32_t *__restrict__ orig_src)
+          const int32_t *__restrict__ task_slot, const int32_t *__restrict__ orig_src,
+          const uint64_t *__restrict__ kpm_bits)
 {
     // The index arrays come in as noalias arguments: no store of this kernel
     // can reach them, so their wave-uniform reads stay scalar loads.
@@ -487,7 +494,8 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     st.h = st.active ? cr / LPH : 0;
     st.head_lead = (lane % LPH) == 0;
     st.smul = a.scale;
-    st.kpm_off = (uint32_t)(b * a.kpm_bstride);
+    st.kbits = kpm_bits;
+    st.kword = (pass * 64u / (uint32_t)cpr) >> 6;   // first sample of the pass / 64
     // byte offsets: per source (uniform), this lane's key and value chunks
     st.row2 = (uint64_t)a.lay.kv_s * sizeof(T);
     if constexpr (W32) {
@@ -633,9 +641,9 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
         if constexpr (sizeof(T) == 2) return bf2f(*p); else return *p;
     };
     float m = -INFINITY, l = 0.f, acc = 0.f;
-    const uint8_t *kpm = a.kpm ? a.kpm + (int64_t)b * a.kpm_bstride : nullptr;
     for (int p = beg; p < end; ++p) {
-        if (kpm && kpm[a.orig_src[p]]) {   // key left out for this sample
+        if (a.kpm_bits &&   // key left out for this sample
+            ((a.kpm_bits[(int64_t)a.orig_src[p] * a.kpm_words + (b >> 6)] >> (b & 63)) & 1u)) {
             if (a.scores && col == c0)
                 a.scores[((int64_t)p * B + b) * a.H + h] = -INFINITY;
             continue;
@@ -854,8 +862,8 @@ EdgeK make_k(const EdgeArgs &x)
     k.passes = 1;
     k.xcd_map = x.xcd_map;
     k.tstride = 0;
-    k.kpm = x.kpm;
-    k.kpm_bstride = x.kpm_bstride;
+    k.kpm_bits = x.kpm_bits;
+    k.kpm_words = x.kpm_words;
     k.orig_src = g->csr_src;
     k.nt = x.nt;
     k.fuse_out = x.fuse_out;
@@ -926,8 +934,8 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     const unsigned nb = (unsigned)blocks;
 #define PMA_EDGE_LAUNCH(W, S, M)                                                          \
     edge_fast<T, CH, LPH, 4, E_FUSE, W, S, M><<<nb, 256, 0, s>>>(                        \
-        k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.orig_src)
-    if (k.kpm) {
+        k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.orig_src, k.kpm_bits)
+    if (k.kpm_bits) {
         if (!w32)   // refused by mask_supported()
             return hipErrorInvalidValue;
         if (k.scores)
@@ -1019,7 +1027,34 @@ hipError_t dispatch_merge(EdgeK k, hipStream_t s)
     return hipGetLastError();
 }
 
+// key_padding_mask bytes -> bits by source: thread (s, w) gathers samples
+// 64 w .. 64 w + 63 of key s (reads of consecutive s are coalesced).
+__global__ void pack_mask_kernel(const uint8_t *mask, int64_t bstride, int64_t B, int64_t S,
+                                 int words, uint64_t *bits)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= S * words)
+        return;
+    const int64_t w = i / S, s = i - w * S;
+    uint64_t v = 0;
+    for (int j = 0; j < 64; ++j) {
+        const int64_t b = w * 64 + j;
+        if (b < B && mask[b * bstride + s])
+            v |= (uint64_t)1 << j;
+    }
+    bits[s * words + w] = v;
+}
+
 }  // namespace
+
+pma_status pack_mask(const uint8_t *mask, int64_t bstride, int64_t B, int64_t S, uint64_t *bits,
+                     hipStream_t s)
+{
+    const int words = (int)((B + 63) / 64);
+    const int64_t n = S * words;
+    pack_mask_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(mask, bstride, B, S, words, bits);
+    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+}
 
 bool mask_supported(const EdgeArgs &x)
 {

@@ -54,6 +54,7 @@ struct pma_plan {
     bool ws_weights = false;
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
+    uint64_t *kpm_bits = nullptr;   // key_padding_mask packed by source
     // profiling
     unsigned prof = 0;   // stages timed: bit s for stage s
     std::vector<EventPair> pending;
@@ -66,18 +67,21 @@ namespace {
 
 void free_workspace(pma_plan *p)
 {
-    void *ptrs[] = {p->qt, p->kv, p->mixed, p->part_acc, p->part_ml, p->stat_ml, p->scores};
+    void *ptrs[] = {p->qt,     p->kv,      p->mixed,  p->part_acc,
+                    p->part_ml, p->stat_ml, p->scores, p->kpm_bits};
     for (void *q : ptrs)
         if (q)
             (void)hipFree(q);
     p->qt = p->kv = p->mixed = nullptr;
     p->part_acc = p->part_ml = p->stat_ml = p->scores = nullptr;
+    p->kpm_bits = nullptr;
     p->ws_B = 0;
     p->ws_weights = false;
 }
 
-// Buffers for a batch of B: q, keys/values, mixed and the split partials;
-// scores and final (max, sum) only for need_weights.
+// Buffers for a batch of B: q, keys/values, mixed, the split partials and
+// the packed key_padding_mask; scores and final (max, sum) only for
+// need_weights.
 pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
 {
     if (B <= p->ws_B && (!weights || p->ws_weights))
@@ -101,6 +105,7 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
         {(void **)&p->part_ml, slots * nB * p->H * 2 * 4},
         {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
         {(void **)&p->scores, nw ? (size_t)p->nnz * nB * p->H * 4 : 0},
+        {(void **)&p->kpm_bits, (size_t)p->S * ((nB + 63) / 64) * 8},
     };
     for (auto &w : want) {
         if (w.bytes == 0)
@@ -477,8 +482,13 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
-    ea.kpm = kpm;
-    ea.kpm_bstride = kpm_per_sample ? S : 0;
+    if (kpm) {
+        st = pma::pack_mask(kpm, kpm_per_sample ? S : 0, B, S, p->kpm_bits, stream);
+        if (st != PMA_OK)
+            return fail(st, "mask packing failed: %s", hipGetErrorString(hipGetLastError()));
+        ea.kpm_bits = p->kpm_bits;
+        ea.kpm_words = (int)((B + 63) / 64);
+    }
     // Automatic choices (measured on MI355X): stream q and mixed past the
     // caches only when the workspace outgrows the 256 MB last-level cache;
     // keep the edge kernel's wavefronts resident and walking pieces when

@@ -100,8 +100,8 @@ struct EdgeArgs {
     int average;
     int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
     int nt = 1;         // non-temporal q loads / mixed stores
-    const uint8_t *kpm = nullptr;  // key_padding_mask bytes (sample b at b * kpm_bstride)
-    int64_t kpm_bstride = 0;
+    const uint64_t *kpm_bits = nullptr;  // key_padding_mask bits (pack_mask layout)
+    int kpm_words = 0;                   // 64-bit words per source
     int persist = 0;    // edge kernel: workgroups per CU, each wavefront walking
                         // several pieces (0: one wavefront per piece and pass)
     // out_proj fused into the edge and merge kernels (out_fusable)
@@ -112,6 +112,12 @@ struct EdgeArgs {
 
 // Whether edge_fast / merge_fast can apply out_proj themselves.
 bool out_fusable(int64_t E, int64_t H, pma_dtype dt);
+
+// key_padding_mask bytes (sample b's S bytes at mask + b * bstride; bstride
+// 0 for one shared mask) -> bits[s * words + b / 64], bit b % 64, words =
+// ceil(B / 64). Asynchronous on s.
+pma_status pack_mask(const uint8_t *mask, int64_t bstride, int64_t B, int64_t S, uint64_t *bits,
+                     hipStream_t s);
 
 // Whether the edge kernels take a key_padding_mask for these arguments (the
 // fast kernel needs every tensor under 2 GiB when masked).
