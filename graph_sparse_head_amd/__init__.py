@@ -328,3 +328,11 @@ def pma_profile_read(plan: Plan) -> dict:
     calls = np.zeros(len(STAGES), np.int64)
     _check(_load().pma_profile_read(plan.handle, ms.ctypes.data, calls.ctypes.data))
     return {name: (float(ms[i]), int(calls[i])) for i, name in enumerate(STAGES)}
+
+
+def __getattr__(name):
+    # The nn.Module surface imports torch; load it on first use.
+    if name in ("PackedMultiheadAttention", "ModuleArgError"):
+        from . import module
+        return getattr(module, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

@@ -1,0 +1,337 @@
+"""torch.nn.Module surface over the C-ABI (kpnn2 0.3.0 API reference,
+PackedMultiheadAttention: constructor parameter table, attributes, "Raises",
+reset_parameters and forward).
+
+Every step of the computation runs in libpma's kernels; this module only
+validates arguments, keeps the four projections as nn.Linear parameters,
+moves layouts (sequence-first <-> batch-first, leading axes) and hands
+pointers to ``pma_forward`` / ``pma_forward_masked``. Plans are built per
+(device, dtype) on first use and cached.
+
+Not covered: dropout in training mode (the kernels compute the eval-mode
+softmax; a training-mode call with dropout > 0 raises), attn_mask and
+is_causal (must be None / False, as on the page), checkpoint identity and
+index digests.
+"""
+from __future__ import annotations
+
+import math
+import numbers
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import pma_create, pma_destroy, pma_edges, pma_forward
+
+__all__ = ["PackedMultiheadAttention", "ModuleArgError"]
+
+
+class ModuleArgError(ValueError):
+    """An argument the layer rejects (the page's Kpnn2Error cases)."""
+
+
+def _is_int(x) -> bool:
+    return isinstance(x, (numbers.Integral, np.integer)) and not isinstance(x, (bool, np.bool_))
+
+
+def _pos_int(x, name: str) -> int:
+    if not _is_int(x) or int(x) <= 0:
+        raise ModuleArgError(f"{name} must be a positive integer, got {x!r}")
+    return int(x)
+
+
+def _index(x, name: str) -> np.ndarray:
+    """1-D integer indices from a tensor, ndarray or sequence (copied)."""
+    if isinstance(x, (set, frozenset, dict)):
+        raise ModuleArgError(f"{name} must be ordered (a set or mapping is rejected)")
+    if isinstance(x, torch.Tensor):
+        if x.is_complex() or x.is_floating_point() or x.dtype == torch.bool:
+            raise ModuleArgError(f"{name} must be an integer tensor")
+        a = x.detach().cpu().numpy()
+    else:
+        a = np.asarray(x)
+        if a.size and (a.dtype == np.bool_ or not np.issubdtype(a.dtype, np.integer)):
+            if a.dtype == object and all(_is_int(v) for v in a.ravel()):
+                a = a.astype(np.int64)
+            else:
+                raise ModuleArgError(f"{name} must hold integers")
+    if a.ndim != 1:
+        raise ModuleArgError(f"{name} must be 1-D")
+    return np.array(a, dtype=np.int64, copy=True)
+
+
+def _bool(x, name: str) -> bool:
+    if not isinstance(x, (bool, np.bool_)):
+        raise ModuleArgError(f"{name} must be a bool, got {x!r}")
+    return bool(x)
+
+
+class PackedMultiheadAttention(torch.nn.Module):
+    """Multi-head attention in which each target token attends only to its
+    listed source tokens (kpnn2 page, class docstring and "Notes")."""
+
+    def __init__(self, source_index, target_index, query_features, key_features, embed_dim,
+                 num_heads, dropout: float = 0.0, bias: bool = True, kdim=None, vdim=None,
+                 batch_first: bool = True, add_self_loops: bool = False, *,
+                 generator: Optional[torch.Generator] = None, device=None, dtype=None):
+        super().__init__()
+        L = _pos_int(query_features, "query_features")
+        S = _pos_int(key_features, "key_features")
+        E = _pos_int(embed_dim, "embed_dim")
+        H = _pos_int(num_heads, "num_heads")
+        if E % H:
+            raise ModuleArgError(f"embed_dim {E} is not divisible by num_heads {H}")
+        if isinstance(dropout, (bool, np.bool_)) or not isinstance(dropout, (numbers.Real, np.floating)):
+            raise ModuleArgError(f"dropout must be a number, got {dropout!r}")
+        dropout = float(dropout)
+        if not math.isfinite(dropout) or not 0.0 <= dropout <= 1.0:
+            raise ModuleArgError(f"dropout must lie in [0, 1], got {dropout}")
+        bias = _bool(bias, "bias")
+        batch_first = _bool(batch_first, "batch_first")
+        add_self_loops = _bool(add_self_loops, "add_self_loops")
+        for n, v in (("kdim", kdim), ("vdim", vdim)):
+            if v is not None and (not _is_int(v) or int(v) != E):
+                raise ModuleArgError(f"{n} must be None or equal to embed_dim ({E}), got {v!r}")
+        if generator is not None and not isinstance(generator, torch.Generator):
+            raise ModuleArgError("generator must be a torch.Generator or None")
+        src = _index(source_index, "source_index")
+        tgt = _index(target_index, "target_index")
+        if src.shape[0] != tgt.shape[0]:
+            raise ModuleArgError("source_index and target_index differ in length")
+        if src.shape[0] == 0:
+            raise ModuleArgError("the indices are empty")
+        if src.min() < 0 or src.max() >= S:
+            raise ModuleArgError(f"source_index outside [0, {S})")
+        if tgt.min() < 0 or tgt.max() >= L:
+            raise ModuleArgError(f"target_index outside [0, {L})")
+        pair = tgt * S + src
+        if np.unique(pair).shape[0] != pair.shape[0]:
+            raise ModuleArgError("target_index/source_index repeat a (source, target) pair")
+        if add_self_loops:
+            if L != S:
+                raise ModuleArgError("add_self_loops needs query_features == key_features")
+            have = np.zeros(L, bool)
+            have[src[src == tgt]] = True
+            extra = np.flatnonzero(~have)          # missing (i, i), ascending i
+            src = np.concatenate([src, extra])
+            tgt = np.concatenate([tgt, extra])
+
+        self.query_features, self.key_features = L, S
+        self.embed_dim, self.num_heads, self.head_dim = E, H, E // H
+        self.dropout, self.batch_first, self.add_self_loops = dropout, batch_first, add_self_loops
+        self.register_buffer("source_index", torch.from_numpy(src), persistent=True)
+        self.register_buffer("target_index", torch.from_numpy(tgt), persistent=True)
+        kw = {"device": device, "dtype": dtype}
+        self.q_proj = torch.nn.Linear(E, E, bias=bias, **kw)
+        self.k_proj = torch.nn.Linear(E, E, bias=bias, **kw)
+        self.v_proj = torch.nn.Linear(E, E, bias=bias, **kw)
+        self.out_proj = torch.nn.Linear(E, E, bias=bias, **kw)
+        self._plans: Dict[Tuple[str, int, str], object] = {}
+        self.reset_parameters(generator)
+
+    # ------------------------------------------------------------------
+    @classmethod
+    def from_edgelist(cls, sources: Sequence, targets: Sequence, embed_dim: int, num_heads: int,
+                      nodes: Optional[Sequence] = None, **kwargs) -> "PackedMultiheadAttention":
+        """Attention within one node set from a named edge list (source ->
+        target). Node i of the token sequence is ``nodes[i]``; without
+        ``nodes`` the order is that of first appearance, sources and targets
+        interleaved edge by edge."""
+        if len(sources) != len(targets):
+            raise ModuleArgError("sources and targets differ in length")
+        if nodes is None:
+            order: Dict[object, int] = {}
+            for s, t in zip(sources, targets):
+                order.setdefault(s, len(order))
+                order.setdefault(t, len(order))
+        else:
+            order = {}
+            for n in nodes:
+                if n in order:
+                    raise ModuleArgError(f"node {n!r} listed twice")
+                order[n] = len(order)
+        try:
+            src = [order[s] for s in sources]
+            tgt = [order[t] for t in targets]
+        except KeyError as e:
+            raise ModuleArgError(f"edge endpoint {e.args[0]!r} is not in nodes") from None
+        n = len(order)
+        layer = cls(src, tgt, n, n, embed_dim, num_heads, **kwargs)
+        layer.nodes = list(order)
+        return layer
+
+    @property
+    def nnz(self) -> int:
+        return int(self.source_index.shape[0])
+
+    def reset_parameters(self, generator: Optional[torch.Generator] = None) -> None:
+        """Xavier-uniform projection weights; biases zeroed (kpnn2 page,
+        reset_parameters)."""
+        with torch.no_grad():
+            for lin in (self.q_proj, self.k_proj, self.v_proj, self.out_proj):
+                bound = math.sqrt(6.0 / (lin.in_features + lin.out_features))
+                w = torch.empty(lin.weight.shape, dtype=torch.float32)
+                w.uniform_(-bound, bound, generator=generator)
+                lin.weight.copy_(w)
+                if lin.bias is not None:
+                    lin.bias.zero_()
+
+    # ------------------------------------------------------------------
+    def _plan(self, device: torch.device, dtype: torch.dtype):
+        if dtype == torch.float32:
+            dt = "f32"
+        elif dtype == torch.bfloat16:
+            dt = "bf16"
+        else:
+            raise ModuleArgError(f"parameters of dtype {dtype} are not supported (float32, bfloat16)")
+        key = (device.type, device.index if device.index is not None else torch.cuda.current_device(), dt)
+        plan = self._plans.get(key)
+        if plan is None:
+            with torch.cuda.device(key[1]):
+                plan = pma_create(self.source_index.cpu().numpy(), self.target_index.cpu().numpy(),
+                                  self.query_features, self.key_features, self.embed_dim,
+                                  self.num_heads, add_self_loops=False, dtype=dt)
+            s, t = pma_edges(plan)
+            assert (s == self.source_index.cpu().numpy()).all() and \
+                (t == self.target_index.cpu().numpy()).all()
+            self._plans[key] = plan
+        return plan
+
+    def _drop_plans(self):
+        for plan in self._plans.values():
+            try:
+                pma_destroy(plan)
+            except Exception:   # pragma: no cover - interpreter shutdown
+                pass
+        self._plans = {}
+
+    def __del__(self):
+        try:
+            self._drop_plans()
+        except Exception:   # pragma: no cover
+            pass
+
+    def _apply(self, fn, *args, **kwargs):
+        # Changing device or dtype invalidates nothing in the plans (they are
+        # keyed by device and dtype), but buffers must stay int64.
+        out = super()._apply(fn, *args, **kwargs)
+        for n in ("source_index", "target_index"):
+            b = getattr(self, n)
+            if b.dtype != torch.int64:
+                setattr(self, n, b.to(torch.int64))
+        return out
+
+    # ------------------------------------------------------------------
+    def _check_tokens(self, x, name: str, seq: int):
+        E = self.embed_dim
+        if not isinstance(x, torch.Tensor):
+            raise ModuleArgError(f"{name} must be a tensor")
+        if not x.is_floating_point():
+            raise ModuleArgError(f"{name} must be floating-point, got {x.dtype}")
+        if x.dim() < 2:
+            raise ModuleArgError(f"{name} needs at least 2 dimensions")
+        if x.shape[-1] != E:
+            raise ModuleArgError(f"{name} has width {x.shape[-1]}, embed_dim is {E}")
+        seq_axis = -2 if (self.batch_first or x.dim() == 2) else 0
+        if x.shape[seq_axis] != seq:
+            raise ModuleArgError(f"{name} has sequence length {x.shape[seq_axis]}, expected {seq}")
+        if not self.batch_first and x.dim() != 2 and x.dim() != 3:
+            raise ModuleArgError(f"batched {name} must be 3-D (seq, batch, E) with batch_first=False")
+
+    def forward(self, query, key, value, key_padding_mask=None, need_weights: bool = False,
+                attn_mask=None, average_attn_weights: bool = True, is_causal: bool = False):
+        """Returns (output in query's layout, weights or None); weights are
+        one per live edge in edge order, (..., nnz) averaged or (..., nnz, H)."""
+        if attn_mask is not None:
+            raise ModuleArgError("attn_mask must be None: the edge list is the mask")
+        if is_causal is not False:
+            raise ModuleArgError("is_causal must be False")
+        need_weights = _bool(need_weights, "need_weights")
+        average_attn_weights = _bool(average_attn_weights, "average_attn_weights")
+        if self.training and self.dropout > 0:
+            raise ModuleArgError("dropout in training mode is not supported; call eval() "
+                                 "or set dropout=0")
+        L, S, E, H = self.query_features, self.key_features, self.embed_dim, self.num_heads
+        self._check_tokens(query, "query", L)
+        self._check_tokens(key, "key", S)
+        self._check_tokens(value, "value", S)
+        if key.shape != value.shape:
+            raise ModuleArgError("key and value shapes differ")
+        unbatched = query.dim() == 2
+        seq_first = not self.batch_first and not unbatched
+
+        def to_bf(x):
+            return x.transpose(0, 1) if seq_first else x
+
+        q, k, v = to_bf(query), to_bf(key), to_bf(value)
+        lead = tuple(q.shape[:-2])
+        if tuple(k.shape[:-2]) != lead or tuple(v.shape[:-2]) != lead:
+            raise ModuleArgError("the batch axes of query, key and value differ")
+        if key_padding_mask is not None:
+            m = key_padding_mask
+            if not isinstance(m, torch.Tensor) or m.dtype != torch.bool:
+                raise ModuleArgError("key_padding_mask must be a boolean tensor")
+            if tuple(m.shape) != (S,) and tuple(m.shape) != lead + (S,):
+                raise ModuleArgError(f"key_padding_mask has shape {tuple(m.shape)}, expected "
+                                     f"({S},) or {lead + (S,)}")
+        w = self.q_proj.weight
+        if query.device != w.device or query.device.type != "cuda":
+            raise ModuleArgError("query, key, value and the layer must be on the same GPU")
+        dt = w.dtype
+        plan = self._plan(w.device, dt)
+
+        def prep(x):
+            return x.to(dt).contiguous()
+
+        same_kv = key is value
+        same_qkv = query is key and same_kv
+        qc = prep(q)
+        kc = qc if same_qkv else prep(k)
+        vc = kc if same_kv else prep(v)
+        mask = None if key_padding_mask is None else key_padding_mask.to(device=qc.device).contiguous()
+        if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad or
+                                        any(p.requires_grad for p in self.parameters())):
+            return _PackedAttnFn.apply(self, plan, qc, kc, vc, mask, need_weights,
+                                       average_attn_weights, same_qkv, same_kv,
+                                       *self._params())
+        out, weights = self._run(plan, qc, kc, vc, mask, need_weights, average_attn_weights)
+        return self._finish(out, weights, seq_first, lead)
+
+    def _params(self):
+        ps = []
+        for lin in (self.q_proj, self.k_proj, self.v_proj, self.out_proj):
+            ps += [lin.weight, lin.bias]
+        return ps
+
+    def _run(self, plan, qc, kc, vc, mask, need_weights, average):
+        def c(t):
+            return None if t is None else t.detach().contiguous()
+        return pma_forward(plan, qc.detach(), kc.detach(), vc.detach(),
+                           c(self.q_proj.weight), c(self.q_proj.bias),
+                           c(self.k_proj.weight), c(self.k_proj.bias),
+                           c(self.v_proj.weight), c(self.v_proj.bias),
+                           c(self.out_proj.weight), c(self.out_proj.bias),
+                           need_weights=need_weights, average_attn_weights=average,
+                           key_padding_mask=mask)
+
+    @staticmethod
+    def _finish(out, weights, seq_first, lead):
+        if seq_first:
+            out = out.transpose(0, 1)
+            if weights is not None:
+                weights = weights.transpose(0, 1)   # (nnz, batch[, H])
+        return out, weights
+
+
+class _PackedAttnFn(torch.autograd.Function):
+    """Autograd hook-up; the backward pass is not available yet."""
+
+    @staticmethod
+    def forward(ctx, layer, plan, q, k, v, mask, need_weights, average, same_qkv, same_kv, *params):
+        raise ModuleArgError("gradients through PackedMultiheadAttention are not available; "
+                             "run the forward under torch.no_grad()")
+
+    @staticmethod
+    def backward(ctx, *grads):  # pragma: no cover
+        raise NotImplementedError
