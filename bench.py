@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--config", default="gene",
                     choices=["tiny", "complete", "gene", "bipartite", "large"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step: pma_forward_train + pma_backward")
     ap.add_argument("--key-padding-mask", type=float, default=0.0, metavar="FRAC",
                     help="mask this fraction of keys per sample (seeded); 0: no mask")
     ap.add_argument("--no-profile", action="store_true",
@@ -170,7 +172,21 @@ def main():
         kpm = torch.from_numpy(np.random.default_rng(3).random((case.B, case.S))
                                < args.key_padding_mask).cuda()
 
+    if args.train:
+        save = torch.empty(pma.pma_train_bytes(plan, case.B), dtype=torch.uint8, device="cuda")
+        gout = torch.randn(out.shape, generator=torch.Generator().manual_seed(4)).to(out.dtype).cuda()
+
     def step():
+        if args.train:
+            pma.pma_forward_train(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"],
+                                  dev["wk"], dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"],
+                                  save=save, out=out, weights=weights,
+                                  need_weights=case.need_weights,
+                                  average_attn_weights=case.average, key_padding_mask=kpm)
+            pma.pma_backward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["wk"],
+                             dev["wv"], dev["wo"], dev["bq"] is not None, save, gout,
+                             key_padding_mask=kpm)
+            return
         pma.pma_forward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"],
                         dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"], out=out,
                         weights=weights, need_weights=case.need_weights,
@@ -232,7 +248,8 @@ def main():
         "config": {"workload": f"{case.name}: L={case.L} S={case.S} nnz={nnz} B={case.B} "
                                f"E={case.E} H={case.H} {case.dtype}"
                                f"{' need_weights' if case.need_weights else ''}"
-                               f"{f' key_padding_mask {args.key_padding_mask:g}' if kpm is not None else ''}",
+                               f"{f' key_padding_mask {args.key_padding_mask:g}' if kpm is not None else ''}"
+                               f"{' train step (forward + backward)' if args.train else ''}",
                    "batch": case.B, "nodes": case.L, "nnz": nnz, "embed_dim": case.E,
                    "num_heads": case.H, "parallelism": "single GPU"},
     }

@@ -18,6 +18,7 @@ import numpy as np
 
 __all__ = [
     "PmaError", "Plan", "pma_create", "pma_forward", "pma_forward_masked", "pma_destroy",
+    "pma_train_bytes", "pma_forward_train", "pma_backward",
     "pma_nnz", "pma_edges",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
     "pma_profile_stages",
@@ -75,6 +76,11 @@ def _load():
         "pma_forward": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P]),
         "pma_forward_masked": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, I32,
                                     P]),
+        "pma_train_bytes": (ctypes.c_size_t, [P, I64]),
+        "pma_forward_train": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, I32, P,
+                                   P]),
+        "pma_backward": (st, [P, I64, P, P, P, P, P, P, P, I32, P, P, P, I32, P, P, P, P, P, P, P,
+                              P, P, P, P, P]),
         "pma_destroy": (st, [P]),
         "pma_nnz": (I64, [P]),
         "pma_edges": (st, [P, P, P]),
@@ -257,6 +263,98 @@ def pma_forward_masked(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v
                        weights=weights, need_weights=need_weights,
                        average_attn_weights=average_attn_weights, stream=stream,
                        key_padding_mask=key_padding_mask)
+
+
+def pma_train_bytes(plan: Plan, batch: int) -> int:
+    return int(_load().pma_train_bytes(plan.handle, int(batch)))
+
+
+def _mask_args(m, lead, S):
+    if m is None:
+        return None, 0
+    if tuple(m.shape) == (S,):
+        per = 0
+    elif tuple(m.shape) == tuple(lead) + (S,):
+        per = 1
+    else:
+        raise PmaError(2, f"key_padding_mask has shape {tuple(m.shape)}, expected ({S},) or "
+                          f"{tuple(lead) + (S,)}")
+    import torch
+    return _dptr(m, "key_padding_mask", torch.bool), per
+
+
+def pma_forward_train(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                      save=None, out=None, weights=None, need_weights: bool = False,
+                      average_attn_weights: bool = True, key_padding_mask=None, stream=None):
+    """``pma_forward_train``: returns (out, weights or None, save) where save
+    is a uint8 GPU tensor holding what ``pma_backward`` needs."""
+    import torch
+    lib = _load()
+    tdt = torch.float32 if plan.dtype == "f32" else torch.bfloat16
+    L, S, E, H = plan.L, plan.S, plan.E, plan.H
+    lead = tuple(query.shape[:-2])
+    B = int(np.prod(lead)) if lead else 1
+    if tuple(key.shape[:-2]) != lead or tuple(value.shape[:-2]) != lead:
+        raise PmaError(2, "the batch axes of query, key and value differ")
+    if save is None:
+        save = torch.empty(pma_train_bytes(plan, B), dtype=torch.uint8, device=query.device)
+    if out is None:
+        out = torch.empty(lead + (L, E), dtype=tdt, device=query.device)
+    want_w = need_weights or weights is not None
+    if want_w and weights is None:
+        nnz = pma_nnz(plan)
+        weights = torch.empty(lead + ((nnz,) if average_attn_weights else (nnz, H)),
+                              dtype=torch.float32, device=query.device)
+    mp, per = _mask_args(key_padding_mask, lead, S)
+    st = lib.pma_forward_train(
+        plan.handle, B, _dptr(query, "query", tdt, (L, E)), _dptr(key, "key", tdt, (S, E)),
+        _dptr(value, "value", tdt, (S, E)), _dptr(q_w, "q_w", tdt, (E, E)), _dptr(q_b, "q_b", tdt),
+        _dptr(k_w, "k_w", tdt, (E, E)), _dptr(k_b, "k_b", tdt), _dptr(v_w, "v_w", tdt, (E, E)),
+        _dptr(v_b, "v_b", tdt), _dptr(o_w, "o_w", tdt, (E, E)), _dptr(o_b, "o_b", tdt),
+        _dptr(out, "out", tdt, (L, E)),
+        _dptr(weights, "weights", torch.float32) if want_w else None,
+        int(bool(average_attn_weights)), mp, per, _dptr(save, "save", torch.uint8),
+        _stream_ptr(stream))
+    _check(st)
+    return out, (weights if want_w else None), save
+
+
+def pma_backward(plan: Plan, query, key, value, q_w, k_w, v_w, o_w, has_bias: bool, save,
+                 grad_out, key_padding_mask=None, stream=None):
+    """``pma_backward``: returns a dict of gradients ("query", "key", "value",
+    "q_w", ..., "o_b"; bias entries only with has_bias). A token tensor given
+    for several of query / key / value gets one gradient, the sum."""
+    import torch
+    lib = _load()
+    tdt = torch.float32 if plan.dtype == "f32" else torch.bfloat16
+    L, S, E = plan.L, plan.S, plan.E
+    lead = tuple(query.shape[:-2])
+    B = int(np.prod(lead)) if lead else 1
+    def new(x):
+        return torch.empty(x.shape, dtype=tdt, device=x.device)
+    gq = new(query)
+    gk = gq if key is query else new(key)
+    gv = gk if value is key else (gq if value is query else new(value))
+    gw = {n: torch.empty(E, E, dtype=tdt, device=query.device) for n in ("q_w", "k_w", "v_w", "o_w")}
+    gb = {n: (torch.empty(E, dtype=tdt, device=query.device) if has_bias else None)
+          for n in ("q_b", "k_b", "v_b", "o_b")}
+    mp, per = _mask_args(key_padding_mask, lead, S)
+    st = lib.pma_backward(
+        plan.handle, B, _dptr(query, "query", tdt, (L, E)), _dptr(key, "key", tdt, (S, E)),
+        _dptr(value, "value", tdt, (S, E)), _dptr(q_w, "q_w", tdt, (E, E)),
+        _dptr(k_w, "k_w", tdt, (E, E)), _dptr(v_w, "v_w", tdt, (E, E)),
+        _dptr(o_w, "o_w", tdt, (E, E)), int(bool(has_bias)), _dptr(save, "save", torch.uint8),
+        _dptr(grad_out, "grad_out", tdt, (L, E)), mp, per, gq.data_ptr(), gk.data_ptr(),
+        gv.data_ptr(), gw["q_w"].data_ptr(), _dptr(gb["q_b"], "q_b", tdt),
+        gw["k_w"].data_ptr(), _dptr(gb["k_b"], "k_b", tdt), gw["v_w"].data_ptr(),
+        _dptr(gb["v_b"], "v_b", tdt), gw["o_w"].data_ptr(), _dptr(gb["o_b"], "o_b", tdt),
+        _stream_ptr(stream))
+    _check(st)
+    res = {"query": gq, "key": gk, "value": gv}
+    res.update(gw)
+    if has_bias:
+        res.update(gb)
+    return res
 
 
 def pma_destroy(plan: Plan) -> None:

@@ -568,7 +568,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
             float out[CH];
 #pragma unroll
             for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
-            if (SC && st.active && st.head_lead) {
+            if (a.stat_ml && st.active && st.head_lead) {   // weights or training
                 float *sp = a.stat_ml;
                 if constexpr (W32)
                     sp += ((uint32_t)t * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;

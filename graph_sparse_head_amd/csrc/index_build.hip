@@ -355,7 +355,8 @@ void free_graph(GraphDev *g)
     int32_t **ptrs[] = {&g->row_ptr,     &g->csr_src,     &g->csr_tgt,    &g->csr_eid,
                         &g->task_target, &g->task_begin,  &g->task_end,   &g->task_slot,
                         &g->task_split,  &g->split_target, &g->split_slot0, &g->split_count,
-                        &g->csr_kv,      &g->kv_rows};
+                        &g->csr_kv,      &g->kv_rows,     &g->csc_ptr,    &g->csc_tgt,
+                        &g->csc_pos};
     for (int32_t **p : ptrs) {
         if (*p)
             (void)hipFree(*p);
@@ -508,6 +509,58 @@ done:
             if (p)
                 (void)hipFree(p);
     }
+    return st;
+}
+
+// Source-major view of the same edges, for the backward pass: positions of
+// the target-grouped entries sorted stably by source (so by (source,
+// target)), each entry's target, and per-source offsets.
+__global__ void csc_fill(const int32_t *perm, const int32_t *csr_tgt, int64_t nnz, int32_t *csc_tgt)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < nnz)
+        csc_tgt[j] = csr_tgt[perm[j]];
+}
+
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, hipStream_t stream, char *err,
+                     size_t errlen)
+{
+    pma_status st = PMA_OK;
+    const size_t i4 = sizeof(int32_t);
+    const int64_t n_sort = std::max(nnz, S);
+    const int64_t ntiles = (n_sort + kTile - 1) / kTile;
+    const int64_t count_len = 256 * ntiles;
+    const int64_t scan_len = (count_len > n_sort ? count_len : n_sort) / kTile + 2;
+    int32_t *perm = nullptr, *perm_tmp = nullptr, *counts = nullptr, *scan_tmp = nullptr,
+            *deg = nullptr;
+    PMA_TRY(hipMalloc(&perm, nnz * i4));
+    PMA_TRY(hipMalloc(&perm_tmp, nnz * i4));
+    PMA_TRY(hipMalloc(&counts, count_len * i4));
+    PMA_TRY(hipMalloc(&scan_tmp, scan_len * i4));
+    PMA_TRY(hipMalloc(&deg, S * i4));
+    PMA_TRY(hipMalloc(&g->csc_ptr, (S + 1) * i4));
+    PMA_TRY(hipMalloc(&g->csc_tgt, nnz * i4));
+    PMA_TRY(hipMemsetAsync(deg, 0, S * i4, stream));
+    iota_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, nnz);
+    PMA_TRY(radix_sort_perm(g->csr_src, bits_for(S - 1), perm, perm_tmp, nnz, counts, scan_tmp,
+                            stream));
+    csc_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, g->csr_tgt, nnz, g->csc_tgt);
+    degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, nnz, deg);
+    PMA_TRY(scan_exclusive(deg, g->csc_ptr, S, g->csc_ptr + S, scan_tmp, stream));
+    PMA_TRY(hipGetLastError());
+    PMA_TRY(hipStreamSynchronize(stream));
+    g->csc_pos = perm;   // kept
+    perm = nullptr;
+    goto done;
+fail:
+    (void)hipStreamSynchronize(stream);
+    if (g->csc_ptr) (void)hipFree(g->csc_ptr);
+    if (g->csc_tgt) (void)hipFree(g->csc_tgt);
+    g->csc_ptr = g->csc_tgt = nullptr;
+done:
+    for (int32_t *q : {perm, perm_tmp, counts, scan_tmp, deg})
+        if (q)
+            (void)hipFree(q);
     return st;
 }
 

@@ -10,6 +10,8 @@
 #include <new>
 #include <vector>
 
+#include <rocblas/rocblas.h>
+
 #include "pma_internal.h"
 
 #define PMA_API extern "C" __attribute__((visibility("default")))
@@ -55,6 +57,10 @@ struct pma_plan {
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
     uint64_t *kpm_bits = nullptr;   // key_padding_mask packed by source
+    // backward: fp32 scratch (grown) and a rocBLAS handle for its plain GEMMs
+    float *bw = nullptr;
+    size_t bw_bytes = 0;
+    rocblas_handle blas = nullptr;
     // profiling
     unsigned prof = 0;   // stages timed: bit s for stage s
     std::vector<EventPair> pending;
@@ -295,6 +301,10 @@ PMA_API pma_status pma_destroy(pma_plan *plan)
     (void)hipDeviceSynchronize();
     pma::free_graph(&plan->g);
     free_workspace(plan);
+    if (plan->bw)
+        (void)hipFree(plan->bw);
+    if (plan->blas)
+        (void)rocblas_destroy_handle(plan->blas);
     for (auto &ev : plan->pending) {
         (void)hipEventDestroy(ev.a);
         (void)hipEventDestroy(ev.b);
@@ -385,11 +395,31 @@ PMA_API pma_status pma_work_split(const pma_plan *plan, int64_t *task_target,
 
 namespace {
 
+// Byte offsets of the training save area: q (B, L, E), k then v (B, S, E),
+// mixed (B, L, E) in the plan's dtype, softmax (max, sum) [L][B][H][2] fp32.
+struct SaveLayout {
+    size_t q, k, v, mixed, ml, total;
+};
+
+SaveLayout save_layout(const pma_plan *p, int64_t B)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
+    SaveLayout s;
+    s.q = 0;
+    s.k = up(s.q + (size_t)B * p->L * p->E * es);
+    s.v = s.k + (size_t)B * p->S * p->E * es;
+    s.mixed = up(s.v + (size_t)B * p->S * p->E * es);
+    s.ml = up(s.mixed + (size_t)B * p->L * p->E * es);
+    s.total = up(s.ml + (size_t)p->L * B * p->H * 2 * 4);
+    return s;
+}
+
 pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const void *key,
                         const void *value, const void *q_w, const void *q_b, const void *k_w,
                         const void *k_b, const void *v_w, const void *v_b, const void *o_w,
                         const void *o_b, void *out, float *weights, int average_attn_weights,
-                        const uint8_t *kpm, int kpm_per_sample, hipStream_t stream)
+                        const uint8_t *kpm, int kpm_per_sample, char *save, hipStream_t stream)
 {
     g_err[0] = 0;
     if (!plan)
@@ -412,7 +442,12 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
         return st;
     StageTimer tm{p, stream};
     const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
-    char *kvc = static_cast<char *>(p->kv);
+    // With a save area (training) q, k, v, mixed and the softmax statistics
+    // go there, batch-first, for pma_backward; otherwise to the workspace.
+    const SaveLayout sv = save_layout(p, B);
+    void *qt = save ? (void *)(save + sv.q) : p->qt;
+    char *kvc = save ? save + sv.k : static_cast<char *>(p->kv);
+    void *mixed_ws = save ? (void *)(save + sv.mixed) : p->mixed;
     // Keys and values are needed only for the sources some edge reads
     // (n_kv of S). Projecting just those rows saves work unless query, key
     // and value are one tensor and most sources are read: then one pass over
@@ -420,15 +455,16 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     // key/value pass re-reads n_kv / S of the tokens; it pays below 3/5).
     const bool shared = query == key && key == value && L == S;
     const int64_t n_kv = p->g.n_kv;
-    const bool compact = n_kv < S && (p->compact >= 0 ? p->compact == 1 : (!shared || 5 * n_kv < 3 * S));
+    const bool compact = !save && n_kv < S &&
+                         (p->compact >= 0 ? p->compact == 1 : (!shared || 5 * n_kv < 3 * S));
     const int64_t S_ws = compact ? n_kv : S;   // key/value rows in the workspace
-    const pma::Layout lay = pma::make_layout(p->batch_first_ws, B, L, S_ws, E);
+    const pma::Layout lay = pma::make_layout(save ? true : p->batch_first_ws, B, L, S_ws, E);
 
     // Step 1: q, k, v projections into the workspace layout. Caller tokens are
     // batch-first and read in storage order (key/value rows through the list
     // of read sources when compact).
     tm.begin(PMA_STAGE_PROJ_IN);
-    const pma::ProjOut oq{q_w, q_b, p->qt, lay.q_b, lay.q_t};
+    const pma::ProjOut oq{q_w, q_b, qt, lay.q_b, lay.q_t};
     const pma::ProjOut ok{k_w, k_b, kvc, lay.kv_b, lay.kv_s};
     const pma::ProjOut ov{v_w, v_b, kvc + (size_t)lay.kv_v * es, lay.kv_b, lay.kv_s};
     auto in_args = [&](const void *x, int64_t n, int nblk, pma::ProjOut o0, pma::ProjOut o1,
@@ -472,13 +508,13 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.nnz = p->nnz;
     ea.dt = p->dtype;
     ea.lay = lay;
-    ea.qt = p->qt;
-    ea.kv = p->kv;
+    ea.qt = qt;
+    ea.kv = kvc;
     ea.kv_bytes = (uint64_t)S_ws * 2 * B * E * es;
-    ea.mixed = p->mixed;
+    ea.mixed = mixed_ws;
     ea.part_acc = p->part_acc;
     ea.part_ml = p->part_ml;
-    ea.stat_ml = weights ? p->stat_ml : nullptr;
+    ea.stat_ml = save ? reinterpret_cast<float *>(save + sv.ml) : (weights ? p->stat_ml : nullptr);
     ea.scores = weights ? p->scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
@@ -498,7 +534,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 12 : 0);
     // out_proj in the edge / merge epilogue where it applies (16-byte aligned
     // Wo and out).
-    ea.fuse_out = p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
+    ea.fuse_out = !save && p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
                   (((uintptr_t)o_w | (uintptr_t)out) & 15) == 0;
     ea.wo = o_w;
     ea.bo = o_b;
@@ -535,7 +571,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     tm.begin(PMA_STAGE_OUT);
     const pma::ProjOut oo{o_w, o_b, out, L * E, E};
     const int mixed_token_major = lay.m_b == E ? 1 : 0;
-    pma::ProjArgs ao{p->mixed, L * B, L, B, mixed_token_major, 1, {oo}};
+    pma::ProjArgs ao{mixed_ws, L * B, L, B, mixed_token_major, 1, {oo}};
     ao.x_token_major = mixed_token_major;
     st = pma::launch_proj(ao, E, p->dtype, stream);
     tm.end();
@@ -553,7 +589,7 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
                                float *weights, int average_attn_weights, hipStream_t stream)
 {
     return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
-                        out, weights, average_attn_weights, nullptr, 0, stream);
+                        out, weights, average_attn_weights, nullptr, 0, nullptr, stream);
 }
 
 PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void *query,
@@ -571,7 +607,243 @@ PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void 
         return fail(PMA_E_ARG, "mask_per_sample must be 0 or 1");
     return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                         out, weights, average_attn_weights, key_padding_mask, mask_per_sample,
-                        stream);
+                        nullptr, stream);
+}
+
+PMA_API size_t pma_train_bytes(const pma_plan *plan, int64_t batch)
+{
+    if (!plan || batch <= 0)
+        return 0;
+    return save_layout(plan, batch).total;
+}
+
+PMA_API pma_status pma_forward_train(pma_plan *plan, int64_t batch, const void *query,
+                                     const void *key, const void *value, const void *q_w,
+                                     const void *q_b, const void *k_w, const void *k_b,
+                                     const void *v_w, const void *v_b, const void *o_w,
+                                     const void *o_b, void *out, float *weights,
+                                     int average_attn_weights, const uint8_t *key_padding_mask,
+                                     int mask_per_sample, void *save, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!save)
+        return fail(PMA_E_NULL, "save is NULL");
+    if (key_padding_mask && mask_per_sample != 0 && mask_per_sample != 1)
+        return fail(PMA_E_ARG, "mask_per_sample must be 0 or 1");
+    return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                        out, weights, average_attn_weights, key_padding_mask,
+                        key_padding_mask ? mask_per_sample : 0, static_cast<char *>(save), stream);
+}
+
+namespace {
+
+// C (m x n) = op(A) op(B) + beta C on row-major fp32 matrices, through the
+// column-major GEMM (a row-major matrix is its transpose column-major).
+//   ta = 0: A is (m x k) row-major; ta = 1: A is (k x m) row-major, used transposed.
+//   tb likewise for B (k x n) / (n x k).
+rocblas_status gemm_rm(rocblas_handle h, int ta, int tb, int64_t m, int64_t n, int64_t k,
+                       const float *A, const float *B, float beta, float *C)
+{
+    const float one = 1.f;
+    // C^T (n x m, column-major) = op(B)^T op(A)^T
+    return rocblas_sgemm(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+                         ta ? rocblas_operation_transpose : rocblas_operation_none,
+                         (rocblas_int)n, (rocblas_int)m, (rocblas_int)k, &one, B,
+                         (rocblas_int)(tb ? k : n), A, (rocblas_int)(ta ? m : k), &beta, C,
+                         (rocblas_int)n);
+}
+
+}  // namespace
+
+PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query,
+                                const void *key, const void *value, const void *q_w,
+                                const void *k_w, const void *v_w, const void *o_w, int has_bias,
+                                const void *save, const void *grad_out,
+                                const uint8_t *key_padding_mask, int mask_per_sample,
+                                void *grad_query, void *grad_key, void *grad_value,
+                                void *grad_q_w, void *grad_q_b, void *grad_k_w, void *grad_k_b,
+                                void *grad_v_w, void *grad_v_b, void *grad_o_w, void *grad_o_b,
+                                hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!plan)
+        return fail(PMA_E_NULL, "plan is NULL");
+    if (batch <= 0)
+        return fail(PMA_E_SIZE, "batch must be positive (got %lld)", (long long)batch);
+    if (!query || !key || !value || !q_w || !k_w || !v_w || !o_w || !save || !grad_out ||
+        !grad_query || !grad_key || !grad_value || !grad_q_w || !grad_k_w || !grad_v_w ||
+        !grad_o_w)
+        return fail(PMA_E_NULL, "a required pointer is NULL");
+    if (has_bias != 0 && has_bias != 1)
+        return fail(PMA_E_ARG, "has_bias must be 0 or 1");
+    if (has_bias && (!grad_q_b || !grad_k_b || !grad_v_b || !grad_o_b))
+        return fail(PMA_E_NULL, "a bias gradient pointer is NULL");
+    if (key_padding_mask && mask_per_sample != 0 && mask_per_sample != 1)
+        return fail(PMA_E_ARG, "mask_per_sample must be 0 or 1");
+    pma_plan *p = plan;
+    const int64_t B = batch, L = p->L, S = p->S, E = p->E, H = p->H, nnz = p->nnz;
+    // a shared gradient output must belong to inputs of one shape
+    if ((grad_key == grad_query || grad_value == grad_query) && L != S)
+        return fail(PMA_E_ARG, "a key/value gradient shares the query's only when L == S");
+    if (E / H > 64)
+        return fail(PMA_E_UNSUPPORTED, "head size above 64 in the backward pass");
+    if ((L > S ? L : S) * B * 2 * E > ((int64_t)1 << 40))
+        return fail(PMA_E_UNSUPPORTED, "batch too large");
+    char err[256] = "";
+    if (!p->g.csc_ptr) {
+        pma_status st = pma::build_csc(&p->g, nnz, S, stream, err, sizeof err);
+        if (st != PMA_OK)
+            return fail(st, "%s", err);
+    }
+    if (!p->blas && rocblas_create_handle(&p->blas) != rocblas_status_success) {
+        p->blas = nullptr;
+        return fail(PMA_E_DEVICE, "rocblas_create_handle failed");
+    }
+    if (rocblas_set_stream(p->blas, stream) != rocblas_status_success)
+        return fail(PMA_E_DEVICE, "rocblas_set_stream failed");
+
+    // fp32 scratch: dO, dm, dq, dk, dv, P, DZ, tokens, mixed, weights, token
+    // gradients, weight and bias gradients
+    const size_t RL = (size_t)B * L * E, RS = (size_t)B * S * E, EE = (size_t)E * E;
+    const size_t PZ = (size_t)nnz * B * H;
+    const size_t need = (3 * RL + 2 * RS + 2 * PZ + (RL + 2 * RS) + RL + 4 * EE + (RL + 2 * RS) +
+                         4 * EE + 4 * E) * sizeof(float) + 64 * 256;
+    if (need > p->bw_bytes) {
+        hipError_t e = hipStreamSynchronize(stream);
+        if (p->bw)
+            (void)hipFree(p->bw);
+        p->bw = nullptr;
+        p->bw_bytes = 0;
+        if (e == hipSuccess)
+            e = hipMalloc(&p->bw, need);
+        if (e != hipSuccess)
+            return fail(e == hipErrorOutOfMemory ? PMA_E_OOM : PMA_E_DEVICE,
+                        "backward scratch of %zu bytes: %s", need, hipGetErrorString(e));
+        p->bw_bytes = need;
+    }
+    float *cur = p->bw;
+    auto take = [&](size_t n) {
+        float *r = cur;
+        cur += (n + 63) & ~(size_t)63;
+        return r;
+    };
+    float *dO = take(RL), *dm = take(RL), *dq = take(RL), *dk = take(RS), *dv = take(RS);
+    float *P = take(PZ), *DZ = take(PZ);
+    float *xq = take(RL), *xk = take(RS), *xv = take(RS), *mix = take(RL);
+    float *W[4] = {take(EE), take(EE), take(EE), take(EE)};
+    float *gxq = take(RL), *gxk = take(RS), *gxv = take(RS);
+    float *gW[4] = {take(EE), take(EE), take(EE), take(EE)};
+    float *gb = take(4 * E);
+
+    const pma_dtype dt = p->dtype;
+    const size_t es = dt == PMA_BF16 ? 2 : 4;
+    const SaveLayout sv = save_layout(p, B);
+    const char *sb = static_cast<const char *>(save);
+    pma_status st = PMA_OK;
+    auto ok = [&](pma_status x) {
+        if (st == PMA_OK)
+            st = x;
+    };
+    ok(pma::to_f32(grad_out, dt, dO, RL, stream));
+    ok(pma::to_f32(sb + sv.mixed, dt, mix, RL, stream));
+    ok(pma::to_f32(query, dt, xq, RL, stream));
+    if (key != query)
+        ok(pma::to_f32(key, dt, xk, RS, stream));
+    if (value != key && value != query)
+        ok(pma::to_f32(value, dt, xv, RS, stream));
+    const float *Xk = key == query ? xq : xk;
+    const float *Xv = value == key ? Xk : (value == query ? xq : xv);
+    const void *ws[4] = {q_w, k_w, v_w, o_w};
+    for (int i = 0; i < 4; ++i)
+        ok(pma::to_f32(ws[i], dt, W[i], EE, stream));
+    if (st != PMA_OK)
+        return fail(st, "conversion failed: %s", hipGetErrorString(hipGetLastError()));
+
+    rocblas_handle h = p->blas;
+    bool blas_ok = true;
+    auto g = [&](rocblas_status r) { blas_ok = blas_ok && r == rocblas_status_success; };
+    const int64_t RLr = B * L, RSr = B * S;
+    // out_proj: dm = dO Wo; dWo = dO^T mixed; dbo = column sums of dO
+    g(gemm_rm(h, 0, 0, RLr, E, E, dO, W[3], 0.f, dm));
+    g(gemm_rm(h, 1, 0, E, E, RLr, dO, mix, 0.f, gW[3]));
+    if (has_bias)
+        ok(pma::colsum(dO, RLr, (int)E, gb + 3 * E, stream));
+
+    // scores, softmax and mix
+    pma::BwdArgs a;
+    a.B = (int)B;
+    a.L = (int)L;
+    a.S = (int)S;
+    a.E = (int)E;
+    a.H = (int)H;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)(E / H)));
+    a.inv_sqrt_d = (float)(1.0 / sqrt((double)(E / H)));
+    a.q = sb + sv.q;
+    a.k = sb + sv.k;
+    a.v = sb + sv.v;
+    a.mixed = sb + sv.mixed;
+    a.ml = reinterpret_cast<const float *>(sb + sv.ml);
+    a.dm = dm;
+    a.row_ptr = p->g.row_ptr;
+    a.csr_src = p->g.csr_src;
+    a.csc_ptr = p->g.csc_ptr;
+    a.csc_tgt = p->g.csc_tgt;
+    a.csc_pos = p->g.csc_pos;
+    a.kpm_bits = nullptr;
+    a.kpm_words = 0;
+    if (key_padding_mask) {
+        pma_status st2 = ensure_workspace(p, B, false, stream);
+        if (st2 != PMA_OK)
+            return st2;
+        ok(pma::pack_mask(key_padding_mask, mask_per_sample ? S : 0, B, S, p->kpm_bits, stream));
+        a.kpm_bits = p->kpm_bits;
+        a.kpm_words = (int)((B + 63) / 64);
+    }
+    a.P = P;
+    a.DZ = DZ;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    ok(pma::launch_bwd_edges(a, dt, stream));
+
+    // q, k, v projections: dW = G^T X, db = column sums of G, dX = G W;
+    // gradients of one shared token tensor accumulate
+    const float *G[3] = {dq, dk, dv};
+    const float *X[3] = {xq, Xk, Xv};
+    const int64_t rows[3] = {RLr, RSr, RSr};
+    void *outs[3] = {grad_query, grad_key, grad_value};
+    float *tmp[3] = {gxq, gxk, gxv};
+    float *dst[3];
+    for (int i = 0; i < 3; ++i) {
+        g(gemm_rm(h, 1, 0, E, E, rows[i], G[i], X[i], 0.f, gW[i]));
+        if (has_bias)
+            ok(pma::colsum(G[i], rows[i], (int)E, gb + i * E, stream));
+        int j = 0;
+        while (j < i && outs[j] != outs[i])
+            ++j;
+        dst[i] = j < i ? dst[j] : tmp[i];
+        g(gemm_rm(h, 0, 0, rows[i], E, E, G[i], W[i], j < i ? 1.f : 0.f, dst[i]));
+    }
+    if (!blas_ok)
+        return fail(PMA_E_DEVICE, "rocBLAS GEMM failed");
+    for (int i = 0; i < 3; ++i) {
+        int j = 0;
+        while (j < i && outs[j] != outs[i])
+            ++j;
+        if (j == i)
+            ok(pma::from_f32(dst[i], dt, outs[i], rows[i] * E, stream));
+    }
+    void *gws[4] = {grad_q_w, grad_k_w, grad_v_w, grad_o_w};
+    void *gbs[4] = {grad_q_b, grad_k_b, grad_v_b, grad_o_b};
+    for (int i = 0; i < 4; ++i) {
+        ok(pma::from_f32(gW[i], dt, gws[i], EE, stream));
+        if (has_bias)
+            ok(pma::from_f32(gb + i * E, dt, gbs[i], E, stream));
+    }
+    (void)es;
+    if (st != PMA_OK)
+        return fail(st, "backward launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PMA_OK;
 }
 
 PMA_API pma_status pma_profile(pma_plan *plan, int enable)

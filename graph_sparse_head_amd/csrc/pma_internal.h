@@ -25,6 +25,10 @@ struct GraphDev {
     // Sources some edge reads, in ascending order (kv_rows[0, n_kv)), and each
     // CSR entry's source as a position in that list (csr_kv, + kSrcPad zeros).
     int32_t *kv_rows = nullptr, *csr_kv = nullptr;
+    // Source-major view, built on first backward: per source s its entries
+    // csc_ptr[s] .. csc_ptr[s+1] give each edge's target (csc_tgt) and its
+    // position in the target-grouped arrays (csc_pos).
+    int32_t *csc_ptr = nullptr, *csc_tgt = nullptr, *csc_pos = nullptr;
     int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0, n_kv = 0;
 };
 
@@ -35,6 +39,9 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
                        int64_t S, int chunk, hipStream_t stream, GraphDev *g, char *err,
                        size_t errlen);
 void free_graph(GraphDev *g);
+// Builds csc_ptr / csc_tgt / csc_pos (blocks on `stream` once).
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, hipStream_t stream, char *err,
+                     size_t errlen);
 
 // ---- projections (proj.hip) ----------------------------------------------
 
@@ -118,6 +125,26 @@ bool out_fusable(int64_t E, int64_t H, pma_dtype dt);
 // ceil(B / 64). Asynchronous on s.
 pma_status pack_mask(const uint8_t *mask, int64_t bstride, int64_t B, int64_t S, uint64_t *bits,
                      hipStream_t s);
+
+// ---- backward pass (backward.hip) ------------------------------------------
+
+struct BwdArgs {
+    int B, L, S, E, H;
+    float scale_log2;    // log2(e) / sqrt(d): the forward's score scale
+    float inv_sqrt_d;
+    const void *q, *k, *v, *mixed;   // saved, batch-first, plan dtype
+    const float *ml;                 // saved [L][B][H][2] (max, sum), base 2
+    const float *dm;                 // (B, L, E) gradient reaching mixed
+    const int32_t *row_ptr, *csr_src, *csc_ptr, *csc_tgt, *csc_pos;
+    const uint64_t *kpm_bits;        // packed mask or nullptr
+    int kpm_words;
+    float *P, *DZ;                   // [nnz][B][H] scratch
+    float *dq, *dk, *dv;             // (B, L, E), (B, S, E), (B, S, E) fp32
+};
+pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s);
+pma_status to_f32(const void *x, pma_dtype dt, float *y, int64_t n, hipStream_t s);
+pma_status from_f32(const float *x, pma_dtype dt, void *y, int64_t n, hipStream_t s);
+pma_status colsum(const float *g, int64_t rows, int E, float *out, hipStream_t s);
 
 // Whether the edge kernels take a key_padding_mask for these arguments (the
 // fast kernel needs every tensor under 2 GiB when masked).

@@ -8,10 +8,11 @@ moves layouts (sequence-first <-> batch-first, leading axes) and hands
 pointers to ``pma_forward`` / ``pma_forward_masked``. Plans are built per
 (device, dtype) on first use and cached.
 
-Not covered: dropout in training mode (the kernels compute the eval-mode
-softmax; a training-mode call with dropout > 0 raises), attn_mask and
-is_causal (must be None / False, as on the page), checkpoint identity and
-index digests.
+Gradients flow through pma_forward_train / pma_backward (a torch.autograd
+Function). Not covered: dropout in training mode (the kernels compute the
+eval-mode softmax; a training-mode call with dropout > 0 raises), attn_mask
+and is_causal (must be None / False, as on the page), checkpoint identity
+and index digests.
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from . import pma_create, pma_destroy, pma_edges, pma_forward
+from . import pma_backward, pma_create, pma_destroy, pma_edges, pma_forward, pma_forward_train
 
 __all__ = ["PackedMultiheadAttention", "ModuleArgError"]
 
@@ -292,10 +293,11 @@ class PackedMultiheadAttention(torch.nn.Module):
         mask = None if key_padding_mask is None else key_padding_mask.to(device=qc.device).contiguous()
         if torch.is_grad_enabled() and (q.requires_grad or k.requires_grad or v.requires_grad or
                                         any(p.requires_grad for p in self.parameters())):
-            return _PackedAttnFn.apply(self, plan, qc, kc, vc, mask, need_weights,
-                                       average_attn_weights, same_qkv, same_kv,
-                                       *self._params())
-        out, weights = self._run(plan, qc, kc, vc, mask, need_weights, average_attn_weights)
+            out, weights = _PackedAttnFn.apply(plan, qc, kc, vc, mask, need_weights,
+                                               average_attn_weights, same_qkv, same_kv,
+                                               *self._params())
+        else:
+            out, weights = self._run(plan, qc, kc, vc, mask, need_weights, average_attn_weights)
         return self._finish(out, weights, seq_first, lead)
 
     def _params(self):
@@ -325,13 +327,40 @@ class PackedMultiheadAttention(torch.nn.Module):
 
 
 class _PackedAttnFn(torch.autograd.Function):
-    """Autograd hook-up; the backward pass is not available yet."""
+    """Forward through pma_forward_train (which keeps what the backward
+    needs in a save area), backward through pma_backward."""
 
     @staticmethod
-    def forward(ctx, layer, plan, q, k, v, mask, need_weights, average, same_qkv, same_kv, *params):
-        raise ModuleArgError("gradients through PackedMultiheadAttention are not available; "
-                             "run the forward under torch.no_grad()")
+    def forward(ctx, plan, q, k, v, mask, need_weights, average, same_qkv, same_kv,
+                q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b):
+        def c(t):
+            return None if t is None else t.detach().contiguous()
+        ws = [c(t) for t in (q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b)]
+        out, weights, save = pma_forward_train(plan, q, k, v, *ws, need_weights=need_weights,
+                                               average_attn_weights=average,
+                                               key_padding_mask=mask)
+        ctx.plan = plan
+        ctx.has_bias = q_b is not None
+        ctx.same = (same_qkv, same_kv)
+        ctx.mask = mask
+        ctx.save_for_backward(q, k, v, save, ws[0], ws[2], ws[4], ws[6])
+        if weights is not None:
+            ctx.mark_non_differentiable(weights)
+        return out, weights
 
     @staticmethod
-    def backward(ctx, *grads):  # pragma: no cover
-        raise NotImplementedError
+    def backward(ctx, grad_out, grad_weights):
+        q, k, v, save, q_w, k_w, v_w, o_w = ctx.saved_tensors
+        same_qkv, same_kv = ctx.same
+        # the forward received one tensor object per shared role; the
+        # gradient of a shared tensor is returned once (autograd sums per use)
+        kk = q if same_qkv else k
+        vv = kk if (same_qkv or same_kv) else v
+        g = pma_backward(ctx.plan, q, kk, vv, q_w, k_w, v_w, o_w, ctx.has_bias, save,
+                         grad_out.contiguous(), key_padding_mask=ctx.mask)
+        gq = g["query"]
+        gk = None if same_qkv else g["key"]
+        gv = None if (same_qkv or same_kv) else g["value"]
+        gb = [g.get(n) for n in ("q_b", "k_b", "v_b", "o_b")]
+        return (None, gq, gk, gv, None, None, None, None, None,
+                g["q_w"], gb[0], g["k_w"], gb[1], g["v_w"], gb[2], g["o_w"], gb[3])

@@ -30,6 +30,7 @@
 #ifndef PMA_H
 #define PMA_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -169,6 +170,66 @@ pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void *query, 
                               const void *o_w, const void *o_b, void *out, float *weights,
                               int average_attn_weights, const uint8_t *key_padding_mask,
                               int mask_per_sample, hipStream_t stream);
+
+/* ---- training ------------------------------------------------------------
+ *
+ * The kpnn2 page's layer trains through torch autograd ("Notes": training
+ * keeps the gathers, or recomputes them, for backward). Here a forward that
+ * will be differentiated writes what the backward needs to a caller-owned
+ * save area, and pma_backward returns the gradients of every input and
+ * parameter. Dropout is not applied (eval-mode softmax).
+ */
+
+/* Bytes of the save area for a batch of `batch` samples (0 for a NULL plan
+   or batch <= 0). */
+size_t pma_train_bytes(const pma_plan *plan, int64_t batch);
+
+/*
+ * pma_forward_train -- pma_forward (masked when key_padding_mask is not
+ * NULL) that also fills `save` (DEVICE, pma_train_bytes(plan, batch) bytes,
+ * 256-byte aligned): the projected q, k, v, the joined mix before out_proj
+ * and each target's softmax statistics. The save area belongs to the caller
+ * and must stay unchanged until the matching pma_backward. Errors: those of
+ * pma_forward_masked, and PMA_E_NULL (save NULL).
+ */
+pma_status pma_forward_train(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                             const void *value, const void *q_w, const void *q_b, const void *k_w,
+                             const void *k_b, const void *v_w, const void *v_b, const void *o_w,
+                             const void *o_b, void *out, float *weights, int average_attn_weights,
+                             const uint8_t *key_padding_mask, int mask_per_sample, void *save,
+                             hipStream_t stream);
+
+/*
+ * pma_backward -- gradients of sum(out * grad_out) for the forward that
+ * filled `save` (same plan, batch, tokens, weights and mask).
+ *
+ *   query, key, value, q_w, k_w, v_w, o_w   DEVICE, as given to the forward.
+ *   has_bias          1 if the forward had biases (then the four bias
+ *                     gradients are written), else 0.
+ *   grad_out          DEVICE (B, L, E), plan dtype.
+ *   key_padding_mask, mask_per_sample       as given to the forward (NULL
+ *                     for none).
+ *   grad_query (B, L, E), grad_key, grad_value (B, S, E), grad_*_w (E, E),
+ *   grad_*_b (E)      DEVICE outputs in the plan dtype, overwritten. When
+ *                     two of query / key / value are one tensor, pass one
+ *                     output pointer for both: it receives the sum of their
+ *                     gradients.
+ *
+ * Computation: out_proj gradients, then two passes over the edges (by
+ * target: query gradients and each edge's softmax weight and score
+ * gradient; by source: key and value gradients), then the projections'
+ * gradients; fp32 throughout, plain GEMMs through rocBLAS. The first call
+ * builds a source-major copy of the edge index (blocks once). Errors:
+ * PMA_E_NULL, PMA_E_SIZE, PMA_E_ARG (flags, a shared gradient output with
+ * L != S), PMA_E_UNSUPPORTED (head size above 64), PMA_E_OOM, PMA_E_DEVICE.
+ */
+pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                        const void *value, const void *q_w, const void *k_w, const void *v_w,
+                        const void *o_w, int has_bias, const void *save, const void *grad_out,
+                        const uint8_t *key_padding_mask, int mask_per_sample, void *grad_query,
+                        void *grad_key, void *grad_value, void *grad_q_w, void *grad_q_b,
+                        void *grad_k_w, void *grad_k_b, void *grad_v_w, void *grad_v_b,
+                        void *grad_o_w, void *grad_o_b, hipStream_t stream);
 
 /* pma_destroy -- free the plan and everything it owns. NULL is a no-op.
    Waits for the device before freeing. */

@@ -1,0 +1,124 @@
+"""Backward pass on the GPU (pma_forward_train + pma_backward) against the
+gradient oracle (oracle/backward.py): gradients of every token tensor and of
+the eight projection parameters, for separate, key=value and shared
+query/key/value tokens, with and without biases and key_padding_mask."""
+import numpy as np
+import pytest
+import torch
+
+import graph_sparse_head_amd as pma
+import oracle
+from oracle import backward as ob
+from graph_sparse_head_amd import synth
+from gpu_helpers import TOL, max_abs_rel, to_f64
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["query", "key", "value", "q_w", "k_w", "v_w", "o_w", "q_b", "k_b", "v_b", "o_b"]
+ORACLE = {"q_w": "wq", "k_w": "wk", "v_w": "wv", "o_w": "wo", "q_b": "bq", "k_b": "bk",
+          "v_b": "bv", "o_b": "bo"}
+
+
+def _grad_check(c, shared, kpm=None, rows=None):
+    print(f"[backward] {c.name} B={c.B} L={c.L} S={c.S} E={c.E} H={c.H} {c.dtype} "
+          f"shared={shared} mask={kpm is not None}", flush=True)
+    dev = synth.to_torch(c)
+    tdt = torch.float32 if c.dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(5)
+    G = rng.standard_normal((c.B, c.L, c.E)).astype(np.float32)
+    if c.dtype == "bf16":
+        G = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(G))
+    g_dev = torch.from_numpy(G).to(tdt).cuda()
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H, add_self_loops=c.add_self_loops,
+                          dtype=c.dtype)
+    try:
+        mask = None if kpm is None else torch.from_numpy(kpm).cuda()
+        args = (dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"], dev["bk"],
+                dev["wv"], dev["bv"], dev["wo"], dev["bo"])
+        out, _, save = pma.pma_forward_train(plan, *args, key_padding_mask=mask)
+        # the training forward computes the same output as the plain one
+        out2, _ = pma.pma_forward(plan, *args, key_padding_mask=mask)
+        torch.cuda.synchronize()
+        assert max_abs_rel(to_f64(out, c.dtype), to_f64(out2, c.dtype)) <= TOL[c.dtype]
+        has_bias = dev["bq"] is not None
+        gr = pma.pma_backward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["wk"],
+                              dev["wv"], dev["wo"], has_bias, save, g_dev, key_padding_mask=mask)
+        torch.cuda.synchronize()
+        src, tgt = oracle.prepare_edges(c.src, c.tgt, c.L, c.S, c.E, c.H, c.add_self_loops)
+        params = {k: oracle.widen(v, c.dtype) for k, v in c.params.items()}
+        xq = oracle.widen(c.xq, c.dtype)
+        xk = xq if shared == "qkv" else oracle.widen(c.xk, c.dtype)
+        xv = xk if shared in ("qkv", "kv") else oracle.widen(c.xv, c.dtype)
+        ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src, tgt,
+                           G.astype(np.float64), kpm, shared=shared)
+        for n in NAMES:
+            if n.endswith("_b") and not has_bias:
+                continue
+            got = to_f64(gr[n], c.dtype)
+            want = ref[n] if n in ("query", "key", "value") else ref[ORACLE[n]]
+            if n == "k_b":
+                # Adding one vector to every key shifts all scores into a
+                # target equally, which the softmax ignores: the key bias
+                # gradient is zero up to rounding, judged on the scale of
+                # the key weight gradient (a sum over the same rows).
+                assert np.abs(got).max() <= TOL[c.dtype] * np.abs(ref["wk"]).max(), n
+                continue
+            err = max_abs_rel(got.reshape(want.shape), want)
+            assert err <= TOL[c.dtype], (n, err)
+    finally:
+        pma.pma_destroy(plan)
+
+
+SHAPES = [("f32", 64, 4), ("f32", 16, 4), ("f32", 24, 2), ("f32", 128, 4), ("bf16", 64, 4),
+          ("bf16", 128, 8)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}_E{s[1]}_H{s[2]}")
+@pytest.mark.parametrize("shared", ["none", "kv", "qkv"])
+def test_backward_random(shape, shared):
+    dt, E, H = shape
+    L = S = 70
+    if shared == "none":
+        S = 90
+    c = synth.random_case(80, 3, L, S, E, H, 0.07, dtype=dt, same_kv=shared != "none",
+                          same_qkv=shared == "qkv", name="bwd")
+    _grad_check(c, shared)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_mask_no_bias_self_loops(dt):
+    c = synth.random_case(81, 4, 60, 60, 64, 4, 0.08, dtype=dt, bias="none", add_self_loops=True,
+                          name="bwd_mask")
+    kpm = np.random.default_rng(82).random((c.B, c.S)) < 0.35
+    kpm[1] = True                                    # one sample entirely masked
+    _grad_check(c, "qkv", kpm=kpm)
+
+
+def test_backward_hub_and_empty_targets():
+    c = synth.random_case(83, 2, 150, 150, 32, 2, 0.02, name="bwd_hub")
+    keep = c.tgt != 7
+    c.src = np.concatenate([c.src[keep], np.arange(140)])
+    c.tgt = np.concatenate([c.tgt[keep], np.full(140, 7)])
+    _grad_check(c, "qkv")
+
+
+def test_backward_rejects():
+    c = synth.random_case(84, 2, 20, 30, 8, 2, 0.2, same_kv=True, name="bwd_bad")
+    dev = synth.to_torch(c)
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H)
+    try:
+        lib = pma._load()
+        z = dev["xq"].data_ptr()
+        st = lib.pma_backward(plan.handle, c.B, z, z, z, z, z, z, z, 0, None, z, None, 0, z, z, z,
+                              z, None, z, None, z, None, z, None, None)
+        assert pma.STATUS[st] == "PMA_E_NULL"
+        st = lib.pma_backward(plan.handle, c.B, z, z, z, z, z, z, z, 2, z, z, None, 0, z, z, z,
+                              z, None, z, None, z, None, z, None, None)
+        assert pma.STATUS[st] == "PMA_E_ARG"
+        # a key gradient shared with the query's needs L == S
+        st = lib.pma_backward(plan.handle, c.B, z, z, z, z, z, z, z, 0, z, z, None, 0, z, z, z,
+                              z, None, z, None, z, None, z, None, None)
+        assert pma.STATUS[st] == "PMA_E_ARG"
+        assert lib.pma_train_bytes(None, 4) == 0 and lib.pma_train_bytes(plan.handle, 0) == 0
+    finally:
+        pma.pma_destroy(plan)

@@ -119,3 +119,43 @@ def test_module_from_edgelist_example():
     # x has only its own loop: weight exactly 1
     e = [i for i in range(m.nnz) if m.source_index[i] == 0 and m.target_index[i] == 0][0]
     assert (w[:, e] == 1).all()
+
+
+@pytest.mark.parametrize("layout", ["batch_first", "seq_first"])
+def test_module_gradients(layout):
+    from oracle import backward as ob
+    bf = layout == "batch_first"
+    m = _layer(50, 50, 32, 4, 0.1, 13, batch_first=bf).cuda().train()
+    x = torch.randn(3, 50, 32, generator=torch.Generator().manual_seed(14)).cuda()
+    xin = (x if bf else x.transpose(0, 1).contiguous()).requires_grad_(True)
+    G = torch.randn(3, 50, 32, generator=torch.Generator().manual_seed(15)).cuda()
+    kpm = torch.rand(3, 50, generator=torch.Generator().manual_seed(16)) < 0.2
+    out, _ = m(xin, xin, xin, key_padding_mask=kpm.cuda())
+    (out * (G if bf else G.transpose(0, 1))).sum().backward()
+    xb = _f64(x)
+    ref = ob.gradients(3, 50, 50, 32, 4, xb, xb, xb, _params(m), m.source_index.cpu().numpy(),
+                       m.target_index.cpu().numpy(), _f64(G), kpm.numpy(), shared="qkv")
+    gx = xin.grad if bf else xin.grad.transpose(0, 1)
+    assert max_abs_rel(_f64(gx), ref["query"]) <= TOL["f32"]
+    for lin, w, b in ((m.q_proj, "wq", "bq"), (m.k_proj, "wk", None), (m.v_proj, "wv", "bv"),
+                      (m.out_proj, "wo", "bo")):
+        assert max_abs_rel(_f64(lin.weight.grad), ref[w]) <= TOL["f32"], w
+        if b is not None:
+            assert max_abs_rel(_f64(lin.bias.grad), ref[b]) <= TOL["f32"], b
+
+
+def test_module_trains():
+    # a few plain gradient steps lower a regression loss
+    m = _layer(40, 40, 16, 2, 0.12, 17).cuda().train()
+    x = torch.randn(4, 40, 16, generator=torch.Generator().manual_seed(18)).cuda()
+    y = torch.randn(4, 40, 16, generator=torch.Generator().manual_seed(19)).cuda()
+    opt = torch.optim.SGD(m.parameters(), lr=0.05)
+    losses = []
+    for _ in range(30):
+        opt.zero_grad()
+        out, _ = m(x, x, x)
+        loss = ((out - y) ** 2).mean()
+        loss.backward()
+        opt.step()
+        losses.append(float(loss.detach()))
+    assert losses[-1] < 0.9 * losses[0]
