@@ -11,32 +11,351 @@
 //   dq_h[t] = sum_e dz_e k_h[s_e] / sqrt(d),
 //   dk_h[s] = sum over edges e out of s of dz_e q_h[t_e] / sqrt(d),
 //   dv_h[s] = sum over edges e out of s of p_e dm_h[t_e].
-// The weights p_e are recomputed from the forward's saved scores' (max, sum)
-// per (target, sample, head), in base 2 as the forward computed them. A
-// first pass walks each target's edges (dq, and p_e, dz_e per edge); a
-// second walks each source's edges through the source-major index (dk, dv),
-// so neither needs atomics. Masked keys have p = dz = 0.
+// The weights p_e are recomputed from the forward's saved (max, sum) per
+// (target, sample, head), in base 2 as the forward computed them. A first
+// pass walks each target's edges (dq, and p_e, dz_e per edge); a second walks
+// each source's edges through the source-major index (dk, dv), so neither
+// needs atomics. Long edge lists are cut into pieces whose partial sums a
+// merge adds up in a fixed order. Masked keys have p = dz = 0.
 //
-// Layouts (batch-first): q, mixed (B, L, E) and k, v (B, S, E) in the plan's
-// dtype; dm, dq (B, L, E) and dk, dv (B, S, E) fp32; ml [L][B][H][2];
-// P and DZ [nnz][B][H] by target-grouped position.
+// The linear maps around it: for y = x W^T + b, dx = dy W (rowmm below) and
+// dW = dy^T x, db = column sums of dy (wgrad below), both on the matrix cores.
+//
+// Layouts (batch-first, plan dtype T unless noted): q, mixed, dm, dq (B, L, E);
+// k, v, dk, dv (B, S, E); ml [L][B][H][2] fp32; P and DZ [nnz][B][H] fp32 by
+// target-grouped position. Gradient tensors are stored in T and accumulated
+// in fp32.
 #include "pma_internal.h"
 
 namespace pma {
 namespace {
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+__device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// two fp32 -> packed bf16, round to nearest even
+__device__ inline uint32_t pack_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ inline uint16_t f2bf(float f) { return (uint16_t)(pack_bf16(f, 0.f) & 0xffffu); }
+
 template <typename T> __device__ inline float ld(const T *p);
 template <> __device__ inline float ld<float>(const float *p) { return *p; }
-template <> __device__ inline float ld<uint16_t>(const uint16_t *p)
+template <> __device__ inline float ld<uint16_t>(const uint16_t *p) { return bf2f(*p); }
+template <typename T> __device__ inline void st(T *p, float x);
+template <> __device__ inline void st<float>(float *p, float x) { *p = x; }
+template <> __device__ inline void st<uint16_t>(uint16_t *p, float x) { *p = f2bf(x); }
+
+// 16 bytes of T widened to fp32 (4 floats or 8 bf16), and back
+template <typename T> struct Vec {
+    static constexpr int N = 16 / (int)sizeof(T);
+};
+template <typename T> __device__ inline void store_vec(T *p, const float (&f)[Vec<T>::N])
 {
-    return __uint_as_float((uint32_t)*p << 16);
+    uint4 u;
+    if constexpr (sizeof(T) == 4) {
+        u = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                       __float_as_uint(f[3]));
+    } else {
+        u = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+                       pack_bf16(f[6], f[7]));
+    }
+    *reinterpret_cast<uint4 *>(p) = u;
+}
+template <int N> __device__ inline void store_f32(float *p, const float (&f)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+        *reinterpret_cast<float4 *>(p + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
 }
 
-// One thread per (target, sample, head); DD = head size when fixed at
-// compile time (registers), 0 for any head size up to 64.
-template <typename T, int DD>
-__global__ void __launch_bounds__(256)
-bwd_target(const BwdArgs a)
+template <int CTRL> __device__ inline float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over each aligned group of G lanes (all of them active); every lane of
+// the group ends with the same bits.
+template <int G> __device__ inline float group_sum(float x)
+{
+    if constexpr (G >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (G >= 16) x += dpp<0x140>(x); // row_mirror
+    return x;
+}
+
+__device__ inline bool masked(const BwdArgs &a, int s, int b)
+{
+    return a.kpm_bits &&
+           ((a.kpm_bits[(int64_t)s * a.kpm_words + (b >> 6)] >> (b & 63)) & 1u);
+}
+
+constexpr int kU = 4;   // edges whose rows are loaded together
+
+template <typename T> __device__ inline void widen(const uint4 &u, float (&f)[Vec<T>::N])
+{
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            f[i] = __uint_as_float(w[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+}
+__device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ---- edge passes, 16-byte lanes -----------------------------------------
+// Thread = (piece, sample, 16-byte chunk of the row), chunks fastest; LPH
+// chunks make one head. With UNI the host has checked that a piece's lanes
+// fill whole wavefronts, so the piece and its edge indices are wavefront-
+// uniform and go through scalar loads. Index arrays carry kSrcPad zero
+// entries past their end, so kU entries are read at a time without clamping
+// (entry 0 is a valid row); the next kU edges' rows are in flight while the
+// current ones are used.
+
+template <typename T, int LPH, bool UNI>
+__global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
+{
+    constexpr int VEC = Vec<T>::N;
+    const int CPR = a.E / VEC;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gb = idx / CPR;
+    const int c = (int)(idx - gb * CPR);
+    int64_t task = gb / a.B;
+    const int b = (int)(gb - task * a.B);
+    if (UNI)
+        task = __builtin_amdgcn_readfirstlane((int)task);
+    if (task >= a.n_ttasks)
+        return;
+    const int t = a.t_target[task], beg = a.t_begin[task], end = a.t_end[task];
+    const int slot = a.t_slot[task];
+    const int h = c / LPH;
+    const int64_t row = ((int64_t)b * a.L + t) * a.E + c * VEC;
+    float qv[VEC], dmv[VEC], mx[VEC];
+    widen<T>(ld16(reinterpret_cast<const T *>(a.q) + row), qv);
+    widen<T>(ld16(reinterpret_cast<const T *>(a.dm) + row), dmv);
+    widen<T>(ld16(reinterpret_cast<const T *>(a.mixed) + row), mx);
+    float D = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+        D = fmaf(dmv[i], mx[i], D);
+    D = group_sum<LPH>(D);
+    const float2 ml =
+        *reinterpret_cast<const float2 *>(a.ml + (((int64_t)t * a.B + b) * a.H + h) * 2);
+    const T *Kb = reinterpret_cast<const T *>(a.k) + (int64_t)b * a.S * a.E + c * VEC;
+    const T *Vb = reinterpret_cast<const T *>(a.v) + (int64_t)b * a.S * a.E + c * VEC;
+    const bool lead = (c & (LPH - 1)) == 0;
+    float dq[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+        dq[i] = 0.f;
+    int s[kU], sn[kU];
+    uint4 kr[kU], vr[kU], kn[kU], vn[kU];
+    auto fetch = [&](int p0, int (&ss)[kU], uint4 (&kq)[kU], uint4 (&vq)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            ss[u] = a.csr_src[p0 + u];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            kq[u] = ld16(Kb + (int64_t)ss[u] * a.E);
+            vq[u] = ld16(Vb + (int64_t)ss[u] * a.E);
+        }
+    };
+    if (beg < end)
+        fetch(beg, s, kr, vr);
+    for (int p0 = beg; p0 < end; p0 += kU) {
+        const bool more = p0 + kU < end;
+        if (more)
+            fetch(p0 + kU, sn, kn, vn);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            float kk[VEC], vv[VEC];
+            widen<T>(kr[u], kk);
+            widen<T>(vr[u], vv);
+            float z = 0.f, dp = 0.f;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                z = fmaf(qv[i], kk[i], z);
+                dp = fmaf(dmv[i], vv[i], dp);
+            }
+            z = group_sum<LPH>(z);
+            dp = group_sum<LPH>(dp);
+            const int p = p0 + u;
+            if (p < end) {
+                float pe = 0.f, dz = 0.f;
+                if (ml.y > 0.f && !masked(a, s[u], b)) {
+                    pe = __builtin_amdgcn_exp2f(z * a.scale_log2 - ml.x) / ml.y;
+                    dz = pe * (dp - D);
+                }
+#pragma unroll
+                for (int i = 0; i < VEC; ++i)
+                    dq[i] = fmaf(dz, kk[i], dq[i]);
+                if (lead) {
+                    const int64_t o = ((int64_t)p * a.B + b) * a.H + h;
+                    a.P[o] = pe;
+                    a.DZ[o] = dz;
+                }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                s[u] = sn[u];
+                kr[u] = kn[u];
+                vr[u] = vn[u];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+        dq[i] *= a.inv_sqrt_d;
+    if (slot < 0)
+        store_vec(reinterpret_cast<T *>(a.dq) + row, dq);
+    else
+        store_f32(a.part_q + ((int64_t)slot * a.B + b) * a.E + c * VEC, dq);
+}
+
+template <typename T, int LPH, bool UNI>
+__global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
+{
+    constexpr int VEC = Vec<T>::N;
+    const int CPR = a.E / VEC;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gb = idx / CPR;
+    const int c = (int)(idx - gb * CPR);
+    int64_t task = gb / a.B;
+    const int b = (int)(gb - task * a.B);
+    if (UNI)
+        task = __builtin_amdgcn_readfirstlane((int)task);
+    if (task >= a.n_stasks)
+        return;
+    const int s = a.s_source[task], beg = a.s_begin[task], end = a.s_end[task];
+    const int slot = a.s_slot[task];
+    const int h = c / LPH;
+    const T *Qb = reinterpret_cast<const T *>(a.q) + (int64_t)b * a.L * a.E + c * VEC;
+    const T *Mb = reinterpret_cast<const T *>(a.dm) + (int64_t)b * a.L * a.E + c * VEC;
+    float dk[VEC], dv[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+        dk[i] = dv[i] = 0.f;
+    float pz[kU], dz[kU], pzn[kU], dzn[kU];
+    uint4 qr[kU], mr[kU], qn[kU], mn[kU];
+    auto fetch = [&](int j0, float (&pp)[kU], float (&zz)[kU], uint4 (&qq)[kU], uint4 (&mm)[kU]) {
+        int t[kU], pos[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            t[u] = a.csc_tgt[j0 + u];
+            pos[u] = a.csc_pos[j0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t o = ((int64_t)pos[u] * a.B + b) * a.H + h;
+            pp[u] = a.P[o];
+            zz[u] = a.DZ[o];
+            qq[u] = ld16(Qb + (int64_t)t[u] * a.E);
+            mm[u] = ld16(Mb + (int64_t)t[u] * a.E);
+        }
+    };
+    if (beg < end)
+        fetch(beg, pz, dz, qr, mr);
+    for (int j0 = beg; j0 < end; j0 += kU) {
+        const bool more = j0 + kU < end;
+        if (more)
+            fetch(j0 + kU, pzn, dzn, qn, mn);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (j0 + u < end) {
+                float qq[VEC], mm[VEC];
+                widen<T>(qr[u], qq);
+                widen<T>(mr[u], mm);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    dk[i] = fmaf(dz[u], qq[i], dk[i]);
+                    dv[i] = fmaf(pz[u], mm[i], dv[i]);
+                }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                pz[u] = pzn[u];
+                dz[u] = dzn[u];
+                qr[u] = qn[u];
+                mr[u] = mn[u];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+        dk[i] *= a.inv_sqrt_d;
+    if (slot < 0) {
+        const int64_t row = ((int64_t)b * a.S + s) * a.E + c * VEC;
+        store_vec(reinterpret_cast<T *>(a.dk) + row, dk);
+        store_vec(reinterpret_cast<T *>(a.dv) + row, dv);
+    } else {
+        float *d = a.part_kv + ((int64_t)slot * a.B + b) * 2 * a.E + c * VEC;
+        store_f32(d, dk);
+        store_f32(d + a.E, dv);
+    }
+}
+
+// Sums the pieces of split targets (dq) / split sources (dk, dv) in slot
+// order. Thread = (split, sample, 16-byte chunk).
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_merge_fast(const BwdArgs a, int sources)
+{
+    constexpr int VEC = Vec<T>::N;
+    const int CPR = a.E / VEC;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gb = idx / CPR;
+    const int c = (int)(idx - gb * CPR);
+    const int64_t i = gb / a.B;
+    const int b = (int)(gb - i * a.B);
+    if (i >= (sources ? a.n_ssplit : a.n_tsplit))
+        return;
+    const int row_id = sources ? a.ss_source[i] : a.ts_target[i];
+    const int slot0 = sources ? a.ss_slot0[i] : a.ts_slot0[i];
+    const int count = sources ? a.ss_count[i] : a.ts_count[i];
+    const int nout = sources ? 2 : 1;
+    const int width = nout * a.E;
+    const float *part = sources ? a.part_kv : a.part_q;
+    for (int o = 0; o < nout; ++o) {
+        float acc[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            acc[j] = 0.f;
+        for (int k = 0; k < count; ++k) {
+            const float *src = part + ((int64_t)(slot0 + k) * a.B + b) * width + o * a.E + c * VEC;
+#pragma unroll
+            for (int j = 0; j < VEC; j += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(src + j);
+                acc[j] += v.x;
+                acc[j + 1] += v.y;
+                acc[j + 2] += v.z;
+                acc[j + 3] += v.w;
+            }
+        }
+        T *dst = sources ? reinterpret_cast<T *>(o == 0 ? a.dk : a.dv) +
+                               ((int64_t)b * a.S + row_id) * a.E
+                         : reinterpret_cast<T *>(a.dq) + ((int64_t)b * a.L + row_id) * a.E;
+        store_vec(dst + c * VEC, acc);
+    }
+}
+
+// ---- edge passes, any head size up to 64 ---------------------------------
+
+// One thread per (target, sample, head), whole edge list.
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_target_generic(const BwdArgs a)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t n = (int64_t)a.L * a.B * a.H;
@@ -46,42 +365,36 @@ bwd_target(const BwdArgs a)
     const int64_t bt = i / a.H;
     const int b = (int)(bt % a.B);
     const int t = (int)(bt / a.B);
-    const int d = DD > 0 ? DD : a.E / a.H;
-    const T *q = reinterpret_cast<const T *>(a.q) + ((int64_t)b * a.L + t) * a.E + h * d;
-    const T *mx = reinterpret_cast<const T *>(a.mixed) + ((int64_t)b * a.L + t) * a.E + h * d;
-    const float *dm = a.dm + ((int64_t)b * a.L + t) * a.E + h * d;
-    const float2 ml = *reinterpret_cast<const float2 *>(a.ml + (((int64_t)t * a.B + b) * a.H + h) * 2);
+    const int d = a.E / a.H;
+    const int64_t row = ((int64_t)b * a.L + t) * a.E + h * d;
+    const T *q = reinterpret_cast<const T *>(a.q) + row;
+    const T *mx = reinterpret_cast<const T *>(a.mixed) + row;
+    const T *dm = reinterpret_cast<const T *>(a.dm) + row;
+    const float2 ml =
+        *reinterpret_cast<const float2 *>(a.ml + (((int64_t)t * a.B + b) * a.H + h) * 2);
     float D = 0.f;
     for (int c = 0; c < d; ++c)
-        D = fmaf(dm[c], ld(mx + c), D);
-    float dq[DD > 0 ? DD : 64];
-#pragma unroll
-    for (int c = 0; c < (DD > 0 ? DD : 64); ++c)
+        D = fmaf(ld(dm + c), ld(mx + c), D);
+    float dq[64];
+    for (int c = 0; c < 64; ++c)
         dq[c] = 0.f;
-    const int beg = a.row_ptr[t], end = a.row_ptr[t + 1];
     const T *K = reinterpret_cast<const T *>(a.k);
     const T *V = reinterpret_cast<const T *>(a.v);
-    for (int p = beg; p < end; ++p) {
+    for (int p = a.row_ptr[t]; p < a.row_ptr[t + 1]; ++p) {
         const int s = a.csr_src[p];
         float pe = 0.f, dz = 0.f;
-        const bool masked =
-            a.kpm_bits && ((a.kpm_bits[(int64_t)s * a.kpm_words + (b >> 6)] >> (b & 63)) & 1u);
-        if (!masked && ml.y > 0.f) {
+        if (ml.y > 0.f && !masked(a, s, b)) {
             const T *kr = K + ((int64_t)b * a.S + s) * a.E + h * d;
             const T *vr = V + ((int64_t)b * a.S + s) * a.E + h * d;
             float z = 0.f, dp = 0.f;
-#pragma unroll
-            for (int c = 0; c < (DD > 0 ? DD : 64); ++c) {
-                if (DD == 0 && c >= d)
-                    break;
+            for (int c = 0; c < d; ++c) {
                 z = fmaf(ld(q + c), ld(kr + c), z);
-                dp = fmaf(dm[c], ld(vr + c), dp);
+                dp = fmaf(ld(dm + c), ld(vr + c), dp);
             }
             pe = __builtin_amdgcn_exp2f(z * a.scale_log2 - ml.x) / ml.y;
             dz = pe * (dp - D);
-#pragma unroll
-            for (int c = 0; c < (DD > 0 ? DD : 64); ++c) {
-                if (DD == 0 && c >= d)
+            for (int c = 0; c < 64; ++c) {
+                if (c >= d)
                     break;
                 dq[c] = fmaf(dz, ld(kr + c), dq[c]);
             }
@@ -90,19 +403,17 @@ bwd_target(const BwdArgs a)
         a.P[o] = pe;
         a.DZ[o] = dz;
     }
-    float *out = a.dq + ((int64_t)b * a.L + t) * a.E + h * d;
-#pragma unroll
-    for (int c = 0; c < (DD > 0 ? DD : 64); ++c) {
-        if (DD == 0 && c >= d)
+    T *out = reinterpret_cast<T *>(a.dq) + row;
+    for (int c = 0; c < 64; ++c) {
+        if (c >= d)
             break;
-        out[c] = dq[c] * a.inv_sqrt_d;
+        st(out + c, dq[c] * a.inv_sqrt_d);
     }
 }
 
-// One thread per (source, sample, channel).
+// One thread per (source, sample, channel), whole edge list.
 template <typename T>
-__global__ void __launch_bounds__(256)
-bwd_source(const BwdArgs a)
+__global__ void __launch_bounds__(256) bwd_source_generic(const BwdArgs a)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t n = (int64_t)a.S * a.B * a.E;
@@ -114,47 +425,412 @@ bwd_source(const BwdArgs a)
     const int s = (int)(bs / a.B);
     const int h = c / (a.E / a.H);
     const T *Q = reinterpret_cast<const T *>(a.q);
+    const T *DM = reinterpret_cast<const T *>(a.dm);
     float dk = 0.f, dv = 0.f;
     for (int j = a.csc_ptr[s]; j < a.csc_ptr[s + 1]; ++j) {
         const int t = a.csc_tgt[j];
         const int64_t o = ((int64_t)a.csc_pos[j] * a.B + b) * a.H + h;
         const int64_t r = ((int64_t)b * a.L + t) * a.E + c;
         dk = fmaf(a.DZ[o], ld(Q + r), dk);
-        dv = fmaf(a.P[o], a.dm[r], dv);
+        dv = fmaf(a.P[o], ld(DM + r), dv);
     }
     const int64_t w = ((int64_t)b * a.S + s) * a.E + c;
-    a.dk[w] = dk * a.inv_sqrt_d;
-    a.dv[w] = dv;
+    st(reinterpret_cast<T *>(a.dk) + w, dk * a.inv_sqrt_d);
+    st(reinterpret_cast<T *>(a.dv) + w, dv);
 }
 
-template <typename T>
-__global__ void to_f32_kernel(const T *x, float *y, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n)
-        y[i] = ld(x + i);
-}
+// ---- dx = sum_j dy_j W_j on the matrix cores ------------------------------
+// Same scheme as the forward projections: the (transposed) weights sit in
+// LDS in MFMA fragment order; each wavefront takes 16-row tiles (stride the
+// grid), keeping the next tile's row fragments in flight, and stores whole
+// 16-byte chunks of whole rows through a per-wavefront LDS staging area.
 
-__global__ void f32_to_bf16_kernel(const float *x, uint16_t *y, int64_t n)
+template <typename T> struct Frag;
+template <> struct Frag<float> {      // v_mfma_f32_16x16x4f32, four per fragment
+    static constexpr int kVec = 4, kStep = 16;
+};
+template <> struct Frag<uint16_t> {   // v_mfma_f32_16x16x32_bf16
+    static constexpr int kVec = 8, kStep = 32;
+};
+
+template <typename T, int E, int NIN, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) bwd_rowmm(const RowMM a)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        // round to nearest even
-        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-        typedef __attribute__((ext_vector_type(2))) float f32x2;
-        const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[i], 0.f}, bf16x2));
-        y[i] = (uint16_t)(w & 0xffffu);
+    constexpr int NKS = E / Frag<T>::kStep;
+    constexpr int NT = E / 16;
+    constexpr int PITCH = E * (int)sizeof(T) + 16;
+    constexpr int CPR = E * (int)sizeof(T) / 16;
+    constexpr int RPI = 64 / CPR;
+    constexpr int KV = Frag<T>::kVec;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *wl = lds;
+    char *stage = lds + NIN * NT * NKS * 1024 + (threadIdx.x >> 6) * (16 * PITCH);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+
+    // fragment (j, nt, ks), lane l: A[m][k] = W_j[k][m] for m = nt*16 + (l & 15),
+    // k = ks * kStep + (l >> 4) * kVec + v
+    for (int cidx = threadIdx.x; cidx < NIN * NT * NKS * 64; cidx += WAVES * 64) {
+        const int f = cidx >> 6, l = cidx & 63;
+        const int ks = f % NKS, nt = (f / NKS) % NT, j = f / (NKS * NT);
+        const T *W = reinterpret_cast<const T *>(a.w[j]);
+        const int m = nt * 16 + (l & 15), k0 = ks * Frag<T>::kStep + (l >> 4) * KV;
+        T v[KV];
+#pragma unroll
+        for (int i = 0; i < KV; ++i)
+            v[i] = W[(int64_t)(k0 + i) * E + m];
+        *reinterpret_cast<uint4 *>(wl + cidx * 16) = *reinterpret_cast<const uint4 *>(v);
+    }
+    __syncthreads();
+
+    const int64_t tile_rows = (int64_t)WAVES * 16;
+    const int64_t ntiles = (a.rows + tile_rows - 1) / tile_rows;
+    uint4 xf[NIN][NKS], xn[NIN][NKS];
+    auto load_x = [&](int64_t tile, uint4 (&dst)[NIN][NKS]) {
+        const int64_t r = tile * tile_rows + wid * 16 + lr;
+        const int64_t rr = r < a.rows ? r : 0;
+#pragma unroll
+        for (int j = 0; j < NIN; ++j) {
+            const T *xr = reinterpret_cast<const T *>(a.x[j]) + rr * E + lg * KV;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                dst[j][ks] = *reinterpret_cast<const uint4 *>(xr + ks * Frag<T>::kStep);
+        }
+    };
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles)
+        load_x(tile, xf);
+    const int cr = lane % CPR, rr = lane / CPR;
+    for (; tile < ntiles; tile += gridDim.x) {
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles)
+            load_x(next, xn);
+        const int64_t row0 = tile * tile_rows + wid * 16;
+#pragma unroll 2
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NIN; ++j) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const uint4 wf = *reinterpret_cast<const uint4 *>(
+                        wl + (((j * NT + nt) * NKS + ks) * 64 + lane) * 16);
+                    if constexpr (sizeof(T) == 2) {
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, wf), __builtin_bit_cast(bf16x8, xf[j][ks]),
+                            acc, 0, 0, 0);
+                    } else {
+                        const float *wv = reinterpret_cast<const float *>(&wf);
+                        const float *xv = reinterpret_cast<const float *>(&xf[j][ks]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[q], xv[q], acc, 0, 0, 0);
+                    }
+                }
+            }
+            // lane holds output channels nt*16 + 4*lg + i of row lr
+            char *d = stage + lr * PITCH + (nt * 16 + 4 * lg) * (int)sizeof(T);
+            if constexpr (sizeof(T) == 2) {
+                uint2 pk;
+                pk.x = pack_bf16(acc[0], acc[1]);
+                pk.y = pack_bf16(acc[2], acc[3]);
+                *reinterpret_cast<uint2 *>(d) = pk;
+            } else {
+                *reinterpret_cast<float4 *>(d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+        // a wavefront reads back only its own staged rows
+        T *dst = reinterpret_cast<T *>(a.y) + cr * (16 / (int)sizeof(T));
+#pragma unroll
+        for (int it = 0; it < 16 / RPI; ++it) {
+            const int lrow = it * RPI + rr;
+            const int64_t r = row0 + lrow;
+            if (r < a.rows) {
+                uint4 v = *reinterpret_cast<const uint4 *>(stage + lrow * PITCH + cr * 16);
+                uint4 *out = reinterpret_cast<uint4 *>(dst + r * E);
+                if constexpr (sizeof(T) == 4) {
+                    if (a.accumulate) {
+                        const float4 o = *reinterpret_cast<const float4 *>(out);
+                        v = make_uint4(__float_as_uint(__uint_as_float(v.x) + o.x),
+                                       __float_as_uint(__uint_as_float(v.y) + o.y),
+                                       __float_as_uint(__uint_as_float(v.z) + o.z),
+                                       __float_as_uint(__uint_as_float(v.w) + o.w));
+                    }
+                }
+                *out = v;
+            }
+        }
+        if (next < ntiles) {
+#pragma unroll
+            for (int j = 0; j < NIN; ++j)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) xf[j][ks] = xn[j][ks];
+        }
     }
 }
 
-// Column sums of a (rows, E) fp32 matrix: one block per column.
-__global__ void __launch_bounds__(256) colsum_kernel(const float *g, int64_t rows, int E, float *out)
+// Any embed_dim: one thread per (row, output channel).
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_rowmm_generic(const RowMM a, int E)
 {
-    const int c = blockIdx.x;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t r = idx / E;
+    const int i = (int)(idx - r * E);
+    if (r >= a.rows)
+        return;
     float acc = 0.f;
-    for (int64_t r = threadIdx.x; r < rows; r += blockDim.x)
-        acc += g[r * E + c];
+    for (int j = 0; j < a.nin; ++j) {
+        const T *x = reinterpret_cast<const T *>(a.x[j]) + r * E;
+        const T *w = reinterpret_cast<const T *>(a.w[j]) + i;
+        for (int o = 0; o < E; ++o)
+            acc = fmaf(ld(x + o), ld(w + (int64_t)o * E), acc);
+    }
+    T *y = reinterpret_cast<T *>(a.y) + r * E + i;
+    if (a.accumulate)
+        acc += ld(y);
+    st(y, acc);
+}
+
+// ---- dW = G^T X and db = column sums of G ---------------------------------
+// Workgroup = (row range, pair, 64 x 64 block of dW). Its four wavefronts
+// take groups of 4 rows in turn; for v_mfma_f32_16x16x4f32 the lane (lr, lc)
+// = (l >> 4, l & 15) supplies G[row lr][n0 + 4 lc + i] as the A value of
+// tile i and X[row lr][k0 + 4 lc + i'] as the B value of tile i', so tile
+// (i, i') accumulates dW[n0 + 4 m + i][k0 + 4 n + i'] at MFMA position
+// (m, n): every load is a plain row-major read. The four wavefronts' sums
+// meet in LDS and each workgroup writes one partial; a second kernel adds
+// the partials in workgroup order.
+constexpr int kWgPart = 64 * 64 + 64;   // floats per partial (dW block, db)
+
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_wgrad(const WGrad a)
+{
+    __shared__ float red[4][64 * 64];
+    __shared__ float bred[4][64];
+    const WGradPair pr = a.p[blockIdx.y];
+    const int zn = a.E / 64, zt = blockIdx.z;
+    const int n0 = (zt / zn) * 64, k0 = (zt % zn) * 64;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lr = lane >> 4, lc = lane & 15;
+    const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
+    const int64_t r_beg = (int64_t)blockIdx.x * per;
+    const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
+    const T *G = reinterpret_cast<const T *>(pr.g) + n0 + 4 * lc;
+    const T *X = reinterpret_cast<const T *>(pr.x) + k0 + 4 * lc;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    auto load4 = [&](const T *p, float (&f)[4]) {
+        if constexpr (sizeof(T) == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(p);
+            f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            f[0] = __uint_as_float(v.x << 16);
+            f[1] = __uint_as_float(v.x & 0xffff0000u);
+            f[2] = __uint_as_float(v.y << 16);
+            f[3] = __uint_as_float(v.y & 0xffff0000u);
+        }
+    };
+    constexpr int UR = 4;   // row groups per wavefront per step
+    for (int64_t r0 = r_beg + wid * 4; r0 < r_end; r0 += 16 * UR) {
+        float g[UR][4], x[UR][4];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t r = r0 + 16 * u + lr;
+            if (r < r_end) {
+                load4(G + r * a.E, g[u]);
+                load4(X + r * a.E, x[u]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) g[u][i] = x[u][i] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bs[i] += g[u][i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(g[u][i], x[u][j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+    // lane holds, for v < 4, MFMA position (m = 4 lr + v, n = lc)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[wid][(4 * (4 * lr + v) + i) * 64 + 4 * lc + j] = acc[i][j][v];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bs[i] += __shfl_xor(bs[i], 16, 64);
+        bs[i] += __shfl_xor(bs[i], 32, 64);
+    }
+    if (lr == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bred[wid][4 * lc + i] = bs[i];
+    }
+    __syncthreads();
+    float *part = a.part + (((int64_t)blockIdx.y * gridDim.z + zt) * a.nwg + blockIdx.x) * kWgPart;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256)
+        part[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+    if (threadIdx.x < 64) {
+        const int e = threadIdx.x;
+        part[64 * 64 + e] = ((bred[0][e] + bred[1][e]) + bred[2][e]) + bred[3][e];
+    }
+}
+
+// bf16: v_mfma_f32_16x16x32_bf16 contracts 8 consecutive rows per lane, so
+// slabs of kWR rows of G and X are first written to LDS transposed (column-
+// major, 4 rows per 8-byte write); wavefront w then owns output rows
+// n0 + 16 w .. + 15 and all 64 columns, so the partial needs no reduction
+// across wavefronts.
+constexpr int kWR = 128;              // rows per slab
+constexpr int kWP = kWR * 2 + 16;     // bytes per transposed column (padded)
+
+__device__ inline uint32_t half16(const uint4 &u, int i)
+{
+    const uint32_t w = i < 2 ? u.x : i < 4 ? u.y : i < 6 ? u.z : u.w;
+    return (i & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+__global__ void __launch_bounds__(256) bwd_wgrad_bf16(const WGrad a)
+{
+    __shared__ __attribute__((aligned(16))) char gt[64 * kWP];
+    __shared__ __attribute__((aligned(16))) char xt[64 * kWP];
+    __shared__ float bl[32][64];
+    const WGradPair pr = a.p[blockIdx.y];
+    const int zn = a.E / 64, zt = blockIdx.z;
+    const int n0 = (zt / zn) * 64, k0 = (zt % zn) * 64;
+    const int tid = threadIdx.x, rq = tid >> 3, cc = tid & 7;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
+    const int64_t r_beg = (int64_t)blockIdx.x * per;
+    const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
+    const uint16_t *G = reinterpret_cast<const uint16_t *>(pr.g) + n0 + 8 * cc;
+    const uint16_t *X = reinterpret_cast<const uint16_t *>(pr.x) + k0 + 8 * cc;
+    f32x4 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float bsum[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        bsum[i] = 0.f;
+    for (int64_t r0 = r_beg; r0 < r_end; r0 += kWR) {
+        uint4 gv[4], xv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t r = r0 + 4 * rq + j;
+            if (r < r_end) {
+                gv[j] = ld16(G + r * a.E);
+                xv[j] = ld16(X + r * a.E);
+            } else {
+                gv[j] = xv[j] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                bsum[i] += __uint_as_float(half16(gv[j], i) << 16);
+        __syncthreads();   // the previous slab's fragments are read
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int off = (8 * cc + i) * kWP + 8 * rq;
+            *reinterpret_cast<uint2 *>(gt + off) =
+                make_uint2(half16(gv[0], i) | (half16(gv[1], i) << 16),
+                           half16(gv[2], i) | (half16(gv[3], i) << 16));
+            *reinterpret_cast<uint2 *>(xt + off) =
+                make_uint2(half16(xv[0], i) | (half16(xv[1], i) << 16),
+                           half16(xv[2], i) | (half16(xv[3], i) << 16));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kWR / 32; ++ks) {
+            const int off = ks * 64 + 16 * (lane >> 4);
+            const uint4 af = *reinterpret_cast<const uint4 *>(gt + (16 * wid + (lane & 15)) * kWP + off);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint4 bf = *reinterpret_cast<const uint4 *>(xt + (16 * nt + (lane & 15)) * kWP + off);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
+            }
+        }
+    }
+    float *part = a.part + (((int64_t)blockIdx.y * gridDim.z + zt) * a.nwg + blockIdx.x) * kWgPart;
+    // lane holds position (m = 4 (lane >> 4) + v, n = lane & 15) of tile (wid, nt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            part[(16 * wid + 4 * (lane >> 4) + v) * 64 + 16 * nt + (lane & 15)] = acc[nt][v];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        bl[rq][8 * cc + i] = bsum[i];
+    __syncthreads();
+    if (tid < 64) {
+        float b = 0.f;
+        for (int q = 0; q < 32; ++q)
+            b += bl[q][tid];
+        part[64 * 64 + tid] = b;
+    }
+}
+
+// Thread (e, q): partial element e summed over the workgroups w = q mod 4,
+// then the four sums in order of q.
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_wgrad_reduce(const WGrad a)
+{
+    __shared__ float red[4][64];
+    const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + el;
+    const WGradPair pr = a.p[blockIdx.z];
+    const int zn = a.E / 64, zt = blockIdx.y;
+    const int n0 = (zt / zn) * 64, k0 = (zt % zn) * 64;
+    float acc = 0.f;
+    if (e < kWgPart) {
+        const float *part = a.part + ((int64_t)blockIdx.z * gridDim.y + zt) * a.nwg * kWgPart + e;
+#pragma unroll 8
+        for (int w = q; w < a.nwg; w += 4)
+            acc += part[(int64_t)w * kWgPart];
+    }
+    red[q][el] = acc;
+    __syncthreads();
+    if (q != 0 || e >= kWgPart)
+        return;
+    acc = ((red[0][el] + red[1][el]) + red[2][el]) + red[3][el];
+    if (e < 64 * 64)
+        st(reinterpret_cast<T *>(pr.dw) + (int64_t)(n0 + e / 64) * a.E + k0 + e % 64, acc);
+    else if (k0 == 0 && pr.db)
+        st(reinterpret_cast<T *>(pr.db) + n0 + (e - 64 * 64), acc);
+}
+
+// Any embed_dim: one workgroup per (output element, pair); element E*E + n
+// is bias entry n.
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_wgrad_generic(const WGrad a)
+{
     __shared__ float red[256];
+    const WGradPair pr = a.p[blockIdx.y];
+    const int e = blockIdx.x, E = a.E;
+    const bool bias = e >= E * E;
+    if (bias && !pr.db)
+        return;
+    const int n = bias ? e - E * E : e / E, k = bias ? 0 : e % E;
+    const T *G = reinterpret_cast<const T *>(pr.g);
+    const T *X = reinterpret_cast<const T *>(pr.x);
+    float acc = 0.f;
+    for (int64_t r = threadIdx.x; r < pr.rows; r += 256)
+        acc = bias ? acc + ld(G + r * E + n) : fmaf(ld(G + r * E + n), ld(X + r * E + k), acc);
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -163,66 +839,244 @@ __global__ void __launch_bounds__(256) colsum_kernel(const float *g, int64_t row
         __syncthreads();
     }
     if (threadIdx.x == 0)
-        out[c] = red[0];
+        st(reinterpret_cast<T *>(bias ? pr.db : pr.dw) + (bias ? n : (int64_t)n * E + k), red[0]);
 }
 
 inline unsigned grid(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int cu_count()
+{
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kRowWaves = 8;
+
+template <typename T, int E, int NIN>
+constexpr size_t rowmm_lds()
+{
+    return (size_t)NIN * (E / 16) * (E / Frag<T>::kStep) * 1024 +
+           (size_t)kRowWaves * 16 * (E * sizeof(T) + 16);
+}
+
+template <typename T, int E, int NIN>
+hipError_t run_rowmm(const RowMM &a, hipStream_t s)
+{
+    constexpr size_t lds = rowmm_lds<T, E, NIN>();
+    static_assert(lds <= (size_t)kLdsBytes, "rowmm tile does not fit in LDS");
+    const int64_t tile_rows = (int64_t)kRowWaves * 16;
+    const int64_t ntiles = (a.rows + tile_rows - 1) / tile_rows;
+    int per_cu = (int)(kLdsBytes / lds);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+    int64_t g = (int64_t)cu_count() * per_cu;
+    if (g > ntiles)
+        g = ntiles;
+    if (lds > 64 * 1024) {
+        static bool raised = false;
+        if (!raised) {
+            hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&bwd_rowmm<T, E, NIN, kRowWaves>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+            if (e != hipSuccess)
+                return e;
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL((bwd_rowmm<T, E, NIN, kRowWaves>), dim3((unsigned)g), dim3(kRowWaves * 64),
+                       lds, s, a);
+    return hipGetLastError();
+}
+
+// NIN inputs in one launch where the weights fit in LDS, else one launch
+// per input accumulating into y (fp32 only).
+template <typename T, int E>
+hipError_t rowmm_e(const RowMM &a, hipStream_t s)
+{
+    constexpr bool fit2 = rowmm_lds<T, E, 2>() <= (size_t)kLdsBytes;
+    constexpr bool fit3 = rowmm_lds<T, E, 3>() <= (size_t)kLdsBytes;
+    if (a.nin == 1)
+        return run_rowmm<T, E, 1>(a, s);
+    if constexpr (fit3) {
+        if (a.nin == 3)
+            return run_rowmm<T, E, 3>(a, s);
+    }
+    if constexpr (fit2) {
+        if (a.nin == 2)
+            return run_rowmm<T, E, 2>(a, s);
+    }
+    for (int j = 0; j < a.nin; ++j) {
+        RowMM one = a;
+        one.nin = 1;
+        one.x[0] = a.x[j];
+        one.w[0] = a.w[j];
+        one.accumulate = j > 0 ? 1 : a.accumulate;
+        hipError_t e = run_rowmm<T, E, 1>(one, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
 
 }  // namespace
 
 pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
 {
-    if (a.E / a.H > 64)
+    const int d = a.E / a.H;
+    if (d > 64)
         return PMA_E_UNSUPPORTED;
-    const int64_t nt = (int64_t)a.L * a.B * a.H, ns = (int64_t)a.S * a.B * a.E;
-    const int d = (int)(a.E / a.H);
-    auto target = [&](auto tag) {
+    const int es = dt == PMA_BF16 ? 2 : 4;
+    const int lph = d * es / 16;
+    const bool fast = (a.E * es) % 16 == 0 && (d * es) % 16 == 0 &&
+                      (lph == 1 || lph == 2 || lph == 4 || lph == 8 || lph == 16) &&
+                      aligned16(a.q) && aligned16(a.k) && aligned16(a.v) && aligned16(a.mixed) &&
+                      aligned16(a.dm) && aligned16(a.dq) && aligned16(a.dk) && aligned16(a.dv);
+    auto go = [&](auto tag) {
         using T = decltype(tag);
-        switch (d) {
-        case 4: bwd_target<T, 4><<<grid(nt), 256, 0, s>>>(a); break;
-        case 8: bwd_target<T, 8><<<grid(nt), 256, 0, s>>>(a); break;
-        case 16: bwd_target<T, 16><<<grid(nt), 256, 0, s>>>(a); break;
-        case 32: bwd_target<T, 32><<<grid(nt), 256, 0, s>>>(a); break;
-        default: bwd_target<T, 0><<<grid(nt), 256, 0, s>>>(a); break;
+        if (!fast) {
+            bwd_target_generic<T><<<grid((int64_t)a.L * a.B * a.H), 256, 0, s>>>(a);
+            bwd_source_generic<T><<<grid((int64_t)a.S * a.B * a.E), 256, 0, s>>>(a);
+            return;
         }
-        bwd_source<T><<<grid(ns), 256, 0, s>>>(a);
+        const int cpr = a.E / Vec<T>::N;
+        const int64_t nt = a.n_ttasks * a.B * cpr, ns = a.n_stasks * a.B * cpr;
+        // a piece's lanes fill whole wavefronts: wavefront-uniform indices
+        const bool uni = ((int64_t)a.B * cpr) % 64 == 0;
+#define PMA_BWD_EDGE(L_)                                                            \
+    case L_:                                                                       \
+        if (uni) {                                                                 \
+            bwd_target_fast<T, L_, true><<<grid(nt), 256, 0, s>>>(a);              \
+            bwd_source_fast<T, L_, true><<<grid(ns), 256, 0, s>>>(a);              \
+        } else {                                                                   \
+            bwd_target_fast<T, L_, false><<<grid(nt), 256, 0, s>>>(a);             \
+            bwd_source_fast<T, L_, false><<<grid(ns), 256, 0, s>>>(a);             \
+        }                                                                          \
+        break;
+        switch (lph) {
+            PMA_BWD_EDGE(1)
+            PMA_BWD_EDGE(2)
+            PMA_BWD_EDGE(4)
+            PMA_BWD_EDGE(8)
+            PMA_BWD_EDGE(16)
+        }
+#undef PMA_BWD_EDGE
+        if (a.n_tsplit > 0)
+            bwd_merge_fast<T><<<grid(a.n_tsplit * a.B * cpr), 256, 0, s>>>(a, 0);
+        if (a.n_ssplit > 0)
+            bwd_merge_fast<T><<<grid(a.n_ssplit * a.B * cpr), 256, 0, s>>>(a, 1);
     };
+    // The fast target pass and the merge share one ordering: the merge runs
+    // after both edge passes, and reads only slots the target / source pass wrote.
     if (dt == PMA_BF16)
-        target(uint16_t{});
+        go(uint16_t{});
     else
-        target(float{});
+        go(float{});
     return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
-pma_status to_f32(const void *x, pma_dtype dt, float *y, int64_t n, hipStream_t s)
+size_t bwd_piece_scratch(const GraphDev &g, int64_t B, int64_t E)
 {
-    if (n <= 0)
+    return ((size_t)g.n_slots * B * E + (size_t)g.n_sslots * B * 2 * E) * sizeof(float);
+}
+
+pma_status launch_rowmm(const RowMM &a, int64_t E, pma_dtype dt, hipStream_t s)
+{
+    if (a.rows <= 0)
         return PMA_OK;
-    if (dt == PMA_BF16)
-        to_f32_kernel<uint16_t><<<grid(n), 256, 0, s>>>(reinterpret_cast<const uint16_t *>(x), y, n);
-    else
-        return hipMemcpyAsync(y, x, n * sizeof(float), hipMemcpyDeviceToDevice, s) == hipSuccess
-                   ? PMA_OK
-                   : PMA_E_DEVICE;
-    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+    if (a.nin < 1 || a.nin > 3 || (a.accumulate && dt != PMA_F32))
+        return PMA_E_ARG;
+    bool al = aligned16(a.y);
+    for (int j = 0; j < a.nin; ++j)
+        al = al && aligned16(a.x[j]);
+    hipError_t e;
+    if (al && dt == PMA_BF16 && E == 64)
+        e = rowmm_e<uint16_t, 64>(a, s);
+    else if (al && dt == PMA_BF16 && E == 128)
+        e = rowmm_e<uint16_t, 128>(a, s);
+    else if (al && dt == PMA_F32 && E == 64)
+        e = rowmm_e<float, 64>(a, s);
+    else if (al && dt == PMA_F32 && E == 128)
+        e = rowmm_e<float, 128>(a, s);
+    else if (dt == PMA_BF16) {
+        bwd_rowmm_generic<uint16_t><<<grid(a.rows * E), 256, 0, s>>>(a, (int)E);
+        e = hipGetLastError();
+    } else {
+        bwd_rowmm_generic<float><<<grid(a.rows * E), 256, 0, s>>>(a, (int)E);
+        e = hipGetLastError();
+    }
+    return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
-pma_status from_f32(const float *x, pma_dtype dt, void *y, int64_t n, hipStream_t s)
+namespace {
+bool wgrad_fast(const WGrad &a, pma_dtype dt)
 {
-    if (n <= 0)
+    if (a.E % 64 != 0)
+        return false;
+    const uintptr_t mask = 15;
+    for (int i = 0; i < a.np; ++i)
+        if (((uintptr_t)a.p[i].g | (uintptr_t)a.p[i].x) & mask)
+            return false;
+    return true;
+}
+}  // namespace
+
+int wgrad_groups(int64_t E, int np, int64_t max_rows)
+{
+    const int64_t nz = (E / 64) * (E / 64);
+    int64_t cap = 2048 / (np * (nz > 0 ? nz : 1));
+    if (cap < 1)
+        cap = 1;
+    int64_t n = (max_rows + 255) / 256;
+    if (n < 1)
+        n = 1;
+    return (int)(n < cap ? n : cap);
+}
+
+size_t wgrad_scratch(int64_t E, int np, int64_t max_rows)
+{
+    if (E % 64 != 0)
+        return 0;
+    const int64_t nz = (E / 64) * (E / 64);
+    return (size_t)np * nz * wgrad_groups(E, np, max_rows) * kWgPart * sizeof(float);
+}
+
+pma_status launch_wgrad(WGrad a, pma_dtype dt, hipStream_t s)
+{
+    if (a.np <= 0)
         return PMA_OK;
-    if (dt == PMA_BF16)
-        f32_to_bf16_kernel<<<grid(n), 256, 0, s>>>(x, reinterpret_cast<uint16_t *>(y), n);
-    else
-        return hipMemcpyAsync(y, x, n * sizeof(float), hipMemcpyDeviceToDevice, s) == hipSuccess
-                   ? PMA_OK
-                   : PMA_E_DEVICE;
-    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
-}
-
-pma_status colsum(const float *g, int64_t rows, int E, float *out, hipStream_t s)
-{
-    colsum_kernel<<<E, 256, 0, s>>>(g, rows, E, out);
+    int64_t max_rows = 0;
+    for (int i = 0; i < a.np; ++i)
+        max_rows = a.p[i].rows > max_rows ? a.p[i].rows : max_rows;
+    const bool bf = dt == PMA_BF16;
+    if (wgrad_fast(a, dt)) {
+        a.nwg = wgrad_groups(a.E, a.np, max_rows);
+        const int zn = a.E / 64;
+        const dim3 g1((unsigned)a.nwg, (unsigned)a.np, (unsigned)(zn * zn));
+        const dim3 g2((unsigned)((kWgPart + 63) / 64), (unsigned)(zn * zn), (unsigned)a.np);
+        if (bf) {
+            bwd_wgrad_bf16<<<g1, 256, 0, s>>>(a);
+            bwd_wgrad_reduce<uint16_t><<<g2, 256, 0, s>>>(a);
+        } else {
+            bwd_wgrad<float><<<g1, 256, 0, s>>>(a);
+            bwd_wgrad_reduce<float><<<g2, 256, 0, s>>>(a);
+        }
+    } else {
+        const dim3 g((unsigned)(a.E * a.E + a.E), (unsigned)a.np);
+        if (bf)
+            bwd_wgrad_generic<uint16_t><<<g, 256, 0, s>>>(a);
+        else
+            bwd_wgrad_generic<float><<<g, 256, 0, s>>>(a);
+    }
     return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 

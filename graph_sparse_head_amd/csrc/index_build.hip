@@ -356,7 +356,8 @@ void free_graph(GraphDev *g)
                         &g->task_target, &g->task_begin,  &g->task_end,   &g->task_slot,
                         &g->task_split,  &g->split_target, &g->split_slot0, &g->split_count,
                         &g->csr_kv,      &g->kv_rows,     &g->csc_ptr,    &g->csc_tgt,
-                        &g->csc_pos};
+                        &g->csc_pos,     &g->s_source,    &g->s_begin,    &g->s_end,
+                        &g->s_slot,      &g->ss_source,   &g->ss_slot0,   &g->ss_count};
     for (int32_t **p : ptrs) {
         if (*p)
             (void)hipFree(*p);
@@ -522,8 +523,8 @@ __global__ void csc_fill(const int32_t *perm, const int32_t *csr_tgt, int64_t nn
         csc_tgt[j] = csr_tgt[perm[j]];
 }
 
-pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, hipStream_t stream, char *err,
-                     size_t errlen)
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t stream,
+                     char *err, size_t errlen)
 {
     pma_status st = PMA_OK;
     const size_t i4 = sizeof(int32_t);
@@ -532,33 +533,81 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, hipStream_t stream, ch
     const int64_t count_len = 256 * ntiles;
     const int64_t scan_len = (count_len > n_sort ? count_len : n_sort) / kTile + 2;
     int32_t *perm = nullptr, *perm_tmp = nullptr, *counts = nullptr, *scan_tmp = nullptr,
-            *deg = nullptr;
-    PMA_TRY(hipMalloc(&perm, nnz * i4));
-    PMA_TRY(hipMalloc(&perm_tmp, nnz * i4));
+            *deg = nullptr, *small = nullptr, *n_piece = nullptr, *n_slot = nullptr,
+            *is_split = nullptr, *piece_base = nullptr, *slot_base = nullptr,
+            *split_base = nullptr, *t_split = nullptr, *t_key = nullptr;
+    int32_t h_small[8] = {0};
+    PMA_TRY(hipMalloc(&perm, (nnz + kSrcPad) * i4));
+    PMA_TRY(hipMalloc(&perm_tmp, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMalloc(&counts, count_len * i4));
     PMA_TRY(hipMalloc(&scan_tmp, scan_len * i4));
     PMA_TRY(hipMalloc(&deg, S * i4));
+    PMA_TRY(hipMalloc(&small, 8 * i4));
+    PMA_TRY(hipMalloc(&n_piece, S * i4));
+    PMA_TRY(hipMalloc(&n_slot, S * i4));
+    PMA_TRY(hipMalloc(&is_split, S * i4));
+    PMA_TRY(hipMalloc(&piece_base, S * i4));
+    PMA_TRY(hipMalloc(&slot_base, S * i4));
+    PMA_TRY(hipMalloc(&split_base, S * i4));
     PMA_TRY(hipMalloc(&g->csc_ptr, (S + 1) * i4));
-    PMA_TRY(hipMalloc(&g->csc_tgt, nnz * i4));
+    PMA_TRY(hipMalloc(&g->csc_tgt, (nnz + kSrcPad) * i4));
+    PMA_TRY(hipMemsetAsync(g->csc_tgt + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMemsetAsync(deg, 0, S * i4, stream));
+    PMA_TRY(hipMemsetAsync(small, 0, 8 * i4, stream));
     iota_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, nnz);
     PMA_TRY(radix_sort_perm(g->csr_src, bits_for(S - 1), perm, perm_tmp, nnz, counts, scan_tmp,
                             stream));
+    PMA_TRY(hipMemsetAsync(perm + nnz, 0, kSrcPad * i4, stream));
     csc_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, g->csr_tgt, nnz, g->csc_tgt);
     degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, nnz, deg);
     PMA_TRY(scan_exclusive(deg, g->csc_ptr, S, g->csc_ptr + S, scan_tmp, stream));
-    PMA_TRY(hipGetLastError());
-    PMA_TRY(hipStreamSynchronize(stream));
     g->csc_pos = perm;   // kept
     perm = nullptr;
+    // pieces per source, as for targets
+    split_count_kernel<<<grid_for(S, 256), 256, 0, stream>>>(deg, S, chunk, n_piece, n_slot,
+                                                             is_split, small + 4);
+    PMA_TRY(scan_exclusive(n_piece, piece_base, S, small + 1, scan_tmp, stream));
+    PMA_TRY(scan_exclusive(n_slot, slot_base, S, small + 2, scan_tmp, stream));
+    PMA_TRY(scan_exclusive(is_split, split_base, S, small + 3, scan_tmp, stream));
+    PMA_TRY(hipGetLastError());
+    PMA_TRY(hipMemcpyAsync(h_small, small, 8 * i4, hipMemcpyDeviceToHost, stream));
+    PMA_TRY(hipStreamSynchronize(stream));
+    g->n_stasks = h_small[1];
+    g->n_sslots = h_small[2];
+    g->n_ssplit = h_small[3];
+    {
+        const int64_t nt = g->n_stasks, ns = g->n_ssplit > 0 ? g->n_ssplit : 1;
+        PMA_TRY(hipMalloc(&g->s_source, nt * i4));
+        PMA_TRY(hipMalloc(&g->s_begin, nt * i4));
+        PMA_TRY(hipMalloc(&g->s_end, nt * i4));
+        PMA_TRY(hipMalloc(&g->s_slot, nt * i4));
+        PMA_TRY(hipMalloc(&t_split, nt * i4));
+        PMA_TRY(hipMalloc(&t_key, nt * i4));
+        PMA_TRY(hipMalloc(&g->ss_source, ns * i4));
+        PMA_TRY(hipMalloc(&g->ss_slot0, ns * i4));
+        PMA_TRY(hipMalloc(&g->ss_count, ns * i4));
+        split_fill_kernel<<<grid_for(S, 256), 256, 0, stream>>>(
+            g->csc_ptr, S, chunk, piece_base, slot_base, split_base, g->s_source, g->s_begin,
+            g->s_end, g->s_slot, t_split, t_key, g->ss_source, g->ss_slot0, g->ss_count);
+        PMA_TRY(hipGetLastError());
+        PMA_TRY(hipStreamSynchronize(stream));
+    }
     goto done;
 fail:
     (void)hipStreamSynchronize(stream);
-    if (g->csc_ptr) (void)hipFree(g->csc_ptr);
-    if (g->csc_tgt) (void)hipFree(g->csc_tgt);
-    g->csc_ptr = g->csc_tgt = nullptr;
+    {
+        int32_t **own[] = {&g->csc_ptr,  &g->csc_tgt, &g->csc_pos,  &g->s_source, &g->s_begin,
+                           &g->s_end,    &g->s_slot,  &g->ss_source, &g->ss_slot0, &g->ss_count};
+        for (int32_t **q : own) {
+            if (*q)
+                (void)hipFree(*q);
+            *q = nullptr;
+        }
+        g->n_stasks = g->n_ssplit = g->n_sslots = 0;
+    }
 done:
-    for (int32_t *q : {perm, perm_tmp, counts, scan_tmp, deg})
+    for (int32_t *q : {perm, perm_tmp, counts, scan_tmp, deg, small, n_piece, n_slot, is_split,
+                       piece_base, slot_base, split_base, t_split, t_key})
         if (q)
             (void)hipFree(q);
     return st;

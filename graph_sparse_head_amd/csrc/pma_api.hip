@@ -10,7 +10,6 @@
 #include <new>
 #include <vector>
 
-#include <rocblas/rocblas.h>
 
 #include "pma_internal.h"
 
@@ -43,6 +42,7 @@ struct pma_plan {
     int64_t L = 0, S = 0, E = 0, H = 0, nnz = 0;
     pma_dtype dtype = PMA_F32;
     int chunk = kChunk;
+    int bchunk = kChunk;        // most edges one source piece of the backward covers
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
@@ -57,10 +57,9 @@ struct pma_plan {
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
     uint64_t *kpm_bits = nullptr;   // key_padding_mask packed by source
-    // backward: fp32 scratch (grown) and a rocBLAS handle for its plain GEMMs
-    float *bw = nullptr;
+    // backward scratch, grown on demand
+    char *bw = nullptr;
     size_t bw_bytes = 0;
-    rocblas_handle blas = nullptr;
     // profiling
     unsigned prof = 0;   // stages timed: bit s for stage s
     std::vector<EventPair> pending;
@@ -247,10 +246,16 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     //                  wavefront walking several pieces (0: one per piece)
     //   PMA_COMPACT    1 / 0: force or forbid projecting keys and values only
     //                  for the sources some edge reads
+    //   PMA_BWD_CHUNK  n: most edges of one source piece in the backward pass
     if (const char *ev = getenv("PMA_CHUNK")) {
         const long c = strtol(ev, nullptr, 10);
         if (c >= 1 && c <= 65535)
             p->chunk = (int)c;
+    }
+    if (const char *ev = getenv("PMA_BWD_CHUNK")) {
+        const long c = strtol(ev, nullptr, 10);
+        if (c >= 1 && c <= 65535)
+            p->bchunk = (int)c;
     }
     if (const char *ev = getenv("PMA_FUSE_OUT"))
         p->fuse_out = ev[0] != '0';
@@ -303,8 +308,6 @@ PMA_API pma_status pma_destroy(pma_plan *plan)
     free_workspace(plan);
     if (plan->bw)
         (void)hipFree(plan->bw);
-    if (plan->blas)
-        (void)rocblas_destroy_handle(plan->blas);
     for (auto &ev : plan->pending) {
         (void)hipEventDestroy(ev.a);
         (void)hipEventDestroy(ev.b);
@@ -635,26 +638,6 @@ PMA_API pma_status pma_forward_train(pma_plan *plan, int64_t batch, const void *
                         key_padding_mask ? mask_per_sample : 0, static_cast<char *>(save), stream);
 }
 
-namespace {
-
-// C (m x n) = op(A) op(B) + beta C on row-major fp32 matrices, through the
-// column-major GEMM (a row-major matrix is its transpose column-major).
-//   ta = 0: A is (m x k) row-major; ta = 1: A is (k x m) row-major, used transposed.
-//   tb likewise for B (k x n) / (n x k).
-rocblas_status gemm_rm(rocblas_handle h, int ta, int tb, int64_t m, int64_t n, int64_t k,
-                       const float *A, const float *B, float beta, float *C)
-{
-    const float one = 1.f;
-    // C^T (n x m, column-major) = op(B)^T op(A)^T
-    return rocblas_sgemm(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
-                         ta ? rocblas_operation_transpose : rocblas_operation_none,
-                         (rocblas_int)n, (rocblas_int)m, (rocblas_int)k, &one, B,
-                         (rocblas_int)(tb ? k : n), A, (rocblas_int)(ta ? m : k), &beta, C,
-                         (rocblas_int)n);
-}
-
-}  // namespace
-
 PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query,
                                 const void *key, const void *value, const void *q_w,
                                 const void *k_w, const void *v_w, const void *o_w, int has_bias,
@@ -691,23 +674,22 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         return fail(PMA_E_UNSUPPORTED, "batch too large");
     char err[256] = "";
     if (!p->g.csc_ptr) {
-        pma_status st = pma::build_csc(&p->g, nnz, S, stream, err, sizeof err);
+        pma_status st = pma::build_csc(&p->g, nnz, S, p->bchunk, stream, err, sizeof err);
         if (st != PMA_OK)
             return fail(st, "%s", err);
     }
-    if (!p->blas && rocblas_create_handle(&p->blas) != rocblas_status_success) {
-        p->blas = nullptr;
-        return fail(PMA_E_DEVICE, "rocblas_create_handle failed");
-    }
-    if (rocblas_set_stream(p->blas, stream) != rocblas_status_success)
-        return fail(PMA_E_DEVICE, "rocblas_set_stream failed");
 
-    // fp32 scratch: dO, dm, dq, dk, dv, P, DZ, tokens, mixed, weights, token
-    // gradients, weight and bias gradients
-    const size_t RL = (size_t)B * L * E, RS = (size_t)B * S * E, EE = (size_t)E * E;
-    const size_t PZ = (size_t)nnz * B * H;
-    const size_t need = (3 * RL + 2 * RS + 2 * PZ + (RL + 2 * RS) + RL + 4 * EE + (RL + 2 * RS) +
-                         4 * EE + 4 * E) * sizeof(float) + 64 * 256;
+    // scratch: dm, dq, dk, dv (plan dtype), per-edge P and DZ, piece
+    // partials and weight-gradient partials (fp32)
+    const pma_dtype dt = p->dtype;
+    const size_t es = dt == PMA_BF16 ? 2 : 4;
+    const int64_t RLr = B * L, RSr = B * S;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t b_dm = up(RLr * E * es), b_dkv = up(RSr * E * es);
+    const size_t b_pz = up((size_t)nnz * B * H * sizeof(float));
+    const size_t b_piece = up(pma::bwd_piece_scratch(p->g, B, E));
+    const size_t b_wg = up(pma::wgrad_scratch(E, 4, RLr > RSr ? RLr : RSr));
+    const size_t need = 2 * b_dm + 2 * b_dkv + 2 * b_pz + b_piece + b_wg;
     if (need > p->bw_bytes) {
         hipError_t e = hipStreamSynchronize(stream);
         if (p->bw)
@@ -721,22 +703,18 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
                         "backward scratch of %zu bytes: %s", need, hipGetErrorString(e));
         p->bw_bytes = need;
     }
-    float *cur = p->bw;
+    char *cur = p->bw;
     auto take = [&](size_t n) {
-        float *r = cur;
-        cur += (n + 63) & ~(size_t)63;
+        char *r = cur;
+        cur += n;
         return r;
     };
-    float *dO = take(RL), *dm = take(RL), *dq = take(RL), *dk = take(RS), *dv = take(RS);
-    float *P = take(PZ), *DZ = take(PZ);
-    float *xq = take(RL), *xk = take(RS), *xv = take(RS), *mix = take(RL);
-    float *W[4] = {take(EE), take(EE), take(EE), take(EE)};
-    float *gxq = take(RL), *gxk = take(RS), *gxv = take(RS);
-    float *gW[4] = {take(EE), take(EE), take(EE), take(EE)};
-    float *gb = take(4 * E);
+    void *dm = take(b_dm), *dq = take(b_dm), *dk = take(b_dkv), *dv = take(b_dkv);
+    float *P = reinterpret_cast<float *>(take(b_pz));
+    float *DZ = reinterpret_cast<float *>(take(b_pz));
+    float *part = reinterpret_cast<float *>(take(b_piece));
+    float *wpart = reinterpret_cast<float *>(take(b_wg));
 
-    const pma_dtype dt = p->dtype;
-    const size_t es = dt == PMA_BF16 ? 2 : 4;
     const SaveLayout sv = save_layout(p, B);
     const char *sb = static_cast<const char *>(save);
     pma_status st = PMA_OK;
@@ -744,30 +722,12 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         if (st == PMA_OK)
             st = x;
     };
-    ok(pma::to_f32(grad_out, dt, dO, RL, stream));
-    ok(pma::to_f32(sb + sv.mixed, dt, mix, RL, stream));
-    ok(pma::to_f32(query, dt, xq, RL, stream));
-    if (key != query)
-        ok(pma::to_f32(key, dt, xk, RS, stream));
-    if (value != key && value != query)
-        ok(pma::to_f32(value, dt, xv, RS, stream));
-    const float *Xk = key == query ? xq : xk;
-    const float *Xv = value == key ? Xk : (value == query ? xq : xv);
-    const void *ws[4] = {q_w, k_w, v_w, o_w};
-    for (int i = 0; i < 4; ++i)
-        ok(pma::to_f32(ws[i], dt, W[i], EE, stream));
-    if (st != PMA_OK)
-        return fail(st, "conversion failed: %s", hipGetErrorString(hipGetLastError()));
 
-    rocblas_handle h = p->blas;
-    bool blas_ok = true;
-    auto g = [&](rocblas_status r) { blas_ok = blas_ok && r == rocblas_status_success; };
-    const int64_t RLr = B * L, RSr = B * S;
-    // out_proj: dm = dO Wo; dWo = dO^T mixed; dbo = column sums of dO
-    g(gemm_rm(h, 0, 0, RLr, E, E, dO, W[3], 0.f, dm));
-    g(gemm_rm(h, 1, 0, E, E, RLr, dO, mix, 0.f, gW[3]));
-    if (has_bias)
-        ok(pma::colsum(dO, RLr, (int)E, gb + 3 * E, stream));
+    // out_proj: dm = dO Wo
+    {
+        pma::RowMM r{{grad_out}, {o_w}, 1, dm, RLr, 0};
+        ok(pma::launch_rowmm(r, E, dt, stream));
+    }
 
     // scores, softmax and mix
     pma::BwdArgs a;
@@ -784,11 +744,30 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     a.mixed = sb + sv.mixed;
     a.ml = reinterpret_cast<const float *>(sb + sv.ml);
     a.dm = dm;
-    a.row_ptr = p->g.row_ptr;
-    a.csr_src = p->g.csr_src;
-    a.csc_ptr = p->g.csc_ptr;
-    a.csc_tgt = p->g.csc_tgt;
-    a.csc_pos = p->g.csc_pos;
+    const pma::GraphDev &gd = p->g;
+    a.row_ptr = gd.row_ptr;
+    a.csr_src = gd.csr_src;
+    a.csc_ptr = gd.csc_ptr;
+    a.csc_tgt = gd.csc_tgt;
+    a.csc_pos = gd.csc_pos;
+    a.t_target = gd.task_target;
+    a.t_begin = gd.task_begin;
+    a.t_end = gd.task_end;
+    a.t_slot = gd.task_slot;
+    a.ts_target = gd.split_target;
+    a.ts_slot0 = gd.split_slot0;
+    a.ts_count = gd.split_count;
+    a.s_source = gd.s_source;
+    a.s_begin = gd.s_begin;
+    a.s_end = gd.s_end;
+    a.s_slot = gd.s_slot;
+    a.ss_source = gd.ss_source;
+    a.ss_slot0 = gd.ss_slot0;
+    a.ss_count = gd.ss_count;
+    a.n_ttasks = gd.n_tasks;
+    a.n_tsplit = gd.n_split;
+    a.n_stasks = gd.n_stasks;
+    a.n_ssplit = gd.n_ssplit;
     a.kpm_bits = nullptr;
     a.kpm_words = 0;
     if (key_padding_mask) {
@@ -801,46 +780,48 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     }
     a.P = P;
     a.DZ = DZ;
+    a.part_q = part;
+    a.part_kv = part + (size_t)gd.n_slots * B * E;
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
     ok(pma::launch_bwd_edges(a, dt, stream));
 
-    // q, k, v projections: dW = G^T X, db = column sums of G, dX = G W;
-    // gradients of one shared token tensor accumulate
-    const float *G[3] = {dq, dk, dv};
-    const float *X[3] = {xq, Xk, Xv};
-    const int64_t rows[3] = {RLr, RSr, RSr};
+    // weight and bias gradients of the four maps
+    {
+        pma::WGrad w;
+        w.np = 4;
+        w.E = (int)E;
+        w.nwg = 0;
+        w.part = wpart;
+        w.p[0] = {grad_out, sb + sv.mixed, RLr, grad_o_w, has_bias ? grad_o_b : nullptr};
+        w.p[1] = {dq, query, RLr, grad_q_w, has_bias ? grad_q_b : nullptr};
+        w.p[2] = {dk, key, RSr, grad_k_w, has_bias ? grad_k_b : nullptr};
+        w.p[3] = {dv, value, RSr, grad_v_w, has_bias ? grad_v_b : nullptr};
+        ok(pma::launch_wgrad(w, dt, stream));
+    }
+
+    // token gradients dX = dY W, summed over the maps that read one tensor
+    const void *G[3] = {dq, dk, dv};
+    const void *Wm[3] = {q_w, k_w, v_w};
     void *outs[3] = {grad_query, grad_key, grad_value};
-    float *tmp[3] = {gxq, gxk, gxv};
-    float *dst[3];
-    for (int i = 0; i < 3; ++i) {
-        g(gemm_rm(h, 1, 0, E, E, rows[i], G[i], X[i], 0.f, gW[i]));
-        if (has_bias)
-            ok(pma::colsum(G[i], rows[i], (int)E, gb + i * E, stream));
-        int j = 0;
-        while (j < i && outs[j] != outs[i])
-            ++j;
-        dst[i] = j < i ? dst[j] : tmp[i];
-        g(gemm_rm(h, 0, 0, rows[i], E, E, G[i], W[i], j < i ? 1.f : 0.f, dst[i]));
-    }
-    if (!blas_ok)
-        return fail(PMA_E_DEVICE, "rocBLAS GEMM failed");
+    const int64_t rows[3] = {RLr, RSr, RSr};
     for (int i = 0; i < 3; ++i) {
         int j = 0;
         while (j < i && outs[j] != outs[i])
             ++j;
-        if (j == i)
-            ok(pma::from_f32(dst[i], dt, outs[i], rows[i] * E, stream));
+        if (j < i)
+            continue;   // handled with its first use
+        pma::RowMM r{{}, {}, 0, outs[i], rows[i], 0};
+        for (int k = i; k < 3; ++k) {
+            if (outs[k] == outs[i]) {
+                r.x[r.nin] = G[k];
+                r.w[r.nin] = Wm[k];
+                ++r.nin;
+            }
+        }
+        ok(pma::launch_rowmm(r, E, dt, stream));
     }
-    void *gws[4] = {grad_q_w, grad_k_w, grad_v_w, grad_o_w};
-    void *gbs[4] = {grad_q_b, grad_k_b, grad_v_b, grad_o_b};
-    for (int i = 0; i < 4; ++i) {
-        ok(pma::from_f32(gW[i], dt, gws[i], EE, stream));
-        if (has_bias)
-            ok(pma::from_f32(gb + i * E, dt, gbs[i], E, stream));
-    }
-    (void)es;
     if (st != PMA_OK)
         return fail(st, "backward launch failed: %s", hipGetErrorString(hipGetLastError()));
     return PMA_OK;

@@ -28,8 +28,16 @@ struct GraphDev {
     // Source-major view, built on first backward: per source s its entries
     // csc_ptr[s] .. csc_ptr[s+1] give each edge's target (csc_tgt) and its
     // position in the target-grouped arrays (csc_pos).
+    // csc_tgt and csc_pos carry kSrcPad zero entries past nnz.
     int32_t *csc_ptr = nullptr, *csc_tgt = nullptr, *csc_pos = nullptr;
+    // Source pieces, built with the source-major view: piece i covers entries
+    // s_begin[i] .. s_end[i] of source s_source[i]; s_slot[i] is its partial
+    // slot, -1 when the source is one piece. Sources in more than one piece:
+    // ss_source, with slots ss_slot0 .. ss_slot0 + ss_count - 1.
+    int32_t *s_source = nullptr, *s_begin = nullptr, *s_end = nullptr, *s_slot = nullptr;
+    int32_t *ss_source = nullptr, *ss_slot0 = nullptr, *ss_count = nullptr;
     int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0, n_kv = 0;
+    int64_t n_stasks = 0, n_ssplit = 0, n_sslots = 0;
 };
 
 // Builds every array of GraphDev from host edges (already validated, loops
@@ -39,9 +47,10 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
                        int64_t S, int chunk, hipStream_t stream, GraphDev *g, char *err,
                        size_t errlen);
 void free_graph(GraphDev *g);
-// Builds csc_ptr / csc_tgt / csc_pos (blocks on `stream` once).
-pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, hipStream_t stream, char *err,
-                     size_t errlen);
+// Builds the source-major view and the source pieces of at most `chunk`
+// entries (blocks on `stream`).
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t stream,
+                     char *err, size_t errlen);
 
 // ---- projections (proj.hip) ----------------------------------------------
 
@@ -134,17 +143,55 @@ struct BwdArgs {
     float inv_sqrt_d;
     const void *q, *k, *v, *mixed;   // saved, batch-first, plan dtype
     const float *ml;                 // saved [L][B][H][2] (max, sum), base 2
-    const float *dm;                 // (B, L, E) gradient reaching mixed
+    const void *dm;                  // (B, L, E) gradient reaching mixed, plan dtype
     const int32_t *row_ptr, *csr_src, *csc_ptr, *csc_tgt, *csc_pos;
+    // target pieces (the forward's) and source pieces, with their splits
+    const int32_t *t_target, *t_begin, *t_end, *t_slot;
+    const int32_t *ts_target, *ts_slot0, *ts_count;
+    const int32_t *s_source, *s_begin, *s_end, *s_slot;
+    const int32_t *ss_source, *ss_slot0, *ss_count;
+    int64_t n_ttasks, n_tsplit, n_stasks, n_ssplit;
     const uint64_t *kpm_bits;        // packed mask or nullptr
     int kpm_words;
     float *P, *DZ;                   // [nnz][B][H] scratch
-    float *dq, *dk, *dv;             // (B, L, E), (B, S, E), (B, S, E) fp32
+    float *part_q;                   // [target slot][B][E] partial dq
+    float *part_kv;                  // [source slot][B][2E] partial dk, dv
+    void *dq, *dk, *dv;              // (B, L, E), (B, S, E), (B, S, E), plan dtype
 };
 pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s);
-pma_status to_f32(const void *x, pma_dtype dt, float *y, int64_t n, hipStream_t s);
-pma_status from_f32(const float *x, pma_dtype dt, void *y, int64_t n, hipStream_t s);
-pma_status colsum(const float *g, int64_t rows, int E, float *out, hipStream_t s);
+// fp32 bytes of part_q + part_kv
+size_t bwd_piece_scratch(const GraphDev &g, int64_t B, int64_t E);
+
+// y (rows, E) = sum_j x_j (rows, E) W_j with W_j (E, E) [out][in]: the
+// gradient of x W^T with respect to x, summed over the maps that read x.
+// accumulate: y += (fp32 plans only). Row-major, plan dtype.
+struct RowMM {
+    const void *x[3];
+    const void *w[3];
+    int nin;
+    void *y;
+    int64_t rows;
+    int accumulate;
+};
+pma_status launch_rowmm(const RowMM &a, int64_t E, pma_dtype dt, hipStream_t s);
+
+// Weight and bias gradients of up to four linear maps y = x W^T + b:
+// dW = G^T X (E, E) [out][in] and db = column sums of G (skipped when db is
+// null), with G = dy and X = x (rows, E) row-major; plan dtype in and out.
+struct WGradPair {
+    const void *g, *x;
+    int64_t rows;
+    void *dw, *db;
+};
+struct WGrad {
+    WGradPair p[4];
+    int np;
+    int E;
+    int nwg;        // set by launch_wgrad
+    float *part;    // wgrad_scratch bytes
+};
+size_t wgrad_scratch(int64_t E, int np, int64_t max_rows);
+pma_status launch_wgrad(WGrad a, pma_dtype dt, hipStream_t s);
 
 // Whether the edge kernels take a key_padding_mask for these arguments (the
 // fast kernel needs every tensor under 2 GiB when masked).

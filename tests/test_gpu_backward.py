@@ -122,3 +122,47 @@ def test_backward_rejects():
         assert lib.pma_train_bytes(None, 4) == 0 and lib.pma_train_bytes(plan.handle, 0) == 0
     finally:
         pma.pma_destroy(plan)
+
+
+# PMA_CHUNK=3 cuts every target and source with more than three edges into
+# pieces, so the partial sums and their merge carry most of the result.
+@pytest.mark.parametrize("shape", [("f32", 64, 4), ("bf16", 64, 4), ("f32", 128, 8),
+                                   ("bf16", 128, 8), ("f32", 16, 4)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_H{s[2]}")
+@pytest.mark.parametrize("shared", ["none", "kv", "qkv"])
+def test_backward_pieces(shape, shared, monkeypatch):
+    monkeypatch.setenv("PMA_CHUNK", "3")
+    dt, E, H = shape
+    L = S = 64
+    if shared == "none":
+        S = 80
+    c = synth.random_case(85, 3, L, S, E, H, 0.12, dtype=dt, same_kv=shared != "none",
+                          same_qkv=shared == "qkv", name="bwd_pieces")
+    _grad_check(c, shared)
+
+
+@pytest.mark.parametrize("chunk", [None, "16"])
+def test_backward_hub_source(chunk, monkeypatch):
+    # source 7 feeds 140 of the 150 targets
+    if chunk:
+        monkeypatch.setenv("PMA_CHUNK", chunk)
+    c = synth.random_case(86, 2, 150, 150, 64, 4, 0.02, name="bwd_hub_src")
+    keep = c.src != 7
+    c.src = np.concatenate([c.src[keep], np.full(140, 7)])
+    c.tgt = np.concatenate([c.tgt[keep], np.arange(140)])
+    _grad_check(c, "qkv")
+
+
+def test_backward_masked_pieces(monkeypatch):
+    monkeypatch.setenv("PMA_CHUNK", "4")
+    c = synth.random_case(87, 5, 50, 50, 64, 4, 0.15, dtype="bf16", name="bwd_mask_pieces")
+    kpm = np.random.default_rng(88).random((c.B, c.S)) < 0.3
+    _grad_check(c, "qkv", kpm=kpm)
+
+
+@pytest.mark.parametrize("cfg", ["gene", "bipartite"])
+def test_backward_full_graph_small_batch(cfg):
+    # the full-size graphs (hub sources feeding thousands of targets, split
+    # targets) at a batch the float64 gradient oracle finishes in seconds
+    c = synth.gene(B=2) if cfg == "gene" else synth.bipartite(B=1)
+    _grad_check(c, "qkv" if cfg == "gene" else "kv")
