@@ -115,6 +115,93 @@ def cpu_baseline(case, budget_s: float = 12.0):
             "cpu": _cpu_model()}
 
 
+def linear_bytes(B, L, nnz, C, s):
+    """Algorithmic bytes of one PackedLinear forward: per sample, gather one
+    source row of C channels per edge and write each target row; plus the
+    weight, source id and edge-order id of every edge and the row pointers."""
+    return B * (nnz * C * s + L * C * s) + nnz * (s + 8) + 4 * (L + 1)
+
+
+def bench_linear(args):
+    """PackedLinear forward (or forward + backward with --train) on the
+    workload's graph, batch and dtype, with ``--channels`` channels per node."""
+    import torch
+    import graph_sparse_head_amd as pma
+    from graph_sparse_head_amd import synth
+    import oracle
+    from oracle import linear as ol
+
+    case = _workload(args.config)
+    C = args.channels
+    rng = np.random.default_rng(5)
+    src, tgt = oracle.prepare_edges(case.src, case.tgt, case.L, case.S, 1, 1, case.add_self_loops)
+    nnz = len(src)
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(tdt)
+    x = dev(rng.standard_normal((case.B, case.S, C)))
+    w = dev(rng.uniform(-1, 1, nnz) / np.sqrt(10.0))
+    b = dev(rng.normal(0, 0.1, case.L))
+    g = dev(rng.standard_normal((case.B, case.L, C)))
+    plan = pma.pma_create_graph(case.src, case.tgt, case.L, case.S,
+                                add_self_loops=case.add_self_loops, dtype=case.dtype)
+    out = torch.empty(case.B, case.L, C, dtype=tdt, device="cuda")
+
+    def step():
+        pma.pma_linear_forward(plan, x, w, b, out=out)
+        if args.train:
+            pma.pma_linear_backward(plan, x, w, g, has_bias=True)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    es = 2 if case.dtype == "bf16" else 4
+    nbytes = linear_bytes(case.B, case.L, nnz, C, es)
+    res = {
+        "metric": "edge-samples/s PackedLinear fwd (nnz·B·C per sec)", "value":
+            nnz * case.B * C / (ms * 1e-3), "unit": "edge-samples/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": f"PackedLinear on the {case.name} graph: L={case.L} S={case.S} "
+                               f"nnz={nnz} B={case.B} C={C} {case.dtype}"
+                               f"{' train step (forward + backward)' if args.train else ''}",
+                   "batch": case.B, "channels": C, "nnz": nnz, "parallelism": "single GPU"},
+    }
+    if not args.train:
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "kernel": "lin_spmm (+ lin_merge), whole call",
+                           "bytes_per_launch": nbytes, "avg_launch_us": ms * 1e3}
+    pma.pma_destroy(plan)
+    if not args.no_cpu_baseline:
+        xs = x.float().cpu().numpy().astype(np.float64)
+        ws = w.float().cpu().numpy().astype(np.float64)
+        bs = b.float().cpu().numpy().astype(np.float64)
+        nb = max(1, min(case.B, 4))
+        t0, reps = time.perf_counter(), 0
+        while reps == 0 or time.perf_counter() - t0 < 10.0:
+            ol.forward(xs[:nb], ws, bs, src, tgt, case.L)
+            reps += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": nnz * nb * C * reps / dt, "unit": "edge-samples/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} forward(s) (fp64) of {nb} of {case.B} samples, "
+                                         f"{dt:.1f} s, numpy on one thread"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +216,10 @@ def main():
                     help="mask this fraction of keys per sample (seeded); 0: no mask")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-stage events (no roofline)")
+    ap.add_argument("--linear", action="store_true",
+                    help="time PackedLinear (pma_linear_forward) on the workload's graph instead")
+    ap.add_argument("--channels", type=int, default=1,
+                    help="channels per node for --linear (1: the nn.Linear-shaped layer)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 5 times (counter calibration)")
     args = ap.parse_args()
@@ -146,6 +237,10 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this path runs on a single GPU)", file=sys.stderr)
         sys.exit(2)
+
+    if args.linear:
+        bench_linear(args)
+        return
 
     import torch
     import graph_sparse_head_amd as pma

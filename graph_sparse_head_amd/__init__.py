@@ -19,6 +19,7 @@ import numpy as np
 __all__ = [
     "PmaError", "Plan", "pma_create", "pma_forward", "pma_forward_masked", "pma_destroy",
     "pma_train_bytes", "pma_forward_train", "pma_backward",
+    "pma_create_graph", "pma_linear_forward", "pma_linear_backward",
     "pma_nnz", "pma_edges",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
     "pma_profile_stages",
@@ -81,6 +82,9 @@ def _load():
                                    P]),
         "pma_backward": (st, [P, I64, P, P, P, P, P, P, P, I32, P, P, P, I32, P, P, P, P, P, P, P,
                               P, P, P, P, P]),
+        "pma_create_graph": (st, [ctypes.POINTER(P), P, P, I64, I64, I64, I32, I32, P]),
+        "pma_linear_forward": (st, [P, I64, I64, P, P, P, P, P]),
+        "pma_linear_backward": (st, [P, I64, I64, P, P, P, P, P, P, P]),
         "pma_destroy": (st, [P]),
         "pma_nnz": (I64, [P]),
         "pma_edges": (st, [P, P, P]),
@@ -357,6 +361,66 @@ def pma_backward(plan: Plan, query, key, value, q_w, k_w, v_w, o_w, has_bias: bo
     return res
 
 
+def pma_create_graph(source_index, target_index, query_features: int, key_features: int,
+                     add_self_loops: bool = False, dtype: str = "f32", stream=None) -> Plan:
+    """A plan for the PackedLinear calls only (see ``pma_create_graph``)."""
+    lib = _load()
+    src = _host_i64(source_index, "source_index")
+    tgt = _host_i64(target_index, "target_index")
+    if src.shape[0] != tgt.shape[0]:
+        raise PmaError(8, "source_index and target_index differ in length")
+    if dtype not in _DTYPES:
+        raise PmaError(7, f"dtype must be one of {sorted(_DTYPES)}")
+    if not isinstance(add_self_loops, (bool, np.bool_)):
+        raise PmaError(8, "add_self_loops must be a bool")
+    h = ctypes.c_void_p()
+    st = lib.pma_create_graph(ctypes.byref(h), src.ctypes.data, tgt.ctypes.data, src.shape[0],
+                              int(query_features), int(key_features), int(bool(add_self_loops)),
+                              _DTYPES[dtype], _stream_ptr(stream))
+    _check(st)
+    return Plan(h, dtype, int(query_features), int(key_features), 0, 0)
+
+
+def pma_linear_forward(plan: Plan, x, weight, bias=None, out=None, stream=None):
+    """``pma_linear_forward``: x (..., S, C) -> out (..., L, C)."""
+    import torch
+    lib = _load()
+    tdt = torch.float32 if plan.dtype == "f32" else torch.bfloat16
+    if x.dim() < 2 or x.shape[-2] != plan.S:
+        raise PmaError(2, f"x has shape {tuple(x.shape)}, expected (..., {plan.S}, C)")
+    C = int(x.shape[-1])
+    lead = tuple(x.shape[:-2])
+    B = int(np.prod(lead)) if lead else 1
+    if out is None:
+        out = torch.empty(*lead, plan.L, C, dtype=tdt, device=x.device)
+    n = plan.nnz
+    st = lib.pma_linear_forward(plan.handle, B, C, _dptr(x, "x", tdt, (plan.S, C)),
+                                _dptr(weight, "weight", tdt, (n,)),
+                                _dptr(bias, "bias", tdt, (plan.L,)),
+                                _dptr(out, "out", tdt, (plan.L, C)), _stream_ptr(stream))
+    _check(st)
+    return out
+
+
+def pma_linear_backward(plan: Plan, x, weight, grad_out, has_bias: bool = True, stream=None):
+    """``pma_linear_backward``: returns (grad_x, grad_weight, grad_bias or None)."""
+    import torch
+    lib = _load()
+    tdt = torch.float32 if plan.dtype == "f32" else torch.bfloat16
+    C = int(x.shape[-1])
+    lead = tuple(x.shape[:-2])
+    B = int(np.prod(lead)) if lead else 1
+    gx = torch.empty(x.shape, dtype=tdt, device=x.device)
+    gw = torch.empty(plan.nnz, dtype=tdt, device=x.device)
+    gb = torch.empty(plan.L, dtype=tdt, device=x.device) if has_bias else None
+    st = lib.pma_linear_backward(plan.handle, B, C, _dptr(x, "x", tdt, (plan.S, C)),
+                                 _dptr(weight, "weight", tdt, (plan.nnz,)),
+                                 _dptr(grad_out, "grad_out", tdt, (plan.L, C)), gx.data_ptr(),
+                                 gw.data_ptr(), _dptr(gb, "grad_bias", tdt), _stream_ptr(stream))
+    _check(st)
+    return gx, gw, gb
+
+
 def pma_destroy(plan: Plan) -> None:
     if plan is None or plan.handle is None or not plan.handle.value:
         return
@@ -430,7 +494,7 @@ def pma_profile_read(plan: Plan) -> dict:
 
 def __getattr__(name):
     # The nn.Module surface imports torch; load it on first use.
-    if name in ("PackedMultiheadAttention", "ModuleArgError"):
+    if name in ("PackedMultiheadAttention", "PackedLinear", "ModuleArgError"):
         from . import module
         return getattr(module, name)
     raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

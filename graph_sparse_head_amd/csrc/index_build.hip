@@ -356,7 +356,7 @@ void free_graph(GraphDev *g)
                         &g->task_target, &g->task_begin,  &g->task_end,   &g->task_slot,
                         &g->task_split,  &g->split_target, &g->split_slot0, &g->split_count,
                         &g->csr_kv,      &g->kv_rows,     &g->csc_ptr,    &g->csc_tgt,
-                        &g->csc_pos,     &g->s_source,    &g->s_begin,    &g->s_end,
+                        &g->csc_pos,     &g->csc_eid,     &g->s_source,   &g->s_begin,    &g->s_end,
                         &g->s_slot,      &g->ss_source,   &g->ss_slot0,   &g->ss_count};
     for (int32_t **p : ptrs) {
         if (*p)
@@ -401,7 +401,8 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     PMA_TRY(hipMalloc(&g->csr_src, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMemsetAsync(g->csr_src + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMalloc(&g->csr_tgt, nnz * i4));
-    PMA_TRY(hipMalloc(&g->csr_eid, nnz * i4));
+    PMA_TRY(hipMalloc(&g->csr_eid, (nnz + kSrcPad) * i4));
+    PMA_TRY(hipMemsetAsync(g->csr_eid + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMalloc(&n_piece, L * i4));
     PMA_TRY(hipMalloc(&n_slot, L * i4));
     PMA_TRY(hipMalloc(&is_split, L * i4));
@@ -516,11 +517,14 @@ done:
 // Source-major view of the same edges, for the backward pass: positions of
 // the target-grouped entries sorted stably by source (so by (source,
 // target)), each entry's target, and per-source offsets.
-__global__ void csc_fill(const int32_t *perm, const int32_t *csr_tgt, int64_t nnz, int32_t *csc_tgt)
+__global__ void csc_fill(const int32_t *perm, const int32_t *csr_tgt, const int32_t *csr_eid,
+                         int64_t nnz, int32_t *csc_tgt, int32_t *csc_eid)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j < nnz)
+    if (j < nnz) {
         csc_tgt[j] = csr_tgt[perm[j]];
+        csc_eid[j] = csr_eid[perm[j]];
+    }
 }
 
 pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t stream,
@@ -552,13 +556,16 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t
     PMA_TRY(hipMalloc(&g->csc_ptr, (S + 1) * i4));
     PMA_TRY(hipMalloc(&g->csc_tgt, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMemsetAsync(g->csc_tgt + nnz, 0, kSrcPad * i4, stream));
+    PMA_TRY(hipMalloc(&g->csc_eid, (nnz + kSrcPad) * i4));
+    PMA_TRY(hipMemsetAsync(g->csc_eid + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMemsetAsync(deg, 0, S * i4, stream));
     PMA_TRY(hipMemsetAsync(small, 0, 8 * i4, stream));
     iota_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, nnz);
     PMA_TRY(radix_sort_perm(g->csr_src, bits_for(S - 1), perm, perm_tmp, nnz, counts, scan_tmp,
                             stream));
     PMA_TRY(hipMemsetAsync(perm + nnz, 0, kSrcPad * i4, stream));
-    csc_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, g->csr_tgt, nnz, g->csc_tgt);
+    csc_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, g->csr_tgt, g->csr_eid, nnz,
+                                                     g->csc_tgt, g->csc_eid);
     degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, nnz, deg);
     PMA_TRY(scan_exclusive(deg, g->csc_ptr, S, g->csc_ptr + S, scan_tmp, stream));
     g->csc_pos = perm;   // kept
@@ -596,7 +603,7 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t
 fail:
     (void)hipStreamSynchronize(stream);
     {
-        int32_t **own[] = {&g->csc_ptr,  &g->csc_tgt, &g->csc_pos,  &g->s_source, &g->s_begin,
+        int32_t **own[] = {&g->csc_ptr,  &g->csc_tgt, &g->csc_pos,  &g->csc_eid,  &g->s_source, &g->s_begin,
                            &g->s_end,    &g->s_slot,  &g->ss_source, &g->ss_slot0, &g->ss_count};
         for (int32_t **q : own) {
             if (*q)

@@ -57,9 +57,11 @@ struct pma_plan {
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
     uint64_t *kpm_bits = nullptr;   // key_padding_mask packed by source
-    // backward scratch, grown on demand
+    // backward and PackedLinear scratch, grown on demand
     char *bw = nullptr;
     size_t bw_bytes = 0;
+    char *lin = nullptr;
+    size_t lin_bytes = 0;
     // profiling
     unsigned prof = 0;   // stages timed: bit s for stage s
     std::vector<EventPair> pending;
@@ -170,10 +172,14 @@ struct StageTimer {
 
 PMA_API const char *pma_last_error(void) { return g_err; }
 
-PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
-                              const int64_t *target_index, int64_t nnz, int64_t query_features,
-                              int64_t key_features, int64_t embed_dim, int64_t num_heads,
-                              int add_self_loops, pma_dtype dtype, hipStream_t stream)
+namespace {
+
+// attn: a plan for the attention calls (embed_dim, num_heads checked); else
+// a graph-only plan (embed_dim = num_heads = 0) for the PackedLinear calls.
+pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64_t *target_index,
+                       int64_t nnz, int64_t query_features, int64_t key_features,
+                       int64_t embed_dim, int64_t num_heads, int add_self_loops, pma_dtype dtype,
+                       hipStream_t stream, bool attn)
 {
     g_err[0] = 0;
     if (!plan)
@@ -184,10 +190,10 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     if (add_self_loops != 0 && add_self_loops != 1)
         return fail(PMA_E_ARG, "add_self_loops must be 0 or 1");
     const int64_t L = query_features, S = key_features, E = embed_dim, H = num_heads;
-    if (L <= 0 || S <= 0 || E <= 0 || H <= 0)
+    if (L <= 0 || S <= 0 || (attn && (E <= 0 || H <= 0)))
         return fail(PMA_E_SIZE, "sizes must be positive (L=%lld S=%lld E=%lld H=%lld)",
                     (long long)L, (long long)S, (long long)E, (long long)H);
-    if (E % H != 0)
+    if (attn && E % H != 0)
         return fail(PMA_E_SIZE, "embed_dim %lld is not divisible by num_heads %lld",
                     (long long)E, (long long)H);
     if (nnz < 1)
@@ -299,6 +305,26 @@ PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
     return PMA_OK;
 }
 
+}  // namespace
+
+PMA_API pma_status pma_create(pma_plan **plan, const int64_t *source_index,
+                              const int64_t *target_index, int64_t nnz, int64_t query_features,
+                              int64_t key_features, int64_t embed_dim, int64_t num_heads,
+                              int add_self_loops, pma_dtype dtype, hipStream_t stream)
+{
+    return create_impl(plan, source_index, target_index, nnz, query_features, key_features,
+                       embed_dim, num_heads, add_self_loops, dtype, stream, true);
+}
+
+PMA_API pma_status pma_create_graph(pma_plan **plan, const int64_t *source_index,
+                                    const int64_t *target_index, int64_t nnz,
+                                    int64_t query_features, int64_t key_features,
+                                    int add_self_loops, pma_dtype dtype, hipStream_t stream)
+{
+    return create_impl(plan, source_index, target_index, nnz, query_features, key_features, 0, 0,
+                       add_self_loops, dtype, stream, false);
+}
+
 PMA_API pma_status pma_destroy(pma_plan *plan)
 {
     if (!plan)
@@ -308,6 +334,8 @@ PMA_API pma_status pma_destroy(pma_plan *plan)
     free_workspace(plan);
     if (plan->bw)
         (void)hipFree(plan->bw);
+    if (plan->lin)
+        (void)hipFree(plan->lin);
     for (auto &ev : plan->pending) {
         (void)hipEventDestroy(ev.a);
         (void)hipEventDestroy(ev.b);
@@ -427,6 +455,8 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     g_err[0] = 0;
     if (!plan)
         return fail(PMA_E_NULL, "plan is NULL");
+    if (plan->E == 0)
+        return fail(PMA_E_ARG, "the plan has no attention sizes (made by pma_create_graph)");
     if (batch <= 0)
         return fail(PMA_E_SIZE, "batch must be positive (got %lld)", (long long)batch);
     if (!query || !key || !value || !q_w || !k_w || !v_w || !o_w || !out)
@@ -615,7 +645,7 @@ PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void 
 
 PMA_API size_t pma_train_bytes(const pma_plan *plan, int64_t batch)
 {
-    if (!plan || batch <= 0)
+    if (!plan || batch <= 0 || plan->E == 0)
         return 0;
     return save_layout(plan, batch).total;
 }
@@ -651,6 +681,8 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     g_err[0] = 0;
     if (!plan)
         return fail(PMA_E_NULL, "plan is NULL");
+    if (plan->E == 0)
+        return fail(PMA_E_ARG, "the plan has no attention sizes (made by pma_create_graph)");
     if (batch <= 0)
         return fail(PMA_E_SIZE, "batch must be positive (got %lld)", (long long)batch);
     if (!query || !key || !value || !q_w || !k_w || !v_w || !o_w || !save || !grad_out ||
@@ -824,6 +856,215 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     }
     if (st != PMA_OK)
         return fail(st, "backward launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PMA_OK;
+}
+
+namespace {
+
+// Checks shared by the PackedLinear calls; grows the plan's scratch to hold
+// fp32 partials of `slots` rows and `nbuf` node-major copies of up to
+// max(L, S) rows, all of R = batch * channels values.
+pma_status linear_common(pma_plan *p, int64_t batch, int64_t channels, int64_t slots, int nbuf,
+                         char **ws)
+{
+    if (!p)
+        return fail(PMA_E_NULL, "plan is NULL");
+    if (batch <= 0 || channels <= 0)
+        return fail(PMA_E_SIZE, "batch and channels must be positive (got %lld, %lld)",
+                    (long long)batch, (long long)channels);
+    const int64_t R = batch * channels;
+    const int64_t rows = (p->L > p->S ? p->L : p->S);
+    if (R > kI32 || rows * R > ((int64_t)1 << 40))
+        return fail(PMA_E_UNSUPPORTED, "batch * channels too large");
+    const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t need = up((size_t)(slots > 0 ? slots : 1) * R * sizeof(float)) +
+                        (size_t)nbuf * up((size_t)rows * R * es);
+    if (need > p->lin_bytes) {
+        if (p->lin) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(p->lin);
+        }
+        p->lin = nullptr;
+        p->lin_bytes = 0;
+        hipError_t e = hipMalloc(&p->lin, need);
+        if (e != hipSuccess)
+            return fail(e == hipErrorOutOfMemory ? PMA_E_OOM : PMA_E_DEVICE,
+                        "PackedLinear scratch of %zu bytes: %s", need, hipGetErrorString(e));
+        p->lin_bytes = need;
+    }
+    *ws = p->lin;
+    return PMA_OK;
+}
+
+}  // namespace
+
+PMA_API pma_status pma_linear_forward(pma_plan *plan, int64_t batch, int64_t channels,
+                                      const void *x, const void *weight, const void *bias,
+                                      void *out, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (plan && (!x || !weight || !out))
+        return fail(PMA_E_NULL, "x, weight or out is NULL");
+    const pma_dtype dt = plan ? plan->dtype : PMA_F32;
+    const void *user[2] = {x, out};
+    // Read the batch-first tensors directly when a sample's channels fill
+    // 16-byte chunks (or there is one sample); else go node-major.
+    const bool direct = batch == 1 || pma::lin_vec(channels, dt, user, 2) > 1;
+    char *ws = nullptr;
+    pma_status st = linear_common(plan, batch, channels, plan ? plan->g.n_slots : 0,
+                                  direct ? 0 : 2, &ws);
+    if (st != PMA_OK)
+        return st;
+    const pma::GraphDev &g = plan->g;
+    const int64_t R = batch * channels, L = plan->L, S = plan->S;
+    const size_t es = dt == PMA_BF16 ? 2 : 4;
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t b_part = up((size_t)(g.n_slots > 0 ? g.n_slots : 1) * R * sizeof(float));
+    const size_t b_row = up((size_t)(L > S ? L : S) * R * es);
+    pma::LinArgs a;
+    a.R = (int)R;
+    if (direct) {
+        a.x = x;
+        a.y = out;
+        a.Cs = (int)channels;
+        a.sn_in = channels;
+        a.sb_in = S * channels;
+        a.sn_out = channels;
+        a.sb_out = L * channels;
+    } else {
+        a.x = ws + b_part;
+        a.y = ws + b_part + b_row;
+        a.Cs = (int)R;
+        a.sn_in = a.sn_out = R;
+        a.sb_in = a.sb_out = 0;
+        st = pma::launch_transpose(x, const_cast<void *>(a.x), batch, S, channels, dt, stream);
+    }
+    a.w = weight;
+    a.bias = bias;
+    a.idx = g.csr_src;
+    a.eid = g.csr_eid;
+    a.t_row = g.task_target;
+    a.t_begin = g.task_begin;
+    a.t_end = g.task_end;
+    a.t_slot = g.task_slot;
+    a.n_tasks = g.n_tasks;
+    a.s_row = g.split_target;
+    a.s_slot0 = g.split_slot0;
+    a.s_count = g.split_count;
+    a.n_split = g.n_split;
+    a.part = reinterpret_cast<float *>(ws);
+    const void *ptrs[2] = {a.x, a.y};
+    if (st == PMA_OK)
+        st = pma::launch_spmm(a, dt, pma::lin_vec(a.Cs, dt, ptrs, 2), stream);
+    if (st == PMA_OK && !direct)
+        st = pma::launch_transpose(a.y, out, L, batch, channels, dt, stream);
+    if (st != PMA_OK)
+        return fail(st, "PackedLinear launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_linear_backward(pma_plan *plan, int64_t batch, int64_t channels,
+                                       const void *x, const void *weight, const void *grad_out,
+                                       void *grad_x, void *grad_weight, void *grad_bias,
+                                       hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (plan && (!x || !weight || !grad_out || !grad_x || !grad_weight))
+        return fail(PMA_E_NULL, "a required pointer is NULL");
+    if (plan && (batch <= 0 || channels <= 0))
+        return fail(PMA_E_SIZE, "batch and channels must be positive (got %lld, %lld)",
+                    (long long)batch, (long long)channels);
+    if (plan && !plan->g.csc_ptr) {
+        char err[256] = "";
+        pma_status st = pma::build_csc(&plan->g, plan->nnz, plan->S, plan->bchunk, stream, err,
+                                       sizeof err);
+        if (st != PMA_OK)
+            return fail(st, "%s", err);
+    }
+    const pma_dtype dt = plan ? plan->dtype : PMA_F32;
+    const void *user[3] = {x, grad_out, grad_x};
+    const bool direct = batch == 1 || pma::lin_vec(channels, dt, user, 3) > 1;
+    char *ws = nullptr;
+    pma_status st = linear_common(plan, batch, channels, plan ? plan->g.n_sslots : 0,
+                                  direct ? 0 : 3, &ws);
+    if (st != PMA_OK)
+        return st;
+    const pma::GraphDev &g = plan->g;
+    const int64_t R = batch * channels, L = plan->L, S = plan->S;
+    const size_t es = dt == PMA_BF16 ? 2 : 4;
+    auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t b_part = up((size_t)(g.n_sslots > 0 ? g.n_sslots : 1) * R * sizeof(float));
+    const size_t b_row = up((size_t)(L > S ? L : S) * R * es);
+    // rows of x, dy and dx: batch-first segments of C, or node-major rows
+    const void *xr = x, *gr = grad_out;
+    void *dxr = grad_x;
+    int Cs = (int)channels;
+    int64_t snx = channels, sbx = S * channels, sng = channels, sbg = L * channels;
+    if (!direct) {
+        xr = ws + b_part;
+        gr = ws + b_part + b_row;
+        dxr = ws + b_part + 2 * b_row;
+        Cs = (int)R;
+        snx = sng = R;
+        sbx = sbg = 0;
+        st = pma::launch_transpose(x, const_cast<void *>(xr), batch, S, channels, dt, stream);
+        if (st == PMA_OK)
+            st = pma::launch_transpose(grad_out, const_cast<void *>(gr), batch, L, channels, dt,
+                                       stream);
+    }
+    // input gradient: the same product over the source-major pieces
+    pma::LinArgs a;
+    a.R = (int)R;
+    a.Cs = Cs;
+    a.sn_in = sng;
+    a.sb_in = sbg;
+    a.sn_out = snx;
+    a.sb_out = sbx;
+    a.x = gr;
+    a.w = weight;
+    a.bias = nullptr;
+    a.y = dxr;
+    a.idx = g.csc_tgt;
+    a.eid = g.csc_eid;
+    a.t_row = g.s_source;
+    a.t_begin = g.s_begin;
+    a.t_end = g.s_end;
+    a.t_slot = g.s_slot;
+    a.n_tasks = g.n_stasks;
+    a.s_row = g.ss_source;
+    a.s_slot0 = g.ss_slot0;
+    a.s_count = g.ss_count;
+    a.n_split = g.n_ssplit;
+    a.part = reinterpret_cast<float *>(ws);
+    const void *ptrs[3] = {xr, gr, dxr};
+    const int vec = pma::lin_vec(Cs, dt, ptrs, 3);
+    if (st == PMA_OK)
+        st = pma::launch_spmm(a, dt, vec, stream);
+    if (st == PMA_OK && !direct)
+        st = pma::launch_transpose(dxr, grad_x, S, batch, channels, dt, stream);
+    if (st == PMA_OK) {
+        pma::RowDots d;
+        d.csr_src = g.csr_src;
+        d.csr_tgt = g.csr_tgt;
+        d.csr_eid = g.csr_eid;
+        d.nnz = plan->nnz;
+        d.L = L;
+        d.R = (int)R;
+        d.Cs = Cs;
+        d.snx = snx;
+        d.sbx = sbx;
+        d.sng = sng;
+        d.sbg = sbg;
+        d.x = xr;
+        d.dy = gr;
+        d.dw = grad_weight;
+        d.db = grad_bias;
+        st = pma::launch_lin_rowdots(d, dt, vec, stream);
+    }
+    if (st != PMA_OK)
+        return fail(st, "PackedLinear backward launch failed: %s",
+                    hipGetErrorString(hipGetLastError()));
     return PMA_OK;
 }
 

@@ -18,18 +18,19 @@ struct GraphDev {
     int32_t *row_ptr = nullptr;   // L + 1
     int32_t *csr_src = nullptr;   // nnz (+ kSrcPad zeros), per target ascending source
     int32_t *csr_tgt = nullptr;   // nnz
-    int32_t *csr_eid = nullptr;   // nnz, position in the edge order
+    int32_t *csr_eid = nullptr;   // nnz (+ kSrcPad zeros), position in the edge order
     int32_t *task_target = nullptr, *task_begin = nullptr, *task_end = nullptr,
             *task_slot = nullptr, *task_split = nullptr; // n_tasks each; split index or -1
     int32_t *split_target = nullptr, *split_slot0 = nullptr, *split_count = nullptr; // n_split
     // Sources some edge reads, in ascending order (kv_rows[0, n_kv)), and each
     // CSR entry's source as a position in that list (csr_kv, + kSrcPad zeros).
     int32_t *kv_rows = nullptr, *csr_kv = nullptr;
-    // Source-major view, built on first backward: per source s its entries
-    // csc_ptr[s] .. csc_ptr[s+1] give each edge's target (csc_tgt) and its
-    // position in the target-grouped arrays (csc_pos).
-    // csc_tgt and csc_pos carry kSrcPad zero entries past nnz.
-    int32_t *csc_ptr = nullptr, *csc_tgt = nullptr, *csc_pos = nullptr;
+    // Source-major view, built on first use by a backward pass: per source s
+    // its entries csc_ptr[s] .. csc_ptr[s+1] give each edge's target
+    // (csc_tgt), its position in the target-grouped arrays (csc_pos) and in
+    // the edge order (csc_eid). csc_tgt, csc_pos and csc_eid carry kSrcPad
+    // zero entries past nnz.
+    int32_t *csc_ptr = nullptr, *csc_tgt = nullptr, *csc_pos = nullptr, *csc_eid = nullptr;
     // Source pieces, built with the source-major view: piece i covers entries
     // s_begin[i] .. s_end[i] of source s_source[i]; s_slot[i] is its partial
     // slot, -1 when the source is one piece. Sources in more than one piece:
@@ -192,6 +193,45 @@ struct WGrad {
 };
 size_t wgrad_scratch(int64_t E, int np, int64_t max_rows);
 pma_status launch_wgrad(WGrad a, pma_dtype dt, hipStream_t s);
+
+// ---- PackedLinear (linear.hip) ----------------------------------------------
+// A node's row is R values in segments of Cs: value (segment b, k) of node n
+// sits at n * sn + b * sb + k (node-major rows: Cs = R, sn = R; batch-first
+// tensors: Cs = C, sn = C, sb = nodes * C). y rows = sum over the entries of
+// each output row's pieces of w[eid] x rows[idx] (+ bias[row] on every
+// value); plan dtype in and out.
+struct LinArgs {
+    int R, Cs;
+    int64_t sn_in, sb_in, sn_out, sb_out;
+    const void *x, *w, *bias;      // bias (rows_out) or nullptr
+    void *y;
+    const int32_t *idx, *eid;      // per entry: input row, position in the edge order
+    const int32_t *t_row, *t_begin, *t_end, *t_slot;
+    int64_t n_tasks;
+    const int32_t *s_row, *s_slot0, *s_count;
+    int64_t n_split;
+    float *part;                   // [slot][R]
+    int nseg = 1, cgp = 64;        // set by the launcher
+};
+// dw_e = dot(dy row of t_e, x row of s_e), edge order; db[t] = sum of the dy
+// row of t when db is not null.
+struct RowDots {
+    const int32_t *csr_src, *csr_tgt, *csr_eid;
+    int64_t nnz, L;
+    int R, Cs;
+    int64_t snx, sbx, sng, sbg;
+    const void *x, *dy;
+    void *dw, *db;
+    int cgp = 64;                  // set by the launcher
+};
+// Values per lane: 16 bytes when Cs fills whole 16-byte chunks and every
+// pointer is 16-byte aligned, else 1.
+int lin_vec(int64_t Cs, pma_dtype dt, const void *const *ptrs, int n);
+pma_status launch_spmm(const LinArgs &a, pma_dtype dt, int vec, hipStream_t s);
+pma_status launch_lin_rowdots(const RowDots &a, pma_dtype dt, int vec, hipStream_t s);
+// out[q][p][c] = in[p][q][c]
+pma_status launch_transpose(const void *in, void *out, int64_t P, int64_t Q, int64_t C,
+                            pma_dtype dt, hipStream_t s);
 
 // Whether the edge kernels take a key_padding_mask for these arguments (the
 // fast kernel needs every tensor under 2 GiB when masked).

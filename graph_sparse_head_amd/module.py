@@ -1,6 +1,6 @@
 """torch.nn.Module surface over the C-ABI (kpnn2 0.3.0 API reference,
 PackedMultiheadAttention: constructor parameter table, attributes, "Raises",
-reset_parameters and forward).
+reset_parameters and forward; and PackedLinear from its "See also").
 
 Every step of the computation runs in libpma's kernels; this module only
 validates arguments, keeps the four projections as nn.Linear parameters,
@@ -23,9 +23,10 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from . import pma_backward, pma_create, pma_destroy, pma_edges, pma_forward, pma_forward_train
+from . import (pma_backward, pma_create, pma_create_graph, pma_destroy, pma_edges, pma_forward,
+               pma_forward_train, pma_linear_backward, pma_linear_forward)
 
-__all__ = ["PackedMultiheadAttention", "ModuleArgError"]
+__all__ = ["PackedMultiheadAttention", "PackedLinear", "ModuleArgError"]
 
 
 class ModuleArgError(ValueError):
@@ -68,6 +69,66 @@ def _bool(x, name: str) -> bool:
     return bool(x)
 
 
+def _edges(source_index, target_index, L: int, S: int, add_self_loops: bool):
+    """Validated edge arrays in the layer's edge order: the given pairs, then
+    the missing (i, i) in ascending i when add_self_loops (kpnn2 page,
+    constructor parameter table and "Raises")."""
+    src = _index(source_index, "source_index")
+    tgt = _index(target_index, "target_index")
+    if src.shape[0] != tgt.shape[0]:
+        raise ModuleArgError("source_index and target_index differ in length")
+    if src.shape[0] == 0:
+        raise ModuleArgError("the indices are empty")
+    if src.min() < 0 or src.max() >= S:
+        raise ModuleArgError(f"source_index outside [0, {S})")
+    if tgt.min() < 0 or tgt.max() >= L:
+        raise ModuleArgError(f"target_index outside [0, {L})")
+    pair = tgt * S + src
+    if np.unique(pair).shape[0] != pair.shape[0]:
+        raise ModuleArgError("target_index/source_index repeat a (source, target) pair")
+    if add_self_loops:
+        if L != S:
+            raise ModuleArgError("add_self_loops needs query_features == key_features")
+        have = np.zeros(L, bool)
+        have[src[src == tgt]] = True
+        extra = np.flatnonzero(~have)          # missing (i, i), ascending i
+        src = np.concatenate([src, extra])
+        tgt = np.concatenate([tgt, extra])
+    return src, tgt
+
+
+def _named_edges(sources: Sequence, targets: Sequence, nodes: Optional[Sequence]):
+    """Node order and integer edges from a named edge list: ``nodes`` when
+    given, else order of first appearance (sources and targets interleaved
+    edge by edge)."""
+    if len(sources) != len(targets):
+        raise ModuleArgError("sources and targets differ in length")
+    order: Dict[object, int] = {}
+    if nodes is None:
+        for s, t in zip(sources, targets):
+            order.setdefault(s, len(order))
+            order.setdefault(t, len(order))
+    else:
+        for n in nodes:
+            if n in order:
+                raise ModuleArgError(f"node {n!r} listed twice")
+            order[n] = len(order)
+    try:
+        src = [order[s] for s in sources]
+        tgt = [order[t] for t in targets]
+    except KeyError as e:
+        raise ModuleArgError(f"edge endpoint {e.args[0]!r} is not in nodes") from None
+    return order, src, tgt
+
+
+def _plan_dtype(dtype: torch.dtype) -> str:
+    if dtype == torch.float32:
+        return "f32"
+    if dtype == torch.bfloat16:
+        return "bf16"
+    raise ModuleArgError(f"parameters of dtype {dtype} are not supported (float32, bfloat16)")
+
+
 class PackedMultiheadAttention(torch.nn.Module):
     """Multi-head attention in which each target token attends only to its
     listed source tokens (kpnn2 page, class docstring and "Notes")."""
@@ -96,27 +157,7 @@ class PackedMultiheadAttention(torch.nn.Module):
                 raise ModuleArgError(f"{n} must be None or equal to embed_dim ({E}), got {v!r}")
         if generator is not None and not isinstance(generator, torch.Generator):
             raise ModuleArgError("generator must be a torch.Generator or None")
-        src = _index(source_index, "source_index")
-        tgt = _index(target_index, "target_index")
-        if src.shape[0] != tgt.shape[0]:
-            raise ModuleArgError("source_index and target_index differ in length")
-        if src.shape[0] == 0:
-            raise ModuleArgError("the indices are empty")
-        if src.min() < 0 or src.max() >= S:
-            raise ModuleArgError(f"source_index outside [0, {S})")
-        if tgt.min() < 0 or tgt.max() >= L:
-            raise ModuleArgError(f"target_index outside [0, {L})")
-        pair = tgt * S + src
-        if np.unique(pair).shape[0] != pair.shape[0]:
-            raise ModuleArgError("target_index/source_index repeat a (source, target) pair")
-        if add_self_loops:
-            if L != S:
-                raise ModuleArgError("add_self_loops needs query_features == key_features")
-            have = np.zeros(L, bool)
-            have[src[src == tgt]] = True
-            extra = np.flatnonzero(~have)          # missing (i, i), ascending i
-            src = np.concatenate([src, extra])
-            tgt = np.concatenate([tgt, extra])
+        src, tgt = _edges(source_index, target_index, L, S, add_self_loops)
 
         self.query_features, self.key_features = L, S
         self.embed_dim, self.num_heads, self.head_dim = E, H, E // H
@@ -139,24 +180,7 @@ class PackedMultiheadAttention(torch.nn.Module):
         target). Node i of the token sequence is ``nodes[i]``; without
         ``nodes`` the order is that of first appearance, sources and targets
         interleaved edge by edge."""
-        if len(sources) != len(targets):
-            raise ModuleArgError("sources and targets differ in length")
-        if nodes is None:
-            order: Dict[object, int] = {}
-            for s, t in zip(sources, targets):
-                order.setdefault(s, len(order))
-                order.setdefault(t, len(order))
-        else:
-            order = {}
-            for n in nodes:
-                if n in order:
-                    raise ModuleArgError(f"node {n!r} listed twice")
-                order[n] = len(order)
-        try:
-            src = [order[s] for s in sources]
-            tgt = [order[t] for t in targets]
-        except KeyError as e:
-            raise ModuleArgError(f"edge endpoint {e.args[0]!r} is not in nodes") from None
+        order, src, tgt = _named_edges(sources, targets, nodes)
         n = len(order)
         layer = cls(src, tgt, n, n, embed_dim, num_heads, **kwargs)
         layer.nodes = list(order)
@@ -180,12 +204,7 @@ class PackedMultiheadAttention(torch.nn.Module):
 
     # ------------------------------------------------------------------
     def _plan(self, device: torch.device, dtype: torch.dtype):
-        if dtype == torch.float32:
-            dt = "f32"
-        elif dtype == torch.bfloat16:
-            dt = "bf16"
-        else:
-            raise ModuleArgError(f"parameters of dtype {dtype} are not supported (float32, bfloat16)")
+        dt = _plan_dtype(dtype)
         key = (device.type, device.index if device.index is not None else torch.cuda.current_device(), dt)
         plan = self._plans.get(key)
         if plan is None:
@@ -364,3 +383,135 @@ class _PackedAttnFn(torch.autograd.Function):
         gb = [g.get(n) for n in ("q_b", "k_b", "v_b", "o_b")]
         return (None, gq, gk, gv, None, None, None, None, None,
                 g["q_w"], gb[0], g["k_w"], gb[1], g["v_w"], gb[2], g["o_w"], gb[3])
+
+
+class PackedLinear(torch.nn.Module):
+    """One trained scalar per edge on the packed pairs (kpnn2
+    PackedMultiheadAttention page, "See also": PackedLinear; information flows
+    from source to target). Input (..., in_features) -> output
+    (..., out_features) with
+
+        out[..., t] = bias[t] + sum over edges e into t of weight[e] input[..., s_e],
+
+    weight in the layer's edge order (given pairs, then appended loops).
+    The product and its gradients run in libpma (pma_linear_forward /
+    pma_linear_backward)."""
+
+    def __init__(self, source_index, target_index, in_features, out_features, bias: bool = True,
+                 add_self_loops: bool = False, *, generator: Optional[torch.Generator] = None,
+                 device=None, dtype=None):
+        super().__init__()
+        S = _pos_int(in_features, "in_features")
+        L = _pos_int(out_features, "out_features")
+        bias = _bool(bias, "bias")
+        add_self_loops = _bool(add_self_loops, "add_self_loops")
+        if generator is not None and not isinstance(generator, torch.Generator):
+            raise ModuleArgError("generator must be a torch.Generator or None")
+        src, tgt = _edges(source_index, target_index, L, S, add_self_loops)
+        self.in_features, self.out_features, self.add_self_loops = S, L, add_self_loops
+        self.register_buffer("source_index", torch.from_numpy(src), persistent=True)
+        self.register_buffer("target_index", torch.from_numpy(tgt), persistent=True)
+        kw = {"device": device, "dtype": dtype}
+        self.weight = torch.nn.Parameter(torch.empty(src.shape[0], **kw))
+        if bias:
+            self.bias = torch.nn.Parameter(torch.empty(L, **kw))
+        else:
+            self.register_parameter("bias", None)
+        self._plans: Dict[Tuple[str, int, str], object] = {}
+        self.reset_parameters(generator)
+
+    @classmethod
+    def from_edgelist(cls, sources: Sequence, targets: Sequence, nodes: Optional[Sequence] = None,
+                      **kwargs) -> "PackedLinear":
+        """A layer over one node set from a named edge list (source -> target),
+        node order as for PackedMultiheadAttention.from_edgelist."""
+        order, src, tgt = _named_edges(sources, targets, nodes)
+        n = len(order)
+        layer = cls(src, tgt, n, n, **kwargs)
+        layer.nodes = list(order)
+        return layer
+
+    @property
+    def nnz(self) -> int:
+        return int(self.source_index.shape[0])
+
+    def reset_parameters(self, generator: Optional[torch.Generator] = None) -> None:
+        """nn.Linear's default draw with each target's in-degree as its fan-in:
+        weight[e] and bias[t] uniform in +-1 / sqrt(in-degree of t) (zero
+        bias for a target with no edge)."""
+        deg = np.bincount(self.target_index.cpu().numpy(), minlength=self.out_features)
+        bt = torch.from_numpy(np.where(deg > 0, 1.0 / np.sqrt(np.maximum(deg, 1)), 0.0))
+        with torch.no_grad():
+            u = torch.rand(self.nnz, dtype=torch.float64, generator=generator)
+            self.weight.copy_((2 * u - 1) * bt[self.target_index.cpu()])
+            if self.bias is not None:
+                u = torch.rand(self.out_features, dtype=torch.float64, generator=generator)
+                self.bias.copy_((2 * u - 1) * bt)
+
+    def _plan(self, device: torch.device, dtype: torch.dtype):
+        dt = _plan_dtype(dtype)
+        key = (device.type, device.index if device.index is not None else torch.cuda.current_device(), dt)
+        plan = self._plans.get(key)
+        if plan is None:
+            with torch.cuda.device(key[1]):
+                plan = pma_create_graph(self.source_index.cpu().numpy(),
+                                        self.target_index.cpu().numpy(), self.out_features,
+                                        self.in_features, add_self_loops=False, dtype=dt)
+            s, t = pma_edges(plan)
+            assert (s == self.source_index.cpu().numpy()).all() and \
+                (t == self.target_index.cpu().numpy()).all()
+            self._plans[key] = plan
+        return plan
+
+    def __del__(self):
+        try:
+            for plan in self._plans.values():
+                pma_destroy(plan)
+            self._plans = {}
+        except Exception:   # pragma: no cover
+            pass
+
+    def _apply(self, fn, *args, **kwargs):
+        out = super()._apply(fn, *args, **kwargs)
+        for n in ("source_index", "target_index"):
+            b = getattr(self, n)
+            if b.dtype != torch.int64:
+                setattr(self, n, b.to(torch.int64))
+        return out
+
+    def forward(self, input):
+        if not isinstance(input, torch.Tensor) or not input.is_floating_point():
+            raise ModuleArgError("input must be a floating-point tensor")
+        if input.dim() < 1 or input.shape[-1] != self.in_features:
+            raise ModuleArgError(f"input has width {input.shape[-1] if input.dim() else None}, "
+                                 f"in_features is {self.in_features}")
+        w = self.weight
+        if input.device != w.device or input.device.type != "cuda":
+            raise ModuleArgError("input and the layer must be on the same GPU")
+        plan = self._plan(w.device, w.dtype)
+        lead = tuple(input.shape[:-1])
+        x = input.to(w.dtype).reshape(-1, self.in_features, 1).contiguous()
+        if torch.is_grad_enabled() and (x.requires_grad or w.requires_grad or
+                                        (self.bias is not None and self.bias.requires_grad)):
+            y = _PackedLinearFn.apply(plan, x, w, self.bias)
+        else:
+            b = None if self.bias is None else self.bias.detach().contiguous()
+            y = pma_linear_forward(plan, x.detach(), w.detach().contiguous(), b)
+        return y.reshape(lead + (self.out_features,))
+
+
+class _PackedLinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, plan, x, weight, bias):
+        w = weight.detach().contiguous()
+        b = None if bias is None else bias.detach().contiguous()
+        ctx.plan, ctx.has_bias = plan, bias is not None
+        ctx.save_for_backward(x.detach(), w)
+        return pma_linear_forward(plan, x.detach(), w, b)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        x, w = ctx.saved_tensors
+        gx, gw, gb = pma_linear_backward(ctx.plan, x, w, grad_out.contiguous(),
+                                         has_bias=ctx.has_bias)
+        return None, gx, gw, gb

@@ -231,6 +231,66 @@ pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query, const 
                         void *grad_k_w, void *grad_k_b, void *grad_v_w, void *grad_v_b,
                         void *grad_o_w, void *grad_o_b, hipStream_t stream);
 
+/* ---- PackedLinear on the same packed pairs ------------------------------ */
+
+/*
+ * The kpnn2 PackedMultiheadAttention page ("See also") describes PackedLinear
+ * as the same packed pairs with one trained scalar per edge, the same for
+ * every sample, information flowing from source to target. Read as a linear
+ * map whose (L x S) weight matrix holds w_e at each live pair (t_e, s_e) and
+ * zero elsewhere, applied to every sample b and channel c:
+ *
+ *   out[b, t, c] = bias[t] + sum over edges e into t of w_e x[b, s_e, c].
+ *
+ * channels = 1 is the nn.Linear-shaped layer (in_features = S nodes,
+ * out_features = L nodes); more channels apply the same map to each.
+ *
+ * pma_create_graph -- a plan for these calls only: pma_create's index rules
+ * and edge order (given pairs, then appended loops when add_self_loops), no
+ * attention sizes. The attention calls reject it with PMA_E_ARG. A plan
+ * from pma_create serves the PackedLinear calls as well.
+ */
+pma_status pma_create_graph(pma_plan **plan, const int64_t *source_index,
+                            const int64_t *target_index, int64_t nnz, int64_t query_features,
+                            int64_t key_features, int add_self_loops, pma_dtype dtype,
+                            hipStream_t stream);
+
+/*
+ * pma_linear_forward -- out = the map above.
+ *
+ *   batch, channels  B > 0 and C > 0.
+ *   x                DEVICE (B, S, C), plan dtype, contiguous.
+ *   weight           DEVICE (nnz) plan dtype: weight[i] belongs to edge i of
+ *                    the edge order (pma_edges).
+ *   bias             DEVICE (L) plan dtype, or NULL (no bias).
+ *   out              DEVICE (B, L, C) plan dtype. A target with no edge gets
+ *                    bias[t] (zero without bias).
+ *
+ * Sums are fp32, in each target's ascending-source order (pieces of long
+ * targets summed in order). Enqueued on `stream`; scratch for split targets
+ * is grown (blocking once) when a larger B * C needs it. Errors: PMA_E_NULL,
+ * PMA_E_SIZE, PMA_E_UNSUPPORTED (B * C beyond 2^31 - 1), PMA_E_OOM,
+ * PMA_E_DEVICE.
+ */
+pma_status pma_linear_forward(pma_plan *plan, int64_t batch, int64_t channels, const void *x,
+                              const void *weight, const void *bias, void *out,
+                              hipStream_t stream);
+
+/*
+ * pma_linear_backward -- gradients of sum(out * grad_out) for the same call:
+ *   grad_x[b, s, c]  = sum over edges e out of s of w_e grad_out[b, t_e, c]
+ *                      (zero for a source no edge reads), DEVICE (B, S, C);
+ *   grad_weight[i]   = sum over b, c of grad_out[b, t_i, c] x[b, s_i, c],
+ *                      DEVICE (nnz), edge order;
+ *   grad_bias[t]     = sum over b, c of grad_out[b, t, c], DEVICE (L), or
+ *                      NULL to skip it.
+ * The first call builds the plan's source-major index (blocking once).
+ * Errors as pma_linear_forward.
+ */
+pma_status pma_linear_backward(pma_plan *plan, int64_t batch, int64_t channels, const void *x,
+                               const void *weight, const void *grad_out, void *grad_x,
+                               void *grad_weight, void *grad_bias, hipStream_t stream);
+
 /* pma_destroy -- free the plan and everything it owns. NULL is a no-op.
    Waits for the device before freeing. */
 pma_status pma_destroy(pma_plan *plan);

@@ -110,3 +110,31 @@ def test_null_plan_calls():
     assert pma.STATUS[lib.pma_profile_read(None, ms.ctypes.data, calls.ctypes.data)] == "PMA_E_NULL"
     assert pma.STATUS[lib.pma_edges(None, None, None)] == "PMA_E_NULL"
     assert pma.STATUS[lib.pma_profile_stages(None, 1)] == "PMA_E_NULL"
+
+
+def test_create_graph_rejects():
+    lib = pma._load()
+    src = np.array([0, 1], np.int64)
+    tgt = np.array([1, 1], np.int64)
+    for args, expect in (((0, 2, 2), "PMA_E_INDEX_EMPTY"), ((2, 0, 2), "PMA_E_SIZE"),
+                         ((2, 2, 0), "PMA_E_SIZE")):
+        h = ctypes.c_void_p(1234)
+        n, L, S = args
+        st = lib.pma_create_graph(ctypes.byref(h), src.ctypes.data, tgt.ctypes.data, n, L, S, 0,
+                                  0, None)
+        assert pma.STATUS[st] == expect and h.value is None
+    h = ctypes.c_void_p(1234)
+    st = lib.pma_create_graph(ctypes.byref(h), src.ctypes.data, tgt.ctypes.data, 2, 2, 3, 1, 0,
+                              None)
+    assert pma.STATUS[st] == "PMA_E_SELF_LOOPS" and h.value is None
+    with pytest.raises(pma.PmaError) as e:
+        pma.pma_create_graph([0, 1], [1], 2, 2)
+    assert e.value.name == "PMA_E_ARG"
+
+
+def test_null_plan_linear_calls():
+    lib = pma._load()
+    z = ctypes.c_void_p(0x10)
+    assert pma.STATUS[lib.pma_linear_forward(None, 1, 1, z, z, None, z, None)] == "PMA_E_NULL"
+    assert pma.STATUS[lib.pma_linear_backward(None, 1, 1, z, z, z, z, z, None, None)] == \
+        "PMA_E_NULL"

@@ -117,3 +117,52 @@ def test_forward_rejects(call):
         m(q, k, v, **kw)
     # every case but the last is caught before the device check
     assert ("same GPU" in str(e.value)) == (call == "cpu")
+
+
+# ---- PackedLinear (CPU: construction and validation only) ----------------
+from graph_sparse_head_amd.module import PackedLinear  # noqa: E402
+
+
+def test_packed_linear_parameters():
+    m = PackedLinear([0, 2, 1, 0], [1, 1, 0, 2], 3, 4, generator=torch.Generator().manual_seed(0))
+    assert m.weight.shape == (4,) and m.bias.shape == (4,) and m.nnz == 4
+    assert m.in_features == 3 and m.out_features == 4
+    # weight of an edge into t and bias[t] lie within 1 / sqrt(in-degree of t)
+    deg = np.bincount(m.target_index.numpy(), minlength=4)
+    bound = 1 / np.sqrt(deg[m.target_index.numpy()])
+    assert (np.abs(m.weight.detach().numpy()) <= bound).all()
+    assert m.bias[3].item() == 0.0                      # target 3 has no edge
+    n = PackedLinear([0, 2, 1, 0], [1, 1, 0, 2], 3, 4, generator=torch.Generator().manual_seed(0))
+    assert torch.equal(m.weight, n.weight) and torch.equal(m.bias, n.bias)
+    nb = PackedLinear([0], [0], 1, 1, bias=False)
+    assert nb.bias is None
+
+
+def test_packed_linear_self_loops_and_edgelist():
+    m = PackedLinear([1], [0], 3, 3, add_self_loops=True)
+    assert m.source_index.tolist() == [1, 0, 1, 2] and m.target_index.tolist() == [0, 0, 1, 2]
+    e = PackedLinear.from_edgelist(["a", "b"], ["b", "c"])
+    assert e.nodes == ["a", "b", "c"] and e.source_index.tolist() == [0, 1]
+
+
+@pytest.mark.parametrize("kw", [
+    dict(source_index=[0, 0], target_index=[1, 1], in_features=2, out_features=2),
+    dict(source_index=[2], target_index=[0], in_features=2, out_features=2),
+    dict(source_index=[0], target_index=[0], in_features=0, out_features=2),
+    dict(source_index=[0], target_index=[0], in_features=2, out_features=3, add_self_loops=True),
+    dict(source_index=[0.0], target_index=[0], in_features=2, out_features=2),
+    dict(source_index=[0], target_index=[0], in_features=2, out_features=2, bias=1),
+])
+def test_packed_linear_rejects(kw):
+    with pytest.raises(ModuleArgError):
+        PackedLinear(**kw)
+
+
+def test_packed_linear_forward_rejects_cpu_and_width():
+    m = PackedLinear([0], [0], 2, 2)
+    with pytest.raises(ModuleArgError):
+        m(torch.zeros(3, 3))
+    with pytest.raises(ModuleArgError):
+        m(torch.zeros(3, 2, dtype=torch.int64))
+    with pytest.raises(ModuleArgError, match="same GPU"):
+        m(torch.zeros(3, 2))
