@@ -151,23 +151,26 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
     D = group_sum<LPH>(D);
     const float2 ml =
         *reinterpret_cast<const float2 *>(a.ml + (((int64_t)t * a.B + b) * a.H + h) * 2);
-    const T *Kb = reinterpret_cast<const T *>(a.k) + (int64_t)b * a.S * a.E + c * VEC;
-    const T *Vb = reinterpret_cast<const T *>(a.v) + (int64_t)b * a.S * a.E + c * VEC;
+    const T *Kb = reinterpret_cast<const T *>(a.k) + (int64_t)b * a.Skv * a.E + c * VEC;
+    const T *Vb = reinterpret_cast<const T *>(a.v) + (int64_t)b * a.Skv * a.E + c * VEC;
     const bool lead = (c & (LPH - 1)) == 0;
     float dq[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dq[i] = 0.f;
-    int s[kU], sn[kU];
+    int s[kU], sn[kU];   // sources (for the mask); rows come through kv_src
     uint4 kr[kU], vr[kU], kn[kU], vn[kU];
     auto fetch = [&](int p0, int (&ss)[kU], uint4 (&kq)[kU], uint4 (&vq)[kU]) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-            ss[u] = a.csr_src[p0 + u];
+        int r[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            kq[u] = ld16(Kb + (int64_t)ss[u] * a.E);
-            vq[u] = ld16(Vb + (int64_t)ss[u] * a.E);
+            ss[u] = a.csr_src[p0 + u];
+            r[u] = a.kv_src[p0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            kq[u] = ld16(Kb + (int64_t)r[u] * a.E);
+            vq[u] = ld16(Vb + (int64_t)r[u] * a.E);
         }
     };
     if (beg < end)
@@ -384,8 +387,9 @@ __global__ void __launch_bounds__(256) bwd_target_generic(const BwdArgs a)
         const int s = a.csr_src[p];
         float pe = 0.f, dz = 0.f;
         if (ml.y > 0.f && !masked(a, s, b)) {
-            const T *kr = K + ((int64_t)b * a.S + s) * a.E + h * d;
-            const T *vr = V + ((int64_t)b * a.S + s) * a.E + h * d;
+            const int64_t kvr = (int64_t)b * a.Skv + a.kv_src[p];
+            const T *kr = K + kvr * a.E + h * d;
+            const T *vr = V + kvr * a.E + h * d;
             float z = 0.f, dp = 0.f;
             for (int c = 0; c < d; ++c) {
                 z = fmaf(ld(q + c), ld(kr + c), z);

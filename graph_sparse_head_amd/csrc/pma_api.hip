@@ -432,6 +432,13 @@ struct SaveLayout {
     size_t q, k, v, mixed, ml, total;
 };
 
+// Whether a training forward projects keys and values only for the sources
+// some edge reads (then the save area holds n_kv key/value rows per sample).
+bool train_compact(const pma_plan *p)
+{
+    return p->g.n_kv < p->S && p->compact != 0;
+}
+
 SaveLayout save_layout(const pma_plan *p, int64_t B)
 {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -486,10 +493,13 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     // and value are one tensor and most sources are read: then one pass over
     // the tokens that writes q, k and v at once moves fewer bytes (a separate
     // key/value pass re-reads n_kv / S of the tokens; it pays below 3/5).
+    // A training forward decides from the plan alone (train_compact), so that
+    // the backward reads the saved keys and values the same way.
     const bool shared = query == key && key == value && L == S;
     const int64_t n_kv = p->g.n_kv;
-    const bool compact = !save && n_kv < S &&
-                         (p->compact >= 0 ? p->compact == 1 : (!shared || 5 * n_kv < 3 * S));
+    const bool compact = save ? train_compact(p)
+                              : n_kv < S && (p->compact >= 0 ? p->compact == 1
+                                                              : (!shared || 5 * n_kv < 3 * S));
     const int64_t S_ws = compact ? n_kv : S;   // key/value rows in the workspace
     const pma::Layout lay = pma::make_layout(save ? true : p->batch_first_ws, B, L, S_ws, E);
 
@@ -770,9 +780,14 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     a.H = (int)H;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)(E / H)));
     a.inv_sqrt_d = (float)(1.0 / sqrt((double)(E / H)));
+    // keys and values as the training forward saved them: n_kv rows per
+    // sample (read sources only) or all S
+    const bool compact = train_compact(p);
+    a.Skv = (int)(compact ? p->g.n_kv : S);
+    a.kv_src = compact ? p->g.csr_kv : p->g.csr_src;
     a.q = sb + sv.q;
     a.k = sb + sv.k;
-    a.v = sb + sv.v;
+    a.v = sb + sv.k + (size_t)B * a.Skv * E * es;
     a.mixed = sb + sv.mixed;
     a.ml = reinterpret_cast<const float *>(sb + sv.ml);
     a.dm = dm;

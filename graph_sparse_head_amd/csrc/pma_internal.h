@@ -143,6 +143,8 @@ struct BwdArgs {
     float scale_log2;    // log2(e) / sqrt(d): the forward's score scale
     float inv_sqrt_d;
     const void *q, *k, *v, *mixed;   // saved, batch-first, plan dtype
+    int Skv;                         // key/value rows per sample in the save area
+    const int32_t *kv_src;           // per CSR entry, its key/value row there
     const float *ml;                 // saved [L][B][H][2] (max, sum), base 2
     const void *dm;                  // (B, L, E) gradient reaching mixed, plan dtype
     const int32_t *row_ptr, *csr_src, *csc_ptr, *csc_tgt, *csc_pos;

@@ -166,3 +166,16 @@ def test_backward_full_graph_small_batch(cfg):
     # targets) at a batch the float64 gradient oracle finishes in seconds
     c = synth.gene(B=2) if cfg == "gene" else synth.bipartite(B=1)
     _grad_check(c, "qkv" if cfg == "gene" else "kv")
+
+
+@pytest.mark.parametrize("compact", ["0", "1"])
+@pytest.mark.parametrize("shared", ["none", "qkv"])
+def test_backward_read_sources_only(compact, shared, monkeypatch):
+    # half of the sources are never read: with PMA_COMPACT=1 the training
+    # forward saves keys and values for the read ones only
+    monkeypatch.setenv("PMA_COMPACT", compact)
+    c = synth.random_case(89, 3, 60, 60, 64, 4, 0.1, dtype="bf16", same_kv=shared != "none",
+                          same_qkv=shared == "qkv", name="bwd_compact")
+    keep = c.src % 2 == 0
+    c.src, c.tgt = c.src[keep], c.tgt[keep]
+    _grad_check(c, shared)
