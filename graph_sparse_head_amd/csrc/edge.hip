@@ -780,28 +780,68 @@ __global__ void __launch_bounds__(256) merge_generic(EdgeK a)
 }
 
 // need_weights: weight = exp2(score - max) / sum, written in edge order.
+// A workgroup takes 64 consecutive CSR positions for every sample: pairs
+// (position, sample) with the sample fastest read the stored scores and the
+// targets' (max, sum) contiguously; head-averaged weights then go through LDS
+// so that each sample's row is written with the position fastest (edges of
+// one target sit together in the edge order as well as in the CSR).
+constexpr int kWeightTile = 64;      // CSR positions per workgroup
+constexpr int kWeightSamples = 256;  // samples per workgroup (blockIdx.y: sample chunk)
+
+__device__ inline float edge_weight(float sc, float m, float l)
+{
+    return l > 0.f ? fast_exp2(sc - m) / l : 0.f;   // l = 0: every key of the target masked
+}
+
+// The H weights of one (edge, sample): scores sc[h], statistics st[2h] (max)
+// and st[2h + 1] (sum); 16-byte loads when H is a multiple of 4.
+template <typename F> __device__ inline void head_weights(const float *sc, const float *st, int H, F &&f)
+{
+    if ((H & 3) == 0) {
+        for (int h = 0; h < H; h += 4) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(sc + h);
+            const float4 a = *reinterpret_cast<const float4 *>(st + 2 * h);
+            const float4 b = *reinterpret_cast<const float4 *>(st + 2 * h + 4);
+            f(h, edge_weight(s4.x, a.x, a.y));
+            f(h + 1, edge_weight(s4.y, a.z, a.w));
+            f(h + 2, edge_weight(s4.z, b.x, b.y));
+            f(h + 3, edge_weight(s4.w, b.z, b.w));
+        }
+    } else {
+        for (int h = 0; h < H; ++h)
+            f(h, edge_weight(sc[h], st[2 * h], st[2 * h + 1]));
+    }
+}
+
 __global__ void __launch_bounds__(256) weights_kernel(EdgeK a)
 {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    extern __shared__ float wt[];   // [samples of the chunk][kWeightTile] head averages
     const int B = a.B, H = a.H;
-    if (idx >= a.nnz * B)
+    const int64_t p0 = (int64_t)blockIdx.x * kWeightTile;
+    const int b0 = blockIdx.y * kWeightSamples;
+    const int np = (int)(a.nnz - p0 < kWeightTile ? a.nnz - p0 : kWeightTile);
+    const int nb = B - b0 < kWeightSamples ? B - b0 : kWeightSamples;
+    for (int i = threadIdx.x; i < np * nb; i += blockDim.x) {
+        const int pl = i / nb, bl = i - pl * nb, b = b0 + bl;
+        const int64_t p = p0 + pl;
+        const int t = a.csr_tgt[p];
+        const float *sc = a.scores + (p * B + b) * H;
+        const float *st = a.stat_ml + ((int64_t)t * B + b) * H * 2;
+        if (a.average) {
+            float sum = 0.f;
+            head_weights(sc, st, H, [&](int, float w) { sum += w; });
+            wt[bl * kWeightTile + pl] = sum / (float)H;
+        } else {
+            float *w = a.weights + ((int64_t)b * a.nnz + a.csr_eid[p]) * H;
+            head_weights(sc, st, H, [&](int h, float v) { w[h] = v; });
+        }
+    }
+    if (!a.average)
         return;
-    const int64_t p = idx / B;
-    const int b = (int)(idx - p * B);
-    const int t = a.csr_tgt[p];
-    const int64_t e = a.csr_eid[p];
-    const float *sc = a.scores + (p * B + b) * H;
-    const float *st = a.stat_ml + ((int64_t)t * B + b) * H * 2;
-    if (a.average) {
-        float sum = 0.f;
-        for (int h = 0; h < H; ++h)
-            if (st[2 * h + 1] > 0.f)   // l = 0: every key of the target masked
-                sum += fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1];
-        a.weights[(int64_t)b * a.nnz + e] = sum / (float)H;
-    } else {
-        float *w = a.weights + ((int64_t)b * a.nnz + e) * H;
-        for (int h = 0; h < H; ++h)
-            w[h] = st[2 * h + 1] > 0.f ? fast_exp2(sc[h] - st[2 * h]) / st[2 * h + 1] : 0.f;
+    __syncthreads();
+    for (int i = threadIdx.x; i < np * nb; i += blockDim.x) {
+        const int bl = i / np, pl = i - bl * np;
+        a.weights[(int64_t)(b0 + bl) * a.nnz + a.csr_eid[p0 + pl]] = wt[bl * kWeightTile + pl];
     }
 }
 
@@ -1116,8 +1156,11 @@ pma_status launch_merge(const EdgeArgs &x, hipStream_t s)
 pma_status launch_weights(const EdgeArgs &x, hipStream_t s)
 {
     EdgeK k = make_k(x);
-    const int64_t n = k.nnz * k.B;
-    weights_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
+    const int64_t chunk_b = k.B < kWeightSamples ? k.B : kWeightSamples;
+    const size_t lds = x.average ? (size_t)chunk_b * kWeightTile * sizeof(float) : 0;
+    const dim3 g((unsigned)((k.nnz + kWeightTile - 1) / kWeightTile),
+                 (unsigned)((k.B + kWeightSamples - 1) / kWeightSamples));
+    weights_kernel<<<g, 256, lds, s>>>(k);
     return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
