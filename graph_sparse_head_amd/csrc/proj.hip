@@ -121,6 +121,10 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
     constexpr int PITCH = E * (int)sizeof(T) + 16;       // bytes per staged row
     constexpr int CPR = E * (int)sizeof(T) / 16;         // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;                        // rows stored per instruction
+    // bf16 results go through a per-wavefront LDS staging area so that stores
+    // are whole 16-byte chunks of whole rows; an fp32 lane already holds 16
+    // contiguous bytes of its row and stores them directly.
+    constexpr bool STAGE = sizeof(T) == 2;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int nblk = a.nblk;
     char *wl = lds;                                      // nblk * NT * NKS KB
@@ -168,6 +172,13 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
         const int cr = lane % CPR, rr = lane / CPR;
         int64_t sb0, si0;
         decompose(a, row0 + rr, sb0, si0);
+        // unstaged: (sample, token) of the row each row group's lane holds
+        int64_t db[RG], di[RG];
+        if constexpr (!STAGE) {
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+                decompose(a, row0 + rg * 16 + lr, db[rg], di[rg]);
+        }
         for (int blk = 0; blk < nblk; ++blk) {
             const ProjOut &o = a.out[blk];
             const T *bias = reinterpret_cast<const T *>(o.b);
@@ -210,18 +221,21 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
                 }
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
-                    char *d = stage + (rg * 16 + lr) * PITCH + n * (int)sizeof(T);
-                    if constexpr (sizeof(T) == 2) {
+                    if constexpr (STAGE) {
+                        char *d = stage + (rg * 16 + lr) * PITCH + n * (int)sizeof(T);
                         uint2 pk;
                         pk.x = pack_bf16(acc[rg][0] + bv[0], acc[rg][1] + bv[1]);
                         pk.y = pack_bf16(acc[rg][2] + bv[2], acc[rg][3] + bv[3]);
                         *reinterpret_cast<uint2 *>(d) = pk;
-                    } else {
+                    } else if (row0 + rg * 16 + lr < a.rows) {
+                        T *d = reinterpret_cast<T *>(o.dst) + db[rg] * o.sb + di[rg] * o.si + n;
                         *reinterpret_cast<float4 *>(d) = make_float4(
                             acc[rg][0] + bv[0], acc[rg][1] + bv[1], acc[rg][2] + bv[2], acc[rg][3] + bv[3]);
                     }
                 }
             }
+            if constexpr (!STAGE)
+                continue;
             // a wavefront reads back only its own staged rows (LDS operations
             // of one wavefront complete in order)
             T *dst = reinterpret_cast<T *>(o.dst) + cr * (16 / (int)sizeof(T));
@@ -302,7 +316,7 @@ hipError_t run_mfma(const ProjArgs &a, hipStream_t s)
     constexpr int NKS = K / Elem<T>::kStep;
     constexpr int PITCH = K * (int)sizeof(T) + 16;
     const size_t wbytes = (size_t)a.nblk * (K / 16) * NKS * 1024;
-    const size_t lds = wbytes + (size_t)WAVES * RG * 16 * PITCH;
+    const size_t lds = wbytes + (sizeof(T) == 2 ? (size_t)WAVES * RG * 16 * PITCH : 0);
     if (lds > (size_t)kLdsBytes) {
         // weights of all blocks do not fit: one launch per output block
         for (int j = 0; j < a.nblk; ++j) {
