@@ -331,26 +331,51 @@ __global__ void __launch_bounds__(256) bwd_merge_fast(const BwdArgs a, int sourc
     const int nout = sources ? 2 : 1;
     const int width = nout * a.E;
     const float *part = sources ? a.part_kv : a.part_q;
-    for (int o = 0; o < nout; ++o) {
-        float acc[VEC];
+    // both outputs at once; slots loaded kM at a time and added in slot order
+    constexpr int kM = 4;
+    float acc[2][VEC];
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
-            acc[j] = 0.f;
-        for (int k = 0; k < count; ++k) {
-            const float *src = part + ((int64_t)(slot0 + k) * a.B + b) * width + o * a.E + c * VEC;
+            acc[o][j] = 0.f;
+    const float *base = part + ((int64_t)slot0 * a.B + b) * width + c * VEC;
+    const int64_t sstride = (int64_t)a.B * width;
+    for (int k0 = 0; k0 < count; k0 += kM) {
+        float4 v[kM][2][VEC / 4];
 #pragma unroll
-            for (int j = 0; j < VEC; j += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(src + j);
-                acc[j] += v.x;
-                acc[j + 1] += v.y;
-                acc[j + 2] += v.z;
-                acc[j + 3] += v.w;
+        for (int u = 0; u < kM; ++u) {
+            if (k0 + u < count) {
+#pragma unroll
+                for (int o = 0; o < 2; ++o)
+                    if (o < nout)
+#pragma unroll
+                        for (int j = 0; j < VEC / 4; ++j)
+                            v[u][o][j] = *reinterpret_cast<const float4 *>(base + (k0 + u) * sstride +
+                                                                          o * a.E + 4 * j);
             }
         }
+#pragma unroll
+        for (int u = 0; u < kM; ++u) {
+            if (k0 + u < count) {
+#pragma unroll
+                for (int o = 0; o < 2; ++o)
+                    if (o < nout)
+#pragma unroll
+                        for (int j = 0; j < VEC / 4; ++j) {
+                            acc[o][4 * j] += v[u][o][j].x;
+                            acc[o][4 * j + 1] += v[u][o][j].y;
+                            acc[o][4 * j + 2] += v[u][o][j].z;
+                            acc[o][4 * j + 3] += v[u][o][j].w;
+                        }
+            }
+        }
+    }
+    for (int o = 0; o < nout; ++o) {
         T *dst = sources ? reinterpret_cast<T *>(o == 0 ? a.dk : a.dv) +
                                ((int64_t)b * a.S + row_id) * a.E
                          : reinterpret_cast<T *>(a.dq) + ((int64_t)b * a.L + row_id) * a.E;
-        store_vec(dst + c * VEC, acc);
+        store_vec(dst + c * VEC, acc[o]);
     }
 }
 
