@@ -22,8 +22,8 @@
 // dW = dy^T x, db = column sums of dy (wgrad below), both on the matrix cores.
 //
 // Layouts (batch-first, plan dtype T unless noted): q, mixed, dm, dq (B, L, E);
-// k, v, dk, dv (B, S, E); ml [L][B][H][2] fp32; P and DZ [nnz][B][H] fp32 by
-// target-grouped position. Gradient tensors are stored in T and accumulated
+// k, v, dk, dv (B, S, E); ml [L][B][H][2] fp32; (p, dz) pairs [nnz][B][H] by
+// target-grouped position (bf16 pairs for bf16 plans, fp32 pairs otherwise). Gradient tensors are stored in T and accumulated
 // in fp32.
 #include "pma_internal.h"
 
@@ -92,6 +92,26 @@ __device__ inline bool masked(const BwdArgs &a, int s, int b)
 {
     return a.kpm_bits &&
            ((a.kpm_bits[(int64_t)s * a.kpm_words + (b >> 6)] >> (b & 63)) & 1u);
+}
+
+// Per (edge, sample, head): the weight p and the score gradient dz, stored
+// together: a bf16 pair (round to nearest even) for bf16 plans, an fp32 pair
+// otherwise.
+template <typename T> __device__ inline void put_pz(void *pz, int64_t o, float p, float dz)
+{
+    if constexpr (sizeof(T) == 2)
+        reinterpret_cast<uint32_t *>(pz)[o] = pack_bf16(p, dz);
+    else
+        reinterpret_cast<float2 *>(pz)[o] = make_float2(p, dz);
+}
+template <typename T> __device__ inline float2 get_pz(const void *pz, int64_t o)
+{
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = reinterpret_cast<const uint32_t *>(pz)[o];
+        return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    } else {
+        return reinterpret_cast<const float2 *>(pz)[o];
+    }
 }
 
 constexpr int kU = 4;   // edges whose rows are loaded together
@@ -204,8 +224,7 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
                     dq[i] = fmaf(dz, kk[i], dq[i]);
                 if (lead) {
                     const int64_t o = ((int64_t)p * a.B + b) * a.H + h;
-                    a.P[o] = pe;
-                    a.DZ[o] = dz;
+                    put_pz<T>(a.PZ, o, pe, dz);
                 }
             }
         }
@@ -262,8 +281,9 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t o = ((int64_t)pos[u] * a.B + b) * a.H + h;
-            pp[u] = a.P[o];
-            zz[u] = a.DZ[o];
+            const float2 v = get_pz<T>(a.PZ, o);
+            pp[u] = v.x;
+            zz[u] = v.y;
             qq[u] = ld16(Qb + (int64_t)t[u] * a.E);
             mm[u] = ld16(Mb + (int64_t)t[u] * a.E);
         }
@@ -429,8 +449,7 @@ __global__ void __launch_bounds__(256) bwd_target_generic(const BwdArgs a)
             }
         }
         const int64_t o = ((int64_t)p * a.B + b) * a.H + h;
-        a.P[o] = pe;
-        a.DZ[o] = dz;
+        put_pz<T>(a.PZ, o, pe, dz);
     }
     T *out = reinterpret_cast<T *>(a.dq) + row;
     for (int c = 0; c < 64; ++c) {
@@ -460,8 +479,9 @@ __global__ void __launch_bounds__(256) bwd_source_generic(const BwdArgs a)
         const int t = a.csc_tgt[j];
         const int64_t o = ((int64_t)a.csc_pos[j] * a.B + b) * a.H + h;
         const int64_t r = ((int64_t)b * a.L + t) * a.E + c;
-        dk = fmaf(a.DZ[o], ld(Q + r), dk);
-        dv = fmaf(a.P[o], ld(DM + r), dv);
+        const float2 v = get_pz<T>(a.PZ, o);
+        dk = fmaf(v.y, ld(Q + r), dk);
+        dv = fmaf(v.x, ld(DM + r), dv);
     }
     const int64_t w = ((int64_t)b * a.S + s) * a.E + c;
     st(reinterpret_cast<T *>(a.dk) + w, dk * a.inv_sqrt_d);

@@ -721,17 +721,17 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
             return fail(st, "%s", err);
     }
 
-    // scratch: dm, dq, dk, dv (plan dtype), per-edge P and DZ, piece
+    // scratch: dm, dq, dk, dv (plan dtype), per-edge (p, dz) pairs, piece
     // partials and weight-gradient partials (fp32)
     const pma_dtype dt = p->dtype;
     const size_t es = dt == PMA_BF16 ? 2 : 4;
     const int64_t RLr = B * L, RSr = B * S;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t b_dm = up(RLr * E * es), b_dkv = up(RSr * E * es);
-    const size_t b_pz = up((size_t)nnz * B * H * sizeof(float));
+    const size_t b_pz = up((size_t)nnz * B * H * 2 * es);   // (p, dz) pairs
     const size_t b_piece = up(pma::bwd_piece_scratch(p->g, B, E));
     const size_t b_wg = up(pma::wgrad_scratch(E, 4, RLr > RSr ? RLr : RSr));
-    const size_t need = 2 * b_dm + 2 * b_dkv + 2 * b_pz + b_piece + b_wg;
+    const size_t need = 2 * b_dm + 2 * b_dkv + b_pz + b_piece + b_wg;
     if (need > p->bw_bytes) {
         hipError_t e = hipStreamSynchronize(stream);
         if (p->bw)
@@ -752,8 +752,7 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         return r;
     };
     void *dm = take(b_dm), *dq = take(b_dm), *dk = take(b_dkv), *dv = take(b_dkv);
-    float *P = reinterpret_cast<float *>(take(b_pz));
-    float *DZ = reinterpret_cast<float *>(take(b_pz));
+    void *PZ = take(b_pz);
     float *part = reinterpret_cast<float *>(take(b_piece));
     float *wpart = reinterpret_cast<float *>(take(b_wg));
 
@@ -825,8 +824,7 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         a.kpm_bits = p->kpm_bits;
         a.kpm_words = (int)((B + 63) / 64);
     }
-    a.P = P;
-    a.DZ = DZ;
+    a.PZ = PZ;
     a.part_q = part;
     a.part_kv = part + (size_t)gd.n_slots * B * E;
     a.dq = dq;

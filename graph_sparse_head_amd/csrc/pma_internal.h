@@ -156,7 +156,7 @@ struct BwdArgs {
     int64_t n_ttasks, n_tsplit, n_stasks, n_ssplit;
     const uint64_t *kpm_bits;        // packed mask or nullptr
     int kpm_words;
-    float *P, *DZ;                   // [nnz][B][H] scratch
+    void *PZ;                        // [nnz][B][H] (p, dz) pairs: bf16 for bf16 plans, fp32 else
     float *part_q;                   // [target slot][B][E] partial dq
     float *part_kv;                  // [source slot][B][2E] partial dk, dv
     void *dq, *dk, *dv;              // (B, L, E), (B, S, E), (B, S, E), plan dtype
