@@ -28,7 +28,7 @@ pma_status fail(pma_status st, const char *fmt, ...)
     return st;
 }
 
-constexpr int kChunk = 256;           // most edges one piece of a target covers
+constexpr int kChunk = 256;           // shortest automatic piece length (edges)
 constexpr int64_t kI32 = 2147483647;  // device edge indices are int32
 
 struct EventPair {
@@ -243,7 +243,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     p->nnz = (int64_t)p->h_src.size();
     p->dtype = dtype;
     // Tuning knobs, read once per plan (defaults are the measured best):
-    //   PMA_CHUNK      most edges per piece of a target (1..65535)
+    //   PMA_CHUNK      most edges per piece of a target (1..65535; default
+    //                  automatic, see below)
     //   PMA_FUSE_OUT   0: out_proj as a separate kernel
     //   PMA_XCD_MAP    1 / 0: force or forbid one sample group per XCD
     //   PMA_NT         1 / 0: non-temporal or cached q / mixed streams
@@ -253,6 +254,19 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_COMPACT    1 / 0: force or forbid projecting keys and values only
     //                  for the sources some edge reads
     //   PMA_BWD_CHUNK  n: most edges of one source piece in the backward pass
+    // Piece length: a target is split only when it has far more edges than
+    // the average target (16x, rounded up to a power of two, at least 256).
+    // Splitting balances graphs with a few very long rows among many short
+    // ones; where rows are uniformly long, whole rows avoid the partial
+    // results and the merge (measured on MI355X: gene-like graphs best at
+    // 256, pathway maps with up to 500 members per row best unsplit).
+    {
+        const double avg = (double)p->nnz / (double)L;
+        int c = kChunk;
+        while (c < 65536 && c < 16.0 * avg)
+            c <<= 1;
+        p->chunk = c > 65535 ? 65535 : c;
+    }
     if (const char *ev = getenv("PMA_CHUNK")) {
         const long c = strtol(ev, nullptr, 10);
         if (c >= 1 && c <= 65535)

@@ -108,8 +108,9 @@ def test_leading_axes(dt):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("deg", [65, 300, 1500])
-def test_split_targets(dt, deg):
+def test_split_targets(dt, deg, monkeypatch):
     """Targets above the plan's chunk are split into pieces and merged."""
+    monkeypatch.setenv("PMA_CHUNK", "256")
     rng = np.random.default_rng(deg)
     L, S, B, E, H = 40, 2000, 3, 64, 4
     src, tgt = [], []
@@ -252,3 +253,20 @@ def test_wavefront_walks_pieces(knobs, dt, monkeypatch):
         monkeypatch.setenv(k, v)
     c = synth.random_case(52, 4, 6000, 6000, 64, 4, 0.0015, dtype=dt, name="walk")
     _full_check(c, need_weights=True, average=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "complete", "gene", "bipartite", "large"])
+def test_automatic_piece_length(name):
+    # a target is split only above 16x the average in-degree (a power of two,
+    # at least 256)
+    c = synth.make_config(name)
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H, add_self_loops=c.add_self_loops,
+                          dtype=c.dtype)
+    try:
+        info = pma.pma_plan_info(plan)
+        want = 256
+        while want < 16 * plan.nnz / c.L:
+            want *= 2
+        assert info["chunk"] == min(want, 65535)
+    finally:
+        pma.pma_destroy(plan)
