@@ -578,15 +578,32 @@ __global__ void __launch_bounds__(WAVES * 64) bwd_rowmm(const RowMM a)
                 }
             }
             // lane holds output channels nt*16 + 4*lg + i of row lr
-            char *d = stage + lr * PITCH + (nt * 16 + 4 * lg) * (int)sizeof(T);
             if constexpr (sizeof(T) == 2) {
+                char *d = stage + lr * PITCH + (nt * 16 + 4 * lg) * (int)sizeof(T);
                 uint2 pk;
                 pk.x = pack_bf16(acc[0], acc[1]);
                 pk.y = pack_bf16(acc[2], acc[3]);
                 *reinterpret_cast<uint2 *>(d) = pk;
-            } else {
-                *reinterpret_cast<float4 *>(d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            } else if (row0 + lr < a.rows) {
+                // fp32: the lane's 16 contiguous bytes go straight out
+                float4 *out = reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.y) +
+                                                         (row0 + lr) * E + nt * 16 + 4 * lg);
+                float4 v = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                if (a.accumulate) {
+                    const float4 o = *out;
+                    v = make_float4(v.x + o.x, v.y + o.y, v.z + o.z, v.w + o.w);
+                }
+                *out = v;
             }
+        }
+        if constexpr (sizeof(T) == 4) {
+            if (next < ntiles) {
+#pragma unroll
+                for (int j = 0; j < NIN; ++j)
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) xf[j][ks] = xn[j][ks];
+            }
+            continue;
         }
         // a wavefront reads back only its own staged rows
         T *dst = reinterpret_cast<T *>(a.y) + cr * (16 / (int)sizeof(T));
@@ -915,8 +932,10 @@ constexpr int kRowWaves = 8;
 template <typename T, int E, int NIN>
 constexpr size_t rowmm_lds()
 {
+    // bf16 rows are staged in LDS for whole-row 16-byte stores; fp32 lanes
+    // store their 16 bytes directly
     return (size_t)NIN * (E / 16) * (E / Frag<T>::kStep) * 1024 +
-           (size_t)kRowWaves * 16 * (E * sizeof(T) + 16);
+           (sizeof(T) == 2 ? (size_t)kRowWaves * 16 * (E * sizeof(T) + 16) : 0);
 }
 
 template <typename T, int E, int NIN>

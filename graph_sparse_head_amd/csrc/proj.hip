@@ -383,6 +383,11 @@ pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s
     } else {
         if (E == 64)
             e = run_mfma<float, 64, 1, 8>(a, s);
+        else if (E == 128 && a.rows >= (int64_t)cu_count() * 16 * 16 * 2)
+            // 64 KB of weights per output block leave room for one or two
+            // workgroups per CU: 16 wavefronts each keep the matrix cores busy
+            // when there are enough rows for every CU
+            e = run_mfma<float, 128, 1, 16>(a, s);
         else if (E == 128)
             e = run_mfma<float, 128, 1, 8>(a, s);
         else
