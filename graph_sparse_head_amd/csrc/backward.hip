@@ -27,6 +27,8 @@
 // in fp32.
 #include "pma_internal.h"
 
+#include <algorithm>
+
 namespace pma {
 namespace {
 
@@ -246,16 +248,28 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
         store_f32(a.part_q + ((int64_t)slot * a.B + b) * a.E + c * VEC, dq);
 }
 
+// With UNI and bands the pieces run band by band on fixed XCDs: workgroups are dealt to
+// the 8 XCDs round-robin, so workgroup i serves band i mod 8, and the pieces
+// of one band (sorted by target) gather their target rows through one L2.
 template <typename T, int LPH, bool UNI>
 __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
 {
     constexpr int VEC = Vec<T>::N;
     const int CPR = a.E / VEC;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t idx, base = 0;
+    if (UNI && a.banded) {
+        const int band = blockIdx.x % kBands;
+        base = a.s_band_off[band];
+        idx = (int64_t)(blockIdx.x / kBands) * blockDim.x + threadIdx.x;
+        if (idx >= (a.s_band_off[band + 1] - base) * a.B * CPR)
+            return;   // whole wavefront (a piece's threads fill wavefronts)
+    } else {
+        idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    }
     const int64_t gb = idx / CPR;
     const int c = (int)(idx - gb * CPR);
-    int64_t task = gb / a.B;
-    const int b = (int)(gb - task * a.B);
+    int64_t task = base + gb / a.B;
+    const int b = (int)(gb - (task - base) * a.B);
     if (UNI)
         task = __builtin_amdgcn_readfirstlane((int)task);
     if (task >= a.n_stasks)
@@ -1020,11 +1034,21 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
         const int64_t nt = a.n_ttasks * a.B * cpr, ns = a.n_stasks * a.B * cpr;
         // a piece's lanes fill whole wavefronts: wavefront-uniform indices
         const bool uni = ((int64_t)a.B * cpr) % 64 == 0;
+        // source pass with UNI: kBands interleaved runs of workgroups
+        int64_t per_band = 0;
+        for (int k = 0; k < kBands; ++k) {
+            const int64_t th = (a.s_band_off[k + 1] - a.s_band_off[k]) * a.B * cpr;
+            per_band = std::max(per_band, (th + 255) / 256);
+        }
+        const unsigned gs_band = (unsigned)(per_band * kBands);
 #define PMA_BWD_EDGE(L_)                                                            \
     case L_:                                                                       \
         if (uni) {                                                                 \
             bwd_target_fast<T, L_, true><<<grid(nt), 256, 0, s>>>(a);              \
-            bwd_source_fast<T, L_, true><<<grid(ns), 256, 0, s>>>(a);              \
+            if (a.banded)                                                          \
+                bwd_source_fast<T, L_, true><<<gs_band, 256, 0, s>>>(a);           \
+            else                                                                   \
+                bwd_source_fast<T, L_, true><<<grid(ns), 256, 0, s>>>(a);          \
         } else {                                                                   \
             bwd_target_fast<T, L_, false><<<grid(nt), 256, 0, s>>>(a);             \
             bwd_source_fast<T, L_, false><<<grid(ns), 256, 0, s>>>(a);             \

@@ -527,8 +527,146 @@ __global__ void csc_fill(const int32_t *perm, const int32_t *csr_tgt, const int3
     }
 }
 
-pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t stream,
-                     char *err, size_t errlen)
+// ---- banded source pieces --------------------------------------------------
+// Sources with at least kBandMinDeg edges are cut at band boundaries, so that
+// each of their pieces gathers target rows of one band only.
+constexpr int kBandMinDeg = 64;
+
+// band_start[k]: the first target whose CSR offset reaches ceil(k nnz / kBands).
+__global__ void band_bounds_kernel(const int32_t *row_ptr, int64_t L, int64_t nnz,
+                                   int32_t *band_start)
+{
+    const int k = threadIdx.x;
+    if (k > kBands)
+        return;
+    if (k == 0 || k == kBands) {
+        band_start[k] = k == 0 ? 0 : (int32_t)L;
+        return;
+    }
+    const int64_t goal = (nnz * k + kBands - 1) / kBands;
+    int64_t lo = 0, hi = L;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (row_ptr[mid] >= goal)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    band_start[k] = (int32_t)lo;
+}
+
+// first j in [b, e) with tgt[j] >= t (tgt ascending there)
+__device__ inline int64_t lower_bound_t(const int32_t *tgt, int64_t b, int64_t e, int32_t t)
+{
+    while (b < e) {
+        const int64_t mid = (b + e) >> 1;
+        if (tgt[mid] >= t)
+            e = mid;
+        else
+            b = mid + 1;
+    }
+    return b;
+}
+
+__device__ inline int64_t pieces_of(int64_t len, int chunk)
+{
+    return len > chunk ? (len + chunk - 1) / chunk : 1;
+}
+
+__global__ void src_piece_count(const int32_t *csc_ptr, const int32_t *csc_tgt,
+                                const int32_t *band_start, int64_t S, int chunk, int32_t *n_piece,
+                                int32_t *n_slot, int32_t *is_split, int32_t *n_long)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= S)
+        return;
+    const int64_t b = csc_ptr[s], e = csc_ptr[s + 1], g = e - b;
+    if (g >= kBandMinDeg)
+        atomicAdd(n_long, 1);
+    int64_t n = 0;
+    if (g < kBandMinDeg) {
+        n = pieces_of(g, chunk);
+    } else {
+        for (int k = 0; k < kBands; ++k) {
+            const int64_t lo = lower_bound_t(csc_tgt, b, e, band_start[k]);
+            const int64_t hi = lower_bound_t(csc_tgt, lo, e, band_start[k + 1]);
+            if (hi > lo)
+                n += pieces_of(hi - lo, chunk);
+        }
+    }
+    n_piece[s] = (int32_t)n;
+    n_slot[s] = n > 1 ? (int32_t)n : 0;
+    is_split[s] = n > 1 ? 1 : 0;
+}
+
+// Pieces of source s at piece_base[s]: per band segment, ceil(len / chunk)
+// even parts in target order. Sort key: band (L + 1), plus first target + 1
+// for the pieces of long sources (short sources keep source order, first).
+__global__ void src_piece_fill(const int32_t *csc_ptr, const int32_t *csc_tgt,
+                               const int32_t *band_start, int64_t S, int64_t L, int chunk,
+                               int banded,
+                               const int32_t *piece_base, const int32_t *slot_base,
+                               const int32_t *split_base, int32_t *u_source, int32_t *u_begin,
+                               int32_t *u_end, int32_t *u_slot, int32_t *u_key,
+                               int32_t *ss_source, int32_t *ss_slot0, int32_t *ss_count)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= S)
+        return;
+    const int64_t b = csc_ptr[s], e = csc_ptr[s + 1], g = e - b;
+    const int64_t pb = piece_base[s];
+    int64_t j = 0;
+    auto emit = [&](int64_t sb, int64_t se, int band, bool by_target) {
+        const int64_t len = se - sb, n = pieces_of(len, chunk);
+        for (int64_t i = 0; i < n; ++i) {
+            const int64_t pbeg = sb + (i * len) / n, pend = sb + ((i + 1) * len) / n;
+            u_source[pb + j] = (int32_t)s;
+            u_begin[pb + j] = (int32_t)pbeg;
+            u_end[pb + j] = (int32_t)pend;
+            u_key[pb + j] = (int32_t)(band * (L + 1) + (by_target && pend > pbeg ? csc_tgt[pbeg] + 1 : 0));
+            ++j;
+        }
+    };
+    if (g < kBandMinDeg)   // short rows: spread over the bands, source order
+        emit(b, e, banded ? (int)(s % kBands) : 0, false);
+    else {
+        for (int k = 0; k < kBands; ++k) {
+            const int64_t lo = lower_bound_t(csc_tgt, b, e, band_start[k]);
+            const int64_t hi = lower_bound_t(csc_tgt, lo, e, band_start[k + 1]);
+            if (hi > lo)
+                emit(lo, hi, k, true);
+        }
+    }
+    for (int64_t i = 0; i < j; ++i)
+        u_slot[pb + i] = j > 1 ? (int32_t)(slot_base[s] + i) : -1;
+    if (j > 1) {
+        const int32_t k = split_base[s];
+        ss_source[k] = (int32_t)s;
+        ss_slot0[k] = slot_base[s];
+        ss_count[k] = (int32_t)j;
+    }
+}
+
+// band_off[k] = first sorted piece whose key is at least k (L + 1)
+__global__ void band_off_kernel(const int32_t *key, int64_t n, int64_t L, int32_t *band_off)
+{
+    const int k = threadIdx.x;
+    if (k > kBands)
+        return;
+    const int64_t goal = (int64_t)k * (L + 1);
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (key[mid] >= goal)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    band_off[k] = (int32_t)lo;
+}
+
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
+                     hipStream_t stream, char *err, size_t errlen)
 {
     pma_status st = PMA_OK;
     const size_t i4 = sizeof(int32_t);
@@ -539,27 +677,31 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t
     int32_t *perm = nullptr, *perm_tmp = nullptr, *counts = nullptr, *scan_tmp = nullptr,
             *deg = nullptr, *small = nullptr, *n_piece = nullptr, *n_slot = nullptr,
             *is_split = nullptr, *piece_base = nullptr, *slot_base = nullptr,
-            *split_base = nullptr, *t_split = nullptr, *t_key = nullptr;
-    int32_t h_small[8] = {0};
+            *split_base = nullptr, *band_start = nullptr;
+    int32_t *u_source = nullptr, *u_begin = nullptr, *u_end = nullptr, *u_slot = nullptr,
+            *u_key = nullptr, *s_key = nullptr, *tperm = nullptr, *tperm_tmp = nullptr,
+            *sc = nullptr;
+    int32_t h_small[8 + kBands + 1] = {0};
     PMA_TRY(hipMalloc(&perm, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMalloc(&perm_tmp, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMalloc(&counts, count_len * i4));
     PMA_TRY(hipMalloc(&scan_tmp, scan_len * i4));
     PMA_TRY(hipMalloc(&deg, S * i4));
-    PMA_TRY(hipMalloc(&small, 8 * i4));
+    PMA_TRY(hipMalloc(&small, (8 + kBands + 1) * i4));
     PMA_TRY(hipMalloc(&n_piece, S * i4));
     PMA_TRY(hipMalloc(&n_slot, S * i4));
     PMA_TRY(hipMalloc(&is_split, S * i4));
     PMA_TRY(hipMalloc(&piece_base, S * i4));
     PMA_TRY(hipMalloc(&slot_base, S * i4));
     PMA_TRY(hipMalloc(&split_base, S * i4));
+    PMA_TRY(hipMalloc(&band_start, (kBands + 1) * i4));
     PMA_TRY(hipMalloc(&g->csc_ptr, (S + 1) * i4));
     PMA_TRY(hipMalloc(&g->csc_tgt, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMemsetAsync(g->csc_tgt + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMalloc(&g->csc_eid, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMemsetAsync(g->csc_eid + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMemsetAsync(deg, 0, S * i4, stream));
-    PMA_TRY(hipMemsetAsync(small, 0, 8 * i4, stream));
+    PMA_TRY(hipMemsetAsync(small, 0, (8 + kBands + 1) * i4, stream));
     iota_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, nnz);
     PMA_TRY(radix_sort_perm(g->csr_src, bits_for(S - 1), perm, perm_tmp, nnz, counts, scan_tmp,
                             stream));
@@ -570,9 +712,11 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t
     PMA_TRY(scan_exclusive(deg, g->csc_ptr, S, g->csc_ptr + S, scan_tmp, stream));
     g->csc_pos = perm;   // kept
     perm = nullptr;
-    // pieces per source, as for targets
-    split_count_kernel<<<grid_for(S, 256), 256, 0, stream>>>(deg, S, chunk, n_piece, n_slot,
-                                                             is_split, small + 4);
+    // pieces per source: band segments, each in pieces of at most chunk
+    band_bounds_kernel<<<1, 64, 0, stream>>>(g->row_ptr, L, nnz, band_start);
+    src_piece_count<<<grid_for(S, 256), 256, 0, stream>>>(g->csc_ptr, g->csc_tgt, band_start, S,
+                                                          chunk, n_piece, n_slot, is_split,
+                                                          small + 4);
     PMA_TRY(scan_exclusive(n_piece, piece_base, S, small + 1, scan_tmp, stream));
     PMA_TRY(scan_exclusive(n_slot, slot_base, S, small + 2, scan_tmp, stream));
     PMA_TRY(scan_exclusive(is_split, split_base, S, small + 3, scan_tmp, stream));
@@ -582,22 +726,46 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t
     g->n_stasks = h_small[1];
     g->n_sslots = h_small[2];
     g->n_ssplit = h_small[3];
+    // Bands only pay where some source has long rows (whose pieces share
+    // target rows); otherwise one band in source order.
+    g->s_banded = h_small[4] > 0;
     {
         const int64_t nt = g->n_stasks, ns = g->n_ssplit > 0 ? g->n_ssplit : 1;
+        const int64_t ntt = (nt + kTile - 1) / kTile;
         PMA_TRY(hipMalloc(&g->s_source, nt * i4));
         PMA_TRY(hipMalloc(&g->s_begin, nt * i4));
         PMA_TRY(hipMalloc(&g->s_end, nt * i4));
         PMA_TRY(hipMalloc(&g->s_slot, nt * i4));
-        PMA_TRY(hipMalloc(&t_split, nt * i4));
-        PMA_TRY(hipMalloc(&t_key, nt * i4));
         PMA_TRY(hipMalloc(&g->ss_source, ns * i4));
         PMA_TRY(hipMalloc(&g->ss_slot0, ns * i4));
         PMA_TRY(hipMalloc(&g->ss_count, ns * i4));
-        split_fill_kernel<<<grid_for(S, 256), 256, 0, stream>>>(
-            g->csc_ptr, S, chunk, piece_base, slot_base, split_base, g->s_source, g->s_begin,
-            g->s_end, g->s_slot, t_split, t_key, g->ss_source, g->ss_slot0, g->ss_count);
+        PMA_TRY(hipMalloc(&u_source, nt * i4));
+        PMA_TRY(hipMalloc(&u_begin, nt * i4));
+        PMA_TRY(hipMalloc(&u_end, nt * i4));
+        PMA_TRY(hipMalloc(&u_slot, nt * i4));
+        PMA_TRY(hipMalloc(&u_key, nt * i4));
+        PMA_TRY(hipMalloc(&s_key, nt * i4));
+        PMA_TRY(hipMalloc(&tperm, nt * i4));
+        PMA_TRY(hipMalloc(&tperm_tmp, nt * i4));
+        PMA_TRY(hipMalloc(&sc, 256 * ntt * i4));
+        src_piece_fill<<<grid_for(S, 256), 256, 0, stream>>>(
+            g->csc_ptr, g->csc_tgt, band_start, S, L, chunk, g->s_banded ? 1 : 0, piece_base,
+            slot_base, split_base, u_source, u_begin, u_end, u_slot, u_key, g->ss_source,
+            g->ss_slot0, g->ss_count);
+        // order: band, then first target (stable)
+        iota_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(tperm, nt);
+        PMA_TRY(radix_sort_perm(u_key, bits_for((int64_t)kBands * (L + 1)), tperm, tperm_tmp, nt,
+                                sc, scan_tmp, stream));
+        gather5_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(
+            tperm, nt, u_source, u_begin, u_end, u_slot, u_key, g->s_source, g->s_begin, g->s_end,
+            g->s_slot, s_key);
+        band_off_kernel<<<1, 64, 0, stream>>>(s_key, nt, L, small + 8);
         PMA_TRY(hipGetLastError());
+        PMA_TRY(hipMemcpyAsync(h_small + 8, small + 8, (kBands + 1) * i4, hipMemcpyDeviceToHost,
+                               stream));
         PMA_TRY(hipStreamSynchronize(stream));
+        for (int k = 0; k <= kBands; ++k)
+            g->s_band_off[k] = h_small[8 + k];
     }
     goto done;
 fail:
@@ -614,7 +782,8 @@ fail:
     }
 done:
     for (int32_t *q : {perm, perm_tmp, counts, scan_tmp, deg, small, n_piece, n_slot, is_split,
-                       piece_base, slot_base, split_base, t_split, t_key})
+                       piece_base, slot_base, split_base, band_start, u_source, u_begin, u_end,
+                       u_slot, u_key, s_key, tperm, tperm_tmp, sc})
         if (q)
             (void)hipFree(q);
     return st;

@@ -730,7 +730,7 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         return fail(PMA_E_UNSUPPORTED, "batch too large");
     char err[256] = "";
     if (!p->g.csc_ptr) {
-        pma_status st = pma::build_csc(&p->g, nnz, S, p->bchunk, stream, err, sizeof err);
+        pma_status st = pma::build_csc(&p->g, nnz, L, S, p->bchunk, stream, err, sizeof err);
         if (st != PMA_OK)
             return fail(st, "%s", err);
     }
@@ -828,6 +828,9 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     a.n_tsplit = gd.n_split;
     a.n_stasks = gd.n_stasks;
     a.n_ssplit = gd.n_ssplit;
+    for (int k = 0; k <= pma::kBands; ++k)
+        a.s_band_off[k] = gd.s_band_off[k];
+    a.banded = gd.s_banded ? 1 : 0;
     a.kpm_bits = nullptr;
     a.kpm_words = 0;
     if (key_padding_mask) {
@@ -1004,7 +1007,7 @@ PMA_API pma_status pma_linear_backward(pma_plan *plan, int64_t batch, int64_t ch
                     (long long)batch, (long long)channels);
     if (plan && !plan->g.csc_ptr) {
         char err[256] = "";
-        pma_status st = pma::build_csc(&plan->g, plan->nnz, plan->S, plan->bchunk, stream, err,
+        pma_status st = pma::build_csc(&plan->g, plan->nnz, plan->L, plan->S, plan->bchunk, stream, err,
                                        sizeof err);
         if (st != PMA_OK)
             return fail(st, "%s", err);

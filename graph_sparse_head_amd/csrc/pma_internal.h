@@ -12,6 +12,9 @@ namespace pma {
 
 // Zero entries kept after the last source index (see GraphDev::csr_src).
 constexpr int kSrcPad = 16;
+// The backward's source pieces are grouped into kBands bands of targets with
+// equal edge counts, one band per XCD (an MI355X has 8).
+constexpr int kBands = 8;
 
 // Device arrays describing one graph; owned by the plan.
 struct GraphDev {
@@ -34,11 +37,15 @@ struct GraphDev {
     // Source pieces, built with the source-major view: piece i covers entries
     // s_begin[i] .. s_end[i] of source s_source[i]; s_slot[i] is its partial
     // slot, -1 when the source is one piece. Sources in more than one piece:
-    // ss_source, with slots ss_slot0 .. ss_slot0 + ss_count - 1.
+    // ss_source, with slots ss_slot0 .. ss_slot0 + ss_count - 1. A piece lies
+    // within one band of targets; pieces are ordered by band, then by their
+    // first target; band k holds pieces s_band_off[k] .. s_band_off[k+1].
     int32_t *s_source = nullptr, *s_begin = nullptr, *s_end = nullptr, *s_slot = nullptr;
     int32_t *ss_source = nullptr, *ss_slot0 = nullptr, *ss_count = nullptr;
     int64_t n_tasks = 0, n_split = 0, n_slots = 0, max_degree = 0, n_kv = 0;
     int64_t n_stasks = 0, n_ssplit = 0, n_sslots = 0;
+    int64_t s_band_off[kBands + 1] = {0};
+    bool s_banded = false;        // false: one band (no source long enough to cut)
 };
 
 // Builds every array of GraphDev from host edges (already validated, loops
@@ -49,9 +56,9 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
                        size_t errlen);
 void free_graph(GraphDev *g);
 // Builds the source-major view and the source pieces of at most `chunk`
-// entries (blocks on `stream`).
-pma_status build_csc(GraphDev *g, int64_t nnz, int64_t S, int chunk, hipStream_t stream,
-                     char *err, size_t errlen);
+// entries, banded (blocks on `stream`).
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
+                     hipStream_t stream, char *err, size_t errlen);
 
 // ---- projections (proj.hip) ----------------------------------------------
 
@@ -154,6 +161,8 @@ struct BwdArgs {
     const int32_t *s_source, *s_begin, *s_end, *s_slot;
     const int32_t *ss_source, *ss_slot0, *ss_count;
     int64_t n_ttasks, n_tsplit, n_stasks, n_ssplit;
+    int64_t s_band_off[kBands + 1];  // source pieces per band (one band per XCD)
+    int banded;                      // 0: one band, launched in plain order
     const uint64_t *kpm_bits;        // packed mask or nullptr
     int kpm_words;
     void *PZ;                        // [nnz][B][H] (p, dz) pairs: bf16 for bf16 plans, fp32 else
