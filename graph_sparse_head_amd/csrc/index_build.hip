@@ -532,18 +532,18 @@ __global__ void csc_fill(const int32_t *perm, const int32_t *csr_tgt, const int3
 // each of their pieces gathers target rows of one band only.
 constexpr int kBandMinDeg = 64;
 
-// band_start[k]: the first target whose CSR offset reaches ceil(k nnz / kBands).
-__global__ void band_bounds_kernel(const int32_t *row_ptr, int64_t L, int64_t nnz,
+// band_start[k]: the first target whose CSR offset reaches ceil(k nnz / nb).
+__global__ void band_bounds_kernel(const int32_t *row_ptr, int64_t L, int64_t nnz, int nb,
                                    int32_t *band_start)
 {
     const int k = threadIdx.x;
-    if (k > kBands)
+    if (k > nb)
         return;
-    if (k == 0 || k == kBands) {
+    if (k == 0 || k == nb) {
         band_start[k] = k == 0 ? 0 : (int32_t)L;
         return;
     }
-    const int64_t goal = (nnz * k + kBands - 1) / kBands;
+    const int64_t goal = (nnz * k + nb - 1) / nb;
     int64_t lo = 0, hi = L;
     while (lo < hi) {
         const int64_t mid = (lo + hi) >> 1;
@@ -574,7 +574,7 @@ __device__ inline int64_t pieces_of(int64_t len, int chunk)
 }
 
 __global__ void src_piece_count(const int32_t *csc_ptr, const int32_t *csc_tgt,
-                                const int32_t *band_start, int64_t S, int chunk, int32_t *n_piece,
+                                const int32_t *band_start, int nb, int64_t S, int chunk, int32_t *n_piece,
                                 int32_t *n_slot, int32_t *is_split, int32_t *n_long)
 {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -587,7 +587,7 @@ __global__ void src_piece_count(const int32_t *csc_ptr, const int32_t *csc_tgt,
     if (g < kBandMinDeg) {
         n = pieces_of(g, chunk);
     } else {
-        for (int k = 0; k < kBands; ++k) {
+        for (int k = 0; k < nb; ++k) {
             const int64_t lo = lower_bound_t(csc_tgt, b, e, band_start[k]);
             const int64_t hi = lower_bound_t(csc_tgt, lo, e, band_start[k + 1]);
             if (hi > lo)
@@ -603,8 +603,8 @@ __global__ void src_piece_count(const int32_t *csc_ptr, const int32_t *csc_tgt,
 // even parts in target order. Sort key: band (L + 1), plus first target + 1
 // for the pieces of long sources (short sources keep source order, first).
 __global__ void src_piece_fill(const int32_t *csc_ptr, const int32_t *csc_tgt,
-                               const int32_t *band_start, int64_t S, int64_t L, int chunk,
-                               int banded,
+                               const int32_t *band_start, int sub, int64_t S, int64_t L,
+                               int chunk, int banded,
                                const int32_t *piece_base, const int32_t *slot_base,
                                const int32_t *split_base, int32_t *u_source, int32_t *u_begin,
                                int32_t *u_end, int32_t *u_slot, int32_t *u_key,
@@ -616,21 +616,23 @@ __global__ void src_piece_fill(const int32_t *csc_ptr, const int32_t *csc_tgt,
     const int64_t b = csc_ptr[s], e = csc_ptr[s + 1], g = e - b;
     const int64_t pb = piece_base[s];
     int64_t j = 0;
+    // band k runs on XCD k mod kBands as its (k / kBands)-th sub-band
     auto emit = [&](int64_t sb, int64_t se, int band, bool by_target) {
+        const int64_t xkey = (int64_t)(band % kBands) * sub + band / kBands;
         const int64_t len = se - sb, n = pieces_of(len, chunk);
         for (int64_t i = 0; i < n; ++i) {
             const int64_t pbeg = sb + (i * len) / n, pend = sb + ((i + 1) * len) / n;
             u_source[pb + j] = (int32_t)s;
             u_begin[pb + j] = (int32_t)pbeg;
             u_end[pb + j] = (int32_t)pend;
-            u_key[pb + j] = (int32_t)(band * (L + 1) + (by_target && pend > pbeg ? csc_tgt[pbeg] + 1 : 0));
+            u_key[pb + j] = (int32_t)(xkey * (L + 1) + (by_target && pend > pbeg ? csc_tgt[pbeg] + 1 : 0));
             ++j;
         }
     };
     if (g < kBandMinDeg)   // short rows: spread over the bands, source order
         emit(b, e, banded ? (int)(s % kBands) : 0, false);
     else {
-        for (int k = 0; k < kBands; ++k) {
+        for (int k = 0; k < kBands * sub; ++k) {
             const int64_t lo = lower_bound_t(csc_tgt, b, e, band_start[k]);
             const int64_t hi = lower_bound_t(csc_tgt, lo, e, band_start[k + 1]);
             if (hi > lo)
@@ -647,13 +649,14 @@ __global__ void src_piece_fill(const int32_t *csc_ptr, const int32_t *csc_tgt,
     }
 }
 
-// band_off[k] = first sorted piece whose key is at least k (L + 1)
-__global__ void band_off_kernel(const int32_t *key, int64_t n, int64_t L, int32_t *band_off)
+// band_off[x] = first sorted piece of XCD x (key at least x sub (L + 1))
+__global__ void band_off_kernel(const int32_t *key, int64_t n, int64_t L, int sub,
+                                int32_t *band_off)
 {
     const int k = threadIdx.x;
     if (k > kBands)
         return;
-    const int64_t goal = (int64_t)k * (L + 1);
+    const int64_t goal = (int64_t)k * sub * (L + 1);
     int64_t lo = 0, hi = n;
     while (lo < hi) {
         const int64_t mid = (lo + hi) >> 1;
@@ -665,9 +668,13 @@ __global__ void band_off_kernel(const int32_t *key, int64_t n, int64_t L, int32_
     band_off[k] = (int32_t)lo;
 }
 
-pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk, int sub,
                      hipStream_t stream, char *err, size_t errlen)
 {
+    // sort keys (sub-band, target) stay below 2^31
+    while (sub > 1 && (int64_t)kBands * sub * (L + 1) >= ((int64_t)1 << 31))
+        sub >>= 1;
+    const int nb = kBands * sub;
     pma_status st = PMA_OK;
     const size_t i4 = sizeof(int32_t);
     const int64_t n_sort = std::max(nnz, S);
@@ -694,7 +701,7 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
     PMA_TRY(hipMalloc(&piece_base, S * i4));
     PMA_TRY(hipMalloc(&slot_base, S * i4));
     PMA_TRY(hipMalloc(&split_base, S * i4));
-    PMA_TRY(hipMalloc(&band_start, (kBands + 1) * i4));
+    PMA_TRY(hipMalloc(&band_start, (nb + 1) * i4));
     PMA_TRY(hipMalloc(&g->csc_ptr, (S + 1) * i4));
     PMA_TRY(hipMalloc(&g->csc_tgt, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMemsetAsync(g->csc_tgt + nnz, 0, kSrcPad * i4, stream));
@@ -713,8 +720,8 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
     g->csc_pos = perm;   // kept
     perm = nullptr;
     // pieces per source: band segments, each in pieces of at most chunk
-    band_bounds_kernel<<<1, 64, 0, stream>>>(g->row_ptr, L, nnz, band_start);
-    src_piece_count<<<grid_for(S, 256), 256, 0, stream>>>(g->csc_ptr, g->csc_tgt, band_start, S,
+    band_bounds_kernel<<<1, 1024, 0, stream>>>(g->row_ptr, L, nnz, nb, band_start);
+    src_piece_count<<<grid_for(S, 256), 256, 0, stream>>>(g->csc_ptr, g->csc_tgt, band_start, nb, S,
                                                           chunk, n_piece, n_slot, is_split,
                                                           small + 4);
     PMA_TRY(scan_exclusive(n_piece, piece_base, S, small + 1, scan_tmp, stream));
@@ -749,17 +756,17 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
         PMA_TRY(hipMalloc(&tperm_tmp, nt * i4));
         PMA_TRY(hipMalloc(&sc, 256 * ntt * i4));
         src_piece_fill<<<grid_for(S, 256), 256, 0, stream>>>(
-            g->csc_ptr, g->csc_tgt, band_start, S, L, chunk, g->s_banded ? 1 : 0, piece_base,
+            g->csc_ptr, g->csc_tgt, band_start, sub, S, L, chunk, g->s_banded ? 1 : 0, piece_base,
             slot_base, split_base, u_source, u_begin, u_end, u_slot, u_key, g->ss_source,
             g->ss_slot0, g->ss_count);
         // order: band, then first target (stable)
         iota_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(tperm, nt);
-        PMA_TRY(radix_sort_perm(u_key, bits_for((int64_t)kBands * (L + 1)), tperm, tperm_tmp, nt,
+        PMA_TRY(radix_sort_perm(u_key, bits_for((int64_t)nb * (L + 1)), tperm, tperm_tmp, nt,
                                 sc, scan_tmp, stream));
         gather5_kernel<<<grid_for(nt, 256), 256, 0, stream>>>(
             tperm, nt, u_source, u_begin, u_end, u_slot, u_key, g->s_source, g->s_begin, g->s_end,
             g->s_slot, s_key);
-        band_off_kernel<<<1, 64, 0, stream>>>(s_key, nt, L, small + 8);
+        band_off_kernel<<<1, 64, 0, stream>>>(s_key, nt, L, sub, small + 8);
         PMA_TRY(hipGetLastError());
         PMA_TRY(hipMemcpyAsync(h_small + 8, small + 8, (kBands + 1) * i4, hipMemcpyDeviceToHost,
                                stream));

@@ -43,6 +43,7 @@ struct pma_plan {
     pma_dtype dtype = PMA_F32;
     int chunk = kChunk;
     int bchunk = kChunk;        // most edges one source piece of the backward covers
+    int bsub = 1;               // PMA_BWD_SUB: target bands per XCD for the backward's source pieces
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
@@ -254,6 +255,7 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_COMPACT    1 / 0: force or forbid projecting keys and values only
     //                  for the sources some edge reads
     //   PMA_BWD_CHUNK  n: most edges of one source piece in the backward pass
+    //   PMA_BWD_SUB    n: target bands per XCD for those pieces (1..64)
     // Piece length: a target is split only when it has far more edges than
     // the average target (16x, rounded up to a power of two, at least 256).
     // Splitting balances graphs with a few very long rows among many short
@@ -276,6 +278,11 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         const long c = strtol(ev, nullptr, 10);
         if (c >= 1 && c <= 65535)
             p->bchunk = (int)c;
+    }
+    if (const char *ev = getenv("PMA_BWD_SUB")) {
+        const long c = strtol(ev, nullptr, 10);
+        if (c >= 1 && c <= 64)
+            p->bsub = (int)c;
     }
     if (const char *ev = getenv("PMA_FUSE_OUT"))
         p->fuse_out = ev[0] != '0';
@@ -730,7 +737,7 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         return fail(PMA_E_UNSUPPORTED, "batch too large");
     char err[256] = "";
     if (!p->g.csc_ptr) {
-        pma_status st = pma::build_csc(&p->g, nnz, L, S, p->bchunk, stream, err, sizeof err);
+        pma_status st = pma::build_csc(&p->g, nnz, L, S, p->bchunk, p->bsub, stream, err, sizeof err);
         if (st != PMA_OK)
             return fail(st, "%s", err);
     }
@@ -1007,7 +1014,7 @@ PMA_API pma_status pma_linear_backward(pma_plan *plan, int64_t batch, int64_t ch
                     (long long)batch, (long long)channels);
     if (plan && !plan->g.csc_ptr) {
         char err[256] = "";
-        pma_status st = pma::build_csc(&plan->g, plan->nnz, plan->L, plan->S, plan->bchunk, stream, err,
+        pma_status st = pma::build_csc(&plan->g, plan->nnz, plan->L, plan->S, plan->bchunk, plan->bsub, stream, err,
                                        sizeof err);
         if (st != PMA_OK)
             return fail(st, "%s", err);

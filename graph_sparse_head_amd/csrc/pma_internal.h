@@ -57,7 +57,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
 void free_graph(GraphDev *g);
 // Builds the source-major view and the source pieces of at most `chunk`
 // entries, banded (blocks on `stream`).
-pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk,
+pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk, int sub,
                      hipStream_t stream, char *err, size_t errlen);
 
 // ---- projections (proj.hip) ----------------------------------------------
