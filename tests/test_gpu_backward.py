@@ -170,12 +170,15 @@ def test_backward_full_graph_small_batch(cfg):
 
 @pytest.mark.parametrize("compact", ["0", "1"])
 @pytest.mark.parametrize("shared", ["none", "qkv"])
-def test_backward_read_sources_only(compact, shared, monkeypatch):
+@pytest.mark.parametrize("mask", [False, True])
+def test_backward_read_sources_only(compact, shared, mask, monkeypatch):
     # half of the sources are never read: with PMA_COMPACT=1 the training
-    # forward saves keys and values for the read ones only
+    # forward saves keys and values for the read ones only (the mask still
+    # refers to the original sources)
     monkeypatch.setenv("PMA_COMPACT", compact)
     c = synth.random_case(89, 3, 60, 60, 64, 4, 0.1, dtype="bf16", same_kv=shared != "none",
                           same_qkv=shared == "qkv", name="bwd_compact")
     keep = c.src % 2 == 0
     c.src, c.tgt = c.src[keep], c.tgt[keep]
-    _grad_check(c, shared)
+    kpm = (np.random.default_rng(91).random((c.B, c.S)) < 0.3) if mask else None
+    _grad_check(c, shared, kpm=kpm)
