@@ -1,8 +1,8 @@
 """Forward throughput of packed multi-head attention over live edges on one GPU.
 
-One step = one pma_forward over one batch: the q/k/v projections, the fused
-edge kernel (scores, online softmax, mix), the merge of split targets and
-out_proj, on the gene-regulatory-prior workload (n = 20,000 nodes, Zipf 1.5
+One step = one pma_forward over one batch: the key/value projection, the
+fused edge kernel (q projection, scores, online softmax, mix and out_proj) and
+the merge of split targets, on the gene-regulatory-prior workload (n = 20,000 nodes, Zipf 1.5
 source hubs, log-normal in-degree of mean 10, B = 32, E = 64, H = 4, bf16
 tokens, fp32 softmax and accumulation). Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.

@@ -16,7 +16,12 @@
 //   * targets longer than the plan's chunk are split into pieces whose
 //     (max, sum, partial mix) are merged afterwards in a fixed order;
 //   * with need_weights the log2-domain scores are stored per CSR position
-//     and normalised once the final (max, sum) of each target is known.
+//     and normalised once the final (max, sum) of each target is known;
+//   * at embed_dim 64 (inference) the same kernel applies out_proj to the
+//     mixed rows it has just made and, for bf16, also projects each target's
+//     q from its query tokens at the start of the piece (step 1), with Wq and
+//     Wo held in LDS as matrix-core fragments: neither q nor the mixed rows
+//     travel through memory.
 //
 // Workspace layouts: q, keys/values and mixed rows are addressed through
 // element strides (Layout); part_acc[slot][B][E], part_ml[slot][B][H][2],
@@ -63,6 +68,10 @@ struct EdgeK {
     int fuse_out, L;
     const void *wo, *bo;
     void *out;
+    // q projection in the prologue (fuse_in): qt / lay address the caller's
+    // query tokens and each piece projects its target's rows with Wq, bq
+    int fuse_in;
+    const void *wq, *bq;
 };
 
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -169,10 +178,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 // lanes x 16 bytes at byte ((nt * KG + kg) * 64 + lane) * 16, lane l holding
 // output channel (E/4)(l%16 / 4) + 4 nt + l%4 at channels (4 kg + l/16) * CH.
 template <typename T, int CH, int E>
-__device__ inline void stage_wo(const EdgeK &a, char *wlds)
+__device__ inline void stage_w(const void *w, const void *b, char *wlds)
 {
     constexpr int KG = E / (4 * CH), NT = E / 16, CPL = E / 4;
-    const T *W = reinterpret_cast<const T *>(a.wo);
+    const T *W = reinterpret_cast<const T *>(w);
     for (int f = threadIdx.x; f < NT * KG * 64; f += blockDim.x) {
         const int lane = f & 63, fk = f >> 6, kg = fk % KG, nt = fk / KG;
         const int n = lane & 15, g = lane >> 4;
@@ -182,7 +191,7 @@ __device__ inline void stage_wo(const EdgeK &a, char *wlds)
     }
     // bias as fp32 after the fragments (zeros without bias)
     float *bl = reinterpret_cast<float *>(wlds + NT * KG * 64 * 16);
-    const T *bias = reinterpret_cast<const T *>(a.bo);
+    const T *bias = reinterpret_cast<const T *>(b);
     for (int c = threadIdx.x; c < E; c += blockDim.x) {
         float v = 0.f;
         if (bias) {
@@ -195,24 +204,39 @@ __device__ inline void stage_wo(const EdgeK &a, char *wlds)
     }
 }
 
-template <typename T, int CH, int E, bool W32>
-__device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane, int t,
-                                     int b_first, const char *wlds)
+// bytes of one staged E x E matrix with its bias
+template <typename T, int E> constexpr int staged_bytes() { return E * E * (int)sizeof(T) + 4 * E; }
+
+template <typename T, int CH, int E>
+__device__ inline void stage_wo(const EdgeK &a, char *wlds)
 {
+    stage_w<T, CH, E>(a.wo, a.bo, wlds);
+}
+
+// y = x W^T + bias for the samples of one wavefront with W staged by
+// stage_w; w holds this lane's 16-byte chunk of x (lane = sample * CPR +
+// chunk). Lane (n, g) = (lane % 16, lane / 16) gets output channels
+// CPL g .. CPL g + CPL - 1 of sample n as T words in ow (zeros-in rows for
+// n >= samples per wavefront).
+template <typename T, int CH, int E, bool OPAQUE = false>
+__device__ inline void proj_wave(const uint32_t *w, int lane, const char *wlds,
+                                 uint32_t *ow)
+{
+    // This lane's byte offsets of its fragments and of its bias slice. With
+    // OPAQUE they are hidden from the optimiser, so that a call inside a loop
+    // re-reads the LDS each time instead of keeping the whole matrix in
+    // registers across the loop.
+    uint32_t fo = (uint32_t)lane * 16, bo = (uint32_t)(lane >> 4) * (E / 4) * 4;
+    if constexpr (OPAQUE) {
+        asm volatile("" : "+v"(fo));
+        asm volatile("" : "+v"(bo));
+    }
     constexpr int CPR = E / CH;     // chunks per sample row
     constexpr int SPW = 64 / CPR;   // samples per wavefront
     constexpr int NT = E / 16;
     constexpr int CPL = E / 4;      // output channels per lane
     const int n = lane & 15, g = lane >> 4;
     const bool has = n < SPW;
-    uint32_t w[4];                  // this lane's mixed chunk as 16 bytes of T
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = pack_bf16(mix[2 * j], mix[2 * j + 1]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(mix[j]);
-    }
     // k-groups: 32 channels (bf16) or 16 channels (fp32) per group
     constexpr int KG = E / (4 * CH);
     uint32_t bw[KG][4];
@@ -225,18 +249,15 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
             bw[kg][j] = has ? (uint32_t)v : 0u;
         }
     }
-    const int b = b_first + n;
     const float *bl = reinterpret_cast<const float *>(wlds + NT * KG * 64 * 16);
     // one n-tile at a time; results packed into T words as they are made
-    constexpr int OW = CPL * (int)sizeof(T) / 4;   // 32-bit words of this lane's output
-    uint32_t ow[OW];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const float4 b4 = *reinterpret_cast<const float4 *>(bl + CPL * g + 4 * nt);
+        const float4 b4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const char *>(bl) + bo + 16 * nt);
         f32x4_t acc = {b4.x, b4.y, b4.z, b4.w};   // bias first
 #pragma unroll
         for (int kg = 0; kg < KG; ++kg) {
-            const uint4 wa = *reinterpret_cast<const uint4 *>(wlds + ((nt * KG + kg) * 64 + lane) * 16);
+            const uint4 wa = *reinterpret_cast<const uint4 *>(wlds + fo + (nt * KG + kg) * 1024);
             if constexpr (sizeof(T) == 2) {
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8_t, wa),
@@ -258,7 +279,28 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
             for (int i = 0; i < 4; ++i) ow[4 * nt + i] = __float_as_uint(o[i]);
         }
     }
-    if (!has || b >= a.B)
+}
+
+template <typename T, int CH, int E, bool W32>
+__device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane, int t,
+                                     int b_first, const char *wlds)
+{
+    constexpr int SPW = 64 / (E / CH);
+    constexpr int CPL = E / 4;
+    constexpr int OW = CPL * (int)sizeof(T) / 4;   // 32-bit words of this lane's output
+    uint32_t w[4];                  // this lane's mixed chunk as 16 bytes of T
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16(mix[2 * j], mix[2 * j + 1]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = __float_as_uint(mix[j]);
+    }
+    uint32_t ow[OW];
+    proj_wave<T, CH, E>(w, lane, wlds, ow);
+    const int n = lane & 15, g = lane >> 4;
+    const int b = b_first + n;
+    if (n >= SPW || b >= a.B)
         return;
     T *o = reinterpret_cast<T *>(a.out);
     if (W32)   // out under 2 GiB: 32-bit element offset
@@ -274,6 +316,35 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
         else
             *reinterpret_cast<uint4 *>(dst + 16 * k) = v;
     }
+}
+
+// q = x Wq^T + bq (kpnn2 page, "Notes" step 1) for the current target of
+// one wavefront, from the lane's chunk of its own x row; returns the lane's
+// chunk of q in the lane layout (lane = sample * CPR + chunk), rounded to T
+// as a separate projection would store it. proj_wave leaves channels
+// CPL g .. of sample n on lane 16 g + n; each lane fetches its CH channels
+// from there (every word, then the ones at its offset are kept).
+template <typename T, int CH, int E>
+__device__ inline uint4 q_proj_wave(const uint4 &x, int lane, const char *wlds)
+{
+    constexpr int CPR = E / CH, CPL = E / 4;
+    constexpr int OW = CPL * (int)sizeof(T) / 4;
+    constexpr int PARTS = CPL / CH;   // CH-channel chunks per MFMA lane
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t ow[OW];
+    proj_wave<T, CH, E, true>(w, lane, wlds, ow);
+    const int s = lane / CPR, c = lane % CPR;
+    const int src = (c / PARTS) * 16 + s, part = c % PARTS;
+    uint32_t r[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < PARTS; ++k) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)ow[4 * k + j]);
+            r[j] = part == k ? v : r[j];
+        }
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // Fast path: d = CH * LPH with 16-byte chunks.
@@ -441,7 +512,7 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
     }
 };
 
-template <typename T, int CH, int LPH, int U, int E_FUSE, bool W32, bool SC, bool KPM>
+template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, bool KPM>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(8)))   // 64 VGPRs
 edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
@@ -451,10 +522,14 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
 {
     // The index arrays come in as noalias arguments: no store of this kernel
     // can reach them, so their wave-uniform reads stay scalar loads.
-    __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? E_FUSE * E_FUSE * sizeof(T) + 4 * E_FUSE : 16];
+    static_assert(!QF || E_FUSE > 0, "the q prologue comes with the out_proj epilogue");
+    constexpr int WB = E_FUSE > 0 ? staged_bytes<T, E_FUSE>() : 16;
+    __shared__ __attribute__((aligned(16))) char wlds[QF ? 2 * WB : WB];
     if constexpr (E_FUSE > 0) {
         if (a.fuse_out) {   // uniform over the launch; before any wavefront exits
             stage_wo<T, CH, E_FUSE>(a, wlds);
+            if constexpr (QF)   // Wq after Wo
+                stage_w<T, CH, E_FUSE>(a.wq, a.bq, wlds + WB);
             __syncthreads();
         }
     }
@@ -538,7 +613,10 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
             end2 = task_end[nxt];
             slot2 = task_slot[nxt];
         }
-        st.q.u = qn;
+        if constexpr (QF)
+            st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
+        else
+            st.q.u = qn;
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
             for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
@@ -683,7 +761,7 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
 template <typename T, int CH, int LPH, int E_FUSE>
 __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
 {
-    __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? E_FUSE * E_FUSE * sizeof(T) + 4 * E_FUSE : 16];
+    __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? staged_bytes<T, E_FUSE>() : 16];
     if constexpr (E_FUSE > 0) {
         if (a.fuse_out) {
             stage_wo<T, CH, E_FUSE>(a, wlds);
@@ -910,6 +988,9 @@ EdgeK make_k(const EdgeArgs &x)
     k.L = (int)x.L;
     k.wo = x.wo;
     k.bo = x.bo;
+    k.fuse_in = x.fuse_in;
+    k.wq = x.wq;
+    k.bq = x.bq;
     k.out = x.out;
     k.scale = (float)(1.4426950408889634 / sqrt((double)k.d));
     k.lay = x.lay;
@@ -943,7 +1024,7 @@ int cu_count()
     return cached[dev];
 }
 
-template <typename T, int CH, int LPH, int E_FUSE>
+template <typename T, int CH, int LPH, int E_FUSE, bool QF>
 hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
 {
     set_passes(k, CH);
@@ -973,7 +1054,7 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     const bool w32 = offsets32(k, sizeof(T));
     const unsigned nb = (unsigned)blocks;
 #define PMA_EDGE_LAUNCH(W, S, M)                                                          \
-    edge_fast<T, CH, LPH, 4, E_FUSE, W, S, M><<<nb, 256, 0, s>>>(                        \
+    edge_fast<T, CH, LPH, 4, E_FUSE, QF, W, S, M><<<nb, 256, 0, s>>>(                    \
         k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.orig_src, k.kpm_bits)
     if (k.kpm_bits) {
         if (!w32)   // refused by mask_supported()
@@ -1006,10 +1087,20 @@ constexpr bool fusable(int E)
 template <typename T, int CH, int LPH>
 hipError_t run_fast_any(EdgeK k, int persist, hipStream_t s)
 {
-    if (k.fuse_out && k.E == 64 && fusable<T, CH>(64))
-        return run_fast<T, CH, LPH, 64>(k, persist, s);
+    const bool ok = k.fuse_out && k.E == 64 && fusable<T, CH>(64);
+    if (k.fuse_in) {   // q exists only in the prologue: no way back
+        // (bf16 only: an fp32 Wq beside Wo is 33 KB of LDS per workgroup,
+        // too much for the gather's occupancy; refused by q_fusable)
+        if constexpr (sizeof(T) == 2) {
+            if (ok)
+                return run_fast<T, CH, LPH, 64, true>(k, persist, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    if (ok)
+        return run_fast<T, CH, LPH, 64, false>(k, persist, s);
     k.fuse_out = 0;
-    return run_fast<T, CH, LPH, 0>(k, persist, s);
+    return run_fast<T, CH, LPH, 0, false>(k, persist, s);
 }
 
 template <typename T>
@@ -1026,6 +1117,8 @@ hipError_t dispatch_edge(EdgeK k, int persist, hipStream_t s)
         default: break;
         }
     }
+    if (k.fuse_in)   // refused by the host (out_fusable)
+        return hipErrorInvalidValue;
     const int64_t n = k.n_tasks * k.B * k.E;
     edge_generic<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(k);
     return hipGetLastError();
@@ -1111,6 +1204,11 @@ bool out_fusable(int64_t E, int64_t H, pma_dtype dt)
     const int64_t d = E / H;
     const int64_t ch = dt == PMA_BF16 ? 8 : 4;
     return E == 64 && d % ch == 0 && (d / ch) <= 16 && ((d / ch) & (d / ch - 1)) == 0;
+}
+
+bool q_fusable(int64_t E, int64_t H, pma_dtype dt)
+{
+    return dt == PMA_BF16 && out_fusable(E, H, dt);
 }
 
 Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)

@@ -47,6 +47,7 @@ struct pma_plan {
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
+    bool fuse_in = true;        // PMA_FUSE_IN=0: q projection as a separate kernel
     int nt = -1;                // PMA_NT: non-temporal (1) or cached (0) q / mixed streams, auto (-1)
     int persist = -1;           // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece, -1 auto)
     int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
@@ -286,6 +287,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     }
     if (const char *ev = getenv("PMA_FUSE_OUT"))
         p->fuse_out = ev[0] != '0';
+    if (const char *ev = getenv("PMA_FUSE_IN"))
+        p->fuse_in = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
         p->xcd_map = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_NT"))
@@ -524,6 +527,14 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     const int64_t S_ws = compact ? n_kv : S;   // key/value rows in the workspace
     const pma::Layout lay = pma::make_layout(save ? true : p->batch_first_ws, B, L, S_ws, E);
 
+    // out_proj in the edge / merge epilogue where it applies (16-byte aligned
+    // Wo and out), and then also the q projection in the edge kernel's
+    // prologue (16-byte aligned Wq and query): q never goes to memory.
+    const bool fuse_out = !save && p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
+                          (((uintptr_t)o_w | (uintptr_t)out) & 15) == 0;
+    const bool fuse_in = fuse_out && p->fuse_in && pma::q_fusable(E, p->H, p->dtype) &&
+                         (((uintptr_t)q_w | (uintptr_t)query) & 15) == 0;
+
     // Step 1: q, k, v projections into the workspace layout. Caller tokens are
     // batch-first and read in storage order (key/value rows through the list
     // of read sources when compact).
@@ -545,10 +556,11 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
         }
         return a;
     };
-    if (shared && !compact) {
+    if (shared && !compact && !fuse_in) {
         st = pma::launch_proj(in_args(query, L, 3, oq, ok, ov), E, p->dtype, stream);
     } else {
-        st = pma::launch_proj(in_args(query, L, 1, oq, oq, oq), E, p->dtype, stream);
+        if (!fuse_in)
+            st = pma::launch_proj(in_args(query, L, 1, oq, oq, oq), E, p->dtype, stream);
         if (st == PMA_OK && key == value) {
             st = pma::launch_proj(kv_args(key, 2, ok, ov), E, p->dtype, stream);
         } else if (st == PMA_OK) {
@@ -573,6 +585,11 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.dt = p->dtype;
     ea.lay = lay;
     ea.qt = qt;
+    if (fuse_in) {   // the edge kernel reads the caller's (B, L, E) query rows
+        ea.qt = query;
+        ea.lay.q_t = E;
+        ea.lay.q_b = L * E;
+    }
     ea.kv = kvc;
     ea.kv_bytes = (uint64_t)S_ws * 2 * B * E * es;
     ea.mixed = mixed_ws;
@@ -596,13 +613,13 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     const double ws_bytes = ((double)L + 2.0 * S_ws) * B * E * es;
     ea.nt = p->nt >= 0 ? p->nt : (ws_bytes > 256.0 * 1024 * 1024 ? 1 : 0);
     ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 12 : 0);
-    // out_proj in the edge / merge epilogue where it applies (16-byte aligned
-    // Wo and out).
-    ea.fuse_out = !save && p->fuse_out && pma::out_fusable(E, p->H, p->dtype) &&
-                  (((uintptr_t)o_w | (uintptr_t)out) & 15) == 0;
+    ea.fuse_out = fuse_out;
     ea.wo = o_w;
     ea.bo = o_b;
     ea.out = out;
+    ea.fuse_in = fuse_in;
+    ea.wq = q_w;
+    ea.bq = q_b;
     // Pinning sample groups to XCDs (where the group count divides 8) gives
     // each L2 the rows of one sample group only; measured faster on all three
     // full-size workloads.

@@ -131,11 +131,17 @@ struct EdgeArgs {
     // out_proj fused into the edge and merge kernels (out_fusable)
     int fuse_out = 0;
     const void *wo = nullptr, *bo = nullptr;
+    // q = query Wq^T + bq inside the edge kernel (needs fuse_out); qt and
+    // lay then address the caller's (B, L, E) query tokens
+    int fuse_in = 0;
+    const void *wq = nullptr, *bq = nullptr;
     void *out = nullptr;
 };
 
 // Whether edge_fast / merge_fast can apply out_proj themselves.
 bool out_fusable(int64_t E, int64_t H, pma_dtype dt);
+// Whether edge_fast can also project q itself (with out_proj fused).
+bool q_fusable(int64_t E, int64_t H, pma_dtype dt);
 
 // key_padding_mask bytes (sample b's S bytes at mask + b * bstride; bstride
 // 0 for one shared mask) -> bits[s * words + b / 64], bit b % 64, words =

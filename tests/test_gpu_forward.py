@@ -222,6 +222,8 @@ KNOBS = [
     {"PMA_CHUNK": "3", "PMA_FUSE_OUT": "0"},
     {"PMA_XCD_MAP": "1"},
     {"PMA_XCD_MAP": "0", "PMA_NT": "0"},
+    {"PMA_FUSE_IN": "0"},
+    {"PMA_FUSE_IN": "0", "PMA_CHUNK": "3"},
 ]
 
 
@@ -239,6 +241,24 @@ def test_tuning_knobs(knobs, shape, monkeypatch):
     keep = ~np.isin(c.tgt, [3, 17]) & (c.src < 120)
     c.src = np.concatenate([c.src[keep], hub_src, hub_src[:60]])
     c.tgt = np.concatenate([c.tgt[keep], np.full(100, 3), np.full(60, 17)])
+    _full_check(c, need_weights=True, average=False)
+
+
+@pytest.mark.parametrize("fuse_in", ["0", "1"])
+@pytest.mark.parametrize("compact", ["0", "1"])
+@pytest.mark.parametrize("shared", ["none", "kv", "qkv"])
+@pytest.mark.parametrize("B", [5, 37])
+def test_q_projection_in_edge_kernel(fuse_in, compact, shared, B, monkeypatch):
+    # bf16 at embed_dim 64: the edge kernel projects q from the query rows
+    # itself (PMA_FUSE_IN=1, the default) or reads a separately projected q;
+    # with shared tokens the key/value projection then runs on its own. B = 5
+    # leaves lanes without a sample, B = 37 a partial sample group.
+    monkeypatch.setenv("PMA_FUSE_IN", fuse_in)
+    monkeypatch.setenv("PMA_COMPACT", compact)
+    c = synth.random_case(93, B, 300, 300, 64, 4, 0.02, dtype="bf16", same_kv=shared != "none",
+                          same_qkv=shared == "qkv", name="fuse_in")
+    keep = c.src < 200   # sources 200.. are never read
+    c.src, c.tgt = c.src[keep], c.tgt[keep]
     _full_check(c, need_weights=True, average=False)
 
 

@@ -84,6 +84,7 @@ def test_mask_all_false_is_unmasked(dt):
 
 
 @pytest.mark.parametrize("knobs", [{"PMA_CHUNK": "3"}, {"PMA_CHUNK": "3", "PMA_FUSE_OUT": "0"},
+                                   {"PMA_CHUNK": "3", "PMA_FUSE_IN": "0"},
                                    {"PMA_PERSIST": "1"}, {"PMA_COMPACT": "0"},
                                    {"PMA_XCD_MAP": "0"}],
                          ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
