@@ -149,13 +149,36 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
 {
     constexpr int VEC = Vec<T>::N;
     const int CPR = a.E / VEC;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t gb = idx / CPR;
-    const int c = (int)(idx - gb * CPR);
-    int64_t task = gb / a.B;
-    const int b = (int)(gb - task * a.B);
-    if (UNI)
-        task = __builtin_amdgcn_readfirstlane((int)task);
+    int64_t task;
+    int b, c;
+    if (UNI && a.t_order != 0) {
+        // one wavefront per (piece, sample group): lane = sample * CPR + chunk
+        int64_t i;
+        int g;
+        if (a.t_order == 1) {   // workgroups dealt round-robin to the 8 XCDs
+            const int x = blockIdx.x & 7;
+            g = x % a.t_groups;
+            i = ((int64_t)(blockIdx.x >> 3) * (8 / a.t_groups) + x / a.t_groups) * blockDim.x +
+                threadIdx.x;
+        } else {
+            const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+            g = (int)(j / a.t_gthreads);
+            i = j - g * a.t_gthreads;
+        }
+        task = __builtin_amdgcn_readfirstlane((int)(i >> 6));
+        const int lane = threadIdx.x & 63;
+        const int bl = lane / CPR;
+        c = lane - bl * CPR;
+        b = g * (64 / CPR) + bl;
+    } else {
+        const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        const int64_t gb = idx / CPR;
+        c = (int)(idx - gb * CPR);
+        task = gb / a.B;
+        b = (int)(gb - task * a.B);
+        if (UNI)
+            task = __builtin_amdgcn_readfirstlane((int)task);
+    }
     if (task >= a.n_ttasks)
         return;
     const int t = a.t_target[task], beg = a.t_begin[task], end = a.t_end[task];
@@ -1041,10 +1064,36 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
             per_band = std::max(per_band, (th + 255) / 256);
         }
         const unsigned gs_band = (unsigned)(per_band * kBands);
+        // target pass order over sample groups (uni only)
+        BwdArgs at = a;
+        unsigned gt = grid(nt);
+        const int G = (int)(((int64_t)a.B * cpr) / 64);
+        at.t_groups = G;
+        if (at.t_order < 0) {
+            // Measured on MI355X, as for the forward's edge kernel: groups
+            // pinned to XCDs pay at 8 groups (4% of a bipartite fp32 step;
+            // at 4 groups they are level with the interleaved order); at 2
+            // groups whose keys and values outgrow the 256 MB last-level
+            // cache, groups in turn pay (1% of the 100k-node step).
+            const uint64_t kv = (uint64_t)a.Skv * a.B * a.E * sizeof(T) * 2;
+            at.t_order = G == 8 ? 1 : (G == 2 && kv > ((uint64_t)256 << 20) ? 2 : 0);
+        }
+        if (!uni || (at.t_order == 1 && 8 % G != 0))
+            at.t_order = 0;
+        if (at.t_order != 0) {
+            const int64_t gblocks = (a.n_ttasks * 64 + 255) / 256;   // per group
+            at.t_gthreads = gblocks * 256;
+            if (at.t_order == 1) {
+                const int64_t per = 8 / G;   // XCDs per group
+                gt = (unsigned)(8 * ((gblocks + per - 1) / per));
+            } else {
+                gt = (unsigned)(gblocks * G);
+            }
+        }
 #define PMA_BWD_EDGE(L_)                                                            \
     case L_:                                                                       \
         if (uni) {                                                                 \
-            bwd_target_fast<T, L_, true><<<grid(nt), 256, 0, s>>>(a);              \
+            bwd_target_fast<T, L_, true><<<gt, 256, 0, s>>>(at);                  \
             if (a.banded)                                                          \
                 bwd_source_fast<T, L_, true><<<gs_band, 256, 0, s>>>(a);           \
             else                                                                   \

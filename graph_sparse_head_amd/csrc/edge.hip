@@ -47,9 +47,13 @@ struct EdgeK {
     // n / passes and n / (E / CH) as (n * m) >> sh for n < 2^31 (see magic31)
     uint32_t pass_m, cpr_m;
     int pass_sh, cpr_sh;
-    int xcd_map;         // 1: sample group fixed per XCD (passes divides 8)
+    // 1: sample group fixed per XCD (passes divides 8); 2: sample groups in
+    // turn (wavefront w serves group w / tstride), 0: interleaved
+    int xcd_map;
     uint32_t xcd_per;    // 8 / passes
     uint32_t tstride;    // pieces between a wavefront's consecutive pieces
+    uint32_t ts_m;       // n / tstride as (n * ts_m) >> ts_sh
+    int ts_sh;
     // key_padding_mask as bits: source s, sample b at bit b % 64 of
     // kpm_bits[s * kpm_words + b / 64] (source id from orig_src); a set bit
     // leaves the key out. nullptr: no mask.
@@ -226,15 +230,15 @@ __device__ inline void proj_wave(const uint32_t *w, int lane, const char *wlds,
     // OPAQUE they are hidden from the optimiser, so that a call inside a loop
     // re-reads the LDS each time instead of keeping the whole matrix in
     // registers across the loop.
-    uint32_t fo = (uint32_t)lane * 16, bo = (uint32_t)(lane >> 4) * (E / 4) * 4;
-    if constexpr (OPAQUE) {
-        asm volatile("" : "+v"(fo));
-        asm volatile("" : "+v"(bo));
-    }
     constexpr int CPR = E / CH;     // chunks per sample row
     constexpr int SPW = 64 / CPR;   // samples per wavefront
     constexpr int NT = E / 16;
     constexpr int CPL = E / 4;      // output channels per lane
+    uint32_t fo = (uint32_t)lane * 16, bo = (uint32_t)(lane >> 4) * CPL * 4;
+    if constexpr (OPAQUE) {
+        asm volatile("" : "+v"(fo));
+        asm volatile("" : "+v"(bo));
+    }
     const int n = lane & 15, g = lane >> 4;
     const bool has = n < SPW;
     // k-groups: 32 channels (bf16) or 16 channels (fp32) per group
@@ -539,13 +543,19 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     // task0, task0 + tstride, ... (the host keeps n_tasks * passes below 2^31
     // and makes the wavefront count a multiple of passes).
     uint32_t task, pass;
-    if (a.xcd_map) {
+    if (a.xcd_map == 1) {
         // Workgroups are dealt to the 8 XCDs round-robin; XCD x serves sample
         // group x % passes (passes divides 8), so its L2 caches only that
         // group's key/value rows.
         const uint32_t x = blockIdx.x & 7, xq = div31(x, a.pass_m, a.pass_sh);
         pass = x - xq * a.passes;
         task = ((blockIdx.x >> 3) * a.xcd_per + xq) * 4 + wave;
+    } else if (a.xcd_map == 2) {
+        // Sample groups one after another in launch order: the wavefronts in
+        // flight read the key/value rows of few groups at a time.
+        const uint32_t w = blockIdx.x * 4 + wave;
+        pass = div31(w, a.ts_m, a.ts_sh);
+        task = w - pass * a.tstride;
     } else {
         const uint32_t w = blockIdx.x * 4 + wave;
         task = div31(w, a.pass_m, a.pass_sh);
@@ -957,7 +967,7 @@ bool offsets32(const EdgeK &k, size_t es)
 
 EdgeK make_k(const EdgeArgs &x)
 {
-    EdgeK k;
+    EdgeK k{};   // fields a launch does not set stay zero
     const GraphDev *g = x.g;
     k.csr_src = x.gather_src;   // key/value workspace rows
     k.csr_tgt = g->csr_tgt;
@@ -1035,7 +1045,7 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     // pieces; otherwise one wavefront per (piece, sample group).
     const int64_t cap = persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
     int64_t blocks;
-    if (k.xcd_map && 8 % k.passes == 0) {
+    if (k.xcd_map == 1 && 8 % k.passes == 0) {
         const int64_t per = 8 / k.passes;   // workgroups per pass per round of 8
         int64_t rounds = (k.n_tasks + 4 * per - 1) / (4 * per);
         rounds = std::min(rounds, std::max<int64_t>(1, cap / 8));
@@ -1043,13 +1053,15 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
         k.xcd_per = (uint32_t)per;
         k.tstride = (uint32_t)(rounds * per * 4);
     } else {
-        k.xcd_map = 0;
+        if (k.xcd_map != 2 || k.passes == 1)
+            k.xcd_map = 0;
         // whole multiples of `passes` wavefronts, so each keeps its pass
         const int64_t g = k.passes / std::__gcd<int64_t>(4, k.passes);
         blocks = (k.n_tasks * k.passes + 3) / 4;
         blocks = std::min(blocks, std::max<int64_t>(g, cap));
         blocks = (blocks + g - 1) / g * g;
         k.tstride = (uint32_t)(blocks * 4 / k.passes);
+        magic31(k.tstride, k.ts_m, k.ts_sh);
     }
     const bool w32 = offsets32(k, sizeof(T));
     const unsigned nb = (unsigned)blocks;

@@ -44,8 +44,9 @@ struct pma_plan {
     int chunk = kChunk;
     int bchunk = kChunk;        // most edges one source piece of the backward covers
     int bsub = 1;               // PMA_BWD_SUB: target bands per XCD for the backward's source pieces
+    int border = -1;            // PMA_BWD_ORDER: backward target pass over sample groups (0, 1, 2; -1 automatic)
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
-    int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 0 off, -1 automatic
+    int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 2 groups in turn, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
     bool fuse_in = true;        // PMA_FUSE_IN=0: q projection as a separate kernel
     int nt = -1;                // PMA_NT: non-temporal (1) or cached (0) q / mixed streams, auto (-1)
@@ -248,7 +249,9 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_CHUNK      most edges per piece of a target (1..65535; default
     //                  automatic, see below)
     //   PMA_FUSE_OUT   0: out_proj as a separate kernel
-    //   PMA_XCD_MAP    1 / 0: force or forbid one sample group per XCD
+    //   PMA_FUSE_IN    0: q projection as a separate kernel
+    //   PMA_XCD_MAP    1: one sample group per XCD, 2: sample groups in
+    //                  turn, 0: interleaved (default automatic)
     //   PMA_NT         1 / 0: non-temporal or cached q / mixed streams
     //   PMA_LAYOUT     "batch": batch-first q / k / v / mixed workspace
     //   PMA_PERSIST    n: at most n edge-kernel workgroups per CU, each
@@ -257,6 +260,7 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //                  for the sources some edge reads
     //   PMA_BWD_CHUNK  n: most edges of one source piece in the backward pass
     //   PMA_BWD_SUB    n: target bands per XCD for those pieces (1..64)
+    //   PMA_BWD_ORDER  backward target pass over sample groups, as PMA_XCD_MAP
     // Piece length: a target is split only when it has far more edges than
     // the average target (16x, rounded up to a power of two, at least 256).
     // Splitting balances graphs with a few very long rows among many short
@@ -280,6 +284,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         if (c >= 1 && c <= 65535)
             p->bchunk = (int)c;
     }
+    if (const char *ev = getenv("PMA_BWD_ORDER"))
+        p->border = ev[0] == '1' ? 1 : ev[0] == '2' ? 2 : 0;
     if (const char *ev = getenv("PMA_BWD_SUB")) {
         const long c = strtol(ev, nullptr, 10);
         if (c >= 1 && c <= 64)
@@ -290,7 +296,7 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     if (const char *ev = getenv("PMA_FUSE_IN"))
         p->fuse_in = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
-        p->xcd_map = ev[0] == '0' ? 0 : 1;
+        p->xcd_map = ev[0] == '0' ? 0 : ev[0] == '2' ? 2 : 1;
     if (const char *ev = getenv("PMA_NT"))
         p->nt = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_LAYOUT"))
@@ -620,10 +626,18 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.fuse_in = fuse_in;
     ea.wq = q_w;
     ea.bq = q_b;
-    // Pinning sample groups to XCDs (where the group count divides 8) gives
-    // each L2 the rows of one sample group only; measured faster on all three
-    // full-size workloads.
-    ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map : 1;
+    // Sample groups (wavefronts of 64 lanes over a target's B rows) and
+    // XCDs: pinning each group to 8 / groups XCDs (where the group count
+    // divides 8) gives each L2 the rows of one group only, which multiplies
+    // its reuse by the group count. Running the groups one after another
+    // instead keeps only one group's keys and values in flight, which pays
+    // when all of them outgrow the 256 MB last-level cache and the L2 gain
+    // is small: measured on MI355X, two groups over 350 MB (embed_dim 128,
+    // B = 8, 100k sources) run 6% faster in turn, while 4 and 8 groups
+    // (B = 32 at embed_dim 64; fp32 B = 16 at 128) are much faster pinned.
+    const int64_t groups = (B * (E / (p->dtype == PMA_BF16 ? 8 : 4)) + 63) / 64;
+    const bool in_turn = groups == 2 && ea.kv_bytes > ((uint64_t)256 << 20) && ea.persist == 0;
+    ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map : (in_turn ? 2 : 1);
 
     if (kpm && !pma::mask_supported(ea))
         return fail(PMA_E_UNSUPPORTED, "key_padding_mask with a workspace tensor of 2 GiB or more");
@@ -855,6 +869,7 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     for (int k = 0; k <= pma::kBands; ++k)
         a.s_band_off[k] = gd.s_band_off[k];
     a.banded = gd.s_banded ? 1 : 0;
+    a.t_order = p->border;
     a.kpm_bits = nullptr;
     a.kpm_words = 0;
     if (key_padding_mask) {

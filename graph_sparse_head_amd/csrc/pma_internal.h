@@ -122,7 +122,8 @@ struct EdgeArgs {
     float *scores;      // [nnz][B][H] log2-domain scores by CSR position, or nullptr
     float *weights;     // caller's weights or nullptr
     int average;
-    int xcd_map = 1;    // sample group fixed per XCD where the pass count divides 8
+    int xcd_map = 1;    // 1: sample group fixed per XCD where the group count
+                        // divides 8; 2: groups in turn; 0: interleaved
     int nt = 1;         // non-temporal q loads / mixed stores
     const uint64_t *kpm_bits = nullptr;  // key_padding_mask bits (pack_mask layout)
     int kpm_words = 0;                   // 64-bit words per source
@@ -169,6 +170,12 @@ struct BwdArgs {
     int64_t n_ttasks, n_tsplit, n_stasks, n_ssplit;
     int64_t s_band_off[kBands + 1];  // source pieces per band (one band per XCD)
     int banded;                      // 0: one band, launched in plain order
+    // target pass order over sample groups of 64 lanes (t_groups of them):
+    // 0 interleaved, 1 group g on the XCDs x with x % t_groups = g (t_groups
+    // divides 8), 2 groups in turn, -1 chosen at launch; t_gthreads threads
+    // per group (whole workgroups)
+    int t_order, t_groups;
+    int64_t t_gthreads;
     const uint64_t *kpm_bits;        // packed mask or nullptr
     int kpm_words;
     void *PZ;                        // [nnz][B][H] (p, dz) pairs: bf16 for bf16 plans, fp32 else

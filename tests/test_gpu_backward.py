@@ -182,3 +182,20 @@ def test_backward_read_sources_only(compact, shared, mask, monkeypatch):
     c.src, c.tgt = c.src[keep], c.tgt[keep]
     kpm = (np.random.default_rng(91).random((c.B, c.S)) < 0.3) if mask else None
     _grad_check(c, shared, kpm=kpm)
+
+
+# The target pass over sample groups of 64 lanes: interleaved (0), groups
+# pinned to XCDs (1) or groups in turn (2). bf16 E = 64 has 8 samples per
+# group: B = 16, 32, 64 give 2, 4 and 8 groups; B = 128 gives 16, which do not
+# divide the 8 XCDs (order 1 then falls back to 0); fp32 E = 128 with B = 6
+# gives 3 groups.
+@pytest.mark.parametrize("order", ["0", "1", "2"])
+@pytest.mark.parametrize("shape", [("bf16", 64, 4, 16), ("bf16", 64, 4, 32), ("bf16", 64, 4, 64),
+                                   ("bf16", 64, 4, 128), ("f32", 128, 8, 6)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_B{s[3]}")
+def test_backward_target_pass_order(order, shape, monkeypatch):
+    monkeypatch.setenv("PMA_BWD_ORDER", order)
+    monkeypatch.setenv("PMA_CHUNK", "5")   # split targets too
+    dt, E, H, B = shape
+    c = synth.random_case(97, B, 70, 70, E, H, 0.08, dtype=dt, same_kv=False, name="bwd_order")
+    _grad_check(c, "none")

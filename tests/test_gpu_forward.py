@@ -224,6 +224,8 @@ KNOBS = [
     {"PMA_XCD_MAP": "0", "PMA_NT": "0"},
     {"PMA_FUSE_IN": "0"},
     {"PMA_FUSE_IN": "0", "PMA_CHUNK": "3"},
+    {"PMA_XCD_MAP": "2"},
+    {"PMA_XCD_MAP": "2", "PMA_PERSIST": "1", "PMA_CHUNK": "3"},
 ]
 
 
@@ -263,6 +265,7 @@ def test_q_projection_in_edge_kernel(fuse_in, compact, shared, B, monkeypatch):
 
 
 @pytest.mark.parametrize("knobs", [{"PMA_PERSIST": "1"}, {"PMA_PERSIST": "1", "PMA_XCD_MAP": "1"},
+                                   {"PMA_PERSIST": "1", "PMA_XCD_MAP": "2"},
                                    {"PMA_PERSIST": "2", "PMA_CHUNK": "5"}],
                          ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
