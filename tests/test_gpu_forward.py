@@ -9,7 +9,7 @@ import torch
 import graph_sparse_head_amd as pma
 import oracle
 from graph_sparse_head_amd import synth
-from gpu_helpers import TOL, max_abs_rel, run, sample_rows
+from gpu_helpers import TOL, make_plan, max_abs_rel, run, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +124,29 @@ def test_split_targets(dt, deg, monkeypatch):
     perm = rng.permutation(c.src.shape[0])
     c.src, c.tgt = c.src[perm], c.tgt[perm]
     _full_check(c, need_weights=True, average=False)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_merge_repeated_calls(dt, monkeypatch):
+    """Repeated forwards on one plan with split targets, with batches of
+    different sample-group counts in between (the partial slots are reused),
+    give the oracle's result and bit-identical repeats."""
+    monkeypatch.setenv("PMA_CHUNK", "3")
+    big = synth.random_case(41, 37, 120, 120, 64, 4, 0.1, dtype=dt, name="merge_big")
+    small = synth.random_case(41, 5, 120, 120, 64, 4, 0.1, dtype=dt, name="merge_small")
+    small.src, small.tgt = big.src, big.tgt
+    plan = make_plan(big)
+    try:
+        first, w_first, _ = run(big, plan=plan, need_weights=True, average=False)
+        for case in (small, big, small):
+            out, w, _ = run(case, plan=plan, need_weights=True, average=False)
+            ref = oracle.case_forward(case, want_weights=True)
+            assert max_abs_rel(out, ref["out"]) <= TOL[dt]
+            assert max_abs_rel(w, ref["weights"]) <= TOL[dt]
+        again, w_again, _ = run(big, plan=plan, need_weights=True, average=False)
+        assert (again == first).all() and (w_again == w_first).all()
+    finally:
+        pma.pma_destroy(plan)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -250,14 +273,16 @@ def test_tuning_knobs(knobs, shape, monkeypatch):
 @pytest.mark.parametrize("compact", ["0", "1"])
 @pytest.mark.parametrize("shared", ["none", "kv", "qkv"])
 @pytest.mark.parametrize("B", [5, 37])
-def test_q_projection_in_edge_kernel(fuse_in, compact, shared, B, monkeypatch):
+@pytest.mark.parametrize("H", [1, 2, 4, 8])
+def test_q_projection_in_edge_kernel(fuse_in, compact, shared, B, H, monkeypatch):
     # bf16 at embed_dim 64: the edge kernel projects q from the query rows
     # itself (PMA_FUSE_IN=1, the default) or reads a separately projected q;
     # with shared tokens the key/value projection then runs on its own. B = 5
-    # leaves lanes without a sample, B = 37 a partial sample group.
+    # leaves lanes without a sample, B = 37 a partial sample group; H = 1..8
+    # puts a head on 8, 4, 2 or 1 lanes.
     monkeypatch.setenv("PMA_FUSE_IN", fuse_in)
     monkeypatch.setenv("PMA_COMPACT", compact)
-    c = synth.random_case(93, B, 300, 300, 64, 4, 0.02, dtype="bf16", same_kv=shared != "none",
+    c = synth.random_case(93, B, 300, 300, 64, H, 0.02, dtype="bf16", same_kv=shared != "none",
                           same_qkv=shared == "qkv", name="fuse_in")
     keep = c.src < 200   # sources 200.. are never read
     c.src, c.tgt = c.src[keep], c.tgt[keep]
