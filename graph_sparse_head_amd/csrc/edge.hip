@@ -60,6 +60,11 @@ struct EdgeK {
     const uint64_t *kpm_bits;
     int kpm_words;
     const int32_t *orig_src;
+    // the same bits by CSR position in 32-bit words: bit b % 32 of
+    // kpm_csr[p * kpm_w32 + b / 32] for the edge at p (edge_fast reads one
+    // uniform word per edge, two when a wavefront spans 64 samples)
+    const uint32_t *kpm_csr;
+    int kpm_w32;
     int nt;              // 1: non-temporal q loads and mixed stores
     float scale;         // log2(e) / sqrt(d)
     Layout lay;
@@ -362,16 +367,18 @@ __device__ inline uint4 q_proj_wave(const uint4 &x, int lane, const char *wlds)
 // address and discard the data. bf16 scores use v_dot2 on the stored bf16 q
 // and k words (fp32 products and sums) and are scaled afterwards. Edges run U
 // at a time, the remainder one at a time.
-template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeLane {
+// KPM: 0 no mask, 1 one mask word per position covers the wavefront's
+// samples, 2 two words (64 samples per wavefront: embed_dim = CH).
+template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
     static constexpr bool BF = sizeof(T) == 2;
 
     const EdgeK &a;
     const int32_t *src;   // gather rows, from a noalias kernel argument
-    const int32_t *osrc;  // source ids (for the key_padding_mask), noalias
-    const uint64_t *kbits;  // mask bits, from a noalias kernel argument
-    uint32_t kword;         // word of this wavefront's samples within a source's bits
+    const uint32_t *kbits;  // mask bits by CSR position, from a noalias kernel argument
+    uint32_t kword;         // first 32-bit word of this wavefront's samples at a position
+    bool khi;               // this lane's sample is in the second of two words (64 samples per wavefront)
     int B, b, h;
     bool active, head_lead;
     Chunk<T, CH> q;
@@ -425,6 +432,19 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
 
     template <int N> __device__ inline void step(int p)
     {
+        // mask words first, as uniform (scalar) loads in flight with the
+        // gathers; with 64 samples per wavefront both words of a position
+        uint32_t mlo[N], mhi[N];
+        if constexpr (KPM > 0) {
+#pragma unroll
+            for (int u = 0; u < N; ++u) {
+                const uint32_t i = __builtin_amdgcn_readfirstlane(
+                    (uint32_t)(p + u) * (uint32_t)a.kpm_w32 + kword);
+                mlo[u] = kbits[i];
+                if constexpr (KPM == 2)
+                    mhi[u] = kbits[i + 1];
+            }
+        }
         Chunk<T, CH> kk[N], vv[N];
 #pragma unroll
         for (int u = 0; u < N; ++u) gather(src[p + u], kk[u], vv[u]);
@@ -448,13 +468,15 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
             if constexpr (BF) dot *= smul;   // fp32 q carries the scale already
             sc[u] = dot;
         }
-        if constexpr (KPM) {   // masked keys leave the softmax
+        if constexpr (KPM > 0) {   // masked keys leave the softmax
             // one uniform 64-bit word per edge holds the bits of all the
             // wavefront's samples
 #pragma unroll
             for (int u = 0; u < N; ++u) {
-                const uint64_t w = kbits[(uint32_t)osrc[p + u] * (uint32_t)a.kpm_words + kword];
-                if ((w >> (b & 63)) & 1u)
+                uint32_t w = mlo[u];
+                if constexpr (KPM == 2)
+                    w = khi ? mhi[u] : w;
+                if ((w >> (b & 31)) & 1u)
                     sc[u] = -INFINITY;
             }
         }
@@ -490,7 +512,7 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
         }
         // With a mask a lane may have seen no live key yet (ms = -inf); its
         // masked scores must then give weight 0, not exp2(-inf + inf).
-        const float base = (KPM && ms == -INFINITY) ? 0.f : ms;
+        const float base = (KPM > 0 && ms == -INFINITY) ? 0.f : ms;
 #pragma unroll
         for (int u = 0; u < N; ++u) {
             const float pe = fast_exp2(sc[u] - base);
@@ -516,13 +538,12 @@ template <typename T, int CH, int LPH, bool W32, bool SC, bool KPM> struct EdgeL
     }
 };
 
-template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, bool KPM>
+template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, int KPM>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(8)))   // 64 VGPRs
 edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
           const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end,
-          const int32_t *__restrict__ task_slot, const int32_t *__restrict__ orig_src,
-          const uint64_t *__restrict__ kpm_bits)
+          const int32_t *__restrict__ task_slot, const uint32_t *__restrict__ kpm_csr)
 {
     // The index arrays come in as noalias arguments: no store of this kernel
     // can reach them, so their wave-uniform reads stay scalar loads.
@@ -566,7 +587,6 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
 
     EdgeLane<T, CH, LPH, W32, SC, KPM> st(a);
     st.src = csr_src;
-    st.osrc = orig_src;
     const int B = a.B, E = a.E;
     const int cpr = E / CH;                       // chunks per sample row
     const uint32_t c = pass * 64 + lane;
@@ -579,8 +599,9 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     st.h = st.active ? cr / LPH : 0;
     st.head_lead = (lane % LPH) == 0;
     st.smul = a.scale;
-    st.kbits = kpm_bits;
-    st.kword = (pass * 64u / (uint32_t)cpr) >> 6;   // first sample of the pass / 64
+    st.kbits = kpm_csr;
+    st.kword = (pass * 64u / (uint32_t)cpr) >> 5;   // first sample of the pass / 32
+    st.khi = cpr == 1 && (b & 32) != 0;
     // byte offsets: per source (uniform), this lane's key and value chunks
     st.row2 = (uint64_t)a.lay.kv_s * sizeof(T);
     if constexpr (W32) {
@@ -991,6 +1012,8 @@ EdgeK make_k(const EdgeArgs &x)
     k.xcd_map = x.xcd_map;
     k.tstride = 0;
     k.kpm_bits = x.kpm_bits;
+    k.kpm_csr = x.kpm_csr;
+    k.kpm_w32 = x.kpm_w32;
     k.kpm_words = x.kpm_words;
     k.orig_src = g->csr_src;
     k.nt = x.nt;
@@ -1067,22 +1090,34 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     const unsigned nb = (unsigned)blocks;
 #define PMA_EDGE_LAUNCH(W, S, M)                                                          \
     edge_fast<T, CH, LPH, 4, E_FUSE, QF, W, S, M><<<nb, 256, 0, s>>>(                    \
-        k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.orig_src, k.kpm_bits)
+        k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.kpm_csr)
     if (k.kpm_bits) {
+        if (!k.kpm_csr)
+            return hipErrorInvalidValue;
         if (!w32)   // refused by mask_supported()
             return hipErrorInvalidValue;
-        if (k.scores)
-            PMA_EDGE_LAUNCH(true, true, true);
-        else
-            PMA_EDGE_LAUNCH(true, false, true);
+        if (k.E / CH == 1) {   // 64 samples per wavefront: two mask words
+            if constexpr (LPH == 1 && E_FUSE == 0) {
+                if (k.scores)
+                    PMA_EDGE_LAUNCH(true, true, 2);
+                else
+                    PMA_EDGE_LAUNCH(true, false, 2);
+            } else {
+                return hipErrorInvalidValue;   // (E = CH means one chunk per head)
+            }
+        } else if (k.scores) {
+            PMA_EDGE_LAUNCH(true, true, 1);
+        } else {
+            PMA_EDGE_LAUNCH(true, false, 1);
+        }
     } else if (w32 && k.scores)
-        PMA_EDGE_LAUNCH(true, true, false);
+        PMA_EDGE_LAUNCH(true, true, 0);
     else if (w32)
-        PMA_EDGE_LAUNCH(true, false, false);
+        PMA_EDGE_LAUNCH(true, false, 0);
     else if (k.scores)
-        PMA_EDGE_LAUNCH(false, true, false);
+        PMA_EDGE_LAUNCH(false, true, 0);
     else
-        PMA_EDGE_LAUNCH(false, false, false);
+        PMA_EDGE_LAUNCH(false, false, 0);
 #undef PMA_EDGE_LAUNCH
     return hipGetLastError();
 }
@@ -1181,13 +1216,30 @@ __global__ void pack_mask_kernel(const uint8_t *mask, int64_t bstride, int64_t B
     if (i >= S * words)
         return;
     const int64_t w = i / S, s = i - w * S;
+    const int nb = (int)(B - w * 64 < 64 ? B - w * 64 : 64);
+    // all 64 loads independent (samples past B re-read the last one and are
+    // dropped), so they are in flight together
     uint64_t v = 0;
+#pragma unroll
     for (int j = 0; j < 64; ++j) {
-        const int64_t b = w * 64 + j;
-        if (b < B && mask[b * bstride + s])
-            v |= (uint64_t)1 << j;
+        const int64_t b = w * 64 + (j < nb ? j : nb - 1);
+        const uint64_t m = mask[b * bstride + s] != 0 && j < nb;
+        v |= m << j;
     }
     bits[s * words + w] = v;
+}
+
+// The packed bits in CSR order, as 32-bit words:
+// out[p * w32 + j] = half j % 2 of bits[src[p] * words + j / 2].
+__global__ void gather_mask_kernel(const uint64_t *bits, int words, int w32, const int32_t *src,
+                                   int64_t nnz, uint32_t *out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nnz * w32)
+        return;
+    const int64_t p = i / w32;
+    const int j = (int)(i - p * w32);
+    out[i] = (uint32_t)(bits[(int64_t)src[p] * words + j / 2] >> (32 * (j & 1)));
 }
 
 }  // namespace
@@ -1201,8 +1253,21 @@ pma_status pack_mask(const uint8_t *mask, int64_t bstride, int64_t B, int64_t S,
     return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
+pma_status gather_mask(const uint64_t *bits, int words, int w32, const int32_t *src, int64_t nnz,
+                       uint32_t *out, hipStream_t s)
+{
+    const int64_t n = nnz * w32;
+    if (n == 0)
+        return PMA_OK;
+    gather_mask_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(bits, words, w32, src, nnz, out);
+    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+}
+
 bool mask_supported(const EdgeArgs &x)
 {
+    // the per-position mask words are indexed with 32 bits
+    if ((uint64_t)x.nnz * (uint64_t)((x.B + 31) / 32) >= ((uint64_t)1 << 31))
+        return false;
     const EdgeK k = make_k(x);
     const int64_t ch = x.dt == PMA_BF16 ? 8 : 4, d = x.E / x.H;
     const bool fast = d % ch == 0 && (d / ch) <= 16 && ((d / ch) & (d / ch - 1)) == 0;

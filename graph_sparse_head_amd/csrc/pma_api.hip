@@ -60,6 +60,7 @@ struct pma_plan {
     void *qt = nullptr, *kv = nullptr, *mixed = nullptr;
     float *part_acc = nullptr, *part_ml = nullptr, *stat_ml = nullptr, *scores = nullptr;
     uint64_t *kpm_bits = nullptr;   // key_padding_mask packed by source
+    uint32_t *kpm_csr = nullptr;    // the same by CSR position (32-bit words)
     // backward and PackedLinear scratch, grown on demand
     char *bw = nullptr;
     size_t bw_bytes = 0;
@@ -78,13 +79,14 @@ namespace {
 void free_workspace(pma_plan *p)
 {
     void *ptrs[] = {p->qt,     p->kv,      p->mixed,  p->part_acc,
-                    p->part_ml, p->stat_ml, p->scores, p->kpm_bits};
+                    p->part_ml, p->stat_ml, p->scores, p->kpm_bits, p->kpm_csr};
     for (void *q : ptrs)
         if (q)
             (void)hipFree(q);
     p->qt = p->kv = p->mixed = nullptr;
     p->part_acc = p->part_ml = p->stat_ml = p->scores = nullptr;
     p->kpm_bits = nullptr;
+    p->kpm_csr = nullptr;
     p->ws_B = 0;
     p->ws_weights = false;
 }
@@ -116,6 +118,7 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
         {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
         {(void **)&p->scores, nw ? (size_t)p->nnz * nB * p->H * 4 : 0},
         {(void **)&p->kpm_bits, (size_t)p->S * ((nB + 63) / 64) * 8},
+        {(void **)&p->kpm_csr, (size_t)p->nnz * ((nB + 31) / 32) * 4},
     };
     for (auto &w : want) {
         if (w.bytes == 0)
@@ -611,6 +614,12 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
             return fail(st, "mask packing failed: %s", hipGetErrorString(hipGetLastError()));
         ea.kpm_bits = p->kpm_bits;
         ea.kpm_words = (int)((B + 63) / 64);
+        ea.kpm_w32 = (int)((B + 31) / 32);
+        st = pma::gather_mask(p->kpm_bits, ea.kpm_words, ea.kpm_w32, p->g.csr_src, p->nnz,
+                              p->kpm_csr, stream);
+        if (st != PMA_OK)
+            return fail(st, "mask packing failed: %s", hipGetErrorString(hipGetLastError()));
+        ea.kpm_csr = p->kpm_csr;
     }
     // Automatic choices (measured on MI355X): stream q and mixed past the
     // caches only when the workspace outgrows the 256 MB last-level cache;

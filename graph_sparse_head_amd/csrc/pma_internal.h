@@ -126,6 +126,8 @@ struct EdgeArgs {
                         // divides 8; 2: groups in turn; 0: interleaved
     int nt = 1;         // non-temporal q loads / mixed stores
     const uint64_t *kpm_bits = nullptr;  // key_padding_mask bits (pack_mask layout)
+    const uint32_t *kpm_csr = nullptr;   // the same by CSR position (gather_mask)
+    int kpm_w32 = 0;                     // its 32-bit words per position
     int kpm_words = 0;                   // 64-bit words per source
     int persist = 0;    // edge kernel: workgroups per CU, each wavefront walking
                         // several pieces (0: one wavefront per piece and pass)
@@ -149,6 +151,10 @@ bool q_fusable(int64_t E, int64_t H, pma_dtype dt);
 // ceil(B / 64). Asynchronous on s.
 pma_status pack_mask(const uint8_t *mask, int64_t bstride, int64_t B, int64_t S, uint64_t *bits,
                      hipStream_t s);
+// bits by CSR position in 32-bit words (w32 = ceil(B / 32) per position):
+// out[p * w32 + j] = half j % 2 of bits[src[p] * words + j / 2].
+pma_status gather_mask(const uint64_t *bits, int words, int w32, const int32_t *src, int64_t nnz,
+                       uint32_t *out, hipStream_t s);
 
 // ---- backward pass (backward.hip) ------------------------------------------
 

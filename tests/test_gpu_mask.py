@@ -61,6 +61,21 @@ def test_mask_per_sample(shape, frac):
     _check(c, kpm, need_weights=True, average=False)
 
 
+# Samples per wavefront of the fast kernel: 64 / (E / chunk). One 32-bit mask
+# word per edge covers them up to 32 samples; embed_dim = chunk (fp32 E = 4,
+# bf16 E = 8) puts 64 samples on a wavefront and two words; B = 70 leaves a
+# partial last group; bf16 E = 16 has 32 samples per wavefront.
+@pytest.mark.parametrize("shape", [("f32", 4, 1), ("bf16", 8, 1), ("bf16", 16, 2), ("f32", 8, 2)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_H{s[2]}")
+def test_mask_many_samples_per_wavefront(shape):
+    dt, E, H = shape
+    c = synth.random_case(79, 70, 60, 60, E, H, 0.1, dtype=dt, name="mask_wide")
+    kpm = np.random.default_rng(80).random((c.B, c.S)) < 0.3
+    kpm[33] = True                                               # a sample of the second word
+    kpm[64] = True                                               # and of the third
+    _check(c, kpm, need_weights=True, average=True)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_mask_shared_and_leading_axes(dt):
     c = synth.random_case(72, 6, 70, 110, 64, 4, 0.1, dtype=dt, same_kv=True, name="mask_kv")
