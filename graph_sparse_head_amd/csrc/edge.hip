@@ -430,7 +430,11 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLa
     float smul, ms = -INFINITY;
     bool fresh = true;
 
-    template <int N> __device__ inline void step(int p)
+    // N live edges starting at CSR position p; with PRE the source ids of the
+    // next N edges are read into nsrc after this step's gathers are issued
+    // (so that the next step's gathers need not wait for them).
+    int nsrc[4];
+    template <int N, bool PRE = false> __device__ inline void step(int p, const int *csrc = nullptr)
     {
         // mask words first, as uniform (scalar) loads in flight with the
         // gathers; with 64 samples per wavefront both words of a position
@@ -447,7 +451,11 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLa
         }
         Chunk<T, CH> kk[N], vv[N];
 #pragma unroll
-        for (int u = 0; u < N; ++u) gather(src[p + u], kk[u], vv[u]);
+        for (int u = 0; u < N; ++u) gather(csrc ? csrc[u] : src[p + u], kk[u], vv[u]);
+        if constexpr (PRE) {
+#pragma unroll
+            for (int u = 0; u < N; ++u) nsrc[u] = src[p + N + u];
+        }
         float sc[N];
 #pragma unroll
         for (int u = 0; u < N; ++u) {
@@ -660,8 +668,24 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
 
         static_assert(U == 4, "the tail below covers up to 3 edges");
         int p = beg;
-        for (; p + U <= end; p += U)
-            st.template step<U>(p);
+        if constexpr (KPM == 0) {
+            for (; p + U <= end; p += U)
+                st.template step<U>(p);
+        } else if (p + U <= end) {
+            // full steps; each reads the next step's source ids in flight
+            // (measured: pays with the mask's extra scalar loads, costs 2-5 %
+            // without them)
+            int cs[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) cs[u] = csr_src[p + u];
+            for (; p + 2 * U <= end; p += U) {
+                st.template step<U, true>(p, cs);
+#pragma unroll
+                for (int u = 0; u < U; ++u) cs[u] = st.nsrc[u];
+            }
+            st.template step<U>(p, cs);
+            p += U;
+        }
         if (p + 2 <= end) {
             st.template step<2>(p);
             p += 2;
