@@ -203,13 +203,22 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dq[i] = 0.f;
-    int s[kU], sn[kU];   // sources (for the mask); rows come through kv_src
+    // Mask: with whole wavefronts per piece and at most 32 samples per
+    // wavefront, one 32-bit word per CSR position (uniform: a scalar load)
+    // holds the bits of the wavefront's samples; otherwise each lane looks up
+    // its sample's bit by source.
+    const bool csr_mask = UNI && a.kpm_csr && CPR > 1;
+    const uint32_t kw = csr_mask ? (uint32_t)__builtin_amdgcn_readfirstlane(b) >> 5 : 0u;
+    int s[kU], sn[kU];   // mask words (csr_mask) or sources; rows come through kv_src
     uint4 kr[kU], vr[kU], kn[kU], vn[kU];
     auto fetch = [&](int p0, int (&ss)[kU], uint4 (&kq)[kU], uint4 (&vq)[kU]) {
         int r[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            ss[u] = a.csr_src[p0 + u];
+            if (csr_mask)
+                ss[u] = (int)a.kpm_csr[(uint32_t)(p0 + u) * (uint32_t)a.kpm_w32 + kw];
+            else
+                ss[u] = a.csr_src[p0 + u];
             r[u] = a.kv_src[p0 + u];
         }
 #pragma unroll
@@ -240,7 +249,9 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
             const int p = p0 + u;
             if (p < end) {
                 float pe = 0.f, dz = 0.f;
-                if (ml.y > 0.f && !masked(a, s[u], b)) {
+                const bool off = csr_mask ? (((uint32_t)s[u] >> (b & 31)) & 1u) != 0
+                                          : masked(a, s[u], b);
+                if (ml.y > 0.f && !off) {
                     pe = __builtin_amdgcn_exp2f(z * a.scale_log2 - ml.x) / ml.y;
                     dz = pe * (dp - D);
                 }

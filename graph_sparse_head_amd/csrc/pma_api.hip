@@ -118,7 +118,8 @@ pma_status ensure_workspace(pma_plan *p, int64_t B, bool weights, hipStream_t s)
         {(void **)&p->stat_ml, nw ? (size_t)p->L * nB * p->H * 2 * 4 : 0},
         {(void **)&p->scores, nw ? (size_t)p->nnz * nB * p->H * 4 : 0},
         {(void **)&p->kpm_bits, (size_t)p->S * ((nB + 63) / 64) * 8},
-        {(void **)&p->kpm_csr, (size_t)p->nnz * ((nB + 31) / 32) * 4},
+        // (+ 4 positions: the backward reads mask words 4 edges at a time)
+        {(void **)&p->kpm_csr, (size_t)(p->nnz + 4) * ((nB + 31) / 32) * 4},
     };
     for (auto &w : want) {
         if (w.bytes == 0)
@@ -881,6 +882,8 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     a.t_order = p->border;
     a.kpm_bits = nullptr;
     a.kpm_words = 0;
+    a.kpm_csr = nullptr;
+    a.kpm_w32 = 0;
     if (key_padding_mask) {
         pma_status st2 = ensure_workspace(p, B, false, stream);
         if (st2 != PMA_OK)
@@ -888,6 +891,10 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         ok(pma::pack_mask(key_padding_mask, mask_per_sample ? S : 0, B, S, p->kpm_bits, stream));
         a.kpm_bits = p->kpm_bits;
         a.kpm_words = (int)((B + 63) / 64);
+        a.kpm_w32 = (int)((B + 31) / 32);
+        ok(pma::gather_mask(p->kpm_bits, a.kpm_words, a.kpm_w32, gd.csr_src, p->nnz, p->kpm_csr,
+                            stream));
+        a.kpm_csr = p->kpm_csr;
     }
     a.PZ = PZ;
     a.part_q = part;

@@ -184,6 +184,8 @@ struct BwdArgs {
     int64_t t_gthreads;
     const uint64_t *kpm_bits;        // packed mask or nullptr
     int kpm_words;
+    const uint32_t *kpm_csr;         // the mask by CSR position (gather_mask), or nullptr
+    int kpm_w32;
     void *PZ;                        // [nnz][B][H] (p, dz) pairs: bf16 for bf16 plans, fp32 else
     float *part_q;                   // [target slot][B][E] partial dq
     float *part_kv;                  // [source slot][B][2E] partial dk, dv

@@ -199,3 +199,18 @@ def test_backward_target_pass_order(order, shape, monkeypatch):
     dt, E, H, B = shape
     c = synth.random_case(97, B, 70, 70, E, H, 0.08, dtype=dt, same_kv=False, name="bwd_order")
     _grad_check(c, "none")
+
+
+# key_padding_mask in the fast target pass: whole wavefronts per piece read
+# one mask word per edge (bf16 E = 64 at B = 16: 8 samples per wavefront;
+# fp32 E = 128 at B = 8: 2), with split pieces; bf16 E = 8 puts 64 samples on
+# a wavefront and looks the bits up per lane.
+@pytest.mark.parametrize("shape", [("bf16", 64, 4, 16), ("f32", 128, 8, 8), ("bf16", 8, 1, 64)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_B{s[3]}")
+def test_backward_mask_whole_wavefronts(shape, monkeypatch):
+    monkeypatch.setenv("PMA_CHUNK", "5")
+    dt, E, H, B = shape
+    c = synth.random_case(98, B, 60, 60, E, H, 0.1, dtype=dt, same_kv=False, name="bwd_mask_uni")
+    kpm = np.random.default_rng(99).random((c.B, c.S)) < 0.3
+    kpm[1] = True                                    # one sample entirely masked
+    _grad_check(c, "none", kpm=kpm)
