@@ -144,7 +144,9 @@ __device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uin
 // (entry 0 is a valid row); the next kU edges' rows are in flight while the
 // current ones are used.
 
-template <typename T, int LPH, bool UNI>
+// CM (UNI only): the mask comes as one uniform word per CSR position
+// (kpm_csr); otherwise each lane looks its bit up by source.
+template <typename T, int LPH, bool UNI, bool CM = false>
 __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
 {
     constexpr int VEC = Vec<T>::N;
@@ -207,15 +209,15 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
     // wavefront, one 32-bit word per CSR position (uniform: a scalar load)
     // holds the bits of the wavefront's samples; otherwise each lane looks up
     // its sample's bit by source.
-    const bool csr_mask = UNI && a.kpm_csr && CPR > 1;
-    const uint32_t kw = csr_mask ? (uint32_t)__builtin_amdgcn_readfirstlane(b) >> 5 : 0u;
+    static_assert(!CM || UNI, "uniform mask words need whole wavefronts per piece");
+    const uint32_t kw = CM ? (uint32_t)__builtin_amdgcn_readfirstlane(b) >> 5 : 0u;
     int s[kU], sn[kU];   // mask words (csr_mask) or sources; rows come through kv_src
     uint4 kr[kU], vr[kU], kn[kU], vn[kU];
     auto fetch = [&](int p0, int (&ss)[kU], uint4 (&kq)[kU], uint4 (&vq)[kU]) {
         int r[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            if (csr_mask)
+            if constexpr (CM)
                 ss[u] = (int)a.kpm_csr[(uint32_t)(p0 + u) * (uint32_t)a.kpm_w32 + kw];
             else
                 ss[u] = a.csr_src[p0 + u];
@@ -249,8 +251,11 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
             const int p = p0 + u;
             if (p < end) {
                 float pe = 0.f, dz = 0.f;
-                const bool off = csr_mask ? (((uint32_t)s[u] >> (b & 31)) & 1u) != 0
-                                          : masked(a, s[u], b);
+                bool off;
+                if constexpr (CM)
+                    off = (((uint32_t)s[u] >> (b & 31)) & 1u) != 0;
+                else
+                    off = masked(a, s[u], b);
                 if (ml.y > 0.f && !off) {
                     pe = __builtin_amdgcn_exp2f(z * a.scale_log2 - ml.x) / ml.y;
                     dz = pe * (dp - D);
@@ -1068,6 +1073,8 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
         const int64_t nt = a.n_ttasks * a.B * cpr, ns = a.n_stasks * a.B * cpr;
         // a piece's lanes fill whole wavefronts: wavefront-uniform indices
         const bool uni = ((int64_t)a.B * cpr) % 64 == 0;
+        // mask words by CSR position: whole wavefronts of at most 32 samples
+        const bool cm = uni && a.kpm_csr && cpr > 1;
         // source pass with UNI: kBands interleaved runs of workgroups
         int64_t per_band = 0;
         for (int k = 0; k < kBands; ++k) {
@@ -1104,7 +1111,10 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
 #define PMA_BWD_EDGE(L_)                                                            \
     case L_:                                                                       \
         if (uni) {                                                                 \
-            bwd_target_fast<T, L_, true><<<gt, 256, 0, s>>>(at);                  \
+            if (cm)                                                                \
+                bwd_target_fast<T, L_, true, true><<<gt, 256, 0, s>>>(at);         \
+            else                                                                   \
+                bwd_target_fast<T, L_, true><<<gt, 256, 0, s>>>(at);               \
             if (a.banded)                                                          \
                 bwd_source_fast<T, L_, true><<<gs_band, 256, 0, s>>>(a);           \
             else                                                                   \
