@@ -128,7 +128,10 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int nblk = a.nblk;
     char *wl = lds;                                      // nblk * NT * NKS KB
-    char *stage = lds + nblk * NT * NKS * 1024 + (threadIdx.x >> 6) * (ROWS * PITCH);
+    // the biases as fp32 (zeros without bias) after the fragments, so that
+    // the compute loop reads no global memory besides the x prefetch
+    float *bl = reinterpret_cast<float *>(lds + nblk * NT * NKS * 1024);
+    char *stage = lds + nblk * NT * NKS * 1024 + nblk * E * 4 + (threadIdx.x >> 6) * (ROWS * PITCH);
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -142,6 +145,18 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
         const T *src = W + (int64_t)(nt * 16 + (l & 15)) * E + ks * Elem<T>::kStep +
                        (l >> 4) * Elem<T>::kVec;
         *reinterpret_cast<uint4 *>(wl + c * 16) = *reinterpret_cast<const uint4 *>(src);
+    }
+    for (int c = threadIdx.x; c < nblk * E; c += WAVES * 64) {
+        const int blk = c / E, n = c - blk * E;
+        const T *bias = reinterpret_cast<const T *>(a.out[blk].b);
+        float v = 0.f;
+        if (bias) {
+            if constexpr (sizeof(T) == 2)
+                v = bf2f(bias[n]);
+            else
+                v = bias[n];
+        }
+        bl[c] = v;
     }
     __syncthreads();
 
@@ -181,7 +196,6 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
         }
         for (int blk = 0; blk < nblk; ++blk) {
             const ProjOut &o = a.out[blk];
-            const T *bias = reinterpret_cast<const T *>(o.b);
 #pragma unroll 2
             for (int nt = 0; nt < NT; ++nt) {
                 f32x4 acc[RG];
@@ -209,16 +223,8 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
                 }
                 // lane holds channels n = nt*16 + 4*lg + i of row (rg*16 + lr)
                 const int n = nt * 16 + 4 * lg;
-                float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (bias) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if constexpr (sizeof(T) == 2)
-                            bv[i] = bf2f(bias[n + i]);
-                        else
-                            bv[i] = bias[n + i];
-                    }
-                }
+                const float4 b4 = *reinterpret_cast<const float4 *>(bl + blk * E + n);
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
                     if constexpr (STAGE) {
@@ -315,7 +321,7 @@ hipError_t run_mfma(const ProjArgs &a, hipStream_t s)
 {
     constexpr int NKS = K / Elem<T>::kStep;
     constexpr int PITCH = K * (int)sizeof(T) + 16;
-    const size_t wbytes = (size_t)a.nblk * (K / 16) * NKS * 1024;
+    const size_t wbytes = (size_t)a.nblk * (K / 16) * NKS * 1024 + (size_t)a.nblk * K * 4;
     const size_t lds = wbytes + (sizeof(T) == 2 ? (size_t)WAVES * RG * 16 * PITCH : 0);
     if (lds > (size_t)kLdsBytes) {
         // weights of all blocks do not fit: one launch per output block
