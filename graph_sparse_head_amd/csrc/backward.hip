@@ -28,6 +28,7 @@
 #include "pma_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace pma {
 namespace {
@@ -115,6 +116,19 @@ template <typename T> __device__ inline float2 get_pz(const void *pz, int64_t o)
         return reinterpret_cast<const float2 *>(pz)[o];
     }
 }
+// The stored pair as loaded (bf16 pair or fp32 pair), widened only where it
+// is used, so that a load issued ahead is not waited for at once.
+template <typename T> struct PZRaw {
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, float2>::type type;
+};
+template <typename T> __device__ inline typename PZRaw<T>::type load_pz(const void *pz, int64_t o)
+{
+    return reinterpret_cast<const typename PZRaw<T>::type *>(pz)[o];
+}
+__device__ inline float pz_p(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float pz_dz(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline float pz_p(float2 v) { return v.x; }
+__device__ inline float pz_dz(float2 v) { return v.y; }
 
 constexpr int kU = 4;   // edges whose rows are loaded together
 
@@ -322,9 +336,10 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dk[i] = dv[i] = 0.f;
-    float pz[kU], dz[kU], pzn[kU], dzn[kU];
+    typedef typename PZRaw<T>::type PZT;
+    PZT pz[kU], pzn[kU];
     uint4 qr[kU], mr[kU], qn[kU], mn[kU];
-    auto fetch = [&](int j0, float (&pp)[kU], float (&zz)[kU], uint4 (&qq)[kU], uint4 (&mm)[kU]) {
+    auto fetch = [&](int j0, PZT (&pp)[kU], uint4 (&qq)[kU], uint4 (&mm)[kU]) {
         int t[kU], pos[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -334,41 +349,43 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t o = ((int64_t)pos[u] * a.B + b) * a.H + h;
-            const float2 v = get_pz<T>(a.PZ, o);
-            pp[u] = v.x;
-            zz[u] = v.y;
+            pp[u] = load_pz<T>(a.PZ, o);
             qq[u] = ld16(Qb + (int64_t)t[u] * a.E);
             mm[u] = ld16(Mb + (int64_t)t[u] * a.E);
         }
     };
-    if (beg < end)
-        fetch(beg, pz, dz, qr, mr);
-    for (int j0 = beg; j0 < end; j0 += kU) {
-        const bool more = j0 + kU < end;
-        if (more)
-            fetch(j0 + kU, pzn, dzn, qn, mn);
+    auto batch = [&](int j0, auto full) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            if (j0 + u < end) {
+            if (decltype(full)::value || j0 + u < end) {
                 float qq[VEC], mm[VEC];
                 widen<T>(qr[u], qq);
                 widen<T>(mr[u], mm);
+                const float pu = pz_p(pz[u]), du = pz_dz(pz[u]);
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
-                    dk[i] = fmaf(dz[u], qq[i], dk[i]);
-                    dv[i] = fmaf(pz[u], mm[i], dv[i]);
+                    dk[i] = fmaf(du, qq[i], dk[i]);
+                    dv[i] = fmaf(pu, mm[i], dv[i]);
                 }
             }
         }
-        if (more) {
+    };
+    // as in the target pass: the successor is fetched first, the last batch
+    // runs after the loop
+    if (beg < end) {
+        fetch(beg, pz, qr, mr);
+        int j0 = beg;
+        for (; j0 + kU < end; j0 += kU) {
+            fetch(j0 + kU, pzn, qn, mn);
+            batch(j0, std::true_type{});
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 pz[u] = pzn[u];
-                dz[u] = dzn[u];
                 qr[u] = qn[u];
                 mr[u] = mn[u];
             }
         }
+        batch(j0, std::false_type{});
     }
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
