@@ -946,35 +946,102 @@ template <typename F> __device__ inline void head_weights(const float *sc, const
     }
 }
 
+// HC: the head count as a constant (its loops unrolled, loads batched), or 0.
+template <int HC>
 __global__ void __launch_bounds__(256) weights_kernel(EdgeK a)
 {
     extern __shared__ float wt[];   // [samples of the chunk][kWeightTile] head averages
-    const int B = a.B, H = a.H;
+    const int B = a.B, H = HC > 0 ? HC : a.H;
     const int64_t p0 = (int64_t)blockIdx.x * kWeightTile;
     const int b0 = blockIdx.y * kWeightSamples;
     const int np = (int)(a.nnz - p0 < kWeightTile ? a.nnz - p0 : kWeightTile);
     const int nb = B - b0 < kWeightSamples ? B - b0 : kWeightSamples;
-    for (int i = threadIdx.x; i < np * nb; i += blockDim.x) {
-        const int pl = i / nb, bl = i - pl * nb, b = b0 + bl;
-        const int64_t p = p0 + pl;
-        const int t = a.csr_tgt[p];
-        const float *sc = a.scores + (p * B + b) * H;
-        const float *st = a.stat_ml + ((int64_t)t * B + b) * H * 2;
-        if (a.average) {
-            float sum = 0.f;
-            head_weights(sc, st, H, [&](int, float w) { sum += w; });
-            wt[bl * kWeightTile + pl] = sum / (float)H;
-        } else {
+    const int n = np * nb;
+    if (!a.average) {
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int pl = i / nb, bl = i - pl * nb, b = b0 + bl;
+            const int64_t p = p0 + pl;
+            const int t = a.csr_tgt[p];
+            const float *sc = a.scores + (p * B + b) * H;
+            const float *st = a.stat_ml + ((int64_t)t * B + b) * H * 2;
             float *w = a.weights + ((int64_t)b * a.nnz + a.csr_eid[p]) * H;
             head_weights(sc, st, H, [&](int h, float v) { w[h] = v; });
         }
-    }
-    if (!a.average)
         return;
+    }
+    // Averaged: KB pairs per thread at a time, every load of the KB pairs
+    // issued before any is used (indices past the end re-read the last pair;
+    // only the LDS stores are guarded).
+    constexpr int KB = 4;
+    for (int i0 = threadIdx.x; i0 < n; i0 += KB * blockDim.x) {
+        int pl[KB], bl[KB], t[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int i = min(i0 + k * (int)blockDim.x, n - 1);
+            pl[k] = i / nb;
+            bl[k] = i - pl[k] * nb;
+            t[k] = a.csr_tgt[p0 + pl[k]];
+        }
+        float v[KB];
+        if constexpr (HC > 0 && HC % 4 == 0) {
+            // every pair's scores and statistics as 16-byte loads, then the sums
+            float4 s4[KB][HC / 4], m4[KB][HC / 2];
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int b = b0 + bl[k];
+                const float4 *sc = reinterpret_cast<const float4 *>(a.scores + ((p0 + pl[k]) * B + b) * HC);
+                const float4 *st = reinterpret_cast<const float4 *>(a.stat_ml + ((int64_t)t[k] * B + b) * HC * 2);
+#pragma unroll
+                for (int j = 0; j < HC / 4; ++j) s4[k][j] = sc[j];
+#pragma unroll
+                for (int j = 0; j < HC / 2; ++j) m4[k][j] = st[j];
+            }
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                float sum = 0.f;
+#pragma unroll
+                for (int j = 0; j < HC / 4; ++j) {
+                    const float4 a0 = m4[k][2 * j], a1 = m4[k][2 * j + 1];
+                    sum += edge_weight(s4[k][j].x, a0.x, a0.y);
+                    sum += edge_weight(s4[k][j].y, a0.z, a0.w);
+                    sum += edge_weight(s4[k][j].z, a1.x, a1.y);
+                    sum += edge_weight(s4[k][j].w, a1.z, a1.w);
+                }
+                v[k] = sum / (float)HC;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int b = b0 + bl[k];
+                const float *sc = a.scores + ((p0 + pl[k]) * B + b) * H;
+                const float *st = a.stat_ml + ((int64_t)t[k] * B + b) * H * 2;
+                float sum = 0.f;
+                head_weights(sc, st, H, [&](int, float w) { sum += w; });
+                v[k] = sum / (float)H;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            if (i0 + k * (int)blockDim.x < n)
+                wt[bl[k] * kWeightTile + pl[k]] = v[k];
+        }
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < np * nb; i += blockDim.x) {
-        const int bl = i / np, pl = i - bl * np;
-        a.weights[(int64_t)(b0 + bl) * a.nnz + a.csr_eid[p0 + pl]] = wt[bl * kWeightTile + pl];
+    // each sample's weights in edge order (positions fastest), KB at a time
+    for (int i0 = threadIdx.x; i0 < n; i0 += KB * blockDim.x) {
+        int e[KB], bl[KB], pl[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int i = min(i0 + k * (int)blockDim.x, n - 1);
+            bl[k] = i / np;
+            pl[k] = i - bl[k] * np;
+            e[k] = a.csr_eid[p0 + pl[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            if (i0 + k * (int)blockDim.x < n)
+                a.weights[(int64_t)(b0 + bl[k]) * a.nnz + e[k]] = wt[bl[k] * kWeightTile + pl[k]];
+        }
     }
 }
 
@@ -1359,7 +1426,14 @@ pma_status launch_weights(const EdgeArgs &x, hipStream_t s)
     const size_t lds = x.average ? (size_t)chunk_b * kWeightTile * sizeof(float) : 0;
     const dim3 g((unsigned)((k.nnz + kWeightTile - 1) / kWeightTile),
                  (unsigned)((k.B + kWeightSamples - 1) / kWeightSamples));
-    weights_kernel<<<g, 256, lds, s>>>(k);
+    switch (k.average ? k.H : 0) {   // (per-head weights: the plain loop)
+    case 1: weights_kernel<1><<<g, 256, lds, s>>>(k); break;
+    case 2: weights_kernel<2><<<g, 256, lds, s>>>(k); break;
+    case 4: weights_kernel<4><<<g, 256, lds, s>>>(k); break;
+    case 8: weights_kernel<8><<<g, 256, lds, s>>>(k); break;
+    case 16: weights_kernel<16><<<g, 256, lds, s>>>(k); break;
+    default: weights_kernel<0><<<g, 256, lds, s>>>(k); break;
+    }
     return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
