@@ -186,31 +186,39 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 // Wo as MFMA A fragments in LDS: fragment (n-tile nt, k-group kg) is 64
 // lanes x 16 bytes at byte ((nt * KG + kg) * 64 + lane) * 16, lane l holding
 // output channel (E/4)(l%16 / 4) + 4 nt + l%4 at channels (4 kg + l/16) * CH.
+// (Workgroups of 256 threads: each thread's loads are issued together, then
+// stored, so staging costs one memory round trip.)
 template <typename T, int CH, int E>
 __device__ inline void stage_w(const void *w, const void *b, char *wlds)
 {
     constexpr int KG = E / (4 * CH), NT = E / 16, CPL = E / 4;
+    constexpr int NF = NT * KG * 64 / 256;   // fragment chunks per thread
+    static_assert(NT * KG * 64 % 256 == 0 && E <= 256, "256 threads stage whole fragments");
     const T *W = reinterpret_cast<const T *>(w);
-    for (int f = threadIdx.x; f < NT * KG * 64; f += blockDim.x) {
+    uint4 v[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int f = threadIdx.x + 256 * i;
         const int lane = f & 63, fk = f >> 6, kg = fk % KG, nt = fk / KG;
         const int n = lane & 15, g = lane >> 4;
         const int orow = CPL * (n >> 2) + 4 * nt + (n & 3);
-        *reinterpret_cast<uint4 *>(wlds + f * 16) =
-            *reinterpret_cast<const uint4 *>(W + orow * E + (4 * kg + g) * CH);
+        v[i] = *reinterpret_cast<const uint4 *>(W + orow * E + (4 * kg + g) * CH);
     }
     // bias as fp32 after the fragments (zeros without bias)
-    float *bl = reinterpret_cast<float *>(wlds + NT * KG * 64 * 16);
     const T *bias = reinterpret_cast<const T *>(b);
-    for (int c = threadIdx.x; c < E; c += blockDim.x) {
-        float v = 0.f;
-        if (bias) {
-            if constexpr (sizeof(T) == 2)
-                v = bf2f(bias[c]);
-            else
-                v = bias[c];
-        }
-        bl[c] = v;
+    const int c = threadIdx.x;
+    float bv = 0.f;
+    if (bias && c < E) {
+        if constexpr (sizeof(T) == 2)
+            bv = bf2f(bias[c]);
+        else
+            bv = bias[c];
     }
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+        *reinterpret_cast<uint4 *>(wlds + (threadIdx.x + 256 * i) * 16) = v[i];
+    if (c < E)
+        reinterpret_cast<float *>(wlds + NT * KG * 64 * 16)[c] = bv;
 }
 
 // bytes of one staged E x E matrix with its bias
