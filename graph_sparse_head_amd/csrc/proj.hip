@@ -136,27 +136,42 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
     const int wid = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
-    // weights -> LDS in fragment order
-    const int nfrag_chunks = nblk * NT * NKS * 64;
-    for (int c = threadIdx.x; c < nfrag_chunks; c += WAVES * 64) {
-        const int f = c >> 6, l = c & 63;
-        const int ks = f % NKS, nt = (f / NKS) % NT, blk = f / (NKS * NT);
+    // weights -> LDS in fragment order: per output block (its weight pointer
+    // uniform), four chunks per thread in flight at a time (indices past the
+    // block's end re-read its last chunk; stores guarded)
+    constexpr int BCH = NT * NKS * 64;   // chunks per block
+    for (int blk = 0; blk < nblk; ++blk) {
         const T *W = reinterpret_cast<const T *>(a.out[blk].w);
-        const T *src = W + (int64_t)(nt * 16 + (l & 15)) * E + ks * Elem<T>::kStep +
-                       (l >> 4) * Elem<T>::kVec;
-        *reinterpret_cast<uint4 *>(wl + c * 16) = *reinterpret_cast<const uint4 *>(src);
-    }
-    for (int c = threadIdx.x; c < nblk * E; c += WAVES * 64) {
-        const int blk = c / E, n = c - blk * E;
-        const T *bias = reinterpret_cast<const T *>(a.out[blk].b);
-        float v = 0.f;
-        if (bias) {
-            if constexpr (sizeof(T) == 2)
-                v = bf2f(bias[n]);
-            else
-                v = bias[n];
+        for (int c0 = threadIdx.x; c0 < BCH; c0 += 4 * WAVES * 64) {
+            uint4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = min(c0 + k * WAVES * 64, BCH - 1);
+                const int f = c >> 6, l = c & 63;
+                const int ks = f % NKS, nt = f / NKS;
+                v[k] = *reinterpret_cast<const uint4 *>(W + (int64_t)(nt * 16 + (l & 15)) * E +
+                                                        ks * Elem<T>::kStep + (l >> 4) * Elem<T>::kVec);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = c0 + k * WAVES * 64;
+                if (c < BCH)
+                    *reinterpret_cast<uint4 *>(wl + (blk * BCH + c) * 16) = v[k];
+            }
         }
-        bl[c] = v;
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+        const T *bias = reinterpret_cast<const T *>(a.out[blk].b);
+        for (int n = threadIdx.x; n < E; n += WAVES * 64) {
+            float v = 0.f;
+            if (bias) {
+                if constexpr (sizeof(T) == 2)
+                    v = bf2f(bias[n]);
+                else
+                    v = bias[n];
+            }
+            bl[blk * E + n] = v;
+        }
     }
     __syncthreads();
 
