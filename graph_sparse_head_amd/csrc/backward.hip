@@ -589,16 +589,32 @@ __global__ void __launch_bounds__(WAVES * 64) bwd_rowmm(const RowMM a)
 
     // fragment (j, nt, ks), lane l: A[m][k] = W_j[k][m] for m = nt*16 + (l & 15),
     // k = ks * kStep + (l >> 4) * kVec + v
-    for (int cidx = threadIdx.x; cidx < NIN * NT * NKS * 64; cidx += WAVES * 64) {
-        const int f = cidx >> 6, l = cidx & 63;
-        const int ks = f % NKS, nt = (f / NKS) % NT, j = f / (NKS * NT);
-        const T *W = reinterpret_cast<const T *>(a.w[j]);
-        const int m = nt * 16 + (l & 15), k0 = ks * Frag<T>::kStep + (l >> 4) * KV;
-        T v[KV];
+    // (per input map j its weight pointer is uniform; a thread's element loads
+    // of up to two chunks are in flight together)
+    constexpr int JCH = NT * NKS * 64;   // chunks per map
 #pragma unroll
-        for (int i = 0; i < KV; ++i)
-            v[i] = W[(int64_t)(k0 + i) * E + m];
-        *reinterpret_cast<uint4 *>(wl + cidx * 16) = *reinterpret_cast<const uint4 *>(v);
+    for (int j = 0; j < NIN; ++j) {
+        const T *W = reinterpret_cast<const T *>(a.w[j]);
+        for (int c0 = threadIdx.x; c0 < JCH; c0 += 2 * WAVES * 64) {
+            T v[2][KV];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = min(c0 + q * WAVES * 64, JCH - 1);
+                const int f = c >> 6, l = c & 63;
+                const int ks = f % NKS, nt = f / NKS;
+                const int m = nt * 16 + (l & 15), k0 = ks * Frag<T>::kStep + (l >> 4) * KV;
+#pragma unroll
+                for (int i = 0; i < KV; ++i)
+                    v[q][i] = W[(int64_t)(k0 + i) * E + m];
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = c0 + q * WAVES * 64;
+                if (c < JCH)
+                    *reinterpret_cast<uint4 *>(wl + (j * JCH + c) * 16) =
+                        *reinterpret_cast<const uint4 *>(v[q]);
+            }
+        }
     }
     __syncthreads();
 
@@ -616,14 +632,9 @@ __global__ void __launch_bounds__(WAVES * 64) bwd_rowmm(const RowMM a)
                 dst[j][ks] = *reinterpret_cast<const uint4 *>(xr + ks * Frag<T>::kStep);
         }
     };
-    int64_t tile = blockIdx.x;
-    if (tile < ntiles)
-        load_x(tile, xf);
     const int cr = lane % CPR, rr = lane / CPR;
-    for (; tile < ntiles; tile += gridDim.x) {
-        const int64_t next = tile + gridDim.x;
-        if (next < ntiles)
-            load_x(next, xn);
+    // One tile from the x fragments in xf.
+    auto process = [&](int64_t tile) {
         const int64_t row0 = tile * tile_rows + wid * 16;
 #pragma unroll 2
         for (int nt = 0; nt < NT; ++nt) {
@@ -666,15 +677,8 @@ __global__ void __launch_bounds__(WAVES * 64) bwd_rowmm(const RowMM a)
                 *out = v;
             }
         }
-        if constexpr (sizeof(T) == 4) {
-            if (next < ntiles) {
-#pragma unroll
-                for (int j = 0; j < NIN; ++j)
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) xf[j][ks] = xn[j][ks];
-            }
-            continue;
-        }
+        if constexpr (sizeof(T) == 4)
+            return;
         // a wavefront reads back only its own staged rows
         T *dst = reinterpret_cast<T *>(a.y) + cr * (16 / (int)sizeof(T));
 #pragma unroll
@@ -696,12 +700,22 @@ __global__ void __launch_bounds__(WAVES * 64) bwd_rowmm(const RowMM a)
                 *out = v;
             }
         }
-        if (next < ntiles) {
+    };
+    // Every tile but the last has a successor, whose fragments are loaded
+    // before the tile is processed; the last one runs after the loop (a
+    // conditional load in the loop makes the compiler wait for it at once).
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles) {
+        load_x(tile, xf);
+        for (; tile + gridDim.x < ntiles; tile += gridDim.x) {
+            load_x(tile + gridDim.x, xn);
+            process(tile);
 #pragma unroll
             for (int j = 0; j < NIN; ++j)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) xf[j][ks] = xn[j][ks];
         }
+        process(tile);
     }
 }
 

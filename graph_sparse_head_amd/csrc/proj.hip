@@ -190,13 +190,8 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
                 dst[rg][ks] = *reinterpret_cast<const uint4 *>(xr + ks * Elem<T>::kStep);
         }
     };
-    int64_t tile = blockIdx.x;
-    if (tile < ntiles)
-        load_x(tile, xf);
-    for (; tile < ntiles; tile += gridDim.x) {
-        const int64_t next = tile + gridDim.x;
-        if (next < ntiles)
-            load_x(next, xn);
+    // One tile from the x fragments in xf.
+    auto process = [&](int64_t tile) {
         const int64_t row0 = tile * tile_rows + wid * ROWS;
         // (sample, token) of this lane's first stored row, once per tile
         const int cr = lane % CPR, rr = lane / CPR;
@@ -272,12 +267,22 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
                 advance(a, sb, si, RPI);
             }
         }
-        if (next < ntiles) {
+    };
+    // Every tile but the last has a successor, whose fragments are loaded
+    // before the tile is processed; the last one runs after the loop (a
+    // conditional load in the loop makes the compiler wait for it at once).
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles) {
+        load_x(tile, xf);
+        for (; tile + gridDim.x < ntiles; tile += gridDim.x) {
+            load_x(tile + gridDim.x, xn);
+            process(tile);
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) xf[rg][ks] = xn[rg][ks];
         }
+        process(tile);
     }
 }
 
