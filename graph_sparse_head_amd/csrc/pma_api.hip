@@ -776,6 +776,9 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         return fail(PMA_E_UNSUPPORTED, "head size above 64 in the backward pass");
     if ((L > S ? L : S) * B * 2 * E > ((int64_t)1 << 40))
         return fail(PMA_E_UNSUPPORTED, "batch too large");
+    // the per-position mask words are indexed with 32 bits
+    if (key_padding_mask && (nnz + 4) * ((B + 31) / 32) >= ((int64_t)1 << 31))
+        return fail(PMA_E_UNSUPPORTED, "key_padding_mask with nnz * ceil(batch / 32) of 2^31 or more");
     char err[256] = "";
     if (!p->g.csc_ptr) {
         pma_status st = pma::build_csc(&p->g, nnz, L, S, p->bchunk, p->bsub, stream, err, sizeof err);

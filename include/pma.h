@@ -162,7 +162,8 @@ pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const v
  *
  * Errors: those of pma_forward, and PMA_E_NULL (key_padding_mask NULL),
  * PMA_E_ARG (mask_per_sample not 0/1), PMA_E_UNSUPPORTED (a workspace tensor
- * of 2 GiB or more with a head size the 16-byte kernel serves).
+ * of 2 GiB or more with a head size the 16-byte kernel serves, or
+ * nnz * ceil(batch / 32) of 2^31 or more).
  */
 pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void *query, const void *key,
                               const void *value, const void *q_w, const void *q_b,
@@ -218,10 +219,13 @@ pma_status pma_forward_train(pma_plan *plan, int64_t batch, const void *query, c
  * Computation: out_proj gradients, then two passes over the edges (by
  * target: query gradients and each edge's softmax weight and score
  * gradient; by source: key and value gradients), then the projections'
- * gradients; fp32 throughout, plain GEMMs through rocBLAS. The first call
- * builds a source-major copy of the edge index (blocks once). Errors:
- * PMA_E_NULL, PMA_E_SIZE, PMA_E_ARG (flags, a shared gradient output with
- * L != S), PMA_E_UNSUPPORTED (head size above 64), PMA_E_OOM, PMA_E_DEVICE.
+ * gradients; fp32 accumulation throughout, intermediates in the plan dtype,
+ * every product on this library's own matrix-core kernels, no atomics
+ * (results are run-to-run identical). The first call builds a source-major
+ * copy of the edge index (blocks once). Errors: PMA_E_NULL, PMA_E_SIZE,
+ * PMA_E_ARG (flags, a shared gradient output with L != S),
+ * PMA_E_UNSUPPORTED (head size above 64; a mask with nnz * ceil(batch / 32)
+ * of 2^31 or more), PMA_E_OOM, PMA_E_DEVICE.
  */
 pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query, const void *key,
                         const void *value, const void *q_w, const void *k_w, const void *v_w,
