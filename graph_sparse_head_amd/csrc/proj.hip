@@ -106,11 +106,12 @@ __device__ inline int64_t out_offset(const ProjArgs &a, const ProjOut &o, uint32
 // copies the weight tiles of all its output blocks into LDS, laid out in
 // MFMA fragment order (one 1 KB fragment per (block, n-tile, k-step), lane l
 // at byte 16 l), so every later fragment read is one conflict-free 16-byte
-// LDS load. It then walks row tiles of WAVES x RG x 16 rows, stride gridDim.
-// Each wavefront keeps its rows' x fragments in registers and loads the next
-// tile's fragments before computing the current one. Every output block goes
-// through a per-wavefront LDS staging area so that stores are whole 16-byte
-// chunks of whole rows.
+// LDS load, and the biases as fp32 after them. It then walks row tiles of
+// WAVES x RG x 16 rows, stride gridDim. Each wavefront keeps its rows' x
+// fragments in registers and loads the next tile's fragments before
+// computing the current one. bf16 output blocks go through a per-wavefront
+// LDS staging area so that stores are whole 16-byte chunks of whole rows;
+// fp32 lanes already hold 16 contiguous bytes and store them directly.
 template <typename T, int K, int RG, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
 {
