@@ -138,28 +138,25 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
     const int lr = lane & 15, lg = lane >> 4;
 
     // weights -> LDS in fragment order: per output block (its weight pointer
-    // uniform), four chunks per thread in flight at a time (indices past the
-    // block's end re-read its last chunk; stores guarded)
-    constexpr int BCH = NT * NKS * 64;   // chunks per block
+    // uniform), all of a thread's chunks of the block loaded before any is
+    // stored
+    constexpr int BCH = NT * NKS * 64;            // chunks per block
+    constexpr int NPT = BCH / (WAVES * 64);       // chunks per thread
+    static_assert(BCH % (WAVES * 64) == 0, "whole chunks per thread");
     for (int blk = 0; blk < nblk; ++blk) {
         const T *W = reinterpret_cast<const T *>(a.out[blk].w);
-        for (int c0 = threadIdx.x; c0 < BCH; c0 += 4 * WAVES * 64) {
-            uint4 v[4];
+        uint4 v[NPT];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = min(c0 + k * WAVES * 64, BCH - 1);
-                const int f = c >> 6, l = c & 63;
-                const int ks = f % NKS, nt = f / NKS;
-                v[k] = *reinterpret_cast<const uint4 *>(W + (int64_t)(nt * 16 + (l & 15)) * E +
-                                                        ks * Elem<T>::kStep + (l >> 4) * Elem<T>::kVec);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = c0 + k * WAVES * 64;
-                if (c < BCH)
-                    *reinterpret_cast<uint4 *>(wl + (blk * BCH + c) * 16) = v[k];
-            }
+        for (int k = 0; k < NPT; ++k) {
+            const int c = threadIdx.x + k * WAVES * 64;
+            const int f = c >> 6, l = c & 63;
+            const int ks = f % NKS, nt = f / NKS;
+            v[k] = *reinterpret_cast<const uint4 *>(W + (int64_t)(nt * 16 + (l & 15)) * E +
+                                                    ks * Elem<T>::kStep + (l >> 4) * Elem<T>::kVec);
         }
+#pragma unroll
+        for (int k = 0; k < NPT; ++k)
+            *reinterpret_cast<uint4 *>(wl + (blk * BCH + threadIdx.x + k * WAVES * 64) * 16) = v[k];
     }
     for (int blk = 0; blk < nblk; ++blk) {
         const T *bias = reinterpret_cast<const T *>(a.out[blk].b);
@@ -191,8 +188,13 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
                 dst[rg][ks] = *reinterpret_cast<const uint4 *>(xr + ks * Elem<T>::kStep);
         }
     };
-    // One tile from the x fragments in xf.
-    auto process = [&](int64_t tile) {
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles)
+        load_x(tile, xf);
+    for (; tile < ntiles; tile += gridDim.x) {
+        const int64_t next = tile + gridDim.x;
+        if (next < ntiles)
+            load_x(next, xn);
         const int64_t row0 = tile * tile_rows + wid * ROWS;
         // (sample, token) of this lane's first stored row, once per tile
         const int cr = lane % CPR, rr = lane / CPR;
@@ -268,22 +270,12 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
                 advance(a, sb, si, RPI);
             }
         }
-    };
-    // Every tile but the last has a successor, whose fragments are loaded
-    // before the tile is processed; the last one runs after the loop (a
-    // conditional load in the loop makes the compiler wait for it at once).
-    int64_t tile = blockIdx.x;
-    if (tile < ntiles) {
-        load_x(tile, xf);
-        for (; tile + gridDim.x < ntiles; tile += gridDim.x) {
-            load_x(tile + gridDim.x, xn);
-            process(tile);
+        if (next < ntiles) {
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) xf[rg][ks] = xn[rg][ks];
         }
-        process(tile);
     }
 }
 
