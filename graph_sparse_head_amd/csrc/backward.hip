@@ -160,10 +160,12 @@ __device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uin
 
 // CM (UNI only): the mask comes as one uniform word per CSR position
 // (kpm_csr); otherwise each lane looks its bit up by source.
+// bf16 plans keep q and dm packed and form the dot products with v_dot2.
 template <typename T, int LPH, bool UNI, bool CM = false>
 __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
 {
     constexpr int VEC = Vec<T>::N;
+    constexpr bool BF = sizeof(T) == 2;
     const int CPR = a.E / VEC;
     int64_t task;
     int b, c;
@@ -201,14 +203,19 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
     const int slot = a.t_slot[task];
     const int h = c / LPH;
     const int64_t row = ((int64_t)b * a.L + t) * a.E + c * VEC;
-    float qv[VEC], dmv[VEC], mx[VEC];
-    widen<T>(ld16(reinterpret_cast<const T *>(a.q) + row), qv);
-    widen<T>(ld16(reinterpret_cast<const T *>(a.dm) + row), dmv);
-    widen<T>(ld16(reinterpret_cast<const T *>(a.mixed) + row), mx);
+    const uint4 qw = ld16(reinterpret_cast<const T *>(a.q) + row);
+    const uint4 dmw = ld16(reinterpret_cast<const T *>(a.dm) + row);
+    float qv[VEC], dmv[VEC];
+    widen<T>(qw, qv);
+    widen<T>(dmw, dmv);
     float D = 0.f;
+    {
+        float mx[VEC];
+        widen<T>(ld16(reinterpret_cast<const T *>(a.mixed) + row), mx);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i)
-        D = fmaf(dmv[i], mx[i], D);
+        for (int i = 0; i < VEC; ++i)
+            D = fmaf(dmv[i], mx[i], D);
+    }
     D = group_sum<LPH>(D);
     const float2 ml =
         *reinterpret_cast<const float2 *>(a.ml + (((int64_t)t * a.B + b) * a.H + h) * 2);
@@ -251,14 +258,29 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
             fetch(p0 + kU, sn, kn, vn);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            float kk[VEC], vv[VEC];
+            float kk[VEC];
             widen<T>(kr[u], kk);
-            widen<T>(vr[u], vv);
             float z = 0.f, dp = 0.f;
+            if constexpr (BF) {
+                typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+                const uint32_t qa[4] = {qw.x, qw.y, qw.z, qw.w}, ma[4] = {dmw.x, dmw.y, dmw.z, dmw.w};
+                const uint32_t ka[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+                const uint32_t va[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                z = fmaf(qv[i], kk[i], z);
-                dp = fmaf(dmv[i], vv[i], dp);
+                for (int w = 0; w < 4; ++w) {
+                    z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qa[w]),
+                                                        __builtin_bit_cast(bf16x2_t, ka[w]), z, false);
+                    dp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ma[w]),
+                                                         __builtin_bit_cast(bf16x2_t, va[w]), dp, false);
+                }
+            } else {
+                float vv[VEC];
+                widen<T>(vr[u], vv);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    z = fmaf(qv[i], kk[i], z);
+                    dp = fmaf(dmv[i], vv[i], dp);
+                }
             }
             z = group_sum<LPH>(z);
             dp = group_sum<LPH>(dp);
