@@ -860,11 +860,80 @@ __global__ void __launch_bounds__(256) bwd_wgrad(const WGrad a)
     }
 }
 
+// fp32 with E = 128: the same MFMA scheme, but wavefront w takes block
+// (w / 2, w % 2) of dW over all rows of the workgroup's range, so each row of
+// G and X comes from HBM once per workgroup (the second wavefront's read of a
+// half row is served by the CU's cache) and the partials need no reduction
+// across wavefronts.
+__global__ void __launch_bounds__(256) bwd_wgrad_quad(const WGrad a)
+{
+    const WGradPair pr = a.p[blockIdx.y];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lr = lane >> 4, lc = lane & 15;
+    const int nb = wid >> 1, kb = wid & 1;
+    const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
+    const int64_t r_beg = (int64_t)blockIdx.x * per;
+    const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
+    const float *G = reinterpret_cast<const float *>(pr.g) + 64 * nb + 4 * lc;
+    const float *X = reinterpret_cast<const float *>(pr.x) + 64 * kb + 4 * lc;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    constexpr int UR = 4;   // row groups of 4 per step
+    for (int64_t r0 = r_beg; r0 < r_end; r0 += 4 * UR) {
+        float4 g[UR], x[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int64_t r = r0 + 4 * u + lr;
+            if (r < r_end) {
+                g[u] = *reinterpret_cast<const float4 *>(G + r * a.E);
+                x[u] = *reinterpret_cast<const float4 *>(X + r * a.E);
+            } else {
+                g[u] = x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const float gg[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+            const float xx[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bs[i] += gg[i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(gg[i], xx[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+    float *part = a.part + (((int64_t)blockIdx.y * 4 + 2 * nb + kb) * a.nwg + blockIdx.x) * kWgPart;
+    // lane holds, for v < 4, MFMA position (m = 4 lr + v, n = lc) of tile (i, j):
+    // dW row 4 m + i, column 4 n + j
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<float4 *>(part + (4 * (4 * lr + v) + i) * 64 + 4 * lc) =
+                make_float4(acc[i][0][v], acc[i][1][v], acc[i][2][v], acc[i][3][v]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bs[i] += __shfl_xor(bs[i], 16, 64);
+        bs[i] += __shfl_xor(bs[i], 32, 64);
+    }
+    if (lr == 0)
+        *reinterpret_cast<float4 *>(part + 64 * 64 + 4 * lc) = make_float4(bs[0], bs[1], bs[2], bs[3]);
+}
+
 // bf16: v_mfma_f32_16x16x32_bf16 contracts 8 consecutive rows per lane, so
 // slabs of kWR rows of G and X are first written to LDS transposed (column-
-// major, 4 rows per 8-byte write); wavefront w then owns output rows
-// n0 + 16 w .. + 15 and all 64 columns, so the partial needs no reduction
-// across wavefronts.
+// major, 2 RPT bytes per write); the workgroup covers a W x W block of dW
+// (W = 64 ZN: ZN = 2 takes all of dW for E = 128, so every row of G and X is
+// read once), wavefront w owns output rows 16 ZN w .. + 16 ZN - 1 and all W
+// columns, so the partial needs no reduction across wavefronts. The next
+// slab's loads are issued into the staging registers as soon as they have
+// been written to LDS, and are in flight during the matrix-core work.
 constexpr int kWR = 128;              // rows per slab
 constexpr int kWP = kWR * 2 + 16;     // bytes per transposed column (padded)
 
@@ -874,34 +943,42 @@ __device__ inline uint32_t half16(const uint4 &u, int i)
     return (i & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
+template <int ZN>
 __global__ void __launch_bounds__(256) bwd_wgrad_bf16(const WGrad a)
 {
-    __shared__ __attribute__((aligned(16))) char gt[64 * kWP];
-    __shared__ __attribute__((aligned(16))) char xt[64 * kWP];
-    __shared__ float bl[32][64];
+    constexpr int W = 64 * ZN;        // block width
+    constexpr int CPR = W / 8;        // 16-byte chunks per slab row
+    constexpr int RQ = 256 / CPR;     // threads per column chunk
+    constexpr int RPT = kWR / RQ;     // slab rows per thread
+    static_assert(RPT == 4 || RPT == 8, "slab rows per thread");
+    static_assert(RQ * W * 4 <= W * kWP, "bias sums fit the G slab");
+    __shared__ __attribute__((aligned(16))) char gt[W * kWP];
+    __shared__ __attribute__((aligned(16))) char xt[W * kWP];
     const WGradPair pr = a.p[blockIdx.y];
     const int zn = a.E / 64, zt = blockIdx.z;
-    const int n0 = (zt / zn) * 64, k0 = (zt % zn) * 64;
-    const int tid = threadIdx.x, rq = tid >> 3, cc = tid & 7;
+    const int n0 = (zt / (zn / ZN)) * W, k0 = (zt % (zn / ZN)) * W;
+    const int tid = threadIdx.x, rq = tid / CPR, cc = tid % CPR;
     const int lane = tid & 63, wid = tid >> 6;
     const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
     const int64_t r_beg = (int64_t)blockIdx.x * per;
     const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
     const uint16_t *G = reinterpret_cast<const uint16_t *>(pr.g) + n0 + 8 * cc;
     const uint16_t *X = reinterpret_cast<const uint16_t *>(pr.x) + k0 + 8 * cc;
-    f32x4 acc[4];
+    f32x4 acc[ZN][4 * ZN];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < ZN; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4 * ZN; ++nt)
+            acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float bsum[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         bsum[i] = 0.f;
-    for (int64_t r0 = r_beg; r0 < r_end; r0 += kWR) {
-        uint4 gv[4], xv[4];
+    uint4 gv[RPT], xv[RPT];
+    auto load = [&](int64_t r0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t r = r0 + 4 * rq + j;
+        for (int j = 0; j < RPT; ++j) {
+            const int64_t r = r0 + RPT * rq + j;
             if (r < r_end) {
                 gv[j] = ld16(G + r * a.E);
                 xv[j] = ld16(X + r * a.E);
@@ -909,51 +986,90 @@ __global__ void __launch_bounds__(256) bwd_wgrad_bf16(const WGrad a)
                 gv[j] = xv[j] = make_uint4(0, 0, 0, 0);
             }
         }
+    };
+    if (r_beg < r_end)
+        load(r_beg);
+    for (int64_t r0 = r_beg; r0 < r_end; r0 += kWR) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < RPT; ++j)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 bsum[i] += __uint_as_float(half16(gv[j], i) << 16);
         __syncthreads();   // the previous slab's fragments are read
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int off = (8 * cc + i) * kWP + 8 * rq;
-            *reinterpret_cast<uint2 *>(gt + off) =
-                make_uint2(half16(gv[0], i) | (half16(gv[1], i) << 16),
-                           half16(gv[2], i) | (half16(gv[3], i) << 16));
-            *reinterpret_cast<uint2 *>(xt + off) =
-                make_uint2(half16(xv[0], i) | (half16(xv[1], i) << 16),
-                           half16(xv[2], i) | (half16(xv[3], i) << 16));
+            const int off = (8 * cc + i) * kWP + 2 * RPT * rq;
+            if constexpr (RPT == 4) {
+                *reinterpret_cast<uint2 *>(gt + off) =
+                    make_uint2(half16(gv[0], i) | (half16(gv[1], i) << 16),
+                               half16(gv[2], i) | (half16(gv[3], i) << 16));
+                *reinterpret_cast<uint2 *>(xt + off) =
+                    make_uint2(half16(xv[0], i) | (half16(xv[1], i) << 16),
+                               half16(xv[2], i) | (half16(xv[3], i) << 16));
+            } else {
+                *reinterpret_cast<uint4 *>(gt + off) =
+                    make_uint4(half16(gv[0], i) | (half16(gv[1], i) << 16),
+                               half16(gv[2], i) | (half16(gv[3], i) << 16),
+                               half16(gv[4], i) | (half16(gv[5], i) << 16),
+                               half16(gv[6], i) | (half16(gv[7], i) << 16));
+                *reinterpret_cast<uint4 *>(xt + off) =
+                    make_uint4(half16(xv[0], i) | (half16(xv[1], i) << 16),
+                               half16(xv[2], i) | (half16(xv[3], i) << 16),
+                               half16(xv[4], i) | (half16(xv[5], i) << 16),
+                               half16(xv[6], i) | (half16(xv[7], i) << 16));
+            }
         }
         __syncthreads();
+        if (r0 + kWR < r_end)
+            load(r0 + kWR);
 #pragma unroll
         for (int ks = 0; ks < kWR / 32; ++ks) {
             const int off = ks * 64 + 16 * (lane >> 4);
-            const uint4 af = *reinterpret_cast<const uint4 *>(gt + (16 * wid + (lane & 15)) * kWP + off);
+            uint4 af[ZN];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
+            for (int mt = 0; mt < ZN; ++mt)
+                af[mt] = *reinterpret_cast<const uint4 *>(gt + (16 * (ZN * wid + mt) + (lane & 15)) * kWP + off);
+#pragma unroll
+            for (int nt = 0; nt < 4 * ZN; ++nt) {
                 const uint4 bf = *reinterpret_cast<const uint4 *>(xt + (16 * nt + (lane & 15)) * kWP + off);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, bf), acc[nt], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < ZN; ++mt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, af[mt]), __builtin_bit_cast(bf16x8, bf), acc[mt][nt], 0, 0, 0);
             }
         }
     }
-    float *part = a.part + (((int64_t)blockIdx.y * gridDim.z + zt) * a.nwg + blockIdx.x) * kWgPart;
-    // lane holds position (m = 4 (lane >> 4) + v, n = lane & 15) of tile (wid, nt)
+    // partials stay in 64 x 64 blocks: block (n0 + 64 i, k0 + 64 j) of dW
+    auto part_of = [&](int i, int j) {
+        const int z = (n0 / 64 + i) * zn + k0 / 64 + j;
+        return a.part + (((int64_t)blockIdx.y * zn * zn + z) * a.nwg + blockIdx.x) * kWgPart;
+    };
+    // lane holds position (m = 4 (lane >> 4) + v, n = lane & 15) of tile (ZN wid + mt, nt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int mt = 0; mt < ZN; ++mt) {
+        const int row = 16 * (ZN * wid + mt) + 4 * (lane >> 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            part[(16 * wid + 4 * (lane >> 4) + v) * 64 + 16 * nt + (lane & 15)] = acc[nt][v];
+        for (int nt = 0; nt < 4 * ZN; ++nt) {
+            float *part = part_of(row / 64, nt / 4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                part[(row % 64 + v) * 64 + 16 * (nt % 4) + (lane & 15)] = acc[mt][nt][v];
+        }
+    }
+    __syncthreads();   // the last slab's fragments are read
+    float *bl = reinterpret_cast<float *>(gt);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        bl[rq][8 * cc + i] = bsum[i];
+        bl[rq * W + 8 * cc + i] = bsum[i];
     __syncthreads();
-    if (tid < 64) {
+    if (tid < W) {
         float b = 0.f;
-        for (int q = 0; q < 32; ++q)
-            b += bl[q][tid];
-        part[64 * 64 + tid] = b;
+        for (int q = 0; q < RQ; ++q)
+            b += bl[q * W + tid];
+        // the same sums in every block column (only column 0 reaches db)
+#pragma unroll
+        for (int j = 0; j < ZN; ++j)
+            part_of(tid / 64, j)[64 * 64 + tid % 64] = b;
     }
 }
 
@@ -1279,10 +1395,16 @@ pma_status launch_wgrad(WGrad a, pma_dtype dt, hipStream_t s)
         const dim3 g1((unsigned)a.nwg, (unsigned)a.np, (unsigned)(zn * zn));
         const dim3 g2((unsigned)((kWgPart + 63) / 64), (unsigned)(zn * zn), (unsigned)a.np);
         if (bf) {
-            bwd_wgrad_bf16<<<g1, 256, 0, s>>>(a);
+            if (zn == 2)   // one workgroup reads its rows once for all of dW
+                bwd_wgrad_bf16<2><<<dim3(g1.x, g1.y, 1), 256, 0, s>>>(a);
+            else
+                bwd_wgrad_bf16<1><<<g1, 256, 0, s>>>(a);
             bwd_wgrad_reduce<uint16_t><<<g2, 256, 0, s>>>(a);
         } else {
-            bwd_wgrad<float><<<g1, 256, 0, s>>>(a);
+            if (zn == 2)
+                bwd_wgrad_quad<<<dim3(g1.x, g1.y, 1), 256, 0, s>>>(a);
+            else
+                bwd_wgrad<float><<<g1, 256, 0, s>>>(a);
             bwd_wgrad_reduce<float><<<g2, 256, 0, s>>>(a);
         }
     } else {

@@ -85,6 +85,16 @@ def test_backward_random(shape, shared):
     _grad_check(c, shared)
 
 
+# Weight gradients over many rows: with E = 128 one workgroup takes all of
+# dW for its row range, here several 128-row slabs (bf16) or 16-row steps
+# (fp32) per workgroup with a ragged last one.
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_weight_gradients_many_rows(dt):
+    c = synth.random_case(84, 5, 2999, 3001, 128, 8, 0.002, dtype=dt, same_kv=True,
+                          same_qkv=False, name="bwd_rows")
+    _grad_check(c, "kv")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_backward_mask_no_bias_self_loops(dt):
     c = synth.random_case(81, 4, 60, 60, 64, 4, 0.08, dtype=dt, bias="none", add_self_loops=True,
