@@ -774,19 +774,44 @@ __global__ void __launch_bounds__(256) bwd_rowmm_generic(const RowMM a, int E)
 // the partials in workgroup order.
 constexpr int kWgPart = 64 * 64 + 64;   // floats per partial (dW block, db)
 
+// Workgroup x of a weight-gradient launch: its pair, its rows, and the
+// partial of 64 x 64 block z (partials of one pair and block are adjacent,
+// in workgroup order).
+struct WgSlice {
+    WGradPair pr;
+    int64_t r_beg, r_end;
+    float *part0;   // partial of block 0; block z at + z * stride
+    int64_t stride;
+};
+__device__ inline WgSlice wg_slice(const WGrad &a, int x)
+{
+    int i = 0;
+    while (i + 1 < a.np && x >= a.off_p[i + 1])
+        ++i;
+    WgSlice w;
+    w.pr = a.p[i];
+    const int n = a.nwg_p[i], k = x - a.off_p[i];
+    const int64_t per = (((w.pr.rows + n - 1) / n) + 15) & ~(int64_t)15;
+    w.r_beg = (int64_t)k * per;
+    w.r_end = w.r_beg + per < w.pr.rows ? w.r_beg + per : w.pr.rows;
+    const int nz = (a.E / 64) * (a.E / 64);
+    w.part0 = a.part + ((int64_t)a.off_p[i] * nz + k) * kWgPart;
+    w.stride = (int64_t)n * kWgPart;
+    return w;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) bwd_wgrad(const WGrad a)
 {
     __shared__ float red[4][64 * 64];
     __shared__ float bred[4][64];
-    const WGradPair pr = a.p[blockIdx.y];
+    const WgSlice ws = wg_slice(a, blockIdx.x);
+    const WGradPair pr = ws.pr;
     const int zn = a.E / 64, zt = blockIdx.z;
     const int n0 = (zt / zn) * 64, k0 = (zt % zn) * 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int lr = lane >> 4, lc = lane & 15;
-    const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
-    const int64_t r_beg = (int64_t)blockIdx.x * per;
-    const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
+    const int64_t r_beg = ws.r_beg, r_end = ws.r_end;
     const T *G = reinterpret_cast<const T *>(pr.g) + n0 + 4 * lc;
     const T *X = reinterpret_cast<const T *>(pr.x) + k0 + 4 * lc;
     f32x4 acc[4][4];
@@ -851,7 +876,7 @@ __global__ void __launch_bounds__(256) bwd_wgrad(const WGrad a)
             bred[wid][4 * lc + i] = bs[i];
     }
     __syncthreads();
-    float *part = a.part + (((int64_t)blockIdx.y * gridDim.z + zt) * a.nwg + blockIdx.x) * kWgPart;
+    float *part = ws.part0 + zt * ws.stride;
     for (int e = threadIdx.x; e < 64 * 64; e += 256)
         part[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
     if (threadIdx.x < 64) {
@@ -867,13 +892,12 @@ __global__ void __launch_bounds__(256) bwd_wgrad(const WGrad a)
 // across wavefronts.
 __global__ void __launch_bounds__(256) bwd_wgrad_quad(const WGrad a)
 {
-    const WGradPair pr = a.p[blockIdx.y];
+    const WgSlice ws = wg_slice(a, blockIdx.x);
+    const WGradPair pr = ws.pr;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int lr = lane >> 4, lc = lane & 15;
     const int nb = wid >> 1, kb = wid & 1;
-    const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
-    const int64_t r_beg = (int64_t)blockIdx.x * per;
-    const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
+    const int64_t r_beg = ws.r_beg, r_end = ws.r_end;
     const float *G = reinterpret_cast<const float *>(pr.g) + 64 * nb + 4 * lc;
     const float *X = reinterpret_cast<const float *>(pr.x) + 64 * kb + 4 * lc;
     f32x4 acc[4][4];
@@ -882,23 +906,28 @@ __global__ void __launch_bounds__(256) bwd_wgrad_quad(const WGrad a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    // Rows are loaded one step ahead (the loads of step k + 1 are in flight
+    // during the matrix-core work of step k); a lane past the range loads
+    // the range's last row and contributes zeros.
     constexpr int UR = 4;   // row groups of 4 per step
-    for (int64_t r0 = r_beg; r0 < r_end; r0 += 4 * UR) {
-        float4 g[UR], x[UR];
+    float4 g[UR], x[UR], gn[UR], xn[UR];
+    auto load = [&](int64_t r0, float4 (&gg)[UR], float4 (&xx)[UR]) {
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const int64_t r = r0 + 4 * u + lr;
-            if (r < r_end) {
-                g[u] = *reinterpret_cast<const float4 *>(G + r * a.E);
-                x[u] = *reinterpret_cast<const float4 *>(X + r * a.E);
-            } else {
-                g[u] = x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            int64_t r = r0 + 4 * u + lr;
+            r = r < r_end ? r : r_end - 1;
+            gg[u] = *reinterpret_cast<const float4 *>(G + r * a.E);
+            xx[u] = *reinterpret_cast<const float4 *>(X + r * a.E);
         }
+    };
+    auto step = [&](int64_t r0) {
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
-            const float gg[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
-            const float xx[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+            const bool in = r0 + 4 * u + lr < r_end;
+            const float gg[4] = {in ? g[u].x : 0.f, in ? g[u].y : 0.f, in ? g[u].z : 0.f,
+                                 in ? g[u].w : 0.f};
+            const float xx[4] = {in ? x[u].x : 0.f, in ? x[u].y : 0.f, in ? x[u].z : 0.f,
+                                 in ? x[u].w : 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bs[i] += gg[i];
@@ -907,8 +936,23 @@ __global__ void __launch_bounds__(256) bwd_wgrad_quad(const WGrad a)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(gg[i], xx[j], acc[i][j], 0, 0, 0);
             }
         }
+    };
+    if (r_beg < r_end) {
+        load(r_beg, g, x);
+        int64_t r0 = r_beg;
+        for (; r0 + 4 * UR < r_end; r0 += 4 * UR) {
+            load(r0 + 4 * UR, gn, xn);
+            __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the work
+            step(r0);
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                g[u] = gn[u];
+                x[u] = xn[u];
+            }
+        }
+        step(r0);
     }
-    float *part = a.part + (((int64_t)blockIdx.y * 4 + 2 * nb + kb) * a.nwg + blockIdx.x) * kWgPart;
+    float *part = ws.part0 + (2 * nb + kb) * ws.stride;
     // lane holds, for v < 4, MFMA position (m = 4 lr + v, n = lc) of tile (i, j):
     // dW row 4 m + i, column 4 n + j
 #pragma unroll
@@ -954,14 +998,13 @@ __global__ void __launch_bounds__(256) bwd_wgrad_bf16(const WGrad a)
     static_assert(RQ * W * 4 <= W * kWP, "bias sums fit the G slab");
     __shared__ __attribute__((aligned(16))) char gt[W * kWP];
     __shared__ __attribute__((aligned(16))) char xt[W * kWP];
-    const WGradPair pr = a.p[blockIdx.y];
+    const WgSlice ws = wg_slice(a, blockIdx.x);
+    const WGradPair pr = ws.pr;
     const int zn = a.E / 64, zt = blockIdx.z;
     const int n0 = (zt / (zn / ZN)) * W, k0 = (zt % (zn / ZN)) * W;
     const int tid = threadIdx.x, rq = tid / CPR, cc = tid % CPR;
     const int lane = tid & 63, wid = tid >> 6;
-    const int64_t per = (((pr.rows + a.nwg - 1) / a.nwg) + 15) & ~(int64_t)15;
-    const int64_t r_beg = (int64_t)blockIdx.x * per;
-    const int64_t r_end = r_beg + per < pr.rows ? r_beg + per : pr.rows;
+    const int64_t r_beg = ws.r_beg, r_end = ws.r_end;
     const uint16_t *G = reinterpret_cast<const uint16_t *>(pr.g) + n0 + 8 * cc;
     const uint16_t *X = reinterpret_cast<const uint16_t *>(pr.x) + k0 + 8 * cc;
     f32x4 acc[ZN][4 * ZN];
@@ -1041,8 +1084,7 @@ __global__ void __launch_bounds__(256) bwd_wgrad_bf16(const WGrad a)
     }
     // partials stay in 64 x 64 blocks: block (n0 + 64 i, k0 + 64 j) of dW
     auto part_of = [&](int i, int j) {
-        const int z = (n0 / 64 + i) * zn + k0 / 64 + j;
-        return a.part + (((int64_t)blockIdx.y * zn * zn + z) * a.nwg + blockIdx.x) * kWgPart;
+        return ws.part0 + ((n0 / 64 + i) * zn + k0 / 64 + j) * ws.stride;
     };
     // lane holds position (m = 4 (lane >> 4) + v, n = lane & 15) of tile (ZN wid + mt, nt)
 #pragma unroll
@@ -1086,9 +1128,10 @@ __global__ void __launch_bounds__(256) bwd_wgrad_reduce(const WGrad a)
     const int n0 = (zt / zn) * 64, k0 = (zt % zn) * 64;
     float acc = 0.f;
     if (e < kWgPart) {
-        const float *part = a.part + ((int64_t)blockIdx.z * gridDim.y + zt) * a.nwg * kWgPart + e;
+        const int n = a.nwg_p[blockIdx.z];
+        const float *part = a.part + ((int64_t)a.off_p[blockIdx.z] * gridDim.y + (int64_t)zt * n) * kWgPart + e;
 #pragma unroll 8
-        for (int w = q; w < a.nwg; w += 4)
+        for (int w = q; w < n; w += 4)
             acc += part[(int64_t)w * kWgPart];
     }
     red[q][el] = acc;
@@ -1361,16 +1404,20 @@ bool wgrad_fast(const WGrad &a, pma_dtype dt)
 }
 }  // namespace
 
-int wgrad_groups(int64_t E, int np, int64_t max_rows)
+// Workgroups of a weight-gradient launch over all its pairs: one per 256
+// rows, at most 2048 / (number of 64 x 64 blocks of dW), i.e. at most 2048
+// partial blocks; launch_wgrad deals them to the pairs in proportion to their
+// rows, at least one each (so at most np more).
+static int64_t wgrad_budget(int64_t E, int64_t rows)
 {
     const int64_t nz = (E / 64) * (E / 64);
-    int64_t cap = 2048 / (np * (nz > 0 ? nz : 1));
+    int64_t cap = 2048 / (nz > 0 ? nz : 1);
     if (cap < 1)
         cap = 1;
-    int64_t n = (max_rows + 255) / 256;
+    int64_t n = (rows + 255) / 256;
     if (n < 1)
         n = 1;
-    return (int)(n < cap ? n : cap);
+    return n < cap ? n : cap;
 }
 
 size_t wgrad_scratch(int64_t E, int np, int64_t max_rows)
@@ -1378,21 +1425,28 @@ size_t wgrad_scratch(int64_t E, int np, int64_t max_rows)
     if (E % 64 != 0)
         return 0;
     const int64_t nz = (E / 64) * (E / 64);
-    return (size_t)np * nz * wgrad_groups(E, np, max_rows) * kWgPart * sizeof(float);
+    return (size_t)(wgrad_budget(E, np * max_rows) + np) * nz * kWgPart * sizeof(float);
 }
 
 pma_status launch_wgrad(WGrad a, pma_dtype dt, hipStream_t s)
 {
     if (a.np <= 0)
         return PMA_OK;
-    int64_t max_rows = 0;
+    int64_t rows = 0;
     for (int i = 0; i < a.np; ++i)
-        max_rows = a.p[i].rows > max_rows ? a.p[i].rows : max_rows;
+        rows += a.p[i].rows;
     const bool bf = dt == PMA_BF16;
     if (wgrad_fast(a, dt)) {
-        a.nwg = wgrad_groups(a.E, a.np, max_rows);
+        const int64_t budget = wgrad_budget(a.E, rows);
+        a.nwg = 0;
+        for (int i = 0; i < a.np; ++i) {
+            const int64_t n = rows > 0 ? budget * a.p[i].rows / rows : 0;
+            a.nwg_p[i] = (int)(n > 1 ? n : 1);
+            a.off_p[i] = a.nwg;
+            a.nwg += a.nwg_p[i];
+        }
         const int zn = a.E / 64;
-        const dim3 g1((unsigned)a.nwg, (unsigned)a.np, (unsigned)(zn * zn));
+        const dim3 g1((unsigned)a.nwg, 1, (unsigned)(zn * zn));
         const dim3 g2((unsigned)((kWgPart + 63) / 64), (unsigned)(zn * zn), (unsigned)a.np);
         if (bf) {
             if (zn == 2)   // one workgroup reads its rows once for all of dW

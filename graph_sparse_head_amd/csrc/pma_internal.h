@@ -220,7 +220,9 @@ struct WGrad {
     WGradPair p[4];
     int np;
     int E;
-    int nwg;        // set by launch_wgrad
+    int nwg;        // set by launch_wgrad: workgroups over all pairs,
+    int nwg_p[4];   // of pair i (in proportion to its rows),
+    int off_p[4];   // the first of pair i
     float *part;    // wgrad_scratch bytes
 };
 size_t wgrad_scratch(int64_t E, int np, int64_t max_rows);
