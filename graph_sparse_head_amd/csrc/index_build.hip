@@ -190,11 +190,26 @@ __global__ void iota_kernel(int32_t *a, int64_t n)
         a[i] = (int32_t)i;
 }
 
-__global__ void degree_kernel(const int32_t *tgt, int64_t nnz, int32_t *deg)
+// Row pointers of a sorted edge list: ptr[k] = the first position j whose key
+// is at least k, for k = 0 .. K, with key(j) = key[perm[j]] (or key[j] when
+// perm is null) ascending in j. One thread per k, by binary search: counting
+// degrees with atomics serialises on the few nodes that hold a large share of
+// the edges (a Zipf-popular source feeds a fifth of them).
+__global__ void bounds_kernel(const int32_t *key, const int32_t *perm, int64_t n, int64_t K,
+                              int32_t *ptr)
 {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < nnz)
-        atomicAdd(&deg[tgt[i]], 1);
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k > K)
+        return;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (key[perm ? perm[mid] : mid] >= k)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    ptr[k] = (int32_t)lo;
 }
 
 // CSR arrays from the sorted permutation, and the duplicate check: after the
@@ -242,13 +257,13 @@ __global__ void kv_remap(const int32_t *csr_src, const int32_t *kv_map, int64_t 
 }
 
 // Per target: number of pieces, partial slots and split flag.
-__global__ void split_count_kernel(const int32_t *deg, int64_t L, int chunk, int32_t *n_piece,
+__global__ void split_count_kernel(const int32_t *row_ptr, int64_t L, int chunk, int32_t *n_piece,
                                    int32_t *n_slot, int32_t *is_split, int32_t *max_deg)
 {
     int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= L)
         return;
-    int32_t g = deg[t];
+    int32_t g = row_ptr[t + 1] - row_ptr[t];
     int32_t n = g > chunk ? (int32_t)((g + (int64_t)chunk - 1) / chunk) : 1;
     n_piece[t] = n;
     n_slot[t] = n > 1 ? n : 0;
@@ -371,7 +386,7 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
 {
     pma_status st = PMA_OK;
     int32_t *d_src = nullptr, *d_tgt = nullptr, *perm = nullptr, *perm_tmp = nullptr;
-    int32_t *counts = nullptr, *scan_tmp = nullptr, *deg = nullptr, *small = nullptr;
+    int32_t *counts = nullptr, *scan_tmp = nullptr, *small = nullptr;
     int32_t *n_piece = nullptr, *n_slot = nullptr, *is_split = nullptr;
     int32_t *piece_base = nullptr, *slot_base = nullptr, *split_base = nullptr;
     int32_t *t_target = nullptr, *t_begin = nullptr, *t_end = nullptr, *t_slot = nullptr,
@@ -393,7 +408,6 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     PMA_TRY(hipMalloc(&perm_tmp, nnz * i4));
     PMA_TRY(hipMalloc(&counts, count_len * i4));
     PMA_TRY(hipMalloc(&scan_tmp, scan_len * i4));
-    PMA_TRY(hipMalloc(&deg, L * i4));
     PMA_TRY(hipMalloc(&small, 8 * i4));
     PMA_TRY(hipMalloc(&g->row_ptr, (L + 1) * i4));
     // csr_src carries kSrcPad zero entries past nnz so that kernels may read a
@@ -418,7 +432,6 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
 
     PMA_TRY(hipMemcpyAsync(d_src, h_src, nnz * i4, hipMemcpyHostToDevice, stream));
     PMA_TRY(hipMemcpyAsync(d_tgt, h_tgt, nnz * i4, hipMemcpyHostToDevice, stream));
-    PMA_TRY(hipMemsetAsync(deg, 0, L * i4, stream));
     PMA_TRY(hipMemsetAsync(small, 0, 8 * i4, stream));
 
     // 1. sort edge ids by (target, source)
@@ -433,10 +446,9 @@ pma_status build_graph(const int32_t *h_src, const int32_t *h_tgt, int64_t nnz, 
     kv_rows_fill<<<grid_for(S, 256), 256, 0, stream>>>(used, kv_map, S, g->kv_rows);
     kv_remap<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, kv_map, nnz, g->csr_kv);
     // 2. row pointers
-    degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(d_tgt, nnz, deg);
-    PMA_TRY(scan_exclusive(deg, g->row_ptr, L, g->row_ptr + L, scan_tmp, stream));
+    bounds_kernel<<<grid_for(L + 1, 256), 256, 0, stream>>>(g->csr_tgt, nullptr, nnz, L, g->row_ptr);
     // 3. pieces per target
-    split_count_kernel<<<grid_for(L, 256), 256, 0, stream>>>(deg, L, chunk, n_piece, n_slot,
+    split_count_kernel<<<grid_for(L, 256), 256, 0, stream>>>(g->row_ptr, L, chunk, n_piece, n_slot,
                                                              is_split, small + 4);
     PMA_TRY(scan_exclusive(n_piece, piece_base, L, small + 1, scan_tmp, stream));
     PMA_TRY(scan_exclusive(n_slot, slot_base, L, small + 2, scan_tmp, stream));
@@ -504,7 +516,7 @@ fail:
 done:
     {
         int32_t *tmps[] = {d_src,     d_tgt,     perm,       perm_tmp,   counts,   scan_tmp,
-                           deg,       small,     n_piece,    n_slot,     is_split, piece_base,
+                           small,     n_piece,    n_slot,     is_split, piece_base,
                            slot_base, split_base, t_target,  t_begin,    t_end,    t_slot,
                            t_split,   t_key,     tperm,      tperm_tmp, used,     kv_map};
         for (int32_t *p : tmps)
@@ -682,7 +694,7 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk, 
     const int64_t count_len = 256 * ntiles;
     const int64_t scan_len = (count_len > n_sort ? count_len : n_sort) / kTile + 2;
     int32_t *perm = nullptr, *perm_tmp = nullptr, *counts = nullptr, *scan_tmp = nullptr,
-            *deg = nullptr, *small = nullptr, *n_piece = nullptr, *n_slot = nullptr,
+            *small = nullptr, *n_piece = nullptr, *n_slot = nullptr,
             *is_split = nullptr, *piece_base = nullptr, *slot_base = nullptr,
             *split_base = nullptr, *band_start = nullptr;
     int32_t *u_source = nullptr, *u_begin = nullptr, *u_end = nullptr, *u_slot = nullptr,
@@ -693,7 +705,6 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk, 
     PMA_TRY(hipMalloc(&perm_tmp, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMalloc(&counts, count_len * i4));
     PMA_TRY(hipMalloc(&scan_tmp, scan_len * i4));
-    PMA_TRY(hipMalloc(&deg, S * i4));
     PMA_TRY(hipMalloc(&small, (8 + kBands + 1) * i4));
     PMA_TRY(hipMalloc(&n_piece, S * i4));
     PMA_TRY(hipMalloc(&n_slot, S * i4));
@@ -707,7 +718,6 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk, 
     PMA_TRY(hipMemsetAsync(g->csc_tgt + nnz, 0, kSrcPad * i4, stream));
     PMA_TRY(hipMalloc(&g->csc_eid, (nnz + kSrcPad) * i4));
     PMA_TRY(hipMemsetAsync(g->csc_eid + nnz, 0, kSrcPad * i4, stream));
-    PMA_TRY(hipMemsetAsync(deg, 0, S * i4, stream));
     PMA_TRY(hipMemsetAsync(small, 0, (8 + kBands + 1) * i4, stream));
     iota_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, nnz);
     PMA_TRY(radix_sort_perm(g->csr_src, bits_for(S - 1), perm, perm_tmp, nnz, counts, scan_tmp,
@@ -715,8 +725,7 @@ pma_status build_csc(GraphDev *g, int64_t nnz, int64_t L, int64_t S, int chunk, 
     PMA_TRY(hipMemsetAsync(perm + nnz, 0, kSrcPad * i4, stream));
     csc_fill<<<grid_for(nnz, 256), 256, 0, stream>>>(perm, g->csr_tgt, g->csr_eid, nnz,
                                                      g->csc_tgt, g->csc_eid);
-    degree_kernel<<<grid_for(nnz, 256), 256, 0, stream>>>(g->csr_src, nnz, deg);
-    PMA_TRY(scan_exclusive(deg, g->csc_ptr, S, g->csc_ptr + S, scan_tmp, stream));
+    bounds_kernel<<<grid_for(S + 1, 256), 256, 0, stream>>>(g->csr_src, perm, nnz, S, g->csc_ptr);
     g->csc_pos = perm;   // kept
     perm = nullptr;
     // pieces per source: band segments, each in pieces of at most chunk
@@ -788,7 +797,7 @@ fail:
         g->n_stasks = g->n_ssplit = g->n_sslots = 0;
     }
 done:
-    for (int32_t *q : {perm, perm_tmp, counts, scan_tmp, deg, small, n_piece, n_slot, is_split,
+    for (int32_t *q : {perm, perm_tmp, counts, scan_tmp, small, n_piece, n_slot, is_split,
                        piece_base, slot_base, split_base, band_start, u_source, u_begin, u_end,
                        u_slot, u_key, s_key, tperm, tperm_tmp, sc})
         if (q)
