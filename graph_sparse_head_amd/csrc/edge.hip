@@ -81,6 +81,11 @@ struct EdgeK {
     // query tokens and each piece projects its target's rows with Wq, bq
     int fuse_in;
     const void *wq, *bq;
+    // hot-row cache (edge_fast with HOT slots): hot_src[i] is the key/value
+    // row cached in slot i; hot_csr is csr_src with ~slot in place of the
+    // cached rows (passed as the gather index of that kernel only)
+    const int32_t *hot_src, *hot_csr;
+    int n_hot;
 };
 
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -364,6 +369,10 @@ __device__ inline uint4 q_proj_wave(const uint4 &x, int lane, const char *wlds)
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
+// Hot-row cache slot: the 16-byte key chunks of a wavefront's 64 lanes, then
+// their value chunks, for one source row.
+constexpr uint32_t kHotSlot = 2048;
+
 // Fast path: d = CH * LPH with 16-byte chunks.
 //
 // Per edge the source's key/value row offset is wave-uniform: one scalar
@@ -377,7 +386,7 @@ __device__ inline uint4 q_proj_wave(const uint4 &x, int lane, const char *wlds)
 // at a time, the remainder one at a time.
 // KPM: 0 no mask, 1 one mask word per position covers the wavefront's
 // samples, 2 two words (64 samples per wavefront: embed_dim = CH).
-template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLane {
+template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = false> struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
     static constexpr bool BF = sizeof(T) == 2;
@@ -398,10 +407,30 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLa
     uint64_t row2;
     Off loff, vloff;   // this lane's key and value chunk inside a source's rows
     uint32_t sc_lane, sc_edge;            // scores element offsets: this lane's, per edge
+    const char *hl;                       // this lane's key chunk in hot-row slot 0 (LDS)
 
     __device__ EdgeLane(const EdgeK &a_) : a(a_) {}
 
+    // a cached row (index ~slot): key and value chunks from LDS
+    __device__ inline void gather_hot(int s, Chunk<T, CH> &k, Chunk<T, CH> &v) const
+    {
+        const char *h = hl + (uint32_t)(~s) * kHotSlot;
+        k.u = *reinterpret_cast<const uint4 *>(h);
+        v.u = *reinterpret_cast<const uint4 *>(h + 1024);
+    }
+
     __device__ inline void gather(int s, Chunk<T, CH> &k, Chunk<T, CH> &v) const
+    {
+        if constexpr (HT) {
+            if (s < 0) {   // wave-uniform
+                gather_hot(s, k, v);
+                return;
+            }
+        }
+        gather_cold(s, k, v);
+    }
+
+    __device__ inline void gather_cold(int s, Chunk<T, CH> &k, Chunk<T, CH> &v) const
     {
         if constexpr (W32) {
             const uint32_t so = (uint32_t)s * (uint32_t)row2;   // uniform
@@ -458,8 +487,26 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLa
             }
         }
         Chunk<T, CH> kk[N], vv[N];
+        if constexpr (HT) {
+            // A row lists its cached sources first: a step is all cached, all
+            // from memory, or (once per piece) the boundary between them.
+            int sv[N];
 #pragma unroll
-        for (int u = 0; u < N; ++u) gather(csrc ? csrc[u] : src[p + u], kk[u], vv[u]);
+            for (int u = 0; u < N; ++u) sv[u] = src[p + u];
+            if (sv[N - 1] < 0) {
+#pragma unroll
+                for (int u = 0; u < N; ++u) gather_hot(sv[u], kk[u], vv[u]);
+            } else if (sv[0] >= 0) {
+#pragma unroll
+                for (int u = 0; u < N; ++u) gather_cold(sv[u], kk[u], vv[u]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < N; ++u) gather(sv[u], kk[u], vv[u]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < N; ++u) gather(csrc ? csrc[u] : src[p + u], kk[u], vv[u]);
+        }
         if constexpr (PRE) {
 #pragma unroll
             for (int u = 0; u < N; ++u) nsrc[u] = src[p + N + u];
@@ -554,12 +601,14 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM> struct EdgeLa
     }
 };
 
-template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, int KPM>
-__global__ void __launch_bounds__(256)
+template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, int KPM,
+          int HOT = 0>
+__global__ void __launch_bounds__(HOT ? 1024 : 256)
 // (at least 7 wavefronts per SIMD: at most 72 VGPRs. The q-projecting variant
 // needs 68 without spilling, which measured 5 % faster than squeezing it into
-// 64 for 8 wavefronts; the variants without the fused projections fit 64.)
-__attribute__((amdgpu_waves_per_eu(7)))
+// 64 for 8 wavefronts; the variants without the fused projections fit 64.
+// With the hot-row cache one 16-wavefront workgroup fills a CU's LDS.)
+__attribute__((amdgpu_waves_per_eu(HOT ? 4 : 7)))
 edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
           const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end,
           const int32_t *__restrict__ task_slot, const uint32_t *__restrict__ kpm_csr)
@@ -567,16 +616,12 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     // The index arrays come in as noalias arguments: no store of this kernel
     // can reach them, so their wave-uniform reads stay scalar loads.
     static_assert(!QF || E_FUSE > 0, "the q prologue comes with the out_proj epilogue");
+    static_assert(HOT == 0 || (QF && W32 && !SC && KPM == 0 && CH * sizeof(T) == 16),
+                  "the hot-row cache serves the unmasked q-projecting kernel");
+    constexpr int WPB = HOT ? 16 : 4;   // wavefronts per workgroup
     constexpr int WB = E_FUSE > 0 ? staged_bytes<T, E_FUSE>() : 16;
     __shared__ __attribute__((aligned(16))) char wlds[QF ? 2 * WB : WB];
-    if constexpr (E_FUSE > 0) {
-        if (a.fuse_out) {   // uniform over the launch; before any wavefront exits
-            stage_wo<T, CH, E_FUSE>(a, wlds);
-            if constexpr (QF)   // Wq after Wo
-                stage_w<T, CH, E_FUSE>(a.wq, a.bq, wlds + WB);
-            __syncthreads();
-        }
-    }
+    __shared__ __attribute__((aligned(16))) char hlds[HOT > 0 ? HOT * kHotSlot : 16];
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Each wavefront serves one sample group (pass) and walks the pieces
@@ -589,23 +634,63 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         // group's key/value rows.
         const uint32_t x = blockIdx.x & 7, xq = div31(x, a.pass_m, a.pass_sh);
         pass = x - xq * a.passes;
-        task = ((blockIdx.x >> 3) * a.xcd_per + xq) * 4 + wave;
+        task = ((blockIdx.x >> 3) * a.xcd_per + xq) * WPB + wave;
     } else if (a.xcd_map == 2) {
         // Sample groups one after another in launch order: the wavefronts in
         // flight read the key/value rows of few groups at a time.
-        const uint32_t w = blockIdx.x * 4 + wave;
+        const uint32_t w = blockIdx.x * WPB + wave;
         pass = div31(w, a.ts_m, a.ts_sh);
         task = w - pass * a.tstride;
     } else {
-        const uint32_t w = blockIdx.x * 4 + wave;
+        const uint32_t w = blockIdx.x * WPB + wave;
         task = div31(w, a.pass_m, a.pass_sh);
         pass = w - task * a.passes;
     }
+    if constexpr (HOT > 0) {
+        // The workgroup's sample group (pass: the same for all its wavefronts,
+        // XCD-pinned launch) reads the key/value rows of a few popular
+        // sources on a large share of its edges: their chunks are copied to
+        // LDS once, in the lane order of the gathers, and read from there.
+        constexpr int NF = HOT * (int)kHotSlot / 16 / (64 * WPB);   // chunks per thread
+        static_assert(HOT * (int)kHotSlot / 16 % (64 * WPB) == 0, "whole chunks per thread");
+        const int cpr = a.E / CH;
+        uint4 v[NF];
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int f = threadIdx.x + 64 * WPB * i;
+            const int slot = f >> 7, ln = f & 63;
+            const uint32_t c = pass * 64 + ln;
+            v[i] = make_uint4(0, 0, 0, 0);
+            if (slot < a.n_hot && c < (uint32_t)(a.B * cpr)) {
+                const int b = (int)div31(c, a.cpr_m, a.cpr_sh);
+                const int col = ((int)c - b * cpr) * CH;
+                uint64_t off = (uint64_t)a.hot_src[slot] * a.lay.kv_s + (uint64_t)b * a.lay.kv_b + col;
+                if (f & 64)
+                    off += a.lay.kv_v;
+                v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const T *>(a.kv) + off);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+            *reinterpret_cast<uint4 *>(hlds + (threadIdx.x + 64 * WPB * i) * 16) = v[i];
+    }
+    if constexpr (E_FUSE > 0) {
+        // uniform over the launch; before any wavefront exits (the staging
+        // is written for 256 threads)
+        if (a.fuse_out && (HOT == 0 || threadIdx.x < 256)) {
+            stage_wo<T, CH, E_FUSE>(a, wlds);
+            if constexpr (QF)   // Wq after Wo
+                stage_w<T, CH, E_FUSE>(a.wq, a.bq, wlds + WB);
+        }
+    }
+    if (HOT > 0 || (E_FUSE > 0 && a.fuse_out))
+        __syncthreads();
     if (task >= (uint32_t)a.n_tasks)
         return;
 
-    EdgeLane<T, CH, LPH, W32, SC, KPM> st(a);
+    EdgeLane<T, CH, LPH, W32, SC, KPM, (HOT > 0)> st(a);
     st.src = csr_src;
+    st.hl = hlds + lane * 16;
     const int B = a.B, E = a.E;
     const int cpr = E / CH;                       // chunks per sample row
     const uint32_t c = pass * 64 + lane;
@@ -1139,6 +1224,9 @@ EdgeK make_k(const EdgeArgs &x)
     k.scores = x.scores;
     k.weights = x.weights;
     k.average = x.average;
+    k.hot_src = x.hot_src;
+    k.hot_csr = x.hot_csr;
+    k.n_hot = x.hot_csr && x.hot_src ? x.n_hot : 0;
     return k;
 }
 
@@ -1168,15 +1256,23 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     // Workgroups of 4 wavefronts. With persist > 0 at most persist
     // workgroups per CU are launched and each wavefront walks several
     // pieces; otherwise one wavefront per (piece, sample group).
-    const int64_t cap = persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
+    const bool w32 = offsets32(k, sizeof(T));
+    // Hot-row cache: one resident 16-wavefront workgroup per CU, XCD-pinned
+    // sample groups (each workgroup serves one group).
+    constexpr int kHot = kHotRows;
+    const bool hot = QF && k.n_hot > 0 && k.n_hot <= kHot && k.xcd_map == 1 &&
+                     8 % k.passes == 0 && w32 && !k.scores && !k.kpm_bits;
+    const int wpb = hot ? 16 : 4;
+    const int64_t cap = hot ? (int64_t)cu_count()
+                            : persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
     int64_t blocks;
     if (k.xcd_map == 1 && 8 % k.passes == 0) {
         const int64_t per = 8 / k.passes;   // workgroups per pass per round of 8
-        int64_t rounds = (k.n_tasks + 4 * per - 1) / (4 * per);
+        int64_t rounds = (k.n_tasks + wpb * per - 1) / (wpb * per);
         rounds = std::min(rounds, std::max<int64_t>(1, cap / 8));
         blocks = 8 * rounds;
         k.xcd_per = (uint32_t)per;
-        k.tstride = (uint32_t)(rounds * per * 4);
+        k.tstride = (uint32_t)(rounds * per * wpb);
     } else {
         if (k.xcd_map != 2 || k.passes == 1)
             k.xcd_map = 0;
@@ -1188,8 +1284,14 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
         k.tstride = (uint32_t)(blocks * 4 / k.passes);
         magic31(k.tstride, k.ts_m, k.ts_sh);
     }
-    const bool w32 = offsets32(k, sizeof(T));
     const unsigned nb = (unsigned)blocks;
+    if constexpr (QF) {
+        if (hot) {
+            edge_fast<T, CH, LPH, 4, E_FUSE, QF, true, false, 0, kHot><<<nb, 1024, 0, s>>>(
+                k, k.hot_csr, k.task_target, k.task_begin, k.task_end, k.task_slot, k.kpm_csr);
+            return hipGetLastError();
+        }
+    }
 #define PMA_EDGE_LAUNCH(W, S, M)                                                          \
     edge_fast<T, CH, LPH, 4, E_FUSE, QF, W, S, M><<<nb, 256, 0, s>>>(                    \
         k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.kpm_csr)

@@ -7,7 +7,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
+#include <numeric>
 #include <vector>
 
 
@@ -52,6 +54,12 @@ struct pma_plan {
     int nt = -1;                // PMA_NT: non-temporal (1) or cached (0) q / mixed streams, auto (-1)
     int persist = -1;           // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece, -1 auto)
     int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
+    bool hot = false;           // PMA_HOT=1: hot-row cache in the q-projecting edge kernel
+    // hot-row cache: the gather index (hot_key) with ~slot for the edges of
+    // the n_hot most-read rows hot_src[slot]
+    int32_t *hot_csr = nullptr, *hot_src = nullptr;
+    const int32_t *hot_key = nullptr;
+    int n_hot = 0;
     std::vector<int64_t> h_src, h_tgt;
     pma::GraphDev g;
     // workspace, grown on demand
@@ -183,6 +191,72 @@ namespace {
 
 // attn: a plan for the attention calls (embed_dim, num_heads checked); else
 // a graph-only plan (embed_dim = num_heads = 0) for the PackedLinear calls.
+// The hot-row cache of the q-projecting edge kernel: the kHotRows rows of the
+// gather index idx (rows rows) that the most edges read, if read by at least
+// two, become LDS slots; hot_csr is idx with ~slot in their place. Built once
+// per index array (host pass over the nnz indices).
+pma_status build_hot(pma_plan *p, const int32_t *idx, int64_t rows, hipStream_t stream)
+{
+    if (p->hot_key == idx)
+        return PMA_OK;
+    const int64_t nnz = p->nnz;
+    std::vector<int32_t> h, order, slot_of;
+    try {
+        h.resize(nnz + pma::kSrcPad, 0);
+        order.resize(rows);
+        slot_of.assign(rows, -1);
+    } catch (...) {
+        return PMA_E_OOM;
+    }
+    if (hipMemcpyAsync(h.data(), idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return PMA_E_DEVICE;
+    std::vector<int64_t> cnt(rows, 0);
+    for (int64_t i = 0; i < nnz; ++i)
+        ++cnt[h[i]];
+    std::iota(order.begin(), order.end(), 0);
+    const int64_t k = std::min<int64_t>(pma::kHotRows, rows);
+    std::partial_sort(order.begin(), order.begin() + k, order.end(), [&](int32_t a, int32_t b) {
+        return cnt[a] > cnt[b] || (cnt[a] == cnt[b] && a < b);
+    });
+    int n = 0;
+    while (n < k && cnt[order[n]] >= 2)
+        ++n;
+    for (int i = 0; i < n; ++i)
+        slot_of[order[i]] = i;
+    for (int64_t i = 0; i < nnz; ++i)
+        if (slot_of[h[i]] >= 0)
+            h[i] = ~slot_of[h[i]];
+    // each target row lists its cached sources first (the edges of a row may
+    // come in any order: the softmax and the mix are sums over them)
+    std::vector<int32_t> rp;
+    try {
+        rp.resize(p->L + 1);
+    } catch (...) {
+        return PMA_E_OOM;
+    }
+    if (hipMemcpyAsync(rp.data(), p->g.row_ptr, (p->L + 1) * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return PMA_E_DEVICE;
+    for (int64_t t = 0; t < p->L; ++t)
+        std::stable_partition(h.begin() + rp[t], h.begin() + rp[t + 1], [](int32_t v) { return v < 0; });
+    if (!p->hot_csr && hipMalloc(&p->hot_csr, (nnz + pma::kSrcPad) * sizeof(int32_t)) != hipSuccess)
+        return PMA_E_OOM;
+    if (!p->hot_src && hipMalloc(&p->hot_src, pma::kHotRows * sizeof(int32_t)) != hipSuccess)
+        return PMA_E_OOM;
+    order.resize(pma::kHotRows, 0);
+    if (hipMemcpyAsync(p->hot_csr, h.data(), (nnz + pma::kSrcPad) * sizeof(int32_t), hipMemcpyHostToDevice,
+                       stream) != hipSuccess ||
+        hipMemcpyAsync(p->hot_src, order.data(), pma::kHotRows * sizeof(int32_t), hipMemcpyHostToDevice,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return PMA_E_DEVICE;
+    p->hot_key = idx;
+    p->n_hot = n;
+    return PMA_OK;
+}
+
 pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64_t *target_index,
                        int64_t nnz, int64_t query_features, int64_t key_features,
                        int64_t embed_dim, int64_t num_heads, int add_self_loops, pma_dtype dtype,
@@ -265,6 +339,7 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_BWD_CHUNK  n: most edges of one source piece in the backward pass
     //   PMA_BWD_SUB    n: target bands per XCD for those pieces (1..64)
     //   PMA_BWD_ORDER  backward target pass over sample groups, as PMA_XCD_MAP
+    //   PMA_HOT        1: hot-row LDS cache in the q-projecting edge kernel
     // Piece length: a target is split only when it has far more edges than
     // the average target (16x, rounded up to a power of two, at least 256).
     // Splitting balances graphs with a few very long rows among many short
@@ -297,6 +372,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     }
     if (const char *ev = getenv("PMA_FUSE_OUT"))
         p->fuse_out = ev[0] != '0';
+    if (const char *ev = getenv("PMA_HOT"))
+        p->hot = ev[0] == '1';
     if (const char *ev = getenv("PMA_FUSE_IN"))
         p->fuse_in = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
@@ -366,6 +443,10 @@ PMA_API pma_status pma_destroy(pma_plan *plan)
     (void)hipDeviceSynchronize();
     pma::free_graph(&plan->g);
     free_workspace(plan);
+    if (plan->hot_csr)
+        (void)hipFree(plan->hot_csr);
+    if (plan->hot_src)
+        (void)hipFree(plan->hot_src);
     if (plan->bw)
         (void)hipFree(plan->bw);
     if (plan->lin)
@@ -648,6 +729,21 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     const int64_t groups = (B * (E / (p->dtype == PMA_BF16 ? 8 : 4)) + 63) / 64;
     const bool in_turn = groups == 2 && ea.kv_bytes > ((uint64_t)256 << 20) && ea.persist == 0;
     ea.xcd_map = p->xcd_map >= 0 ? p->xcd_map : (in_turn ? 2 : 1);
+    // Hot-row cache for the q-projecting kernel (no mask, no weights; opt-in):
+    // each workgroup keeps the key/value rows of the most-read sources for
+    // its sample group in LDS. Measured on MI355X it is slower on the
+    // gene-regulatory workload (166 against 134 us per forward): the one
+    // resident 16-wavefront workgroup per CU that the 128 KB cache needs runs
+    // 4 wavefronts per SIMD instead of 7 and gives up the balancing of queued
+    // workgroups, which costs more than the key/value reads it saves.
+    if (fuse_in && p->hot && !kpm && !weights && ea.xcd_map == 1) {
+        st = build_hot(p, ea.gather_src, S_ws, stream);
+        if (st != PMA_OK)
+            return fail(st, "hot-row index build failed");
+        ea.hot_csr = p->hot_csr;
+        ea.hot_src = p->hot_src;
+        ea.n_hot = p->n_hot;
+    }
 
     if (kpm && !pma::mask_supported(ea))
         return fail(PMA_E_UNSUPPORTED, "key_padding_mask with a workspace tensor of 2 GiB or more");

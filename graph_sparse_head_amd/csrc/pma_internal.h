@@ -12,6 +12,8 @@ namespace pma {
 
 // Zero entries kept after the last source index (see GraphDev::csr_src).
 constexpr int kSrcPad = 16;
+// rows the q-projecting edge kernel keeps in LDS (64 x 2 KB per workgroup)
+constexpr int kHotRows = 64;
 // The backward's source pieces are grouped into kBands bands of targets with
 // equal edge counts, one band per XCD (an MI355X has 8).
 constexpr int kBands = 8;
@@ -139,6 +141,10 @@ struct EdgeArgs {
     int fuse_in = 0;
     const void *wq = nullptr, *bq = nullptr;
     void *out = nullptr;
+    // hot-row cache of the q-projecting edge kernel: gather_src with ~slot for
+    // the edges of the n_hot rows hot_src[slot] (nullptr: no cache)
+    const int32_t *hot_csr = nullptr, *hot_src = nullptr;
+    int n_hot = 0;
 };
 
 // Whether edge_fast / merge_fast can apply out_proj themselves.

@@ -247,6 +247,7 @@ KNOBS = [
     {"PMA_XCD_MAP": "0", "PMA_NT": "0"},
     {"PMA_FUSE_IN": "0"},
     {"PMA_FUSE_IN": "0", "PMA_CHUNK": "3"},
+    {"PMA_HOT": "1"},
     {"PMA_XCD_MAP": "2"},
     {"PMA_XCD_MAP": "2", "PMA_PERSIST": "1", "PMA_CHUNK": "3"},
 ]
@@ -287,6 +288,27 @@ def test_q_projection_in_edge_kernel(fuse_in, compact, shared, B, H, monkeypatch
     keep = c.src < 200   # sources 200.. are never read
     c.src, c.tgt = c.src[keep], c.tgt[keep]
     _full_check(c, need_weights=True, average=False)
+
+
+# Hot-row cache (PMA_HOT=1; bf16 inference with the q projection in the edge
+# kernel, no weights, no mask): each workgroup keeps the key/value rows of the 64
+# most-read sources in LDS and a target row lists those sources first, so a
+# piece runs all-cached steps, all-memory steps and at most one step across
+# the boundary. Zipf-popular sources, split targets (PMA_CHUNK=5), compacted
+# key/value rows, one and four sample groups and partial ones.
+@pytest.mark.parametrize("hot", ["0", "1"])
+@pytest.mark.parametrize("chunk", ["auto", "5"])
+@pytest.mark.parametrize("compact", ["0", "1"])
+@pytest.mark.parametrize("B,H", [(3, 4), (8, 4), (32, 4), (8, 1), (8, 8), (20, 2)])
+def test_hot_row_cache(hot, chunk, compact, B, H, monkeypatch):
+    monkeypatch.setenv("PMA_HOT", hot)
+    monkeypatch.setenv("PMA_COMPACT", compact)
+    if chunk != "auto":
+        monkeypatch.setenv("PMA_CHUNK", chunk)
+    c = synth.gene(n=3000, B=B, H=H, max_deg=400)
+    keep = c.src % 7 != 3   # some sources never read (compaction renumbers the rest)
+    c.src, c.tgt = c.src[keep], c.tgt[keep]
+    _full_check(c, need_weights=False)
 
 
 @pytest.mark.parametrize("knobs", [{"PMA_PERSIST": "1"}, {"PMA_PERSIST": "1", "PMA_XCD_MAP": "1"},
