@@ -233,7 +233,8 @@ def test_backward_full_size_sampled_rows():
     # origin. A target's query-gradient row depends only on the edges into
     # it, and a source's key/value-gradient rows only on the edges into the
     # targets it feeds: the gradient oracle runs on those subgraphs. The
-    # out_proj bias gradient is the column sum of the upstream gradient.
+    # out_proj bias gradient is the column sum of the upstream gradient, its
+    # weight gradient the upstream gradient times the forward's mixed rows.
     c = synth.gene()
     g = np.random.default_rng(11)
     c.xk = synth._tokens(g, c.xq.shape, c.dtype)
@@ -251,7 +252,7 @@ def test_backward_full_size_sampled_rows():
                               dev["wv"], dev["wo"], True, save,
                               torch.from_numpy(G).to(torch.bfloat16).cuda())
         torch.cuda.synchronize()
-        got = {n: to_f64(gr[n], c.dtype) for n in ("query", "key", "value", "o_b")}
+        got = {n: to_f64(gr[n], c.dtype) for n in ("query", "key", "value", "o_w", "o_b")}
     finally:
         pma.pma_destroy(plan)
     src, tgt = oracle.prepare_edges(c.src, c.tgt, c.L, c.S, c.E, c.H, False)
@@ -283,3 +284,9 @@ def test_backward_full_size_sampled_rows():
         assert err <= TOL[c.dtype], (n, err)
     err = max_abs_rel(got["o_b"], G64.sum(axis=(0, 1)))
     assert err <= TOL[c.dtype], ("o_b", err)
+    # the out_proj weight gradient over all 640,000 rows: G^T mixed, with
+    # mixed from the forward oracle
+    mixed = oracle.case_forward(c, want_mixed=True)["mixed"].reshape(-1, c.E)
+    dwo = G64.reshape(-1, c.E).T @ mixed
+    err = max_abs_rel(got["o_w"].reshape(c.E, c.E), dwo)
+    assert err <= TOL[c.dtype], ("o_w", err)
