@@ -226,67 +226,83 @@ def test_backward_mask_whole_wavefronts(shape, monkeypatch):
     _grad_check(c, "none", kpm=kpm)
 
 
-def test_backward_full_size_sampled_rows():
-    # The gene workload at its full size and batch (B = 32: four sample
-    # groups, split targets, hub sources in the backward's source bands),
-    # with separate key and value tokens so that each gradient row has one
-    # origin. A target's query-gradient row depends only on the edges into
-    # it, and a source's key/value-gradient rows only on the edges into the
-    # targets it feeds: the gradient oracle runs on those subgraphs. The
-    # out_proj bias gradient is the column sum of the upstream gradient, its
-    # weight gradient the upstream gradient times the forward's mixed rows.
-    c = synth.gene()
+def _sampled_rows_check(c, shared, mid_range):
+    """Query-gradient rows of sampled targets and key/value-gradient rows of
+    sampled sources against the gradient oracle on the subgraphs that
+    determine them, plus the out_proj bias and weight gradients over all rows
+    (column sums of G, and G^T times the forward oracle's mixed rows)."""
     g = np.random.default_rng(11)
-    c.xk = synth._tokens(g, c.xq.shape, c.dtype)
-    c.xv = synth._tokens(g, c.xq.shape, c.dtype)
-    print(f"[backward] full gene B={c.B} nnz={len(c.src)} sampled rows", flush=True)
+    print(f"[backward] full {c.name} B={c.B} nnz={len(c.src)} {c.dtype} sampled rows", flush=True)
     dev = synth.to_torch(c)
     G = g.standard_normal((c.B, c.L, c.E)).astype(np.float32)
-    G = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(G))
+    if c.dtype == "bf16":
+        G = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(G))
+    tdt = torch.float32 if c.dtype == "f32" else torch.bfloat16
     plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H, dtype=c.dtype)
     try:
         args = (dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"], dev["bk"],
                 dev["wv"], dev["bv"], dev["wo"], dev["bo"])
         _, _, save = pma.pma_forward_train(plan, *args)
         gr = pma.pma_backward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["wk"],
-                              dev["wv"], dev["wo"], True, save,
-                              torch.from_numpy(G).to(torch.bfloat16).cuda())
+                              dev["wv"], dev["wo"], True, save, torch.from_numpy(G).to(tdt).cuda())
         torch.cuda.synchronize()
         got = {n: to_f64(gr[n], c.dtype) for n in ("query", "key", "value", "o_w", "o_b")}
     finally:
         pma.pma_destroy(plan)
     src, tgt = oracle.prepare_edges(c.src, c.tgt, c.L, c.S, c.E, c.H, False)
     params = {k: oracle.widen(v, c.dtype) for k, v in c.params.items()}
-    xq, xk, xv = (oracle.widen(x, c.dtype) for x in (c.xq, c.xk, c.xv))
+    xq = oracle.widen(c.xq, c.dtype)
+    xk = xq if shared == "qkv" else oracle.widen(c.xk, c.dtype)
+    xv = xk if shared in ("kv", "qkv") else oracle.widen(c.xv, c.dtype)
     G64 = G.astype(np.float64)
     got["query"] = got["query"].reshape(c.B, c.L, c.E)
     got["key"] = got["key"].reshape(c.B, c.S, c.E)
     got["value"] = got["value"].reshape(c.B, c.S, c.E)
     deg_in = np.bincount(tgt, minlength=c.L)
     deg_out = np.bincount(src, minlength=c.S)
-    # targets: the longest row (split into pieces), 30 random live ones, one without edges
+    # targets: the longest row, 30 random live ones, one without edges
     live = np.flatnonzero(deg_in > 0)
-    T = np.unique(np.concatenate([[deg_in.argmax()], g.choice(live, 30, replace=False),
+    T = np.unique(np.concatenate([[deg_in.argmax()], g.choice(live, min(30, len(live)), replace=False),
                                   np.flatnonzero(deg_in == 0)[:1]]))
     sub = np.isin(tgt, T)
-    ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64)
+    ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
+                       shared=shared)
     err = max_abs_rel(got["query"][:, T], ref["query"][:, T])
     assert err <= TOL[c.dtype], ("query", err)
-    # sources: 12 with at most 300 edges and one with 1000-3000 (split in bands)
+    # sources: 12 with few edges and one with many (mid_range)
     small = np.flatnonzero((deg_out > 0) & (deg_out <= 300))
-    mid = np.flatnonzero((deg_out >= 1000) & (deg_out <= 3000))
+    mid = np.flatnonzero((deg_out >= mid_range[0]) & (deg_out <= mid_range[1]))
     Ssel = np.unique(np.concatenate([g.choice(small, 12, replace=False), mid[:1]]))
     T2 = np.unique(tgt[np.isin(src, Ssel)])
     sub = np.isin(tgt, T2)
-    ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64)
+    ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
+                       shared=shared)
     for n in ("key", "value"):
         err = max_abs_rel(got[n][:, Ssel], ref[n][:, Ssel])
         assert err <= TOL[c.dtype], (n, err)
     err = max_abs_rel(got["o_b"], G64.sum(axis=(0, 1)))
     assert err <= TOL[c.dtype], ("o_b", err)
-    # the out_proj weight gradient over all 640,000 rows: G^T mixed, with
-    # mixed from the forward oracle
     mixed = oracle.case_forward(c, want_mixed=True)["mixed"].reshape(-1, c.E)
     dwo = G64.reshape(-1, c.E).T @ mixed
     err = max_abs_rel(got["o_w"].reshape(c.E, c.E), dwo)
     assert err <= TOL[c.dtype], ("o_w", err)
+
+
+def test_backward_full_size_sampled_rows():
+    # The gene workload at its full size and batch (B = 32: four sample
+    # groups, split targets, hub sources in the backward's source bands; the
+    # training benchmark's launch configuration), with separate key and value
+    # tokens so that each gradient row has one origin. A target's
+    # query-gradient row depends only on the edges into it, and a source's
+    # key/value-gradient rows only on the edges into the targets it feeds.
+    c = synth.gene()
+    g = np.random.default_rng(12)
+    c.xk = synth._tokens(g, c.xq.shape, c.dtype)
+    c.xv = synth._tokens(g, c.xq.shape, c.dtype)
+    _sampled_rows_check(c, "none", (1000, 3000))
+
+
+def test_backward_full_size_sampled_rows_bipartite():
+    # The bipartite workload at its full size and batch (fp32, B = 16, key =
+    # value tokens: the key and value gradients are one tensor's).
+    _sampled_rows_check(synth.bipartite(), "kv", (20, 60))
