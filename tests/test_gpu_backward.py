@@ -238,7 +238,8 @@ def _sampled_rows_check(c, shared, mid_range):
     if c.dtype == "bf16":
         G = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(G))
     tdt = torch.float32 if c.dtype == "f32" else torch.bfloat16
-    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H, dtype=c.dtype)
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H, add_self_loops=c.add_self_loops,
+                          dtype=c.dtype)
     try:
         args = (dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"], dev["bk"],
                 dev["wv"], dev["bv"], dev["wo"], dev["bo"])
@@ -249,7 +250,7 @@ def _sampled_rows_check(c, shared, mid_range):
         got = {n: to_f64(gr[n], c.dtype) for n in ("query", "key", "value", "o_w", "o_b")}
     finally:
         pma.pma_destroy(plan)
-    src, tgt = oracle.prepare_edges(c.src, c.tgt, c.L, c.S, c.E, c.H, False)
+    src, tgt = oracle.prepare_edges(c.src, c.tgt, c.L, c.S, c.E, c.H, c.add_self_loops)
     params = {k: oracle.widen(v, c.dtype) for k, v in c.params.items()}
     xq = oracle.widen(c.xq, c.dtype)
     xk = xq if shared == "qkv" else oracle.widen(c.xk, c.dtype)
@@ -260,26 +261,43 @@ def _sampled_rows_check(c, shared, mid_range):
     got["value"] = got["value"].reshape(c.B, c.S, c.E)
     deg_in = np.bincount(tgt, minlength=c.L)
     deg_out = np.bincount(src, minlength=c.S)
-    # targets: the longest row, 30 random live ones, one without edges
-    live = np.flatnonzero(deg_in > 0)
-    T = np.unique(np.concatenate([[deg_in.argmax()], g.choice(live, min(30, len(live)), replace=False),
-                                  np.flatnonzero(deg_in == 0)[:1]]))
-    sub = np.isin(tgt, T)
-    ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
-                       shared=shared)
-    err = max_abs_rel(got["query"][:, T], ref["query"][:, T])
-    assert err <= TOL[c.dtype], ("query", err)
-    # sources: 12 with few edges and one with many (mid_range)
     small = np.flatnonzero((deg_out > 0) & (deg_out <= 300))
     mid = np.flatnonzero((deg_out >= mid_range[0]) & (deg_out <= mid_range[1]))
-    Ssel = np.unique(np.concatenate([g.choice(small, 12, replace=False), mid[:1]]))
-    T2 = np.unique(tgt[np.isin(src, Ssel)])
-    sub = np.isin(tgt, T2)
-    ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
-                       shared=shared)
-    for n in ("key", "value"):
-        err = max_abs_rel(got[n][:, Ssel], ref[n][:, Ssel])
-        assert err <= TOL[c.dtype], (n, err)
+    if shared == "qkv":
+        # one token tensor: a node's gradient row sums its uses as query,
+        # key and value, so its subgraph is the edges into the node and into
+        # every target it feeds (the longest row's node among the samples)
+        R = np.unique(np.concatenate([g.choice(small, 12, replace=False), mid[:1],
+                                      [deg_in.argmax()]]))
+        T2 = np.unique(np.concatenate([R, tgt[np.isin(src, R)]]))
+        sub = np.isin(tgt, T2)
+        ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
+                           shared=shared)
+        err = max_abs_rel(got["query"][:, R], ref["query"][:, R])
+        assert err <= TOL[c.dtype], ("tokens", err)
+        T = Ssel = np.zeros(0, np.int64)
+    else:
+        T = Ssel = None
+    # targets: the longest row, 30 random live ones, one without edges
+    if T is None:
+        live = np.flatnonzero(deg_in > 0)
+        T = np.unique(np.concatenate([[deg_in.argmax()],
+                                      g.choice(live, min(30, len(live)), replace=False),
+                                      np.flatnonzero(deg_in == 0)[:1]]))
+        sub = np.isin(tgt, T)
+        ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
+                           shared=shared)
+        err = max_abs_rel(got["query"][:, T], ref["query"][:, T])
+        assert err <= TOL[c.dtype], ("query", err)
+        # sources: 12 with few edges and one with many (mid_range)
+        Ssel = np.unique(np.concatenate([g.choice(small, 12, replace=False), mid[:1]]))
+        T2 = np.unique(tgt[np.isin(src, Ssel)])
+        sub = np.isin(tgt, T2)
+        ref = ob.gradients(c.B, c.L, c.S, c.E, c.H, xq, xk, xv, params, src[sub], tgt[sub], G64,
+                           shared=shared)
+        for n in ("key", "value"):
+            err = max_abs_rel(got[n][:, Ssel], ref[n][:, Ssel])
+            assert err <= TOL[c.dtype], (n, err)
     err = max_abs_rel(got["o_b"], G64.sum(axis=(0, 1)))
     assert err <= TOL[c.dtype], ("o_b", err)
     mixed = oracle.case_forward(c, want_mixed=True)["mixed"].reshape(-1, c.E)
@@ -306,3 +324,9 @@ def test_backward_full_size_sampled_rows_bipartite():
     # The bipartite workload at its full size and batch (fp32, B = 16, key =
     # value tokens: the key and value gradients are one tensor's).
     _sampled_rows_check(synth.bipartite(), "kv", (20, 60))
+
+
+def test_backward_full_size_sampled_rows_large():
+    # The 100k-node workload at its full size and batch (bf16, B = 8, E =
+    # 128, one token tensor, self loops, 5.1M edges).
+    _sampled_rows_check(synth.large(), "qkv", (200, 2000))
