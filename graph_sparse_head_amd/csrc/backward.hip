@@ -184,10 +184,11 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
             i = j - g * a.t_gthreads;
         }
         task = __builtin_amdgcn_readfirstlane((int)(i >> 6));
-        const int lane = threadIdx.x & 63;
-        const int bl = lane / CPR;
-        c = lane - bl * CPR;
-        b = g * (64 / CPR) + bl;
+        // lane l of group g is chunk (64 g + l) of the piece's B * CPR chunks
+        // (CPR need not divide 64)
+        const int cg = g * 64 + (threadIdx.x & 63);
+        b = cg / CPR;
+        c = cg - b * CPR;
     } else {
         const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
         const int64_t gb = idx / CPR;
@@ -226,10 +227,10 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dq[i] = 0.f;
-    // Mask: with whole wavefronts per piece and at most 32 samples per
-    // wavefront, one 32-bit word per CSR position (uniform: a scalar load)
-    // holds the bits of the wavefront's samples; otherwise each lane looks up
-    // its sample's bit by source.
+    // Mask: with whole wavefronts per piece whose samples lie in one 32-sample
+    // word (the host's choice of CM), one 32-bit word per CSR position
+    // (uniform: a scalar load) holds the bits of the wavefront's samples;
+    // otherwise each lane looks up its sample's bit by source.
     static_assert(!CM || UNI, "uniform mask words need whole wavefronts per piece");
     const uint32_t kw = CM ? (uint32_t)__builtin_amdgcn_readfirstlane(b) >> 5 : 0u;
     int s[kU], sn[kU];   // mask words (csr_mask) or sources; rows come through kv_src
@@ -1285,8 +1286,11 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
         const int64_t nt = a.n_ttasks * a.B * cpr, ns = a.n_stasks * a.B * cpr;
         // a piece's lanes fill whole wavefronts: wavefront-uniform indices
         const bool uni = ((int64_t)a.B * cpr) % 64 == 0;
-        // mask words by CSR position: whole wavefronts of at most 32 samples
-        const bool cm = uni && a.kpm_csr && cpr > 1;
+        // mask words by CSR position: whole wavefronts whose samples lie in
+        // one 32-sample word (a power-of-two cpr >= 2: 64 / cpr samples
+        // from a multiple of 64 / cpr; other cpr, e.g. 3 heads of one chunk,
+        // make wavefronts straddle words, so those look bits up by source)
+        const bool cm = uni && a.kpm_csr && cpr > 1 && (cpr & (cpr - 1)) == 0;
         // source pass with UNI: kBands interleaved runs of workgroups
         int64_t per_band = 0;
         for (int k = 0; k < kBands; ++k) {

@@ -385,7 +385,10 @@ constexpr uint32_t kHotSlot = 2048;
 // and k words (fp32 products and sums) and are scaled afterwards. Edges run U
 // at a time, the remainder one at a time.
 // KPM: 0 no mask, 1 one mask word per position covers the wavefront's
-// samples, 2 two words (64 samples per wavefront: embed_dim = CH).
+// samples, 2 two words (a wavefront's samples may straddle a multiple of
+// 32: 64 samples per wavefront, or a row of chunks that is not a power of
+// two, so that wavefronts start mid-row); each lane picks the word of its
+// own sample.
 template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = false> struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -395,7 +398,7 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = fal
     const int32_t *src;   // gather rows, from a noalias kernel argument
     const uint32_t *kbits;  // mask bits by CSR position, from a noalias kernel argument
     uint32_t kword;         // first 32-bit word of this wavefront's samples at a position
-    bool khi;               // this lane's sample is in the second of two words (64 samples per wavefront)
+    bool khi;               // this lane's sample is in the word after kword (KPM == 2)
     int B, b, h;
     bool active, head_lead;
     Chunk<T, CH> q;
@@ -532,8 +535,8 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = fal
             sc[u] = dot;
         }
         if constexpr (KPM > 0) {   // masked keys leave the softmax
-            // one uniform 64-bit word per edge holds the bits of all the
-            // wavefront's samples
+            // one or two uniform 32-bit words per edge hold the bits of all
+            // the wavefront's samples
 #pragma unroll
             for (int u = 0; u < N; ++u) {
                 uint32_t w = mlo[u];
@@ -705,7 +708,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     st.smul = a.scale;
     st.kbits = kpm_csr;
     st.kword = (pass * 64u / (uint32_t)cpr) >> 5;   // first sample of the pass / 32
-    st.khi = cpr == 1 && (b & 32) != 0;
+    st.khi = ((uint32_t)b >> 5) != st.kword;         // (only KPM == 2 reads it)
     // byte offsets: per source (uniform), this lane's key and value chunks
     st.row2 = (uint64_t)a.lay.kv_s * sizeof(T);
     if constexpr (W32) {
@@ -1300,14 +1303,21 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
             return hipErrorInvalidValue;
         if (!w32)   // refused by mask_supported()
             return hipErrorInvalidValue;
-        if (k.E / CH == 1) {   // 64 samples per wavefront: two mask words
-            if constexpr (LPH == 1 && E_FUSE == 0) {
+        // One 32-bit word per position holds a wavefront's samples when the
+        // chunks per row are a power of two of at least 2 (then a wavefront
+        // covers 64 / cpr <= 32 samples starting at a multiple of 64 / cpr).
+        // Otherwise (64 samples per wavefront, or e.g. 3 heads of one chunk:
+        // wavefronts of 21-22 samples starting anywhere) its samples may
+        // straddle two words.
+        const int cpr = k.E / CH;
+        if (cpr == 1 || (cpr & (cpr - 1)) != 0) {
+            if constexpr (E_FUSE == 0) {   // (embed_dim 64 has 8 or 16 chunks per row)
                 if (k.scores)
                     PMA_EDGE_LAUNCH(true, true, 2);
                 else
                     PMA_EDGE_LAUNCH(true, false, 2);
             } else {
-                return hipErrorInvalidValue;   // (E = CH means one chunk per head)
+                return hipErrorInvalidValue;
             }
         } else if (k.scores) {
             PMA_EDGE_LAUNCH(true, true, 1);

@@ -8,7 +8,7 @@ import pytest
 import graph_sparse_head_amd as pma
 import oracle
 from graph_sparse_head_amd import synth
-from gpu_helpers import TOL, max_abs_rel, run, sample_rows
+from gpu_helpers import TOL, max_abs_rel, record, run
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,22 @@ def test_mask_split_targets_and_knobs(knobs, dt, monkeypatch):
     _check(c, kpm, need_weights=True, average=True)
 
 
+# Rows of 3 chunks (3 heads of one 16-byte chunk each): wavefronts cover
+# 21-22 samples starting mid-row, so above 32 samples some wavefronts hold
+# samples on both sides of a multiple of 32 and need both mask words of an
+# edge (B = 64 and B = 70 both have such wavefronts).
+@pytest.mark.parametrize("shape", [("bf16", 24, 3), ("f32", 12, 3)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_H{s[2]}")
+@pytest.mark.parametrize("B", [64, 70])
+@pytest.mark.parametrize("need_weights", [False, True])
+def test_mask_rows_of_three_chunks(shape, B, need_weights):
+    dt, E, H = shape
+    c = synth.random_case(90 + B, B, 60, 60, E, H, 0.1, dtype=dt, name="mask_cpr3")
+    kpm = np.random.default_rng(91).random((c.B, c.S)) < 0.3
+    kpm[40] = True                                               # a fully masked sample past 32
+    _check(c, kpm, need_weights=need_weights, average=False)
+
+
 def test_mask_rejects():
     import torch
     c = synth.random_case(78, 2, 20, 20, 8, 2, 0.2, name="mask_bad")
@@ -143,24 +159,28 @@ def test_mask_rejects():
         pma.pma_destroy(plan)
 
 
-@pytest.mark.parametrize("name", ["gene", "bipartite"])
-def test_mask_full_size_sampled(name):
+@pytest.mark.parametrize("name", ["gene", "bipartite", "large"])
+def test_mask_full_size(name):
+    # every output element and every per-edge weight, a quarter of the keys
+    # masked per sample
     c = synth.make_config(name)
     kpm = np.random.default_rng(79).random((c.B, c.S)) < 0.25
     print(f"[mask] full {name}", flush=True)
     out, w, plan = run(c, kpm=kpm)
     try:
         src, tgt = pma.pma_edges(plan)
-        rows = sample_rows(c, tgt)
-        ref = oracle.case_forward(c, rows=rows, want_weights=c.need_weights, key_padding_mask=kpm)
-        err = max_abs_rel(out[rows[:, 0], rows[:, 1]], ref["out"])
-        assert err <= TOL[c.dtype], err
-        live = _live(kpm, src, tgt, c.B, c.L)
-        bo = oracle.widen(c.params["bo"], c.dtype)
-        assert (out[~live] == bo).all()
-        if c.need_weights:
-            rw = oracle.average_heads(ref["weights"])
-            have = ~np.isnan(rw)
-            assert max_abs_rel(w[have], rw[have]) <= TOL[c.dtype]
     finally:
         pma.pma_destroy(plan)
+    ref = oracle.case_forward(c, want_weights=c.need_weights, key_padding_mask=kpm)
+    err = max_abs_rel(out, ref["out"])
+    record(f"masked forward {name}", "out", err, TOL[c.dtype])
+    assert err <= TOL[c.dtype], err
+    live = _live(kpm, src, tgt, c.B, c.L)
+    bo = oracle.widen(c.params["bo"], c.dtype)
+    assert (out[~live] == bo).all()
+    if c.need_weights:
+        rw = oracle.average_heads(ref["weights"])
+        werr = max_abs_rel(w, rw)
+        record(f"masked forward {name}", "weights", werr, TOL[c.dtype])
+        assert werr <= TOL[c.dtype], werr
+        assert (w[kpm[:, src]] == 0).all()                       # masked: weight 0
