@@ -195,6 +195,18 @@ def _dptr(t, name: str, dtype, shape_tail: Optional[Sequence[int]] = None):
     return t.data_ptr()
 
 
+def _full_shape(t, name: str, shape) -> None:
+    """A caller-supplied buffer must have exactly ``shape``: the kernels read
+    or write that many elements through its pointer."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise PmaError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _weights_shape(plan: "Plan", lead, average: bool):
+    nnz = pma_nnz(plan)
+    return tuple(lead) + ((nnz,) if average else (nnz, plan.H))
+
+
 def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                 out=None, weights=None, need_weights: bool = False,
                 average_attn_weights: bool = True, stream=None, key_padding_mask=None):
@@ -221,18 +233,24 @@ def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w
     qp = _dptr(query, "query", tdt, (L, E))
     kp = _dptr(key, "key", tdt, (S, E))
     vp = _dptr(value, "value", tdt, (S, E))
+    for w, n in ((q_w, "q_w"), (k_w, "k_w"), (v_w, "v_w"), (o_w, "o_w")):
+        _full_shape(w, n, (E, E))
+    for b, n in ((q_b, "q_b"), (k_b, "k_b"), (v_b, "v_b"), (o_b, "o_b")):
+        _full_shape(b, n, (E,))
     wps = [_dptr(w, n, tdt, (E, E)) for w, n in ((q_w, "q_w"), (k_w, "k_w"), (v_w, "v_w"),
                                                   (o_w, "o_w"))]
     bps = [_dptr(b, n, tdt, (E,)) for b, n in ((q_b, "q_b"), (k_b, "k_b"), (v_b, "v_b"),
                                                 (o_b, "o_b"))]
     if out is None:
         out = torch.empty(lead + (L, E), dtype=tdt, device=query.device)
+    _full_shape(out, "out", lead + (L, E))
     op = _dptr(out, "out", tdt, (L, E))
     want_w = need_weights or weights is not None
+    wshape = _weights_shape(plan, lead, average_attn_weights)
     if want_w and weights is None:
-        nnz = pma_nnz(plan)
-        shape = lead + ((nnz,) if average_attn_weights else (nnz, H))
-        weights = torch.empty(shape, dtype=torch.float32, device=query.device)
+        weights = torch.empty(wshape, dtype=torch.float32, device=query.device)
+    if want_w:
+        _full_shape(weights, "weights", wshape)
     wp = _dptr(weights, "weights", torch.float32) if want_w else None
     if key_padding_mask is None:
         st = lib.pma_forward(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1], wps[2],
@@ -300,21 +318,31 @@ def pma_forward_train(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_
     B = int(np.prod(lead)) if lead else 1
     if tuple(key.shape[:-2]) != lead or tuple(value.shape[:-2]) != lead:
         raise PmaError(2, "the batch axes of query, key and value differ")
+    need = pma_train_bytes(plan, B)
     if save is None:
-        save = torch.empty(pma_train_bytes(plan, B), dtype=torch.uint8, device=query.device)
+        save = torch.empty(need, dtype=torch.uint8, device=query.device)
+    if save.numel() * save.element_size() < need:
+        raise PmaError(2, f"save holds {save.numel() * save.element_size()} bytes, "
+                          f"pma_train_bytes gives {need}")
     if out is None:
         out = torch.empty(lead + (L, E), dtype=tdt, device=query.device)
+    _full_shape(out, "out", lead + (L, E))
     want_w = need_weights or weights is not None
+    wshape = _weights_shape(plan, lead, average_attn_weights)
     if want_w and weights is None:
-        nnz = pma_nnz(plan)
-        weights = torch.empty(lead + ((nnz,) if average_attn_weights else (nnz, H)),
-                              dtype=torch.float32, device=query.device)
+        weights = torch.empty(wshape, dtype=torch.float32, device=query.device)
+    if want_w:
+        _full_shape(weights, "weights", wshape)
+    for w, n in ((q_w, "q_w"), (k_w, "k_w"), (v_w, "v_w"), (o_w, "o_w")):
+        _full_shape(w, n, (E, E))
+    for b, n in ((q_b, "q_b"), (k_b, "k_b"), (v_b, "v_b"), (o_b, "o_b")):
+        _full_shape(b, n, (E,))
     mp, per = _mask_args(key_padding_mask, lead, S)
     st = lib.pma_forward_train(
         plan.handle, B, _dptr(query, "query", tdt, (L, E)), _dptr(key, "key", tdt, (S, E)),
-        _dptr(value, "value", tdt, (S, E)), _dptr(q_w, "q_w", tdt, (E, E)), _dptr(q_b, "q_b", tdt),
-        _dptr(k_w, "k_w", tdt, (E, E)), _dptr(k_b, "k_b", tdt), _dptr(v_w, "v_w", tdt, (E, E)),
-        _dptr(v_b, "v_b", tdt), _dptr(o_w, "o_w", tdt, (E, E)), _dptr(o_b, "o_b", tdt),
+        _dptr(value, "value", tdt, (S, E)), _dptr(q_w, "q_w", tdt, (E, E)), _dptr(q_b, "q_b", tdt, (E,)),
+        _dptr(k_w, "k_w", tdt, (E, E)), _dptr(k_b, "k_b", tdt, (E,)), _dptr(v_w, "v_w", tdt, (E, E)),
+        _dptr(v_b, "v_b", tdt, (E,)), _dptr(o_w, "o_w", tdt, (E, E)), _dptr(o_b, "o_b", tdt, (E,)),
         _dptr(out, "out", tdt, (L, E)),
         _dptr(weights, "weights", torch.float32) if want_w else None,
         int(bool(average_attn_weights)), mp, per, _dptr(save, "save", torch.uint8),
@@ -334,6 +362,15 @@ def pma_backward(plan: Plan, query, key, value, q_w, k_w, v_w, o_w, has_bias: bo
     L, S, E = plan.L, plan.S, plan.E
     lead = tuple(query.shape[:-2])
     B = int(np.prod(lead)) if lead else 1
+    if tuple(key.shape[:-2]) != lead or tuple(value.shape[:-2]) != lead:
+        raise PmaError(2, "the batch axes of query, key and value differ")
+    _full_shape(grad_out, "grad_out", lead + (L, E))
+    for w, n in ((q_w, "q_w"), (k_w, "k_w"), (v_w, "v_w"), (o_w, "o_w")):
+        _full_shape(w, n, (E, E))
+    need = pma_train_bytes(plan, B)
+    if save.numel() * save.element_size() < need:
+        raise PmaError(2, f"save holds {save.numel() * save.element_size()} bytes, "
+                          f"pma_train_bytes gives {need}")
     def new(x):
         return torch.empty(x.shape, dtype=tdt, device=x.device)
     gq = new(query)
@@ -393,7 +430,10 @@ def pma_linear_forward(plan: Plan, x, weight, bias=None, out=None, stream=None):
     B = int(np.prod(lead)) if lead else 1
     if out is None:
         out = torch.empty(*lead, plan.L, C, dtype=tdt, device=x.device)
+    _full_shape(out, "out", lead + (plan.L, C))
     n = plan.nnz
+    _full_shape(weight, "weight", (n,))
+    _full_shape(bias, "bias", (plan.L,))
     st = lib.pma_linear_forward(plan.handle, B, C, _dptr(x, "x", tdt, (plan.S, C)),
                                 _dptr(weight, "weight", tdt, (n,)),
                                 _dptr(bias, "bias", tdt, (plan.L,)),
@@ -407,9 +447,13 @@ def pma_linear_backward(plan: Plan, x, weight, grad_out, has_bias: bool = True, 
     import torch
     lib = _load()
     tdt = torch.float32 if plan.dtype == "f32" else torch.bfloat16
+    if x.dim() < 2 or x.shape[-2] != plan.S:
+        raise PmaError(2, f"x has shape {tuple(x.shape)}, expected (..., {plan.S}, C)")
     C = int(x.shape[-1])
     lead = tuple(x.shape[:-2])
     B = int(np.prod(lead)) if lead else 1
+    _full_shape(weight, "weight", (plan.nnz,))
+    _full_shape(grad_out, "grad_out", lead + (plan.L, C))
     gx = torch.empty(x.shape, dtype=tdt, device=x.device)
     gw = torch.empty(plan.nnz, dtype=tdt, device=x.device)
     gb = torch.empty(plan.L, dtype=tdt, device=x.device) if has_bias else None

@@ -9,6 +9,12 @@ from graph_sparse_head_amd import synth
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
+def record(name, tensor, err, tol):
+    """Keep a parity figure for the terminal summary (tests/conftest.py)."""
+    from parity_log import PARITY
+    PARITY.append((name, tensor, float(err), float(tol)))
+
+
 def max_abs_rel(got, ref):
     """max |got - ref| / max |ref| over the whole tensor."""
     got = np.asarray(got, np.float64)
@@ -61,21 +67,3 @@ def run(case, plan=None, need_weights=None, average=None, dev=None, lead=None, k
     if w is not None:
         wn = w.cpu().numpy().astype(np.float64).reshape(case.B, plan.nnz, *([] if avg else [case.H]))
     return o, wn, plan
-
-
-def sample_rows(case, tgt, n_random=256, seed=0):
-    """(sample, target) rows for a sampled check: random rows, the largest
-    in-degree targets, targets without edges and targets with one edge."""
-    rng = np.random.default_rng(seed)
-    deg = np.bincount(tgt, minlength=case.L)
-    picks = set()
-    for t in np.argsort(-deg, kind="stable")[:8]:
-        picks.add(int(t))
-    for t in np.nonzero(deg == 0)[0][:8]:
-        picks.add(int(t))
-    for t in np.nonzero(deg == 1)[0][:8]:
-        picks.add(int(t))
-    rows = [(int(rng.integers(0, case.B)), int(t)) for t in picks]
-    rows += [(int(rng.integers(0, case.B)), int(rng.integers(0, case.L))) for _ in range(n_random)]
-    rows += [(case.B - 1, case.L - 1), (0, 0)]
-    return np.array(sorted(set(rows)), np.int64)

@@ -9,7 +9,7 @@ import torch
 import graph_sparse_head_amd as pma
 import oracle
 from graph_sparse_head_amd import synth
-from gpu_helpers import TOL, make_plan, max_abs_rel, run, sample_rows
+from gpu_helpers import TOL, make_plan, max_abs_rel, record, run
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +21,8 @@ def _full_check(case, need_weights=True, average=True, lead=None):
     try:
         ref = oracle.case_forward(case, want_weights=need_weights)
         err = max_abs_rel(out, ref["out"])
+        if case.name in ("tiny", "complete"):
+            record(f"forward {case.name}", "out", err, TOL[case.dtype])
         assert err <= TOL[case.dtype], err
         deg = np.bincount(ref["tgt"], minlength=case.L)
         bo = case.params["bo"]
@@ -197,36 +199,86 @@ def test_forward_rejects():
         pma.pma_destroy(plan)
 
 
+def test_binding_rejects_buffers_of_the_wrong_size():
+    """Preallocated outputs, save areas and gradients are checked against the
+    plan's sizes before any launch (a smaller buffer would be written past its
+    end on the device)."""
+    c = synth.tiny()
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H)
+    dev = synth.to_torch(c)
+    args = (plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"], dev["bk"],
+            dev["wv"], dev["bv"], dev["wo"], dev["bo"])
+    n = plan.nnz
+    f32 = dict(dtype=torch.float32, device="cuda")
+    try:
+        for kw in (dict(out=torch.empty(1, c.L, c.E, **f32)),
+                   dict(weights=torch.empty(c.B, n - 1, **f32)),
+                   dict(weights=torch.empty(c.B, n, **f32), average_attn_weights=False),
+                   dict(weights=torch.empty(1, n, **f32))):
+            with pytest.raises(pma.PmaError) as e:
+                pma.pma_forward(*args, **kw)
+            assert e.value.name == "PMA_E_SIZE", kw
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_forward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"][:4].contiguous(),
+                            dev["bq"], dev["wk"], dev["bk"], dev["wv"], dev["bv"], dev["wo"],
+                            dev["bo"])
+        assert e.value.name == "PMA_E_SIZE"
+        small = torch.empty(pma.pma_train_bytes(plan, c.B) - 256, dtype=torch.uint8,
+                            device="cuda")
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_forward_train(*args, save=small)
+        assert e.value.name == "PMA_E_SIZE"
+        out, _, save = pma.pma_forward_train(*args)
+        g = torch.empty(1, c.L, c.E, **f32)
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_backward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["wk"],
+                             dev["wv"], dev["wo"], True, save, g)
+        assert e.value.name == "PMA_E_SIZE"
+        with pytest.raises(pma.PmaError) as e:
+            pma.pma_backward(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["wk"],
+                             dev["wv"], dev["wo"], True, save[:64],
+                             torch.zeros(c.B, c.L, c.E, **f32))
+        assert e.value.name == "PMA_E_SIZE"
+        torch.cuda.synchronize()
+    finally:
+        pma.pma_destroy(plan)
+
+
 # ---------------------------------------------------------------------------
-# full-size workloads, sampled rows checked against the oracle
+# full-size workloads in the launch configuration the benchmark times: every
+# output element (and every per-edge weight) against the oracle
 
 
 @pytest.mark.parametrize("name", ["gene", "bipartite", "large"])
-def test_full_size_sampled(name):
+def test_full_size(name):
     c = synth.make_config(name)
     print(f"[forward] full {name} nnz0={c.nnz0}", flush=True)
     out, w, plan = run(c)
     try:
         src, tgt = pma.pma_edges(plan)
-        rows = sample_rows(c, tgt)
-        ref = oracle.case_forward(c, rows=rows, want_weights=c.need_weights)
-        got = out[rows[:, 0], rows[:, 1]]
-        err = max_abs_rel(got, ref["out"])
-        assert err <= TOL[c.dtype], err
-        deg = np.bincount(tgt, minlength=c.L)
-        bo = oracle.widen(c.params["bo"], c.dtype)
-        assert (out[:, deg == 0] == bo).all()
-        if c.need_weights:
-            rw = oracle.average_heads(ref["weights"])
-            have = ~np.isnan(rw)
-            werr = max_abs_rel(w[have], rw[have])
-            assert werr <= TOL[c.dtype], werr
-            # every target's weights sum to 1 (or 0 without edges), at every sample
-            sums = np.zeros((c.B, c.L))
-            np.add.at(sums, (slice(None), tgt), w)
-            assert np.abs(sums[:, deg > 0] - 1).max() <= 1e-4
     finally:
         pma.pma_destroy(plan)
+    ref = oracle.case_forward(c, want_weights=c.need_weights)
+    assert (ref["src"] == src).all() and (ref["tgt"] == tgt).all()
+    err = max_abs_rel(out, ref["out"])
+    record(f"forward {name}", "out", err, TOL[c.dtype])
+    assert err <= TOL[c.dtype], err
+    deg = np.bincount(tgt, minlength=c.L)
+    bo = oracle.widen(c.params["bo"], c.dtype)
+    assert (out[:, deg == 0] == bo).all()                       # exactly the bias
+    if c.need_weights:
+        rw = oracle.average_heads(ref["weights"])
+        werr = max_abs_rel(w, rw)
+        record(f"forward {name}", "weights", werr, TOL[c.dtype])
+        assert werr <= TOL[c.dtype], werr
+        assert (w >= 0).all()
+        assert (w[:, deg[tgt] == 1] == 1.0).all()               # lone edge: weight 1
+        # every target's weights sum to 1 at every sample
+        sums = np.zeros((c.B, c.L))
+        np.add.at(sums, (slice(None), tgt), w)
+        serr = np.abs(sums[:, deg > 0] - 1).max()
+        record(f"forward {name}", "weight sums", serr, TOL[c.dtype])
+        assert serr <= TOL[c.dtype], serr
 
 
 # ---------------------------------------------------------------------------
