@@ -2,15 +2,21 @@
 
 One step = one pma_forward over one batch: the key/value projection, the
 fused edge kernel (q projection, scores, online softmax, mix and out_proj) and
-the merge of split targets, on the gene-regulatory-prior workload (n = 20,000 nodes, Zipf 1.5
-source hubs, log-normal in-degree of mean 10, B = 32, E = 64, H = 4, bf16
-tokens, fp32 softmax and accumulation). Inputs are seeded synthetic tensors
+the merge of split targets, on the gene-regulatory-prior workload (n = 20,000
+nodes, Zipf 1.5 source hubs, log-normal in-degree of mean 10, B = 32, E = 64,
+H = 4, bf16 tokens; softmax, mixing weights and sums in fp32). Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.
 
 Prints one JSON line. ``value`` is edge-heads per second (nnz * H * B per
-forward); ``roofline`` rates the edge kernel, timed with HIP events on the
-forward's own stream, against MI355X's 8 TB/s HBM; ``cpu_baseline`` times the
-plain CPU oracle on a bounded sample of the same workload.
+forward) over the cold-cache leg: before each step a 1 GiB buffer is
+overwritten outside the step's events, so no input is still cached from the
+step before; the warm leg (steps back to back) is reported beside it.
+``roofline`` rates the edge kernel, timed with HIP events on the forward's own
+stream inside the headline leg, against MI355X's 8 TB/s HBM, counting the
+launch's compulsory bytes (each input and output byte once); the gather model
+(every edge's key and value rows per sample, mostly served by the caches) is
+reported under its own key. ``cpu_baseline`` times the plain CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -34,16 +40,28 @@ def _workload(name: str):
     return synth.make_config(name)
 
 
-def edge_kernel_bytes(B, L, nnz, E, s, weights=False, H=1, average=True):
-    """Algorithmic bytes of one edge-kernel launch: per sample, read each
-    target's query row and write its mixed row, and gather one key row and one
-    value row per live edge; plus the target-grouped edge index (row pointers
-    and one source id per edge). need_weights adds one fp32 weight per edge
-    (per head unless averaged) and the edge-order map."""
-    b = B * (L * E * s + nnz * 2 * E * s + L * E * s) + 4 * (L + 1) + 4 * nnz
+def edge_kernel_bytes(B, L, n_kv, nnz, n_tasks, E, s, weights=False, H=1):
+    """Compulsory HBM bytes of one edge-kernel launch: what the launch must
+    move at the least, each byte once. Per (target, sample): its query row in
+    (query tokens when the kernel projects q itself, else the projected q)
+    and its output row out (out when out_proj is fused, else the mixed row):
+    2 E s. Per (read source, sample): its key row and value row, once: 2 E s.
+    Per edge its gather index (4 B) and per piece its bounds, target and slot
+    (16 B). need_weights adds the stored score of every (edge, sample, head)
+    and the (max, sum) of every (target, sample, head), 4 B each."""
+    b = B * L * 2 * E * s + B * n_kv * 2 * E * s + 4 * nnz + 16 * n_tasks
     if weights:
-        b += 4 * nnz + 4 * B * nnz * (1 if average else H)
+        b += 4 * B * nnz * H + 8 * B * L * H
     return b
+
+
+def edge_gather_bytes(B, L, nnz, E, s):
+    """The gather model: every edge reads its source's key and value rows for
+    every sample (2 E s per edge and sample), plus each target's query row in
+    and output row out. Most of these reads are served by the L2 and the
+    last-level cache (hub sources repeat), so this counts the bytes the
+    vector memory path delivers, not HBM bytes."""
+    return B * (L * E * s + nnz * 2 * E * s + L * E * s) + 4 * (L + 1) + 4 * nnz
 
 
 def _traffic(cfg_name: str):
@@ -220,6 +238,9 @@ def main():
                     help="time PackedLinear (pma_linear_forward) on the workload's graph instead")
     ap.add_argument("--channels", type=int, default=1,
                     help="channels per node for --linear (1: the nn.Linear-shaped layer)")
+    ap.add_argument("--legs", default="cold,warm",
+                    help="timed legs in order: cold (each step after a 1 GiB cache overwrite; "
+                         "the first leg is the headline) and/or warm (steps back to back)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 5 times (counter calibration)")
     args = ap.parse_args()
@@ -241,6 +262,9 @@ def main():
     if args.linear:
         bench_linear(args)
         return
+    legs = [x for x in args.legs.split(",") if x]
+    if not legs or any(x not in ("cold", "warm") for x in legs) or len(set(legs)) != len(legs):
+        ap.error("--legs takes cold and/or warm")
 
     import torch
     import graph_sparse_head_amd as pma
@@ -287,89 +311,139 @@ def main():
                         weights=weights, need_weights=case.need_weights,
                         average_attn_weights=case.average, key_padding_mask=kpm)
 
-    for _ in range(args.warmup):
+    stream = torch.cuda.current_stream()
+    lib = pma._load()
+    # Cold cache (the headline): before every step, overwrite a 1 GiB buffer
+    # (four times the 256 MB last-level cache) outside the step's events, so
+    # that no input, weight or workspace line is still cached from the step
+    # before. Warm: steps back to back, for context.
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if "cold" in legs else None
+
+    def timed_steps(n, cold, stage_mask_of=None):
+        """Per-step event times (ms) of n steps; stage_mask_of(i) picks the
+        stages timed with HIP events inside step i (None: none)."""
+        evs = []
+        for i in range(n):
+            if cold:
+                scratch.fill_(float(i))
+            if stage_mask_of is not None:
+                lib.pma_profile_stages(plan.handle, stage_mask_of(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        if stage_mask_of is not None:
+            lib.pma_profile_stages(plan.handle, 0)
+        return [a.elapsed_time(b) for a, b in evs]
+
+    first = legs[0]
+    for i in range(args.warmup):
+        if first == "cold":
+            scratch.fill_(float(i))
         step()
     torch.cuda.synchronize()
     if not args.no_profile:
         pma.pma_profile_read(plan)          # discard anything earlier
-    # Inside the measured region the edge kernel is timed with HIP events on
-    # the forward's own stream in every EVERY-th step: each timed stage adds
-    # two event records, which themselves cost a few microseconds per step.
+    # The edge kernel is timed with HIP events on the forward's own stream in
+    # every EVERY-th step of the headline leg: each timed stage adds two event
+    # records, which themselves cost a few microseconds of that step.
     EVERY = 5
-    edge_only = pma.STAGES.index("edge")
-    lib = pma._load()
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        if not args.no_profile:
-            lib.pma_profile_stages(plan.handle, (1 << edge_only) if i % EVERY == 0 else 0)
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    stages = pma.pma_profile_read(plan) if not args.no_profile else None
-    if not args.no_profile:
-        pma.pma_profile_stages(plan, [])
+    edge_bit = 1 << pma.STAGES.index("edge")
+    times, stages = {}, None
+    for leg in legs:
+        prof = None if args.no_profile or leg != first else \
+            (lambda i: edge_bit if i % EVERY == 0 else 0)
+        torch.cuda.synchronize()
+        times[leg] = timed_steps(args.steps, leg == "cold", prof)
+        if prof is not None:
+            stages = pma.pma_profile_read(plan)
     all_stages = None
     if not args.no_profile:
-        # per-stage breakdown from a separate pass (outside the measured region)
-        pma.pma_profile(plan, True)
-        for _ in range(args.steps):
-            step()
+        # per-stage breakdown from a separate pass (outside the measured legs),
+        # under the headline leg's cache state
+        timed_steps(args.steps, first == "cold", lambda i: (1 << len(pma.STAGES)) - 1)
         all_stages = pma.pma_profile_read(plan)
-        pma.pma_profile(plan, False)
-    ms_per_step = total_ms / args.steps
-
-    # Cold-cache steps, for context: before each one, overwrite a 1 GiB buffer
-    # (four times the last-level cache) outside the timed events.
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    cold = []
-    for i in range(args.steps):
-        scratch.fill_(float(i))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+    probe = None
+    if not args.train and not args.no_profile:
+        # Calibration: the edge kernel's loads alone (same pieces, order,
+        # lanes and gather index; no arithmetic), under the same cache state:
+        # what the memory path needs for this access pattern.
         step()
-        e1.record(stream)
-        cold.append((e0, e1))
-    torch.cuda.synchronize()
-    cold_ms = sorted(a.elapsed_time(b) for a, b in cold)
+        pt = []
+        for i in range(args.steps):
+            if first == "cold":
+                scratch.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            try:
+                pma.pma_gather_probe(plan)
+            except pma.PmaError:     # head sizes of the per-channel kernel
+                break
+            e1.record(stream)
+            pt.append((e0, e1))
+        torch.cuda.synchronize()
+        if pt:
+            probe = sum(a.elapsed_time(b) for a, b in pt) / len(pt) * 1e-3
     del scratch
+    head = times[first]
+    ms_per_step = sum(head) / len(head)
     edge_heads = nnz * case.H * case.B
     value = edge_heads / (ms_per_step * 1e-3)
 
     es = 2 if case.dtype == "bf16" else 4
+    fused = case.E == 64                     # q projection and out_proj inside the edge kernel
     res = {
         "metric": METRIC, "value": value, "unit": "edge-heads/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": case.dtype, "data": "synthetic",
-        "config": {"workload": f"{case.name}: L={case.L} S={case.S} nnz={nnz} B={case.B} "
-                               f"E={case.E} H={case.H} {case.dtype}"
-                               f"{' need_weights' if case.need_weights else ''}"
-                               f"{f' key_padding_mask {args.key_padding_mask:g}' if kpm is not None else ''}"
-                               f"{' train step (forward + backward)' if args.train else ''}",
+        "config": {"workload": (f"{case.name}: L={case.L} S={case.S} nnz={nnz} B={case.B} "
+                                f"E={case.E} H={case.H} {case.dtype}"
+                                f"{' (fp32 softmax, sums and mixing weights; q, k, v, mixed stored bf16)' if case.dtype == 'bf16' else ''}"
+                                f"{' need_weights' if case.need_weights else ''}"
+                                f"{f' key_padding_mask {args.key_padding_mask:g}' if kpm is not None else ''}"
+                                f"{' train step (forward + backward)' if args.train else ''}"
+                                + ("; cold cache: each step after a 1 GiB overwrite"
+                                   if first == "cold" else "; warm cache: steps back to back")),
                    "batch": case.B, "nodes": case.L, "nnz": nnz, "embed_dim": case.E,
                    "num_heads": case.H, "parallelism": "single GPU"},
     }
-    if stages is not None:
+    for leg in legs:
+        t = sorted(times[leg])
+        res[f"{leg}_ms_per_step"] = {"mean": sum(t) / len(t), "median": t[len(t) // 2],
+                                     "min": t[0]}
+    if stages is not None and not args.train:
         edge_ms, edge_calls = stages["edge"]
         edge_avg_s = edge_ms / max(edge_calls, 1) * 1e-3
-        nbytes = edge_kernel_bytes(case.B, case.L, nnz, case.E, es, case.need_weights, case.H,
-                                   case.average)
+        nbytes = edge_kernel_bytes(case.B, case.L, info["kv_rows"], nnz, info["n_tasks"],
+                                   case.E, es, case.need_weights, case.H)
+        gbytes = edge_gather_bytes(case.B, case.L, nnz, case.E, es)
         achieved = nbytes / edge_avg_s / 1e9
-        traffic = _traffic(args.config)
-        res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                           "kernel": "edge_fast", "bytes_per_launch": nbytes,
-                           "avg_launch_us": edge_avg_s * 1e6, "timed_launches": edge_calls}
+        res["roofline"] = {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(args.config),
+            "kernel": "edge_fast" + (" (q projection and out_proj fused)" if fused else ""),
+            "bytes_per_launch": nbytes, "bytes": "compulsory: each input and output byte once",
+            "avg_launch_us": edge_avg_s * 1e6, "timed_launches": edge_calls,
+            "gather_model": {"bytes_per_launch": gbytes,
+                             "delivered_GBs": gbytes / edge_avg_s / 1e9,
+                             "note": "every edge's key and value rows per sample; mostly "
+                                     "served by L2 and the last-level cache, not an HBM rate"},
+        }
+        if probe is not None:
+            res["roofline"]["gather_probe"] = {
+                "avg_launch_us": probe * 1e6, "delivered_GBs": gbytes / probe / 1e9,
+                "edge_frac_of_probe": probe / edge_avg_s,
+                "note": "the edge kernel's loads and stores alone (pma_gather_probe): the "
+                        "memory path's time for this access pattern"}
+    if all_stages is not None:
         res["stages_us"] = {k: (v[0] / max(v[1], 1)) * 1e3 for k, v in all_stages.items() if v[1]}
-    res["cold_ms_per_step"] = {"median": cold_ms[len(cold_ms) // 2], "min": cold_ms[0]}
     res["create_ms"] = create_ms
-    res["plan"] = {k: info[k] for k in ("n_tasks", "n_split", "chunk", "max_degree")}
+    res["plan"] = {k: info[k] for k in ("n_tasks", "n_split", "chunk", "max_degree", "kv_rows")}
     pma.pma_destroy(plan)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case)

@@ -23,7 +23,7 @@ __all__ = [
     "pma_nnz", "pma_edges",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
     "pma_profile_stages",
-    "pma_profile_read", "STATUS", "STAGES", "library_path",
+    "pma_profile_read", "pma_gather_probe", "STATUS", "STAGES", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,7 @@ def _load():
         "pma_profile": (st, [P, I32]),
         "pma_profile_stages": (st, [P, ctypes.c_uint32]),
         "pma_profile_read": (st, [P, P, P]),
+        "pma_gather_probe": (st, [P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -534,6 +535,11 @@ def pma_profile_read(plan: Plan) -> dict:
     calls = np.zeros(len(STAGES), np.int64)
     _check(_load().pma_profile_read(plan.handle, ms.ctypes.data, calls.ctypes.data))
     return {name: (float(ms[i]), int(calls[i])) for i, name in enumerate(STAGES)}
+
+
+def pma_gather_probe(plan: Plan, stream=None) -> None:
+    """``pma_gather_probe``: the last forward's edge-kernel loads alone."""
+    _check(_load().pma_gather_probe(plan.handle, _stream_ptr(stream)))
 
 
 def __getattr__(name):

@@ -584,17 +584,14 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = fal
             const float pe = fast_exp2(sc[u] - base);
             l += pe;
             if constexpr (BF) {
-                // The weight meets the bf16 values as a bf16 operand of
-                // v_dot2 (products and sums stay fp32): (p, 0) against a
-                // value word picks its low channel, (0, p) its high one.
-                const uint32_t plo = pack_bf16(pe, 0.f), phi = plo << 16;
+                // The weight stays fp32: each bf16 value channel is widened
+                // exactly (the low channel shifted up, the high one masked)
+                // and multiplied in with a scalar fp32 fma.
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const bf16x2 vw = __builtin_bit_cast(bf16x2, vv[u].word(k));
-                    acc[2 * k] = __builtin_amdgcn_fdot2_f32_bf16(
-                        vw, __builtin_bit_cast(bf16x2, plo), acc[2 * k], false);
-                    acc[2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(
-                        vw, __builtin_bit_cast(bf16x2, phi), acc[2 * k + 1], false);
+                    const uint32_t w = vv[u].word(k);
+                    acc[2 * k] = fmaf(pe, __uint_as_float(w << 16), acc[2 * k]);
+                    acc[2 * k + 1] = fmaf(pe, __uint_as_float(w & 0xffff0000u), acc[2 * k + 1]);
                 }
             } else {
 #pragma unroll
@@ -846,6 +843,94 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         beg = beg2;
         end = end2;
         slot = slot2;
+    }
+}
+
+// Calibration (not part of the forward): the loads of edge_fast with no
+// arithmetic beyond folding the loaded words together with XOR. The same
+// grid, piece walk, lane layout and gather index: per piece the target's
+// query chunk, per edge the source's key and value chunks (buffer loads with
+// a uniform row offset, four edges in flight), and per piece one 16-byte
+// store where edge_fast stores a mixed chunk. Its launch time is what the
+// memory path takes for exactly edge_fast's access pattern.
+template <typename T, int CH>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7)))
+gather_probe(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
+             const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end)
+{
+    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+    constexpr int WPB = 4;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t task, pass;
+    if (a.xcd_map == 1) {
+        const uint32_t x = blockIdx.x & 7, xq = div31(x, a.pass_m, a.pass_sh);
+        pass = x - xq * a.passes;
+        task = ((blockIdx.x >> 3) * a.xcd_per + xq) * WPB + wave;
+    } else if (a.xcd_map == 2) {
+        const uint32_t w = blockIdx.x * WPB + wave;
+        pass = div31(w, a.ts_m, a.ts_sh);
+        task = w - pass * a.tstride;
+    } else {
+        const uint32_t w = blockIdx.x * WPB + wave;
+        task = div31(w, a.pass_m, a.pass_sh);
+        pass = w - task * a.passes;
+    }
+    if (task >= (uint32_t)a.n_tasks)
+        return;
+    const int cpr = a.E / CH;
+    const uint32_t c = pass * 64 + lane;
+    const bool active = c < (uint32_t)(a.B * cpr);
+    const int b = active ? (int)div31(c, a.cpr_m, a.cpr_sh) : 0;
+    const int col = active ? ((int)c - b * cpr) * CH : 0;
+    const uint32_t row2 = (uint32_t)a.lay.kv_s * (uint32_t)sizeof(T);
+    const uint32_t loff = ((uint32_t)b * (uint32_t)a.lay.kv_b + col) * (uint32_t)sizeof(T);
+    const uint32_t vloff = loff + (uint32_t)a.lay.kv_v * (uint32_t)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(a.kv), (short)0, (int)(uint32_t)a.kv_bytes, 0x00020000);
+    const T *qt = reinterpret_cast<const T *>(a.qt);
+    T *mixed = reinterpret_cast<T *>(a.mixed);
+    for (;;) {
+        const int t = task_target[task], beg = task_begin[task], end = task_end[task];
+        const uint4 *qp = reinterpret_cast<const uint4 *>(
+            qt + ((uint32_t)t * (uint32_t)a.lay.q_t + (uint32_t)b * (uint32_t)a.lay.q_b + col));
+        uint4 acc = a.nt ? load_nt(qp) : *qp;
+        int p = beg;
+        for (; p + 4 <= end; p += 4) {
+            u32x4 kw[4], vw[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t so = (uint32_t)csr_src[p + u] * row2;
+                kw[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, so, 0);
+                vw[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vloff, so, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc.x ^= kw[u].x ^ vw[u].x;
+                acc.y ^= kw[u].y ^ vw[u].y;
+                acc.z ^= kw[u].z ^ vw[u].z;
+                acc.w ^= kw[u].w ^ vw[u].w;
+            }
+        }
+        for (; p < end; ++p) {
+            const uint32_t so = (uint32_t)csr_src[p] * row2;
+            const u32x4 kw = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, so, 0);
+            const u32x4 vw = __builtin_amdgcn_raw_buffer_load_b128(rsrc, vloff, so, 0);
+            acc.x ^= kw.x ^ vw.x;
+            acc.y ^= kw.y ^ vw.y;
+            acc.z ^= kw.z ^ vw.z;
+            acc.w ^= kw.w ^ vw.w;
+        }
+        if (active) {
+            void *dst = mixed + ((uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col);
+            if (a.nt)
+                store_nt(dst, acc);
+            else
+                *reinterpret_cast<uint4 *>(dst) = acc;
+        }
+        task += a.tstride;
+        if (task >= (uint32_t)a.n_tasks)
+            break;
     }
 }
 
@@ -1250,24 +1335,12 @@ int cu_count()
     return cached[dev];
 }
 
-template <typename T, int CH, int LPH, int E_FUSE, bool QF>
-hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
+// Workgroup count of an edge_fast launch of wpb wavefronts per workgroup and
+// at most cap workgroups, and the walk it implies: sets k.xcd_map (the
+// order actually used), xcd_per, tstride and its divisor. (The gather probe
+// takes the same grid, so that it walks the pieces in the same order.)
+int64_t edge_grid(EdgeK &k, int wpb, int64_t cap)
 {
-    set_passes(k, CH);
-    if (k.n_tasks * k.passes >= ((int64_t)1 << 31))
-        return hipErrorInvalidConfiguration;
-    // Workgroups of 4 wavefronts. With persist > 0 at most persist
-    // workgroups per CU are launched and each wavefront walks several
-    // pieces; otherwise one wavefront per (piece, sample group).
-    const bool w32 = offsets32(k, sizeof(T));
-    // Hot-row cache: one resident 16-wavefront workgroup per CU, XCD-pinned
-    // sample groups (each workgroup serves one group).
-    constexpr int kHot = kHotRows;
-    const bool hot = QF && k.n_hot > 0 && k.n_hot <= kHot && k.xcd_map == 1 &&
-                     8 % k.passes == 0 && w32 && !k.scores && !k.kpm_bits;
-    const int wpb = hot ? 16 : 4;
-    const int64_t cap = hot ? (int64_t)cu_count()
-                            : persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
     int64_t blocks;
     if (k.xcd_map == 1 && 8 % k.passes == 0) {
         const int64_t per = 8 / k.passes;   // workgroups per pass per round of 8
@@ -1287,7 +1360,28 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
         k.tstride = (uint32_t)(blocks * 4 / k.passes);
         magic31(k.tstride, k.ts_m, k.ts_sh);
     }
-    const unsigned nb = (unsigned)blocks;
+    return blocks;
+}
+
+template <typename T, int CH, int LPH, int E_FUSE, bool QF>
+hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
+{
+    set_passes(k, CH);
+    if (k.n_tasks * k.passes >= ((int64_t)1 << 31))
+        return hipErrorInvalidConfiguration;
+    // Workgroups of 4 wavefronts. With persist > 0 at most persist
+    // workgroups per CU are launched and each wavefront walks several
+    // pieces; otherwise one wavefront per (piece, sample group).
+    const bool w32 = offsets32(k, sizeof(T));
+    // Hot-row cache: one resident 16-wavefront workgroup per CU, XCD-pinned
+    // sample groups (each workgroup serves one group).
+    constexpr int kHot = kHotRows;
+    const bool hot = QF && k.n_hot > 0 && k.n_hot <= kHot && k.xcd_map == 1 &&
+                     8 % k.passes == 0 && w32 && !k.scores && !k.kpm_bits;
+    const int wpb = hot ? 16 : 4;
+    const int64_t cap = hot ? (int64_t)cu_count()
+                            : persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
+    const unsigned nb = (unsigned)edge_grid(k, wpb, cap);
     if constexpr (QF) {
         if (hot) {
             edge_fast<T, CH, LPH, 4, E_FUSE, QF, true, false, 0, kHot><<<nb, 1024, 0, s>>>(
@@ -1531,6 +1625,28 @@ pma_status launch_edge(const EdgeArgs &x, hipStream_t s)
     hipError_t e = x.dt == PMA_BF16 ? dispatch_edge<uint16_t>(k, x.persist, s)
                                     : dispatch_edge<float>(k, x.persist, s);
     return e == hipSuccess ? PMA_OK : PMA_E_DEVICE;
+}
+
+pma_status launch_gather_probe(const EdgeArgs &x, hipStream_t s)
+{
+    EdgeK k = make_k(x);
+    const size_t es = x.dt == PMA_BF16 ? 2 : 4;
+    const int ch = (int)(16 / es);
+    const int64_t lph = k.d % ch == 0 ? k.d / ch : 0;
+    if (lph < 1 || lph > 16 || (lph & (lph - 1)) != 0)
+        return PMA_E_UNSUPPORTED;   // head sizes of the per-channel kernel
+    set_passes(k, ch);
+    if (k.n_tasks * k.passes >= ((int64_t)1 << 31) || !offsets32(k, es))
+        return PMA_E_UNSUPPORTED;
+    const int64_t cap = x.persist > 0 ? (int64_t)cu_count() * x.persist : ((int64_t)1 << 40);
+    const unsigned nb = (unsigned)edge_grid(k, 4, cap);
+    if (x.dt == PMA_BF16)
+        gather_probe<uint16_t, 8><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin,
+                                                     k.task_end);
+    else
+        gather_probe<float, 4><<<nb, 256, 0, s>>>(k, k.csr_src, k.task_target, k.task_begin,
+                                                  k.task_end);
+    return hipGetLastError() == hipSuccess ? PMA_OK : PMA_E_DEVICE;
 }
 
 pma_status launch_merge(const EdgeArgs &x, hipStream_t s)

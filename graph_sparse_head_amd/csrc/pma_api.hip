@@ -74,6 +74,10 @@ struct pma_plan {
     size_t bw_bytes = 0;
     char *lin = nullptr;
     size_t lin_bytes = 0;
+    // the edge-kernel arguments of the last inference forward (for
+    // pma_gather_probe); probe_ok is cleared when the workspace is reallocated
+    pma::EdgeArgs probe_ea;
+    bool probe_ok = false;
     // profiling
     unsigned prof = 0;   // stages timed: bit s for stage s
     std::vector<EventPair> pending;
@@ -97,6 +101,7 @@ void free_workspace(pma_plan *p)
     p->kpm_csr = nullptr;
     p->ws_B = 0;
     p->ws_weights = false;
+    p->probe_ok = false;
 }
 
 // Buffers for a batch of B: q, keys/values, mixed, the split partials and
@@ -752,6 +757,10 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     tm.begin(PMA_STAGE_EDGE);
     st = pma::launch_edge(ea, stream);
     tm.end();
+    if (!save) {
+        p->probe_ea = ea;
+        p->probe_ok = true;
+    }
     if (st == PMA_OK && p->g.n_split > 0) {
         tm.begin(PMA_STAGE_MERGE);
         st = pma::launch_merge(ea, stream);
@@ -809,6 +818,21 @@ PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void 
     return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                         out, weights, average_attn_weights, key_padding_mask, mask_per_sample,
                         nullptr, stream);
+}
+
+PMA_API pma_status pma_gather_probe(pma_plan *plan, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!plan)
+        return fail(PMA_E_NULL, "plan is NULL");
+    if (!plan->probe_ok)
+        return fail(PMA_E_ARG, "no inference forward on this plan's current workspace");
+    const pma_status st = pma::launch_gather_probe(plan->probe_ea, stream);
+    if (st == PMA_E_UNSUPPORTED)
+        return fail(st, "the probe serves the 16-byte edge kernel with tensors under 2 GiB");
+    if (st != PMA_OK)
+        return fail(st, "probe launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PMA_OK;
 }
 
 PMA_API size_t pma_train_bytes(const pma_plan *plan, int64_t batch)

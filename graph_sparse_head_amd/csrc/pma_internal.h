@@ -279,6 +279,10 @@ bool mask_supported(const EdgeArgs &x);
 pma_status launch_edge(const EdgeArgs &a, hipStream_t s);
 
 pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
+// The edge kernel's loads alone (calibration; see gather_probe in edge.hip).
+// PMA_E_UNSUPPORTED where the 16-byte kernel does not serve the head size or
+// a tensor is 2 GiB or more.
+pma_status launch_gather_probe(const EdgeArgs &a, hipStream_t s);
 pma_status launch_weights(const EdgeArgs &a, hipStream_t s);
 
 }  // namespace pma

@@ -361,6 +361,21 @@ pma_status pma_profile_stages(pma_plan *plan, unsigned mask);
    since the last read, and reset the sums. */
 pma_status pma_profile_read(pma_plan *plan, double *ms, int64_t *calls);
 
+/*
+ * pma_gather_probe -- calibration, not part of the method. Enqueues one launch
+ * that performs the loads of the edge kernel of this plan's last pma_forward
+ * or pma_forward_masked: the same pieces in the same order, lane layout and
+ * gather index, the plan's key/value workspace and that forward's query
+ * tokens (which must still be valid), with no arithmetic beyond folding the
+ * loaded words together, and one 16-byte store per (piece, sample, chunk)
+ * into the plan's workspace. Its duration is what the memory path needs for
+ * the edge kernel's access pattern (masks and weights left out). Errors:
+ * PMA_E_NULL, PMA_E_ARG (no inference forward since the plan's workspace was
+ * last allocated), PMA_E_UNSUPPORTED (head sizes the 16-byte kernel does not
+ * serve; a tensor of 2 GiB or more), PMA_E_DEVICE.
+ */
+pma_status pma_gather_probe(pma_plan *plan, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
