@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "PmaError", "Plan", "pma_create", "pma_forward", "pma_forward_masked", "pma_destroy",
+    "PmaError", "Plan", "pma_create", "pma_forward", "pma_forward_masked", "pma_forward_static",
+    "pma_destroy",
     "pma_train_bytes", "pma_forward_train", "pma_backward",
     "pma_create_graph", "pma_linear_forward", "pma_linear_backward",
     "pma_nnz", "pma_edges",
@@ -77,6 +78,7 @@ def _load():
         "pma_forward": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P]),
         "pma_forward_masked": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, I32,
                                     P]),
+        "pma_forward_static": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P]),
         "pma_train_bytes": (ctypes.c_size_t, [P, I64]),
         "pma_forward_train": (st, [P, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, I32, P, I32, P,
                                    P]),
@@ -208,9 +210,23 @@ def _weights_shape(plan: "Plan", lead, average: bool):
     return tuple(lead) + ((nnz,) if average else (nnz, plan.H))
 
 
+def pma_forward_static(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                       out=None, weights=None, need_weights: bool = False,
+                       average_attn_weights: bool = True, stream=None):
+    """``pma_forward_static``: pma_forward without any device allocation in the
+    library (its workspace is the library's fixed static scratch; see
+    include/pma.h). ``out`` / ``weights`` are allocated here by torch when not
+    given, before the call."""
+    return pma_forward(plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b, out=out,
+                       weights=weights, need_weights=need_weights,
+                       average_attn_weights=average_attn_weights, stream=stream,
+                       _static=True)
+
+
 def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                 out=None, weights=None, need_weights: bool = False,
-                average_attn_weights: bool = True, stream=None, key_padding_mask=None):
+                average_attn_weights: bool = True, stream=None, key_padding_mask=None,
+                _static: bool = False):
     """One forward pass (see ``pma_forward`` / ``pma_forward_masked`` in
     include/pma.h).
 
@@ -253,7 +269,13 @@ def pma_forward(plan: Plan, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w
     if want_w:
         _full_shape(weights, "weights", wshape)
     wp = _dptr(weights, "weights", torch.float32) if want_w else None
-    if key_padding_mask is None:
+    if _static:
+        if key_padding_mask is not None:
+            raise PmaError(8, "pma_forward_static takes no key_padding_mask")
+        st = lib.pma_forward_static(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1],
+                                    wps[2], bps[2], wps[3], bps[3], op, wp,
+                                    int(bool(average_attn_weights)), _stream_ptr(stream))
+    elif key_padding_mask is None:
         st = lib.pma_forward(plan.handle, B, qp, kp, vp, wps[0], bps[0], wps[1], bps[1], wps[2],
                              bps[2], wps[3], bps[3], op, wp, int(bool(average_attn_weights)),
                              _stream_ptr(stream))

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <vector>
@@ -37,6 +38,18 @@ struct EventPair {
     hipEvent_t a, b;
     int stage;
 };
+
+// Workspace of pma_forward_static: one file-scope device array of fixed size.
+// Each GPU the library runs on holds its own copy (at its own address) from
+// the module's load until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device may reach a kernel.
+static_assert(PMA_STATIC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __attribute__((aligned(256))) char scratch[PMA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of `scratch`, per device ordinal
 
 }  // namespace
 
@@ -165,10 +178,11 @@ hipEvent_t take_event(pma_plan *p)
 struct StageTimer {
     pma_plan *p;
     hipStream_t s;
+    bool off = false;   // no events at all (the allocation-free forward)
     EventPair cur{nullptr, nullptr, -1};
     void begin(int stage)
     {
-        if (!((p->prof >> stage) & 1u))
+        if (off || !((p->prof >> stage) & 1u))
             return;
         cur.a = take_event(p);
         cur.b = take_event(p);
@@ -178,7 +192,7 @@ struct StageTimer {
     }
     void end()
     {
-        if (!p->prof || cur.stage < 0)
+        if (off || !p->prof || cur.stage < 0)
             return;
         if (cur.a && cur.b) {
             (void)hipEventRecord(cur.b, s);
@@ -573,11 +587,84 @@ SaveLayout save_layout(const pma_plan *p, int64_t B)
     return s;
 }
 
+// The workspace pointers one forward uses (see ensure_workspace).
+struct Ws {
+    void *qt, *kv, *mixed;
+    float *part_acc, *part_ml, *stat_ml, *scores;
+};
+
+// Device address of the static scratch on the current device, looked up once
+// per device (with that device current) and kept.
+pma_status static_scratch(char **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(PMA_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PMA_E_UNSUPPORTED, "device ordinal %d beyond the static scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !a)
+            return fail(PMA_E_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch[dev] = a;
+    }
+    *ptr = static_cast<char *>(g_scratch[dev]);
+    return PMA_OK;
+}
+
+// The allocation-free forward's workspace, carved from the static scratch in
+// 256-byte aligned pieces: q (unless projected inside the edge kernel), the
+// S_ws key/value rows, mixed (unless out_proj is fused), the partial results
+// of split targets and, with need_weights, the softmax statistics and scores.
+// Every piece is written before it is read within the forward, so nothing is
+// cleared. Fails with PMA_E_SIZE, before any launch, beyond the scratch size.
+pma_status carve_static(const pma_plan *p, int64_t B, int64_t S_ws, bool need_q, bool need_mixed,
+                        bool weights, Ws *w)
+{
+    const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
+    const size_t slots = (size_t)(p->g.n_slots > 0 ? p->g.n_slots : 1);
+    const size_t rows = (size_t)p->L * B * p->E * es;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    const size_t o_q = need_q ? take(rows) : 0;
+    const size_t o_kv = take((size_t)S_ws * 2 * B * p->E * es);
+    const size_t o_mixed = need_mixed ? take(rows) : 0;
+    const size_t o_pacc = take(slots * B * p->E * 4);
+    const size_t o_pml = take(slots * B * p->H * 2 * 4);
+    const size_t o_stat = weights ? take((size_t)p->L * B * p->H * 2 * 4) : 0;
+    const size_t o_sc = weights ? take((size_t)p->nnz * B * p->H * 4) : 0;
+    if (off > PMA_STATIC_SCRATCH_BYTES)
+        return fail(PMA_E_SIZE,
+                    "this forward needs %zu bytes of workspace; the allocation-free forward's "
+                    "static scratch holds %zu",
+                    off, (size_t)PMA_STATIC_SCRATCH_BYTES);
+    char *base = nullptr;
+    const pma_status st = static_scratch(&base);
+    if (st != PMA_OK)
+        return st;
+    w->qt = need_q ? base + o_q : nullptr;
+    w->kv = base + o_kv;
+    w->mixed = need_mixed ? base + o_mixed : nullptr;
+    w->part_acc = reinterpret_cast<float *>(base + o_pacc);
+    w->part_ml = reinterpret_cast<float *>(base + o_pml);
+    w->stat_ml = weights ? reinterpret_cast<float *>(base + o_stat) : nullptr;
+    w->scores = weights ? reinterpret_cast<float *>(base + o_sc) : nullptr;
+    return PMA_OK;
+}
+
 pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const void *key,
                         const void *value, const void *q_w, const void *q_b, const void *k_w,
                         const void *k_b, const void *v_w, const void *v_b, const void *o_w,
                         const void *o_b, void *out, float *weights, int average_attn_weights,
-                        const uint8_t *kpm, int kpm_per_sample, char *save, hipStream_t stream)
+                        const uint8_t *kpm, int kpm_per_sample, char *save, bool no_alloc,
+                        hipStream_t stream)
 {
     g_err[0] = 0;
     if (!plan)
@@ -597,17 +684,12 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     const int64_t B = batch, L = p->L, S = p->S, E = p->E;
     if ((L > S ? L : S) * B * 2 * E > ((int64_t)1 << 40))
         return fail(PMA_E_UNSUPPORTED, "batch too large for one forward");
-    pma_status st = ensure_workspace(p, B, weights != nullptr, stream);
-    if (st != PMA_OK)
-        return st;
+    if (no_alloc && (kpm || save))
+        return fail(PMA_E_ARG, "the allocation-free forward takes no mask and no save area");
+    pma_status st = PMA_OK;
     StageTimer tm{p, stream};
+    tm.off = no_alloc;
     const size_t es = p->dtype == PMA_BF16 ? 2 : 4;
-    // With a save area (training) q, k, v, mixed and the softmax statistics
-    // go there, batch-first, for pma_backward; otherwise to the workspace.
-    const SaveLayout sv = save_layout(p, B);
-    void *qt = save ? (void *)(save + sv.q) : p->qt;
-    char *kvc = save ? save + sv.k : static_cast<char *>(p->kv);
-    void *mixed_ws = save ? (void *)(save + sv.mixed) : p->mixed;
     // Keys and values are needed only for the sources some edge reads
     // (n_kv of S). Projecting just those rows saves work unless query, key
     // and value are one tensor and most sources are read: then one pass over
@@ -630,6 +712,24 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
                           (((uintptr_t)o_w | (uintptr_t)out) & 15) == 0;
     const bool fuse_in = fuse_out && p->fuse_in && pma::q_fusable(E, p->H, p->dtype) &&
                          (((uintptr_t)q_w | (uintptr_t)query) & 15) == 0;
+
+    // Workspace: the plan's (grown on demand), or for the allocation-free
+    // forward carved from the static scratch array, only what this call uses.
+    Ws w;
+    if (no_alloc) {
+        st = carve_static(p, B, S_ws, !fuse_in, !fuse_out, weights != nullptr, &w);
+    } else {
+        st = ensure_workspace(p, B, weights != nullptr, stream);
+        w = {p->qt, p->kv, p->mixed, p->part_acc, p->part_ml, p->stat_ml, p->scores};
+    }
+    if (st != PMA_OK)
+        return st;
+    // With a save area (training) q, k, v, mixed and the softmax statistics
+    // go there, batch-first, for pma_backward; otherwise to the workspace.
+    const SaveLayout sv = save_layout(p, B);
+    void *qt = save ? (void *)(save + sv.q) : w.qt;
+    char *kvc = save ? save + sv.k : static_cast<char *>(w.kv);
+    void *mixed_ws = save ? (void *)(save + sv.mixed) : w.mixed;
 
     // Step 1: q, k, v projections into the workspace layout. Caller tokens are
     // batch-first and read in storage order (key/value rows through the list
@@ -689,10 +789,10 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.kv = kvc;
     ea.kv_bytes = (uint64_t)S_ws * 2 * B * E * es;
     ea.mixed = mixed_ws;
-    ea.part_acc = p->part_acc;
-    ea.part_ml = p->part_ml;
-    ea.stat_ml = save ? reinterpret_cast<float *>(save + sv.ml) : (weights ? p->stat_ml : nullptr);
-    ea.scores = weights ? p->scores : nullptr;
+    ea.part_acc = w.part_acc;
+    ea.part_ml = w.part_ml;
+    ea.stat_ml = save ? reinterpret_cast<float *>(save + sv.ml) : (weights ? w.stat_ml : nullptr);
+    ea.scores = weights ? w.scores : nullptr;
     ea.weights = weights;
     ea.average = average_attn_weights;
     if (kpm) {
@@ -741,7 +841,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     // resident 16-wavefront workgroup per CU that the 128 KB cache needs runs
     // 4 wavefronts per SIMD instead of 7 and gives up the balancing of queued
     // workgroups, which costs more than the key/value reads it saves.
-    if (fuse_in && p->hot && !kpm && !weights && ea.xcd_map == 1) {
+    if (fuse_in && p->hot && !kpm && !weights && ea.xcd_map == 1 && !no_alloc) {
         st = build_hot(p, ea.gather_src, S_ws, stream);
         if (st != PMA_OK)
             return fail(st, "hot-row index build failed");
@@ -757,7 +857,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     tm.begin(PMA_STAGE_EDGE);
     st = pma::launch_edge(ea, stream);
     tm.end();
-    if (!save) {
+    if (!save && !no_alloc) {
         p->probe_ea = ea;
         p->probe_ok = true;
     }
@@ -799,7 +899,18 @@ PMA_API pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query,
                                float *weights, int average_attn_weights, hipStream_t stream)
 {
     return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
-                        out, weights, average_attn_weights, nullptr, 0, nullptr, stream);
+                        out, weights, average_attn_weights, nullptr, 0, nullptr, false, stream);
+}
+
+PMA_API pma_status pma_forward_static(pma_plan *plan, int64_t batch, const void *query,
+                                      const void *key, const void *value, const void *q_w,
+                                      const void *q_b, const void *k_w, const void *k_b,
+                                      const void *v_w, const void *v_b, const void *o_w,
+                                      const void *o_b, void *out, float *weights,
+                                      int average_attn_weights, hipStream_t stream)
+{
+    return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
+                        out, weights, average_attn_weights, nullptr, 0, nullptr, true, stream);
 }
 
 PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void *query,
@@ -817,7 +928,7 @@ PMA_API pma_status pma_forward_masked(pma_plan *plan, int64_t batch, const void 
         return fail(PMA_E_ARG, "mask_per_sample must be 0 or 1");
     return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                         out, weights, average_attn_weights, key_padding_mask, mask_per_sample,
-                        nullptr, stream);
+                        nullptr, false, stream);
 }
 
 PMA_API pma_status pma_gather_probe(pma_plan *plan, hipStream_t stream)
@@ -857,7 +968,8 @@ PMA_API pma_status pma_forward_train(pma_plan *plan, int64_t batch, const void *
         return fail(PMA_E_ARG, "mask_per_sample must be 0 or 1");
     return forward_impl(plan, batch, query, key, value, q_w, q_b, k_w, k_b, v_w, v_b, o_w, o_b,
                         out, weights, average_attn_weights, key_padding_mask,
-                        key_padding_mask ? mask_per_sample : 0, static_cast<char *>(save), stream);
+                        key_padding_mask ? mask_per_sample : 0, static_cast<char *>(save), false,
+                        stream);
 }
 
 PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query,

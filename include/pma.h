@@ -146,6 +146,36 @@ pma_status pma_forward(pma_plan *plan, int64_t batch, const void *query, const v
                        hipStream_t stream);
 
 /*
+ * pma_forward_static -- pma_forward that allocates nothing, for callers that
+ * cannot allocate device memory during the call: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and errors as pma_forward, plus PMA_E_SIZE (below).
+ *
+ * Its workspace (the projected keys and values; q and the mixed rows where
+ * they are not fused away; the partial results of split targets; with
+ * weights the scores and softmax statistics) is carved from one file-scope
+ * device array of PMA_STATIC_SCRATCH_BYTES, which each GPU the library runs
+ * on holds from the library's first use on it until the process ends. The
+ * plan's own workspace is neither used nor grown, and no stage timing is
+ * recorded. A forward that would need more than the array fails with
+ * PMA_E_SIZE before any launch (the 20,000-node gene workload at batch 32,
+ * embed_dim 64, bf16 needs about 67 MB; the bipartite and 100k-node
+ * workloads need more and are refused).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (on other streams, from other
+ * threads, with other plans) race with each other, so the caller must order
+ * them (e.g. one stream).
+ */
+#define PMA_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
+
+pma_status pma_forward_static(pma_plan *plan, int64_t batch, const void *query, const void *key,
+                              const void *value, const void *q_w, const void *q_b,
+                              const void *k_w, const void *k_b, const void *v_w, const void *v_b,
+                              const void *o_w, const void *o_b, void *out, float *weights,
+                              int average_attn_weights, hipStream_t stream);
+
+/*
  * pma_forward_masked -- pma_forward with a key_padding_mask (kpnn2 page,
  * forward parameter table, key_padding_mask; "Notes" step 3 and the
  * paragraph on queries with no live keys).
