@@ -21,7 +21,7 @@ __all__ = [
     "pma_destroy",
     "pma_train_bytes", "pma_forward_train", "pma_backward",
     "pma_create_graph", "pma_linear_forward", "pma_linear_backward",
-    "pma_nnz", "pma_edges",
+    "pma_nnz", "pma_edges", "pma_edge_list",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
     "pma_profile_stages",
     "pma_profile_read", "pma_gather_probe", "STATUS", "STAGES", "library_path",
@@ -98,6 +98,7 @@ def _load():
         "pma_profile_stages": (st, [P, ctypes.c_uint32]),
         "pma_profile_read": (st, [P, P, P]),
         "pma_gather_probe": (st, [P, P]),
+        "pma_edge_list": (st, [P, P, I64, I64, I64, I32, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -493,6 +494,29 @@ def pma_destroy(plan: Plan) -> None:
         return
     _check(_load().pma_destroy(plan.handle))
     plan.handle = ctypes.c_void_p()
+
+
+def pma_edge_list(source_index, target_index, query_features: int, key_features: int,
+                  add_self_loops: bool = False):
+    """``pma_edge_list``: the validated final edge list (given pairs, then the
+    missing self loops), computed on the host by the library's index rules.
+    Returns (src, tgt) int64 arrays."""
+    lib = _load()
+    src = _host_i64(source_index, "source_index")
+    tgt = _host_i64(target_index, "target_index")
+    if src.shape[0] != tgt.shape[0]:
+        raise PmaError(8, "source_index and target_index differ in length")
+    if not isinstance(add_self_loops, (bool, np.bool_)):
+        raise PmaError(8, "add_self_loops must be a bool")
+    cap = src.shape[0] + (max(int(query_features), 0) if add_self_loops else 0)
+    so = np.empty(max(cap, 1), np.int64)
+    to = np.empty(max(cap, 1), np.int64)
+    n = ctypes.c_int64(0)
+    _check(lib.pma_edge_list(src.ctypes.data if src.size else None,
+                             tgt.ctypes.data if tgt.size else None, src.shape[0],
+                             int(query_features), int(key_features), int(bool(add_self_loops)),
+                             cap, so.ctypes.data, to.ctypes.data, ctypes.byref(n)))
+    return so[:n.value].copy(), to[:n.value].copy()
 
 
 def pma_nnz(plan: Plan) -> int:

@@ -276,6 +276,53 @@ pma_status build_hot(pma_plan *p, const int32_t *idx, int64_t rows, hipStream_t 
     return PMA_OK;
 }
 
+// The constructor's index rules on the host (kpnn2 page, constructor
+// parameter table and "Raises"): nnz >= 1, indices present and in range,
+// add_self_loops only with L == S; then the edge order: the given pairs, and
+// with add_self_loops every missing (i, i) after them in ascending i. Sizes
+// are checked by the caller. Repeated pairs are left to the caller
+// (pma_create finds them on the device after sorting; pma_edge_list on the
+// host).
+pma_status host_edges(const int64_t *source_index, const int64_t *target_index, int64_t nnz,
+                      int64_t L, int64_t S, int add_self_loops, std::vector<int64_t> &src,
+                      std::vector<int64_t> &tgt)
+{
+    if (nnz < 1)
+        return fail(PMA_E_INDEX_EMPTY, "the indices are empty (nnz = %lld)", (long long)nnz);
+    if (!source_index || !target_index)
+        return fail(PMA_E_NULL, "source_index or target_index is NULL");
+    if (add_self_loops && L != S)
+        return fail(PMA_E_SELF_LOOPS,
+                    "add_self_loops needs query_features == key_features (%lld != %lld)",
+                    (long long)L, (long long)S);
+    for (int64_t i = 0; i < nnz; ++i) {
+        if (source_index[i] < 0 || source_index[i] >= S)
+            return fail(PMA_E_INDEX_RANGE, "source_index[%lld] = %lld outside [0, %lld)",
+                        (long long)i, (long long)source_index[i], (long long)S);
+        if (target_index[i] < 0 || target_index[i] >= L)
+            return fail(PMA_E_INDEX_RANGE, "target_index[%lld] = %lld outside [0, %lld)",
+                        (long long)i, (long long)target_index[i], (long long)L);
+    }
+    try {
+        src.assign(source_index, source_index + nnz);
+        tgt.assign(target_index, target_index + nnz);
+        if (add_self_loops) {
+            std::vector<char> has(L, 0);
+            for (int64_t i = 0; i < nnz; ++i)
+                if (source_index[i] == target_index[i])
+                    has[source_index[i]] = 1;
+            for (int64_t i = 0; i < L; ++i)
+                if (!has[i]) {
+                    src.push_back(i);
+                    tgt.push_back(i);
+                }
+        }
+    } catch (...) {
+        return fail(PMA_E_OOM, "host allocation failed");
+    }
+    return PMA_OK;
+}
+
 pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64_t *target_index,
                        int64_t nnz, int64_t query_features, int64_t key_features,
                        int64_t embed_dim, int64_t num_heads, int add_self_loops, pma_dtype dtype,
@@ -296,45 +343,20 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     if (attn && E % H != 0)
         return fail(PMA_E_SIZE, "embed_dim %lld is not divisible by num_heads %lld",
                     (long long)E, (long long)H);
-    if (nnz < 1)
-        return fail(PMA_E_INDEX_EMPTY, "the indices are empty (nnz = %lld)", (long long)nnz);
-    if (!source_index || !target_index)
-        return fail(PMA_E_NULL, "source_index or target_index is NULL");
-    if (add_self_loops && L != S)
-        return fail(PMA_E_SELF_LOOPS,
-                    "add_self_loops needs query_features == key_features (%lld != %lld)",
-                    (long long)L, (long long)S);
-    for (int64_t i = 0; i < nnz; ++i) {
-        if (source_index[i] < 0 || source_index[i] >= S)
-            return fail(PMA_E_INDEX_RANGE, "source_index[%lld] = %lld outside [0, %lld)",
-                        (long long)i, (long long)source_index[i], (long long)S);
-        if (target_index[i] < 0 || target_index[i] >= L)
-            return fail(PMA_E_INDEX_RANGE, "target_index[%lld] = %lld outside [0, %lld)",
-                        (long long)i, (long long)target_index[i], (long long)L);
-    }
     if (L > kI32 || S > kI32 || nnz > kI32)
         return fail(PMA_E_UNSUPPORTED, "more than 2^31 - 1 edges or tokens");
 
     pma_plan *p = new (std::nothrow) pma_plan;
     if (!p)
         return fail(PMA_E_OOM, "host allocation failed");
-    try {
-        p->h_src.assign(source_index, source_index + nnz);
-        p->h_tgt.assign(target_index, target_index + nnz);
-        if (add_self_loops) {
-            std::vector<char> has(L, 0);
-            for (int64_t i = 0; i < nnz; ++i)
-                if (source_index[i] == target_index[i])
-                    has[source_index[i]] = 1;
-            for (int64_t i = 0; i < L; ++i)
-                if (!has[i]) {
-                    p->h_src.push_back(i);
-                    p->h_tgt.push_back(i);
-                }
+    {
+        // (repeated pairs are found on the device after the sort, below)
+        const pma_status st = host_edges(source_index, target_index, nnz, L, S, add_self_loops,
+                                         p->h_src, p->h_tgt);
+        if (st != PMA_OK) {
+            delete p;
+            return st;
         }
-    } catch (...) {
-        delete p;
-        return fail(PMA_E_OOM, "host allocation failed");
     }
     p->L = L;
     p->S = S;
@@ -477,6 +499,56 @@ PMA_API pma_status pma_destroy(pma_plan *plan)
     for (hipEvent_t ev : plan->pool)
         (void)hipEventDestroy(ev);
     delete plan;
+    return PMA_OK;
+}
+
+PMA_API pma_status pma_edge_list(const int64_t *source_index, const int64_t *target_index,
+                                 int64_t nnz, int64_t query_features, int64_t key_features,
+                                 int add_self_loops, int64_t capacity, int64_t *src_out,
+                                 int64_t *tgt_out, int64_t *nnz_out)
+{
+    g_err[0] = 0;
+    if (!nnz_out)
+        return fail(PMA_E_NULL, "nnz_out is NULL");
+    *nnz_out = 0;
+    if (add_self_loops != 0 && add_self_loops != 1)
+        return fail(PMA_E_ARG, "add_self_loops must be 0 or 1");
+    const int64_t L = query_features, S = key_features;
+    if (L <= 0 || S <= 0)
+        return fail(PMA_E_SIZE, "sizes must be positive (L=%lld S=%lld)", (long long)L,
+                    (long long)S);
+    if (L > kI32 || S > kI32 || nnz > kI32)
+        return fail(PMA_E_UNSUPPORTED, "more than 2^31 - 1 edges or tokens");
+    std::vector<int64_t> src, tgt;
+    pma_status st = host_edges(source_index, target_index, nnz, L, S, add_self_loops, src, tgt);
+    if (st != PMA_OK)
+        return st;
+    // repeated pairs: sort (target, source) keys, compare neighbours; the
+    // appended loops are never repeats (only missing ones are appended)
+    {
+        std::vector<int64_t> key;
+        try {
+            key.resize(nnz);
+        } catch (...) {
+            return fail(PMA_E_OOM, "host allocation failed");
+        }
+        for (int64_t i = 0; i < nnz; ++i)
+            key[i] = target_index[i] * S + source_index[i];
+        std::sort(key.begin(), key.end());
+        for (int64_t i = 1; i < nnz; ++i)
+            if (key[i] == key[i - 1])
+                return fail(PMA_E_INDEX_DUPLICATE, "the pair (source %lld, target %lld) repeats",
+                            (long long)(key[i] % S), (long long)(key[i] / S));
+    }
+    const int64_t n = (int64_t)src.size();
+    *nnz_out = n;
+    if (capacity < n)
+        return fail(PMA_E_SIZE, "the edge list has %lld entries, capacity is %lld", (long long)n,
+                    (long long)capacity);
+    if (!src_out || !tgt_out)
+        return fail(PMA_E_NULL, "src_out or tgt_out is NULL");
+    memcpy(src_out, src.data(), n * sizeof(int64_t));
+    memcpy(tgt_out, tgt.data(), n * sizeof(int64_t));
     return PMA_OK;
 }
 

@@ -23,8 +23,9 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-from . import (pma_backward, pma_create, pma_create_graph, pma_destroy, pma_edges, pma_forward,
-               pma_forward_train, pma_linear_backward, pma_linear_forward)
+from . import (PmaError, pma_backward, pma_create, pma_create_graph, pma_destroy, pma_edge_list,
+               pma_edges, pma_forward, pma_forward_train, pma_linear_backward,
+               pma_linear_forward)
 
 __all__ = ["PackedMultiheadAttention", "PackedLinear", "ModuleArgError"]
 
@@ -71,30 +72,16 @@ def _bool(x, name: str) -> bool:
 
 def _edges(source_index, target_index, L: int, S: int, add_self_loops: bool):
     """Validated edge arrays in the layer's edge order: the given pairs, then
-    the missing (i, i) in ascending i when add_self_loops (kpnn2 page,
-    constructor parameter table and "Raises")."""
+    the missing (i, i) in ascending i when add_self_loops. The index rules
+    (kpnn2 page, constructor parameter table and "Raises") are the library's
+    own (pma_edge_list, host only); its rejections surface here as
+    ModuleArgError."""
     src = _index(source_index, "source_index")
     tgt = _index(target_index, "target_index")
-    if src.shape[0] != tgt.shape[0]:
-        raise ModuleArgError("source_index and target_index differ in length")
-    if src.shape[0] == 0:
-        raise ModuleArgError("the indices are empty")
-    if src.min() < 0 or src.max() >= S:
-        raise ModuleArgError(f"source_index outside [0, {S})")
-    if tgt.min() < 0 or tgt.max() >= L:
-        raise ModuleArgError(f"target_index outside [0, {L})")
-    pair = tgt * S + src
-    if np.unique(pair).shape[0] != pair.shape[0]:
-        raise ModuleArgError("target_index/source_index repeat a (source, target) pair")
-    if add_self_loops:
-        if L != S:
-            raise ModuleArgError("add_self_loops needs query_features == key_features")
-        have = np.zeros(L, bool)
-        have[src[src == tgt]] = True
-        extra = np.flatnonzero(~have)          # missing (i, i), ascending i
-        src = np.concatenate([src, extra])
-        tgt = np.concatenate([tgt, extra])
-    return src, tgt
+    try:
+        return pma_edge_list(src, tgt, L, S, add_self_loops)
+    except PmaError as e:
+        raise ModuleArgError(str(e)) from None
 
 
 def _named_edges(sources: Sequence, targets: Sequence, nodes: Optional[Sequence]):

@@ -329,6 +329,30 @@ pma_status pma_linear_backward(pma_plan *plan, int64_t batch, int64_t channels, 
    Waits for the device before freeing. */
 pma_status pma_destroy(pma_plan *plan);
 
+/*
+ * pma_edge_list -- the edge order a plan for these indices would have,
+ * computed on the host alone (no HIP call; for callers that validate and
+ * store a graph before any GPU is involved). The same rules as pma_create
+ * (kpnn2 page, constructor parameter table and "Raises"): nnz >= 1, sources
+ * in [0, key_features), targets in [0, query_features), no repeated
+ * (source, target) pair, add_self_loops (0 or 1) only with query_features
+ * == key_features; the given pairs in order, then with add_self_loops every
+ * missing (i, i) in ascending i.
+ *
+ *   source_index, target_index  HOST, nnz int64 each; read only.
+ *   capacity        entries src_out and tgt_out can hold (nnz + L always
+ *                   suffices).
+ *   src_out, tgt_out HOST outputs: the final edge list.
+ *   nnz_out         HOST: its length (also set when capacity is too small).
+ *
+ * Errors: PMA_E_NULL, PMA_E_SIZE (a size <= 0, or capacity below the list's
+ * length), PMA_E_INDEX_EMPTY, PMA_E_INDEX_RANGE, PMA_E_INDEX_DUPLICATE,
+ * PMA_E_SELF_LOOPS, PMA_E_ARG, PMA_E_OOM.
+ */
+pma_status pma_edge_list(const int64_t *source_index, const int64_t *target_index, int64_t nnz,
+                         int64_t query_features, int64_t key_features, int add_self_loops,
+                         int64_t capacity, int64_t *src_out, int64_t *tgt_out, int64_t *nnz_out);
+
 /* Number of live edges, counting appended self-loops (kpnn2 page, attribute
    nnz); -1 for a NULL plan. */
 int64_t pma_nnz(const pma_plan *plan);

@@ -138,3 +138,52 @@ def test_null_plan_linear_calls():
     assert pma.STATUS[lib.pma_linear_forward(None, 1, 1, z, z, None, z, None)] == "PMA_E_NULL"
     assert pma.STATUS[lib.pma_linear_backward(None, 1, 1, z, z, z, z, z, None, None)] == \
         "PMA_E_NULL"
+
+
+# ---------------------------------------------------------------------------
+# pma_edge_list: the library's host-side index rules against the oracle's
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_edge_list_matches_oracle(seed):
+    import oracle
+    from graph_sparse_head_amd import synth
+    rng = np.random.default_rng(300 + seed)
+    L = int(rng.integers(1, 40))
+    S = L if rng.random() < 0.5 else int(rng.integers(1, 40))
+    src, tgt = synth.random_graph(rng, L, S, float(rng.uniform(0.05, 0.5)))
+    if src.size == 0:
+        src, tgt = np.array([0]), np.array([0])
+    perm = rng.permutation(src.size)
+    src, tgt = src[perm], tgt[perm]
+    loops = L == S and bool(rng.random() < 0.6)
+    s, t = pma.pma_edge_list(src, tgt, L, S, add_self_loops=loops)
+    rs, rt = oracle.prepare_edges(src, tgt, L, S, 1, 1, loops)
+    assert (s == rs).all() and (t == rt).all()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(src=[], tgt=[]), "PMA_E_INDEX_EMPTY"),
+    (dict(src=[0, 4], tgt=[1, 0]), "PMA_E_INDEX_RANGE"),
+    (dict(src=[0, 1], tgt=[1, -1]), "PMA_E_INDEX_RANGE"),
+    (dict(src=[0, 1, 0], tgt=[1, 2, 1]), "PMA_E_INDEX_DUPLICATE"),
+    (dict(src=[0, 1], tgt=[1, 2], L=3, S=5, loops=True), "PMA_E_SELF_LOOPS"),
+    (dict(src=[0], tgt=[0], L=0), "PMA_E_SIZE"),
+])
+def test_edge_list_rejects(kw, expect):
+    L, S = kw.get("L", 4), kw.get("S", 4)
+    with pytest.raises(pma.PmaError) as e:
+        pma.pma_edge_list(np.array(kw["src"], np.int64), np.array(kw["tgt"], np.int64), L, S,
+                          add_self_loops=kw.get("loops", False))
+    assert e.value.name == expect
+
+
+def test_edge_list_reports_its_length_when_capacity_is_short():
+    lib = pma._load()
+    src = np.array([0, 1], np.int64)
+    tgt = np.array([1, 0], np.int64)
+    out = np.empty(8, np.int64)
+    n = ctypes.c_int64(-1)
+    st = lib.pma_edge_list(src.ctypes.data, tgt.ctypes.data, 2, 3, 3, 1, 2, out.ctypes.data,
+                           out.ctypes.data, ctypes.byref(n))
+    assert pma.STATUS[st] == "PMA_E_SIZE" and n.value == 5
