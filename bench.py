@@ -32,7 +32,7 @@ METRIC = "edge-heads/s fwd (nnz·H·B per sec) + % HBM roofline, 20k-node gene g
 HBM_PEAK_GBS = 8000.0
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "edge_gene_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def _workload(name: str):
@@ -68,7 +68,7 @@ def _traffic(cfg_name: str):
     """HBM bytes per edge-kernel launch from committed rocprofv3 counters, if
     they were taken for this kernel build and workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"edge_{cfg_name}_traffic.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
