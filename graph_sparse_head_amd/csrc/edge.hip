@@ -1001,48 +1001,76 @@ template <typename T, int CH, int LPH, int E_FUSE>
 __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
 {
     __shared__ __attribute__((aligned(16))) char wlds[E_FUSE > 0 ? staged_bytes<T, E_FUSE>() : 16];
-    if constexpr (E_FUSE > 0) {
-        if (a.fuse_out) {
-            stage_wo<T, CH, E_FUSE>(a, wlds);
-            __syncthreads();
-        }
-    }
     const int lane = threadIdx.x & 63;
     const uint32_t unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (unit >= (uint32_t)(a.n_split * a.passes))
-        return;
-    const uint32_t k = div31(unit, a.pass_m, a.pass_sh);
+    const bool valid = unit < (uint32_t)(a.n_split * a.passes);
+    const uint32_t k = valid ? div31(unit, a.pass_m, a.pass_sh) : 0;
     const int pass = (int)(unit - k * a.passes);
     const int B = a.B, E = a.E, H = a.H;
     const int cpr = E / CH;
     const int c = pass * 64 + lane;
-    const bool active = c < B * cpr;
+    const bool active = valid && c < B * cpr;
     const int b = active ? (int)div31(c, a.cpr_m, a.cpr_sh) : 0, cr = c - b * cpr,
               col = active ? cr * CH : 0;
     const int h = active ? cr / LPH : 0;
-    const int t = a.split_target[k], s0 = a.split_slot0[k], n = active ? a.split_count[k] : 0;
+    const int t = valid ? a.split_target[k] : 0, s0 = valid ? a.split_slot0[k] : 0;
+    const int n = active ? a.split_count[k] : 0;
+    // The partials of the first PF pieces are requested before Wo is staged,
+    // so that their memory latency overlaps the staging and its barrier.
+    constexpr int PF = 4;
+    auto ml_at = [&](int j) {
+        return *reinterpret_cast<const float2 *>(a.part_ml + (((int64_t)(s0 + j) * B + b) * H + h) * 2);
+    };
+    auto acc_at = [&](int j) {
+        return reinterpret_cast<const float4 *>(a.part_acc + ((int64_t)(s0 + j) * B + b) * E + col);
+    };
+    float2 pml[PF];
+    float4 pacc[PF][CH / 4];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        if (j < n) {
+            pml[j] = ml_at(j);
+#pragma unroll
+            for (int q = 0; q < CH / 4; ++q) pacc[j][q] = acc_at(j)[q];
+        }
+    }
+    if constexpr (E_FUSE > 0) {
+        if (a.fuse_out) {   // (every wavefront of the workgroup takes part)
+            stage_wo<T, CH, E_FUSE>(a, wlds);
+            __syncthreads();
+        }
+    }
+    if (!valid)
+        return;
     float M = -INFINITY;
-    for (int j = 0; j < n; ++j)
-        M = fmaxf(M, a.part_ml[(((int64_t)(s0 + j) * B + b) * H + h) * 2]);
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (j < n) M = fmaxf(M, pml[j].x);
+    for (int j = PF; j < n; ++j)
+        M = fmaxf(M, ml_at(j).x);
     float l = 0.f, acc[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc[i] = 0.f;
-    for (int j = 0; j < n; ++j) {
-        const float2 ml = *reinterpret_cast<const float2 *>(
-            a.part_ml + (((int64_t)(s0 + j) * B + b) * H + h) * 2);
-        // (a piece whose keys are all masked has l = 0 and m = -inf)
+    // (a piece whose keys are all masked has l = 0 and m = -inf)
+    auto add = [&](const float2 ml, const float4 *v) {
         const float w = ml.y > 0.f ? fast_exp2(ml.x - M) : 0.f;
         l = fmaf(ml.y, w, l);
-        const float4 *pa = reinterpret_cast<const float4 *>(
-            a.part_acc + ((int64_t)(s0 + j) * B + b) * E + col);
 #pragma unroll
         for (int q = 0; q < CH / 4; ++q) {
-            const float4 v = pa[q];
-            acc[4 * q + 0] = fmaf(v.x, w, acc[4 * q + 0]);
-            acc[4 * q + 1] = fmaf(v.y, w, acc[4 * q + 1]);
-            acc[4 * q + 2] = fmaf(v.z, w, acc[4 * q + 2]);
-            acc[4 * q + 3] = fmaf(v.w, w, acc[4 * q + 3]);
+            acc[4 * q + 0] = fmaf(v[q].x, w, acc[4 * q + 0]);
+            acc[4 * q + 1] = fmaf(v[q].y, w, acc[4 * q + 1]);
+            acc[4 * q + 2] = fmaf(v[q].z, w, acc[4 * q + 2]);
+            acc[4 * q + 3] = fmaf(v[q].w, w, acc[4 * q + 3]);
         }
+    };
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (j < n) add(pml[j], pacc[j]);
+    for (int j = PF; j < n; ++j) {
+        float4 v[CH / 4];
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) v[q] = acc_at(j)[q];
+        add(ml_at(j), v);
     }
     const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
     float out[CH];
