@@ -238,6 +238,9 @@ def main():
                     help="time PackedLinear (pma_linear_forward) on the workload's graph instead")
     ap.add_argument("--channels", type=int, default=1,
                     help="channels per node for --linear (1: the nn.Linear-shaped layer)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph that captured one pma_forward_static "
+                         "(needs a workspace within the static scratch)")
     ap.add_argument("--legs", default="cold,warm",
                     help="timed legs in order: cold (each step after a 1 GiB cache overwrite; "
                          "the first leg is the headline) and/or warm (steps back to back)")
@@ -295,7 +298,31 @@ def main():
         save = torch.empty(pma.pma_train_bytes(plan, case.B), dtype=torch.uint8, device="cuda")
         gout = torch.randn(out.shape, generator=torch.Generator().manual_seed(4)).to(out.dtype).cuda()
 
+    graph = None
+    if args.graph:
+        if args.train or kpm is not None:
+            ap.error("--graph times the inference forward without a mask")
+        fargs = (dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"], dev["bk"],
+                 dev["wv"], dev["bv"], dev["wo"], dev["bo"])
+        pma.pma_forward_static(plan, *fargs, out=out, weights=weights,
+                               need_weights=case.need_weights, average_attn_weights=case.average)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                pma.pma_forward_static(plan, *fargs, out=out, weights=weights,
+                                       need_weights=case.need_weights,
+                                       average_attn_weights=case.average)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        args.no_profile = True    # (a replay records no stage events)
+
     def step():
+        if graph is not None:
+            graph.replay()
+            return
         if args.train:
             pma.pma_forward_train(plan, dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"],
                                   dev["wk"], dev["bk"], dev["wv"], dev["bv"], dev["wo"], dev["bo"],
@@ -407,6 +434,7 @@ def main():
                                 f"{' need_weights' if case.need_weights else ''}"
                                 f"{f' key_padding_mask {args.key_padding_mask:g}' if kpm is not None else ''}"
                                 f"{' train step (forward + backward)' if args.train else ''}"
+                                f"{'; HIP graph replay of pma_forward_static' if graph is not None else ''}"
                                 + ("; cold cache: each step after a 1 GiB overwrite"
                                    if first == "cold" else "; warm cache: steps back to back")),
                    "batch": case.B, "nodes": case.L, "nnz": nnz, "embed_dim": case.E,

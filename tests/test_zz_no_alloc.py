@@ -114,3 +114,59 @@ def test_static_forward_refuses_a_workspace_beyond_the_scratch():
         assert torch.equal(o1, o2)
     finally:
         pma.pma_destroy(plan)
+
+
+# The reason for the entry point: it can be captured in a HIP graph
+# (torch.cuda.CUDAGraph) and replayed. Each replay follows eager work of the
+# program (new tokens copied into the captured inputs, synchronisation), and
+# its output must equal an eager pma_forward on the same inputs bit for bit.
+@pytest.mark.parametrize("case", ["bf16_fused_split", "f32_weights", "complete"])
+def test_static_forward_replayed_from_a_graph(case, monkeypatch):
+    if case == "bf16_fused_split":
+        monkeypatch.setenv("PMA_CHUNK", "7")
+        c = synth.random_case(210, 8, 200, 200, 64, 4, 0.05, dtype="bf16", name=case)
+        nw = False
+    elif case == "f32_weights":
+        c = synth.random_case(211, 4, 90, 150, 128, 8, 0.05, dtype="f32", same_kv=True,
+                              same_qkv=False, name=case)
+        nw = True
+    else:
+        c = synth.complete()
+        nw = True
+    print(f"[graph] {case}", flush=True)
+    dev = synth.to_torch(c)
+    plan = pma.pma_create(c.src, c.tgt, c.L, c.S, c.E, c.H, add_self_loops=c.add_self_loops,
+                          dtype=c.dtype)
+    try:
+        args = [dev["xq"], dev["xk"], dev["xv"], dev["wq"], dev["bq"], dev["wk"], dev["bk"],
+                dev["wv"], dev["bv"], dev["wo"], dev["bo"]]
+        out = torch.empty(c.B, c.L, c.E, dtype=dev["xq"].dtype, device="cuda")
+        w = torch.empty(c.B, plan.nnz, dtype=torch.float32, device="cuda") if nw else None
+        pma.pma_forward_static(plan, *args, out=out, weights=w)      # first use on the device
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                pma.pma_forward_static(plan, *args, out=out, weights=w)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gen = torch.Generator(device="cpu").manual_seed(7)
+        for r in range(4):
+            # new tokens in the captured input tensors (eager work between replays)
+            for t in {id(x): x for x in args[:3]}.values():
+                t.copy_(torch.randn(t.shape, generator=gen).to(t.dtype))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ref_out, ref_w = pma.pma_forward(plan, *args, need_weights=nw)
+            torch.cuda.synchronize()
+            a = out.view(torch.int16) if out.dtype == torch.bfloat16 else out
+            b = ref_out.view(torch.int16) if ref_out.dtype == torch.bfloat16 else ref_out
+            assert torch.equal(a, b), (case, r)
+            if nw:
+                assert torch.equal(w, ref_w), (case, r)
+        del g
+    finally:
+        pma.pma_destroy(plan)
