@@ -424,27 +424,33 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
     }
 }
 
-// Sums the pieces of split targets (dq) / split sources (dk, dv) in slot
-// order. Thread = (split, sample, 16-byte chunk).
-template <typename T>
+// Sums the pieces of split targets (dq) / split sources (dk, dv): G lanes
+// per (split, sample, 16-byte chunk).
+template <typename T, int G>
 __global__ void __launch_bounds__(256) bwd_merge_fast(const BwdArgs a, int sources)
 {
+    // G adjacent lanes serve one (split row, sample, 16-byte chunk): lane g
+    // adds slots g, g + G, g + 2G, ... in slot order, kM of them in flight,
+    // and the G partial sums meet in a fixed butterfly (deterministic; long
+    // rows such as hub sources cut into hundreds of pieces no longer add
+    // their slots one round trip at a time).
     constexpr int VEC = Vec<T>::N;
     const int CPR = a.E / VEC;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t gb = idx / CPR;
-    const int c = (int)(idx - gb * CPR);
+    const int g = (int)(idx & (G - 1));
+    const int64_t gi = idx / G;
+    const int64_t gb = gi / CPR;
+    const int c = (int)(gi - gb * CPR);
     const int64_t i = gb / a.B;
     const int b = (int)(gb - i * a.B);
     if (i >= (sources ? a.n_ssplit : a.n_tsplit))
-        return;
+        return;   // (the whole group of G lanes)
     const int row_id = sources ? a.ss_source[i] : a.ts_target[i];
     const int slot0 = sources ? a.ss_slot0[i] : a.ts_slot0[i];
     const int count = sources ? a.ss_count[i] : a.ts_count[i];
     const int nout = sources ? 2 : 1;
     const int width = nout * a.E;
     const float *part = sources ? a.part_kv : a.part_q;
-    // both outputs at once; slots loaded kM at a time and added in slot order
     constexpr int kM = 4;
     float acc[2][VEC];
 #pragma unroll
@@ -454,23 +460,23 @@ __global__ void __launch_bounds__(256) bwd_merge_fast(const BwdArgs a, int sourc
             acc[o][j] = 0.f;
     const float *base = part + ((int64_t)slot0 * a.B + b) * width + c * VEC;
     const int64_t sstride = (int64_t)a.B * width;
-    for (int k0 = 0; k0 < count; k0 += kM) {
+    for (int k0 = g; k0 < count; k0 += G * kM) {
         float4 v[kM][2][VEC / 4];
 #pragma unroll
         for (int u = 0; u < kM; ++u) {
-            if (k0 + u < count) {
+            if (k0 + u * G < count) {
 #pragma unroll
                 for (int o = 0; o < 2; ++o)
                     if (o < nout)
 #pragma unroll
                         for (int j = 0; j < VEC / 4; ++j)
-                            v[u][o][j] = *reinterpret_cast<const float4 *>(base + (k0 + u) * sstride +
-                                                                          o * a.E + 4 * j);
+                            v[u][o][j] = *reinterpret_cast<const float4 *>(
+                                base + (k0 + u * G) * sstride + o * a.E + 4 * j);
             }
         }
 #pragma unroll
         for (int u = 0; u < kM; ++u) {
-            if (k0 + u < count) {
+            if (k0 + u * G < count) {
 #pragma unroll
                 for (int o = 0; o < 2; ++o)
                     if (o < nout)
@@ -483,6 +489,17 @@ __global__ void __launch_bounds__(256) bwd_merge_fast(const BwdArgs a, int sourc
                         }
             }
         }
+    }
+    if constexpr (G > 1) {
+#pragma unroll
+        for (int off = 1; off < G; off <<= 1)
+#pragma unroll
+            for (int o = 0; o < 2; ++o)
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    acc[o][j] += __shfl_xor(acc[o][j], off, 64);
+        if (g != 0)
+            return;
     }
     for (int o = 0; o < nout; ++o) {
         T *dst = sources ? reinterpret_cast<T *>(o == 0 ? a.dk : a.dv) +
@@ -1348,10 +1365,18 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
             PMA_BWD_EDGE(16)
         }
 #undef PMA_BWD_EDGE
-        if (a.n_tsplit > 0)
-            bwd_merge_fast<T><<<grid(a.n_tsplit * a.B * cpr), 256, 0, s>>>(a, 0);
-        if (a.n_ssplit > 0)
-            bwd_merge_fast<T><<<grid(a.n_ssplit * a.B * cpr), 256, 0, s>>>(a, 1);
+        // eight lanes per merged chunk where rows have many slots on average
+        // (hub sources), one lane otherwise
+        auto merge = [&](int64_t nsplit, int64_t nslots, int sources) {
+            if (nsplit <= 0)
+                return;
+            if (nslots > 8 * nsplit)
+                bwd_merge_fast<T, 8><<<grid(nsplit * a.B * cpr * 8), 256, 0, s>>>(a, sources);
+            else
+                bwd_merge_fast<T, 1><<<grid(nsplit * a.B * cpr), 256, 0, s>>>(a, sources);
+        };
+        merge(a.n_tsplit, a.n_tslots, 0);
+        merge(a.n_ssplit, a.n_sslots, 1);
     };
     // The fast target pass and the merge share one ordering: the merge runs
     // after both edge passes, and reads only slots the target / source pass wrote.

@@ -1183,6 +1183,8 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
     a.n_tsplit = gd.n_split;
     a.n_stasks = gd.n_stasks;
     a.n_ssplit = gd.n_ssplit;
+    a.n_tslots = gd.n_slots;
+    a.n_sslots = gd.n_sslots;
     for (int k = 0; k <= pma::kBands; ++k)
         a.s_band_off[k] = gd.s_band_off[k];
     a.banded = gd.s_banded ? 1 : 0;

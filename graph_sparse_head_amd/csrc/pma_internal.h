@@ -180,6 +180,7 @@ struct BwdArgs {
     const int32_t *s_source, *s_begin, *s_end, *s_slot;
     const int32_t *ss_source, *ss_slot0, *ss_count;
     int64_t n_ttasks, n_tsplit, n_stasks, n_ssplit;
+    int64_t n_tslots, n_sslots;      // partial slots of the split targets / sources
     int64_t s_band_off[kBands + 1];  // source pieces per band (one band per XCD)
     int banded;                      // 0: one band, launched in plain order
     // target pass order over sample groups of 64 lanes (t_groups of them):
