@@ -220,6 +220,45 @@ def bench_linear(args):
     print(json.dumps(res), flush=True)
 
 
+# Table sizes of the gather-ceiling calibration: within one CU's 32 KB L1,
+# within one XCD's 4 MB L2, within the 256 MB last-level cache, and far past it.
+CEILING_TABLES = (("L1", 16 << 10), ("L2", 2 << 20), ("LLC", 128 << 20), ("HBM", 3 << 30))
+
+
+def gather_ceiling(n_rows=1 << 24, per=64, launches=10):
+    """Rate of random 1 KB row gathers (16 bytes per lane, eight rows in
+    flight per wavefront) from each level of the memory hierarchy: the
+    ceiling for the edge kernel's key and value gathers."""
+    import torch
+    import graph_sparse_head_amd as pma
+    g = torch.Generator(device="cuda").manual_seed(11)
+    sink = torch.empty(((n_rows + per - 1) // per) * 1024, dtype=torch.uint8, device="cuda")
+    res = {"rows_per_launch": n_rows, "row_bytes": 1024, "rows_per_wave": per, "levels": {}}
+    for name, nbytes in CEILING_TABLES:
+        table = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        rows = torch.randint(0, nbytes // 1024, (n_rows,), generator=g, device="cuda",
+                             dtype=torch.int32)
+        for _ in range(3):
+            pma.pma_gather_ceiling(table, rows, per, sink)
+        st = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(launches):
+            pma.pma_gather_ceiling(table, rows, per, sink)
+        b.record(st)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / launches
+        rate = n_rows * 1024 / (us * 1e-6)
+        res["levels"][name] = {"table_bytes": nbytes, "avg_launch_us": us,
+                               "delivered_TBs": rate / 1e12,
+                               "bytes_per_clk_per_cu": rate / (2.4e9 * 256)}
+        del table, rows
+        print(f"gather ceiling {name:4s} table {nbytes:>11d} B: {us:9.1f} us per launch, "
+              f"{rate / 1e12:6.2f} TB/s, {rate / (2.4e9 * 256):5.1f} B/clk/CU", file=sys.stderr,
+              flush=True)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +285,13 @@ def main():
                          "the first leg is the headline) and/or warm (steps back to back)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 5 times (counter calibration)")
+    ap.add_argument("--gather-ceiling", action="store_true",
+                    help="only time pma_gather_ceiling (random 1 KB row gathers) from tables "
+                         "sized for L1, L2, the last-level cache and HBM")
     args = ap.parse_args()
+    if args.gather_ceiling:
+        gather_ceiling()
+        return
     if args.copy_probe:
         import torch
         n = args.copy_probe << 20

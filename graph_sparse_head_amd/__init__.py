@@ -24,7 +24,7 @@ __all__ = [
     "pma_nnz", "pma_edges", "pma_edge_list",
     "pma_last_error", "pma_plan_info", "pma_csr", "pma_work_split", "pma_profile",
     "pma_profile_stages",
-    "pma_profile_read", "pma_gather_probe", "STATUS", "STAGES", "library_path",
+    "pma_profile_read", "pma_gather_probe", "pma_gather_ceiling", "STATUS", "STAGES", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +98,7 @@ def _load():
         "pma_profile_stages": (st, [P, ctypes.c_uint32]),
         "pma_profile_read": (st, [P, P, P]),
         "pma_gather_probe": (st, [P, P]),
+        "pma_gather_ceiling": (st, [P, ctypes.c_uint64, P, I64, I64, P, P]),
         "pma_edge_list": (st, [P, P, I64, I64, I64, I32, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -586,6 +587,25 @@ def pma_profile_read(plan: Plan) -> dict:
 def pma_gather_probe(plan: Plan, stream=None) -> None:
     """``pma_gather_probe``: the last forward's edge-kernel loads alone."""
     _check(_load().pma_gather_probe(plan.handle, _stream_ptr(stream)))
+
+
+def pma_gather_ceiling(table, rows, rows_per_wave: int, sink, stream=None) -> None:
+    """``pma_gather_ceiling``: 1 KB row gathers from ``table`` (a contiguous
+    CUDA tensor of whole KiB) at the int32 CUDA tensor ``rows``; ``sink`` is a
+    contiguous CUDA tensor of at least ceil(len(rows) / rows_per_wave) KiB."""
+    import torch
+    for name, t in (("table", table), ("rows", rows), ("sink", sink)):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise PmaError(8, f"{name} must be a contiguous GPU tensor")
+    if rows.dtype != torch.int32 or rows.dim() != 1:
+        raise PmaError(7, "rows must be a 1-d int32 tensor")
+    n = rows.numel()
+    waves = -(-n // rows_per_wave) if rows_per_wave > 0 else 0
+    if sink.numel() * sink.element_size() < waves * 1024:
+        raise PmaError(2, "sink holds less than 1 KiB per wavefront")
+    _check(_load().pma_gather_ceiling(table.data_ptr(), table.numel() * table.element_size(),
+                                      rows.data_ptr(), n, rows_per_wave, sink.data_ptr(),
+                                      _stream_ptr(stream)))
 
 
 def __getattr__(name):

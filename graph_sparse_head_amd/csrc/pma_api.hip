@@ -1018,6 +1018,26 @@ PMA_API pma_status pma_gather_probe(pma_plan *plan, hipStream_t stream)
     return PMA_OK;
 }
 
+PMA_API pma_status pma_gather_ceiling(const void *table, uint64_t table_bytes, const int32_t *rows,
+                                      int64_t n_rows, int64_t rows_per_wave, void *sink,
+                                      hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!table || !rows || !sink)
+        return fail(PMA_E_NULL, "table, rows and sink must be device pointers");
+    if (table_bytes < 1024 || table_bytes % 1024 != 0 || table_bytes >= ((uint64_t)1 << 32))
+        return fail(PMA_E_ARG, "table_bytes must be a multiple of 1024 in [1024, 2^32)");
+    if (n_rows < 1 || rows_per_wave < 1 || rows_per_wave > (1 << 20))
+        return fail(PMA_E_ARG, "n_rows >= 1 and rows_per_wave in [1, 2^20] required");
+    if ((n_rows + rows_per_wave - 1) / rows_per_wave > ((int64_t)1 << 30))
+        return fail(PMA_E_ARG, "more than 2^30 wavefronts");
+    const pma_status st = pma::launch_gather_ceiling(table, table_bytes, rows, n_rows, rows_per_wave,
+                                                     sink, stream);
+    if (st != PMA_OK)
+        return fail(st, "gather ceiling launch failed: %s", hipGetErrorString(hipGetLastError()));
+    return PMA_OK;
+}
+
 PMA_API size_t pma_train_bytes(const pma_plan *plan, int64_t batch)
 {
     if (!plan || batch <= 0 || plan->E == 0)

@@ -284,6 +284,9 @@ pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
 // PMA_E_UNSUPPORTED where the 16-byte kernel does not serve the head size or
 // a tensor is 2 GiB or more.
 pma_status launch_gather_probe(const EdgeArgs &a, hipStream_t s);
+// Calibration: n 1 KB row gathers from a table (pma_gather_ceiling).
+pma_status launch_gather_ceiling(const void *table, uint64_t table_bytes, const int32_t *rows,
+                                 int64_t n, int64_t per, void *sink, hipStream_t s);
 pma_status launch_weights(const EdgeArgs &a, hipStream_t s);
 
 }  // namespace pma

@@ -430,6 +430,28 @@ pma_status pma_profile_read(pma_plan *plan, double *ms, int64_t *calls);
  */
 pma_status pma_gather_probe(pma_plan *plan, hipStream_t stream);
 
+/*
+ * pma_gather_ceiling -- calibration, not part of the method. Enqueues one
+ * launch in which wavefront w gathers the 1024-byte rows rows[w * rows_per_wave
+ * .. (w + 1) * rows_per_wave - 1] (the last wavefront fewer) of `table`, one
+ * 16-byte chunk per lane and eight rows in flight, folds the loaded words
+ * together and writes one 16-byte word per lane to sink[w * 1024 ..]. Its rate
+ * over a table sized for L1, L2, the last-level cache or HBM is what the
+ * vector memory path delivers for random-row gathers from that level: the
+ * ceiling against which the edge kernel's gathers are read.
+ *   table        DEVICE, table_bytes bytes (a multiple of 1024, under 2^32);
+ *                read only
+ *   rows         DEVICE int32[n_rows], row indices; an index at or past
+ *                table_bytes / 1024 (or negative) reads the table's last row
+ *   sink         DEVICE, ceil(n_rows / rows_per_wave) * 1024 bytes, written
+ * All buffers stay the caller's. Errors: PMA_E_NULL, PMA_E_ARG (sizes out of
+ * range, rows_per_wave outside [1, 2^20], more than 2^30 wavefronts),
+ * PMA_E_DEVICE.
+ */
+pma_status pma_gather_ceiling(const void *table, uint64_t table_bytes, const int32_t *rows,
+                              int64_t n_rows, int64_t rows_per_wave, void *sink,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -187,3 +187,19 @@ def test_edge_list_reports_its_length_when_capacity_is_short():
     st = lib.pma_edge_list(src.ctypes.data, tgt.ctypes.data, 2, 3, 3, 1, 2, out.ctypes.data,
                            out.ctypes.data, ctypes.byref(n))
     assert pma.STATUS[st] == "PMA_E_SIZE" and n.value == 5
+
+
+def test_gather_ceiling_rejects_before_any_launch():
+    # argument checks of the calibration entry point (no device memory is
+    # touched: every call below returns before a launch)
+    lib = pma._load()
+    z = ctypes.c_void_p(0x1000)
+    st = lambda *a: pma.STATUS[lib.pma_gather_ceiling(*a)]
+    assert st(None, 1024, z, 8, 8, z, None) == "PMA_E_NULL"
+    assert st(z, 1024, None, 8, 8, z, None) == "PMA_E_NULL"
+    assert st(z, 1024, z, 8, 8, None, None) == "PMA_E_NULL"
+    for tb in (0, 1000, 1536, 1 << 32):
+        assert st(z, tb, z, 8, 8, z, None) == "PMA_E_ARG", tb
+    for n, per in ((0, 8), (8, 0), (8, (1 << 20) + 1), (-1, 8), ((1 << 31) + 1, 1)):
+        assert st(z, 1024, z, n, per, z, None) == "PMA_E_ARG", (n, per)
+    assert "rows_per_wave" in pma.pma_last_error() or "wavefronts" in pma.pma_last_error()
