@@ -161,8 +161,11 @@ __device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uin
 // CM (UNI only): the mask comes as one uniform word per CSR position
 // (kpm_csr); otherwise each lane looks its bit up by source.
 // bf16 plans keep q and dm packed and form the dot products with v_dot2.
-template <typename T, int LPH, bool UNI, bool CM = false>
-__global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
+// PF: the next kU edges' rows are requested before the current ones are
+// used (twice the row registers); otherwise each step loads, then uses.
+template <typename T, int LPH, bool UNI, bool CM = false, bool PF = true>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PF ? 1 : 7)))
+bwd_target_fast(const BwdArgs a)
 {
     constexpr int VEC = Vec<T>::N;
     constexpr bool BF = sizeof(T) == 2;
@@ -251,12 +254,16 @@ __global__ void __launch_bounds__(256) bwd_target_fast(const BwdArgs a)
             vq[u] = ld16(Vb + (int64_t)r[u] * a.E);
         }
     };
-    if (beg < end)
+    if (PF && beg < end)
         fetch(beg, s, kr, vr);
     for (int p0 = beg; p0 < end; p0 += kU) {
-        const bool more = p0 + kU < end;
-        if (more)
-            fetch(p0 + kU, sn, kn, vn);
+        const bool more = PF && p0 + kU < end;
+        if constexpr (PF) {
+            if (more)
+                fetch(p0 + kU, sn, kn, vn);
+        } else {
+            fetch(p0, s, kr, vr);
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float kk[VEC];
@@ -1331,6 +1338,16 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
         }
         if (!uni || (at.t_order == 1 && 8 % G != 0))
             at.t_order = 0;
+        if (at.t_pf < 0) {
+            // Requesting a step's rows one step ahead doubles their registers
+            // (4 wavefronts per SIMD instead of 7 for bf16). Measured on
+            // MI355X: where the bf16 keys and values outgrow the 256 MB
+            // last-level cache, more wavefronts with one step in flight each
+            // win (100k-node target pass 1784 -> 1686 us); on the gene and
+            // bipartite steps the two are level (within 1 %).
+            const uint64_t kv = (uint64_t)a.Skv * a.B * a.E * sizeof(T) * 2;
+            at.t_pf = sizeof(T) == 2 && kv > ((uint64_t)256 << 20) ? 0 : 1;
+        }
         if (at.t_order != 0) {
             const int64_t gblocks = (a.n_ttasks * 64 + 255) / 256;   // per group
             at.t_gthreads = gblocks * 256;
@@ -1344,10 +1361,14 @@ pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
 #define PMA_BWD_EDGE(L_)                                                            \
     case L_:                                                                       \
         if (uni) {                                                                 \
-            if (cm)                                                                \
+            if (cm && at.t_pf)                                                     \
                 bwd_target_fast<T, L_, true, true><<<gt, 256, 0, s>>>(at);         \
-            else                                                                   \
+            else if (cm)                                                           \
+                bwd_target_fast<T, L_, true, true, false><<<gt, 256, 0, s>>>(at);  \
+            else if (at.t_pf)                                                      \
                 bwd_target_fast<T, L_, true><<<gt, 256, 0, s>>>(at);               \
+            else                                                                   \
+                bwd_target_fast<T, L_, true, false, false><<<gt, 256, 0, s>>>(at); \
             if (a.banded)                                                          \
                 bwd_source_fast<T, L_, true><<<gs_band, 256, 0, s>>>(a);           \
             else                                                                   \

@@ -188,6 +188,7 @@ struct BwdArgs {
     // divides 8), 2 groups in turn, -1 chosen at launch; t_gthreads threads
     // per group (whole workgroups)
     int t_order, t_groups;
+    int t_pf = -1;       // target pass: next rows requested ahead (1), not (0), automatic (-1)
     int64_t t_gthreads;
     const uint64_t *kpm_bits;        // packed mask or nullptr
     int kpm_words;

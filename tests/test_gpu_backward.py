@@ -229,6 +229,27 @@ def test_backward_target_pass_order(order, shape, monkeypatch):
     _grad_check(c, "none")
 
 
+# The target pass with each step's rows loaded when they are used
+# (PMA_BWD_PF=0) instead of one step ahead: unsplit and split targets
+# (ragged last steps), masks with uniform words and per-lane bits.
+@pytest.mark.parametrize("shape", [("bf16", 64, 4, 16), ("bf16", 128, 8, 8), ("f32", 128, 8, 6),
+                                   ("f32", 64, 4, 4), ("bf16", 8, 1, 64)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_B{s[3]}")
+@pytest.mark.parametrize("chunk", ["auto", "5"])
+@pytest.mark.parametrize("mask", [False, True])
+def test_backward_target_pass_without_prefetch(shape, chunk, mask, monkeypatch):
+    monkeypatch.setenv("PMA_BWD_PF", "0")
+    if chunk != "auto":
+        monkeypatch.setenv("PMA_CHUNK", chunk)
+    dt, E, H, B = shape
+    c = synth.random_case(96, B, 70, 70, E, H, 0.08, dtype=dt, same_kv=False, name="bwd_nopf")
+    kpm = None
+    if mask:
+        kpm = np.random.default_rng(95).random((c.B, c.S)) < 0.3
+        kpm[1] = True
+    _grad_check(c, "none", kpm=kpm)
+
+
 # key_padding_mask in the fast target pass: whole wavefronts per piece read
 # one mask word per edge (bf16 E = 64 at B = 16: 8 samples per wavefront;
 # fp32 E = 128 at B = 8: 2), with split pieces; bf16 E = 8 puts 64 samples on
