@@ -250,6 +250,22 @@ def test_backward_target_pass_without_prefetch(shape, chunk, mask, monkeypatch):
     _grad_check(c, "none", kpm=kpm)
 
 
+# Source pieces of the backward's source pass: short pieces (PMA_BWD_CHUNK)
+# split most sources, and target bands cut into sub-bands per XCD
+# (PMA_BWD_SUB) reorder the pieces; both only change which partial sums the
+# merge adds.
+@pytest.mark.parametrize("knobs", [{"PMA_BWD_CHUNK": "3"}, {"PMA_BWD_CHUNK": "16"},
+                                   {"PMA_BWD_SUB": "2"}, {"PMA_BWD_SUB": "5", "PMA_BWD_CHUNK": "4"},
+                                   {"PMA_BWD_PF": "1"}],
+                         ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_source_piece_knobs(knobs, dt, monkeypatch):
+    for k, v in knobs.items():
+        monkeypatch.setenv(k, v)
+    c = synth.random_case(94, 8, 90, 110, 128, 8, 0.08, dtype=dt, same_kv=False, name="bwd_knobs")
+    _grad_check(c, "none")
+
+
 # key_padding_mask in the fast target pass: whole wavefronts per piece read
 # one mask word per edge (bf16 E = 64 at B = 16: 8 samples per wavefront;
 # fp32 E = 128 at B = 8: 2), with split pieces; bf16 E = 8 puts 64 samples on
