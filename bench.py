@@ -74,7 +74,7 @@ def _traffic(cfg_name: str):
         return None
     if t.get("workload") != cfg_name or t.get("kernel_sha") != _kernel_sha():
         return None
-    return t.get("bytes_per_launch")
+    return t
 
 
 def _kernel_sha():
@@ -225,7 +225,7 @@ def bench_linear(args):
 CEILING_TABLES = (("L1", 16 << 10), ("L2", 2 << 20), ("LLC", 128 << 20), ("HBM", 3 << 30))
 
 
-def gather_ceiling(n_rows=1 << 24, per=64, launches=10):
+def gather_ceiling(n_rows=1 << 24, per=64, launches=10, levels=None, verbose=True):
     """Rate of random 1 KB row gathers (16 bytes per lane, eight rows in
     flight per wavefront) from each level of the memory hierarchy: the
     ceiling for the edge kernel's key and value gathers."""
@@ -235,6 +235,8 @@ def gather_ceiling(n_rows=1 << 24, per=64, launches=10):
     sink = torch.empty(((n_rows + per - 1) // per) * 1024, dtype=torch.uint8, device="cuda")
     res = {"rows_per_launch": n_rows, "row_bytes": 1024, "rows_per_wave": per, "levels": {}}
     for name, nbytes in CEILING_TABLES:
+        if levels is not None and name not in levels:
+            continue
         table = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
         rows = torch.randint(0, nbytes // 1024, (n_rows,), generator=g, device="cuda",
                              dtype=torch.int32)
@@ -253,10 +255,11 @@ def gather_ceiling(n_rows=1 << 24, per=64, launches=10):
                                "delivered_TBs": rate / 1e12,
                                "bytes_per_clk_per_cu": rate / (2.4e9 * 256)}
         del table, rows
-        print(f"gather ceiling {name:4s} table {nbytes:>11d} B: {us:9.1f} us per launch, "
-              f"{rate / 1e12:6.2f} TB/s, {rate / (2.4e9 * 256):5.1f} B/clk/CU", file=sys.stderr,
-              flush=True)
-    print(json.dumps(res), flush=True)
+        if verbose:
+            print(f"gather ceiling {name:4s} table {nbytes:>11d} B: {us:9.1f} us per launch, "
+                  f"{rate / 1e12:6.2f} TB/s, {rate / (2.4e9 * 256):5.1f} B/clk/CU",
+                  file=sys.stderr, flush=True)
+    return res
 
 
 def main():
@@ -290,7 +293,7 @@ def main():
                          "sized for L1, L2, the last-level cache and HBM")
     args = ap.parse_args()
     if args.gather_ceiling:
-        gather_ceiling()
+        print(json.dumps(gather_ceiling()), flush=True)
         return
     if args.copy_probe:
         import torch
@@ -461,6 +464,11 @@ def main():
         if pt:
             probe = sum(a.elapsed_time(b) for a, b in pt) / len(pt) * 1e-3
     del scratch
+    ceiling = None
+    if not args.train and not args.no_profile:
+        # Calibration: what the memory path delivers for random 1 KB row
+        # gathers from L2 and from the last-level cache (a few ms)
+        ceiling = gather_ceiling(n_rows=1 << 22, launches=5, levels=("L2", "LLC"), verbose=False)
     head = times[first]
     ms_per_step = sum(head) / len(head)
     edge_heads = nnz * case.H * case.B
@@ -496,9 +504,11 @@ def main():
                                    case.E, es, case.need_weights, case.H)
         gbytes = edge_gather_bytes(case.B, case.L, nnz, case.E, es)
         achieved = nbytes / edge_avg_s / 1e9
+        traffic = _traffic(args.config)
         res["roofline"] = {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(args.config),
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic["bytes_per_launch"] if traffic else None,
             "kernel": "edge_fast" + (" (q projection and out_proj fused)" if fused else ""),
             "bytes_per_launch": nbytes, "bytes": "compulsory: each input and output byte once",
             "avg_launch_us": edge_avg_s * 1e6, "timed_launches": edge_calls,
@@ -507,6 +517,19 @@ def main():
                              "note": "every edge's key and value rows per sample; mostly "
                                      "served by L2 and the last-level cache, not an HBM rate"},
         }
+        if ceiling is not None:
+            lv = ceiling["levels"]
+            l2, llc = lv["L2"]["delivered_TBs"], lv["LLC"]["delivered_TBs"]
+            gc = {"L2_TBs": l2, "LLC_TBs": llc,
+                  "gather_vs_L2": gbytes / edge_avg_s / 1e12 / l2,
+                  "note": "pma_gather_ceiling: random 1 KB row gathers (the edge kernel's lane "
+                          "layout) from a 2 MiB table (L2) and a 128 MiB one (last-level cache); "
+                          "gather_vs_L2 = the gather model's rate over the L2 ceiling"}
+            if traffic:
+                rd = traffic["read_bytes"] / edge_avg_s / 1e12
+                gc["beyond_L2_read_TBs"] = rd
+                gc["beyond_L2_vs_LLC"] = rd / llc
+            res["roofline"]["gather_ceiling"] = gc
         if probe is not None:
             res["roofline"]["gather_probe"] = {
                 "avg_launch_us": probe * 1e6, "delivered_GBs": gbytes / probe / 1e9,
