@@ -61,6 +61,9 @@ struct pma_plan {
     int bsub = 1;               // PMA_BWD_SUB: target bands per XCD for the backward's source pieces
     int border = -1;            // PMA_BWD_ORDER: backward target pass over sample groups (0, 1, 2; -1 automatic)
     int bpf = -1;               // PMA_BWD_PF: backward target pass requests the next rows ahead (1), not (0), auto (-1)
+    // PMA_BWD_SORDER: banded source pass with its sample groups in turn
+    // within each band (2, default) or interleaved (0)
+    int bsorder = 2;
     bool batch_first_ws = false; // PMA_LAYOUT=batch: q/k/v/mixed workspace batch-first
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 2 groups in turn, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
@@ -383,6 +386,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_BWD_ORDER  backward target pass over sample groups, as PMA_XCD_MAP
     //   PMA_BWD_PF     1 / 0: backward target pass with or without the next
     //                  rows requested ahead (default automatic)
+    //   PMA_BWD_SORDER 0: banded source pass with its sample groups
+    //                  interleaved instead of in turn within each band
     //   PMA_HOT        1: hot-row LDS cache in the q-projecting edge kernel
     // Piece length: a target is split only when it has far more edges than
     // the average target (16x, rounded up to a power of two, at least 256).
@@ -407,6 +412,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         if (c >= 1 && c <= 65535)
             p->bchunk = (int)c;
     }
+    if (const char *ev = getenv("PMA_BWD_SORDER"))
+        p->bsorder = ev[0] == '0' ? 0 : 2;
     if (const char *ev = getenv("PMA_BWD_PF"))
         p->bpf = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_BWD_ORDER"))
@@ -1214,6 +1221,7 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         a.s_band_off[k] = gd.s_band_off[k];
     a.banded = gd.s_banded ? 1 : 0;
     a.t_order = p->border;
+    a.s_order = p->bsorder;
     a.t_pf = p->bpf;
     a.kpm_bits = nullptr;
     a.kpm_words = 0;

@@ -183,6 +183,9 @@ struct BwdArgs {
     int64_t n_tslots, n_sslots;      // partial slots of the split targets / sources
     int64_t s_band_off[kBands + 1];  // source pieces per band (one band per XCD)
     int banded;                      // 0: one band, launched in plain order
+    // banded source pass: 2 = sample groups in turn within each band (the
+    // band's wavefronts for group 0, then group 1, ...), 0 = interleaved
+    int s_order = 2;
     // target pass order over sample groups of 64 lanes (t_groups of them):
     // 0 interleaved, 1 group g on the XCDs x with x % t_groups = g (t_groups
     // divides 8), 2 groups in turn, -1 chosen at launch; t_gthreads threads

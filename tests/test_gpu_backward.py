@@ -181,6 +181,31 @@ def test_backward_hub_source(chunk, monkeypatch):
     _grad_check(c, "qkv")
 
 
+# Hub sources (70-280 targets each) are cut at eight target bands, one per
+# XCD; the band's pieces run with their sample groups interleaved (default)
+# or one group after another (PMA_BWD_SORDER=2), with short pieces too.
+@pytest.mark.parametrize("order", ["0", "2"])
+@pytest.mark.parametrize("chunk", ["auto", "32"])
+@pytest.mark.parametrize("shape", [("bf16", 128, 8, 8), ("f32", 128, 8, 8), ("bf16", 64, 4, 16)],
+                         ids=lambda s: f"{s[0]}_E{s[1]}_B{s[3]}")
+def test_backward_banded_source_order(order, chunk, shape, monkeypatch):
+    monkeypatch.setenv("PMA_BWD_SORDER", order)
+    if chunk != "auto":
+        monkeypatch.setenv("PMA_BWD_CHUNK", chunk)
+    dt, E, H, B = shape
+    c = synth.random_case(89, B, 300, 200, E, H, 0.01, dtype=dt, same_kv=False,
+                          name="bwd_bands")
+    rng = np.random.default_rng(90)
+    hubs = [3, 11, 50, 120]
+    keep = ~np.isin(c.src, hubs)
+    src, tgt = [c.src[keep]], [c.tgt[keep]]
+    for h, n in zip(hubs, (70, 140, 210, 280)):
+        src.append(np.full(n, h))
+        tgt.append(rng.choice(c.L, size=n, replace=False))
+    c.src, c.tgt = np.concatenate(src), np.concatenate(tgt)
+    _grad_check(c, "none")
+
+
 def test_backward_masked_pieces(monkeypatch):
     monkeypatch.setenv("PMA_CHUNK", "4")
     c = synth.random_case(87, 5, 50, 50, 64, 4, 0.15, dtype="bf16", name="bwd_mask_pieces")
