@@ -254,6 +254,24 @@ bwd_target_fast(const BwdArgs a)
             vq[u] = ld16(Vb + (int64_t)r[u] * a.E);
         }
     };
+    // With PF a step's (p, dz) pairs are stored after the next step's loads
+    // are issued: vector memory operations complete in order, so a store
+    // issued before those loads would hold back their use until it is
+    // acknowledged (bipartite step 1.83 -> 1.81 ms). Without PF the held
+    // pairs would cost registers the variant does not have (7 spills, 100k-
+    // node step 5.93 -> 6.03 ms): each edge's pair is stored at once.
+    typedef typename PZRaw<T>::type PZT;
+    PZT pzs[kU];
+    int pz0 = -1;   // first position of the held pairs (wave-uniform), -1: none
+    auto flush = [&]() {
+        if (PF && pz0 >= 0 && lead) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (pz0 + u < end)
+                    reinterpret_cast<PZT *>(a.PZ)[((int64_t)(pz0 + u) * a.B + b) * a.H + h] = pzs[u];
+            }
+        }
+    };
     if (PF && beg < end)
         fetch(beg, s, kr, vr);
     for (int p0 = beg; p0 < end; p0 += kU) {
@@ -264,6 +282,7 @@ bwd_target_fast(const BwdArgs a)
         } else {
             fetch(p0, s, kr, vr);
         }
+        flush();
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float kk[VEC];
@@ -307,12 +326,17 @@ bwd_target_fast(const BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
                     dq[i] = fmaf(dz, kk[i], dq[i]);
-                if (lead) {
-                    const int64_t o = ((int64_t)p * a.B + b) * a.H + h;
-                    put_pz<T>(a.PZ, o, pe, dz);
+                if constexpr (!PF) {
+                    if (lead)
+                        put_pz<T>(a.PZ, ((int64_t)p * a.B + b) * a.H + h, pe, dz);
+                } else if constexpr (sizeof(T) == 2) {
+                    pzs[u] = pack_bf16(pe, dz);
+                } else {
+                    pzs[u] = make_float2(pe, dz);
                 }
             }
         }
+        pz0 = p0;
         if (more) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
@@ -322,6 +346,7 @@ bwd_target_fast(const BwdArgs a)
             }
         }
     }
+    flush();
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dq[i] *= a.inv_sqrt_d;
