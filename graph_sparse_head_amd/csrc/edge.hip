@@ -389,7 +389,9 @@ constexpr uint32_t kHotSlot = 2048;
 // 32: 64 samples per wavefront, or a row of chunks that is not a power of
 // two, so that wavefronts start mid-row); each lane picks the word of its
 // own sample.
-template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = false> struct EdgeLane {
+template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = false,
+          bool HS = false>
+struct EdgeLane {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
     static constexpr bool BF = sizeof(T) == 2;
@@ -474,6 +476,35 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = fal
     // next N edges are read into nsrc after this step's gathers are issued
     // (so that the next step's gathers need not wait for them).
     int nsrc[4];
+
+    // Scores held for storing (SC with HS): hn of them from CSR position hp.
+    // The kernel asks for it where the four registers are free; elsewhere
+    // holding them spills (4-36 registers) and each step's scores are stored
+    // at once.
+    static constexpr bool HOLD = SC && HS;
+    float hsc[HOLD ? 4 : 1];
+    int hp = 0, hn = 0;
+    __device__ inline void flush_scores()
+    {
+        if constexpr (HOLD) {
+            if (active && head_lead) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (u < hn) {
+                        // (a store through a buffer resource would hide from
+                        // alias analysis that csr_src is never written, and
+                        // turn its uniform scalar loads into vector loads)
+                        if constexpr (W32)
+                            a.scores[(uint32_t)(hp + u) * sc_edge + sc_lane] = hsc[u];
+                        else
+                            a.scores[(((int64_t)(hp + u)) * B + b) * a.H + h] = hsc[u];
+                    }
+                }
+            }
+            hn = 0;
+        }
+    }
+
     template <int N, bool PRE = false> __device__ inline void step(int p, const int *csrc = nullptr)
     {
         // mask words first, as uniform (scalar) loads in flight with the
@@ -546,12 +577,20 @@ template <typename T, int CH, int LPH, bool W32, bool SC, int KPM, bool HT = fal
                     sc[u] = -INFINITY;
             }
         }
-        if (SC && active && head_lead) {
+        if constexpr (HOLD) {
+            // The previous step's scores go out now that this step's gathers
+            // are issued (vector memory operations complete in order: stored
+            // before them, they would hold back their use; bipartite edge
+            // kernel 347 -> 341 us); this step's are held until the next step
+            // or the end of the piece.
+            flush_scores();
+#pragma unroll
+            for (int u = 0; u < N; ++u) hsc[u] = sc[u];
+            hp = p;
+            hn = N;
+        } else if (SC && active && head_lead) {
 #pragma unroll
             for (int u = 0; u < N; ++u) {
-                // (a store through a buffer resource would hide from alias
-                // analysis that csr_src is never written, and turn its
-                // uniform scalar loads into vector loads)
                 if constexpr (W32)
                     a.scores[(uint32_t)(p + u) * sc_edge + sc_lane] = sc[u];
                 else
@@ -688,7 +727,10 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     if (task >= (uint32_t)a.n_tasks)
         return;
 
-    EdgeLane<T, CH, LPH, W32, SC, KPM, (HOT > 0)> st(a);
+    // (held scores where they compile without spills: fp32, no fused
+    // out_proj, no mask, heads of other than 2 lanes)
+    EdgeLane<T, CH, LPH, W32, SC, KPM, (HOT > 0),
+             (sizeof(T) == 4 && E_FUSE == 0 && KPM == 0 && LPH != 2)> st(a);
     st.src = csr_src;
     st.hl = hlds + lane * 16;
     const int B = a.B, E = a.E;
@@ -791,6 +833,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         if (more)
             qn = load_q(t2);
 
+        st.flush_scores();
         const float m = st.ms, l = st.l;
         if (slot < 0) {
             const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
