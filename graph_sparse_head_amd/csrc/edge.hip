@@ -643,11 +643,13 @@ struct EdgeLane {
 template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, int KPM,
           int HOT = 0>
 __global__ void __launch_bounds__(HOT ? 1024 : 256)
-// (at least 7 wavefronts per SIMD: at most 72 VGPRs. The q-projecting variant
-// needs 68 without spilling, which measured 5 % faster than squeezing it into
-// 64 for 8 wavefronts; the variants without the fused projections fit 64.
-// With the hot-row cache one 16-wavefront workgroup fills a CU's LDS.)
-__attribute__((amdgpu_waves_per_eu(HOT ? 4 : 7)))
+// (at least 7 wavefronts per SIMD: at most 72 VGPRs; the variants without the
+// fused projections fit 64. The q-projecting variant without weights or mask
+// fits 64 for 8 wavefronts once it stops prefetching the next piece's query
+// chunk (below); with its prefetch it had needed 68, and squeezing that into
+// 64 had spilled and run 5 % slower. With the hot-row cache one 16-wavefront
+// workgroup fills a CU's LDS.)
+__attribute__((amdgpu_waves_per_eu(HOT ? 4 : (QF && W32 && !SC && KPM == 0 ? 8 : 7))))
 edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restrict__ task_target,
           const int32_t *__restrict__ task_begin, const int32_t *__restrict__ task_end,
           const int32_t *__restrict__ task_slot, const uint32_t *__restrict__ kpm_csr)
@@ -777,7 +779,12 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     int t = task_target[task];
     int beg = task_begin[task], end = task_end[task];
     int slot = task_slot[task];
-    uint4 qn = load_q(t);
+    // The next piece's query chunk is requested while this one runs, except
+    // in the q-projecting kernel without weights or mask (32-bit offsets): there the four
+    // registers it holds are what 8 wavefronts per SIMD need (63 registers,
+    // no spills, against 72 and 7; gene edge kernel 128.5 -> 126.8 us).
+    constexpr bool LEAN = QF && W32 && !SC && KPM == 0 && HOT == 0;
+    uint4 qn = LEAN ? make_uint4(0, 0, 0, 0) : load_q(t);
     for (;;) {
         // The next piece's bounds and query chunk are requested while this
         // one runs (wave-uniform branch).
@@ -790,10 +797,14 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
             end2 = task_end[nxt];
             slot2 = task_slot[nxt];
         }
-        if constexpr (QF)
+        if constexpr (LEAN) {
+            qn = load_q(t);
             st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
-        else
+        } else if constexpr (QF) {
+            st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
+        } else {
             st.q.u = qn;
+        }
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
             for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
@@ -830,7 +841,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         }
         if (p < end)
             st.template step<1>(p);
-        if (more)
+        if (!LEAN && more)
             qn = load_q(t2);
 
         st.flush_scores();
