@@ -162,9 +162,10 @@ __device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uin
 // (kpm_csr); otherwise each lane looks its bit up by source.
 // bf16 plans keep q and dm packed and form the dot products with v_dot2.
 // PF: the next kU edges' rows are requested before the current ones are
-// used (twice the row registers); otherwise each step loads, then uses.
+// used (twice the row registers); otherwise each step loads, then uses (at
+// most 80 registers: 6 wavefronts per SIMD).
 template <typename T, int LPH, bool UNI, bool CM = false, bool PF = true>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PF ? 1 : 7)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PF ? 1 : 6)))
 bwd_target_fast(const BwdArgs a)
 {
     constexpr int VEC = Vec<T>::N;
@@ -254,17 +255,16 @@ bwd_target_fast(const BwdArgs a)
             vq[u] = ld16(Vb + (int64_t)r[u] * a.E);
         }
     };
-    // With PF a step's (p, dz) pairs are stored after the next step's loads
-    // are issued: vector memory operations complete in order, so a store
-    // issued before those loads would hold back their use until it is
-    // acknowledged (bipartite step 1.83 -> 1.81 ms). Without PF the held
-    // pairs would cost registers the variant does not have (7 spills, 100k-
-    // node step 5.93 -> 6.03 ms): each edge's pair is stored at once.
+    // A step's (p, dz) pairs are stored after the next step's loads are
+    // issued: vector memory operations complete in order, so a store issued
+    // before those loads would hold back their use until it is acknowledged
+    // (bipartite step 1.83 -> 1.81 ms; without PF, at 6 wavefronts per SIMD
+    // so that the held pairs do not spill, 100k-node step 5.94 -> 5.91 ms).
     typedef typename PZRaw<T>::type PZT;
     PZT pzs[kU];
     int pz0 = -1;   // first position of the held pairs (wave-uniform), -1: none
     auto flush = [&]() {
-        if (PF && pz0 >= 0 && lead) {
+        if (pz0 >= 0 && lead) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if (pz0 + u < end)
@@ -326,10 +326,7 @@ bwd_target_fast(const BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
                     dq[i] = fmaf(dz, kk[i], dq[i]);
-                if constexpr (!PF) {
-                    if (lead)
-                        put_pz<T>(a.PZ, ((int64_t)p * a.B + b) * a.H + h, pe, dz);
-                } else if constexpr (sizeof(T) == 2) {
+                if constexpr (sizeof(T) == 2) {
                     pzs[u] = pack_bf16(pe, dz);
                 } else {
                     pzs[u] = make_float2(pe, dz);
