@@ -13,18 +13,22 @@
 //   dv_h[s] = sum over edges e out of s of p_e dm_h[t_e].
 // The weights p_e are recomputed from the forward's saved (max, sum) per
 // (target, sample, head), in base 2 as the forward computed them. A first
-// pass walks each target's edges (dq, and p_e, dz_e per edge); a second walks
-// each source's edges through the source-major index (dk, dv), so neither
-// needs atomics. Long edge lists are cut into pieces whose partial sums a
+// pass walks each target's edges (dq); a second walks each source's edges
+// through the source-major index (dk, dv), so neither needs atomics. The
+// second needs p_e and dz_e again: with 16-byte lanes it recomputes them from
+// the target's q and dm rows and a per-(target, sample, head) pair
+// (m + log2 l, D) the first pass leaves; the per-channel path stores them per
+// edge instead. Long edge lists are cut into pieces whose partial sums a
 // merge adds up in a fixed order. Masked keys have p = dz = 0.
 //
 // The linear maps around it: for y = x W^T + b, dx = dy W (rowmm below) and
 // dW = dy^T x, db = column sums of dy (wgrad below), both on the matrix cores.
 //
 // Layouts (batch-first, plan dtype T unless noted): q, mixed, dm, dq (B, L, E);
-// k, v, dk, dv (B, S, E); ml [L][B][H][2] fp32; (p, dz) pairs [nnz][B][H] by
-// target-grouped position (bf16 pairs for bf16 plans, fp32 pairs otherwise). Gradient tensors are stored in T and accumulated
-// in fp32.
+// k, v, dk, dv (B, S, E); ml and (m + log2 l, D) [L][B][H][2] fp32; on the
+// per-channel path (p, dz) pairs [nnz][B][H] by target-grouped position (bf16
+// pairs for bf16 plans, fp32 pairs otherwise). Gradient tensors are stored in
+// T and accumulated in fp32.
 #include "pma_internal.h"
 
 #include <algorithm>
@@ -97,9 +101,9 @@ __device__ inline bool masked(const BwdArgs &a, int s, int b)
            ((a.kpm_bits[(int64_t)s * a.kpm_words + (b >> 6)] >> (b & 63)) & 1u);
 }
 
-// Per (edge, sample, head): the weight p and the score gradient dz, stored
-// together: a bf16 pair (round to nearest even) for bf16 plans, an fp32 pair
-// otherwise.
+// Per-channel path, per (edge, sample, head): the weight p and the score
+// gradient dz, stored together: a bf16 pair (round to nearest even) for bf16
+// plans, an fp32 pair otherwise.
 template <typename T> __device__ inline void put_pz(void *pz, int64_t o, float p, float dz)
 {
     if constexpr (sizeof(T) == 2)
@@ -116,19 +120,6 @@ template <typename T> __device__ inline float2 get_pz(const void *pz, int64_t o)
         return reinterpret_cast<const float2 *>(pz)[o];
     }
 }
-// The stored pair as loaded (bf16 pair or fp32 pair), widened only where it
-// is used, so that a load issued ahead is not waited for at once.
-template <typename T> struct PZRaw {
-    typedef typename std::conditional<sizeof(T) == 2, uint32_t, float2>::type type;
-};
-template <typename T> __device__ inline typename PZRaw<T>::type load_pz(const void *pz, int64_t o)
-{
-    return reinterpret_cast<const typename PZRaw<T>::type *>(pz)[o];
-}
-__device__ inline float pz_p(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float pz_dz(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline float pz_p(float2 v) { return v.x; }
-__device__ inline float pz_dz(float2 v) { return v.y; }
 
 constexpr int kU = 4;   // edges whose rows are loaded together
 
@@ -224,9 +215,17 @@ bwd_target_fast(const BwdArgs a)
     D = group_sum<LPH>(D);
     const float2 ml =
         *reinterpret_cast<const float2 *>(a.ml + (((int64_t)t * a.B + b) * a.H + h) * 2);
+    const bool lead = (c & (LPH - 1)) == 0;
+    // For the source pass, which recomputes each edge's weight and score
+    // gradient: m' = m + log2(l) (weight = exp2(z - m'); +inf when the
+    // target has no live edge, so every weight is 0) and D. Every piece of a
+    // split target writes the same values.
+    if (lead) {
+        const float mq = ml.y > 0.f ? ml.x + __builtin_amdgcn_logf(ml.y) : INFINITY;
+        *reinterpret_cast<float2 *>(a.mD + (((int64_t)t * a.B + b) * a.H + h) * 2) = make_float2(mq, D);
+    }
     const T *Kb = reinterpret_cast<const T *>(a.k) + (int64_t)b * a.Skv * a.E + c * VEC;
     const T *Vb = reinterpret_cast<const T *>(a.v) + (int64_t)b * a.Skv * a.E + c * VEC;
-    const bool lead = (c & (LPH - 1)) == 0;
     float dq[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
@@ -255,23 +254,6 @@ bwd_target_fast(const BwdArgs a)
             vq[u] = ld16(Vb + (int64_t)r[u] * a.E);
         }
     };
-    // A step's (p, dz) pairs are stored after the next step's loads are
-    // issued: vector memory operations complete in order, so a store issued
-    // before those loads would hold back their use until it is acknowledged
-    // (bipartite step 1.83 -> 1.81 ms; without PF, at 6 wavefronts per SIMD
-    // so that the held pairs do not spill, 100k-node step 5.94 -> 5.91 ms).
-    typedef typename PZRaw<T>::type PZT;
-    PZT pzs[kU];
-    int pz0 = -1;   // first position of the held pairs (wave-uniform), -1: none
-    auto flush = [&]() {
-        if (pz0 >= 0 && lead) {
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                if (pz0 + u < end)
-                    reinterpret_cast<PZT *>(a.PZ)[((int64_t)(pz0 + u) * a.B + b) * a.H + h] = pzs[u];
-            }
-        }
-    };
     if (PF && beg < end)
         fetch(beg, s, kr, vr);
     for (int p0 = beg; p0 < end; p0 += kU) {
@@ -282,7 +264,6 @@ bwd_target_fast(const BwdArgs a)
         } else {
             fetch(p0, s, kr, vr);
         }
-        flush();
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             float kk[VEC];
@@ -326,14 +307,8 @@ bwd_target_fast(const BwdArgs a)
 #pragma unroll
                 for (int i = 0; i < VEC; ++i)
                     dq[i] = fmaf(dz, kk[i], dq[i]);
-                if constexpr (sizeof(T) == 2) {
-                    pzs[u] = pack_bf16(pe, dz);
-                } else {
-                    pzs[u] = make_float2(pe, dz);
-                }
             }
         }
-        pz0 = p0;
         if (more) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
@@ -343,7 +318,6 @@ bwd_target_fast(const BwdArgs a)
             }
         }
     }
-    flush();
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dq[i] *= a.inv_sqrt_d;
@@ -397,38 +371,80 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
     const int s = a.s_source[task], beg = a.s_begin[task], end = a.s_end[task];
     const int slot = a.s_slot[task];
     const int h = c / LPH;
+    constexpr bool BF = sizeof(T) == 2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
     const T *Qb = reinterpret_cast<const T *>(a.q) + (int64_t)b * a.L * a.E + c * VEC;
     const T *Mb = reinterpret_cast<const T *>(a.dm) + (int64_t)b * a.L * a.E + c * VEC;
+    const float *MD = a.mD + (int64_t)b * a.H * 2 + h * 2;   // (m', D) of (t, b, h) at + t B H 2
     float dk[VEC], dv[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i)
         dk[i] = dv[i] = 0.f;
-    typedef typename PZRaw<T>::type PZT;
-    PZT pz[kU], pzn[kU];
+    // The source's own key and value chunks (its saved row through the
+    // compact row index of any of its edges); a key masked for this sample
+    // leaves every one of its edges out (weight and score gradient 0).
+    const bool live = beg < end && !masked(a, s, b);
+    uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
+    if (live) {
+        const int r = a.kv_src[a.csc_pos[beg]];
+        kw = ld16(reinterpret_cast<const T *>(a.k) + ((int64_t)b * a.Skv + r) * a.E + c * VEC);
+        vw = ld16(reinterpret_cast<const T *>(a.v) + ((int64_t)b * a.Skv + r) * a.E + c * VEC);
+    }
+    float kf[BF ? 1 : VEC], vf[BF ? 1 : VEC];
+    if constexpr (!BF) {
+        widen<T>(kw, kf);
+        widen<T>(vw, vf);
+    }
+    float2 md[kU], mdn[kU];
     uint4 qr[kU], mr[kU], qn[kU], mn[kU];
-    auto fetch = [&](int j0, PZT (&pp)[kU], uint4 (&qq)[kU], uint4 (&mm)[kU]) {
-        int t[kU], pos[kU];
+    auto fetch = [&](int j0, float2 (&dd)[kU], uint4 (&qq)[kU], uint4 (&mm)[kU]) {
+        int t[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) t[u] = a.csc_tgt[j0 + u];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            t[u] = a.csc_tgt[j0 + u];
-            pos[u] = a.csc_pos[j0 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t o = ((int64_t)pos[u] * a.B + b) * a.H + h;
-            pp[u] = load_pz<T>(a.PZ, o);
             qq[u] = ld16(Qb + (int64_t)t[u] * a.E);
             mm[u] = ld16(Mb + (int64_t)t[u] * a.E);
+            dd[u] = *reinterpret_cast<const float2 *>(MD + (int64_t)t[u] * a.B * a.H * 2);
         }
     };
+    // per edge: z = q_t . k_s and dp = dm_t . v_s over the head, the weight
+    // p = exp2(z log2(e)/sqrt(d) - m') and dz = p (dp - D), as the target
+    // pass computed them; then dk += dz q_t, dv += p dm_t
     auto batch = [&](int j0, auto full) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            if (decltype(full)::value || j0 + u < end) {
+            float z = 0.f, dp = 0.f;
+            if constexpr (BF) {
+                const uint32_t qa[4] = {qr[u].x, qr[u].y, qr[u].z, qr[u].w};
+                const uint32_t ma[4] = {mr[u].x, mr[u].y, mr[u].z, mr[u].w};
+                const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w};
+                const uint32_t va[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qa[w]),
+                                                        __builtin_bit_cast(bf16x2_t, ka[w]), z, false);
+                    dp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ma[w]),
+                                                         __builtin_bit_cast(bf16x2_t, va[w]), dp, false);
+                }
+            } else {
                 float qq[VEC], mm[VEC];
                 widen<T>(qr[u], qq);
                 widen<T>(mr[u], mm);
-                const float pu = pz_p(pz[u]), du = pz_dz(pz[u]);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    z = fmaf(qq[i], kf[i], z);
+                    dp = fmaf(mm[i], vf[i], dp);
+                }
+            }
+            z = group_sum<LPH>(z);
+            dp = group_sum<LPH>(dp);
+            if (decltype(full)::value || j0 + u < end) {
+                const float pu = live ? __builtin_amdgcn_exp2f(z * a.scale_log2 - md[u].x) : 0.f;
+                const float du = pu * (dp - md[u].y);
+                float qq[VEC], mm[VEC];
+                widen<T>(qr[u], qq);
+                widen<T>(mr[u], mm);
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) {
                     dk[i] = fmaf(du, qq[i], dk[i]);
@@ -437,17 +453,17 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
             }
         }
     };
-    // as in the target pass: the successor is fetched first, the last batch
-    // runs after the loop
-    if (beg < end) {
-        fetch(beg, pz, qr, mr);
+    if (live) {
+        // as in the target pass: the successor is fetched first, the last
+        // batch runs after the loop
+        fetch(beg, md, qr, mr);
         int j0 = beg;
         for (; j0 + kU < end; j0 += kU) {
-            fetch(j0 + kU, pzn, qn, mn);
+            fetch(j0 + kU, mdn, qn, mn);
             batch(j0, std::true_type{});
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                pz[u] = pzn[u];
+                md[u] = mdn[u];
                 qr[u] = qn[u];
                 mr[u] = mn[u];
             }
@@ -1325,17 +1341,26 @@ hipError_t rowmm_e(const RowMM &a, hipStream_t s)
 
 }  // namespace
 
+bool bwd_edges_fast(int64_t E, int64_t H, pma_dtype dt, const void *q, const void *k,
+                    const void *v, const void *mixed)
+{
+    const int64_t d = E / H, es = dt == PMA_BF16 ? 2 : 4, lph = d * es / 16;
+    return (E * es) % 16 == 0 && (d * es) % 16 == 0 &&
+           (lph == 1 || lph == 2 || lph == 4 || lph == 8 || lph == 16) && aligned16(q) &&
+           aligned16(k) && aligned16(v) && aligned16(mixed);
+}
+
 pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s)
 {
     const int d = a.E / a.H;
     if (d > 64)
         return PMA_E_UNSUPPORTED;
-    const int es = dt == PMA_BF16 ? 2 : 4;
-    const int lph = d * es / 16;
-    const bool fast = (a.E * es) % 16 == 0 && (d * es) % 16 == 0 &&
-                      (lph == 1 || lph == 2 || lph == 4 || lph == 8 || lph == 16) &&
-                      aligned16(a.q) && aligned16(a.k) && aligned16(a.v) && aligned16(a.mixed) &&
-                      aligned16(a.dm) && aligned16(a.dq) && aligned16(a.dk) && aligned16(a.dv);
+    // (dm, dq, dk, dv come from the plan's 256-byte aligned scratch)
+    const int lph = d * (dt == PMA_BF16 ? 2 : 4) / 16;
+    const bool fast = bwd_edges_fast(a.E, a.H, dt, a.q, a.k, a.v, a.mixed) && aligned16(a.dm) &&
+                      aligned16(a.dq) && aligned16(a.dk) && aligned16(a.dv);
+    if (fast ? !a.mD : !a.PZ)
+        return PMA_E_ARG;
     auto go = [&](auto tag) {
         using T = decltype(tag);
         if (!fast) {

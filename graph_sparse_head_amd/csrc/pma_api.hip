@@ -1122,14 +1122,22 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
             return fail(st, "%s", err);
     }
 
-    // scratch: dm, dq, dk, dv (plan dtype), per-edge (p, dz) pairs, piece
-    // partials and weight-gradient partials (fp32)
+    // scratch: dm, dq, dk, dv (plan dtype); for the 16-byte edge passes the
+    // per-(target, sample, head) (m + log2 l, D), for the per-channel ones the
+    // per-edge (p, dz) pairs; piece partials and weight-gradient partials (fp32)
     const pma_dtype dt = p->dtype;
     const size_t es = dt == PMA_BF16 ? 2 : 4;
     const int64_t RLr = B * L, RSr = B * S;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t b_dm = up(RLr * E * es), b_dkv = up(RSr * E * es);
-    const size_t b_pz = up((size_t)nnz * B * H * 2 * es);   // (p, dz) pairs
+    const SaveLayout sv0 = save_layout(p, B);
+    const char *sb0 = static_cast<const char *>(save);
+    const int64_t skv0 = train_compact(p) ? p->g.n_kv : S;   // saved key/value rows per sample
+    const bool fast_edges =
+        pma::bwd_edges_fast(E, H, dt, sb0 + sv0.q, sb0 + sv0.k,
+                            sb0 + sv0.k + (size_t)B * skv0 * E * es, sb0 + sv0.mixed);
+    const size_t b_pz = fast_edges ? up((size_t)L * B * H * 2 * 4)     // (m', D)
+                                   : up((size_t)nnz * B * H * 2 * es); // (p, dz) pairs
     const size_t b_piece = up(pma::bwd_piece_scratch(p->g, B, E));
     const size_t b_wg = up(pma::wgrad_scratch(E, 4, RLr > RSr ? RLr : RSr));
     const size_t need = 2 * b_dm + 2 * b_dkv + b_pz + b_piece + b_wg;
@@ -1239,7 +1247,8 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
                             stream));
         a.kpm_csr = p->kpm_csr;
     }
-    a.PZ = PZ;
+    a.PZ = fast_edges ? nullptr : PZ;
+    a.mD = fast_edges ? static_cast<float *>(PZ) : nullptr;
     a.part_q = part;
     a.part_kv = part + (size_t)gd.n_slots * B * E;
     a.dq = dq;

@@ -197,11 +197,16 @@ struct BwdArgs {
     int kpm_words;
     const uint32_t *kpm_csr;         // the mask by CSR position (gather_mask), or nullptr
     int kpm_w32;
-    void *PZ;                        // [nnz][B][H] (p, dz) pairs: bf16 for bf16 plans, fp32 else
+    void *PZ;                        // per-channel path: [nnz][B][H] (p, dz) pairs, bf16 for bf16 plans
+    float *mD;                       // 16-byte path: [L][B][H] (m + log2 l, D) from the target pass
     float *part_q;                   // [target slot][B][E] partial dq
     float *part_kv;                  // [source slot][B][2E] partial dk, dv
     void *dq, *dk, *dv;              // (B, L, E), (B, S, E), (B, S, E), plan dtype
 };
+// Whether the backward's edge passes take the 16-byte kernels (which need no
+// per-edge (p, dz) array) for these sizes and saved tensors.
+bool bwd_edges_fast(int64_t E, int64_t H, pma_dtype dt, const void *q, const void *k,
+                    const void *v, const void *mixed);
 pma_status launch_bwd_edges(const BwdArgs &a, pma_dtype dt, hipStream_t s);
 // fp32 bytes of part_q + part_kv
 size_t bwd_piece_scratch(const GraphDev &g, int64_t B, int64_t E);
