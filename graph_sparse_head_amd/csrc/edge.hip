@@ -86,6 +86,12 @@ struct EdgeK {
     // cached rows (passed as the gather index of that kernel only)
     const int32_t *hot_src, *hot_csr;
     int n_hot;
+    // split targets merged by the edge kernel itself (see edge_fast):
+    // allow_coop where every split target has at most 4 pieces; coop_blocks
+    // leading workgroups of the launch serve them (0: merge launch instead)
+    const int32_t *row_ptr;
+    int allow_coop;
+    uint32_t coop_blocks;
 };
 
 __device__ inline float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -367,6 +373,96 @@ __device__ inline uint4 q_proj_wave(const uint4 &x, int lane, const char *wlds)
         }
     }
     return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// Merge of split target k's pieces for sample group `pass` (kpnn2 page,
+// "Notes" step 3 over the union of the pieces' edges): each piece left its
+// (max, sum) per head and its unnormalised mix in its partial slot; they are
+// combined in slot order against the largest maximum. `staged` is called by
+// every thread once the first PF pieces' partials are requested (merge_fast
+// stages Wo there, so that their memory latency overlaps the staging and its
+// barrier; in the edge kernel Wo is staged already, and holding partials
+// there would raise the register count of the whole kernel). Lanes of an
+// invalid unit return after it.
+template <typename T, int CH, int LPH, int E_FUSE, int PF, typename F>
+__device__ inline void merge_split(const EdgeK &a, uint32_t k, int pass, bool valid, int lane,
+                                   const char *wlds, F &&staged)
+{
+    const int B = a.B, E = a.E, H = a.H;
+    const int cpr = E / CH;
+    const int c = pass * 64 + lane;
+    const bool active = valid && c < B * cpr;
+    const int b = active ? (int)div31(c, a.cpr_m, a.cpr_sh) : 0, cr = c - b * cpr,
+              col = active ? cr * CH : 0;
+    const int h = active ? cr / LPH : 0;
+    const int t = valid ? a.split_target[k] : 0, s0 = valid ? a.split_slot0[k] : 0;
+    const int n = active ? a.split_count[k] : 0;
+    auto ml_at = [&](int j) {
+        return *reinterpret_cast<const float2 *>(a.part_ml + (((int64_t)(s0 + j) * B + b) * H + h) * 2);
+    };
+    auto acc_at = [&](int j) {
+        return reinterpret_cast<const float4 *>(a.part_acc + ((int64_t)(s0 + j) * B + b) * E + col);
+    };
+    float2 pml[PF];
+    float4 pacc[PF][CH / 4];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        if (j < n) {
+            pml[j] = ml_at(j);
+#pragma unroll
+            for (int q = 0; q < CH / 4; ++q) pacc[j][q] = acc_at(j)[q];
+        }
+    }
+    staged();
+    if (!valid)
+        return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (j < n) M = fmaxf(M, pml[j].x);
+    for (int j = PF; j < n; ++j)
+        M = fmaxf(M, ml_at(j).x);
+    float l = 0.f, acc[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) acc[i] = 0.f;
+    // (a piece whose keys are all masked has l = 0 and m = -inf)
+    auto add = [&](const float2 ml, const float4 *v) {
+        const float w = ml.y > 0.f ? fast_exp2(ml.x - M) : 0.f;
+        l = fmaf(ml.y, w, l);
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) {
+            acc[4 * q + 0] = fmaf(v[q].x, w, acc[4 * q + 0]);
+            acc[4 * q + 1] = fmaf(v[q].y, w, acc[4 * q + 1]);
+            acc[4 * q + 2] = fmaf(v[q].z, w, acc[4 * q + 2]);
+            acc[4 * q + 3] = fmaf(v[q].w, w, acc[4 * q + 3]);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (j < n) add(pml[j], pacc[j]);
+    for (int j = PF; j < n; ++j) {
+        float4 v[CH / 4];
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) v[q] = acc_at(j)[q];
+        add(ml_at(j), v);
+    }
+    const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+    float out[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) out[i] = acc[i] * inv;
+    if (active && a.stat_ml && (lane % LPH) == 0) {
+        float *st = a.stat_ml + (((int64_t)t * B + b) * H + h) * 2;
+        st[0] = M;
+        st[1] = l;
+    }
+    if constexpr (E_FUSE > 0) {
+        if (a.fuse_out) {
+            out_proj_wave<T, CH, E_FUSE, false>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+            return;
+        }
+    }
+    if (active)
+        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
 }
 
 // Hot-row cache slot: the 16-byte key chunks of a wavefront's 64 lanes, then
@@ -665,25 +761,40 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     __shared__ __attribute__((aligned(16))) char hlds[HOT > 0 ? HOT * kHotSlot : 16];
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Split targets of at most 4 pieces can be merged here (coop_blocks > 0,
+    // XCD-pinned launches only): the first coop_blocks workgroups each take
+    // one (split target, sample group), wavefront w walks the target's piece
+    // w, and after a workgroup barrier wavefront 0 merges the pieces in slot
+    // order as merge_fast does, so no merge launch follows. Workgroup 8 r + x
+    // serves split target r * xcd_per + x / passes for sample group
+    // x % passes, on the XCDs that the main walk pins that group to; the main
+    // walk numbers its workgroups from coop_blocks (a multiple of 8, so the
+    // XCD of a number is unchanged) and skips the split pieces.
+    const bool coop = HOT == 0 && blockIdx.x < a.coop_blocks;   // workgroup-uniform
+    const uint32_t bid = blockIdx.x - (coop ? 0u : a.coop_blocks);
     // Each wavefront serves one sample group (pass) and walks the pieces
     // task0, task0 + tstride, ... (the host keeps n_tasks * passes below 2^31
     // and makes the wavefront count a multiple of passes).
-    uint32_t task, pass;
-    if (a.xcd_map == 1) {
+    uint32_t task = 0, pass, coop_k = 0;
+    if (coop) {
+        const uint32_t x = bid & 7, xq = div31(x, a.pass_m, a.pass_sh);
+        pass = x - xq * a.passes;
+        coop_k = (bid >> 3) * a.xcd_per + xq;
+    } else if (a.xcd_map == 1) {
         // Workgroups are dealt to the 8 XCDs round-robin; XCD x serves sample
         // group x % passes (passes divides 8), so its L2 caches only that
         // group's key/value rows.
-        const uint32_t x = blockIdx.x & 7, xq = div31(x, a.pass_m, a.pass_sh);
+        const uint32_t x = bid & 7, xq = div31(x, a.pass_m, a.pass_sh);
         pass = x - xq * a.passes;
-        task = ((blockIdx.x >> 3) * a.xcd_per + xq) * WPB + wave;
+        task = ((bid >> 3) * a.xcd_per + xq) * WPB + wave;
     } else if (a.xcd_map == 2) {
         // Sample groups one after another in launch order: the wavefronts in
         // flight read the key/value rows of few groups at a time.
-        const uint32_t w = blockIdx.x * WPB + wave;
+        const uint32_t w = bid * WPB + wave;
         pass = div31(w, a.ts_m, a.ts_sh);
         task = w - pass * a.tstride;
     } else {
-        const uint32_t w = blockIdx.x * WPB + wave;
+        const uint32_t w = bid * WPB + wave;
         task = div31(w, a.pass_m, a.pass_sh);
         pass = w - task * a.passes;
     }
@@ -726,8 +837,8 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     }
     if (HOT > 0 || (E_FUSE > 0 && a.fuse_out))
         __syncthreads();
-    if (task >= (uint32_t)a.n_tasks)
-        return;
+    if (coop ? coop_k >= (uint32_t)a.n_split : task >= (uint32_t)a.n_tasks)
+        return;   // (workgroup-uniform for coop)
 
     // (held scores where they compile without spills: fp32, no fused
     // out_proj, no mask, heads of other than 2 lanes)
@@ -776,9 +887,24 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         return a.nt ? load_nt(qp) : *qp;
     };
 
-    int t = task_target[task];
-    int beg = task_begin[task], end = task_end[task];
-    int slot = task_slot[task];
+    int t, beg, end, slot;
+    bool has_piece = true;
+    if (coop) {
+        // piece `wave` of the split target, cut as the index build cuts it
+        const int cnt = a.split_count[coop_k];
+        t = a.split_target[coop_k];
+        const int64_t r0 = a.row_ptr[t], g = a.row_ptr[t + 1] - r0;
+        has_piece = (int)wave < cnt;
+        const int w = has_piece ? (int)wave : 0;
+        beg = (int)(r0 + ((int64_t)w * g) / cnt);
+        end = (int)(r0 + ((int64_t)(w + 1) * g) / cnt);
+        slot = a.split_slot0[coop_k] + w;
+    } else {
+        t = task_target[task];
+        beg = task_begin[task];
+        end = task_end[task];
+        slot = task_slot[task];
+    }
     // The next piece's query chunk is requested while this one runs, except
     // in the q-projecting kernel without weights or mask (32-bit offsets): there the four
     // registers it holds are what 8 wavefronts per SIMD need (63 registers,
@@ -789,7 +915,9 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         // The next piece's bounds and query chunk are requested while this
         // one runs (wave-uniform branch).
         const uint32_t nxt = task + a.tstride;
-        const bool more = nxt < (uint32_t)a.n_tasks;
+        const bool more = !coop && nxt < (uint32_t)a.n_tasks;
+        // a split piece is the coop workgroups' (wave-uniform)
+        const bool skip = coop ? !has_piece : (a.coop_blocks != 0 && slot >= 0);
         int t2 = 0, beg2 = 0, end2 = 0, slot2 = 0;
         if (more) {
             t2 = task_target[nxt];
@@ -797,98 +925,102 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
             end2 = task_end[nxt];
             slot2 = task_slot[nxt];
         }
-        if constexpr (LEAN) {
-            qn = load_q(t);
-            st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
-        } else if constexpr (QF) {
-            st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
-        } else {
-            st.q.u = qn;
-        }
-        if constexpr (sizeof(T) == 4) {
-#pragma unroll
-            for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
-        }
-#pragma unroll
-        for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
-        st.l = 0.f;
-        st.ms = -INFINITY;
-        st.fresh = true;
-
-        static_assert(U == 4, "the tail below covers up to 3 edges");
-        int p = beg;
-        if constexpr (KPM == 0) {
-            for (; p + U <= end; p += U)
-                st.template step<U>(p);
-        } else if (p + U <= end) {
-            // full steps; each reads the next step's source ids in flight
-            // (measured: pays with the mask's extra scalar loads, costs 2-5 %
-            // without them)
-            int cs[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) cs[u] = csr_src[p + u];
-            for (; p + 2 * U <= end; p += U) {
-                st.template step<U, true>(p, cs);
-#pragma unroll
-                for (int u = 0; u < U; ++u) cs[u] = st.nsrc[u];
+        if (!skip) {
+            if constexpr (LEAN) {
+                qn = load_q(t);
+                st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
+            } else if constexpr (QF) {
+                st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
+            } else {
+                st.q.u = qn;
             }
-            st.template step<U>(p, cs);
-            p += U;
+            if constexpr (sizeof(T) == 4) {
+    #pragma unroll
+                for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
+            }
+    #pragma unroll
+            for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
+            st.l = 0.f;
+            st.ms = -INFINITY;
+            st.fresh = true;
+
+            static_assert(U == 4, "the tail below covers up to 3 edges");
+            int p = beg;
+            if constexpr (KPM == 0) {
+                for (; p + U <= end; p += U)
+                    st.template step<U>(p);
+            } else if (p + U <= end) {
+                // full steps; each reads the next step's source ids in flight
+                // (measured: pays with the mask's extra scalar loads, costs 2-5 %
+                // without them)
+                int cs[U];
+    #pragma unroll
+                for (int u = 0; u < U; ++u) cs[u] = csr_src[p + u];
+                for (; p + 2 * U <= end; p += U) {
+                    st.template step<U, true>(p, cs);
+    #pragma unroll
+                    for (int u = 0; u < U; ++u) cs[u] = st.nsrc[u];
+                }
+                st.template step<U>(p, cs);
+                p += U;
+            }
+            if (p + 2 <= end) {
+                st.template step<2>(p);
+                p += 2;
+            }
+            if (p < end)
+                st.template step<1>(p);
         }
-        if (p + 2 <= end) {
-            st.template step<2>(p);
-            p += 2;
-        }
-        if (p < end)
-            st.template step<1>(p);
         if (!LEAN && more)
             qn = load_q(t2);
 
-        st.flush_scores();
-        const float m = st.ms, l = st.l;
-        if (slot < 0) {
-            const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
-            float out[CH];
-#pragma unroll
-            for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
-            if (a.stat_ml && st.active && st.head_lead) {   // weights or training
-                float *sp = a.stat_ml;
-                if constexpr (W32)
-                    sp += ((uint32_t)t * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
-                else
-                    sp += (((int64_t)t * B + b) * a.H + st.h) * 2;
-                *reinterpret_cast<float2 *>(sp) = make_float2(m, l);
-            }
-            bool done = false;
-            if constexpr (E_FUSE > 0) {
-                if (a.fuse_out) {   // wave-uniform
-                    out_proj_wave<T, CH, E_FUSE, W32>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
-                    done = true;
+        if (!skip) {
+            st.flush_scores();
+            const float m = st.ms, l = st.l;
+            if (slot < 0) {
+                const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+                float out[CH];
+    #pragma unroll
+                for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
+                if (a.stat_ml && st.active && st.head_lead) {   // weights or training
+                    float *sp = a.stat_ml;
+                    if constexpr (W32)
+                        sp += ((uint32_t)t * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
+                    else
+                        sp += (((int64_t)t * B + b) * a.H + st.h) * 2;
+                    *reinterpret_cast<float2 *>(sp) = make_float2(m, l);
                 }
+                bool done = false;
+                if constexpr (E_FUSE > 0) {
+                    if (a.fuse_out) {   // wave-uniform
+                        out_proj_wave<T, CH, E_FUSE, W32>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+                        done = true;
+                    }
+                }
+                if (!done && st.active) {
+                    T *dst = reinterpret_cast<T *>(a.mixed);
+                    if constexpr (W32)
+                        dst += (uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col;
+                    else
+                        dst += t * a.lay.m_t + b * a.lay.m_b + col;
+                    store_chunk<T, CH>(dst, out, a.nt != 0);
+                }
+            } else if (st.active) {
+                float *pa = a.part_acc, *pm = a.part_ml;
+                if constexpr (W32) {
+                    pa += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)E + col;
+                    pm += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
+                } else {
+                    pa += ((int64_t)slot * B + b) * E + col;
+                    pm += (((int64_t)slot * B + b) * a.H + st.h) * 2;
+                }
+                *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
+                if constexpr (CH == 8)
+                    *reinterpret_cast<float4 *>(pa + 4) =
+                        make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
+                if (st.head_lead)
+                    *reinterpret_cast<float2 *>(pm) = make_float2(m, l);
             }
-            if (!done && st.active) {
-                T *dst = reinterpret_cast<T *>(a.mixed);
-                if constexpr (W32)
-                    dst += (uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col;
-                else
-                    dst += t * a.lay.m_t + b * a.lay.m_b + col;
-                store_chunk<T, CH>(dst, out, a.nt != 0);
-            }
-        } else if (st.active) {
-            float *pa = a.part_acc, *pm = a.part_ml;
-            if constexpr (W32) {
-                pa += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)E + col;
-                pm += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
-            } else {
-                pa += ((int64_t)slot * B + b) * E + col;
-                pm += (((int64_t)slot * B + b) * a.H + st.h) * 2;
-            }
-            *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
-            if constexpr (CH == 8)
-                *reinterpret_cast<float4 *>(pa + 4) =
-                    make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
-            if (st.head_lead)
-                *reinterpret_cast<float2 *>(pm) = make_float2(m, l);
         }
         if (!more)
             break;
@@ -897,6 +1029,16 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         beg = beg2;
         end = end2;
         slot = slot2;
+    }
+    if constexpr (HOT == 0) {
+        if (coop) {
+            // every wavefront of the workgroup gets here (no return since the
+            // uniform one above); the barrier orders the pieces' partial
+            // stores before wavefront 0 reads them back
+            __syncthreads();
+            if (wave == 0)
+                merge_split<T, CH, LPH, E_FUSE, 1>(a, coop_k, (int)pass, true, lane, wlds, [] {});
+        }
     }
 }
 
@@ -1051,6 +1193,8 @@ __global__ void __launch_bounds__(256) edge_generic(EdgeK a)
 
 // Merge the pieces of each split target, in piece order. Same lane layout
 // as edge_fast: one wavefront per (split target, sample group).
+// The merge as a launch of its own: one wavefront per (split target, sample
+// group).
 template <typename T, int CH, int LPH, int E_FUSE>
 __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
 {
@@ -1060,89 +1204,14 @@ __global__ void __launch_bounds__(256) merge_fast(EdgeK a)
     const bool valid = unit < (uint32_t)(a.n_split * a.passes);
     const uint32_t k = valid ? div31(unit, a.pass_m, a.pass_sh) : 0;
     const int pass = (int)(unit - k * a.passes);
-    const int B = a.B, E = a.E, H = a.H;
-    const int cpr = E / CH;
-    const int c = pass * 64 + lane;
-    const bool active = valid && c < B * cpr;
-    const int b = active ? (int)div31(c, a.cpr_m, a.cpr_sh) : 0, cr = c - b * cpr,
-              col = active ? cr * CH : 0;
-    const int h = active ? cr / LPH : 0;
-    const int t = valid ? a.split_target[k] : 0, s0 = valid ? a.split_slot0[k] : 0;
-    const int n = active ? a.split_count[k] : 0;
-    // The partials of the first PF pieces are requested before Wo is staged,
-    // so that their memory latency overlaps the staging and its barrier.
-    constexpr int PF = 4;
-    auto ml_at = [&](int j) {
-        return *reinterpret_cast<const float2 *>(a.part_ml + (((int64_t)(s0 + j) * B + b) * H + h) * 2);
-    };
-    auto acc_at = [&](int j) {
-        return reinterpret_cast<const float4 *>(a.part_acc + ((int64_t)(s0 + j) * B + b) * E + col);
-    };
-    float2 pml[PF];
-    float4 pacc[PF][CH / 4];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-        if (j < n) {
-            pml[j] = ml_at(j);
-#pragma unroll
-            for (int q = 0; q < CH / 4; ++q) pacc[j][q] = acc_at(j)[q];
+    merge_split<T, CH, LPH, E_FUSE, 4>(a, k, pass, valid, lane, wlds, [&]() {
+        if constexpr (E_FUSE > 0) {
+            if (a.fuse_out) {   // (every wavefront of the workgroup takes part)
+                stage_wo<T, CH, E_FUSE>(a, wlds);
+                __syncthreads();
+            }
         }
-    }
-    if constexpr (E_FUSE > 0) {
-        if (a.fuse_out) {   // (every wavefront of the workgroup takes part)
-            stage_wo<T, CH, E_FUSE>(a, wlds);
-            __syncthreads();
-        }
-    }
-    if (!valid)
-        return;
-    float M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < PF; ++j)
-        if (j < n) M = fmaxf(M, pml[j].x);
-    for (int j = PF; j < n; ++j)
-        M = fmaxf(M, ml_at(j).x);
-    float l = 0.f, acc[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) acc[i] = 0.f;
-    // (a piece whose keys are all masked has l = 0 and m = -inf)
-    auto add = [&](const float2 ml, const float4 *v) {
-        const float w = ml.y > 0.f ? fast_exp2(ml.x - M) : 0.f;
-        l = fmaf(ml.y, w, l);
-#pragma unroll
-        for (int q = 0; q < CH / 4; ++q) {
-            acc[4 * q + 0] = fmaf(v[q].x, w, acc[4 * q + 0]);
-            acc[4 * q + 1] = fmaf(v[q].y, w, acc[4 * q + 1]);
-            acc[4 * q + 2] = fmaf(v[q].z, w, acc[4 * q + 2]);
-            acc[4 * q + 3] = fmaf(v[q].w, w, acc[4 * q + 3]);
-        }
-    };
-#pragma unroll
-    for (int j = 0; j < PF; ++j)
-        if (j < n) add(pml[j], pacc[j]);
-    for (int j = PF; j < n; ++j) {
-        float4 v[CH / 4];
-#pragma unroll
-        for (int q = 0; q < CH / 4; ++q) v[q] = acc_at(j)[q];
-        add(ml_at(j), v);
-    }
-    const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
-    float out[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) out[i] = acc[i] * inv;
-    if (active && a.stat_ml && (lane % LPH) == 0) {
-        float *st = a.stat_ml + (((int64_t)t * B + b) * H + h) * 2;
-        st[0] = M;
-        st[1] = l;
-    }
-    if constexpr (E_FUSE > 0) {
-        if (a.fuse_out) {
-            out_proj_wave<T, CH, E_FUSE, false>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
-            return;
-        }
-    }
-    if (active)
-        store_chunk<T, CH>(reinterpret_cast<T *>(a.mixed) + t * a.lay.m_t + b * a.lay.m_b + col, out);
+    });
 }
 
 // Any head size: one thread per (split target, sample, channel).
@@ -1397,7 +1466,18 @@ EdgeK make_k(const EdgeArgs &x)
     k.hot_src = x.hot_src;
     k.hot_csr = x.hot_csr;
     k.n_hot = x.hot_csr && x.hot_src ? x.n_hot : 0;
+    k.row_ptr = g->row_ptr;
+    k.allow_coop = x.coop && x.max_pieces <= 4 && !x.hot_csr;
+    k.coop_blocks = 0;
     return k;
+}
+
+// Whether a launch of edge_fast with these (passes set) merges the split
+// targets itself: each has at most 4 pieces and the sample groups are pinned
+// to XCDs.
+bool coop_merge(const EdgeK &k)
+{
+    return k.allow_coop && k.n_split > 0 && k.xcd_map == 1 && 8 % k.passes == 0;
 }
 
 int cu_count()
@@ -1463,7 +1543,11 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     const int wpb = hot ? 16 : 4;
     const int64_t cap = hot ? (int64_t)cu_count()
                             : persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
-    const unsigned nb = (unsigned)edge_grid(k, wpb, cap);
+    unsigned nb = (unsigned)edge_grid(k, wpb, cap);
+    if (!hot && coop_merge(k)) {   // (edge_grid keeps xcd_map 1 only where pinned)
+        k.coop_blocks = (uint32_t)(8 * ((k.n_split + k.xcd_per - 1) / k.xcd_per));
+        nb += k.coop_blocks;
+    }
     if constexpr (QF) {
         if (hot) {
             edge_fast<T, CH, LPH, 4, E_FUSE, QF, true, false, 0, kHot><<<nb, 1024, 0, s>>>(
@@ -1699,6 +1783,19 @@ Layout make_layout(bool batch_first, int64_t B, int64_t L, int64_t S, int64_t E)
         y.m_b = E;
     }
     return y;
+}
+
+bool edge_merges_splits(const EdgeArgs &x)
+{
+    EdgeK k = make_k(x);
+    const int ch = x.dt == PMA_BF16 ? 8 : 4;
+    if (k.d % ch != 0)
+        return false;   // the per-channel kernel: merge launch
+    const int lph = k.d / ch;
+    if (lph > 16 || (lph & (lph - 1)) != 0)
+        return false;
+    set_passes(k, ch);
+    return coop_merge(k);
 }
 
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)

@@ -72,6 +72,7 @@ struct pma_plan {
     int persist = -1;           // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece, -1 auto)
     int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
     bool hot = false;           // PMA_HOT=1: hot-row cache in the q-projecting edge kernel
+    int coop = 1;               // PMA_COOP=0: split targets merged by a launch of their own
     // hot-row cache: the gather index (hot_key) with ~slot for the edges of
     // the n_hot most-read rows hot_src[slot]
     int32_t *hot_csr = nullptr, *hot_src = nullptr;
@@ -389,6 +390,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_BWD_SORDER 0: banded source pass with its sample groups
     //                  interleaved instead of in turn within each band
     //   PMA_HOT        1: hot-row LDS cache in the q-projecting edge kernel
+    //   PMA_COOP       0: merge split targets in a launch of their own instead
+    //                  of in the edge kernel's leading workgroups
     // Piece length: a target is split only when it has far more edges than
     // the average target (16x, rounded up to a power of two, at least 256).
     // Splitting balances graphs with a few very long rows among many short
@@ -427,6 +430,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         p->fuse_out = ev[0] != '0';
     if (const char *ev = getenv("PMA_HOT"))
         p->hot = ev[0] == '1';
+    if (const char *ev = getenv("PMA_COOP"))
+        p->coop = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_FUSE_IN"))
         p->fuse_in = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
@@ -906,6 +911,8 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     ea.fuse_in = fuse_in;
     ea.wq = q_w;
     ea.bq = q_b;
+    ea.coop = p->coop;
+    ea.max_pieces = p->g.max_degree > p->chunk ? (int)((p->g.max_degree + p->chunk - 1) / p->chunk) : 1;
     // Sample groups (wavefronts of 64 lanes over a target's B rows) and
     // XCDs: pinning each group to 8 / groups XCDs (where the group count
     // divides 8) gives each L2 the rows of one group only, which multiplies
@@ -945,7 +952,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
         p->probe_ea = ea;
         p->probe_ok = true;
     }
-    if (st == PMA_OK && p->g.n_split > 0) {
+    if (st == PMA_OK && p->g.n_split > 0 && !pma::edge_merges_splits(ea)) {
         tm.begin(PMA_STAGE_MERGE);
         st = pma::launch_merge(ea, stream);
         tm.end();

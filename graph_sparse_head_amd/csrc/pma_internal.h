@@ -145,6 +145,10 @@ struct EdgeArgs {
     // the edges of the n_hot rows hot_src[slot] (nullptr: no cache)
     const int32_t *hot_csr = nullptr, *hot_src = nullptr;
     int n_hot = 0;
+    // split targets merged inside the edge kernel where each has at most 4
+    // pieces (max_pieces: the most pieces of one target; see edge_fast)
+    int coop = 1;
+    int max_pieces = 0;
 };
 
 // Whether edge_fast / merge_fast can apply out_proj themselves.
@@ -293,6 +297,8 @@ pma_status launch_merge(const EdgeArgs &a, hipStream_t s);
 // PMA_E_UNSUPPORTED where the 16-byte kernel does not serve the head size or
 // a tensor is 2 GiB or more.
 pma_status launch_gather_probe(const EdgeArgs &a, hipStream_t s);
+// Whether launch_edge merges the split targets itself (then no launch_merge).
+bool edge_merges_splits(const EdgeArgs &a);
 // Calibration: n 1 KB row gathers from a table (pma_gather_ceiling).
 pma_status launch_gather_ceiling(const void *table, uint64_t table_bytes, const int32_t *rows,
                                  int64_t n, int64_t per, void *sink, hipStream_t s);
