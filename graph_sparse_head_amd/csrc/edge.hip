@@ -737,7 +737,7 @@ struct EdgeLane {
 };
 
 template <typename T, int CH, int LPH, int U, int E_FUSE, bool QF, bool W32, bool SC, int KPM,
-          int HOT = 0>
+          int HOT = 0, bool COOP = false>
 __global__ void __launch_bounds__(HOT ? 1024 : 256)
 // (at least 7 wavefronts per SIMD: at most 72 VGPRs; the variants without the
 // fused projections fit 64. The q-projecting variant without weights or mask
@@ -755,13 +755,14 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     static_assert(!QF || E_FUSE > 0, "the q prologue comes with the out_proj epilogue");
     static_assert(HOT == 0 || (QF && W32 && !SC && KPM == 0 && CH * sizeof(T) == 16),
                   "the hot-row cache serves the unmasked q-projecting kernel");
+    static_assert(!COOP || (HOT == 0 && KPM == 0), "split targets merged here without a mask");
     constexpr int WPB = HOT ? 16 : 4;   // wavefronts per workgroup
     constexpr int WB = E_FUSE > 0 ? staged_bytes<T, E_FUSE>() : 16;
     __shared__ __attribute__((aligned(16))) char wlds[QF ? 2 * WB : WB];
     __shared__ __attribute__((aligned(16))) char hlds[HOT > 0 ? HOT * kHotSlot : 16];
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Split targets of at most 4 pieces can be merged here (coop_blocks > 0,
+    // Split targets of at most 4 pieces can be merged here (COOP variants,
     // XCD-pinned launches only): the first coop_blocks workgroups each take
     // one (split target, sample group), wavefront w walks the target's piece
     // w, and after a workgroup barrier wavefront 0 merges the pieces in slot
@@ -770,8 +771,8 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
     // x % passes, on the XCDs that the main walk pins that group to; the main
     // walk numbers its workgroups from coop_blocks (a multiple of 8, so the
     // XCD of a number is unchanged) and skips the split pieces.
-    const bool coop = HOT == 0 && blockIdx.x < a.coop_blocks;   // workgroup-uniform
-    const uint32_t bid = blockIdx.x - (coop ? 0u : a.coop_blocks);
+    const bool coop = COOP && blockIdx.x < a.coop_blocks;   // workgroup-uniform
+    const uint32_t bid = COOP && !coop ? blockIdx.x - a.coop_blocks : blockIdx.x;
     // Each wavefront serves one sample group (pass) and walks the pieces
     // task0, task0 + tstride, ... (the host keeps n_tasks * passes below 2^31
     // and makes the wavefront count a multiple of passes).
@@ -887,37 +888,139 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         return a.nt ? load_nt(qp) : *qp;
     };
 
-    int t, beg, end, slot;
-    bool has_piece = true;
-    if (coop) {
-        // piece `wave` of the split target, cut as the index build cuts it
-        const int cnt = a.split_count[coop_k];
-        t = a.split_target[coop_k];
-        const int64_t r0 = a.row_ptr[t], g = a.row_ptr[t + 1] - r0;
-        has_piece = (int)wave < cnt;
-        const int w = has_piece ? (int)wave : 0;
-        beg = (int)(r0 + ((int64_t)w * g) / cnt);
-        end = (int)(r0 + ((int64_t)(w + 1) * g) / cnt);
-        slot = a.split_slot0[coop_k] + w;
-    } else {
-        t = task_target[task];
-        beg = task_begin[task];
-        end = task_end[task];
-        slot = task_slot[task];
-    }
     // The next piece's query chunk is requested while this one runs, except
     // in the q-projecting kernel without weights or mask (32-bit offsets): there the four
     // registers it holds are what 8 wavefronts per SIMD need (63 registers,
     // no spills, against 72 and 7; gene edge kernel 128.5 -> 126.8 us).
     constexpr bool LEAN = QF && W32 && !SC && KPM == 0 && HOT == 0;
-    uint4 qn = LEAN ? make_uint4(0, 0, 0, 0) : load_q(t);
+    uint4 qn = make_uint4(0, 0, 0, 0);
+    // One piece of target t: its q (projected here with QF), the walk over
+    // its edges, then its output row or, for a piece of a split target, its
+    // partial; `mid` runs between the walk and the output.
+    auto piece = [&](const int t, const int beg, const int end, const int slot, auto &&mid) {
+        if constexpr (LEAN) {
+            qn = load_q(t);
+            st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
+        } else if constexpr (QF) {
+            st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
+        } else {
+            st.q.u = qn;
+        }
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
+        st.l = 0.f;
+        st.ms = -INFINITY;
+        st.fresh = true;
+
+        static_assert(U == 4, "the tail below covers up to 3 edges");
+        int p = beg;
+        if constexpr (KPM == 0) {
+            for (; p + U <= end; p += U)
+                st.template step<U>(p);
+        } else if (p + U <= end) {
+            // full steps; each reads the next step's source ids in flight
+            // (measured: pays with the mask's extra scalar loads, costs 2-5 %
+            // without them)
+            int cs[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) cs[u] = csr_src[p + u];
+            for (; p + 2 * U <= end; p += U) {
+                st.template step<U, true>(p, cs);
+#pragma unroll
+                for (int u = 0; u < U; ++u) cs[u] = st.nsrc[u];
+            }
+            st.template step<U>(p, cs);
+            p += U;
+        }
+        if (p + 2 <= end) {
+            st.template step<2>(p);
+            p += 2;
+        }
+        if (p < end)
+            st.template step<1>(p);
+        mid();
+        st.flush_scores();
+        const float m = st.ms, l = st.l;
+        if (slot < 0) {
+            const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+            float out[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
+            if (a.stat_ml && st.active && st.head_lead) {   // weights or training
+                float *sp = a.stat_ml;
+                if constexpr (W32)
+                    sp += ((uint32_t)t * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
+                else
+                    sp += (((int64_t)t * B + b) * a.H + st.h) * 2;
+                *reinterpret_cast<float2 *>(sp) = make_float2(m, l);
+            }
+            bool done = false;
+            if constexpr (E_FUSE > 0) {
+                if (a.fuse_out) {   // wave-uniform
+                    out_proj_wave<T, CH, E_FUSE, W32>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
+                    done = true;
+                }
+            }
+            if (!done && st.active) {
+                T *dst = reinterpret_cast<T *>(a.mixed);
+                if constexpr (W32)
+                    dst += (uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col;
+                else
+                    dst += t * a.lay.m_t + b * a.lay.m_b + col;
+                store_chunk<T, CH>(dst, out, a.nt != 0);
+            }
+        } else if (st.active) {
+            float *pa = a.part_acc, *pm = a.part_ml;
+            if constexpr (W32) {
+                pa += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)E + col;
+                pm += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
+            } else {
+                pa += ((int64_t)slot * B + b) * E + col;
+                pm += (((int64_t)slot * B + b) * a.H + st.h) * 2;
+            }
+            *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
+            if constexpr (CH == 8)
+                *reinterpret_cast<float4 *>(pa + 4) =
+                    make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
+            if (st.head_lead)
+                *reinterpret_cast<float2 *>(pm) = make_float2(m, l);
+        }
+    };
+    if constexpr (COOP) {
+        if (coop) {
+            // piece `wave` of the split target, cut as the index build cuts it
+            const int cnt = a.split_count[coop_k];
+            if ((int)wave < cnt) {   // wave-uniform
+                const int t = a.split_target[coop_k];
+                const int64_t r0 = a.row_ptr[t], g = a.row_ptr[t + 1] - r0;
+                const int beg = (int)(r0 + ((int64_t)wave * g) / cnt);
+                const int end = (int)(r0 + ((int64_t)(wave + 1) * g) / cnt);
+                if constexpr (!LEAN)
+                    qn = load_q(t);
+                piece(t, beg, end, a.split_slot0[coop_k] + (int)wave, [] {});
+            }
+            // every wavefront of the workgroup gets here; the barrier orders
+            // the pieces' partial stores before wavefront 0 reads them back
+            __syncthreads();
+            if (wave == 0)
+                merge_split<T, CH, LPH, E_FUSE, 1>(a, coop_k, (int)pass, true, lane, wlds, [] {});
+            return;
+        }
+    }
+    int t = task_target[task];
+    int beg = task_begin[task], end = task_end[task];
+    int slot = task_slot[task];
+    if constexpr (!LEAN)
+        qn = load_q(t);
     for (;;) {
         // The next piece's bounds and query chunk are requested while this
         // one runs (wave-uniform branch).
         const uint32_t nxt = task + a.tstride;
-        const bool more = !coop && nxt < (uint32_t)a.n_tasks;
-        // a split piece is the coop workgroups' (wave-uniform)
-        const bool skip = coop ? !has_piece : (a.coop_blocks != 0 && slot >= 0);
+        const bool more = nxt < (uint32_t)a.n_tasks;
         int t2 = 0, beg2 = 0, end2 = 0, slot2 = 0;
         if (more) {
             t2 = task_target[nxt];
@@ -925,103 +1028,14 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
             end2 = task_end[nxt];
             slot2 = task_slot[nxt];
         }
-        if (!skip) {
-            if constexpr (LEAN) {
-                qn = load_q(t);
-                st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
-            } else if constexpr (QF) {
-                st.q.u = q_proj_wave<T, CH, E_FUSE>(qn, lane, wlds + WB);
-            } else {
-                st.q.u = qn;
-            }
-            if constexpr (sizeof(T) == 4) {
-    #pragma unroll
-                for (int i = 0; i < CH; ++i) st.qf[i] = st.q[i] * a.scale;
-            }
-    #pragma unroll
-            for (int i = 0; i < CH; ++i) st.acc[i] = 0.f;
-            st.l = 0.f;
-            st.ms = -INFINITY;
-            st.fresh = true;
-
-            static_assert(U == 4, "the tail below covers up to 3 edges");
-            int p = beg;
-            if constexpr (KPM == 0) {
-                for (; p + U <= end; p += U)
-                    st.template step<U>(p);
-            } else if (p + U <= end) {
-                // full steps; each reads the next step's source ids in flight
-                // (measured: pays with the mask's extra scalar loads, costs 2-5 %
-                // without them)
-                int cs[U];
-    #pragma unroll
-                for (int u = 0; u < U; ++u) cs[u] = csr_src[p + u];
-                for (; p + 2 * U <= end; p += U) {
-                    st.template step<U, true>(p, cs);
-    #pragma unroll
-                    for (int u = 0; u < U; ++u) cs[u] = st.nsrc[u];
-                }
-                st.template step<U>(p, cs);
-                p += U;
-            }
-            if (p + 2 <= end) {
-                st.template step<2>(p);
-                p += 2;
-            }
-            if (p < end)
-                st.template step<1>(p);
-        }
-        if (!LEAN && more)
-            qn = load_q(t2);
-
-        if (!skip) {
-            st.flush_scores();
-            const float m = st.ms, l = st.l;
-            if (slot < 0) {
-                const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
-                float out[CH];
-    #pragma unroll
-                for (int i = 0; i < CH; ++i) out[i] = st.acc[i] * inv;
-                if (a.stat_ml && st.active && st.head_lead) {   // weights or training
-                    float *sp = a.stat_ml;
-                    if constexpr (W32)
-                        sp += ((uint32_t)t * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
-                    else
-                        sp += (((int64_t)t * B + b) * a.H + st.h) * 2;
-                    *reinterpret_cast<float2 *>(sp) = make_float2(m, l);
-                }
-                bool done = false;
-                if constexpr (E_FUSE > 0) {
-                    if (a.fuse_out) {   // wave-uniform
-                        out_proj_wave<T, CH, E_FUSE, W32>(a, out, lane, t, pass * (64 / (E_FUSE / CH)), wlds);
-                        done = true;
-                    }
-                }
-                if (!done && st.active) {
-                    T *dst = reinterpret_cast<T *>(a.mixed);
-                    if constexpr (W32)
-                        dst += (uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col;
-                    else
-                        dst += t * a.lay.m_t + b * a.lay.m_b + col;
-                    store_chunk<T, CH>(dst, out, a.nt != 0);
-                }
-            } else if (st.active) {
-                float *pa = a.part_acc, *pm = a.part_ml;
-                if constexpr (W32) {
-                    pa += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)E + col;
-                    pm += ((uint32_t)slot * (uint32_t)B + (uint32_t)b) * (uint32_t)(2 * a.H) + 2 * st.h;
-                } else {
-                    pa += ((int64_t)slot * B + b) * E + col;
-                    pm += (((int64_t)slot * B + b) * a.H + st.h) * 2;
-                }
-                *reinterpret_cast<float4 *>(pa) = make_float4(st.acc[0], st.acc[1], st.acc[2], st.acc[3]);
-                if constexpr (CH == 8)
-                    *reinterpret_cast<float4 *>(pa + 4) =
-                        make_float4(st.acc[4], st.acc[5], st.acc[6], st.acc[7]);
-                if (st.head_lead)
-                    *reinterpret_cast<float2 *>(pm) = make_float2(m, l);
-            }
-        }
+        auto next_q = [&] {
+            if (!LEAN && more)
+                qn = load_q(t2);
+        };
+        if (!COOP || slot < 0)   // (split pieces are the coop workgroups')
+            piece(t, beg, end, slot, next_q);
+        else
+            next_q();
         if (!more)
             break;
         task = nxt;
@@ -1029,16 +1043,6 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         beg = beg2;
         end = end2;
         slot = slot2;
-    }
-    if constexpr (HOT == 0) {
-        if (coop) {
-            // every wavefront of the workgroup gets here (no return since the
-            // uniform one above); the barrier orders the pieces' partial
-            // stores before wavefront 0 reads them back
-            __syncthreads();
-            if (wave == 0)
-                merge_split<T, CH, LPH, E_FUSE, 1>(a, coop_k, (int)pass, true, lane, wlds, [] {});
-        }
     }
 }
 
@@ -1473,11 +1477,11 @@ EdgeK make_k(const EdgeArgs &x)
 }
 
 // Whether a launch of edge_fast with these (passes set) merges the split
-// targets itself: each has at most 4 pieces and the sample groups are pinned
-// to XCDs.
+// targets itself: each has at most 4 pieces, the sample groups are pinned to
+// XCDs and there is no mask (the launch also needs 32-bit offsets).
 bool coop_merge(const EdgeK &k)
 {
-    return k.allow_coop && k.n_split > 0 && k.xcd_map == 1 && 8 % k.passes == 0;
+    return k.allow_coop && k.n_split > 0 && k.xcd_map == 1 && 8 % k.passes == 0 && !k.kpm_bits;
 }
 
 int cu_count()
@@ -1544,7 +1548,7 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
     const int64_t cap = hot ? (int64_t)cu_count()
                             : persist > 0 ? (int64_t)cu_count() * persist : ((int64_t)1 << 40);
     unsigned nb = (unsigned)edge_grid(k, wpb, cap);
-    if (!hot && coop_merge(k)) {   // (edge_grid keeps xcd_map 1 only where pinned)
+    if (!hot && w32 && coop_merge(k)) {   // (edge_grid keeps xcd_map 1 only where pinned)
         k.coop_blocks = (uint32_t)(8 * ((k.n_split + k.xcd_per - 1) / k.xcd_per));
         nb += k.coop_blocks;
     }
@@ -1558,6 +1562,15 @@ hipError_t run_fast(EdgeK k, int persist, hipStream_t s)
 #define PMA_EDGE_LAUNCH(W, S, M)                                                          \
     edge_fast<T, CH, LPH, 4, E_FUSE, QF, W, S, M><<<nb, 256, 0, s>>>(                    \
         k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.kpm_csr)
+    if (k.coop_blocks > 0) {   // (coop_merge: no mask, 32-bit offsets)
+        if (k.scores)
+            edge_fast<T, CH, LPH, 4, E_FUSE, QF, true, true, 0, 0, true><<<nb, 256, 0, s>>>(
+                k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.kpm_csr);
+        else
+            edge_fast<T, CH, LPH, 4, E_FUSE, QF, true, false, 0, 0, true><<<nb, 256, 0, s>>>(
+                k, k.csr_src, k.task_target, k.task_begin, k.task_end, k.task_slot, k.kpm_csr);
+        return hipGetLastError();
+    }
     if (k.kpm_bits) {
         if (!k.kpm_csr)
             return hipErrorInvalidValue;
@@ -1795,7 +1808,7 @@ bool edge_merges_splits(const EdgeArgs &x)
     if (lph > 16 || (lph & (lph - 1)) != 0)
         return false;
     set_passes(k, ch);
-    return coop_merge(k);
+    return coop_merge(k) && offsets32(k, x.dt == PMA_BF16 ? 2 : 4);
 }
 
 pma_status launch_edge(const EdgeArgs &x, hipStream_t s)

@@ -72,7 +72,7 @@ struct pma_plan {
     int persist = -1;           // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece, -1 auto)
     int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
     bool hot = false;           // PMA_HOT=1: hot-row cache in the q-projecting edge kernel
-    int coop = 1;               // PMA_COOP=0: split targets merged by a launch of their own
+    int coop = 0;               // PMA_COOP=1: split targets merged inside the edge kernel
     // hot-row cache: the gather index (hot_key) with ~slot for the edges of
     // the n_hot most-read rows hot_src[slot]
     int32_t *hot_csr = nullptr, *hot_src = nullptr;
@@ -390,8 +390,10 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_BWD_SORDER 0: banded source pass with its sample groups
     //                  interleaved instead of in turn within each band
     //   PMA_HOT        1: hot-row LDS cache in the q-projecting edge kernel
-    //   PMA_COOP       0: merge split targets in a launch of their own instead
-    //                  of in the edge kernel's leading workgroups
+    //   PMA_COOP       1: merge split targets of at most 4 pieces in the edge
+    //                  kernel's leading workgroups (one per target and sample
+    //                  group) instead of a launch of their own; measured
+    //                  on MI355X 2-3 us slower on the gene-regulatory forward
     // Piece length: a target is split only when it has far more edges than
     // the average target (16x, rounded up to a power of two, at least 256).
     // Splitting balances graphs with a few very long rows among many short
@@ -431,7 +433,7 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     if (const char *ev = getenv("PMA_HOT"))
         p->hot = ev[0] == '1';
     if (const char *ev = getenv("PMA_COOP"))
-        p->coop = ev[0] == '0' ? 0 : 1;
+        p->coop = ev[0] == '1' ? 1 : 0;
     if (const char *ev = getenv("PMA_FUSE_IN"))
         p->fuse_in = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))

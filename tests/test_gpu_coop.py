@@ -1,8 +1,8 @@
-"""Split targets merged inside the edge kernel. Where every split target has
-at most four pieces and the sample groups are pinned to XCDs, one workgroup
-per (split target, sample group) walks the target's pieces, one per
-wavefront, and merges them after a workgroup barrier, so no merge launch
-follows. Checked here: parity with the oracle, outputs, weights, softmax
+"""Split targets merged inside the edge kernel (opt-in, PMA_COOP=1). Where
+every split target has at most four pieces, the sample groups are pinned to
+XCDs and there is no key_padding_mask, one workgroup per (split target,
+sample group) walks the target's pieces, one per wavefront, and merges them
+after a workgroup barrier, so no merge launch follows. Checked here: parity with the oracle, outputs, weights, softmax
 statistics and gradients bit-identical to the separate merge launch
 (PMA_COOP=0), and which of the two a plan takes (the merge stage's launch
 count)."""
@@ -105,13 +105,14 @@ def test_coop_without_weights_and_averaged(dt, monkeypatch):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_coop_with_mask(dt, monkeypatch):
-    # per-sample mask; sample 1 masks every key of the first hub (its pieces
-    # then carry m = -inf, l = 0 and the target outputs the bias)
+def test_masked_forward_uses_the_merge_launch(dt, monkeypatch):
+    # with a key_padding_mask split targets keep the merge launch; sample 1
+    # masks every key of the first hub (its pieces then carry m = -inf, l = 0
+    # and the target outputs the bias)
     c = _hub_case(63, 8, 64, 4, dt, [50, 64])
     kpm = np.random.default_rng(64).random((c.B, c.S)) < 0.3
     kpm[1, c.src[c.tgt == 0]] = True
-    _pair(c, monkeypatch, kpm=kpm, need_weights=True, average=False)
+    _pair(c, monkeypatch, kpm=kpm, need_weights=True, average=False, expect_coop=False)
 
 
 def test_five_pieces_use_the_merge_launch(monkeypatch):
