@@ -65,7 +65,7 @@ struct EdgeK {
     // uniform word per edge, two when a wavefront spans 64 samples)
     const uint32_t *kpm_csr;
     int kpm_w32;
-    int nt;              // 1: non-temporal q loads and mixed stores
+    int nt;              // bit 0: non-temporal q loads, bit 1: non-temporal mixed / out stores
     float scale;         // log2(e) / sqrt(d)
     Layout lay;
     const void *qt, *kv;
@@ -339,7 +339,7 @@ __device__ inline void out_proj_wave(const EdgeK &a, const float *mix, int lane,
 #pragma unroll
     for (int k = 0; k < OW / 4; ++k) {
         const uint4 v = make_uint4(ow[4 * k], ow[4 * k + 1], ow[4 * k + 2], ow[4 * k + 3]);
-        if (a.nt)
+        if (a.nt & 2)
             store_nt(dst + 16 * k, v);
         else
             *reinterpret_cast<uint4 *>(dst + 16 * k) = v;
@@ -885,7 +885,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
         else
             qa = qt + tq * a.lay.q_t + b * a.lay.q_b + col;
         const uint4 *qp = reinterpret_cast<const uint4 *>(qa);
-        return a.nt ? load_nt(qp) : *qp;
+        return (a.nt & 1) ? load_nt(qp) : *qp;
     };
 
     // The next piece's query chunk is requested while this one runs, except
@@ -971,7 +971,7 @@ edge_fast(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__restric
                     dst += (uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col;
                 else
                     dst += t * a.lay.m_t + b * a.lay.m_b + col;
-                store_chunk<T, CH>(dst, out, a.nt != 0);
+                store_chunk<T, CH>(dst, out, (a.nt & 2) != 0);
             }
         } else if (st.active) {
             float *pa = a.part_acc, *pm = a.part_ml;
@@ -1094,7 +1094,7 @@ gather_probe(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__rest
         const int t = task_target[task], beg = task_begin[task], end = task_end[task];
         const uint4 *qp = reinterpret_cast<const uint4 *>(
             qt + ((uint32_t)t * (uint32_t)a.lay.q_t + (uint32_t)b * (uint32_t)a.lay.q_b + col));
-        uint4 acc = a.nt ? load_nt(qp) : *qp;
+        uint4 acc = (a.nt & 1) ? load_nt(qp) : *qp;
         int p = beg;
         for (; p + 4 <= end; p += 4) {
             u32x4 kw[4], vw[4];
@@ -1123,7 +1123,7 @@ gather_probe(EdgeK a, const int32_t *__restrict__ csr_src, const int32_t *__rest
         }
         if (active) {
             void *dst = mixed + ((uint32_t)t * (uint32_t)a.lay.m_t + (uint32_t)b * (uint32_t)a.lay.m_b + col);
-            if (a.nt)
+            if (a.nt & 2)
                 store_nt(dst, acc);
             else
                 *reinterpret_cast<uint4 *>(dst) = acc;

@@ -68,7 +68,7 @@ struct pma_plan {
     int xcd_map = -1;           // PMA_XCD_MAP: 1 sample group per XCD, 2 groups in turn, 0 off, -1 automatic
     bool fuse_out = true;       // PMA_FUSE_OUT=0: out_proj as a separate kernel
     bool fuse_in = true;        // PMA_FUSE_IN=0: q projection as a separate kernel
-    int nt = -1;                // PMA_NT: non-temporal (1) or cached (0) q / mixed streams, auto (-1)
+    int nt = -1;                // PMA_NT: non-temporal streams (bit 0 q loads, bit 1 mixed / out stores), auto (-1)
     int persist = -1;           // PMA_PERSIST: edge-kernel workgroups per CU (0: one per piece, -1 auto)
     int compact = -1;           // PMA_COMPACT: key/value rows only for read sources (1), all (0), auto (-1)
     bool hot = false;           // PMA_HOT=1: hot-row cache in the q-projecting edge kernel
@@ -376,7 +376,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //   PMA_FUSE_IN    0: q projection as a separate kernel
     //   PMA_XCD_MAP    1: one sample group per XCD, 2: sample groups in
     //                  turn, 0: interleaved (default automatic)
-    //   PMA_NT         1 / 0: non-temporal or cached q / mixed streams
+    //   PMA_NT         0..3: non-temporal q loads (bit 0) and mixed / out
+    //                  stores (bit 1)
     //   PMA_LAYOUT     "batch": batch-first q / k / v / mixed workspace
     //   PMA_PERSIST    n: at most n edge-kernel workgroups per CU, each
     //                  wavefront walking several pieces (0: one per piece)
@@ -438,8 +439,11 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         p->fuse_in = ev[0] != '0';
     if (const char *ev = getenv("PMA_XCD_MAP"))
         p->xcd_map = ev[0] == '0' ? 0 : ev[0] == '2' ? 2 : 1;
-    if (const char *ev = getenv("PMA_NT"))
-        p->nt = ev[0] == '0' ? 0 : 1;
+    if (const char *ev = getenv("PMA_NT")) {
+        const long v = strtol(ev, nullptr, 10);
+        if (v >= 0 && v <= 3)
+            p->nt = (int)v;
+    }
     if (const char *ev = getenv("PMA_LAYOUT"))
         p->batch_first_ws = strcmp(ev, "batch") == 0;
     if (const char *ev = getenv("PMA_COMPACT"))
@@ -899,12 +903,17 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
             return fail(st, "mask packing failed: %s", hipGetErrorString(hipGetLastError()));
         ea.kpm_csr = p->kpm_csr;
     }
-    // Automatic choices (measured on MI355X): stream q and mixed past the
+    // Automatic choices (measured on MI355X): the inference forward reads
+    // each query row once, past the caches, so that its misses evict (and
+    // write back) nothing (gene edge kernel 126 -> 112 us when the caches
+    // hold a previous kernel's dirty lines, level when they hold clean ones;
+    // only a forward repeated on the very same tokens loses, 96 -> 114 us);
+    // mixed and out stores, and the training forward's q loads, go past the
     // caches only when the workspace outgrows the 256 MB last-level cache;
     // keep the edge kernel's wavefronts resident and walking pieces when
     // pieces are short (then per-piece start-up latency dominates).
     const double ws_bytes = ((double)L + 2.0 * S_ws) * B * E * es;
-    ea.nt = p->nt >= 0 ? p->nt : (ws_bytes > 256.0 * 1024 * 1024 ? 1 : 0);
+    ea.nt = p->nt >= 0 ? p->nt : ((ws_bytes > 256.0 * 1024 * 1024 ? 3 : 0) | (save ? 0 : 1));
     ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 12 : 0);
     ea.fuse_out = fuse_out;
     ea.wo = o_w;

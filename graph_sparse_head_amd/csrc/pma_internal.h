@@ -126,7 +126,7 @@ struct EdgeArgs {
     int average;
     int xcd_map = 1;    // 1: sample group fixed per XCD where the group count
                         // divides 8; 2: groups in turn; 0: interleaved
-    int nt = 1;         // non-temporal q loads / mixed stores
+    int nt = 3;         // bit 0: non-temporal q loads, bit 1: non-temporal mixed / out stores
     const uint64_t *kpm_bits = nullptr;  // key_padding_mask bits (pack_mask layout)
     const uint32_t *kpm_csr = nullptr;   // the same by CSR position (gather_mask)
     int kpm_w32 = 0;                     // its 32-bit words per position

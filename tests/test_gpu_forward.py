@@ -297,6 +297,8 @@ KNOBS = [
     {"PMA_CHUNK": "3", "PMA_FUSE_OUT": "0"},
     {"PMA_XCD_MAP": "1"},
     {"PMA_XCD_MAP": "0", "PMA_NT": "0"},
+    {"PMA_NT": "2", "PMA_CHUNK": "3"},
+    {"PMA_NT": "3", "PMA_FUSE_OUT": "0"},
     {"PMA_FUSE_IN": "0"},
     {"PMA_FUSE_IN": "0", "PMA_CHUNK": "3"},
     {"PMA_HOT": "1"},
