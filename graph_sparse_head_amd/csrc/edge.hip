@@ -473,7 +473,7 @@ constexpr uint32_t kHotSlot = 2048;
 //
 // Per edge the source's key/value row offset is wave-uniform: one scalar
 // multiply gives it, and each lane adds its fixed offset inside the row. When
-// the key/value workspace is under 4 GiB the gathers are buffer loads whose
+// every tensor the kernel addresses is under 2 GiB the gathers are buffer loads whose
 // scalar offset is that product (no vector address arithmetic; a read past
 // the buffer returns zeros instead of faulting); otherwise they are global
 // loads from a uniform 64-bit base. Lanes past the last chunk read lane 0's

@@ -328,6 +328,28 @@ def random_case(seed: int, B: int, L: int, S: int, E: int, H: int, p: float,
                 xq, xk, xv, params)
 
 
+def wide(seed: int, dtype: str, B: int, E: int, H: int, L: int, S: int, deg: int,
+         hub: int, need_weights: bool = True, name: str = "wide") -> Case:
+    """Few targets over many sources, so that the key / value rows of the
+    batch pass 2 GiB: every target has ``deg`` distinct uniform sources, except
+    targets 0 and 1 (``hub`` each), every 97th from 3 (none) and every 89th
+    from 5 (one). Query tokens distinct from key = value tokens."""
+    g = np.random.default_rng(seed)
+    src, tgt = [], []
+    for t in range(L):
+        d = hub if t < 2 else 0 if t % 97 == 3 else 1 if t % 89 == 5 else deg
+        src.append(g.choice(S, size=d, replace=False))
+        tgt.append(np.full(d, t, np.int64))
+    src = np.concatenate(src).astype(np.int64)
+    tgt = np.concatenate(tgt)
+    perm = g.permutation(src.shape[0])
+    xq = _tokens(g, (B, L, E), dtype)
+    xk = _tokens(g, (B, S, E), dtype)
+    params = _params(g, E, dtype, _xavier_bound(E), "normal")
+    return Case(name, B, L, S, E, H, dtype, src[perm], tgt[perm], False, need_weights, True,
+                xq, xk, xk, params)
+
+
 CONFIGS = ("tiny", "complete", "gene", "bipartite", "large")
 
 
