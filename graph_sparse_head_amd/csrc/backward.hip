@@ -855,6 +855,16 @@ constexpr int kWgPart = 64 * 64 + 64;   // floats per partial (dW block, db)
 // Workgroup x of a weight-gradient launch: its pair, its rows, and the
 // partial of 64 x 64 block z (partials of one pair and block are adjacent,
 // in workgroup order).
+// Storage row of pair row r (the row list, where there is one).
+__device__ inline int64_t wg_row(const WGradPair &p, int64_t r)
+{
+    if (!p.list)
+        return r;
+    const uint32_t rr = (uint32_t)r, n = (uint32_t)p.n;
+    const uint32_t b = rr / n;
+    return (int64_t)b * p.n_in + p.list[rr - b * n];
+}
+
 struct WgSlice {
     WGradPair pr;
     int64_t r_beg, r_end;
@@ -917,8 +927,9 @@ __global__ void __launch_bounds__(256) bwd_wgrad(const WGrad a)
         for (int u = 0; u < UR; ++u) {
             const int64_t r = r0 + 16 * u + lr;
             if (r < r_end) {
-                load4(G + r * a.E, g[u]);
-                load4(X + r * a.E, x[u]);
+                const int64_t rr = wg_row(pr, r);
+                load4(G + rr * a.E, g[u]);
+                load4(X + rr * a.E, x[u]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) g[u][i] = x[u][i] = 0.f;
@@ -993,7 +1004,7 @@ __global__ void __launch_bounds__(256) bwd_wgrad_quad(const WGrad a)
 #pragma unroll
         for (int u = 0; u < UR; ++u) {
             int64_t r = r0 + 4 * u + lr;
-            r = r < r_end ? r : r_end - 1;
+            r = wg_row(pr, r < r_end ? r : r_end - 1);
             gg[u] = *reinterpret_cast<const float4 *>(G + r * a.E);
             xx[u] = *reinterpret_cast<const float4 *>(X + r * a.E);
         }
@@ -1101,8 +1112,9 @@ __global__ void __launch_bounds__(256) bwd_wgrad_bf16(const WGrad a)
         for (int j = 0; j < RPT; ++j) {
             const int64_t r = r0 + RPT * rq + j;
             if (r < r_end) {
-                gv[j] = ld16(G + r * a.E);
-                xv[j] = ld16(X + r * a.E);
+                const int64_t rr = wg_row(pr, r);
+                gv[j] = ld16(G + rr * a.E);
+                xv[j] = ld16(X + rr * a.E);
             } else {
                 gv[j] = xv[j] = make_uint4(0, 0, 0, 0);
             }
@@ -1238,8 +1250,10 @@ __global__ void __launch_bounds__(256) bwd_wgrad_generic(const WGrad a)
     const T *G = reinterpret_cast<const T *>(pr.g);
     const T *X = reinterpret_cast<const T *>(pr.x);
     float acc = 0.f;
-    for (int64_t r = threadIdx.x; r < pr.rows; r += 256)
-        acc = bias ? acc + ld(G + r * E + n) : fmaf(ld(G + r * E + n), ld(X + r * E + k), acc);
+    for (int64_t r = threadIdx.x; r < pr.rows; r += 256) {
+        const int64_t rr = wg_row(pr, r);
+        acc = bias ? acc + ld(G + rr * E + n) : fmaf(ld(G + rr * E + n), ld(X + rr * E + k), acc);
+    }
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {

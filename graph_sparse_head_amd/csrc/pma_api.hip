@@ -1285,6 +1285,16 @@ PMA_API pma_status pma_backward(pma_plan *plan, int64_t batch, const void *query
         w.p[1] = {dq, query, RLr, grad_q_w, has_bias ? grad_q_b : nullptr};
         w.p[2] = {dk, key, RSr, grad_k_w, has_bias ? grad_k_b : nullptr};
         w.p[3] = {dv, value, RSr, grad_v_w, has_bias ? grad_v_b : nullptr};
+        if (compact && RSr < ((int64_t)1 << 31)) {
+            // dk and dv are zero on the sources no edge reads: only the
+            // read sources' rows of dk, dv and the key / value tokens
+            for (int i = 2; i < 4; ++i) {
+                w.p[i].rows = B * gd.n_kv;
+                w.p[i].list = gd.kv_rows;
+                w.p[i].n = gd.n_kv;
+                w.p[i].n_in = S;
+            }
+        }
         ok(pma::launch_wgrad(w, dt, stream));
     }
 

@@ -235,6 +235,11 @@ struct WGradPair {
     const void *g, *x;
     int64_t rows;
     void *dw, *db;
+    // With a row list (B * n_in < 2^31), pair row r = b * n + i reads row
+    // b * n_in + list[i] of G and of X: the rows of the other tokens are zero
+    // in G (sources that no edge reads) and are skipped.
+    const int32_t *list = nullptr;
+    int64_t n = 0, n_in = 0;
 };
 struct WGrad {
     WGradPair p[4];
