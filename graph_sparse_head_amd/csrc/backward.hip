@@ -139,6 +139,12 @@ template <typename T> __device__ inline void widen(const uint4 &u, float (&f)[Ve
     }
 }
 __device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_nt;
+__device__ inline uint4 ld16_nt(const void *p)
+{
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---- edge passes, 16-byte lanes -----------------------------------------
 // Thread = (piece, sample, 16-byte chunk of the row), chunks fastest; LPH
@@ -199,15 +205,17 @@ bwd_target_fast(const BwdArgs a)
     const int slot = a.t_slot[task];
     const int h = c / LPH;
     const int64_t row = ((int64_t)b * a.L + t) * a.E + c * VEC;
-    const uint4 qw = ld16(reinterpret_cast<const T *>(a.q) + row);
-    const uint4 dmw = ld16(reinterpret_cast<const T *>(a.dm) + row);
+    const T *qp = reinterpret_cast<const T *>(a.q) + row, *dmp = reinterpret_cast<const T *>(a.dm) + row;
+    const uint4 qw = (a.nt & 2) ? ld16_nt(qp) : ld16(qp);
+    const uint4 dmw = (a.nt & 2) ? ld16_nt(dmp) : ld16(dmp);
     float qv[VEC], dmv[VEC];
     widen<T>(qw, qv);
     widen<T>(dmw, dmv);
     float D = 0.f;
     {
         float mx[VEC];
-        widen<T>(ld16(reinterpret_cast<const T *>(a.mixed) + row), mx);
+        const T *mp = reinterpret_cast<const T *>(a.mixed) + row;
+        widen<T>((a.nt & 1) ? ld16_nt(mp) : ld16(mp), mx);
 #pragma unroll
         for (int i = 0; i < VEC; ++i)
             D = fmaf(dmv[i], mx[i], D);
