@@ -61,7 +61,8 @@ template <> __device__ inline void st<uint16_t>(uint16_t *p, float x) { *p = f2b
 template <typename T> struct Vec {
     static constexpr int N = 16 / (int)sizeof(T);
 };
-template <typename T> __device__ inline void store_vec(T *p, const float (&f)[Vec<T>::N])
+template <typename T>
+__device__ inline void store_vec(T *p, const float (&f)[Vec<T>::N], bool nt = false)
 {
     uint4 u;
     if constexpr (sizeof(T) == 4) {
@@ -71,7 +72,11 @@ template <typename T> __device__ inline void store_vec(T *p, const float (&f)[Ve
         u = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
                        pack_bf16(f[6], f[7]));
     }
-    *reinterpret_cast<uint4 *>(p) = u;
+    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_s;
+    if (nt)
+        __builtin_nontemporal_store(u32x4_s{u.x, u.y, u.z, u.w}, reinterpret_cast<u32x4_s *>(p));
+    else
+        *reinterpret_cast<uint4 *>(p) = u;
 }
 template <int N> __device__ inline void store_f32(float *p, const float (&f)[N])
 {
@@ -330,7 +335,7 @@ bwd_target_fast(const BwdArgs a)
     for (int i = 0; i < VEC; ++i)
         dq[i] *= a.inv_sqrt_d;
     if (slot < 0)
-        store_vec(reinterpret_cast<T *>(a.dq) + row, dq);
+        store_vec(reinterpret_cast<T *>(a.dq) + row, dq, (a.nt & 8) != 0);
     else
         store_f32(a.part_q + ((int64_t)slot * a.B + b) * a.E + c * VEC, dq);
 }
@@ -395,8 +400,10 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
     uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
     if (live) {
         const int r = a.kv_src[a.csc_pos[beg]];
-        kw = ld16(reinterpret_cast<const T *>(a.k) + ((int64_t)b * a.Skv + r) * a.E + c * VEC);
-        vw = ld16(reinterpret_cast<const T *>(a.v) + ((int64_t)b * a.Skv + r) * a.E + c * VEC);
+        const T *kp = reinterpret_cast<const T *>(a.k) + ((int64_t)b * a.Skv + r) * a.E + c * VEC;
+        const T *vp = reinterpret_cast<const T *>(a.v) + ((int64_t)b * a.Skv + r) * a.E + c * VEC;
+        kw = (a.nt & 4) ? ld16_nt(kp) : ld16(kp);
+        vw = (a.nt & 4) ? ld16_nt(vp) : ld16(vp);
     }
     float kf[BF ? 1 : VEC], vf[BF ? 1 : VEC];
     if constexpr (!BF) {
@@ -483,8 +490,8 @@ __global__ void __launch_bounds__(256) bwd_source_fast(const BwdArgs a)
         dk[i] *= a.inv_sqrt_d;
     if (slot < 0) {
         const int64_t row = ((int64_t)b * a.S + s) * a.E + c * VEC;
-        store_vec(reinterpret_cast<T *>(a.dk) + row, dk);
-        store_vec(reinterpret_cast<T *>(a.dv) + row, dv);
+        store_vec(reinterpret_cast<T *>(a.dk) + row, dk, (a.nt & 8) != 0);
+        store_vec(reinterpret_cast<T *>(a.dv) + row, dv, (a.nt & 8) != 0);
     } else {
         float *d = a.part_kv + ((int64_t)slot * a.B + b) * 2 * a.E + c * VEC;
         store_f32(d, dk);

@@ -61,7 +61,7 @@ struct pma_plan {
     int bsub = 1;               // PMA_BWD_SUB: target bands per XCD for the backward's source pieces
     int border = -1;            // PMA_BWD_ORDER: backward target pass over sample groups (0, 1, 2; -1 automatic)
     int bpf = -1;               // PMA_BWD_PF: backward target pass requests the next rows ahead (1), not (0), auto (-1)
-    int bnt = 3;                // PMA_BWD_NT: target pass loads mixed (bit 0), q and dm (bit 1) non-temporally
+    int bnt = 15;               // PMA_BWD_NT: non-temporal target-pass loads of mixed (bit 0), q and dm (bit 1), source-pass key / value loads (bit 2), dq / dk / dv stores (bit 3)
     // PMA_BWD_SORDER: banded source pass with its sample groups in turn
     // within each band (2, default) or interleaved (0)
     int bsorder = 2;
@@ -391,10 +391,12 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //                  rows requested ahead (default automatic)
     //   PMA_BWD_SORDER 0: banded source pass with its sample groups
     //                  interleaved instead of in turn within each band
-    //   PMA_BWD_NT     0..3: backward target pass loads the mixed rows (bit
-    //                  0) and the q and dm rows (bit 1) non-temporally
-    //                  (default 3: each is read once there; 100k-node
-    //                  training step 5.54 -> 5.50 ms, gene 0.89 -> 0.88 ms)
+    //   PMA_BWD_NT     0..15: non-temporal backward streams, each read or
+    //                  written once there: the target pass's mixed rows (bit
+    //                  0) and q and dm rows (bit 1), the source pass's own
+    //                  key and value rows (bit 2), the dq, dk, dv stores (bit
+    //                  3); default 15 (training step, cold: gene 0.887 ->
+    //                  0.866 ms, 100k-node 5.54 -> 5.48, bipartite 1.84 -> 1.80)
     //   PMA_HOT        1: hot-row LDS cache in the q-projecting edge kernel
     //   PMA_COOP       1: merge split targets of at most 4 pieces in the edge
     //                  kernel's leading workgroups (one per target and sample
@@ -429,7 +431,7 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         p->bpf = ev[0] == '0' ? 0 : 1;
     if (const char *ev = getenv("PMA_BWD_NT")) {
         const long v = strtol(ev, nullptr, 10);
-        if (v >= 0 && v <= 3)
+        if (v >= 0 && v <= 15)
             p->bnt = (int)v;
     }
     if (const char *ev = getenv("PMA_BWD_ORDER"))
@@ -913,17 +915,18 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
             return fail(st, "mask packing failed: %s", hipGetErrorString(hipGetLastError()));
         ea.kpm_csr = p->kpm_csr;
     }
-    // Automatic choices (measured on MI355X): the inference forward reads
-    // each query row once, past the caches, so that its misses evict (and
-    // write back) nothing (gene edge kernel 126 -> 112 us when the caches
-    // hold a previous kernel's dirty lines, level when they hold clean ones;
-    // only a forward repeated on the very same tokens loses, 96 -> 114 us);
-    // mixed and out stores, and the training forward's q loads, go past the
-    // caches only when the workspace outgrows the 256 MB last-level cache;
-    // keep the edge kernel's wavefronts resident and walking pieces when
-    // pieces are short (then per-piece start-up latency dominates).
+    // Automatic choices (measured on MI355X): the forward reads each query
+    // row once, past the caches, so that its misses evict (and write back)
+    // nothing (gene edge kernel 126 -> 112 us when the caches hold a previous
+    // kernel's dirty lines, level when they hold clean ones; only a forward
+    // repeated on the very same tokens loses, 96 -> 114 us); mixed and out
+    // stores go past the caches in training (the backward reads them much
+    // later; with the q loads, gene training step 0.870 -> 0.857 ms) and
+    // where the workspace outgrows the 256 MB last-level cache; keep the
+    // edge kernel's wavefronts resident and walking pieces when pieces are
+    // short (then per-piece start-up latency dominates).
     const double ws_bytes = ((double)L + 2.0 * S_ws) * B * E * es;
-    ea.nt = p->nt >= 0 ? p->nt : ((ws_bytes > 256.0 * 1024 * 1024 ? 3 : 0) | (save ? 0 : 1));
+    ea.nt = p->nt >= 0 ? p->nt : (save || ws_bytes > 256.0 * 1024 * 1024 ? 3 : 1);
     ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 12 : 0);
     ea.fuse_out = fuse_out;
     ea.wo = o_w;

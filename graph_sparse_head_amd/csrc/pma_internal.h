@@ -173,7 +173,9 @@ struct BwdArgs {
     float scale_log2;    // log2(e) / sqrt(d): the forward's score scale
     float inv_sqrt_d;
     const void *q, *k, *v, *mixed;   // saved, batch-first, plan dtype
-    int nt = 0;                      // target pass: non-temporal mixed (bit 0), q and dm (bit 1)
+    // non-temporal: target-pass loads of mixed (bit 0), of q and dm (bit 1),
+    // source-pass key / value loads (bit 2), dq / dk / dv stores (bit 3)
+    int nt = 0;
     int Skv;                         // key/value rows per sample in the save area
     const int32_t *kv_src;           // per CSR entry, its key/value row there
     const float *ml;                 // saved [L][B][H][2] (max, sum), base 2

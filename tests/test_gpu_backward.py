@@ -282,7 +282,7 @@ def test_backward_target_pass_without_prefetch(shape, chunk, mask, monkeypatch):
 @pytest.mark.parametrize("knobs", [{"PMA_BWD_CHUNK": "3"}, {"PMA_BWD_CHUNK": "16"},
                                    {"PMA_BWD_SUB": "2"}, {"PMA_BWD_SUB": "5", "PMA_BWD_CHUNK": "4"},
                                    {"PMA_BWD_PF": "1"}, {"PMA_BWD_NT": "0"},
-                                   {"PMA_BWD_NT": "1", "PMA_BWD_PF": "0"}],
+                                   {"PMA_BWD_NT": "1", "PMA_BWD_PF": "0"}, {"PMA_BWD_NT": "6"}],
                          ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()))
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_backward_source_piece_knobs(knobs, dt, monkeypatch):
