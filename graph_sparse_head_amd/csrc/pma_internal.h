@@ -126,7 +126,7 @@ struct EdgeArgs {
     int average;
     int xcd_map = 1;    // 1: sample group fixed per XCD where the group count
                         // divides 8; 2: groups in turn; 0: interleaved
-    int nt = 3;         // bit 0: non-temporal q loads, bit 1: non-temporal mixed / out stores
+    int nt = 0;         // bit 0: non-temporal q loads, bit 1: non-temporal mixed / out stores
     const uint64_t *kpm_bits = nullptr;  // key_padding_mask bits (pack_mask layout)
     const uint32_t *kpm_csr = nullptr;   // the same by CSR position (gather_mask)
     int kpm_w32 = 0;                     // its 32-bit words per position
@@ -147,7 +147,7 @@ struct EdgeArgs {
     int n_hot = 0;
     // split targets merged inside the edge kernel where each has at most 4
     // pieces (max_pieces: the most pieces of one target; see edge_fast)
-    int coop = 1;
+    int coop = 0;
     int max_pieces = 0;
 };
 
