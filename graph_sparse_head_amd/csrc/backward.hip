@@ -61,6 +61,13 @@ template <> __device__ inline void st<uint16_t>(uint16_t *p, float x) { *p = f2b
 template <typename T> struct Vec {
     static constexpr int N = 16 / (int)sizeof(T);
 };
+// 16-byte loads and stores past the caches (rows read or written once)
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_nt;
+__device__ inline uint4 ld16_nt(const void *p)
+{
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 template <typename T>
 __device__ inline void store_vec(T *p, const float (&f)[Vec<T>::N], bool nt = false)
 {
@@ -72,9 +79,8 @@ __device__ inline void store_vec(T *p, const float (&f)[Vec<T>::N], bool nt = fa
         u = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
                        pack_bf16(f[6], f[7]));
     }
-    typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_s;
     if (nt)
-        __builtin_nontemporal_store(u32x4_s{u.x, u.y, u.z, u.w}, reinterpret_cast<u32x4_s *>(p));
+        __builtin_nontemporal_store(u32x4_nt{u.x, u.y, u.z, u.w}, reinterpret_cast<u32x4_nt *>(p));
     else
         *reinterpret_cast<uint4 *>(p) = u;
 }
@@ -144,12 +150,6 @@ template <typename T> __device__ inline void widen(const uint4 &u, float (&f)[Ve
     }
 }
 __device__ inline uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_nt;
-__device__ inline uint4 ld16_nt(const void *p)
-{
-    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // ---- edge passes, 16-byte lanes -----------------------------------------
 // Thread = (piece, sample, 16-byte chunk of the row), chunks fastest; LPH
@@ -867,9 +867,6 @@ __global__ void __launch_bounds__(256) bwd_rowmm_generic(const RowMM a, int E)
 // the partials in workgroup order.
 constexpr int kWgPart = 64 * 64 + 64;   // floats per partial (dW block, db)
 
-// Workgroup x of a weight-gradient launch: its pair, its rows, and the
-// partial of 64 x 64 block z (partials of one pair and block are adjacent,
-// in workgroup order).
 // Storage row of pair row r (the row list, where there is one).
 __device__ inline int64_t wg_row(const WGradPair &p, int64_t r)
 {
@@ -880,6 +877,9 @@ __device__ inline int64_t wg_row(const WGradPair &p, int64_t r)
     return (int64_t)b * p.n_in + p.list[rr - b * n];
 }
 
+// Workgroup x of a weight-gradient launch: its pair, its rows, and the
+// partial of 64 x 64 block z (partials of one pair and block are adjacent,
+// in workgroup order).
 struct WgSlice {
     WGradPair pr;
     int64_t r_beg, r_end;
