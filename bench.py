@@ -40,7 +40,7 @@ def _workload(name: str):
     return synth.make_config(name)
 
 
-def edge_kernel_bytes(B, L, n_kv, nnz, n_tasks, E, s, weights=False, H=1):
+def edge_kernel_bytes(B, L, n_kv, nnz, n_tasks, E, s, weights=False, H=1, masked=False):
     """Compulsory HBM bytes of one edge-kernel launch: what the launch must
     move at the least, each byte once. Per (target, sample): its query row in
     (query tokens when the kernel projects q itself, else the projected q)
@@ -48,10 +48,14 @@ def edge_kernel_bytes(B, L, n_kv, nnz, n_tasks, E, s, weights=False, H=1):
     2 E s. Per (read source, sample): its key row and value row, once: 2 E s.
     Per edge its gather index (4 B) and per piece its bounds, target and slot
     (16 B). need_weights adds the stored score of every (edge, sample, head)
-    and the (max, sum) of every (target, sample, head), 4 B each."""
+    and the (max, sum) of every (target, sample, head), 4 B each. A
+    key_padding_mask adds its bits by edge position: one 32-bit word per
+    edge and 32 samples."""
     b = B * L * 2 * E * s + B * n_kv * 2 * E * s + 4 * nnz + 16 * n_tasks
     if weights:
         b += 4 * B * nnz * H + 8 * B * L * H
+    if masked:
+        b += 4 * nnz * ((B + 31) // 32)
     return b
 
 
@@ -501,10 +505,11 @@ def main():
         edge_ms, edge_calls = stages["edge"]
         edge_avg_s = edge_ms / max(edge_calls, 1) * 1e-3
         nbytes = edge_kernel_bytes(case.B, case.L, info["kv_rows"], nnz, info["n_tasks"],
-                                   case.E, es, case.need_weights, case.H)
+                                   case.E, es, case.need_weights, case.H, kpm is not None)
         gbytes = edge_gather_bytes(case.B, case.L, nnz, case.E, es)
         achieved = nbytes / edge_avg_s / 1e9
-        traffic = _traffic(args.config)
+        # (the committed counters are of the unmasked forward)
+        traffic = _traffic(args.config) if kpm is None else None
         res["roofline"] = {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,

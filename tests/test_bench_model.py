@@ -29,3 +29,14 @@ def test_gather_model_of_the_gene_workload():
     g = bench.edge_gather_bytes(32, 20000, 196614, 64, 2)
     assert g == 32 * (20000 * 128 + 196614 * 256 + 20000 * 128) + 4 * 20001 + 4 * 196614
     assert g == 1_775_368_348
+
+
+def test_compulsory_bytes_with_a_key_padding_mask():
+    # one 32-bit mask word per edge position and 32 samples: gene B = 32
+    # needs one word per edge, 70 samples three
+    base = bench.edge_kernel_bytes(32, 20000, 8096, 196614, 20033, 64, 2)
+    masked = bench.edge_kernel_bytes(32, 20000, 8096, 196614, 20033, 64, 2, masked=True)
+    assert masked - base == 196614 * 4
+    b70 = bench.edge_kernel_bytes(70, 10, 10, 100, 10, 64, 2, masked=True) - \
+        bench.edge_kernel_bytes(70, 10, 10, 100, 10, 64, 2)
+    assert b70 == 100 * 4 * 3
