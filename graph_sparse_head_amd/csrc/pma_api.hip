@@ -61,6 +61,7 @@ struct pma_plan {
     int bsub = 1;               // PMA_BWD_SUB: target bands per XCD for the backward's source pieces
     int border = -1;            // PMA_BWD_ORDER: backward target pass over sample groups (0, 1, 2; -1 automatic)
     int bpf = -1;               // PMA_BWD_PF: backward target pass requests the next rows ahead (1), not (0), auto (-1)
+    bool x3 = true;             // PMA_F32_SPLIT=0: fp32 projections on the fp32 matrix cores
     int bnt = 15;               // PMA_BWD_NT: non-temporal target-pass loads of mixed (bit 0), q and dm (bit 1), source-pass key / value loads (bit 2), dq / dk / dv stores (bit 3)
     // PMA_BWD_SORDER: banded source pass with its sample groups in turn
     // within each band (2, default) or interleaved (0)
@@ -391,6 +392,9 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
     //                  rows requested ahead (default automatic)
     //   PMA_BWD_SORDER 0: banded source pass with its sample groups
     //                  interleaved instead of in turn within each band
+    //   PMA_F32_SPLIT  0: fp32 projections at embed_dim 128 on the fp32
+    //                  matrix cores instead of split-bf16 products (proj_x3;
+    //                  bipartite key/value projection 206 -> 2 x 90 us)
     //   PMA_BWD_NT     0..15: non-temporal backward streams, each read or
     //                  written once there: the target pass's mixed rows (bit
     //                  0) and q and dm rows (bit 1), the source pass's own
@@ -429,6 +433,8 @@ pma_status create_impl(pma_plan **plan, const int64_t *source_index, const int64
         p->bsorder = ev[0] == '0' ? 0 : 2;
     if (const char *ev = getenv("PMA_BWD_PF"))
         p->bpf = ev[0] == '0' ? 0 : 1;
+    if (const char *ev = getenv("PMA_F32_SPLIT"))
+        p->x3 = ev[0] != '0';
     if (const char *ev = getenv("PMA_BWD_NT")) {
         const long v = strtol(ev, nullptr, 10);
         if (v >= 0 && v <= 15)
@@ -849,6 +855,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
                        pma::ProjOut o2) {
         pma::ProjArgs a{x, B * n, n, B, 0, nblk, {o0, o1, o2}};
         a.x_token_major = 0;
+        a.x3 = p->x3 && p->dtype == PMA_F32;
         return a;
     };
     auto kv_args = [&](const void *x, int nblk, pma::ProjOut o0, pma::ProjOut o1) {

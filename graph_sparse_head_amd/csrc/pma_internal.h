@@ -91,6 +91,7 @@ struct ProjArgs {
     // b * n_in + row_list[i] (batch-first input of n_in tokens per sample).
     const int32_t *row_list = nullptr;
     int64_t n_in = 0;
+    int x3 = 0;       // fp32, embed_dim 128: split-bf16 matrix-core products (proj_x3)
 };
 
 pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s);

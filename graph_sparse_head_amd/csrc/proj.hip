@@ -279,6 +279,134 @@ __global__ void __launch_bounds__(WAVES * 64) proj_mfma(ProjArgs a)
     }
 }
 
+// fp32 values as the sum of three bf16 values: hi = bf16(x), mid =
+// bf16(x - hi), lo = bf16(x - hi - mid). Each rounding keeps the next 8
+// significant bits and the differences are exact in fp32, so hi + mid + lo
+// is x itself (24 significant bits) for every x away from the bottom of the
+// exponent range. Eight consecutive values become three bf16x8 operands.
+__device__ inline void split3(const float (&x)[8], uint4 &h, uint4 &m, uint4 &l)
+{
+    float r1[8], r2[8];
+    uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hw[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+        r1[2 * i] = x[2 * i] - bf2f((uint16_t)(hw[i] & 0xffffu));
+        r1[2 * i + 1] = x[2 * i + 1] - bf2f((uint16_t)(hw[i] >> 16));
+        mw[i] = pack_bf16(r1[2 * i], r1[2 * i + 1]);
+        r2[2 * i] = r1[2 * i] - bf2f((uint16_t)(mw[i] & 0xffffu));
+        r2[2 * i + 1] = r1[2 * i + 1] - bf2f((uint16_t)(mw[i] >> 16));
+        lw[i] = pack_bf16(r2[2 * i], r2[2 * i + 1]);
+    }
+    h = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    m = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    l = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+
+// fp32 projection at embed_dim 128 on the bf16 matrix cores: x W^T with x
+// and W each split into three bf16 parts (split3) and six of the nine part
+// products summed in fp32 (hi hi, hi mid, mid hi, hi lo, lo hi, mid mid;
+// the three left out are below 2^-23 of each product, the size of an fp32
+// rounding). Per 32 multiply-adds of a lane the fp32 path issues eight
+// v_mfma_f32_16x16x4f32 and this one six v_mfma_f32_16x16x32_bf16, each at
+// twice the rate: 6/16 of the fp32 matrix-core time. One output block per launch: its weight parts
+// fill 96 KB of LDS in fragment order (part, n-tile, k-step; lane (m, g)
+// holds W[16 n-tile + m][32 k-step + 8 g .. + 7]); the workgroup's 16
+// wavefronts walk tiles of 16 rows each, the next tile's x loaded ahead.
+// Lane (n, g) of a wavefront loads x[row n][32 ks + 8 g .. + 7] and ends
+// with output channels 16 nt + 4 g .. + 3 of row n, which it stores.
+constexpr int kX3Waves = 16;
+constexpr size_t kX3Lds = 3 * 8 * 4 * 1024 + 128 * 4;
+__global__ void __launch_bounds__(kX3Waves * 64) proj_x3(ProjArgs a)
+{
+    constexpr int E = 128, NT = E / 16, NKS = E / 32;
+    constexpr int PART = NT * NKS * 1024;     // bytes of one weight part
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    float *bl = reinterpret_cast<float *>(lds + 3 * PART);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int ln = lane & 15, lg = lane >> 4;
+    const ProjOut &o = a.out[0];
+    {
+        const float *W = reinterpret_cast<const float *>(o.w);
+        for (int f = threadIdx.x; f < NT * NKS * 64; f += kX3Waves * 64) {
+            const int l = f & 63, fk = f >> 6, ks = fk % NKS, nt = fk / NKS;
+            const float *wr = W + (nt * 16 + (l & 15)) * E + ks * 32 + (l >> 4) * 8;
+            const float4 w0 = *reinterpret_cast<const float4 *>(wr);
+            const float4 w1 = *reinterpret_cast<const float4 *>(wr + 4);
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            uint4 h, m, lo;
+            split3(wv, h, m, lo);
+            *reinterpret_cast<uint4 *>(lds + f * 16) = h;
+            *reinterpret_cast<uint4 *>(lds + PART + f * 16) = m;
+            *reinterpret_cast<uint4 *>(lds + 2 * PART + f * 16) = lo;
+        }
+        const float *bias = reinterpret_cast<const float *>(o.b);
+        for (int n = threadIdx.x; n < E; n += kX3Waves * 64)
+            bl[n] = bias ? bias[n] : 0.f;
+    }
+    __syncthreads();
+
+    const int64_t tile_rows = (int64_t)kX3Waves * 16;
+    const int64_t ntiles = (a.rows + tile_rows - 1) / tile_rows;
+    uint4 xn[NKS][2];
+    auto load_x = [&](int64_t tile) {
+        const int64_t r = tile * tile_rows + wid * 16 + ln;
+        const float *xr = reinterpret_cast<const float *>(a.x) + in_row(a, r < a.rows ? r : 0) * E +
+                          lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            xn[ks][0] = *reinterpret_cast<const uint4 *>(xr + ks * 32);
+            xn[ks][1] = *reinterpret_cast<const uint4 *>(xr + ks * 32 + 4);
+        }
+    };
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles)
+        load_x(tile);
+    for (; tile < ntiles; tile += gridDim.x) {
+        uint4 xh[NKS], xm[NKS], xl[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const float xv[8] = {__uint_as_float(xn[ks][0].x), __uint_as_float(xn[ks][0].y),
+                                 __uint_as_float(xn[ks][0].z), __uint_as_float(xn[ks][0].w),
+                                 __uint_as_float(xn[ks][1].x), __uint_as_float(xn[ks][1].y),
+                                 __uint_as_float(xn[ks][1].z), __uint_as_float(xn[ks][1].w)};
+            split3(xv, xh[ks], xm[ks], xl[ks]);
+        }
+        if (tile + gridDim.x < ntiles)
+            load_x(tile + gridDim.x);
+        const int64_t r = tile * tile_rows + wid * 16 + ln;
+        int64_t db, di;
+        decompose(a, r, db, di);
+#pragma unroll 2
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = nt * 16 + 4 * lg;
+            const float4 b4 = *reinterpret_cast<const float4 *>(bl + n);
+            f32x4 acc = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const char *fr = lds + ((nt * NKS + ks) * 64 + lane) * 16;
+                const bf16x8 wh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(fr));
+                const bf16x8 wm = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(fr + PART));
+                const bf16x8 wl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(fr + 2 * PART));
+                const bf16x8 ph = __builtin_bit_cast(bf16x8, xh[ks]);
+                const bf16x8 pm = __builtin_bit_cast(bf16x8, xm[ks]);
+                const bf16x8 pl = __builtin_bit_cast(bf16x8, xl[ks]);
+                // smallest products first
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wm, pm, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, ph, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, pl, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wm, ph, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, pm, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, ph, acc, 0, 0, 0);
+            }
+            if (r < a.rows) {
+                float *d = reinterpret_cast<float *>(o.dst) + db * o.sb + di * o.si + n;
+                *reinterpret_cast<float4 *>(d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+    }
+}
+
 // Any embed_dim: one thread per (row, output channel), fp32 fused multiply-add.
 template <typename T>
 __global__ void __launch_bounds__(256) proj_generic(ProjArgs a, int E)
@@ -370,6 +498,31 @@ hipError_t run_mfma(const ProjArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t run_x3(const ProjArgs &a, hipStream_t s)
+{
+    static bool raised = false;
+    if (!raised) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&proj_x3),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (e != hipSuccess)
+            return e;
+        raised = true;
+    }
+    const int64_t tile_rows = (int64_t)kX3Waves * 16;
+    const int64_t ntiles = (a.rows + tile_rows - 1) / tile_rows;
+    const int64_t grid = ntiles < cu_count() ? ntiles : cu_count();
+    for (int j = 0; j < a.nblk; ++j) {   // one output block per launch
+        ProjArgs one = a;
+        one.nblk = 1;
+        one.out[0] = a.out[j];
+        hipLaunchKernelGGL(proj_x3, dim3((unsigned)grid), dim3(kX3Waves * 64), kX3Lds, s, one);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
 template <typename T>
 hipError_t run_generic(const ProjArgs &a, int64_t E, hipStream_t s)
 {
@@ -402,6 +555,8 @@ pma_status launch_proj(const ProjArgs &a, int64_t E, pma_dtype dt, hipStream_t s
     } else {
         if (E == 64)
             e = run_mfma<float, 64, 1, 8>(a, s);
+        else if (E == 128 && a.x3)
+            e = run_x3(a, s);
         else if (E == 128 && a.rows >= (int64_t)cu_count() * 16 * 16 * 2)
             // 64 KB of weights per output block leave room for one or two
             // workgroups per CU: 16 wavefronts each keep the matrix cores busy

@@ -244,6 +244,24 @@ def test_binding_rejects_buffers_of_the_wrong_size():
         pma.pma_destroy(plan)
 
 
+# fp32 at embed_dim 128: projections as split-bf16 matrix-core products
+# (default) or on the fp32 matrix cores (PMA_F32_SPLIT=0); ragged row tiles
+# (B * L and B * S not multiples of 256), separate query / key / value tokens,
+# with and without biases, per-head weights.
+@pytest.mark.parametrize("split", ["1", "0"])
+@pytest.mark.parametrize("bias", ["normal", "none"])
+def test_fp32_embed128_projections(split, bias, monkeypatch):
+    monkeypatch.setenv("PMA_F32_SPLIT", split)
+    c = synth.random_case(101, 3, 171, 203, 128, 8, 0.05, dtype="f32", bias=bias, same_kv=False,
+                          same_qkv=False, name="f32_e128")
+    print(f"[forward] fp32 E=128 split={split} bias={bias}", flush=True)
+    out, w, plan = run(c, need_weights=True, average=False)
+    pma.pma_destroy(plan)
+    ref = oracle.case_forward(c, want_weights=True)
+    assert max_abs_rel(out, ref["out"]) <= TOL["f32"]
+    assert max_abs_rel(w, ref["weights"]) <= TOL["f32"]
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads in the launch configuration the benchmark times: every
 # output element (and every per-edge weight) against the oracle
