@@ -1005,6 +1005,7 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     const int mixed_token_major = lay.m_b == E ? 1 : 0;
     pma::ProjArgs ao{mixed_ws, L * B, L, B, mixed_token_major, 1, {oo}};
     ao.x_token_major = mixed_token_major;
+    ao.x3 = p->x3 && p->dtype == PMA_F32;
     st = pma::launch_proj(ao, E, p->dtype, stream);
     tm.end();
     if (st != PMA_OK)
