@@ -934,7 +934,9 @@ pma_status forward_impl(pma_plan *plan, int64_t batch, const void *query, const 
     // short (then per-piece start-up latency dominates).
     const double ws_bytes = ((double)L + 2.0 * S_ws) * B * E * es;
     ea.nt = p->nt >= 0 ? p->nt : (save || ws_bytes > 256.0 * 1024 * 1024 ? 3 : 1);
-    ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 12 : 0);
+    // (16 workgroups per CU: gene forward 151.8-152.5 -> 150.0-150.4 us cold
+    // against 12, four alternations of 60 steps)
+    ea.persist = p->persist >= 0 ? p->persist : (p->nnz < 32 * p->g.n_tasks ? 16 : 0);
     ea.fuse_out = fuse_out;
     ea.wo = o_w;
     ea.bo = o_b;
